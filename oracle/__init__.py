@@ -1,0 +1,194 @@
+"""ctypes wrapper of the plain CPU oracle (oracle.c) -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may use
+this package. The GPU library neither imports nor links it, and it imports
+nothing from the GPU package.
+
+All results are float64 numpy arrays (ids and permutation arrays int32).
+Inputs are numpy arrays in their storage formats: x float32 or bf16 bits
+(uint16), router weights float32, expert weights as produced by
+``synth.gen_experts``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "oracle.c")
+
+DT = {"f32": 0, "bf16": 1, "fp8": 2, "fp4": 3}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O2, no fast-math, OpenMP) into liboracle.so."""
+    if force or not os.path.exists(LIB_PATH):
+        tmp = LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-Wall", "-Wno-unknown-pragmas", SRC_PATH, "-o", tmp, "-lm"])
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC_PATH):
+            build()
+        _lib = ctypes.CDLL(LIB_PATH)
+    return _lib
+
+
+def _p(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _check(rc, fn):
+    if rc != 0:
+        raise RuntimeError(f"oracle {fn} failed with code {rc}")
+
+
+def _rows(rows):
+    if rows is None:
+        return None
+    return np.ascontiguousarray(rows, dtype=np.int64)
+
+
+def _xdt(x):
+    if x.dtype == np.float32:
+        return DT["f32"]
+    if x.dtype == np.uint16:
+        return DT["bf16"]
+    raise TypeError(f"x must be float32 or bf16 bits (uint16), got {x.dtype}")
+
+
+def format_op(kind: str, values) -> np.ndarray:
+    """Format decoding/rounding of the oracle: kind in bf16, e4m3, e2m1 (codes -> value),
+    round_bf16, round_f32 (value -> rounded value)."""
+    k = {"bf16": 0, "e4m3": 1, "e2m1": 2, "round_bf16": 3, "round_f32": 4}[kind]
+    v = np.ascontiguousarray(values, dtype=np.float64).ravel()
+    out = np.empty_like(v)
+    f = lib().oracle_format
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    _check(f(k, _p(v), v.size, _p(out)), "format")
+    return out.reshape(np.shape(values))
+
+
+def logits(x, w_router, bias=None, rows=None) -> np.ndarray:
+    """Exact router logits [n, E] (float64)."""
+    x = np.ascontiguousarray(x)
+    T, H = x.shape
+    wr = np.ascontiguousarray(w_router, dtype=np.float32)
+    E = wr.shape[1]
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    r = _rows(rows)
+    n = T if r is None else r.size
+    out = np.empty((n, E), np.float64)
+    f = lib().oracle_logits
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    _check(f(_xdt(x), _p(x), T, H, _p(wr), _p(b), E, _p(r), n, _p(out)), "logits")
+    return out
+
+
+def route(logits_, k: int, sel_dtype: str = "bf16", want_sel: bool = False):
+    """(ids [n,k] int32, w [n,k] float64[, sel [n,E]]) from logits [n,E]."""
+    lg = np.ascontiguousarray(logits_, dtype=np.float64)
+    n, E = lg.shape
+    ids = np.empty((n, k), np.int32)
+    w = np.empty((n, k), np.float64)
+    sel = np.empty((n, E), np.float64) if want_sel else None
+    f = lib().oracle_route
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    _check(f(DT[sel_dtype], _p(lg), n, E, k, _p(ids), _p(w), _p(sel)), "route")
+    return (ids, w, sel) if want_sel else (ids, w)
+
+
+def permute(ids, E: int):
+    """(counts [E], offsets [E+1], sorted_pair [T*k], pair_pos [T*k]) int32."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T, k = ids.shape
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    sp = np.empty(T * k, np.int32)
+    pp = np.empty(T * k, np.int32)
+    f = lib().oracle_permute
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 4
+    _check(f(_p(ids), T, k, E, _p(counts), _p(offsets), _p(sp), _p(pp)), "permute")
+    return counts, offsets, sp, pp
+
+
+def _wargs(experts: dict):
+    dt = DT[experts["dtype"]]
+    arr = lambda key: (None if experts.get(key) is None else np.ascontiguousarray(experts[key]))
+    gu, dn = arr("gate_up"), arr("down")
+    gus, dns = arr("gate_up_scale"), arr("down_scale")
+    gug, dng = arr("gate_up_gscale"), arr("down_gscale")
+    keep = (gu, dn, gus, dns, gug, dng)
+    return dt, keep
+
+
+def expert_rows(x, experts: dict, I: int, tokens, expert_ids, want_h: bool = False):
+    """y [n, H] (and h [n, I]) for the (token, expert) rows given."""
+    x = np.ascontiguousarray(x)
+    T, H = x.shape
+    dt, (gu, dn, gus, dns, gug, dng) = _wargs(experts)
+    E = gu.shape[0]
+    tok = np.ascontiguousarray(tokens, dtype=np.int32).ravel()
+    ex = np.ascontiguousarray(expert_ids, dtype=np.int32).ravel()
+    n = tok.size
+    y = np.empty((n, H), np.float64)
+    h = np.empty((n, I), np.float64) if want_h else None
+    f = lib().oracle_expert_rows
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_int] + [ctypes.c_void_p] * 8 + [ctypes.c_int64] + [ctypes.c_void_p] * 2
+    _check(f(_xdt(x), _p(x), T, H, I, E, dt, _p(gu), _p(dn), _p(gus), _p(dns), _p(gug), _p(dng),
+             _p(tok), _p(ex), n, _p(y), _p(h)), "expert_rows")
+    return (y, h) if want_h else y
+
+
+def finalize(y_sorted, pair_pos, w, k: int, rows=None) -> np.ndarray:
+    """out [n, H] (float64) = slot-ordered weighted sum of the fp32 sorted expert rows."""
+    ys = np.ascontiguousarray(y_sorted, dtype=np.float32)
+    pp = np.ascontiguousarray(pair_pos, dtype=np.int32).ravel()
+    ww = np.ascontiguousarray(w, dtype=np.float32).ravel()
+    H = ys.shape[1]
+    T = pp.size // k
+    r = _rows(rows)
+    n = T if r is None else r.size
+    out = np.empty((n, H), np.float64)
+    f = lib().oracle_finalize
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    _check(f(_p(ys), _p(pp), _p(ww), T, k, H, _p(r), n, _p(out)), "finalize")
+    return out
+
+
+def layer(x, w_router, bias, experts: dict, I: int, k: int, sel_dtype: str = "bf16", rows=None):
+    """Whole layer for the given tokens: dict(out [n,H], ids [n,k], w [n,k], logits [n,E])."""
+    x = np.ascontiguousarray(x)
+    T, H = x.shape
+    wr = np.ascontiguousarray(w_router, dtype=np.float32)
+    E = wr.shape[1]
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    dt, (gu, dn, gus, dns, gug, dng) = _wargs(experts)
+    r = _rows(rows)
+    n = T if r is None else r.size
+    out = np.empty((n, H), np.float64)
+    ids = np.empty((n, k), np.int32)
+    w = np.empty((n, k), np.float64)
+    lg = np.empty((n, E), np.float64)
+    f = lib().oracle_layer
+    f.argtypes = ([ctypes.c_int, ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_int32] * 4 +
+                  [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 7 +
+                  [ctypes.c_int64] + [ctypes.c_void_p] * 4)
+    _check(f(_xdt(x), _p(x), T, H, I, E, k, _p(wr), _p(b), DT[sel_dtype], dt, _p(gu), _p(dn),
+             _p(gus), _p(dns), _p(gug), _p(dng), _p(r), n, _p(out), _p(ids), _p(w), _p(lg)), "layer")
+    return {"out": out, "ids": ids, "w": w, "logits": lg}

@@ -1,0 +1,456 @@
+/*
+ * oracle.c -- plain CPU oracle of Beam's routed mixture-of-experts layer.
+ *
+ * TEST INFRASTRUCTURE ONLY. The test suite, the smoke check and the
+ * benchmark's CPU-baseline leg are the only callers; the GPU library never
+ * links, loads or calls this code, and the two share no source.
+ *
+ * Everything is computed in double precision, without fast-math, in the
+ * order the definition states. Inputs arrive in their storage formats
+ * (fp32, bf16 bits, FP8 E4M3 codes, packed FP4 E2M1 codes with E4M3 block
+ * scales) and are decoded exactly, element by element, from the format
+ * definitions below.
+ *
+ * What the layer computes, and where it is stated:
+ *  - router: a GEMM of shape (5120, 256) with BF16 output (vLLM PR #61978
+ *    "Day-0 support for Reflection's Beam-1.0", Status table, row #62042),
+ *    accumulated in FP32 (UpstreamBeat, "vLLM adds day-zero Reflection Beam
+ *    serving...", section "Agents worked on the serving path": a specialized
+ *    FP32 router kernel);
+ *  - each token goes to 8 of 256 routed experts (vLLM recipe
+ *    "reflection/Beam-1.0-501B-A23B", Guide > Overview);
+ *  - routed expert outputs are combined by a "MoE finalize" step (PR #61978,
+ *    Status table row #62366 and Remaining work);
+ *  - the NVFP4 variant quantises the routed experts only and, on Hopper,
+ *    runs them with BF16 activations (recipe, Guide > Variants).
+ * The routing function (softmax over all E logits, top-k with ties to the
+ * lowest expert id, renormalised weights), SwiGLU with gate columns [0, I)
+ * and up columns [I, 2I) of the merged gate/up matrix, and the expert width
+ * are conventions the pages leave open; they are the readings this oracle
+ * fixes.
+ *
+ * Parity pins: every function here is checked by the CPU test suite against
+ * brute force, closed forms or library routines (see tests/test_oracle_*.py).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ODT_F32 = 0, ODT_BF16 = 1, ODT_FP8 = 2, ODT_FP4 = 3 };
+enum { ORACLE_OK = 0, ORACLE_EINVAL = 1, ORACLE_ENOMEM = 2 };
+
+/* ------------------------------------------------------------------ formats */
+
+/* bf16: the upper 16 bits of an IEEE binary32. */
+static double bf16_value(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* FP8 E4M3 ("fn"): sign, 4 exponent bits (bias 7), 3 mantissa bits; no
+   infinities, S.1111.111 is NaN; exponent 0 is subnormal (m/8 * 2^-6). */
+static double e4m3_value(uint8_t c) {
+  int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+  return s ? -v : v;
+}
+
+/* FP4 E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit; exponent 0 is
+   subnormal (m * 0.5). Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+static double e2m1_value(uint8_t c) {
+  int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+  double v = (e == 0) ? 0.5 * m : ldexp((double)(2 + m), e - 2); /* (1 + m/2) 2^(e-1) */
+  return s ? -v : v;
+}
+
+/* Round to the nearest bf16 value, ties to even, in one step from double. */
+static double round_bf16(double v) {
+  if (v == 0.0 || !isfinite(v)) return v;
+  int e;
+  double m = frexp(v, &e); /* v = m * 2^e, 0.5 <= |m| < 1 */
+  if (e - 1 < -126) /* below the smallest normal: fixed quantum 2^-133 */
+    return ldexp(nearbyint(ldexp(v, 133)), -133);
+  return ldexp(nearbyint(ldexp(m, 8)), e - 8); /* 8 significant bits */
+}
+
+/* Round to the nearest fp32 value, ties to even (C's conversion). */
+static double round_f32(double v) { return (double)(float)v; }
+
+static double x_value(int x_dt, const void* x, int64_t i) {
+  return x_dt == ODT_F32 ? (double)((const float*)x)[i] : bf16_value(((const uint16_t*)x)[i]);
+}
+
+/* Exported for the format pins. kind: 0 bf16 code, 1 e4m3 code, 2 e2m1 code,
+   3 round-to-bf16, 4 round-to-fp32. Codes are passed as doubles. */
+int oracle_format(int kind, const double* in, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) {
+    switch (kind) {
+      case 0: out[i] = bf16_value((uint16_t)in[i]); break;
+      case 1: out[i] = e4m3_value((uint8_t)in[i]); break;
+      case 2: out[i] = e2m1_value((uint8_t)in[i]); break;
+      case 3: out[i] = round_bf16(in[i]); break;
+      case 4: out[i] = round_f32(in[i]); break;
+      default: return ORACLE_EINVAL;
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------ router */
+
+/* logits[i, e] = bias[e] + sum_h x[t, h] * W_r[h, e], h ascending, for the
+   tokens t = rows[i] (all tokens when rows is NULL). x is bf16 or fp32, W_r is
+   fp32 [H, E]; every product is exact in double (at most 8 + 24 significant
+   bits), so the sum is the exact logit up to double rounding of the sum. */
+int oracle_logits(int x_dt, const void* x, int64_t T, int32_t H, const float* w_router,
+                  const float* bias, int32_t E, const int64_t* rows, int64_t n, double* out) {
+  if (!x || !w_router || !out || H <= 0 || E <= 0 || T < 0) return ORACLE_EINVAL;
+  if (x_dt != ODT_F32 && x_dt != ODT_BF16) return ORACLE_EINVAL;
+  for (int64_t i = 0; i < n; ++i)
+    if (rows && (rows[i] < 0 || rows[i] >= T)) return ORACLE_EINVAL;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t t = rows ? rows[i] : i;
+    double* o = out + i * E;
+    for (int e = 0; e < E; ++e) o[e] = bias ? (double)bias[e] : 0.0;
+    for (int h = 0; h < H; ++h) {
+      double xv = x_value(x_dt, x, t * H + h);
+      const float* w = w_router + (int64_t)h * E;
+      for (int e = 0; e < E; ++e) o[e] += xv * (double)w[e];
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------ routing */
+
+typedef struct {
+  double v;
+  int id;
+} cand;
+
+/* larger value first; equal values: lower expert id first */
+static int cand_cmp(const void* a, const void* b) {
+  const cand* x = (const cand*)a;
+  const cand* y = (const cand*)b;
+  if (x->v > y->v) return -1;
+  if (x->v < y->v) return 1;
+  return (x->id > y->id) - (x->id < y->id);
+}
+
+/* Routing of n tokens from their logits.
+   The selection value is the logit as the router emits it: rounded to bf16
+   (sel_dt = BF16) or to fp32 (sel_dt = F32). p = softmax over all E selection
+   values; the k chosen experts are the first k in the order (value desc,
+   id asc), emitted in that order; w_j = p[S_j] / sum_j' p[S_j'].
+   sel (optional, [n, E]) receives the selection values. */
+int oracle_route(int sel_dt, const double* logits, int64_t n, int32_t E, int32_t k, int32_t* ids,
+                 double* w, double* sel) {
+  if (!logits || !ids || !w || E <= 0 || k <= 0 || k > E) return ORACLE_EINVAL;
+  if (sel_dt != ODT_F32 && sel_dt != ODT_BF16) return ORACLE_EINVAL;
+  int err = ORACLE_OK;
+#pragma omp parallel
+  {
+    cand* c = (cand*)malloc(sizeof(cand) * (size_t)E);
+    double* p = (double*)malloc(sizeof(double) * (size_t)E);
+    if (!c || !p) {
+#pragma omp atomic write
+      err = ORACLE_ENOMEM;
+    } else {
+#pragma omp for schedule(static)
+      for (int64_t i = 0; i < n; ++i) {
+        const double* l = logits + i * E;
+        double mx = -INFINITY, z = 0.0, zs = 0.0;
+        for (int e = 0; e < E; ++e) {
+          double v = sel_dt == ODT_BF16 ? round_bf16(l[e]) : round_f32(l[e]);
+          c[e].v = v;
+          c[e].id = e;
+          if (sel) sel[i * E + e] = v;
+          if (v > mx) mx = v;
+        }
+        for (int e = 0; e < E; ++e) {
+          p[e] = exp(c[e].v - mx);
+          z += p[e];
+        }
+        for (int e = 0; e < E; ++e) p[e] /= z;
+        qsort(c, (size_t)E, sizeof(cand), cand_cmp);
+        for (int j = 0; j < k; ++j) zs += p[c[j].id];
+        for (int j = 0; j < k; ++j) {
+          ids[i * k + j] = c[j].id;
+          w[i * k + j] = p[c[j].id] / zs;
+        }
+      }
+    }
+    free(c);
+    free(p);
+  }
+  return err;
+}
+
+/* ------------------------------------------------------------------ permute */
+
+/* Stable counting sort of the pair indices p = t*k + j by expert:
+   counts[e] = #pairs routed to e; offsets = exclusive prefix sum (E+1 long);
+   sorted_pair lists the pairs ordered by (expert, p); pair_pos is its inverse. */
+int oracle_permute(const int32_t* ids, int64_t T, int32_t k, int32_t E, int32_t* counts,
+                   int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos) {
+  int64_t P = T * k;
+  if (!counts || !offsets || E <= 0 || k <= 0 || T < 0) return ORACLE_EINVAL;
+  for (int64_t p = 0; p < P; ++p)
+    if (ids[p] < 0 || ids[p] >= E) return ORACLE_EINVAL;
+  int32_t* cursor = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+  if (!cursor) return ORACLE_ENOMEM;
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t p = 0; p < P; ++p) counts[ids[p]]++;
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  for (int e = 0; e < E; ++e) cursor[e] = offsets[e];
+  for (int64_t p = 0; p < P; ++p) {
+    int32_t r = cursor[ids[p]]++;
+    sorted_pair[r] = (int32_t)p;
+    pair_pos[p] = r;
+  }
+  free(cursor);
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------ experts */
+
+typedef struct {
+  int dt;
+  int32_t H, I;
+  const void *gate_up, *down;
+  const void *gate_up_scale, *down_scale;
+  const float *gate_up_gscale, *down_gscale;
+} weights;
+
+/* Row h (K index) of expert e's gate/up matrix, all 2I columns, as doubles.
+   f32/bf16 layout [E, H, 2I]; fp8 [E, 2I, H] codes with fp32 [E, 2I] channel
+   scales; fp4 [E, 2I, H/2] packed codes (even k in the low nibble) with E4M3
+   block scales [E, 2I, H/16] and an fp32 scale per expert. */
+static void gate_up_row(const weights* W, int e, int h, double* row) {
+  int64_t N = 2 * (int64_t)W->I, H = W->H;
+  switch (W->dt) {
+    case ODT_F32: {
+      const float* s = (const float*)W->gate_up + ((int64_t)e * H + h) * N;
+      for (int64_t n = 0; n < N; ++n) row[n] = s[n];
+    } break;
+    case ODT_BF16: {
+      const uint16_t* s = (const uint16_t*)W->gate_up + ((int64_t)e * H + h) * N;
+      for (int64_t n = 0; n < N; ++n) row[n] = bf16_value(s[n]);
+    } break;
+    case ODT_FP8: {
+      const uint8_t* q = (const uint8_t*)W->gate_up;
+      const float* sc = (const float*)W->gate_up_scale;
+      for (int64_t n = 0; n < N; ++n)
+        row[n] = e4m3_value(q[((int64_t)e * N + n) * H + h]) * (double)sc[(int64_t)e * N + n];
+    } break;
+    case ODT_FP4: {
+      const uint8_t* q = (const uint8_t*)W->gate_up;
+      const uint8_t* sb = (const uint8_t*)W->gate_up_scale;
+      double g = W->gate_up_gscale[e];
+      for (int64_t n = 0; n < N; ++n) {
+        uint8_t byte = q[((int64_t)e * N + n) * (H / 2) + h / 2];
+        uint8_t nib = (h & 1) ? (byte >> 4) : (byte & 15);
+        row[n] = e2m1_value(nib) * e4m3_value(sb[((int64_t)e * N + n) * (H / 16) + h / 16]) * g;
+      }
+    } break;
+  }
+}
+
+/* Row i (K index) of expert e's down matrix, all H columns.
+   f32/bf16 [E, I, H]; fp8 [E, H, I] + [E, H]; fp4 [E, H, I/2] + [E, H, I/16] + [E]. */
+static void down_row(const weights* W, int e, int i, double* row) {
+  int64_t N = W->H, I = W->I;
+  switch (W->dt) {
+    case ODT_F32: {
+      const float* s = (const float*)W->down + ((int64_t)e * I + i) * N;
+      for (int64_t n = 0; n < N; ++n) row[n] = s[n];
+    } break;
+    case ODT_BF16: {
+      const uint16_t* s = (const uint16_t*)W->down + ((int64_t)e * I + i) * N;
+      for (int64_t n = 0; n < N; ++n) row[n] = bf16_value(s[n]);
+    } break;
+    case ODT_FP8: {
+      const uint8_t* q = (const uint8_t*)W->down;
+      const float* sc = (const float*)W->down_scale;
+      for (int64_t n = 0; n < N; ++n)
+        row[n] = e4m3_value(q[((int64_t)e * N + n) * I + i]) * (double)sc[(int64_t)e * N + n];
+    } break;
+    case ODT_FP4: {
+      const uint8_t* q = (const uint8_t*)W->down;
+      const uint8_t* sb = (const uint8_t*)W->down_scale;
+      double g = W->down_gscale[e];
+      for (int64_t n = 0; n < N; ++n) {
+        uint8_t byte = q[((int64_t)e * N + n) * (I / 2) + i / 2];
+        uint8_t nib = (i & 1) ? (byte >> 4) : (byte & 15);
+        row[n] = e2m1_value(nib) * e4m3_value(sb[((int64_t)e * N + n) * (I / 16) + i / 16]) * g;
+      }
+    } break;
+  }
+}
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* One routed expert applied to one token, as a SwiGLU FFN:
+   a = x_t W_gu[e] (length 2I), h = silu(a[0:I]) * a[I:2I], y = h W_d[e]
+   (length H). Sums run over ascending K; no intermediate rounding. */
+static void expert_ffn(int x_dt, const void* x, int64_t t, const weights* W, int e, double* a,
+                       double* row, double* y, double* h_out) {
+  int64_t H = W->H, I = W->I;
+  for (int64_t n = 0; n < 2 * I; ++n) a[n] = 0.0;
+  for (int64_t h = 0; h < H; ++h) {
+    double xv = x_value(x_dt, x, t * H + h);
+    gate_up_row(W, e, (int)h, row);
+    for (int64_t n = 0; n < 2 * I; ++n) a[n] += xv * row[n];
+  }
+  for (int64_t i = 0; i < I; ++i) a[i] = silu(a[i]) * a[I + i];
+  if (h_out)
+    for (int64_t i = 0; i < I; ++i) h_out[i] = a[i];
+  for (int64_t n = 0; n < H; ++n) y[n] = 0.0;
+  for (int64_t i = 0; i < I; ++i) {
+    down_row(W, e, (int)i, row);
+    for (int64_t n = 0; n < H; ++n) y[n] += a[i] * row[n];
+  }
+}
+
+static int make_weights(weights* W, int w_dt, int32_t H, int32_t I, const void* gate_up,
+                        const void* down, const void* gate_up_scale, const void* down_scale,
+                        const float* gate_up_gscale, const float* down_gscale) {
+  if (H <= 0 || I <= 0 || !gate_up || !down) return ORACLE_EINVAL;
+  if (w_dt < ODT_F32 || w_dt > ODT_FP4) return ORACLE_EINVAL;
+  if (w_dt == ODT_FP8 && (!gate_up_scale || !down_scale)) return ORACLE_EINVAL;
+  if (w_dt == ODT_FP4 && (!gate_up_scale || !down_scale || !gate_up_gscale || !down_gscale ||
+                          H % 16 || I % 16))
+    return ORACLE_EINVAL;
+  W->dt = w_dt;
+  W->H = H;
+  W->I = I;
+  W->gate_up = gate_up;
+  W->down = down;
+  W->gate_up_scale = gate_up_scale;
+  W->down_scale = down_scale;
+  W->gate_up_gscale = gate_up_gscale;
+  W->down_gscale = down_gscale;
+  return ORACLE_OK;
+}
+
+/* y[r] = FFN_{experts[r]}(x[tokens[r]]) for n (token, expert) rows;
+   optionally also the SwiGLU activations h[r] (length I). */
+int oracle_expert_rows(int x_dt, const void* x, int64_t T, int32_t H, int32_t I, int32_t E,
+                       int w_dt, const void* gate_up, const void* down, const void* gate_up_scale,
+                       const void* down_scale, const float* gate_up_gscale,
+                       const float* down_gscale, const int32_t* tokens, const int32_t* experts,
+                       int64_t n, double* y, double* h_out) {
+  weights W;
+  int rc = make_weights(&W, w_dt, H, I, gate_up, down, gate_up_scale, down_scale,
+                        gate_up_gscale, down_gscale);
+  if (rc) return rc;
+  if (!x || !tokens || !experts || !y) return ORACLE_EINVAL;
+  for (int64_t r = 0; r < n; ++r)
+    if (tokens[r] < 0 || tokens[r] >= T || experts[r] < 0 || experts[r] >= E) return ORACLE_EINVAL;
+  int err = ORACLE_OK;
+#pragma omp parallel
+  {
+    int64_t wmax = 2 * (int64_t)I > H ? 2 * (int64_t)I : H;
+    double* a = (double*)malloc(sizeof(double) * 2 * (size_t)I);
+    double* row = (double*)malloc(sizeof(double) * (size_t)wmax);
+    if (!a || !row) {
+#pragma omp atomic write
+      err = ORACLE_ENOMEM;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t r = 0; r < n; ++r)
+        expert_ffn(x_dt, x, tokens[r], &W, experts[r], a, row, y + r * H,
+                   h_out ? h_out + r * I : NULL);
+    }
+    free(a);
+    free(row);
+  }
+  return err;
+}
+
+/* ------------------------------------------------------------------ finalize */
+
+/* out[i] = sum_{j=0..k-1} w[t, j] * y_sorted[pair_pos[t*k + j]] for t = rows[i]
+   (all tokens when rows is NULL), summed in slot order. */
+int oracle_finalize(const float* y_sorted, const int32_t* pair_pos, const float* w, int64_t T,
+                    int32_t k, int32_t H, const int64_t* rows, int64_t n, double* out) {
+  if (!y_sorted || !pair_pos || !w || !out || k <= 0 || H <= 0) return ORACLE_EINVAL;
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t t = rows ? rows[i] : i;
+    if (t < 0 || t >= T) return ORACLE_EINVAL;
+    for (int j = 0; j < k; ++j)
+      if (pair_pos[t * k + j] < 0 || pair_pos[t * k + j] >= T * k) return ORACLE_EINVAL;
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t t = rows ? rows[i] : i;
+    double* o = out + i * H;
+    for (int h = 0; h < H; ++h) o[h] = 0.0;
+    for (int j = 0; j < k; ++j) {
+      const float* yr = y_sorted + (int64_t)pair_pos[t * k + j] * H;
+      double wj = w[t * k + j];
+      for (int h = 0; h < H; ++h) o[h] += wj * (double)yr[h];
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------ layer */
+
+/* The whole layer for the tokens rows[0..n) (all tokens when rows is NULL):
+   logits -> routing -> for each chosen expert its SwiGLU FFN ->
+   out[t] = sum_j w[t, j] * FFN_{S[t, j]}(x_t), in slot order.
+   Optional outputs: ids [n, k], w [n, k], logits [n, E] (exact, pre-rounding). */
+int oracle_layer(int x_dt, const void* x, int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                 const float* w_router, const float* bias, int sel_dt, int w_dt,
+                 const void* gate_up, const void* down, const void* gate_up_scale,
+                 const void* down_scale, const float* gate_up_gscale, const float* down_gscale,
+                 const int64_t* rows, int64_t n, double* out, int32_t* ids_out, double* w_out,
+                 double* logits_out) {
+  if (!out || k <= 0 || k > E) return ORACLE_EINVAL;
+  int rc = ORACLE_OK;
+  double* lg = logits_out ? logits_out : (double*)malloc(sizeof(double) * (size_t)(n * E + 1));
+  int32_t* ids = ids_out ? ids_out : (int32_t*)malloc(sizeof(int32_t) * (size_t)(n * k + 1));
+  double* w = w_out ? w_out : (double*)malloc(sizeof(double) * (size_t)(n * k + 1));
+  int32_t* tok = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n * k + 1));
+  double* y = (double*)malloc(sizeof(double) * (size_t)(n * k * (int64_t)H + 1));
+  if (!lg || !ids || !w || !tok || !y) {
+    rc = ORACLE_ENOMEM;
+    goto done;
+  }
+  rc = oracle_logits(x_dt, x, T, H, w_router, bias, E, rows, n, lg);
+  if (rc) goto done;
+  rc = oracle_route(sel_dt, lg, n, E, k, ids, w, NULL);
+  if (rc) goto done;
+  for (int64_t i = 0; i < n; ++i)
+    for (int j = 0; j < k; ++j) tok[i * k + j] = (int32_t)(rows ? rows[i] : i);
+  rc = oracle_expert_rows(x_dt, x, T, H, I, E, w_dt, gate_up, down, gate_up_scale, down_scale,
+                          gate_up_gscale, down_gscale, tok, ids, n * k, y, NULL);
+  if (rc) goto done;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    double* o = out + i * H;
+    for (int h = 0; h < H; ++h) o[h] = 0.0;
+    for (int j = 0; j < k; ++j) {
+      const double* yr = y + (i * k + j) * (int64_t)H;
+      for (int h = 0; h < H; ++h) o[h] += w[i * k + j] * yr[h];
+    }
+  }
+done:
+  if (!logits_out) free(lg);
+  if (!ids_out) free(ids);
+  if (!w_out) free(w);
+  free(tok);
+  free(y);
+  return rc;
+}
