@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MoE layer (Beam: H=5120, E=256, top-8, I=1536) on one MI355X.
+
+One step = one whole layer (router GEMM + top-k, permute, grouped SwiGLU expert
+GEMMs, finalize) over one batch of synthetic input already resident in HBM.
+The headline workload is decode (T=128 tokens, bf16 weights, near-uniform
+routing), bound by streaming the touched experts' weights from HBM; prefill
+(T=16384 = 8 x 2048 tokens, Zipf(1.1) expert load) is reported beside it
+against the bf16 MFMA peak.
+
+Prints one JSON line. Options: --gpus N (only 1 is supported), --steps K,
+--warmup W, --workload decode|prefill (headline), --no-prefill, --no-cpu.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s (H5120,E256,k8) + % peak HBM BW decode / % MFMA prefill"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", choices=["decode", "prefill"], default="decode")
+    p.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill line")
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    return p.parse_args()
+
+
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Workload:
+    """Device-resident inputs, outputs and workspace of one configuration."""
+
+    def __init__(self, cfg, moe, torch, dev_weights=None):
+        import synth
+        self.cfg, self.moe, self.torch = cfg, moe, torch
+        T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
+        self.x_host = synth.gen_x(cfg)
+        self.wr_host, self.bias_host = synth.gen_router(cfg)
+        self.x = moe.to_device_bf16(self.x_host)
+        self.wr = torch.from_numpy(self.wr_host).cuda()
+        self.bias = None if self.bias_host is None else torch.from_numpy(self.bias_host).cuda()
+        if dev_weights is None:
+            self.w_host = synth.gen_experts(cfg)
+            dev_weights = moe.experts_to_device(self.w_host)
+        self.w = dev_weights
+        P = T * k
+        dt = torch.bfloat16
+        self.out = torch.empty((T, H), dtype=dt, device="cuda")
+        self.logits = torch.empty((T, E), dtype=dt, device="cuda")
+        self.ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        self.tw = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        self.ws = moe.workspace(moe.moe_forward_workspace_size(T, H, I, E, k, self.w))
+        # stage-by-stage buffers
+        self.rws = moe.workspace(moe.moe_route_workspace_size(T, H, E))
+        self.counts = torch.empty(E, dtype=torch.int32, device="cuda")
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+        self.sp = torch.empty(P, dtype=torch.int32, device="cuda")
+        self.pp = torch.empty(P, dtype=torch.int32, device="cuda")
+        self.y = torch.empty((P, H), dtype=torch.float32, device="cuda")
+        self.ews = moe.workspace(moe.moe_experts_workspace_size(T, H, I, E, k, self.w))
+
+    def forward(self):
+        c = self.cfg
+        self.moe.moe_forward(self.x, self.wr, self.bias, self.w, c.I, c.k, self.out, self.ws,
+                             logits=self.logits, topk_ids=self.ids, topk_w=self.tw)
+
+    def stage_calls(self):
+        c, m = self.cfg, self.moe
+        return [
+            ("route", lambda: m.moe_route(self.x, self.wr, self.bias, c.k, m.MOE_BF16, self.logits,
+                                          None, self.ids, self.tw, self.rws)),
+            ("permute", lambda: m.moe_permute(self.ids, c.E, self.counts, self.offsets, self.sp,
+                                              self.pp)),
+            ("experts", lambda: m.moe_experts(self.x, c.I, c.E, c.k, self.offsets, self.sp, self.w,
+                                              self.y, self.ews)),
+            ("finalize", lambda: m.moe_finalize(self.y, self.pp, self.tw, self.out)),
+        ]
+
+    def time_forward(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.forward()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            self.forward()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    def time_stages(self, steps):
+        """Per-stage average durations (ms) from events recorded between the stage
+        calls on the stream the kernels run on."""
+        torch = self.torch
+        calls = self.stage_calls()
+        for _, f in calls:
+            f()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+               for _ in range(steps)]
+        for s in range(steps):
+            evs[s][0].record()
+            for i, (_, f) in enumerate(calls):
+                f()
+                evs[s][i + 1].record()
+        torch.cuda.synchronize()
+        out = {}
+        for i, (name, _) in enumerate(calls):
+            out[name] = float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)]))
+        return out
+
+    def touched(self):
+        self.torch.cuda.synchronize()
+        return self.counts.cpu().numpy()
+
+
+def expert_bytes(cfg):
+    """Bytes of one expert's bf16 weights: gate/up [H, 2I] + down [I, H]."""
+    return 2 * (cfg.H * 2 * cfg.I + cfg.I * cfg.H)
+
+
+def cpu_baseline(wl, budget_s=10.0):
+    """Oracle (fp64, OpenMP) on a bounded sample of the workload's tokens."""
+    import oracle
+    c = wl.cfg
+    n = 8
+    t = time.perf_counter()
+    oracle.layer(wl.x_host, wl.wr_host, wl.bias_host, wl.w_host, c.I, c.k, "bf16",
+                 rows=np.arange(n))
+    dt = time.perf_counter() - t
+    n2 = int(min(c.T, max(n, n * budget_s / max(dt, 1e-3))))
+    rows = np.linspace(0, c.T - 1, n2).astype(np.int64)
+    t = time.perf_counter()
+    oracle.layer(wl.x_host, wl.wr_host, wl.bias_host, wl.w_host, c.I, c.k, "bf16", rows=rows)
+    dt = time.perf_counter() - t
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(n2 / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n2} of the {c.T} {c.name} tokens (whole layer per token, fp64), {dt:.1f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the layer is measured "
+              f"unsharded on a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sparse_moe_layer_gemm_amd as moe
+    import synth
+
+    dec_cfg = synth.CONFIGS["decode_t128"]
+    pre_cfg = synth.CONFIGS["prefill_t16384_zipf"]
+    progress("generating decode inputs (T=128, bf16 experts)")
+    dec = Workload(dec_cfg, moe, torch)
+    progress("timing decode")
+    dec_ms = dec.time_forward(a.steps, a.warmup)
+    dec_stage = dec.time_stages(a.steps)
+    counts = dec.touched()
+    n_touched = int((counts > 0).sum())
+    wbytes = n_touched * expert_bytes(dec_cfg)
+    layer_bytes = wbytes + dec_cfg.H * dec_cfg.E * 4 + 2 * dec_cfg.T * dec_cfg.H * 2
+    dec_line = {
+        "value": dec_cfg.T / (dec_ms / 1e3),
+        "ms_per_step": dec_ms,
+        "stages_ms": dec_stage,
+        "touched_experts": n_touched,
+        "layer_hbm_frac": layer_bytes / (dec_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": "moe_experts (gate/up + down stream GEMMs)",
+                     "achieved": wbytes / (dec_stage["experts"] / 1e3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None},
+    }
+    dec_line["roofline"]["frac"] = dec_line["roofline"]["achieved"] / HBM_PEAK_GBS
+
+    pre_line = None
+    if not a.no_prefill or a.workload == "prefill":
+        progress("generating prefill inputs (T=16384, Zipf load; same expert weights)")
+        pre = Workload(pre_cfg, moe, torch, dev_weights=dec.w)
+        pre.w_host = dec.w_host
+        progress("timing prefill")
+        pre_ms = pre.time_forward(max(3, a.steps // 2), max(1, a.warmup // 2))
+        pre_stage = pre.time_stages(max(3, a.steps // 2))
+        P = pre_cfg.T * pre_cfg.k
+        flops = 2.0 * P * (pre_cfg.H * 2 * pre_cfg.I + pre_cfg.I * pre_cfg.H)
+        router_flops = 2.0 * pre_cfg.T * pre_cfg.H * pre_cfg.E
+        pc = pre.touched()
+        pre_line = {
+            "value": pre_cfg.T / (pre_ms / 1e3),
+            "ms_per_step": pre_ms,
+            "stages_ms": pre_stage,
+            "expert_load": {"max": int(pc.max()), "median": float(np.median(pc)), "min": int(pc.min())},
+            "layer_mfma_frac": (flops + router_flops) / (pre_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
+            "roofline": {"bound": "mfma", "kernel": "moe_experts (gate/up + down grouped GEMMs)",
+                         "achieved": flops / (pre_stage["experts"] / 1e3) / 1e12,
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "traffic": None},
+        }
+        pre_line["roofline"]["frac"] = pre_line["roofline"]["achieved"] / BF16_PEAK_TFLOPS
+
+    head, head_cfg = (dec_line, dec_cfg) if a.workload == "decode" else (pre_line, pre_cfg)
+    cpu = None
+    if not a.no_cpu:
+        progress("timing the CPU oracle on a token sample")
+        cpu = cpu_baseline(dec if a.workload == "decode" else pre)
+
+    line = {
+        "metric": METRIC,
+        "value": round(head["value"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": head_cfg.name, "T": head_cfg.T, "H": head_cfg.H, "E": head_cfg.E,
+                   "k": head_cfg.k, "I": head_cfg.I, "expert_weights": head_cfg.w_dtype,
+                   "routing": "zipf(1.1)" if head_cfg.zipf_s else "near-uniform",
+                   "parallelism": "single GPU, one unsharded layer"},
+        "roofline": head["roofline"],
+        "cpu_baseline": cpu,
+        "stages_ms": {k: round(v, 4) for k, v in head["stages_ms"].items()},
+    }
+    if a.workload == "decode":
+        line["touched_experts"] = dec_line["touched_experts"]
+        line["layer_hbm_frac"] = round(dec_line["layer_hbm_frac"], 4)
+        if pre_line is not None:
+            line["prefill"] = {"workload": pre_cfg.name, "value": round(pre_line["value"], 1),
+                               "unit": "tokens/s", "ms_per_step": round(pre_line["ms_per_step"], 4),
+                               "layer_mfma_frac": round(pre_line["layer_mfma_frac"], 4),
+                               "roofline": pre_line["roofline"],
+                               "stages_ms": {k: round(v, 4) for k, v in pre_line["stages_ms"].items()},
+                               "expert_load": pre_line["expert_load"]}
+    else:
+        line["expert_load"] = pre_line["expert_load"]
+        line["layer_mfma_frac"] = round(pre_line["layer_mfma_frac"], 4)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed mixture-of-experts layer of
+ * Reflection's Beam model: hidden 5120, 256 routed experts, 8 per token.
+ *
+ * The layer, as the pages state it:
+ *  - the router is a GEMM of shape (5120, 256) with BF16 output (vLLM PR
+ *    #61978 "Day-0 support for Reflection's Beam-1.0", Status table, row
+ *    #62042), computed by an FP32 router kernel (UpstreamBeat "vLLM adds
+ *    day-zero Reflection Beam serving...", section "Agents worked on the
+ *    serving path"; the pre-release router-dtype switch is gone, PR #61978
+ *    "What landed differs");
+ *  - every token is routed to 8 of 256 experts (vLLM recipe
+ *    "reflection/Beam-1.0-501B-A23B", Guide > Overview);
+ *  - the expert GEMMs are grouped per expert, gate and up projections are
+ *    one merged GEMM ("merged projections", UpstreamBeat, same section);
+ *  - a "MoE finalize" step combines the routed outputs per token (PR #61978,
+ *    Status table row #62366 and Remaining work);
+ *  - the quantised variant stores only the routed experts in NVFP4 and runs
+ *    them with BF16 activations (recipe, Guide > Variants).
+ * Conventions the pages leave open and this library fixes: softmax over all
+ * E logits, top-k by (logit desc, expert id asc), weights renormalised over
+ * the k chosen experts; SwiGLU h = silu(g) * u with gate = columns [0, I) and
+ * up = columns [I, 2I) of the merged matrix; no biases in the experts.
+ *
+ * Calling conventions (all entry points):
+ *  - Array arguments are DEVICE pointers owned by the caller (for example
+ *    torch tensors' data_ptr()), row-major and contiguous, 16-byte aligned.
+ *    The library allocates no memory and keeps no global state.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on
+ *    it and the call returns without synchronising the host, so a whole
+ *    forward pass can be captured into a hipGraph.
+ *  - Arguments are validated on the host before anything is enqueued; on any
+ *    error nothing is enqueued and a non-zero moe_status is returned. Device
+ *    faults surface at the caller's next synchronisation.
+ *  - Supported range: 1 <= k <= 8, k <= E <= 256, H and I multiples of 64,
+ *    T >= 0 (T == 0 is a successful no-op), T*k < 2^31. Outside it the call
+ *    returns MOE_ERR_UNSUPPORTED.
+ *  - Dtype combinations: x fp32 with fp32 expert weights (logits fp32), or
+ *    x bf16 with bf16, FP8-E4M3 or NVFP4 expert weights. The router weights
+ *    are always fp32.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1, /* null required pointer, negative size, k > E, bad dtype */
+  MOE_ERR_UNSUPPORTED = 2,      /* valid but outside the supported range or combination */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_LAUNCH = 4 /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum moe_dtype {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_FP8_E4M3 = 2, /* OCP E4M3 (bias 7, no infinities, max 448) */
+  MOE_FP4_E2M1 = 3  /* NVFP4: E2M1 codes, E4M3 scale per 16 K elements, fp32 scale per expert */
+} moe_dtype;
+
+/* Expert weights of one layer (device pointers).
+ *  MOE_F32 / MOE_BF16: gate_up [E, H, 2I], down [E, I, H] (N contiguous);
+ *      scales NULL.
+ *  MOE_FP8_E4M3: gate_up [E, 2I, H] and down [E, H, I] E4M3 codes (K
+ *      contiguous); gate_up_scale f32 [E, 2I], down_scale f32 [E, H] (one per
+ *      output channel); gscales NULL. W = e4m3(q) * scale.
+ *  MOE_FP4_E2M1: gate_up [E, 2I, H/2] and down [E, H, I/2] bytes of two E2M1
+ *      codes (element 2j in the low nibble, K contiguous); gate_up_scale
+ *      [E, 2I, H/16] and down_scale [E, H, I/16] E4M3 block scales;
+ *      gate_up_gscale, down_gscale f32 [E]. W = e2m1(q) * e4m3(s_blk) * s_glob.
+ * Quantised weights are dequantised exactly; activations stay bf16. */
+typedef struct moe_expert_weights {
+  int32_t dtype; /* moe_dtype */
+  int32_t reserved;
+  const void* gate_up;
+  const void* down;
+  const void* gate_up_scale;
+  const void* down_scale;
+  const float* gate_up_gscale;
+  const float* down_gscale;
+} moe_expert_weights;
+
+/* Human-readable name of a status code (static storage). */
+const char* moe_status_string(int32_t status);
+
+/* ------------------------------------------------------------ router
+ * Router GEMM and top-k (steps 1 and 2 of the layer).
+ * logit[t, e] = bias[e] + sum_h x[t, h] * w_router[h, e], accumulated in fp32
+ * and emitted as logits_dtype (bf16: round to nearest even; fp32 allowed only
+ * with fp32 x). Selection works on the emitted logits: p = softmax over all E,
+ * ids = the k largest (ties to the lowest id), ordered by (logit desc, id asc),
+ * topk_w[t, j] = p[ids[t, j]] / sum_j' p[ids[t, j']].
+ *   x          [T, H]  x_dtype (MOE_BF16 or MOE_F32)
+ *   w_router   [H, E]  f32
+ *   bias       [E]     f32, or NULL for none
+ *   logits     [T, E]  logits_dtype, or NULL (then workspace holds them)
+ *   logits_f32 [T, E]  f32 pre-rounding logits, or NULL
+ *   topk_ids   [T, k]  int32;  topk_w [T, k] f32
+ *   workspace          device scratch of moe_route_workspace_size() bytes */
+size_t moe_route_workspace_size(int64_t T, int32_t H, int32_t E);
+moe_status moe_route(const void* x, int32_t x_dtype, int64_t T, int32_t H, const float* w_router,
+                     const float* bias, int32_t E, int32_t k, int32_t logits_dtype, void* logits,
+                     float* logits_f32, int32_t* topk_ids, float* topk_w, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------ permute
+ * Token permute by expert (step 3): a stable counting sort of the pairs
+ * p = t*k + j by expert id topk_ids[p]. counts[e] = number of pairs routed to
+ * e; offsets = exclusive prefix sum of counts (E + 1 entries, offsets[E] =
+ * T*k); sorted_pair[r] = the r-th pair in (expert, p) order; pair_pos is its
+ * inverse (pair_pos[sorted_pair[r]] = r). Results are deterministic.
+ * Ids outside [0, E) are not counted and not written (the outputs are then
+ * incomplete; the router never produces them). */
+size_t moe_permute_workspace_size(int64_t T, int32_t k, int32_t E);
+moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------ experts
+ * Grouped SwiGLU expert GEMMs (step 4). For each expert e and each sorted row
+ * r in [offsets[e], offsets[e+1]), with token t = sorted_pair[r] / k:
+ *   a = x[t] . gate_up[e]  (length 2I, fp32 accumulate)
+ *   h = silu(a[0:I]) * a[I:2I]   (rounded to bf16 for bf16 x; fp32 for fp32 x)
+ *   y_sorted[r] = h . down[e]    (length H, fp32)
+ * offsets and sorted_pair are moe_permute's outputs. */
+size_t moe_experts_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                  const moe_expert_weights* w);
+moe_status moe_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I, int32_t E,
+                       int32_t k, const int32_t* offsets, const int32_t* sorted_pair,
+                       const moe_expert_weights* w, float* y_sorted, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------ finalize
+ * MoE finalize (step 5), the weighted un-permute:
+ *   out[t] = sum_{j=0..k-1} topk_w[t, j] * y_sorted[pair_pos[t*k + j]]
+ * accumulated in fp32 in slot order j = 0..k-1, emitted as out_dtype (bf16:
+ * round to nearest even). out_f32 [T, H] (nullable) receives the fp32 sums. */
+moe_status moe_finalize(const float* y_sorted, const int32_t* pair_pos, const float* topk_w,
+                        int64_t T, int32_t k, int32_t H, int32_t out_dtype, void* out,
+                        float* out_f32, void* stream);
+
+/* ------------------------------------------------------------ whole layer
+ * The five steps in order on one stream: route, permute, experts, finalize.
+ * out [T, H] out_dtype; out_f32, logits, topk_ids, topk_w are optional
+ * (NULL: kept in the workspace). logits_dtype as for moe_route. */
+size_t moe_forward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                  const moe_expert_weights* w);
+moe_status moe_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I, int32_t E,
+                       int32_t k, const float* w_router, const float* bias,
+                       const moe_expert_weights* w, int32_t out_dtype, void* out, float* out_f32,
+                       int32_t logits_dtype, void* logits, int32_t* topk_ids, float* topk_w,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

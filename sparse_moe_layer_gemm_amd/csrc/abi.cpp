@@ -1,0 +1,333 @@
+// C ABI of the routed MoE layer (include/moe.h): argument validation on the
+// host, workspace carving and kernel dispatch on the caller's stream. Nothing
+// is enqueued unless every check passes; nothing here synchronises the host.
+#include "moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "moe_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxPairs = (int64_t(1) << 31) - 1;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool ok_or_null(const void* p) { return p == nullptr || aligned16(p); }
+
+struct Carver {
+  char* base;
+  size_t cap;
+  size_t off = 0;
+  void* take(size_t bytes) {
+    void* p = base + off;
+    off += align_up(bytes);
+    return p;
+  }
+};
+
+moe_status launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+// -------------------------------------------------------------- shared checks
+// Sizes common to every call. T == 0 is valid (no-op).
+moe_status check_shape(int64_t T, int32_t H, int32_t E, int32_t k) {
+  if (T < 0 || H <= 0 || E <= 0 || k <= 0 || k > E) return MOE_ERR_INVALID_ARGUMENT;
+  if (k > 8 || E > 256 || H % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (T * k > kMaxPairs) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Router split plan: enough K slices that small batches still spread the
+// fp32 router weights over many workgroups; slices are multiples of 32.
+void router_plan(int64_t T, int32_t H, int* n_split, int* split_len) {
+  const int64_t row_tiles = (T + 63) / 64;
+  int64_t s = (256 + row_tiles - 1) / row_tiles;
+  if (s < 1) s = 1;
+  if (s > 16) s = 16;
+  const int chunks = H / 32;
+  if (s > chunks) s = chunks;
+  const int per = (int)((chunks + s - 1) / s);
+  *split_len = per * 32;
+  *n_split = (chunks + per - 1) / per;
+}
+
+size_t route_ws_bytes(int64_t T, int32_t H, int32_t E) {
+  int S, L;
+  router_plan(T, H, &S, &L);
+  return align_up((size_t)S * T * E * sizeof(float)) + align_up((size_t)T * E * sizeof(float));
+}
+
+moe_status check_weights(const moe_expert_weights* w, int32_t x_dtype, int32_t H, int32_t I) {
+  if (!w) return MOE_ERR_INVALID_ARGUMENT;
+  if (!w->gate_up || !w->down) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(w->gate_up) || !aligned16(w->down)) return MOE_ERR_INVALID_ARGUMENT;
+  if (I <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (I % 64 != 0 || H % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  switch (w->dtype) {
+    case MOE_F32:
+      if (x_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+      return MOE_OK;
+    case MOE_BF16:
+      if (x_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+      return MOE_OK;
+    case MOE_FP8_E4M3:
+      if (x_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+      if (!w->gate_up_scale || !w->down_scale) return MOE_ERR_INVALID_ARGUMENT;
+      if (!aligned16(w->gate_up_scale) || !aligned16(w->down_scale)) return MOE_ERR_INVALID_ARGUMENT;
+      return MOE_OK;
+    case MOE_FP4_E2M1:
+      if (x_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+      if (!w->gate_up_scale || !w->down_scale || !w->gate_up_gscale || !w->down_gscale)
+        return MOE_ERR_INVALID_ARGUMENT;
+      if (!aligned16(w->gate_up_scale) || !aligned16(w->down_scale) ||
+          !aligned16(w->gate_up_gscale) || !aligned16(w->down_gscale))
+        return MOE_ERR_INVALID_ARGUMENT;
+      return MOE_OK;
+    default:
+      return MOE_ERR_INVALID_ARGUMENT;
+  }
+}
+
+size_t experts_ws_bytes(int64_t T, int32_t I, int32_t k, int32_t w_dtype) {
+  const size_t P = (size_t)T * k;
+  const size_t h_elem = w_dtype == MOE_F32 ? sizeof(float) : sizeof(uint16_t);
+  return align_up(P * I * h_elem);
+}
+
+// -------------------------------------------------------------- enqueue helpers
+// (arguments already validated, T > 0)
+moe_status enqueue_route(const void* x, int32_t x_dtype, int64_t T, int32_t H, const float* wr,
+                         const float* bias, int32_t E, int32_t k, int32_t logits_dtype,
+                         void* logits, float* logits_f32, int32_t* ids, float* w, void* ws,
+                         hipStream_t st) {
+  int S, L;
+  router_plan(T, H, &S, &L);
+  Carver c{static_cast<char*>(ws), 0};
+  float* part = static_cast<float*>(c.take((size_t)S * T * E * sizeof(float)));
+  void* lbuf = c.take((size_t)T * E * sizeof(float));
+  if (!logits) logits = lbuf;
+  hipError_t e = moe::launch_router_gemm(x, x_dtype == MOE_BF16, (int)T, H, wr, E, S, L, part, st);
+  if (e != hipSuccess) return MOE_ERR_LAUNCH;
+  e = moe::launch_router_select(part, S, (int)T, E, k, bias, logits_dtype == MOE_BF16, logits,
+                                logits_f32, ids, w, st);
+  return launch_status(e);
+}
+
+moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I,
+                           int32_t E, int32_t k, const int32_t* offsets,
+                           const int32_t* sorted_pair, const moe_expert_weights* w,
+                           float* y_sorted, void* ws, hipStream_t st) {
+  const int P = (int)(T * k);
+  if (w->dtype == MOE_F32) {
+    return launch_status(moe::launch_expert_f32(
+        static_cast<const float*>(x), (int)T, H, I, E, k, P, offsets, sorted_pair,
+        static_cast<const float*>(w->gate_up), static_cast<const float*>(w->down),
+        static_cast<float*>(ws), y_sorted, st));
+  }
+  (void)x_dtype;
+  const int wf = w->dtype == MOE_BF16 ? moe::W_BF16 : w->dtype == MOE_FP8_E4M3 ? moe::W_FP8 : moe::W_FP4;
+  uint16_t* h = static_cast<uint16_t*>(ws);
+  moe::StreamGemmArgs a{};
+  a.offsets = offsets;
+  a.sorted_pair = sorted_pair;
+  a.k = k;
+  a.E = E;
+  a.I = I;
+  // gate/up: [T, H] x [H, 2I] -> h [P, I]
+  a.a = static_cast<const uint16_t*>(x);
+  a.K = H;
+  a.N = 2 * I;
+  a.w = w->gate_up;
+  a.w_scale = w->gate_up_scale;
+  a.w_gscale = w->gate_up_gscale;
+  a.h_out = h;
+  a.y_out = nullptr;
+  hipError_t e = moe::launch_expert_stream(wf, true, a, st);
+  if (e != hipSuccess) return MOE_ERR_LAUNCH;
+  // down: [P, I] x [I, H] -> y_sorted [P, H]
+  a.a = h;
+  a.K = I;
+  a.N = H;
+  a.w = w->down;
+  a.w_scale = w->down_scale;
+  a.w_gscale = w->down_gscale;
+  a.h_out = nullptr;
+  a.y_out = y_sorted;
+  return launch_status(moe::launch_expert_stream(wf, false, a, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int32_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_LAUNCH: return "MOE_ERR_LAUNCH";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+// ---------------------------------------------------------------- route
+size_t moe_route_workspace_size(int64_t T, int32_t H, int32_t E) {
+  if (T <= 0 || H <= 0 || E <= 0 || H % 64 != 0) return 0;
+  return route_ws_bytes(T, H, E);
+}
+
+moe_status moe_route(const void* x, int32_t x_dtype, int64_t T, int32_t H, const float* w_router,
+                     const float* bias, int32_t E, int32_t k, int32_t logits_dtype, void* logits,
+                     float* logits_f32, int32_t* topk_ids, float* topk_w, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  moe_status s = check_shape(T, H, E, k);
+  if (s != MOE_OK) return s;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  if (logits_dtype != MOE_F32 && logits_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  if (logits_dtype == MOE_F32 && x_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !topk_ids || !topk_w || !workspace) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(w_router) || !ok_or_null(bias) || !ok_or_null(logits) ||
+      !ok_or_null(logits_f32) || !aligned16(topk_ids) || !aligned16(topk_w) ||
+      !aligned16(workspace))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < route_ws_bytes(T, H, E)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return enqueue_route(x, x_dtype, T, H, w_router, bias, E, k, logits_dtype, logits, logits_f32,
+                       topk_ids, topk_w, workspace, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------- permute
+size_t moe_permute_workspace_size(int64_t T, int32_t k, int32_t E) {
+  (void)T;
+  (void)k;
+  (void)E;
+  return 0;
+}
+
+moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (T < 0 || E <= 0 || k <= 0 || k > E) return MOE_ERR_INVALID_ARGUMENT;
+  if (k > 8 || E > 256) return MOE_ERR_UNSUPPORTED;
+  if (T * k > kMaxPairs) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!topk_ids || !counts || !offsets || !sorted_pair || !pair_pos) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(topk_ids) || !aligned16(counts) || !aligned16(offsets) ||
+      !aligned16(sorted_pair) || !aligned16(pair_pos))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return launch_status(moe::launch_permute(topk_ids, (int)(T * k), E, counts, offsets, sorted_pair,
+                                           pair_pos, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- experts
+size_t moe_experts_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                  const moe_expert_weights* w) {
+  if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || !w) return 0;
+  return experts_ws_bytes(T, I, k, w->dtype);
+}
+
+moe_status moe_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I, int32_t E,
+                       int32_t k, const int32_t* offsets, const int32_t* sorted_pair,
+                       const moe_expert_weights* w, float* y_sorted, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  moe_status s = check_shape(T, H, E, k);
+  if (s != MOE_OK) return s;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  s = check_weights(w, x_dtype, H, I);
+  if (s != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  if (!x || !offsets || !sorted_pair || !y_sorted || !workspace) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(offsets) || !aligned16(sorted_pair) || !aligned16(y_sorted) ||
+      !aligned16(workspace))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < experts_ws_bytes(T, I, k, w->dtype)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return enqueue_experts(x, x_dtype, T, H, I, E, k, offsets, sorted_pair, w, y_sorted, workspace,
+                         static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------- finalize
+moe_status moe_finalize(const float* y_sorted, const int32_t* pair_pos, const float* topk_w,
+                        int64_t T, int32_t k, int32_t H, int32_t out_dtype, void* out,
+                        float* out_f32, void* stream) {
+  if (T < 0 || k <= 0 || H <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  if (k > 8 || H % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (T * k > kMaxPairs) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!y_sorted || !pair_pos || !topk_w || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(y_sorted) || !aligned16(pair_pos) || !aligned16(topk_w) || !aligned16(out) ||
+      !ok_or_null(out_f32))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return launch_status(moe::launch_finalize(y_sorted, pair_pos, topk_w, (int)T, k, H,
+                                            out_dtype == MOE_BF16, out, out_f32,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- forward
+size_t moe_forward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                  const moe_expert_weights* w) {
+  if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || !w || H % 64 != 0) return 0;
+  const size_t P = (size_t)T * k;
+  return route_ws_bytes(T, H, E) + align_up((size_t)T * E * sizeof(float)) +
+         2 * align_up(P * sizeof(int32_t)) /* ids, w */ + align_up(E * sizeof(int32_t)) +
+         align_up((E + 1) * sizeof(int32_t)) + 2 * align_up(P * sizeof(int32_t)) +
+         align_up(P * H * sizeof(float)) + experts_ws_bytes(T, I, k, w->dtype);
+}
+
+moe_status moe_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I, int32_t E,
+                       int32_t k, const float* w_router, const float* bias,
+                       const moe_expert_weights* w, int32_t out_dtype, void* out, float* out_f32,
+                       int32_t logits_dtype, void* logits, int32_t* topk_ids, float* topk_w,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status s = check_shape(T, H, E, k);
+  if (s != MOE_OK) return s;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  if (logits_dtype != MOE_F32 && logits_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  if (logits_dtype == MOE_F32 && x_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  s = check_weights(w, x_dtype, H, I);
+  if (s != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !out || !workspace) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(w_router) || !ok_or_null(bias) || !aligned16(out) ||
+      !ok_or_null(out_f32) || !ok_or_null(logits) || !ok_or_null(topk_ids) ||
+      !ok_or_null(topk_w) || !aligned16(workspace))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < moe_forward_workspace_size(T, H, I, E, k, w))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t P = (size_t)T * k;
+  Carver c{static_cast<char*>(workspace), workspace_bytes};
+  void* route_ws = c.take(route_ws_bytes(T, H, E));
+  void* lbuf = c.take((size_t)T * E * sizeof(float));
+  int32_t* ids = static_cast<int32_t*>(c.take(P * sizeof(int32_t)));
+  float* tw = static_cast<float*>(c.take(P * sizeof(float)));
+  int32_t* counts = static_cast<int32_t*>(c.take(E * sizeof(int32_t)));
+  int32_t* offsets = static_cast<int32_t*>(c.take((E + 1) * sizeof(int32_t)));
+  int32_t* sorted_pair = static_cast<int32_t*>(c.take(P * sizeof(int32_t)));
+  int32_t* pair_pos = static_cast<int32_t*>(c.take(P * sizeof(int32_t)));
+  float* y_sorted = static_cast<float*>(c.take(P * H * sizeof(float)));
+  void* exp_ws = c.take(experts_ws_bytes(T, I, k, w->dtype));
+  if (topk_ids) ids = topk_ids;
+  if (topk_w) tw = topk_w;
+  if (!logits) logits = lbuf;
+
+  s = enqueue_route(x, x_dtype, T, H, w_router, bias, E, k, logits_dtype, logits, nullptr, ids, tw,
+                    route_ws, st);
+  if (s != MOE_OK) return s;
+  s = launch_status(moe::launch_permute(ids, (int)P, E, counts, offsets, sorted_pair, pair_pos, st));
+  if (s != MOE_OK) return s;
+  s = enqueue_experts(x, x_dtype, T, H, I, E, k, offsets, sorted_pair, w, y_sorted, exp_ws, st);
+  if (s != MOE_OK) return s;
+  return launch_status(moe::launch_finalize(y_sorted, pair_pos, tw, (int)T, k, H,
+                                            out_dtype == MOE_BF16, out, out_f32, st));
+}
+
+}  // extern "C"

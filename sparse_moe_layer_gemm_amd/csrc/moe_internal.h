@@ -1,0 +1,75 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------- vector types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- device helpers
+// bf16 <-> fp32 (round to nearest, ties to even; inputs are finite)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Order-preserving map of a float onto uint32 (larger float -> larger integer).
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float float_from_order_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ---------------------------------------------------------------- launchers
+// Router GEMM partial sums: part[s][t][e] = sum over K-slice s of x[t,h] w[h,e].
+hipError_t launch_router_gemm(const void* x, bool x_bf16, int T, int H, const float* w_router,
+                              int E, int n_split, int split_len, float* part, hipStream_t st);
+// Sum of partials + bias -> logits (bf16 or fp32), softmax, top-k, renormalised weights.
+hipError_t launch_router_select(const float* part, int n_split, int T, int E, int k,
+                                const float* bias, bool logits_bf16, void* logits,
+                                float* logits_f32, int32_t* ids, float* w, hipStream_t st);
+// Stable counting sort of pairs by expert.
+hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_pair, int32_t* pair_pos, hipStream_t st);
+
+enum WFormat { W_BF16 = 1, W_FP8 = 2, W_FP4 = 3 };
+
+struct StreamGemmArgs {
+  const uint16_t* a;       // gate/up: x [T, K] bf16; down: h [P, K] bf16
+  const int32_t* offsets;  // [E + 1]
+  const int32_t* sorted_pair;
+  int k;                   // experts per token (gather divisor)
+  int E, K, N, I;          // N = output columns of the matrix (2I or H)
+  const void* w;           // expert weights of this matrix
+  const void* w_scale;     // FP8: f32 [E, N]; FP4: e4m3 [E, N, K/16]
+  const float* w_gscale;   // FP4: f32 [E]
+  uint16_t* h_out;         // gate/up output [P, I] bf16
+  float* y_out;            // down output [P, N] f32
+};
+// Grouped expert GEMM for small row counts per expert: each wavefront owns a
+// 128-column slice of one expert's matrix and streams it once per 32 rows.
+hipError_t launch_expert_stream(int wfmt, bool gate_up, const StreamGemmArgs& a, hipStream_t st);
+
+// fp32 expert path (reference-precision layer; one thread per output element).
+hipError_t launch_expert_f32(const float* x, int T, int H, int I, int E, int k, int P,
+                             const int32_t* offsets, const int32_t* sorted_pair,
+                             const float* gate_up, const float* down, float* h, float* y,
+                             hipStream_t st);
+
+// Weighted un-permute.
+hipError_t launch_finalize(const float* y_sorted, const int32_t* pair_pos, const float* w, int T,
+                           int k, int H, bool out_bf16, void* out, float* out_f32,
+                           hipStream_t st);
+
+}  // namespace moe

@@ -126,15 +126,45 @@ def _round_to_grid(mag: np.ndarray, grid: np.ndarray) -> np.ndarray:
     return np.where(pick_hi, hi, lo)
 
 
-def encode_e4m3(v: np.ndarray) -> np.ndarray:
+def encode_e4m3_table(v: np.ndarray) -> np.ndarray:
+    """Reference encoder: nearest value of the positive E4M3 table, ties to even."""
     v = np.asarray(v, dtype=np.float64)
     idx = _round_to_grid(np.abs(v), _E4M3_POS)
     return (idx | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
 
 
-def encode_e2m1(v: np.ndarray) -> np.ndarray:
+def encode_e2m1_table(v: np.ndarray) -> np.ndarray:
     v = np.asarray(v, dtype=np.float64)
     idx = _round_to_grid(np.abs(v), _E2M1_POS)
+    return (idx | np.where(np.signbit(v), 0x8, 0)).astype(np.uint8)
+
+
+def encode_e4m3(v: np.ndarray) -> np.ndarray:
+    """fp32 values -> E4M3 codes, nearest with ties to even, saturating at 448.
+
+    Normal range: round the fp32 mantissa to 3 bits on the bit pattern;
+    below 2^-6: multiples of the subnormal quantum 2^-9 (np.rint is RNE).
+    """
+    v = np.asarray(v, dtype=np.float32)
+    mag = np.minimum(np.abs(v), np.float32(448.0))
+    u = mag.view(np.uint32)
+    r = (u + np.uint32((1 << 19) - 1) + ((u >> np.uint32(20)) & np.uint32(1))) >> np.uint32(20)
+    exp = (r >> np.uint32(3)).astype(np.int32) - 127 + 7
+    normal = ((exp << 3) | (r & np.uint32(7)).astype(np.int32))
+    sub = np.rint(mag * np.float32(512.0)).astype(np.int32)
+    code = np.where(mag < np.float32(2.0 ** -6), sub, normal)
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def encode_e2m1(v: np.ndarray) -> np.ndarray:
+    """fp32 values -> E2M1 codes, nearest with ties to even (saturating at 6).
+
+    The grid is 0, .5, 1, 1.5, 2, 3, 4, 6; each midpoint goes to the even index.
+    """
+    v = np.asarray(v, dtype=np.float32)
+    m = np.abs(v)
+    idx = ((m > 0.25).astype(np.uint8) + (m >= 0.75) + (m > 1.25) + (m >= 1.75) + (m > 2.5)
+           + (m >= 3.5) + (m > 5.0))
     return (idx | np.where(np.signbit(v), 0x8, 0)).astype(np.uint8)
 
 
@@ -152,26 +182,25 @@ def quantize_nvfp4(w_nk: np.ndarray):
     Returns (packed [N, K/2] u8, block scales [N, K/16] u8 (E4M3), s_g float32).
     """
     N, K = w_nk.shape
-    w = w_nk.astype(np.float64)
-    amax = float(np.max(np.abs(w)))
-    s_g = np.float32(amax / (448.0 * 6.0)) if amax > 0 else np.float32(1.0)
-    blk = w.reshape(N, K // 16, 16)
+    blk = np.asarray(w_nk, dtype=np.float32).reshape(N, K // 16, 16)
     amax_b = np.max(np.abs(blk), axis=2)
-    sb_codes = encode_e4m3(amax_b / (6.0 * float(s_g)))
-    sb_val = _E4M3_POS[sb_codes & 0x7F]
-    denom = (sb_val * float(s_g))[:, :, None]
-    with np.errstate(divide="ignore", invalid="ignore"):
-        scaled = np.where(denom > 0, blk / np.where(denom > 0, denom, 1.0), 0.0)
+    amax = float(amax_b.max())
+    s_g = np.float32(amax / (448.0 * 6.0)) if amax > 0 else np.float32(1.0)
+    sb_codes = encode_e4m3(amax_b / (np.float32(6.0) * s_g))
+    sb_val = _E4M3_POS[sb_codes & 0x7F].astype(np.float32)
+    denom = (sb_val * s_g)[:, :, None]
+    safe = np.where(denom > 0, denom, np.float32(1.0))
+    scaled = np.where(denom > 0, blk / safe, np.float32(0.0))
     q = encode_e2m1(scaled).reshape(N, K)
     return pack_nibbles(q), sb_codes, s_g
 
 
 def quantize_fp8_channel(w_nk: np.ndarray):
     """FP8 E4M3 with one fp32 scale per output channel: s = amax_row / 448."""
-    w = w_nk.astype(np.float64)
+    w = np.asarray(w_nk, dtype=np.float32)
     amax = np.max(np.abs(w), axis=1)
-    s = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
-    q = encode_e4m3(w / s.astype(np.float64)[:, None])
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    q = encode_e4m3(w / s[:, None])
     return q, s
 
 

@@ -1,0 +1,273 @@
+"""Shared helpers of the GPU parity tests: upload seeded inputs, run the layer
+through the C ABI stage by stage, and compare with the oracle.
+
+Tolerances (fixed by the layer's statement of parity, readings in the tests):
+  - router logits: max_e |l_gpu - l_ref| <= 1e-5 * scale per token, scale = the
+    row's max |l_ref| (no less than the RMS of the batch's logits);
+  - expert ids: bit-exact, except tokens whose ranking a 1e-5 relative change
+    of the logits could alter (counted and reported);
+  - outputs: max |out_gpu - out_ref| / rms(out_ref) <= 2e-2 (bf16 experts),
+    3e-2 (FP8), 6e-2 (NVFP4), 1e-4 (all-fp32 layer).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import sparse_moe_layer_gemm_amd as moe
+import synth
+
+DEV = "cuda"
+TOL_OUT = {"bf16": 2e-2, "fp8": 3e-2, "fp4": 6e-2, "f32": 1e-4}
+LOGIT_REL = 1e-5
+
+_weight_cache: dict = {}
+
+
+def log(msg: str):
+    print(msg, flush=True)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 device tensor -> uint16 bit patterns on the host."""
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host_experts(cfg: synth.MoEConfig) -> dict:
+    key = (cfg.weight_seed if cfg.weight_seed is not None else cfg.seed, cfg.w_dtype, cfg.E, cfg.H, cfg.I)
+    if key not in _weight_cache:
+        _weight_cache.clear()  # keep one layer's weights at a time
+        hostw = synth.gen_experts(cfg)
+        _weight_cache[key] = (hostw, moe.experts_to_device(hostw, DEV))
+    return _weight_cache[key]
+
+
+class Layer:
+    """Seeded inputs of one configuration, on the host and on the device."""
+
+    def __init__(self, cfg: synth.MoEConfig, x: np.ndarray | None = None):
+        self.cfg = cfg
+        self.x = synth.gen_x(cfg) if x is None else x
+        self.wr, self.bias = synth.gen_router(cfg)
+        if cfg.x_dtype == "f32":
+            self.dx = torch.from_numpy(self.x).to(DEV)
+        else:
+            self.dx = moe.to_device_bf16(self.x, DEV)
+        self.dwr = torch.from_numpy(self.wr).to(DEV)
+        self.dbias = None if self.bias is None else torch.from_numpy(self.bias).to(DEV)
+        if not cfg.router_only:
+            self.hw, self.dw = host_experts(cfg)
+
+    @property
+    def ldt(self):
+        return moe.MOE_F32 if self.cfg.x_dtype == "f32" else moe.MOE_BF16
+
+    def route(self):
+        c = self.cfg
+        T, E, k = c.T, c.E, c.k
+        tdt = torch.float32 if c.x_dtype == "f32" else torch.bfloat16
+        r = {"logits": torch.empty((T, E), dtype=tdt, device=DEV),
+             "logits_f32": torch.empty((T, E), dtype=torch.float32, device=DEV),
+             "ids": torch.empty((T, k), dtype=torch.int32, device=DEV),
+             "w": torch.empty((T, k), dtype=torch.float32, device=DEV)}
+        ws = moe.workspace(moe.moe_route_workspace_size(T, c.H, E))
+        moe.moe_route(self.dx, self.dwr, self.dbias, k, self.ldt, r["logits"], r["logits_f32"],
+                      r["ids"], r["w"], ws)
+        return r
+
+    def stages(self):
+        """route -> permute -> experts -> finalize, each through its own entry point."""
+        c = self.cfg
+        T, H, E, k, I = c.T, c.H, c.E, c.k, c.I
+        r = self.route()
+        P = T * k
+        r["counts"] = torch.empty(E, dtype=torch.int32, device=DEV)
+        r["offsets"] = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+        r["sorted_pair"] = torch.empty(P, dtype=torch.int32, device=DEV)
+        r["pair_pos"] = torch.empty(P, dtype=torch.int32, device=DEV)
+        moe.moe_permute(r["ids"], E, r["counts"], r["offsets"], r["sorted_pair"], r["pair_pos"])
+        r["y"] = torch.empty((P, H), dtype=torch.float32, device=DEV)
+        ws = moe.workspace(moe.moe_experts_workspace_size(T, H, I, E, k, self.dw))
+        moe.moe_experts(self.dx, I, E, k, r["offsets"], r["sorted_pair"], self.dw, r["y"], ws)
+        r["out"] = torch.empty((T, H), dtype=self.dx.dtype, device=DEV)
+        r["out_f32"] = torch.empty((T, H), dtype=torch.float32, device=DEV)
+        moe.moe_finalize(r["y"], r["pair_pos"], r["w"], r["out"], r["out_f32"])
+        torch.cuda.synchronize()
+        return r
+
+    def forward(self):
+        c = self.cfg
+        T, H, E, k, I = c.T, c.H, c.E, c.k, c.I
+        f = {"out": torch.empty((T, H), dtype=self.dx.dtype, device=DEV),
+             "out_f32": torch.empty((T, H), dtype=torch.float32, device=DEV),
+             "ids": torch.empty((T, k), dtype=torch.int32, device=DEV),
+             "w": torch.empty((T, k), dtype=torch.float32, device=DEV)}
+        ws = moe.workspace(moe.moe_forward_workspace_size(T, H, I, E, k, self.dw))
+        moe.moe_forward(self.dx, self.dwr, self.dbias, self.dw, I, k, f["out"], ws,
+                        out_f32=f["out_f32"], topk_ids=f["ids"], topk_w=f["w"])
+        torch.cuda.synchronize()
+        return f
+
+
+# ------------------------------------------------------------------ comparisons
+def round_sel(values: np.ndarray, sel: str) -> np.ndarray:
+    if sel == "bf16":
+        return oracle.format_op("round_bf16", values)
+    return values.astype(np.float32).astype(np.float64)
+
+
+def logit_scale(lref: np.ndarray) -> np.ndarray:
+    """Per-token scale of the 1e-5 logit tolerance: the row's largest |logit|, but no
+    less than the RMS of all logits of the batch (a row of one or two experts can
+    cancel to a tiny logit whose fp32 rounding error is set by its terms, not by it)."""
+    rms = float(np.sqrt(np.mean(lref ** 2))) if lref.size else 0.0
+    return np.maximum(np.abs(lref).max(axis=1), rms)
+
+
+def ambiguous_tokens(lref: np.ndarray, k: int, sel: str, rel: float = LOGIT_REL) -> np.ndarray:
+    """Tokens whose top-k set or order a relative logit change of `rel` could alter.
+
+    (i) the exact gap between the k-th and (k+1)-th logit is below rel, or
+    (ii) with d = rel * (the token's logit scale), some adjacent pair (a before b) among the first
+    k + 1 in selection order has (round(l_a - d), -a) <= (round(l_b + d), -b).
+    """
+    n, E = lref.shape
+    ids = np.broadcast_to(np.arange(E), (n, E))
+    v = round_sel(lref, sel)
+    order = np.lexsort((ids, -v), axis=-1)
+    d = rel * logit_scale(lref)[:, None]
+    lo = round_sel(lref - d, sel)
+    hi = round_sel(lref + d, sel)
+    amb = np.zeros(n, dtype=bool)
+    ex = np.sort(lref, axis=1)[:, ::-1]
+    if k < E:
+        amb |= (ex[:, k - 1] - ex[:, k]) < rel
+    m = min(k + 1, E)
+    rows = np.arange(n)
+    for i in range(m - 1):
+        a, b = order[:, i], order[:, i + 1]
+        la, hb = lo[rows, a], hi[rows, b]
+        amb |= (la < hb) | ((la == hb) & (a > b))
+    return amb
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    rms = float(np.sqrt(np.mean(ref.astype(np.float64) ** 2)))
+    return float(np.max(np.abs(got.astype(np.float64) - ref))) / max(rms, 1e-30)
+
+
+def check_router(layer: Layer, r: dict, rows=None) -> dict:
+    """Logits vs the exact oracle logits; selection vs oracle on the GPU's own logits."""
+    c = layer.cfg
+    sel = c.logits_dtype
+    lref = oracle.logits(layer.x, layer.wr, layer.bias, rows=rows)
+    lf = r["logits_f32"].cpu().numpy().astype(np.float64)
+    if rows is not None:
+        lf = lf[rows]
+    scale = logit_scale(lref)
+    worst = float(np.max(np.abs(lf - lref).max(axis=1) / scale))
+    assert worst <= LOGIT_REL, f"logits rel err {worst}"
+    # emitted logits are the rounding of the fp32 sums
+    if sel == "bf16":
+        lb = oracle.format_op("bf16", bits(r["logits"]).astype(np.float64))
+        if rows is not None:
+            lb = lb[rows]
+        assert np.array_equal(lb, oracle.format_op("round_bf16", lf.astype(np.float32).astype(np.float64)))
+    else:
+        lb = r["logits"].cpu().numpy().astype(np.float64)
+        if rows is not None:
+            lb = lb[rows]
+        assert np.array_equal(lb, lf)
+    # stage-isolated selection: oracle routing on the GPU's own emitted logits, no exceptions
+    ids = r["ids"].cpu().numpy()
+    w = r["w"].cpu().numpy()
+    if rows is not None:
+        ids, w = ids[rows], w[rows]
+    oid, ow = oracle.route(lb, c.k, sel)
+    assert np.array_equal(ids, oid), "selection on the GPU's logits differs from the oracle's"
+    assert np.max(np.abs(w - ow)) <= 2e-6
+    assert np.allclose(w.sum(1), 1.0, atol=1e-5)
+    # end to end: routing of the exact logits, ambiguous tokens excepted
+    rid, _ = oracle.route(lref, c.k, sel)
+    amb = ambiguous_tokens(lref, c.k, sel)
+    mism = np.any(ids != rid, axis=1)
+    assert not np.any(mism & ~amb), f"{int(np.sum(mism & ~amb))} unambiguous tokens routed differently"
+    return {"logit_rel_err": worst, "ambiguous": int(amb.sum()), "ambiguous_mismatched": int(mism.sum()),
+            "tokens": len(ids), "lref": lref, "amb": amb}
+
+
+def check_permute(layer: Layer, r: dict):
+    ids = r["ids"].cpu().numpy()
+    counts, offsets, sp, pp = oracle.permute(ids, layer.cfg.E)
+    assert np.array_equal(r["counts"].cpu().numpy(), counts)
+    assert np.array_equal(r["offsets"].cpu().numpy(), offsets)
+    assert np.array_equal(r["sorted_pair"].cpu().numpy(), sp)
+    assert np.array_equal(r["pair_pos"].cpu().numpy(), pp)
+    return counts
+
+
+def check_experts(layer: Layer, r: dict, rows: np.ndarray) -> float:
+    """Sorted rows y[r] vs the oracle's FFN of (token, expert) of that row."""
+    c = layer.cfg
+    sp = r["sorted_pair"].cpu().numpy()
+    ids = r["ids"].cpu().numpy().ravel()
+    rows = np.asarray(rows, dtype=np.int64)
+    pairs = sp[rows]
+    yref = oracle.expert_rows(layer.x, layer.hw, c.I, pairs // c.k, ids[pairs])
+    idx = torch.from_numpy(rows).to(DEV)
+    y = r["y"].index_select(0, idx).cpu().numpy()
+    err = rel_err(y, yref)
+    assert err <= TOL_OUT[c.w_dtype], f"expert rows rel err {err}"
+    return err
+
+
+def check_finalize(layer: Layer, r: dict, tokens=None) -> float:
+    """Finalize vs the oracle's weighted sum of the GPU's own rows, and bf16 = RNE(fp32)."""
+    c = layer.cfg
+    pp = r["pair_pos"].cpu().numpy()
+    w = r["w"].cpu().numpy()
+    if tokens is None:
+        y = r["y"].cpu().numpy()
+        ref = oracle.finalize(y, pp, w, c.k)
+        got = r["out_f32"].cpu().numpy()
+    else:
+        tokens = np.asarray(tokens, dtype=np.int64)
+        need = np.unique(pp.reshape(c.T, c.k)[tokens].ravel())
+        ysub = r["y"].index_select(0, torch.from_numpy(need).to(DEV)).cpu().numpy()
+        remap = np.full(c.T * c.k, -1, np.int64)
+        remap[need] = np.arange(len(need))
+        pp_sub = remap[pp.reshape(c.T, c.k)[tokens]].astype(np.int32)
+        ref = oracle.finalize(ysub, pp_sub.ravel(), w[tokens], c.k)
+        got = r["out_f32"].cpu().numpy()[tokens]
+    err = rel_err(got, ref)
+    assert err <= 1e-5, f"finalize rel err {err}"
+    outf = r["out_f32"].cpu().numpy()
+    if c.x_dtype == "bf16":
+        want = torch.from_numpy(outf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(bits(r["out"]), want), "bf16 output is not RNE of the fp32 output"
+    else:
+        assert np.array_equal(r["out"].cpu().numpy(), outf)
+    return err
+
+
+def check_layer(layer: Layer, r: dict, tokens, amb_all=None) -> dict:
+    """End to end: GPU fp32 output vs the oracle's layer, unambiguous tokens."""
+    c = layer.cfg
+    tokens = np.asarray(tokens, dtype=np.int64)
+    ref = oracle.layer(layer.x, layer.wr, layer.bias, layer.hw, c.I, c.k, c.logits_dtype, rows=tokens)
+    amb = ambiguous_tokens(ref["logits"], c.k, c.logits_dtype)
+    keep = ~amb
+    outf = r["out_f32"].cpu().numpy()[tokens]
+    err = rel_err(outf[keep], ref["out"][keep]) if keep.any() else 0.0
+    out_bits = bits(r["out"])[tokens] if c.x_dtype == "bf16" else None
+    lit = None
+    if out_bits is not None and keep.any():
+        ob = oracle.format_op("bf16", out_bits.astype(np.float64))
+        lit = rel_err(ob[keep], ref["out"][keep])
+        floor = rel_err(oracle.format_op("round_bf16", ref["out"][keep]), ref["out"][keep])
+    else:
+        floor = None
+    assert err <= TOL_OUT[c.w_dtype], f"layer output rel err {err}"
+    return {"out_rel_err": err, "out_bf16_rel_err": lit, "bf16_floor": floor,
+            "ambiguous": int(amb.sum()), "tokens": len(tokens)}
