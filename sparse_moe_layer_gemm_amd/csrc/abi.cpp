@@ -91,10 +91,16 @@ moe_status check_weights(const moe_expert_weights* w, int32_t x_dtype, int32_t H
   }
 }
 
-size_t experts_ws_bytes(int64_t T, int32_t I, int32_t k, int32_t w_dtype) {
+size_t experts_ws_bytes(int64_t T, int32_t I, int32_t E, int32_t k, int32_t w_dtype) {
   const size_t P = (size_t)T * k;
   const size_t h_elem = w_dtype == MOE_F32 ? sizeof(float) : sizeof(uint16_t);
-  return align_up(P * I * h_elem);
+  return align_up(P * I * h_elem) + align_up(moe::expert_tile_ws_bytes((int)P, E));
+}
+
+// The tiled grouped GEMM pays off once experts average enough rows to fill
+// its 128-row tiles; below that, streaming each weight once per 32 rows wins.
+bool use_tile_kernel(int32_t w_dtype, int64_t P, int32_t E) {
+  return w_dtype == MOE_BF16 && P >= (int64_t)moe::kTileMinRowsPerExpert * E;
 }
 
 // -------------------------------------------------------------- enqueue helpers
@@ -130,6 +136,7 @@ moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H,
   (void)x_dtype;
   const int wf = w->dtype == MOE_BF16 ? moe::W_BF16 : w->dtype == MOE_FP8_E4M3 ? moe::W_FP8 : moe::W_FP4;
   uint16_t* h = static_cast<uint16_t*>(ws);
+  void* tile_ws = static_cast<char*>(ws) + align_up((size_t)P * I * sizeof(uint16_t));
   moe::StreamGemmArgs a{};
   a.offsets = offsets;
   a.sorted_pair = sorted_pair;
@@ -145,18 +152,21 @@ moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H,
   a.w_gscale = w->gate_up_gscale;
   a.h_out = h;
   a.y_out = nullptr;
+  // down: [P, I] x [I, H] -> y_sorted [P, H]
+  moe::StreamGemmArgs d = a;
+  d.a = h;
+  d.K = I;
+  d.N = H;
+  d.w = w->down;
+  d.w_scale = w->down_scale;
+  d.w_gscale = w->down_gscale;
+  d.h_out = nullptr;
+  d.y_out = y_sorted;
+  if (use_tile_kernel(w->dtype, P, E))
+    return launch_status(moe::launch_expert_tile(wf, a, d, P, tile_ws, st));
   hipError_t e = moe::launch_expert_stream(wf, true, a, st);
   if (e != hipSuccess) return MOE_ERR_LAUNCH;
-  // down: [P, I] x [I, H] -> y_sorted [P, H]
-  a.a = h;
-  a.K = I;
-  a.N = H;
-  a.w = w->down;
-  a.w_scale = w->down_scale;
-  a.w_gscale = w->down_gscale;
-  a.h_out = nullptr;
-  a.y_out = y_sorted;
-  return launch_status(moe::launch_expert_stream(wf, false, a, st));
+  return launch_status(moe::launch_expert_stream(wf, false, d, st));
 }
 
 }  // namespace
@@ -229,7 +239,7 @@ moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
 size_t moe_experts_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                                   const moe_expert_weights* w) {
   if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || !w) return 0;
-  return experts_ws_bytes(T, I, k, w->dtype);
+  return experts_ws_bytes(T, I, E, k, w->dtype);
 }
 
 moe_status moe_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I, int32_t E,
@@ -246,7 +256,7 @@ moe_status moe_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
   if (!aligned16(x) || !aligned16(offsets) || !aligned16(sorted_pair) || !aligned16(y_sorted) ||
       !aligned16(workspace))
     return MOE_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < experts_ws_bytes(T, I, k, w->dtype)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace_bytes < experts_ws_bytes(T, I, E, k, w->dtype)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   return enqueue_experts(x, x_dtype, T, H, I, E, k, offsets, sorted_pair, w, y_sorted, workspace,
                          static_cast<hipStream_t>(stream));
 }
@@ -277,7 +287,7 @@ size_t moe_forward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, in
   return route_ws_bytes(T, H, E) + align_up((size_t)T * E * sizeof(float)) +
          2 * align_up(P * sizeof(int32_t)) /* ids, w */ + align_up(E * sizeof(int32_t)) +
          align_up((E + 1) * sizeof(int32_t)) + 2 * align_up(P * sizeof(int32_t)) +
-         align_up(P * H * sizeof(float)) + experts_ws_bytes(T, I, k, w->dtype);
+         align_up(P * H * sizeof(float)) + experts_ws_bytes(T, I, E, k, w->dtype);
 }
 
 moe_status moe_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I, int32_t E,
@@ -314,7 +324,7 @@ moe_status moe_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
   int32_t* sorted_pair = static_cast<int32_t*>(c.take(P * sizeof(int32_t)));
   int32_t* pair_pos = static_cast<int32_t*>(c.take(P * sizeof(int32_t)));
   float* y_sorted = static_cast<float*>(c.take(P * H * sizeof(float)));
-  void* exp_ws = c.take(experts_ws_bytes(T, I, k, w->dtype));
+  void* exp_ws = c.take(experts_ws_bytes(T, I, E, k, w->dtype));
   if (topk_ids) ids = topk_ids;
   if (topk_w) tw = topk_w;
   if (!logits) logits = lbuf;

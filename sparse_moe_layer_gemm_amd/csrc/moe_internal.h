@@ -61,6 +61,15 @@ struct StreamGemmArgs {
 // 128-column slice of one expert's matrix and streams it once per 32 rows.
 hipError_t launch_expert_stream(int wfmt, bool gate_up, const StreamGemmArgs& a, hipStream_t st);
 
+// Grouped expert GEMMs for many rows per expert: 128 x 256 MFMA tiles through
+// double-buffered LDS (bf16 weights). Runs gate/up then down; ws holds the
+// M-tile table (expert_tile_ws_bytes).
+size_t expert_tile_ws_bytes(int P, int E);
+hipError_t launch_expert_tile(int wfmt, const StreamGemmArgs& gate_up, const StreamGemmArgs& down,
+                              int P, void* ws, hipStream_t st);
+// Rows per expert from which the tiled kernel replaces the streaming one.
+constexpr int kTileMinRowsPerExpert = 32;
+
 // fp32 expert path (reference-precision layer; one thread per output element).
 hipError_t launch_expert_f32(const float* x, int T, int H, int I, int E, int k, int P,
                              const int32_t* offsets, const int32_t* sorted_pair,
