@@ -168,35 +168,38 @@ def main():
 
     dec_cfg = synth.CONFIGS["decode_t128"]
     pre_cfg = synth.CONFIGS["prefill_t16384_zipf"]
-    progress("generating decode inputs (T=128, bf16 experts)")
-    dec = Workload(dec_cfg, moe, torch)
-    progress("timing decode")
-    dec_ms = dec.time_forward(a.steps, a.warmup)
-    dec_stage = dec.time_stages(a.steps)
-    counts = dec.touched()
-    n_touched = int((counts > 0).sum())
-    wbytes = n_touched * expert_bytes(dec_cfg)
-    layer_bytes = wbytes + dec_cfg.H * dec_cfg.E * 4 + 2 * dec_cfg.T * dec_cfg.H * 2
-    dec_line = {
-        "value": dec_cfg.T / (dec_ms / 1e3),
-        "ms_per_step": dec_ms,
-        "stages_ms": dec_stage,
-        "touched_experts": n_touched,
-        "layer_hbm_frac": layer_bytes / (dec_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-        "roofline": {"bound": "hbm", "kernel": "moe_experts (gate/up + down stream GEMMs)",
-                     "achieved": wbytes / (dec_stage["experts"] / 1e3) / 1e9,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None},
-    }
-    dec_line["roofline"]["frac"] = dec_line["roofline"]["achieved"] / HBM_PEAK_GBS
+    dec_line = pre_line = dec = pre = None
+    if a.workload == "decode":
+        progress("generating decode inputs (T=128, bf16 experts)")
+        dec = Workload(dec_cfg, moe, torch)
+        progress("timing decode")
+        dec_ms = dec.time_forward(a.steps, a.warmup)
+        dec_stage = dec.time_stages(a.steps)
+        counts = dec.touched()
+        n_touched = int((counts > 0).sum())
+        wbytes = n_touched * expert_bytes(dec_cfg)
+        layer_bytes = wbytes + dec_cfg.H * dec_cfg.E * 4 + 2 * dec_cfg.T * dec_cfg.H * 2
+        dec_line = {
+            "value": dec_cfg.T / (dec_ms / 1e3),
+            "ms_per_step": dec_ms,
+            "stages_ms": dec_stage,
+            "touched_experts": n_touched,
+            "layer_hbm_frac": layer_bytes / (dec_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "roofline": {"bound": "hbm", "kernel": "moe_experts (gate/up + down stream GEMMs)",
+                         "achieved": wbytes / (dec_stage["experts"] / 1e3) / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None},
+        }
+        dec_line["roofline"]["frac"] = dec_line["roofline"]["achieved"] / HBM_PEAK_GBS
 
-    pre_line = None
-    if not a.no_prefill or a.workload == "prefill":
-        progress("generating prefill inputs (T=16384, Zipf load; same expert weights)")
-        pre = Workload(pre_cfg, moe, torch, dev_weights=dec.w)
-        pre.w_host = dec.w_host
+    if a.workload == "prefill" or not a.no_prefill:
+        progress("generating prefill inputs (T=16384, Zipf load)")
+        pre = Workload(pre_cfg, moe, torch, dev_weights=None if dec is None else dec.w)
+        if dec is not None:
+            pre.w_host = dec.w_host  # the same expert weights (same seed)
         progress("timing prefill")
-        pre_ms = pre.time_forward(max(3, a.steps // 2), max(1, a.warmup // 2))
-        pre_stage = pre.time_stages(max(3, a.steps // 2))
+        psteps = a.steps if a.workload == "prefill" else max(3, a.steps // 2)
+        pre_ms = pre.time_forward(psteps, max(1, a.warmup // 2))
+        pre_stage = pre.time_stages(psteps)
         P = pre_cfg.T * pre_cfg.k
         flops = 2.0 * P * (pre_cfg.H * 2 * pre_cfg.I + pre_cfg.I * pre_cfg.H)
         router_flops = 2.0 * pre_cfg.T * pre_cfg.H * pre_cfg.E

@@ -4,43 +4,85 @@
 // Same operation as the streaming kernel (per-expert GEMMs with gate and up
 // merged, "merged projections", UpstreamBeat "vLLM adds day-zero Reflection
 // Beam serving...", section "Agents worked on the serving path"), scheduled
-// for the dense-contraction regime:
-//  - one workgroup (4 wavefronts) computes a 128-row x 256-column output tile
-//    of one expert; each wavefront owns 64 x 128 (4 x 8 MFMA 16x16x32 tiles);
-//  - K advances 64 at a time through double-buffered LDS (96 KB): the next
-//    K step's global loads are issued before the current step's MFMAs and
-//    written to the other buffer afterwards, one barrier per step;
-//  - A rows are gathered (token rows of x for gate/up, rows of h for down);
-//    B is stored [K, N] (N contiguous), so each thread loads an 8 x 8 block
-//    and transposes it in registers into K-contiguous 16-byte granules;
-//  - LDS rows are 128 bytes with the 16-byte granule index XOR-swizzled by
-//    the row, so the fragment reads of 16 consecutive rows are conflict-free;
-//  - for gate/up the tile holds 128 gate columns and the matching 128 up
-//    columns, so each lane forms silu(gate) * up from two of its own
-//    accumulators;
+// for the dense-contraction regime, where the budget that matters is LDS
+// bandwidth per MFMA:
+//  - one workgroup (4 wavefronts, 2 x 2) computes a 256 x 256 output tile of
+//    one expert; each wavefront owns 128 x 128 (4 x 4 MFMA 32x32x16 tiles,
+//    256 fp32 accumulators), the largest tile whose accumulators fit, which
+//    halves LDS reads per MFMA against a 64 x 128 wave tile. The 32x32x16
+//    bf16 MFMA issues at twice the rate of the 16x16x32 one on gfx950;
+//  - K advances 32 per step through four LDS stages filled by direct
+//    global->LDS loads (16 B per lane; no registers stage the tiles), issued
+//    three steps ahead of the MFMAs: with one wavefront per SIMD nothing else
+//    hides a load that misses L2, so the pipeline depth has to;
+//  - the fragment reads are issued as inline ds_read instructions with
+//    explicit waits: the compiler would otherwise wait for every
+//    outstanding global->LDS load before any LDS read it can see;
+//  - A rows are gathered (token rows of x for gate/up, rows of h for down)
+//    and read as K-contiguous 16-byte fragments; B stays in its stored
+//    [K, N] layout (N contiguous) and is transposed by ds_read_b64_tr_b16;
+//  - every wave instruction that fills LDS writes one contiguous 1 KB
+//    block; reads use XOR-swizzled 16-byte granules so the 16 (b128) or 8
+//    (transpose) rows read together fall in distinct banks;
+//  - for gate/up the tile holds 128 gate and the matching 128 up columns, so
+//    each lane forms silu(gate) * up from two of its own accumulators;
+//  - the epilogue goes through LDS so output rows leave in 16-byte stores;
 //  - workgroups map onto (M tile, N tile) so that consecutive work items,
-//    which share A rows and B panels, land on the same XCD (and its L2).
+//    which share A rows and B panels, run on the same XCD (and its L2).
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int TBM = 128, TBN = 256, TBK = 64;
-constexpr int TSTAGE_A = TBM * TBK * 2;  // bytes per A stage
-constexpr int TSTAGE_B = TBN * TBK * 2;  // bytes per B stage
+constexpr int TBM = 256, TBN = 256, TBK = 32;
+constexpr int A_STAGE = TBM * TBK * 2;  // 16 KB: 256 rows x 64 B
+constexpr int B_STAGE = TBK * TBN * 2;  // 16 KB: 32 rows x 512 B
+constexpr int STAGE = A_STAGE + B_STAGE;
+constexpr int NSTAGE = 4;
+constexpr int LDS_BYTES = NSTAGE * STAGE;  // 128 KB (also holds the epilogue staging)
 
-__device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Direct global -> LDS load: lane l's 16 bytes land at lds + 16 * l.
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+// LDS reads the compiler does not see (their results are only valid after an
+// explicit lgkmcnt wait that takes them as operands).
+__device__ __forceinline__ u32x4 lds_b128(uint32_t addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+__device__ __forceinline__ u32x2 lds_tr16(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+
+// v_mfma_f32_32x32x16_bf16: lane l supplies A row l%32 / B column l%32 with K
+// block l/32 (8 values); the result lane l holds column l%32, rows
+// 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Byte offset of 16-byte granule kb (8 K values) of LDS row `row` (128 B rows).
-__device__ __forceinline__ int lds_off(int row, int kb) {
-  const int g = ((row >> 1) ^ (row >> 3)) & 7;
-  return row * 128 + ((kb ^ g) << 4);
-}
+// A rows are 64 B (4 granules); granule g of row r sits at g ^ ((r >> 2) & 3), so
+// the 16 consecutive rows of one fragment read cover all 16 bank groups.
+__device__ __forceinline__ int a_off(int row, int g) { return row * 64 + ((g ^ ((row >> 2) & 3)) << 4); }
+// B rows are 512 B (32 granules). A half-wave of transpose reads touches 4
+// consecutive K rows at two adjacent 32-byte column chunks; XOR-ing the
+// granule index with 4 * (row % 4) puts those 8 reads in distinct banks.
+__device__ __forceinline__ int b_swz(int row) { return (row & 3) << 2; }
 
-// M-tile table: tiles of TBM rows per expert, in expert order.
+// M-tile table: tiles of bm rows per expert, in expert order.
 __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restrict__ offsets,
                                                          int E, int bm,
                                                          int32_t* __restrict__ tile_e,
@@ -51,8 +93,7 @@ __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restri
   const int c = (e < E) ? (offsets[e + 1] - offsets[e] + bm - 1) / bm : 0;
   cnt[e] = c;
   __syncthreads();
-  // inclusive scan (Hillis-Steele over 256 entries)
-  for (int d = 1; d < 256; d <<= 1) {
+  for (int d = 1; d < 256; d <<= 1) {  // inclusive scan
     const int v = (e >= d) ? cnt[e - d] : 0;
     __syncthreads();
     cnt[e] += v;
@@ -72,11 +113,11 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
                                                            const int32_t* __restrict__ tile_m0,
                                                            const int32_t* __restrict__ n_tiles_p,
                                                            int NT) {
-  __shared__ __align__(16) uint8_t smem[2 * (TSTAGE_A + TSTAGE_B)];
+  __shared__ __align__(1024) uint8_t smem[LDS_BYTES];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- work item (XCD-aware: consecutive items on the same XCD)
+  // ---- work item: consecutive items (same M tile, neighbouring N tiles) on one XCD
   const int total = *n_tiles_p * NT;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int per = (total + 7) >> 3;
@@ -90,123 +131,203 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
   const int cnt = a.offsets[e + 1] - r0;
   const int K = a.K, N = a.N;
 
-  // ---- global load assignments
-  // A: thread owns half a row (4 granules) of the 128-row tile
-  const int arow = tid >> 1, ahalf = tid & 1;
-  const bool a_ok = m0 + arow < cnt;
-  const uint16_t* aptr = a.a;
-  {
-    size_t row = 0;
-    if (a_ok) row = GATE_UP ? (size_t)(a.sorted_pair[r0 + m0 + arow] / a.k) : (size_t)(r0 + m0 + arow);
-    aptr = a.a + row * K + ahalf * 32;
+  // ---- global -> register loads. Rows past the expert's end and columns past
+  // N read a clamped valid address: they only feed accumulators never stored.
+  // A: instruction q of this wave fills rows 64*wave + 16q .. +16 (1 KB); lane p
+  // holds physical granule p%4 of row 64*wave + 16q + p/4.
+  const uint16_t* asrc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = 64 * wave + 16 * q + (lane >> 2);
+    const int lg = (lane & 3) ^ ((row >> 2) & 3);
+    size_t grow = 0;
+    if (m0 + row < cnt)
+      grow = GATE_UP ? (size_t)(a.sorted_pair[r0 + m0 + row] / a.k) : (size_t)(r0 + m0 + row);
+    asrc[q] = a.a + grow * K + 8 * lg;
   }
-  // B: thread owns the 8 x 8 block (kb, nb) of the 64 x 256 tile
-  const int bkb = tid >> 5, bnb = tid & 31;
-  int bcol;  // global column of the block's first column
-  if (GATE_UP) {
-    const int g0 = nt * (TBN / 2);
-    bcol = (bnb < 16) ? g0 + 8 * bnb : a.I + g0 + 8 * (bnb - 16);
-  } else {
-    bcol = nt * TBN + 8 * bnb;
+  // B: instruction q fills K rows 8*wave + 2q .. +2 (1 KB); lane p holds
+  // physical granule p%32 of row 8*wave + 2q + p/32.
+  const uint16_t* bsrc[4];
+  const uint16_t* wbase = static_cast<const uint16_t*>(a.w) + (size_t)e * K * N;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = 8 * wave + 2 * q + (lane >> 5);
+    const int lg = (lane & 31) ^ b_swz(row);
+    int col;
+    bool ok;
+    if (GATE_UP) {
+      const int gc = nt * (TBN / 2) + 8 * (lg & 15);
+      ok = gc < a.I;
+      col = (lg < 16) ? gc : a.I + gc;
+    } else {
+      col = nt * TBN + 8 * lg;
+      ok = col < N;
+    }
+    bsrc[q] = wbase + (size_t)row * N + (ok ? col : 0);
   }
-  const bool b_ok = GATE_UP ? (nt * (TBN / 2) + 8 * (bnb & 15) < a.I) : (bcol < N);
-  const uint16_t* bptr = static_cast<const uint16_t*>(a.w) + (size_t)e * K * N + (b_ok ? bcol : 0) +
-                         (size_t)(8 * bkb) * N;
-
-  const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
-  u32x4 ra[4], rb[8];
-  auto gload = [&](int kt) {
+  // issue the direct loads of K step kt into stage buffer st
+  auto issue = [&](int kt, int st) {
+    uint8_t* As = smem + st * STAGE;
+    uint8_t* Bs = As + A_STAGE;
     const int k0 = kt * TBK;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      ra[q] = a_ok ? *reinterpret_cast<const u32x4*>(aptr + k0 + 8 * q) : zero;
+    for (int q = 0; q < 4; ++q) dma16(asrc[q] + k0, As + (64 * wave + 16 * q) * 64);
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-      rb[r] = b_ok ? *reinterpret_cast<const u32x4*>(bptr + (size_t)(k0 + r) * N) : zero;
-  };
-  auto lstore = [&](int buf) {
-    uint8_t* As = smem + buf * (TSTAGE_A + TSTAGE_B);
-    uint8_t* Bs = As + TSTAGE_A;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<u32x4*>(As + lds_off(arow, 4 * ahalf + q)) = ra[q];
-    // 8 x 8 transpose: column c's 8 K values -> one granule
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      u32x4 lo, hi;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t x0 = rb[2 * p][d], x1 = rb[2 * p + 1][d];
-        lo[p] = (x0 & 0xFFFFu) | (x1 << 16);
-        hi[p] = (x0 >> 16) | (x1 & 0xFFFF0000u);
-      }
-      *reinterpret_cast<u32x4*>(Bs + lds_off(8 * bnb + 2 * d, bkb)) = lo;
-      *reinterpret_cast<u32x4*>(Bs + lds_off(8 * bnb + 2 * d + 1, bkb)) = hi;
-    }
+    for (int q = 0; q < 4; ++q) dma16(bsrc[q] + (size_t)k0 * N, Bs + (8 * wave + 2 * q) * 512);
   };
 
-  f32x4 acc[4][8];
+  f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // LDS column of this wave's n-tile j
-  auto bcol_lds = [&](int j) -> int {
-    if (GATE_UP) return (j < 4) ? 64 * wn + 16 * j : 128 + 64 * wn + 16 * (j - 4);
-    return 128 * wn + 16 * j;
+  // LDS column of this wave's 32-column tile j (gate/up: 2 gate tiles, then the
+  // 2 matching up tiles)
+  auto bcol = [&](int j) -> int {
+    if (GATE_UP) return (j < 2) ? 64 * wn + 32 * j : 128 + 64 * wn + 32 * (j - 2);
+    return 128 * wn + 32 * j;
   };
-
-  const int nk = K / TBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint8_t* As = smem + (kt & 1) * (TSTAGE_A + TSTAGE_B);
-    const uint8_t* Bs = As + TSTAGE_A;
+  const int l32 = lane & 31, kh = lane >> 5;  // MFMA row/column and K block
+  const int tj = lane & 15, tg = lane >> 4;   // transpose-read lane and group
+  const uint32_t lds0 = (uint32_t)(size_t)(lds_u8*)smem;
+  // per-lane LDS byte offsets within a stage, for the two 16-deep K halves
+  uint32_t aoff[2][4], boff[2][4][2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int kb = 4 * s + (lane >> 4);
-      u32x4 fa[4], fb[8];
+  for (int s = 0; s < 2; ++s) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[i] = *reinterpret_cast<const u32x4*>(As + lds_off(64 * wm + 16 * i + (lane & 15), kb));
+    for (int i = 0; i < 4; ++i) aoff[s][i] = a_off(128 * wm + 32 * i + l32, 2 * s + kh);
+    // B: group tg reads K rows 16s + 8*(tg>>1) + tj/4 (+4) at columns
+    // bcol + 16*(tg&1) + 4*(tj%4); the lane receives its column's 8 K values
+    const int krow = 16 * s + 8 * (tg >> 1) + (tj >> 2);
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        fb[j] = *reinterpret_cast<const u32x4*>(Bs + lds_off(bcol_lds(j) + (lane & 15), kb));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = mfma_bf16(fa[i], fb[j], acc[i][j]);
+    for (int j = 0; j < 4; ++j) {
+      const int c = bcol(j) + 16 * (tg & 1) + 4 * (tj & 3);
+      boff[s][j][0] = A_STAGE + krow * 512 + (((c >> 3) ^ b_swz(krow)) << 4) + ((c & 7) << 1);
+      boff[s][j][1] = A_STAGE + (krow + 4) * 512 + (((c >> 3) ^ b_swz(krow + 4)) << 4) + ((c & 7) << 1);
     }
-    if (kt + 1 < nk) lstore((kt + 1) & 1);
-    __syncthreads();
   }
+  // Fragments of one 16-deep K half: 4 A tiles and 4 B tiles (two transpose
+  // reads each). Reads are issued asynchronously; lgk_wait() publishes them.
+  struct Frag {
+    u32x4 a[4];
+    u32x2 lo[4], hi[4];
+  };
+  auto read_frag = [&](Frag& f, int st, int s) {
+    const uint32_t base = lds0 + st * STAGE;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f.lo[j] = lds_tr16(base + boff[s][j][0]);
+      f.hi[j] = lds_tr16(base + boff[s][j][1]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = lds_b128(base + aoff[s][i]);
+  };
+  // Wait until at most `pending` LDS reads (those issued after f's) are
+  // outstanding; f's registers are operands so nothing consumes them earlier.
+#define MOE_LGK_WAIT(f, pending)                                                              \
+  asm volatile("s_waitcnt lgkmcnt(" #pending ")"                                              \
+               : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.lo[0]),        \
+                 "+v"(f.lo[1]), "+v"(f.lo[2]), "+v"(f.lo[3]), "+v"(f.hi[0]), "+v"(f.hi[1]),   \
+                 "+v"(f.hi[2]), "+v"(f.hi[3])                                                  \
+               :                                                                               \
+               : "memory")
+  auto mfma_frag = [&](const Frag& f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 b = u32x4{f.lo[j][0], f.lo[j][1], f.hi[j][0], f.hi[j][1]};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i][j] = mfma32(f.a[i], b, acc[i][j]);
+    }
+  };
+  // Pipeline, with a branch-free step body (in-flight fragment registers must
+  // never meet a control-flow merge, where copies could read them early):
+  // every step issues one K step of loads (clamped to the last step near the
+  // end, into the buffer of step kt-1, which is free), so "step kt+1 landed"
+  // is always vmcnt(8); the next half's fragments are always read, the extra
+  // read after the last step is discarded. Within a step the second K half's
+  // fragments are read while the first half's MFMAs run, and the next step's
+  // first half is read (after the barrier that publishes that step's data and
+  // frees the buffer of step kt-1) while the second half's MFMAs run.
+  const int nk = K / TBK;
+  issue(0, 0);
+  issue(nk > 1 ? 1 : nk - 1, 1);
+  issue(nk > 2 ? 2 : nk - 1, 2);
+  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  Frag f0, f1;
+  read_frag(f0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    read_frag(f1, kt % NSTAGE, 1);
+    MOE_LGK_WAIT(f0, 12);
+    mfma_frag(f0);
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    issue(kt + 3 < nk ? kt + 3 : nk - 1, (kt + 3) % NSTAGE);
+    read_frag(f0, (kt + 1) % NSTAGE, 0);
+    MOE_LGK_WAIT(f1, 12);
+    mfma_frag(f1);
+  }
+  MOE_LGK_WAIT(f0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#undef MOE_LGK_WAIT
+  __builtin_amdgcn_s_barrier();
 
-  // ---- epilogue: lane holds rows 4*(lane>>4)+r of column lane&15 of each 16x16 tile
-  const int cl = lane & 15, rq = 4 * (lane >> 4);
+  // ---- epilogue through LDS (the K loop ended with a barrier, so LDS is free):
+  // per 32-row slice the wave writes its results into its own LDS strip, then
+  // reads them back row-contiguous for 16-byte global stores. Lane l holds
+  // column l%32 of each 32x32 tile at rows 8*(r/4) + 4*(l/32) + r%4.
+  auto tile_row = [&](int r) { return 8 * (r >> 2) + 4 * kh + (r & 3); };
+  if (GATE_UP) {
+    uint16_t* strip = reinterpret_cast<uint16_t*>(smem + wave * 4096);  // 32 x 64 bf16
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + 64 * wm + 16 * i + rq + r;
-      if (m >= cnt) continue;
-      const size_t row = (size_t)(r0 + m);
-      if (GATE_UP) {
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = nt * (TBN / 2) + 64 * wn + 16 * j + cl;
-          if (col < a.I)
-            a.h_out[row * a.I + col] = (uint16_t)f32_to_bf16_bits(silu(acc[i][j][r]) * acc[i][j + 4][r]);
-        }
-      } else {
+        for (int r = 0; r < 16; ++r)
+          strip[tile_row(r) * 64 + 32 * j + l32] =
+              (uint16_t)f32_to_bf16_bits(silu(acc[i][j][r]) * acc[i][j + 2][r]);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int col = nt * TBN + 128 * wn + 16 * j + cl;
-          if (col < N) a.y_out[row * N + col] = acc[i][j][r];
-        }
+      for (int t = 0; t < 4; ++t) {  // 32 rows x 8 chunks of 16 B
+        const int c = lane + 64 * t, rr = c >> 3, ch = c & 7;
+        const int m = m0 + 128 * wm + 32 * i + rr;
+        const int col = nt * (TBN / 2) + 64 * wn + 8 * ch;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(strip + rr * 64 + 8 * ch);
+        if (m < cnt && col < a.I)
+          *reinterpret_cast<u32x4*>(a.h_out + (size_t)(r0 + m) * a.I + col) = v;
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  } else {
+    float* strip = reinterpret_cast<float*>(smem + wave * 16384);  // 32 x 128 fp32
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) strip[tile_row(r) * 128 + 32 * j + l32] = acc[i][j][r];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {  // 32 rows x 32 chunks of 16 B
+        const int c = lane + 64 * t, rr = c >> 5, ch = c & 31;
+        const int m = m0 + 128 * wm + 32 * i + rr;
+        const int col = nt * TBN + 128 * wn + 4 * ch;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(strip + rr * 128 + 4 * ch);
+        if (m < cnt && col < N) *reinterpret_cast<f32x4*>(a.y_out + (size_t)(r0 + m) * N + col) = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
 }
