@@ -37,6 +37,8 @@ def parse():
     p.add_argument("--workload", choices=["decode", "prefill"], default="decode")
     p.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill line")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    p.add_argument("--hbm-probe", action="store_true",
+                   help="time a plain 4 GiB device copy (the reference kernel for HBM counters) and exit")
     return p.parse_args()
 
 
@@ -132,6 +134,52 @@ class Workload:
         return self.counts.cpu().numpy()
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_t128_moe_experts_hbm_traffic.md")
+STREAM_SRC = os.path.join(ROOT, "sparse_moe_layer_gemm_amd", "csrc", "expert_stream.hip")
+
+
+def source_sha256(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per moe_experts launch at decode, from the committed rocprofv3 counter
+    summary, or None when it is missing or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if line.startswith("TRAFFIC_JSON:"):
+                    d = json.loads(line.split(":", 1)[1])
+                    if d.get("source_sha256") == source_sha256(STREAM_SRC):
+                        return d["hbm_bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
+
+
+def hbm_probe(torch):
+    """Plain device copy of 4 GiB: reads and writes a known number of bytes."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    nbytes = n * 4
+    print(json.dumps({"probe": "device copy", "bytes_read_per_launch": nbytes,
+                      "bytes_written_per_launch": nbytes, "ms_per_launch": ms,
+                      "GB/s (read+write)": 2 * nbytes / (ms / 1e3) / 1e9}), flush=True)
+
+
 def expert_bytes(cfg):
     """Bytes of one expert's bf16 weights: gate/up [H, 2I] + down [I, H]."""
     return 2 * (cfg.H * 2 * cfg.I + cfg.I * cfg.H)
@@ -163,6 +211,9 @@ def main():
               f"unsharded on a single MI355X.", file=sys.stderr)
         sys.exit(2)
     import torch
+    if a.hbm_probe:
+        hbm_probe(torch)
+        return
     import sparse_moe_layer_gemm_amd as moe
     import synth
 
@@ -187,7 +238,7 @@ def main():
             "layer_hbm_frac": layer_bytes / (dec_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
             "roofline": {"bound": "hbm", "kernel": "moe_experts (gate/up + down stream GEMMs)",
                          "achieved": wbytes / (dec_stage["experts"] / 1e3) / 1e9,
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": None},
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": measured_traffic()},
         }
         dec_line["roofline"]["frac"] = dec_line["roofline"]["achieved"] / HBM_PEAK_GBS
 
