@@ -54,10 +54,22 @@ void router_plan(int64_t T, int32_t H, int* n_split, int* split_len) {
   *n_split = (chunks + per - 1) / per;
 }
 
+// Large bf16 batches run the router as three bf16 GEMMs on the tiled MFMA
+// kernel (exact split of the fp32 weights); small ones on the fp32-MFMA kernel.
+bool router_use_bf16x3(int32_t x_dtype, int64_t T) {
+  return x_dtype == MOE_BF16 && T >= 1024;
+}
+
 size_t route_ws_bytes(int64_t T, int32_t H, int32_t E) {
   int S, L;
   router_plan(T, H, &S, &L);
-  return align_up((size_t)S * T * E * sizeof(float)) + align_up((size_t)T * E * sizeof(float));
+  size_t fp32_path = align_up((size_t)S * T * E * sizeof(float));
+  size_t bf16x3_path = 0;
+  if (T >= 1024)
+    bf16x3_path = align_up((size_t)moe::router_bf16x3_splits() * T * 256 * sizeof(float)) +
+                  align_up(moe::router_bf16x3_ws_bytes((int)T, H));
+  return (fp32_path > bf16x3_path ? fp32_path : bf16x3_path) +
+         align_up((size_t)T * E * sizeof(float));
 }
 
 moe_status check_weights(const moe_expert_weights* w, int32_t x_dtype, int32_t H, int32_t I) {
@@ -111,14 +123,30 @@ moe_status enqueue_route(const void* x, int32_t x_dtype, int64_t T, int32_t H, c
                          hipStream_t st) {
   int S, L;
   router_plan(T, H, &S, &L);
+  const bool x3 = router_use_bf16x3(x_dtype, T);
+  const size_t part_bytes = x3 ? (size_t)moe::router_bf16x3_splits() * T * 256 * sizeof(float)
+                               : (size_t)S * T * E * sizeof(float);
   Carver c{static_cast<char*>(ws), 0};
-  float* part = static_cast<float*>(c.take((size_t)S * T * E * sizeof(float)));
-  void* lbuf = c.take((size_t)T * E * sizeof(float));
+  float* part = static_cast<float*>(c.take(part_bytes));
+  void* x3ws = x3 ? c.take(moe::router_bf16x3_ws_bytes((int)T, H)) : nullptr;
+  // the fp32 logits scratch sits at the end of the route workspace
+  void* lbuf = static_cast<char*>(ws) + route_ws_bytes(T, H, E) -
+               align_up((size_t)T * E * sizeof(float));
   if (!logits) logits = lbuf;
-  hipError_t e = moe::launch_router_gemm(x, x_dtype == MOE_BF16, (int)T, H, wr, E, S, L, part, st);
+  hipError_t e;
+  int nsplit, ldp;
+  if (x3) {
+    e = moe::launch_router_bf16x3(static_cast<const uint16_t*>(x), (int)T, H, wr, E, part, x3ws, st);
+    nsplit = moe::router_bf16x3_splits();
+    ldp = 256;
+  } else {
+    e = moe::launch_router_gemm(x, x_dtype == MOE_BF16, (int)T, H, wr, E, S, L, part, st);
+    nsplit = S;
+    ldp = E;
+  }
   if (e != hipSuccess) return MOE_ERR_LAUNCH;
-  e = moe::launch_router_select(part, S, (int)T, E, k, bias, logits_dtype == MOE_BF16, logits,
-                                logits_f32, ids, w, st);
+  e = moe::launch_router_select(part, nsplit, ldp, (int)T, E, k, bias, logits_dtype == MOE_BF16,
+                                logits, logits_f32, ids, w, st);
   return launch_status(e);
 }
 

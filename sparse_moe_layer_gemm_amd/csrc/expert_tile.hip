@@ -130,6 +130,14 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
   const int r0 = a.offsets[e];
   const int cnt = a.offsets[e + 1] - r0;
   const int K = a.K, N = a.N;
+  // split-K / weight plane of this workgroup (a single split for the experts)
+  const int split = blockIdx.y;
+  const int kslice = split % a.nk_split, plane = split / a.nk_split;
+  const int lda = a.lda ? a.lda : K;
+  const uint16_t* A = a.a + (size_t)kslice * K;
+  const uint16_t* W = static_cast<const uint16_t*>(a.w) + (size_t)plane * a.w_plane_stride +
+                      (size_t)kslice * K * N;
+  float* Yout = a.y_out + (size_t)split * a.y_split_stride;
 
   // ---- global -> register loads. Rows past the expert's end and columns past
   // N read a clamped valid address: they only feed accumulators never stored.
@@ -143,12 +151,12 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
     size_t grow = 0;
     if (m0 + row < cnt)
       grow = GATE_UP ? (size_t)(a.sorted_pair[r0 + m0 + row] / a.k) : (size_t)(r0 + m0 + row);
-    asrc[q] = a.a + grow * K + 8 * lg;
+    asrc[q] = A + grow * lda + 8 * lg;
   }
   // B: instruction q fills K rows 8*wave + 2q .. +2 (1 KB); lane p holds
   // physical granule p%32 of row 8*wave + 2q + p/32.
   const uint16_t* bsrc[4];
-  const uint16_t* wbase = static_cast<const uint16_t*>(a.w) + (size_t)e * K * N;
+  const uint16_t* wbase = W + (size_t)e * K * N;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int row = 8 * wave + 2 * q + (lane >> 5);
@@ -323,7 +331,7 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
         const int m = m0 + 128 * wm + 32 * i + rr;
         const int col = nt * TBN + 128 * wn + 4 * ch;
         const f32x4 v = *reinterpret_cast<const f32x4*>(strip + rr * 128 + 4 * ch);
-        if (m < cnt && col < N) *reinterpret_cast<f32x4*>(a.y_out + (size_t)(r0 + m) * N + col) = v;
+        if (m < cnt && col < N) *reinterpret_cast<f32x4*>(Yout + (size_t)(r0 + m) * N + col) = v;
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -332,11 +340,83 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
   }
 }
 
+
+// fp32 router weights [H, E] -> three bf16 planes [3][H][256] (columns >= E zero):
+// hi = RNE(w), mid = RNE(w - hi), lo = RNE(w - hi - mid); both differences are
+// exact in fp32. Also writes the one-expert offsets {0, T} the tiled kernel uses.
+__global__ __launch_bounds__(256) void router_pack_kernel(const float* __restrict__ w, int H, int E,
+                                                          uint16_t* __restrict__ planes,
+                                                          int32_t* __restrict__ offsets, int T) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;  // over H * 256
+  if (i == 0) {
+    offsets[0] = 0;
+    offsets[1] = T;
+  }
+  if (i >= (size_t)H * 256) return;
+  const int h = (int)(i >> 8), c = (int)(i & 255);
+  const float v = c < E ? w[(size_t)h * E + c] : 0.f;
+  const uint32_t hi = f32_to_bf16_bits(v);
+  const float r1 = v - bf16_bits_to_f32(hi);
+  const uint32_t mid = f32_to_bf16_bits(r1);
+  const float r2 = r1 - bf16_bits_to_f32(mid);
+  const uint32_t lo = f32_to_bf16_bits(r2);
+  const size_t plane = (size_t)H * 256;
+  planes[i] = (uint16_t)hi;
+  planes[plane + i] = (uint16_t)mid;
+  planes[2 * plane + i] = (uint16_t)lo;
+}
+
+constexpr int ROUTER_NKS = 2;  // K slices per plane (3 * 2 splits in all)
+
 }  // namespace
 
 size_t expert_tile_ws_bytes(int P, int E) {
   const int max_tiles = (P + TBM - 1) / TBM + E;
   return (size_t)(2 * max_tiles + 64) * sizeof(int32_t);
+}
+
+int router_bf16x3_splits() { return 3 * ROUTER_NKS; }
+
+size_t router_bf16x3_ws_bytes(int T, int H) {
+  const int tiles = (T + TBM - 1) / TBM + 1;
+  return (size_t)3 * H * 256 * sizeof(uint16_t) + (size_t)(2 * tiles + 64) * sizeof(int32_t) + 256;
+}
+
+hipError_t launch_router_bf16x3(const uint16_t* x, int T, int H, const float* w_router, int E,
+                                float* part, void* ws, hipStream_t st) {
+  if (H % (TBK * ROUTER_NKS) != 0) return hipErrorInvalidValue;
+  uint16_t* planes = static_cast<uint16_t*>(ws);
+  int32_t* offsets = reinterpret_cast<int32_t*>(planes + (size_t)3 * H * 256);
+  const int max_tiles = (T + TBM - 1) / TBM + 1;
+  int32_t* tile_e = offsets + 64;
+  int32_t* tile_m0 = tile_e + max_tiles;
+  int32_t* n_tiles = tile_m0 + max_tiles;
+  router_pack_kernel<<<(unsigned)(((size_t)H * 256 + 255) / 256), 256, 0, st>>>(w_router, H, E, planes,
+                                                                              offsets, T);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  tile_table_kernel<<<1, 256, 0, st>>>(offsets, 1, TBM, tile_e, tile_m0, n_tiles);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  StreamGemmArgs a{};
+  a.a = x;
+  a.offsets = offsets;
+  a.sorted_pair = nullptr;
+  a.k = 1;
+  a.E = 1;
+  a.K = H / ROUTER_NKS;
+  a.lda = H;
+  a.N = 256;
+  a.I = 0;
+  a.w = planes;
+  a.y_out = part;
+  a.nsplit = 3 * ROUTER_NKS;
+  a.nk_split = ROUTER_NKS;
+  a.w_plane_stride = (long long)H * 256;
+  a.y_split_stride = (long long)T * 256;
+  const unsigned grid = (unsigned)(((max_tiles + 7) / 8) * 8);
+  tile_bf16_kernel<false><<<dim3(grid, a.nsplit), 256, 0, st>>>(a, tile_e, tile_m0, n_tiles, 1);
+  return hipGetLastError();
 }
 
 hipError_t launch_expert_tile(int wfmt, const StreamGemmArgs& gu, const StreamGemmArgs& dn, int P,

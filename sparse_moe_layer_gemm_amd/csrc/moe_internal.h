@@ -36,7 +36,7 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 hipError_t launch_router_gemm(const void* x, bool x_bf16, int T, int H, const float* w_router,
                               int E, int n_split, int split_len, float* part, hipStream_t st);
 // Sum of partials + bias -> logits (bf16 or fp32), softmax, top-k, renormalised weights.
-hipError_t launch_router_select(const float* part, int n_split, int T, int E, int k,
+hipError_t launch_router_select(const float* part, int n_split, int ldp, int T, int E, int k,
                                 const float* bias, bool logits_bf16, void* logits,
                                 float* logits_f32, int32_t* ids, float* w, hipStream_t st);
 // Stable counting sort of pairs by expert.
@@ -56,6 +56,12 @@ struct StreamGemmArgs {
   const float* w_gscale;   // FP4: f32 [E]
   uint16_t* h_out;         // gate/up output [P, I] bf16
   float* y_out;            // down output [P, N] f32
+  // Split-K over blockIdx.y (tiled kernel, down mode only): split s reads the
+  // K slice (s % nk_split) of length K from A (row stride lda) and from weight
+  // plane (s / nk_split), and writes partial sums to y_out + s * y_split_stride.
+  int lda = 0;             // 0: lda = K
+  int nsplit = 1, nk_split = 1;
+  long long w_plane_stride = 0, y_split_stride = 0;
 };
 // Grouped expert GEMM for small row counts per expert: each wavefront owns a
 // 128-column slice of one expert's matrix and streams it once per 32 rows.
@@ -67,6 +73,14 @@ hipError_t launch_expert_stream(int wfmt, bool gate_up, const StreamGemmArgs& a,
 size_t expert_tile_ws_bytes(int P, int E);
 hipError_t launch_expert_tile(int wfmt, const StreamGemmArgs& gate_up, const StreamGemmArgs& down,
                               int P, void* ws, hipStream_t st);
+// Router logits as three bf16 GEMMs on the tiled kernel: the fp32 router
+// weights split into bf16 planes hi + mid + lo (24 significant bits), x being
+// exactly bf16, so every product is exact and accumulation is fp32. Writes
+// 3 * n_khalf partial sums [split][T][256] for the select kernel to add.
+size_t router_bf16x3_ws_bytes(int T, int H);
+int router_bf16x3_splits();
+hipError_t launch_router_bf16x3(const uint16_t* x, int T, int H, const float* w_router, int E,
+                                float* part, void* ws, hipStream_t st);
 // Rows per expert from which the tiled kernel replaces the streaming one.
 constexpr int kTileMinRowsPerExpert = 32;
 

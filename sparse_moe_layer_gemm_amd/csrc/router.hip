@@ -125,7 +125,7 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
 // wave-wide max picks the largest logit and, on equal logits, the lowest id.
 template <bool BF16_LOGITS>
 __global__ __launch_bounds__(256) void router_select_kernel(
-    const float* __restrict__ part, int n_split, int T, int E, int k,
+    const float* __restrict__ part, int n_split, int ldp, int T, int E, int k,
     const float* __restrict__ bias, void* __restrict__ logits, float* __restrict__ logits_f32,
     int32_t* __restrict__ ids, float* __restrict__ w) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     key[q] = 0;
     if (e < E) {
       float v = 0.f;
-      for (int s = 0; s < n_split; ++s) v += part[((size_t)s * T + t) * E + e];
+      for (int s = 0; s < n_split; ++s) v += part[((size_t)s * T + t) * ldp + e];
       if (bias) v += bias[e];
       if (logits_f32) logits_f32[(size_t)t * E + e] = v;
       float sv = v;
@@ -203,15 +203,15 @@ hipError_t launch_router_gemm(const void* x, bool x_bf16, int T, int H, const fl
   return hipGetLastError();
 }
 
-hipError_t launch_router_select(const float* part, int n_split, int T, int E, int k,
+hipError_t launch_router_select(const float* part, int n_split, int ldp, int T, int E, int k,
                                 const float* bias, bool logits_bf16, void* logits,
                                 float* logits_f32, int32_t* ids, float* w, hipStream_t st) {
   dim3 grid((T + 3) / 4);
   if (logits_bf16)
-    router_select_kernel<true><<<grid, 256, 0, st>>>(part, n_split, T, E, k, bias, logits,
+    router_select_kernel<true><<<grid, 256, 0, st>>>(part, n_split, ldp, T, E, k, bias, logits,
                                                      logits_f32, ids, w);
   else
-    router_select_kernel<false><<<grid, 256, 0, st>>>(part, n_split, T, E, k, bias, logits,
+    router_select_kernel<false><<<grid, 256, 0, st>>>(part, n_split, ldp, T, E, k, bias, logits,
                                                       logits_f32, ids, w);
   return hipGetLastError();
 }

@@ -78,6 +78,21 @@ def test_router_beam_shape():
     log(f"  logits rel err {rt['logit_rel_err']:.2e}, ambiguous tokens {rt['ambiguous']}/{rt['tokens']}")
 
 
+# Batches of >= 1024 bf16 tokens take the router through three bf16 products on
+# the tiled MFMA kernel (weights split exactly into hi/mid/lo bf16 planes); all
+# logits are checked, with a ragged last M tile and, for E = 200, zero-padded
+# expert columns.
+@pytest.mark.parametrize("T,H,E,k", [(1300, 5120, 256, 8), (1030, 640, 200, 6)])
+def test_router_split_bf16_full(T, H, E, k):
+    cfg = MC(f"router_x3_t{T}_e{E}", 120 + E, T=T, H=H, E=E, k=k, I=64, router_only=True)
+    log(f"[parity] {cfg.name}")
+    L = Layer(cfg)
+    r = L.route()
+    torch.cuda.synchronize()
+    rt = check_router(L, r)
+    log(f"  logits rel err {rt['logit_rel_err']:.2e}, ambiguous tokens {rt['ambiguous']}/{rt['tokens']}")
+
+
 @pytest.fixture(scope="module")
 def decode_layer():
     cfg = synth.CONFIGS["decode_t128"]
