@@ -11,6 +11,11 @@
 //    256 fp32 accumulators), the largest tile whose accumulators fit, which
 //    halves LDS reads per MFMA against a 64 x 128 wave tile. The 32x32x16
 //    bf16 MFMA issues at twice the rate of the 16x16x32 one on gfx950;
+//  - an expert's last partial tile of at most 128 rows runs instead as a
+//    128 x 512 tile (1 x 4 wavefronts, same 128 x 128 per wavefront) in a
+//    second launch: with skewed routing most experts hold a few hundred
+//    rows, and padding their tails to 256 rows wasted about a quarter of
+//    the MFMA work. The wider tile keeps the weight bytes per MAC unchanged;
 //  - K advances 32 per step through four LDS stages filled by direct
 //    global->LDS loads (16 B per lane; no registers stage the tiles), issued
 //    three steps ahead of the MFMAs: with one wavefront per SIMD nothing else
@@ -24,8 +29,8 @@
 //  - every wave instruction that fills LDS writes one contiguous 1 KB
 //    block; reads use XOR-swizzled 16-byte granules so the 16 (b128) or 8
 //    (transpose) rows read together fall in distinct banks;
-//  - for gate/up the tile holds 128 gate and the matching 128 up columns, so
-//    each lane forms silu(gate) * up from two of its own accumulators;
+//  - for gate/up the tile holds BN/2 gate and the matching BN/2 up columns,
+//    so each lane forms silu(gate) * up from two of its own accumulators;
 //  - the epilogue goes through LDS so output rows leave in 16-byte stores;
 //  - workgroups map onto (M tile, N tile) so that consecutive work items,
 //    which share A rows and B panels, run on the same XCD (and its L2).
@@ -34,12 +39,24 @@
 namespace moe {
 namespace {
 
-constexpr int TBM = 256, TBN = 256, TBK = 32;
-constexpr int A_STAGE = TBM * TBK * 2;  // 16 KB: 256 rows x 64 B
-constexpr int B_STAGE = TBK * TBN * 2;  // 16 KB: 32 rows x 512 B
-constexpr int STAGE = A_STAGE + B_STAGE;
-constexpr int NSTAGE = 4;
-constexpr int LDS_BYTES = NSTAGE * STAGE;  // 128 KB (also holds the epilogue staging)
+constexpr int TBK = 32, NSTAGE = 4;
+constexpr int TBM = 256;  // rows of the large tile (tile table sizing, router)
+
+// Workgroup tile shapes. WM wavefronts along M: WM = 2 gives 256 x 256 tiles,
+// WM = 1 gives 128 x 512 tiles (for experts, or expert tails, of <= 128 rows);
+// every wavefront computes 128 x 128 either way.
+template <int WM>
+struct TileShape {
+  static constexpr int BM = 128 * WM, BN = 512 / WM;
+  static constexpr int WN = 4 / WM;             // wavefronts along N
+  static constexpr int A_STAGE = BM * TBK * 2;  // BM rows x 64 B
+  static constexpr int B_STAGE = TBK * BN * 2;  // 32 rows x 2*BN B
+  static constexpr int STAGE = A_STAGE + B_STAGE;
+  static constexpr int LDS = NSTAGE * STAGE;    // 128 KB / 160 KB (also the epilogue staging)
+  static constexpr int QA = BM / 64;            // 1 KB A loads per wavefront per K step
+  static constexpr int QB = BN / 64;            // 1 KB B loads per wavefront per K step
+  static constexpr int RPI = 512 / BN;          // B rows per load
+};
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -82,21 +99,32 @@ __device__ __forceinline__ int a_off(int row, int g) { return row * 64 + ((g ^ (
 // granule index with 4 * (row % 4) puts those 8 reads in distinct banks.
 __device__ __forceinline__ int b_swz(int row) { return (row & 3) << 2; }
 
-// M-tile table: tiles of bm rows per expert, in expert order.
+// M-tile tables, in expert order: tiles of bm rows per expert; with `split`, an
+// expert's last partial tile of at most bm/2 rows goes to a second table of
+// half-height tiles instead.
 __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restrict__ offsets,
-                                                         int E, int bm,
+                                                         int E, int bm, int split,
                                                          int32_t* __restrict__ tile_e,
                                                          int32_t* __restrict__ tile_m0,
-                                                         int32_t* __restrict__ n_tiles) {
-  __shared__ int cnt[256];
+                                                         int32_t* __restrict__ n_tiles,
+                                                         int32_t* __restrict__ half_e,
+                                                         int32_t* __restrict__ half_m0,
+                                                         int32_t* __restrict__ n_half) {
+  __shared__ int cnt[256], hcnt[256];
   const int e = threadIdx.x;
-  const int c = (e < E) ? (offsets[e + 1] - offsets[e] + bm - 1) / bm : 0;
+  const int rows = (e < E) ? offsets[e + 1] - offsets[e] : 0;
+  const int rem = rows % bm;
+  const int h = (split && rem > 0 && rem <= bm / 2) ? 1 : 0;
+  const int c = rows / bm + ((rem > 0 && !h) ? 1 : 0);
   cnt[e] = c;
+  hcnt[e] = h;
   __syncthreads();
-  for (int d = 1; d < 256; d <<= 1) {  // inclusive scan
+  for (int d = 1; d < 256; d <<= 1) {  // inclusive scans
     const int v = (e >= d) ? cnt[e - d] : 0;
+    const int vh = (e >= d) ? hcnt[e - d] : 0;
     __syncthreads();
     cnt[e] += v;
+    hcnt[e] += vh;
     __syncthreads();
   }
   const int base = cnt[e] - c;
@@ -104,18 +132,26 @@ __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restri
     tile_e[base + j] = e;
     tile_m0[base + j] = j * bm;
   }
-  if (e == 255) *n_tiles = cnt[255];
+  if (h) {
+    half_e[hcnt[e] - 1] = e;
+    half_m0[hcnt[e] - 1] = (rows / bm) * bm;
+  }
+  if (e == 255) {
+    *n_tiles = cnt[255];
+    if (split) *n_half = hcnt[255];
+  }
 }
 
-template <bool GATE_UP>
+template <bool GATE_UP, int WM>
 __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
                                                            const int32_t* __restrict__ tile_e,
                                                            const int32_t* __restrict__ tile_m0,
                                                            const int32_t* __restrict__ n_tiles_p,
                                                            int NT) {
-  __shared__ __align__(1024) uint8_t smem[LDS_BYTES];
+  using S = TileShape<WM>;
+  __shared__ __align__(1024) uint8_t smem[S::LDS];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / S::WN, wn = wave % S::WN;
 
   // ---- work item: consecutive items (same M tile, neighbouring N tiles) on one XCD
   const int total = *n_tiles_p * NT;
@@ -143,10 +179,10 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
   // N read a clamped valid address: they only feed accumulators never stored.
   // A: instruction q of this wave fills rows 64*wave + 16q .. +16 (1 KB); lane p
   // holds physical granule p%4 of row 64*wave + 16q + p/4.
-  const uint16_t* asrc[4];
+  const uint16_t* asrc[S::QA];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int row = 64 * wave + 16 * q + (lane >> 2);
+  for (int q = 0; q < S::QA; ++q) {
+    const int row = (S::BM / 4) * wave + 16 * q + (lane >> 2);
     const int lg = (lane & 3) ^ ((row >> 2) & 3);
     size_t grow = 0;
     if (m0 + row < cnt)
@@ -155,33 +191,34 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
   }
   // B: instruction q fills K rows 8*wave + 2q .. +2 (1 KB); lane p holds
   // physical granule p%32 of row 8*wave + 2q + p/32.
-  const uint16_t* bsrc[4];
+  const uint16_t* bsrc[S::QB];
   const uint16_t* wbase = W + (size_t)e * K * N;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int row = 8 * wave + 2 * q + (lane >> 5);
-    const int lg = (lane & 31) ^ b_swz(row);
+  for (int q = 0; q < S::QB; ++q) {
+    const int row = 8 * wave + S::RPI * q + lane / (64 / S::RPI);
+    const int lg = (lane % (64 / S::RPI)) ^ b_swz(row);
     int col;
     bool ok;
     if (GATE_UP) {
-      const int gc = nt * (TBN / 2) + 8 * (lg & 15);
+      const int gc = nt * (S::BN / 2) + 8 * (lg % (S::BN / 16));
       ok = gc < a.I;
-      col = (lg < 16) ? gc : a.I + gc;
+      col = (lg < S::BN / 16) ? gc : a.I + gc;
     } else {
-      col = nt * TBN + 8 * lg;
+      col = nt * S::BN + 8 * lg;
       ok = col < N;
     }
     bsrc[q] = wbase + (size_t)row * N + (ok ? col : 0);
   }
   // issue the direct loads of K step kt into stage buffer st
   auto issue = [&](int kt, int st) {
-    uint8_t* As = smem + st * STAGE;
-    uint8_t* Bs = As + A_STAGE;
+    uint8_t* As = smem + st * S::STAGE;
+    uint8_t* Bs = As + S::A_STAGE;
     const int k0 = kt * TBK;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dma16(asrc[q] + k0, As + (64 * wave + 16 * q) * 64);
+    for (int q = 0; q < S::QA; ++q) dma16(asrc[q] + k0, As + ((S::BM / 4) * wave + 16 * q) * 64);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dma16(bsrc[q] + (size_t)k0 * N, Bs + (8 * wave + 2 * q) * 512);
+    for (int q = 0; q < S::QB; ++q)
+      dma16(bsrc[q] + (size_t)k0 * N, Bs + (8 * wave + S::RPI * q) * (2 * S::BN));
   };
 
   f32x16 acc[4][4];
@@ -195,7 +232,7 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
   // LDS column of this wave's 32-column tile j (gate/up: 2 gate tiles, then the
   // 2 matching up tiles)
   auto bcol = [&](int j) -> int {
-    if (GATE_UP) return (j < 2) ? 64 * wn + 32 * j : 128 + 64 * wn + 32 * (j - 2);
+    if (GATE_UP) return (j < 2) ? 64 * wn + 32 * j : S::BN / 2 + 64 * wn + 32 * (j - 2);
     return 128 * wn + 32 * j;
   };
   const int l32 = lane & 31, kh = lane >> 5;  // MFMA row/column and K block
@@ -213,8 +250,10 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = bcol(j) + 16 * (tg & 1) + 4 * (tj & 3);
-      boff[s][j][0] = A_STAGE + krow * 512 + (((c >> 3) ^ b_swz(krow)) << 4) + ((c & 7) << 1);
-      boff[s][j][1] = A_STAGE + (krow + 4) * 512 + (((c >> 3) ^ b_swz(krow + 4)) << 4) + ((c & 7) << 1);
+      boff[s][j][0] = S::A_STAGE + krow * (2 * S::BN) + (((c >> 3) ^ b_swz(krow)) << 4) +
+                      ((c & 7) << 1);
+      boff[s][j][1] = S::A_STAGE + (krow + 4) * (2 * S::BN) +
+                      (((c >> 3) ^ b_swz(krow + 4)) << 4) + ((c & 7) << 1);
     }
   }
   // Fragments of one 16-deep K half: 4 A tiles and 4 B tiles (two transpose
@@ -224,7 +263,7 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
     u32x2 lo[4], hi[4];
   };
   auto read_frag = [&](Frag& f, int st, int s) {
-    const uint32_t base = lds0 + st * STAGE;
+    const uint32_t base = lds0 + st * S::STAGE;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       f.lo[j] = lds_tr16(base + boff[s][j][0]);
@@ -263,7 +302,11 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
   issue(0, 0);
   issue(nk > 1 ? 1 : nk - 1, 1);
   issue(nk > 2 ? 2 : nk - 1, 2);
-  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  // "step kt+1 landed" = at most two later steps (2 * (QA + QB) loads) in flight
+  if constexpr (WM == 2)
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   Frag f0, f1;
   read_frag(f0, 0, 0);
@@ -271,7 +314,10 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
     read_frag(f1, kt % NSTAGE, 1);
     MOE_LGK_WAIT(f0, 12);
     mfma_frag(f0);
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    if constexpr (WM == 2)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     issue(kt + 3 < nk ? kt + 3 : nk - 1, (kt + 3) % NSTAGE);
     read_frag(f0, (kt + 1) % NSTAGE, 0);
@@ -305,7 +351,7 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
       for (int t = 0; t < 4; ++t) {  // 32 rows x 8 chunks of 16 B
         const int c = lane + 64 * t, rr = c >> 3, ch = c & 7;
         const int m = m0 + 128 * wm + 32 * i + rr;
-        const int col = nt * (TBN / 2) + 64 * wn + 8 * ch;
+        const int col = nt * (S::BN / 2) + 64 * wn + 8 * ch;
         const u32x4 v = *reinterpret_cast<const u32x4*>(strip + rr * 64 + 8 * ch);
         if (m < cnt && col < a.I)
           *reinterpret_cast<u32x4*>(a.h_out + (size_t)(r0 + m) * a.I + col) = v;
@@ -329,7 +375,7 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
       for (int t = 0; t < 16; ++t) {  // 32 rows x 32 chunks of 16 B
         const int c = lane + 64 * t, rr = c >> 5, ch = c & 31;
         const int m = m0 + 128 * wm + 32 * i + rr;
-        const int col = nt * TBN + 128 * wn + 4 * ch;
+        const int col = nt * S::BN + 128 * wn + 4 * ch;
         const f32x4 v = *reinterpret_cast<const f32x4*>(strip + rr * 128 + 4 * ch);
         if (m < cnt && col < N) *reinterpret_cast<f32x4*>(Yout + (size_t)(r0 + m) * N + col) = v;
       }
@@ -372,7 +418,7 @@ constexpr int ROUTER_NKS = 2;  // K slices per plane (3 * 2 splits in all)
 
 size_t expert_tile_ws_bytes(int P, int E) {
   const int max_tiles = (P + TBM - 1) / TBM + E;
-  return (size_t)(2 * max_tiles + 64) * sizeof(int32_t);
+  return (size_t)(2 * max_tiles + 2 * E + 64) * sizeof(int32_t);
 }
 
 int router_bf16x3_splits() { return 3 * ROUTER_NKS; }
@@ -395,7 +441,8 @@ hipError_t launch_router_bf16x3(const uint16_t* x, int T, int H, const float* w_
                                                                               offsets, T);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  tile_table_kernel<<<1, 256, 0, st>>>(offsets, 1, TBM, tile_e, tile_m0, n_tiles);
+  tile_table_kernel<<<1, 256, 0, st>>>(offsets, 1, TBM, 0, tile_e, tile_m0, n_tiles, nullptr,
+                                       nullptr, nullptr);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   StreamGemmArgs a{};
@@ -415,36 +462,43 @@ hipError_t launch_router_bf16x3(const uint16_t* x, int T, int H, const float* w_
   a.w_plane_stride = (long long)H * 256;
   a.y_split_stride = (long long)T * 256;
   const unsigned grid = (unsigned)(((max_tiles + 7) / 8) * 8);
-  tile_bf16_kernel<false><<<dim3(grid, a.nsplit), 256, 0, st>>>(a, tile_e, tile_m0, n_tiles, 1);
+  tile_bf16_kernel<false, 2><<<dim3(grid, a.nsplit), 256, 0, st>>>(a, tile_e, tile_m0, n_tiles, 1);
+  return hipGetLastError();
+}
+
+template <bool GATE_UP, int WM>
+static hipError_t launch_tiles(const StreamGemmArgs& g, const int32_t* te, const int32_t* tm,
+                               const int32_t* nt_p, int max_tiles, hipStream_t st) {
+  using S = TileShape<WM>;
+  const int NT = GATE_UP ? (g.I + S::BN / 2 - 1) / (S::BN / 2) : (g.N + S::BN - 1) / S::BN;
+  const long long items = (long long)max_tiles * NT;
+  const unsigned grid = (unsigned)(((items + 7) / 8) * 8);
+  if (grid == 0) return hipSuccess;
+  tile_bf16_kernel<GATE_UP, WM><<<grid, 256, 0, st>>>(g, te, tm, nt_p, NT);
   return hipGetLastError();
 }
 
 hipError_t launch_expert_tile(int wfmt, const StreamGemmArgs& gu, const StreamGemmArgs& dn, int P,
                               void* ws, hipStream_t st) {
   if (wfmt != W_BF16) return hipErrorInvalidValue;
-  const int max_tiles = (P + TBM - 1) / TBM + gu.E;
+  const int E = gu.E;
+  const int max_tiles = (P + TBM - 1) / TBM + E;
   int32_t* tile_e = static_cast<int32_t*>(ws);
   int32_t* tile_m0 = tile_e + max_tiles;
-  int32_t* n_tiles = tile_m0 + max_tiles;
-  tile_table_kernel<<<1, 256, 0, st>>>(gu.offsets, gu.E, TBM, tile_e, tile_m0, n_tiles);
+  int32_t* half_e = tile_m0 + max_tiles;
+  int32_t* half_m0 = half_e + E;
+  int32_t* counts = half_m0 + E;  // [0]: full tiles, [1]: half tiles
+  tile_table_kernel<<<1, 256, 0, st>>>(gu.offsets, E, TBM, 1, tile_e, tile_m0, counts, half_e,
+                                       half_m0, counts + 1);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  {
-    const int NT = (gu.I + TBN / 2 - 1) / (TBN / 2);
-    const long long items = (long long)max_tiles * NT;
-    const unsigned grid = (unsigned)(((items + 7) / 8) * 8);
-    tile_bf16_kernel<true><<<grid, 256, 0, st>>>(gu, tile_e, tile_m0, n_tiles, NT);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  {
-    const int NT = (dn.N + TBN - 1) / TBN;
-    const long long items = (long long)max_tiles * NT;
-    const unsigned grid = (unsigned)(((items + 7) / 8) * 8);
-    tile_bf16_kernel<false><<<grid, 256, 0, st>>>(dn, tile_e, tile_m0, n_tiles, NT);
-    err = hipGetLastError();
-  }
-  return err;
+  err = launch_tiles<true, 2>(gu, tile_e, tile_m0, counts, max_tiles, st);
+  if (err != hipSuccess) return err;
+  err = launch_tiles<true, 1>(gu, half_e, half_m0, counts + 1, E, st);
+  if (err != hipSuccess) return err;
+  err = launch_tiles<false, 2>(dn, tile_e, tile_m0, counts, max_tiles, st);
+  if (err != hipSuccess) return err;
+  return launch_tiles<false, 1>(dn, half_e, half_m0, counts + 1, E, st);
 }
 
 }  // namespace moe
