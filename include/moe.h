@@ -33,7 +33,7 @@
  *    error nothing is enqueued and a non-zero moe_status is returned. Device
  *    faults surface at the caller's next synchronisation.
  *  - Supported range: 1 <= k <= 8, k <= E <= 256, H and I multiples of 64,
- *    T >= 0 (T == 0 is a successful no-op), T*k < 2^31. Outside it the call
+ *    0 <= T < 2^24 (T == 0 is a successful no-op), T*k < 2^31. Outside it the call
  *    returns MOE_ERR_UNSUPPORTED.
  *  - Dtype combinations: x fp32 with fp32 expert weights (logits fp32), or
  *    x bf16 with bf16, FP8-E4M3 or NVFP4 expert weights. The router weights

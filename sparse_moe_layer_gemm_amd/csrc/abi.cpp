@@ -13,6 +13,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int64_t kMaxPairs = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxTokens = int64_t(1) << 24;  // one select workgroup per token
 
 size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -36,17 +37,18 @@ moe_status launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E
 moe_status check_shape(int64_t T, int32_t H, int32_t E, int32_t k) {
   if (T < 0 || H <= 0 || E <= 0 || k <= 0 || k > E) return MOE_ERR_INVALID_ARGUMENT;
   if (k > 8 || E > 256 || H % 64 != 0) return MOE_ERR_UNSUPPORTED;
-  if (T * k > kMaxPairs) return MOE_ERR_UNSUPPORTED;
+  if (T * k > kMaxPairs || T >= kMaxTokens) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
-// Router split plan: enough K slices that small batches still spread the
-// fp32 router weights over many workgroups; slices are multiples of 32.
-void router_plan(int64_t T, int32_t H, int* n_split, int* split_len) {
-  const int64_t row_tiles = (T + 63) / 64;
-  int64_t s = (256 + row_tiles - 1) / row_tiles;
+// Router split plan: enough K slices that the fp32 router GEMM spreads over
+// at least 256 workgroups (64 tokens x 64 experts each); slices are multiples
+// of 32 and there are at most 32 of them.
+void router_plan(int64_t T, int32_t H, int32_t E, int* n_split, int* split_len) {
+  const int64_t blocks = ((T + 63) / 64) * ((E + 63) / 64);
+  int64_t s = (256 + blocks - 1) / blocks;
   if (s < 1) s = 1;
-  if (s > 16) s = 16;
+  if (s > 32) s = 32;
   const int chunks = H / 32;
   if (s > chunks) s = chunks;
   const int per = (int)((chunks + s - 1) / s);
@@ -62,7 +64,7 @@ bool router_use_bf16x3(int32_t x_dtype, int64_t T) {
 
 size_t route_ws_bytes(int64_t T, int32_t H, int32_t E) {
   int S, L;
-  router_plan(T, H, &S, &L);
+  router_plan(T, H, E, &S, &L);
   size_t fp32_path = align_up((size_t)S * T * E * sizeof(float));
   size_t bf16x3_path = 0;
   if (T >= 1024)
@@ -122,7 +124,7 @@ moe_status enqueue_route(const void* x, int32_t x_dtype, int64_t T, int32_t H, c
                          void* logits, float* logits_f32, int32_t* ids, float* w, void* ws,
                          hipStream_t st) {
   int S, L;
-  router_plan(T, H, &S, &L);
+  router_plan(T, H, E, &S, &L);
   const bool x3 = router_use_bf16x3(x_dtype, T);
   const size_t part_bytes = x3 ? (size_t)moe::router_bf16x3_splits() * T * 256 * sizeof(float)
                                : (size_t)S * T * E * sizeof(float);
@@ -253,7 +255,7 @@ moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
   (void)workspace_bytes;
   if (T < 0 || E <= 0 || k <= 0 || k > E) return MOE_ERR_INVALID_ARGUMENT;
   if (k > 8 || E > 256) return MOE_ERR_UNSUPPORTED;
-  if (T * k > kMaxPairs) return MOE_ERR_UNSUPPORTED;
+  if (T * k > kMaxPairs || T >= kMaxTokens) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!topk_ids || !counts || !offsets || !sorted_pair || !pair_pos) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(topk_ids) || !aligned16(counts) || !aligned16(offsets) ||
@@ -296,7 +298,7 @@ moe_status moe_finalize(const float* y_sorted, const int32_t* pair_pos, const fl
   if (T < 0 || k <= 0 || H <= 0) return MOE_ERR_INVALID_ARGUMENT;
   if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
   if (k > 8 || H % 64 != 0) return MOE_ERR_UNSUPPORTED;
-  if (T * k > kMaxPairs) return MOE_ERR_UNSUPPORTED;
+  if (T * k > kMaxPairs || T >= kMaxTokens) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!y_sorted || !pair_pos || !topk_w || !out) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(y_sorted) || !aligned16(pair_pos) || !aligned16(topk_w) || !aligned16(out) ||

@@ -4,37 +4,48 @@
 // fp32 accumulation in slot order, then round-to-nearest-even to bf16.
 //
 // Bound by HBM: every fp32 expert row is read once and every output row
-// written once. One workgroup per token; the k row positions and weights are
-// wave-uniform (scalar loads), and each lane streams float4 columns.
+// written once. One workgroup per (token, 1024-column chunk) work item, so
+// that small batches still spread over the chip; the k row positions and weights are
+// wave-uniform (scalar loads), each lane issues its k float4 loads together
+// (rows past k repeat the first and are not added) and sums in slot order.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
+constexpr int FCOLS = 1024;  // columns per workgroup (256 lanes x float4)
+
 template <bool BF16_OUT>
 __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ y,
                                                        const int32_t* __restrict__ pair_pos,
                                                        const float* __restrict__ w, int k, int H,
+                                                       int n_chunks, long long n_items,
                                                        void* __restrict__ out,
                                                        float* __restrict__ out_f32) {
-  const int t = blockIdx.x;
-  int pos[8];
-  float wt[8];
+  for (long long item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const long long t = item / n_chunks;
+    const int c = (int)(item - t * n_chunks) * FCOLS + threadIdx.x * 4;
+    int pos[8];
+    float wt[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    pos[j] = (j < k) ? pair_pos[(size_t)t * k + j] : 0;
-    wt[j] = (j < k) ? w[(size_t)t * k + j] : 0.f;
-  }
-  for (int c = threadIdx.x * 4; c < H; c += 256 * 4) {
+    for (int j = 0; j < 8; ++j) {
+      pos[j] = pair_pos[t * k + (j < k ? j : 0)];
+      wt[j] = (j < k) ? w[t * k + j] : 0.f;
+    }
+    if (c >= H) continue;
+    float4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = *reinterpret_cast<const float4*>(y + (size_t)pos[j] * H + c);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (j >= k) break;
-      const float4 v = *reinterpret_cast<const float4*>(y + (size_t)pos[j] * H + c);
-      acc.x = fmaf(wt[j], v.x, acc.x);
-      acc.y = fmaf(wt[j], v.y, acc.y);
-      acc.z = fmaf(wt[j], v.z, acc.z);
-      acc.w = fmaf(wt[j], v.w, acc.w);
+      if (j < k) {
+        acc.x = fmaf(wt[j], v[j].x, acc.x);
+        acc.y = fmaf(wt[j], v[j].y, acc.y);
+        acc.z = fmaf(wt[j], v[j].z, acc.z);
+        acc.w = fmaf(wt[j], v[j].w, acc.w);
+      }
     }
     if (out_f32) *reinterpret_cast<float4*>(out_f32 + (size_t)t * H + c) = acc;
     if constexpr (BF16_OUT) {
@@ -53,10 +64,15 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
 hipError_t launch_finalize(const float* y_sorted, const int32_t* pair_pos, const float* w, int T,
                            int k, int H, bool out_bf16, void* out, float* out_f32,
                            hipStream_t st) {
+  const int n_chunks = (H + FCOLS - 1) / FCOLS;
+  const long long items = (long long)T * n_chunks;
+  const unsigned grid = (unsigned)(items < (1 << 20) ? items : (1 << 20));
   if (out_bf16)
-    finalize_kernel<true><<<T, 256, 0, st>>>(y_sorted, pair_pos, w, k, H, out, out_f32);
+    finalize_kernel<true><<<grid, 256, 0, st>>>(y_sorted, pair_pos, w, k, H, n_chunks, items, out,
+                                                out_f32);
   else
-    finalize_kernel<false><<<T, 256, 0, st>>>(y_sorted, pair_pos, w, k, H, out, out_f32);
+    finalize_kernel<false><<<grid, 256, 0, st>>>(y_sorted, pair_pos, w, k, H, n_chunks, items, out,
+                                                 out_f32);
   return hipGetLastError();
 }
 

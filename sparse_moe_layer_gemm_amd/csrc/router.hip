@@ -8,28 +8,32 @@
 namespace moe {
 namespace {
 
-constexpr int RBM = 64;   // tokens per workgroup
-constexpr int RBK = 32;   // K elements per LDS stage
-constexpr int XS_LD = RBM + 16;  // LDS row stride of the transposed x tile (conflict-free reads)
+constexpr int RBM = 64;  // tokens per workgroup
+constexpr int RBN = 64;  // experts per workgroup
+constexpr int RBK = 32;  // K per step
 
-// One workgroup = 4 wavefronts = 64 tokens x 256 expert columns (64 per wave)
-// over one K slice. fp32 MFMA 16x16x4: the B fragment is one fp32 per lane,
-// so W_r rows are read straight from global memory, 4 consecutive columns per
-// lane (one float4); the four columns feed four MFMAs whose output columns
-// are strided by 4. x is staged through LDS, transposed to [k][token].
+// One workgroup computes a 64-token x 64-expert block of partial logits over
+// one K slice; its four wavefronts take the slice's 32-deep steps in turn and
+// their sums are added in LDS in wave order. fp32 MFMA 16x16x4 with both
+// operands loaded straight into registers, one step ahead: in MFMA s of a step,
+// lane group g supplies k = k0 + 8g + s, so a lane's A values for the step are
+// 8 consecutive x elements (one 16-byte load for bf16) and its B values are
+// rows k0 + 8g + s of W_r at 4 consecutive columns (one float4 each); the four
+// columns feed four MFMAs whose output columns are strided by 4.
 template <bool XBF16>
 __global__ __launch_bounds__(256) void router_gemm_kernel(const void* __restrict__ xv, int T,
                                                           int H, const float* __restrict__ wr,
                                                           int E, int split_len,
                                                           float* __restrict__ part) {
-  __shared__ float xs[RBK][XS_LD];
+  __shared__ f32x4 red[4][16][64];  // per wave: 16 accumulator tiles x 64 lanes
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int kl = lane >> 4, jl = lane & 15;
-  const int m0 = blockIdx.x * RBM;
+  const int g = lane >> 4, jl = lane & 15;
+  const int m0 = blockIdx.x * RBM, n0 = blockIdx.z * RBN;
   const int s = blockIdx.y;
   const int kbeg = s * split_len;
   const int kend = min(H, kbeg + split_len);
-  const int c0 = wave * 64 + 4 * jl;  // this lane's first column
+  const int c0 = n0 + 4 * jl;  // this lane's first column
+  const bool col_ok = c0 < E;
   const bool vec_ok = (E % 4) == 0 && c0 + 3 < E;
 
   f32x4 acc[4][4];
@@ -38,80 +42,102 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const void* __restrict
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int lrow = tid >> 2, lk = (tid & 3) * 8;
-  const int lt = m0 + lrow;
-  for (int k0 = kbeg; k0 < kend; k0 += RBK) {
-    float v[8];
-    if (lt < T) {
+  // A rows of this lane (rows past T read row 0; their results are never stored)
+  const int arow[4] = {m0 + jl < T ? m0 + jl : 0, m0 + 16 + jl < T ? m0 + 16 + jl : 0,
+                       m0 + 32 + jl < T ? m0 + 32 + jl : 0, m0 + 48 + jl < T ? m0 + 48 + jl : 0};
+  float xa[4][8], xn[4][8];
+  float4 wa[8], wn[8];
+  auto load = [&](int k0, float (&xd)[4][8], float4 (&wd)[8]) {
+    const int kk = k0 + 8 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
       if constexpr (XBF16) {
-        const uint4 q = *reinterpret_cast<const uint4*>(
-            static_cast<const uint16_t*>(xv) + (size_t)lt * H + k0 + lk);
+        const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xv) +
+                                                        (size_t)arow[i] * H + kk);
         const uint32_t d[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[2 * i] = __uint_as_float(d[i] << 16);
-          v[2 * i + 1] = __uint_as_float(d[i] & 0xFFFF0000u);
+        for (int e = 0; e < 4; ++e) {
+          xd[i][2 * e] = __uint_as_float(d[e] << 16);
+          xd[i][2 * e + 1] = __uint_as_float(d[e] & 0xFFFF0000u);
         }
       } else {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(xv) +
-                                                          (size_t)lt * H + k0 + lk);
-        const float4 a = p[0], b = p[1];
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        const float4* p =
+            reinterpret_cast<const float4*>(static_cast<const float*>(xv) + (size_t)arow[i] * H + kk);
+        const float4 u = p[0], v = p[1];
+        xd[i][0] = u.x; xd[i][1] = u.y; xd[i][2] = u.z; xd[i][3] = u.w;
+        xd[i][4] = v.x; xd[i][5] = v.y; xd[i][6] = v.z; xd[i][7] = v.w;
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.f;
     }
-    __syncthreads();  // previous stage's readers are done
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xs[lk + i][lrow] = v[i];
-    __syncthreads();
+    for (int e = 0; e < 8; ++e) {
+      const float* wrow = wr + (size_t)(kk + e) * E;
+      if (vec_ok) {
+        wd[e] = *reinterpret_cast<const float4*>(wrow + c0);
+      } else {
+        wd[e].x = (c0 < E) ? wrow[c0] : 0.f;
+        wd[e].y = (c0 + 1 < E) ? wrow[c0 + 1] : 0.f;
+        wd[e].z = (c0 + 2 < E) ? wrow[c0 + 2] : 0.f;
+        wd[e].w = (c0 + 3 < E) ? wrow[c0 + 3] : 0.f;
+      }
+    }
+  };
 
-    if (wave * 64 < E) {
-#pragma unroll 2
-      for (int st = 0; st < RBK / 4; ++st) {
-        const int kk = k0 + st * 4 + kl;
-        const float* wrow = wr + (size_t)kk * E;
-        float b[4];
-        if (vec_ok) {
-          const float4 q = *reinterpret_cast<const float4*>(wrow + c0);
-          b[0] = q.x; b[1] = q.y; b[2] = q.z; b[3] = q.w;
-        } else {
+  int k0 = kbeg + wave * RBK;
+  if (k0 < kend) {
+    load(k0, xa, wa);
+    for (; k0 < kend; k0 += 4 * RBK) {
+      const int kn = (k0 + 4 * RBK < kend) ? k0 + 4 * RBK : k0;  // last step reloads itself
+      load(kn, xn, wn);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) b[q] = (c0 + q < E) ? wrow[c0 + q] : 0.f;
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float b[4] = {wa[e].x, wa[e].y, wa[e].z, wa[e].w};
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const float a = xs[st * 4 + kl][rt * 16 + jl];
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            acc[rt][q] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b[q], acc[rt][q], 0, 0, 0);
-        }
+            acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[i][e], b[q], acc[i][q], 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        wa[e] = wn[e];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xa[i][e] = xn[i][e];
       }
     }
   }
 
-  // D layout: lane (kl, jl) holds rows 4*kl + r of column jl of each 16x16 tile;
-  // MFMA q's column jl is global column c0 + q.
-  if (wave * 64 >= E || c0 >= E) return;
+  // add the four wavefronts' sums in wave order
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) red[wave][4 * i + q][lane] = acc[i][q];
+  __syncthreads();
+  // thread (wave, lane) finishes tiles 4*wave .. 4*wave+3 of lane `lane`
+  // D layout: lane (g, jl) holds rows 4g + r of column jl of each 16x16 tile;
+  // tile (i, q)'s column jl is global column c0 + q.
+  const int i = wave;
+  f32x4 v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[q] = red[0][4 * i + q][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v[q] += red[w][4 * i + q][lane];
+  }
+  if (!col_ok) return;
   float* dst = part + (size_t)s * T * E;
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int r = 0; r < 4; ++r) {
+    const int t = m0 + 16 * i + 4 * g + r;
+    if (t >= T) continue;
+    float* o = dst + (size_t)t * E + c0;
+    if (vec_ok) {
+      *reinterpret_cast<float4*>(o) = make_float4(v[0][r], v[1][r], v[2][r], v[3][r]);
+    } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = m0 + rt * 16 + 4 * kl + r;
-      if (t >= T) continue;
-      float* o = dst + (size_t)t * E + c0;
-      if (vec_ok) {
-        *reinterpret_cast<float4*>(o) =
-            make_float4(acc[rt][0][r], acc[rt][1][r], acc[rt][2][r], acc[rt][3][r]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (c0 + q < E) o[q] = acc[rt][q][r];
-      }
+      for (int q = 0; q < 4; ++q)
+        if (c0 + q < E) o[q] = v[q][r];
     }
+  }
 }
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
@@ -120,73 +146,89 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// One wavefront per token; lane l holds experts l, l+64, l+128, l+192.
-// The selection key packs (order-preserving logit, 0xFFFF - id) so that a
-// wave-wide max picks the largest logit and, on equal logits, the lowest id.
+// One workgroup per token; wavefront w owns experts 64w .. 64w+63, one per
+// lane, and adds that expert's split partials (all loads in flight at once),
+// the bias, and rounds to the logits dtype. The selection key packs
+// (order-preserving logit, 0xFFFF - id), so a maximum picks the largest logit
+// and, on equal logits, the lowest id. Each wavefront finds its own 8 largest
+// keys; wavefront 0 merges the 32 candidates into the token's top k.
 template <bool BF16_LOGITS>
 __global__ __launch_bounds__(256) void router_select_kernel(
     const float* __restrict__ part, int n_split, int ldp, int T, int E, int k,
     const float* __restrict__ bias, void* __restrict__ logits, float* __restrict__ logits_f32,
     int32_t* __restrict__ ids, float* __restrict__ w) {
+  __shared__ uint64_t cand[4][8];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= T) return;
-  uint64_t key[4];
+  const int t = blockIdx.x;
+  const int e = 64 * wave + lane;
+  uint64_t key = 0;
+  if (e < E) {
+    const float* p = part + (size_t)t * ldp + e;
+    const size_t sstride = (size_t)T * ldp;
+    float v = 0.f;
+    int sp = 0;
+    for (; sp + 8 <= n_split; sp += 8) {
+      float u[8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + 64 * q;
-    key[q] = 0;
-    if (e < E) {
-      float v = 0.f;
-      for (int s = 0; s < n_split; ++s) v += part[((size_t)s * T + t) * ldp + e];
-      if (bias) v += bias[e];
-      if (logits_f32) logits_f32[(size_t)t * E + e] = v;
-      float sv = v;
-      if constexpr (BF16_LOGITS) {
-        const uint32_t b = f32_to_bf16_bits(v);
-        static_cast<uint16_t*>(logits)[(size_t)t * E + e] = (uint16_t)b;
-        sv = bf16_bits_to_f32(b);
-      } else {
-        static_cast<float*>(logits)[(size_t)t * E + e] = v;
-      }
-      key[q] = ((uint64_t)float_order_key(sv) << 32) | (uint32_t)(0xFFFF - e);
+      for (int j = 0; j < 8; ++j) u[j] = p[(size_t)(sp + j) * sstride];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v += u[j];
     }
+    for (; sp < n_split; ++sp) v += p[(size_t)sp * sstride];
+    if (bias) v += bias[e];
+    if (logits_f32) logits_f32[(size_t)t * E + e] = v;
+    float sv = v;
+    if constexpr (BF16_LOGITS) {
+      const uint32_t b = f32_to_bf16_bits(v);
+      static_cast<uint16_t*>(logits)[(size_t)t * E + e] = (uint16_t)b;
+      sv = bf16_bits_to_f32(b);
+    } else {
+      static_cast<float*>(logits)[(size_t)t * E + e] = v;
+    }
+    key = ((uint64_t)float_order_key(sv) << 32) | (uint32_t)(0xFFFF - e);
   }
+  // this wavefront's 8 largest keys, in decreasing order (0 where it has fewer)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint64_t best = key;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const uint64_t o = shfl_xor_u64(best, m);
+      best = o > best ? o : best;
+    }
+    if (key == best) key = 0;
+    if (lane == 0) cand[wave][j] = best;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  uint64_t c = (lane < 32) ? cand[lane >> 3][lane & 7] : 0;
   float topv[8];
   int topi[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    topv[j] = 0.f;
-    topi[j] = 0;
-    if (j < k) {
-      uint64_t best = key[0];
+    uint64_t best = c;
 #pragma unroll
-      for (int q = 1; q < 4; ++q) best = key[q] > best ? key[q] : best;
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const uint64_t o = shfl_xor_u64(best, m);
-        best = o > best ? o : best;
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (key[q] == best) key[q] = 0;
-      topi[j] = 0xFFFF - (int)(best & 0xFFFFu);
-      topv[j] = float_from_order_key((uint32_t)(best >> 32));
+    for (int m = 16; m >= 1; m >>= 1) {
+      const uint64_t o = shfl_xor_u64(best, m);
+      best = o > best ? o : best;
     }
+    if (c == best) c = 0;
+    topi[j] = 0xFFFF - (int)(best & 0xFFFFu);
+    topv[j] = float_from_order_key((uint32_t)(best >> 32));
   }
   if (lane == 0) {
     // softmax over all E, restricted to the chosen set: the normaliser cancels
-    float p[8], z = 0.f;
+    float pr[8], z = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      p[j] = (j < k) ? expf(topv[j] - topv[0]) : 0.f;
-      z += p[j];
+      pr[j] = (j < k) ? expf(topv[j] - topv[0]) : 0.f;
+      z += pr[j];
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       if (j < k) {
         ids[(size_t)t * k + j] = topi[j];
-        w[(size_t)t * k + j] = p[j] / z;
+        w[(size_t)t * k + j] = pr[j] / z;
       }
   }
 }
@@ -195,7 +237,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
 
 hipError_t launch_router_gemm(const void* x, bool x_bf16, int T, int H, const float* w_router,
                               int E, int n_split, int split_len, float* part, hipStream_t st) {
-  dim3 grid((T + RBM - 1) / RBM, n_split);
+  dim3 grid((T + RBM - 1) / RBM, n_split, (E + RBN - 1) / RBN);
   if (x_bf16)
     router_gemm_kernel<true><<<grid, 256, 0, st>>>(x, T, H, w_router, E, split_len, part);
   else
@@ -206,13 +248,12 @@ hipError_t launch_router_gemm(const void* x, bool x_bf16, int T, int H, const fl
 hipError_t launch_router_select(const float* part, int n_split, int ldp, int T, int E, int k,
                                 const float* bias, bool logits_bf16, void* logits,
                                 float* logits_f32, int32_t* ids, float* w, hipStream_t st) {
-  dim3 grid((T + 3) / 4);
   if (logits_bf16)
-    router_select_kernel<true><<<grid, 256, 0, st>>>(part, n_split, ldp, T, E, k, bias, logits,
-                                                     logits_f32, ids, w);
+    router_select_kernel<true><<<T, 256, 0, st>>>(part, n_split, ldp, T, E, k, bias, logits,
+                                                  logits_f32, ids, w);
   else
-    router_select_kernel<false><<<grid, 256, 0, st>>>(part, n_split, ldp, T, E, k, bias, logits,
-                                                      logits_f32, ids, w);
+    router_select_kernel<false><<<T, 256, 0, st>>>(part, n_split, ldp, T, E, k, bias, logits,
+                                                   logits_f32, ids, w);
   return hipGetLastError();
 }
 

@@ -69,6 +69,7 @@ def test_route_validation():
     assert route(x=MIS) == INVAL
     assert route(ws_bytes=16) == WS_SMALL
     assert route(T=(1 << 31) // 8) == UNSUP
+    assert route(T=1 << 24, k=1) == UNSUP  # token limit
 
 
 def test_route_workspace_size_positive():
