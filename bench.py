@@ -6,10 +6,12 @@ GEMMs, finalize) over one batch of synthetic input already resident in HBM.
 The headline workload is decode (T=128 tokens, bf16 weights, near-uniform
 routing), bound by streaming the touched experts' weights from HBM; prefill
 (T=16384 = 8 x 2048 tokens, Zipf(1.1) expert load) is reported beside it
-against the bf16 MFMA peak.
+against the bf16 MFMA peak, and the NVFP4-weight layer (T=4096) against the
+bound it is closer to (HBM bytes or bf16 MFMA).
 
 Prints one JSON line. Options: --gpus N (only 1 is supported), --steps K,
---warmup W, --workload decode|prefill (headline), --no-prefill, --no-cpu.
+--warmup W, --workload decode|prefill (headline), --no-prefill, --no-quant,
+--no-cpu.
 """
 from __future__ import annotations
 
@@ -36,6 +38,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", choices=["decode", "prefill"], default="decode")
     p.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill line")
+    p.add_argument("--no-quant", action="store_true", help="skip the secondary NVFP4 line")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--hbm-probe", action="store_true",
                    help="time a plain 4 GiB device copy (the reference kernel for HBM counters) and exit")
@@ -181,8 +184,13 @@ def hbm_probe(torch):
 
 
 def expert_bytes(cfg):
-    """Bytes of one expert's bf16 weights: gate/up [H, 2I] + down [I, H]."""
-    return 2 * (cfg.H * 2 * cfg.I + cfg.I * cfg.H)
+    """Bytes of one expert's weights: gate/up [H, 2I] + down [I, H] (with scales)."""
+    n = cfg.H * 2 * cfg.I + cfg.I * cfg.H
+    if cfg.w_dtype == "fp4":
+        return n // 2 + n // 16 + 2 * 4  # E2M1 codes, one E4M3 scale per 16, two global scales
+    if cfg.w_dtype == "fp8":
+        return n + 4 * (2 * cfg.I + cfg.H)  # E4M3 codes, one fp32 scale per output channel
+    return 2 * n
 
 
 def cpu_baseline(wl, budget_s=10.0):
@@ -267,6 +275,34 @@ def main():
         }
         pre_line["roofline"]["frac"] = pre_line["roofline"]["achieved"] / BF16_PEAK_TFLOPS
 
+    q_cfg = synth.CONFIGS["nvfp4_t4096"]
+    q_line = None
+    if a.workload == "decode" and not a.no_quant:
+        progress("generating NVFP4 inputs (T=4096)")
+        qw = Workload(q_cfg, moe, torch)
+        progress("timing NVFP4")
+        qsteps = max(3, a.steps // 2)
+        q_ms = qw.time_forward(qsteps, max(1, a.warmup // 2))
+        q_stage = qw.time_stages(qsteps)
+        qc = qw.touched()
+        P = q_cfg.T * q_cfg.k
+        flops = 2.0 * P * 3 * q_cfg.H * q_cfg.I
+        wbytes = int((qc > 0).sum()) * expert_bytes(q_cfg)
+        tb = wbytes / (q_stage["experts"] / 1e3) / 1e9
+        tf = flops / (q_stage["experts"] / 1e3) / 1e12
+        hbm_frac, mfma_frac = tb / HBM_PEAK_GBS, tf / BF16_PEAK_TFLOPS
+        q_line = {"workload": q_cfg.name, "value": round(q_cfg.T / (q_ms / 1e3), 1),
+                  "unit": "tokens/s", "ms_per_step": round(q_ms, 4),
+                  "stages_ms": {k: round(v, 4) for k, v in q_stage.items()},
+                  "roofline": {"bound": "hbm" if hbm_frac >= mfma_frac else "mfma",
+                               "kernel": "moe_experts (NVFP4 weights, bf16 MFMA)",
+                               "achieved": tb if hbm_frac >= mfma_frac else tf,
+                               "peak": HBM_PEAK_GBS if hbm_frac >= mfma_frac else BF16_PEAK_TFLOPS,
+                               "unit": "GB/s" if hbm_frac >= mfma_frac else "TFLOP/s",
+                               "frac": max(hbm_frac, mfma_frac), "traffic": None,
+                               "weight_GBps": round(tb, 1), "TFLOPs": round(tf, 1)}}
+        del qw
+
     head, head_cfg = (dec_line, dec_cfg) if a.workload == "decode" else (pre_line, pre_cfg)
     cpu = None
     if not a.no_cpu:
@@ -304,6 +340,8 @@ def main():
                                "roofline": pre_line["roofline"],
                                "stages_ms": {k: round(v, 4) for k, v in pre_line["stages_ms"].items()},
                                "expert_load": pre_line["expert_load"]}
+        if q_line is not None:
+            line["quantised"] = q_line
     else:
         line["expert_load"] = pre_line["expert_load"]
         line["layer_mfma_frac"] = round(pre_line["layer_mfma_frac"], 4)

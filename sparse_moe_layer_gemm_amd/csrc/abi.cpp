@@ -111,10 +111,10 @@ size_t experts_ws_bytes(int64_t T, int32_t I, int32_t E, int32_t k, int32_t w_dt
   return align_up(P * I * h_elem) + align_up(moe::expert_tile_ws_bytes((int)P, E));
 }
 
-// The tiled grouped GEMM pays off once experts average enough rows to fill
-// its 128-row tiles; below that, streaming each weight once per 32 rows wins.
+// The tiled grouped GEMMs pay off once experts average enough rows to fill
+// their 128-row tiles; below that, streaming each weight once per 32 rows wins.
 bool use_tile_kernel(int32_t w_dtype, int64_t P, int32_t E) {
-  return w_dtype == MOE_BF16 && P >= (int64_t)moe::kTileMinRowsPerExpert * E;
+  return w_dtype != MOE_F32 && P >= (int64_t)moe::kTileMinRowsPerExpert * E;
 }
 
 // -------------------------------------------------------------- enqueue helpers

@@ -387,6 +387,373 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
 }
 
 
+// ------------------------------------------------------------------ FP8 / NVFP4 weights
+// Same tiling for K-contiguous quantised weights ([E, N, K] E4M3 codes, or
+// [E, N, K/2] E2M1 codes with one E4M3 scale per 16 K values): per K step a
+// column's codes (16 B for E2M1, 32 B for E4M3) and, for E2M1, the dword of
+// block scales holding this step's two come in by direct loads next to the A
+// tile. B fragments are read as one contiguous run per lane and converted to
+// bf16 in registers: E4M3 -> bf16 is exact in the hardware converter; for
+// E2M1 the converter applies the power of two of the E4M3 block scale and an
+// fp32 multiply the scale's mantissa factor (the product has at most 6
+// significant bits, so it is exact, as is its bf16 upper half). Per-channel
+// (E4M3) and per-expert (E2M1) fp32 scales multiply the accumulators in the
+// epilogue. Within a K step, lane half kh takes K 16*kh .. 16*kh+15 (MFMA s
+// the 8 from 16*kh + 8*s), so a lane's codes are contiguous and, for E2M1,
+// each lane needs a single block scale per step.
+template <int WF, int WM>
+struct QShape {
+  using T = TileShape<WM>;
+  static constexpr int BM = T::BM, BN = T::BN, WN = T::WN;
+  static constexpr int COL = WF == W_FP4 ? 16 : 32;   // code bytes per column per K step
+  static constexpr int SCL = WF == W_FP4 ? 4 : 0;     // scale bytes per column per K step
+  static constexpr int A_STAGE = T::A_STAGE;
+  static constexpr int B_STAGE = BN * COL;
+  static constexpr int S_STAGE = BN * SCL;
+  static constexpr int STAGE = A_STAGE + B_STAGE + S_STAGE;
+  static constexpr int PIPE = NSTAGE * STAGE;
+  static constexpr int EPI = 65536;                   // epilogue strips (4 x 16 KB)
+  static constexpr int LDS = PIPE > EPI ? PIPE : EPI;
+  static constexpr int QA = T::QA;
+  static constexpr int QB = B_STAGE / 4096;           // 1 KB code loads per wavefront
+  static constexpr int QS = S_STAGE / 1024;           // 256 B scale loads per wavefront
+  static constexpr int PER_STEP = QA + QB + QS;       // loads per wavefront per K step
+  static_assert(PER_STEP == 6, "the waits below assume 6 loads per K step");
+};
+
+__device__ __forceinline__ u32x2 lds_b64(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+// raw codes of one column per lane per K step: 8 B (E2M1) or 16 B (E4M3)
+template <int WF> struct QRaw { typedef u32x4 type; };
+template <> struct QRaw<W_FP4> { typedef u32x2 type; };
+__device__ __forceinline__ uint32_t lds_byte(uint32_t addr) {
+  uint32_t r;
+  asm volatile("ds_read_u8 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+// dword direct load: lane l's 4 bytes land at lds + 4 * l
+__device__ __forceinline__ void dma4(const void* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
+}
+
+// E4M3 block scale -> (power of two, mantissa factor) as fp32; subnormal
+// scales m * 2^-9 become (2^-9, m), zero becomes a zero factor.
+__device__ __forceinline__ void e4m3_split(uint32_t c, float& p2, float& fm) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const bool normal = e != 0u;
+  p2 = __uint_as_float(normal ? (e + 120u) << 23 : 118u << 23);
+  const float f = normal ? __uint_as_float(0x3F800000u | (m << 20)) : (float)m;
+  fm = (c & 0x80u) ? -f : f;
+}
+
+// 8 E2M1 codes (one dword, even K in the low nibble) x block scale -> bf16 fragment
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// two scaled codes -> packed bf16 (upper halves of the exact fp32 products)
+__device__ __forceinline__ uint32_t fp4_pair(f32x2 v, float fm) {
+  return __builtin_amdgcn_perm(__float_as_uint(v.y * fm), __float_as_uint(v.x * fm), 0x07060302u);
+}
+__device__ __forceinline__ u32x4 fp4_frag(uint32_t d, float p2, float fm) {
+  u32x4 r;
+  r[0] = fp4_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 0), fm);
+  r[1] = fp4_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 1), fm);
+  r[2] = fp4_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 2), fm);
+  r[3] = fp4_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 3), fm);
+  return r;
+}
+// 8 E4M3 codes (two dwords) -> bf16 fragment (exact)
+__device__ __forceinline__ u32x4 fp8_frag(uint32_t d0, uint32_t d1) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true));
+  return r;
+}
+
+template <int WF, bool GATE_UP, int WM>
+__global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
+                                                        const int32_t* __restrict__ tile_e,
+                                                        const int32_t* __restrict__ tile_m0,
+                                                        const int32_t* __restrict__ n_tiles_p,
+                                                        int NT) {
+  using S = QShape<WF, WM>;
+  __shared__ __align__(1024) uint8_t smem[S::LDS];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave / S::WN, wn = wave % S::WN;
+
+  const int total = *n_tiles_p * NT;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int per = (total + 7) >> 3;
+  if (slot >= per) return;
+  const int w = xcd * per + slot;
+  if (w >= total) return;
+  const int mt = w / NT, nt = w - mt * NT;
+  const int e = tile_e[mt];
+  const int m0 = tile_m0[mt];
+  const int r0 = a.offsets[e];
+  const int cnt = a.offsets[e + 1] - r0;
+  const int K = a.K, N = a.N;
+
+  // A: as in the bf16 kernel (gathered rows, 16 rows per 1 KB load)
+  const uint16_t* asrc[S::QA];
+#pragma unroll
+  for (int q = 0; q < S::QA; ++q) {
+    const int row = (S::BM / 4) * wave + 16 * q + (lane >> 2);
+    const int lg = (lane & 3) ^ ((row >> 2) & 3);
+    size_t grow = 0;
+    if (m0 + row < cnt)
+      grow = GATE_UP ? (size_t)(a.sorted_pair[r0 + m0 + row] / a.k) : (size_t)(r0 + m0 + row);
+    asrc[q] = a.a + grow * K + 8 * lg;
+  }
+  // matrix column of LDS column c (gate/up: BN/2 gate, then the matching up)
+  auto mcol = [&](int c) -> int {
+    if (GATE_UP) {
+      const int gc = nt * (S::BN / 2) + (c < S::BN / 2 ? c : c - S::BN / 2);
+      if (gc >= a.I) return 0;  // clamped: feeds accumulators never stored
+      return c < S::BN / 2 ? gc : a.I + gc;
+    }
+    const int col = nt * S::BN + c;
+    return col < N ? col : 0;
+  };
+  const uint8_t* wq = static_cast<const uint8_t*>(a.w);
+  const size_t row_bytes = WF == W_FP4 ? (size_t)K / 2 : (size_t)K;
+  // codes: fp4 load q covers LDS columns 64*qi .. +63 (16 B each); fp8 load q
+  // covers 32 columns (two 16 B halves each)
+  const uint8_t* bsrc[S::QB];
+#pragma unroll
+  for (int q = 0; q < S::QB; ++q) {
+    const int qi = wave * S::QB + q;
+    if (WF == W_FP4) {
+      bsrc[q] = wq + ((size_t)e * N + mcol(64 * qi + lane)) * row_bytes;
+    } else {
+      bsrc[q] = wq + ((size_t)e * N + mcol(32 * qi + (lane >> 1))) * row_bytes + 16 * (lane & 1);
+    }
+  }
+  const uint8_t* ssrc[S::QS > 0 ? S::QS : 1];
+#pragma unroll
+  for (int q = 0; q < S::QS; ++q) {
+    const int qi = wave * S::QS + q;
+    ssrc[q] = static_cast<const uint8_t*>(a.w_scale) +
+              ((size_t)e * N + mcol(64 * qi + lane)) * (size_t)(K / 16);
+  }
+  auto issue = [&](int kt, int st) {
+    uint8_t* As = smem + st * S::STAGE;
+    uint8_t* Bs = As + S::A_STAGE;
+    uint8_t* Ss = Bs + S::B_STAGE;
+    const int k0 = kt * TBK;
+#pragma unroll
+    for (int q = 0; q < S::QA; ++q) dma16(asrc[q] + k0, As + ((S::BM / 4) * wave + 16 * q) * 64);
+#pragma unroll
+    for (int q = 0; q < S::QB; ++q) {
+      const int qi = wave * S::QB + q;
+      if (WF == W_FP4)
+        dma16(bsrc[q] + 16 * kt, Bs + 64 * qi * 16);
+      else
+        dma16(bsrc[q] + 32 * kt, Bs + 32 * qi * 32);
+    }
+#pragma unroll
+    for (int q = 0; q < S::QS; ++q) {
+      const int qi = wave * S::QS + q;
+      dma4(ssrc[q] + ((2 * kt) & ~3), Ss + 64 * qi * 4);
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto bcol = [&](int j) -> int {
+    if (GATE_UP) return (j < 2) ? 64 * wn + 32 * j : S::BN / 2 + 64 * wn + 32 * (j - 2);
+    return 128 * wn + 32 * j;
+  };
+  const int l32 = lane & 31, kh = lane >> 5;
+  const uint32_t lds0 = (uint32_t)(size_t)(lds_u8*)smem;
+  uint32_t aoff[2][4], boff[4], soff[4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) aoff[s][i] = a_off(128 * wm + 32 * i + l32, 2 * kh + s);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = bcol(j) + l32;
+    boff[j] = S::A_STAGE + c * S::COL + (S::COL / 2) * kh;
+    soff[j] = S::A_STAGE + S::B_STAGE + c * 4 + kh;
+  }
+  // first half of a K step: A (K half 0), the codes and the block scales;
+  // second half: A (K half 1)
+  struct FragQ0 {
+    u32x4 a[4];
+    typename QRaw<WF>::type b[4];
+    uint32_t sc[4];
+  };
+  struct FragQ1 {
+    u32x4 a[4];
+  };
+  auto read0 = [&](FragQ0& f, int st, int kt) {
+    const uint32_t base = lds0 + st * S::STAGE;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (WF == W_FP4)
+        f.b[j] = lds_b64(base + boff[j]);
+      else
+        f.b[j] = lds_b128(base + boff[j]);
+    }
+    if (WF == W_FP4) {
+      const uint32_t sh = 2 * (kt & 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f.sc[j] = lds_byte(base + soff[j] + sh);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = lds_b128(base + aoff[0][i]);
+  };
+  auto read1 = [&](FragQ1& f, int st) {
+    const uint32_t base = lds0 + st * S::STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = lds_b128(base + aoff[1][i]);
+  };
+#define MOE_LGK_WAIT0(f, pending)                                                              \
+  asm volatile("s_waitcnt lgkmcnt(" #pending ")"                                              \
+               : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0]),         \
+                 "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3]), "+v"(f.sc[0]), "+v"(f.sc[1]),       \
+                 "+v"(f.sc[2]), "+v"(f.sc[3])                                                  \
+               :                                                                               \
+               : "memory")
+#define MOE_LGK_WAIT1(f, pending)                                                              \
+  asm volatile("s_waitcnt lgkmcnt(" #pending ")"                                              \
+               : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3])                        \
+               :                                                                               \
+               : "memory")
+  // codes of both K halves -> bf16 fragments
+  u32x4 bq[2][4];
+  auto dequant = [&](const FragQ0& f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (WF == W_FP4) {
+        float p2, fm;
+        e4m3_split(f.sc[j], p2, fm);
+        bq[0][j] = fp4_frag(f.b[j][0], p2, fm);
+        bq[1][j] = fp4_frag(f.b[j][1], p2, fm);
+      } else {
+        bq[0][j] = fp8_frag(f.b[j][0], f.b[j][1]);
+        bq[1][j] = fp8_frag(f.b[j][2], f.b[j][3]);
+      }
+    }
+  };
+  auto mfma_half = [&](const u32x4 (&af)[4], int s) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i][j] = mfma32(af[i], bq[s][j], acc[i][j]);
+  };
+  // Pipeline as in the bf16 kernel: "step kt+1 landed" is vmcnt(6) once three
+  // steps are in flight; f1 (4 reads) is read while f0's MFMAs run, f0 of the
+  // next step (8 or 12 reads) while f1's run.
+  const int nk = K / TBK;
+  issue(0, 0);
+  issue(nk > 1 ? 1 : nk - 1, 1);
+  issue(nk > 2 ? 2 : nk - 1, 2);
+  asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  FragQ0 f0;
+  FragQ1 f1;
+  read0(f0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    read1(f1, kt % NSTAGE);
+    MOE_LGK_WAIT0(f0, 4);
+    dequant(f0);
+    mfma_half(f0.a, 0);
+    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    issue(kt + 3 < nk ? kt + 3 : nk - 1, (kt + 3) % NSTAGE);
+    read0(f0, (kt + 1) % NSTAGE, kt + 1);
+    if (WF == W_FP4)
+      MOE_LGK_WAIT1(f1, 12);
+    else
+      MOE_LGK_WAIT1(f1, 8);
+    mfma_half(f1.a, 1);
+  }
+  MOE_LGK_WAIT0(f0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#undef MOE_LGK_WAIT0
+#undef MOE_LGK_WAIT1
+  __builtin_amdgcn_s_barrier();
+
+  // ---- epilogue through LDS, scales applied first
+  const float gsc = WF == W_FP4 ? a.w_gscale[e] : 1.f;
+  const float* chs = WF == W_FP8 ? static_cast<const float*>(a.w_scale) + (size_t)e * N : nullptr;
+  auto tile_row = [&](int r) { return 8 * (r >> 2) + 4 * kh + (r & 3); };
+  if (GATE_UP) {
+    float sg[2], su[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (WF == W_FP8) {
+        sg[j] = chs[mcol(bcol(j) + l32)];
+        su[j] = chs[mcol(bcol(j + 2) + l32)];
+      } else {
+        sg[j] = su[j] = gsc;
+      }
+    }
+    uint16_t* strip = reinterpret_cast<uint16_t*>(smem + wave * 4096);  // 32 x 64 bf16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          strip[tile_row(r) * 64 + 32 * j + l32] = (uint16_t)f32_to_bf16_bits(
+              silu(acc[i][j][r] * sg[j]) * (acc[i][j + 2][r] * su[j]));
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int c = lane + 64 * t, rr = c >> 3, ch = c & 7;
+        const int m = m0 + 128 * wm + 32 * i + rr;
+        const int col = nt * (S::BN / 2) + 64 * wn + 8 * ch;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(strip + rr * 64 + 8 * ch);
+        if (m < cnt && col < a.I)
+          *reinterpret_cast<u32x4*>(a.h_out + (size_t)(r0 + m) * a.I + col) = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  } else {
+    float sd[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sd[j] = WF == W_FP8 ? chs[mcol(bcol(j) + l32)] : gsc;
+    float* strip = reinterpret_cast<float*>(smem + wave * 16384);  // 32 x 128 fp32
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) strip[tile_row(r) * 128 + 32 * j + l32] = acc[i][j][r] * sd[j];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int c = lane + 64 * t, rr = c >> 5, ch = c & 31;
+        const int m = m0 + 128 * wm + 32 * i + rr;
+        const int col = nt * S::BN + 128 * wn + 4 * ch;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(strip + rr * 128 + 4 * ch);
+        if (m < cnt && col < N) *reinterpret_cast<f32x4*>(a.y_out + (size_t)(r0 + m) * N + col) = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+}
+
 // fp32 router weights [H, E] -> three bf16 planes [3][H][256] (columns >= E zero):
 // hi = RNE(w), mid = RNE(w - hi), lo = RNE(w - hi - mid); both differences are
 // exact in fp32. Also writes the one-expert offsets {0, T} the tiled kernel uses.
@@ -478,9 +845,41 @@ static hipError_t launch_tiles(const StreamGemmArgs& g, const int32_t* te, const
   return hipGetLastError();
 }
 
+template <int WF, bool GATE_UP, int WM>
+static hipError_t launch_q(const StreamGemmArgs& g, const int32_t* te, const int32_t* tm,
+                           const int32_t* nt_p, int max_tiles, hipStream_t st) {
+  using S = QShape<WF, WM>;
+  const int NT = GATE_UP ? (g.I + S::BN / 2 - 1) / (S::BN / 2) : (g.N + S::BN - 1) / S::BN;
+  const long long items = (long long)max_tiles * NT;
+  const unsigned grid = (unsigned)(((items + 7) / 8) * 8);
+  if (grid == 0) return hipSuccess;
+  tile_q_kernel<WF, GATE_UP, WM><<<grid, 256, 0, st>>>(g, te, tm, nt_p, NT);
+  return hipGetLastError();
+}
+
+template <int WF>
+static hipError_t launch_all(const StreamGemmArgs& gu, const StreamGemmArgs& dn,
+                             const int32_t* tile_e, const int32_t* tile_m0, const int32_t* half_e,
+                             const int32_t* half_m0, const int32_t* counts, int max_tiles,
+                             hipStream_t st) {
+  const int E = gu.E;
+  hipError_t err;
+  if constexpr (WF == W_BF16) {
+    err = launch_tiles<true, 2>(gu, tile_e, tile_m0, counts, max_tiles, st);
+    if (err == hipSuccess) err = launch_tiles<true, 1>(gu, half_e, half_m0, counts + 1, E, st);
+    if (err == hipSuccess) err = launch_tiles<false, 2>(dn, tile_e, tile_m0, counts, max_tiles, st);
+    if (err == hipSuccess) err = launch_tiles<false, 1>(dn, half_e, half_m0, counts + 1, E, st);
+  } else {
+    err = launch_q<WF, true, 2>(gu, tile_e, tile_m0, counts, max_tiles, st);
+    if (err == hipSuccess) err = launch_q<WF, true, 1>(gu, half_e, half_m0, counts + 1, E, st);
+    if (err == hipSuccess) err = launch_q<WF, false, 2>(dn, tile_e, tile_m0, counts, max_tiles, st);
+    if (err == hipSuccess) err = launch_q<WF, false, 1>(dn, half_e, half_m0, counts + 1, E, st);
+  }
+  return err;
+}
+
 hipError_t launch_expert_tile(int wfmt, const StreamGemmArgs& gu, const StreamGemmArgs& dn, int P,
                               void* ws, hipStream_t st) {
-  if (wfmt != W_BF16) return hipErrorInvalidValue;
   const int E = gu.E;
   const int max_tiles = (P + TBM - 1) / TBM + E;
   int32_t* tile_e = static_cast<int32_t*>(ws);
@@ -492,13 +891,16 @@ hipError_t launch_expert_tile(int wfmt, const StreamGemmArgs& gu, const StreamGe
                                        half_m0, counts + 1);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  err = launch_tiles<true, 2>(gu, tile_e, tile_m0, counts, max_tiles, st);
-  if (err != hipSuccess) return err;
-  err = launch_tiles<true, 1>(gu, half_e, half_m0, counts + 1, E, st);
-  if (err != hipSuccess) return err;
-  err = launch_tiles<false, 2>(dn, tile_e, tile_m0, counts, max_tiles, st);
-  if (err != hipSuccess) return err;
-  return launch_tiles<false, 1>(dn, half_e, half_m0, counts + 1, E, st);
+  switch (wfmt) {
+    case W_BF16:
+      return launch_all<W_BF16>(gu, dn, tile_e, tile_m0, half_e, half_m0, counts, max_tiles, st);
+    case W_FP8:
+      return launch_all<W_FP8>(gu, dn, tile_e, tile_m0, half_e, half_m0, counts, max_tiles, st);
+    case W_FP4:
+      return launch_all<W_FP4>(gu, dn, tile_e, tile_m0, half_e, half_m0, counts, max_tiles, st);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace moe

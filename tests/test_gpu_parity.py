@@ -35,6 +35,11 @@ SMALL = [
     # (I = 192: second gate/up tile half valid; H = 192: down tile 3/4 valid)
     MC("tile_ragged", 112, T=150, H=192, E=4, k=2, I=192),
     MC("tile_zipf", 113, T=512, H=256, E=16, k=4, I=128, zipf_s=1.1),
+    # quantised weights on the tiled kernels (>= 32 rows per expert): partial
+    # N tiles on both tile shapes, Zipf load for a mix of 256- and 128-row tiles
+    MC("fp8_tile", 114, T=200, H=256, E=8, k=4, I=192, w_dtype="fp8"),
+    MC("fp4_tile_ragged", 115, T=150, H=192, E=4, k=2, I=192, w_dtype="fp4"),
+    MC("fp4_tile_zipf", 116, T=512, H=256, E=16, k=4, I=128, zipf_s=1.1, w_dtype="fp4"),
 ]
 
 
