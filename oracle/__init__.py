@@ -70,8 +70,10 @@ def _xdt(x):
 
 def format_op(kind: str, values) -> np.ndarray:
     """Format decoding/rounding of the oracle: kind in bf16, e4m3, e2m1 (codes -> value),
-    round_bf16, round_f32 (value -> rounded value)."""
-    k = {"bf16": 0, "e4m3": 1, "e2m1": 2, "round_bf16": 3, "round_f32": 4}[kind]
+    round_bf16, round_f32, round_e4m3 (value -> rounded value), block_exp (amax -> the
+    power-of-two block exponent of the fp8-MFMA mode)."""
+    k = {"bf16": 0, "e4m3": 1, "e2m1": 2, "round_bf16": 3, "round_f32": 4, "round_e4m3": 5,
+         "block_exp": 6}[kind]
     v = np.ascontiguousarray(values, dtype=np.float64).ravel()
     out = np.empty_like(v)
     f = lib().oracle_format
@@ -154,6 +156,41 @@ def expert_rows(x, experts: dict, I: int, tokens, expert_ids, want_h: bool = Fal
     return (y, h) if want_h else y
 
 
+def expert_rows_f8(x, experts: dict, I: int, tokens, expert_ids, want_h: bool = False):
+    """F8 mode (fp8-MFMA encodings, see oracle.c): y [n, H], and with want_h also
+    h [n, I] (bf16-rounded) and hq [n, I] (dequantised E4M3 codes times 2^e)."""
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.uint16:
+        raise TypeError("F8 mode takes bf16 activations")
+    T, H = x.shape
+    dt, (gu, dn, gus, dns, gug, dng) = _wargs(experts)
+    E = gu.shape[0]
+    tok = np.ascontiguousarray(tokens, dtype=np.int32).ravel()
+    ex = np.ascontiguousarray(expert_ids, dtype=np.int32).ravel()
+    n = tok.size
+    y = np.empty((n, H), np.float64)
+    h = np.empty((n, I), np.float64) if want_h else None
+    hq = np.empty((n, I), np.float64) if want_h else None
+    f = lib().oracle_expert_rows_f8
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int] + [ctypes.c_void_p] * 8 + [ctypes.c_int64] + [ctypes.c_void_p] * 3
+    _check(f(_p(x), T, H, I, E, dt, _p(gu), _p(dn), _p(gus), _p(dns), _p(gug), _p(dng),
+             _p(tok), _p(ex), n, _p(y), _p(h), _p(hq)), "expert_rows_f8")
+    return (y, h, hq) if want_h else y
+
+
+def quantize_x(x):
+    """F8-mode activation quantisation: (E4M3 values [T, H], fp32 scales [T])."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    T, H = x.shape
+    xq = np.empty((T, H), np.float64)
+    s = np.empty(T, np.float32)
+    f = lib().oracle_quantize_x
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    _check(f(_p(x), T, H, _p(xq), _p(s)), "quantize_x")
+    return xq, s
+
+
 def finalize(y_sorted, pair_pos, w, k: int, rows=None) -> np.ndarray:
     """out [n, H] (float64) = slot-ordered weighted sum of the fp32 sorted expert rows."""
     ys = np.ascontiguousarray(y_sorted, dtype=np.float32)
@@ -171,8 +208,10 @@ def finalize(y_sorted, pair_pos, w, k: int, rows=None) -> np.ndarray:
     return out
 
 
-def layer(x, w_router, bias, experts: dict, I: int, k: int, sel_dtype: str = "bf16", rows=None):
-    """Whole layer for the given tokens: dict(out [n,H], ids [n,k], w [n,k], logits [n,E])."""
+def layer(x, w_router, bias, experts: dict, I: int, k: int, sel_dtype: str = "bf16", rows=None,
+          qmode: str = "w"):
+    """Whole layer for the given tokens: dict(out [n,H], ids [n,k], w [n,k], logits [n,E]).
+    qmode "w": quantised weights dequantised exactly, bf16 activations; "f8": fp8-MFMA mode."""
     x = np.ascontiguousarray(x)
     T, H = x.shape
     wr = np.ascontiguousarray(w_router, dtype=np.float32)
@@ -185,10 +224,11 @@ def layer(x, w_router, bias, experts: dict, I: int, k: int, sel_dtype: str = "bf
     ids = np.empty((n, k), np.int32)
     w = np.empty((n, k), np.float64)
     lg = np.empty((n, E), np.float64)
-    f = lib().oracle_layer
-    f.argtypes = ([ctypes.c_int, ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_int32] * 4 +
+    f = lib().oracle_layer_q
+    f.argtypes = ([ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64] + [ctypes.c_int32] * 4 +
                   [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 7 +
                   [ctypes.c_int64] + [ctypes.c_void_p] * 4)
-    _check(f(_xdt(x), _p(x), T, H, I, E, k, _p(wr), _p(b), DT[sel_dtype], dt, _p(gu), _p(dn),
-             _p(gus), _p(dns), _p(gug), _p(dng), _p(r), n, _p(out), _p(ids), _p(w), _p(lg)), "layer")
+    _check(f({"w": 0, "f8": 1}[qmode], _xdt(x), _p(x), T, H, I, E, k, _p(wr), _p(b), DT[sel_dtype],
+             dt, _p(gu), _p(dn), _p(gus), _p(dns), _p(gug), _p(dng), _p(r), n, _p(out), _p(ids),
+             _p(w), _p(lg)), "layer")
     return {"out": out, "ids": ids, "w": w, "logits": lg}

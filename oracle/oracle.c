@@ -84,12 +84,39 @@ static double round_bf16(double v) {
 /* Round to the nearest fp32 value, ties to even (C's conversion). */
 static double round_f32(double v) { return (double)(float)v; }
 
+/* Round onto the E4M3 grid, ties to even, saturating at +-448: quantum 2^-9
+   below 2^-6 (subnormals), else 2^(floor(log2|v|) - 3) (3 mantissa bits). */
+static double q_e4m3(double v) {
+  double a = fabs(v), q;
+  if (a >= 448.0) return v < 0 ? -448.0 : 448.0;
+  if (a < 0.015625) {
+    q = ldexp(nearbyint(ldexp(a, 9)), -9);
+  } else {
+    int e;
+    frexp(a, &e); /* a = m * 2^e, 0.5 <= m < 1: floor(log2 a) = e - 1 */
+    q = ldexp(nearbyint(ldexp(a, 4 - e)), e - 4);
+  }
+  return v < 0 ? -q : q;
+}
+
+/* Power-of-two block scale: the smallest e with 448 * 2^e >= amax, clamped to
+   the E8M0 range [-127, 127]; 0 for an all-zero block. With amax = M * 2^E,
+   1 <= M < 2: e = E - 8 when M <= 1.75 (448 = 1.75 * 2^8), else E - 7. */
+static int block_exp(double amax) {
+  if (amax == 0.0) return 0;
+  int ex;
+  double m = frexp(amax, &ex); /* amax = m * 2^ex, 0.5 <= m < 1 */
+  int e = (2.0 * m <= 1.75) ? ex - 1 - 8 : ex - 1 - 7;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
 static double x_value(int x_dt, const void* x, int64_t i) {
   return x_dt == ODT_F32 ? (double)((const float*)x)[i] : bf16_value(((const uint16_t*)x)[i]);
 }
 
 /* Exported for the format pins. kind: 0 bf16 code, 1 e4m3 code, 2 e2m1 code,
-   3 round-to-bf16, 4 round-to-fp32. Codes are passed as doubles. */
+   3 round-to-bf16, 4 round-to-fp32, 5 round-to-E4M3 (saturating), 6 block
+   exponent of an amax. Codes are passed as doubles. */
 int oracle_format(int kind, const double* in, int64_t n, double* out) {
   for (int64_t i = 0; i < n; ++i) {
     switch (kind) {
@@ -98,6 +125,8 @@ int oracle_format(int kind, const double* in, int64_t n, double* out) {
       case 2: out[i] = e2m1_value((uint8_t)in[i]); break;
       case 3: out[i] = round_bf16(in[i]); break;
       case 4: out[i] = round_f32(in[i]); break;
+      case 5: out[i] = q_e4m3(in[i]); break;
+      case 6: out[i] = (double)block_exp(in[i]); break;
       default: return ORACLE_EINVAL;
     }
   }
@@ -378,6 +407,125 @@ int oracle_expert_rows(int x_dt, const void* x, int64_t T, int32_t H, int32_t I,
   return err;
 }
 
+/* ------------------------------------------------------------------ fp8-MFMA mode */
+/* The quantised experts run on fp8 MFMA ("F8" mode): every operand of both
+   expert GEMMs is an E4M3 value, encoded step by step as follows.
+   - Activations x (bf16): one fp32 scale per token, s_t = amax_t / 448 (1 for
+     an all-zero row), computed in fp32 as the kernel does; codes
+     RNE_e4m3(x / s_t) with the division in fp32.
+   - FP8 weights are used as stored (their per-channel scale multiplies the
+     accumulated sum); NVFP4 weights become E4M3 codes RNE_e4m3(e2m1 * s_blk /
+     8): the exact product scaled by 2^-3, the largest shift any NVFP4 block
+     needs (6 * 448 / 8 = 336 <= 448), so no code saturates; 8 * s_glob
+     multiplies the sum.
+   - h = silu(g) * u, rounded to bf16 as in the bf16 path, then per row and
+     128-column block a power-of-two scale 2^e (block_exp of the block's amax)
+     and codes RNE_e4m3(h * 2^-e).
+   - The down GEMM sums each block's code products times its 2^e. */
+
+/* E4M3 value of weight (K index kk, column n) of a quantised matrix, without
+   its per-channel / per-expert scale; q: codes [E, N, K] (fp8) or packed
+   [E, N, K/2] (fp4) with block scales [E, N, K/16]. */
+static double w8_value(int dt, const void* q, const void* sb, int64_t N, int64_t K, int e,
+                       int64_t n, int64_t kk) {
+  if (dt == ODT_FP8) return e4m3_value(((const uint8_t*)q)[((int64_t)e * N + n) * K + kk]);
+  uint8_t byte = ((const uint8_t*)q)[((int64_t)e * N + n) * (K / 2) + kk / 2];
+  uint8_t nib = (kk & 1) ? (byte >> 4) : (byte & 15);
+  double s = e4m3_value(((const uint8_t*)sb)[((int64_t)e * N + n) * (K / 16) + kk / 16]);
+  return q_e4m3(e2m1_value(nib) * s / 8.0);
+}
+static double w8_scale(int dt, const void* sc, const float* gs, int64_t N, int e, int64_t n) {
+  return dt == ODT_FP8 ? (double)((const float*)sc)[(int64_t)e * N + n] : 8.0 * (double)gs[e];
+}
+
+/* Per-token activation quantisation: xq[h] (E4M3 values) and the fp32 scale. */
+static float quantize_x_row(const uint16_t* xr, int64_t H, double* xq) {
+  float amax = 0.0f;
+  for (int64_t h = 0; h < H; ++h) {
+    float v = fabsf((float)bf16_value(xr[h]));
+    if (v > amax) amax = v;
+  }
+  float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  for (int64_t h = 0; h < H; ++h) xq[h] = q_e4m3((double)((float)bf16_value(xr[h]) / s));
+  return s;
+}
+
+/* One expert on one token in F8 mode; h_out (bf16-rounded h) and hq_out (the
+   dequantised codes q * 2^e) are optional. */
+static void expert_ffn_f8(const void* x, int64_t t, const weights* W, int e, double* a,
+                          double* xq, double* y, double* h_out, double* hq_out) {
+  int64_t H = W->H, I = W->I, N1 = 2 * I;
+  float s_t = quantize_x_row((const uint16_t*)x + t * H, H, xq);
+  for (int64_t n = 0; n < N1; ++n) {
+    double acc = 0.0;
+    for (int64_t h = 0; h < H; ++h)
+      acc += xq[h] * w8_value(W->dt, W->gate_up, W->gate_up_scale, N1, H, e, n, h);
+    a[n] = acc * (double)s_t * w8_scale(W->dt, W->gate_up_scale, W->gate_up_gscale, N1, e, n);
+  }
+  for (int64_t i = 0; i < I; ++i) a[i] = round_bf16(silu(a[i]) * a[I + i]);
+  if (h_out)
+    for (int64_t i = 0; i < I; ++i) h_out[i] = a[i];
+  /* h quantisation per 128-column block (a[0..I) -> a[I..2I) as q * 2^e) */
+  for (int64_t b0 = 0; b0 < I; b0 += 128) {
+    int64_t b1 = b0 + 128 < I ? b0 + 128 : I;
+    double amax = 0.0;
+    for (int64_t i = b0; i < b1; ++i) amax = fabs(a[i]) > amax ? fabs(a[i]) : amax;
+    int eb = block_exp(amax);
+    for (int64_t i = b0; i < b1; ++i) a[I + i] = ldexp(q_e4m3(ldexp(a[i], -eb)), eb);
+  }
+  if (hq_out)
+    for (int64_t i = 0; i < I; ++i) hq_out[i] = a[I + i];
+  for (int64_t n = 0; n < H; ++n) {
+    double acc = 0.0;
+    for (int64_t i = 0; i < I; ++i)
+      acc += a[I + i] * w8_value(W->dt, W->down, W->down_scale, H, I, e, n, i);
+    y[n] = acc * w8_scale(W->dt, W->down_scale, W->down_gscale, H, e, n);
+  }
+}
+
+/* y[r] for n (token, expert) rows as oracle_expert_rows, in F8 mode (bf16 x,
+   FP8 or NVFP4 weights); optional h (bf16-rounded) and dequantised h codes. */
+int oracle_expert_rows_f8(const void* x, int64_t T, int32_t H, int32_t I, int32_t E, int w_dt,
+                          const void* gate_up, const void* down, const void* gate_up_scale,
+                          const void* down_scale, const float* gate_up_gscale,
+                          const float* down_gscale, const int32_t* tokens, const int32_t* experts,
+                          int64_t n, double* y, double* h_out, double* hq_out) {
+  weights W;
+  if (w_dt != ODT_FP8 && w_dt != ODT_FP4) return ORACLE_EINVAL;
+  int rc = make_weights(&W, w_dt, H, I, gate_up, down, gate_up_scale, down_scale,
+                        gate_up_gscale, down_gscale);
+  if (rc) return rc;
+  if (!x || !tokens || !experts || !y) return ORACLE_EINVAL;
+  for (int64_t r = 0; r < n; ++r)
+    if (tokens[r] < 0 || tokens[r] >= T || experts[r] < 0 || experts[r] >= E) return ORACLE_EINVAL;
+  int err = ORACLE_OK;
+#pragma omp parallel
+  {
+    double* a = (double*)malloc(sizeof(double) * 2 * (size_t)I);
+    double* xq = (double*)malloc(sizeof(double) * (size_t)H);
+    if (!a || !xq) {
+#pragma omp atomic write
+      err = ORACLE_ENOMEM;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t r = 0; r < n; ++r)
+        expert_ffn_f8(x, tokens[r], &W, experts[r], a, xq, y + r * H, h_out ? h_out + r * I : NULL,
+                      hq_out ? hq_out + r * I : NULL);
+    }
+    free(a);
+    free(xq);
+  }
+  return err;
+}
+
+/* Activation quantisation alone, for the GPU's quantised x: values and scales. */
+int oracle_quantize_x(const uint16_t* x, int64_t T, int32_t H, double* xq, float* scale) {
+  if (!x || !xq || !scale || H <= 0) return ORACLE_EINVAL;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) scale[t] = quantize_x_row(x + t * H, H, xq + t * H);
+  return ORACLE_OK;
+}
+
 /* ------------------------------------------------------------------ finalize */
 
 /* out[i] = sum_{j=0..k-1} w[t, j] * y_sorted[pair_pos[t*k + j]] for t = rows[i]
@@ -411,12 +559,19 @@ int oracle_finalize(const float* y_sorted, const int32_t* pair_pos, const float*
    logits -> routing -> for each chosen expert its SwiGLU FFN ->
    out[t] = sum_j w[t, j] * FFN_{S[t, j]}(x_t), in slot order.
    Optional outputs: ids [n, k], w [n, k], logits [n, E] (exact, pre-rounding). */
-int oracle_layer(int x_dt, const void* x, int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
-                 const float* w_router, const float* bias, int sel_dt, int w_dt,
-                 const void* gate_up, const void* down, const void* gate_up_scale,
-                 const void* down_scale, const float* gate_up_gscale, const float* down_gscale,
-                 const int64_t* rows, int64_t n, double* out, int32_t* ids_out, double* w_out,
-                 double* logits_out) {
+int oracle_expert_rows_f8(const void* x, int64_t T, int32_t H, int32_t I, int32_t E, int w_dt,
+                          const void* gate_up, const void* down, const void* gate_up_scale,
+                          const void* down_scale, const float* gate_up_gscale,
+                          const float* down_gscale, const int32_t* tokens, const int32_t* experts,
+                          int64_t n, double* y, double* h_out, double* hq_out);
+
+/* qmode 0: weights dequantised exactly, activations bf16; 1: F8 mode (above). */
+int oracle_layer_q(int qmode, int x_dt, const void* x, int64_t T, int32_t H, int32_t I, int32_t E,
+                   int32_t k, const float* w_router, const float* bias, int sel_dt, int w_dt,
+                   const void* gate_up, const void* down, const void* gate_up_scale,
+                   const void* down_scale, const float* gate_up_gscale, const float* down_gscale,
+                   const int64_t* rows, int64_t n, double* out, int32_t* ids_out, double* w_out,
+                   double* logits_out) {
   if (!out || k <= 0 || k > E) return ORACLE_EINVAL;
   int rc = ORACLE_OK;
   double* lg = logits_out ? logits_out : (double*)malloc(sizeof(double) * (size_t)(n * E + 1));
@@ -434,8 +589,17 @@ int oracle_layer(int x_dt, const void* x, int64_t T, int32_t H, int32_t I, int32
   if (rc) goto done;
   for (int64_t i = 0; i < n; ++i)
     for (int j = 0; j < k; ++j) tok[i * k + j] = (int32_t)(rows ? rows[i] : i);
-  rc = oracle_expert_rows(x_dt, x, T, H, I, E, w_dt, gate_up, down, gate_up_scale, down_scale,
-                          gate_up_gscale, down_gscale, tok, ids, n * k, y, NULL);
+  if (qmode == 1) {
+    if (x_dt != ODT_BF16) {
+      rc = ORACLE_EINVAL;
+      goto done;
+    }
+    rc = oracle_expert_rows_f8(x, T, H, I, E, w_dt, gate_up, down, gate_up_scale, down_scale,
+                               gate_up_gscale, down_gscale, tok, ids, n * k, y, NULL, NULL);
+  } else {
+    rc = oracle_expert_rows(x_dt, x, T, H, I, E, w_dt, gate_up, down, gate_up_scale, down_scale,
+                            gate_up_gscale, down_gscale, tok, ids, n * k, y, NULL);
+  }
   if (rc) goto done;
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) {
@@ -453,4 +617,15 @@ done:
   free(tok);
   free(y);
   return rc;
+}
+
+int oracle_layer(int x_dt, const void* x, int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                 const float* w_router, const float* bias, int sel_dt, int w_dt,
+                 const void* gate_up, const void* down, const void* gate_up_scale,
+                 const void* down_scale, const float* gate_up_gscale, const float* down_gscale,
+                 const int64_t* rows, int64_t n, double* out, int32_t* ids_out, double* w_out,
+                 double* logits_out) {
+  return oracle_layer_q(0, x_dt, x, T, H, I, E, k, w_router, bias, sel_dt, w_dt, gate_up, down,
+                        gate_up_scale, down_scale, gate_up_gscale, down_gscale, rows, n, out,
+                        ids_out, w_out, logits_out);
 }
