@@ -74,10 +74,20 @@ typedef enum moe_dtype {
  *      codes (element 2j in the low nibble, K contiguous); gate_up_scale
  *      [E, 2I, H/16] and down_scale [E, H, I/16] E4M3 block scales;
  *      gate_up_gscale, down_gscale f32 [E]. W = e2m1(q) * e4m3(s_blk) * s_glob.
- * Quantised weights are dequantised exactly; activations stay bf16. */
+ * qmode selects how quantised weights are computed with:
+ *  MOE_QMODE_W (0): dequantised exactly to bf16, activations stay bf16, bf16
+ *      MFMA (the weight-only W4A16 / W8A16 semantics; vLLM recipe
+ *      "reflection/Beam-1.0-501B-A23B", Guide > Variants);
+ *  MOE_QMODE_F8 (1): fp8 MFMA: x quantised per token to E4M3 with an fp32
+ *      scale (amax / 448), NVFP4 weights re-encoded to E4M3 in registers
+ *      (RNE of e2m1 * s_blk / 8), h quantised per row and 128-column block to
+ *      E4M3 with a power-of-two scale; needs I <= 4096.
+ * qmode must be 0 for MOE_F32 / MOE_BF16 weights. */
+typedef enum moe_qmode { MOE_QMODE_W = 0, MOE_QMODE_F8 = 1 } moe_qmode;
+
 typedef struct moe_expert_weights {
   int32_t dtype; /* moe_dtype */
-  int32_t reserved;
+  int32_t qmode; /* moe_qmode */
   const void* gate_up;
   const void* down;
   const void* gate_up_scale;
@@ -128,7 +138,10 @@ moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
  *   a = x[t] . gate_up[e]  (length 2I, fp32 accumulate)
  *   h = silu(a[0:I]) * a[I:2I]   (rounded to bf16 for bf16 x; fp32 for fp32 x)
  *   y_sorted[r] = h . down[e]    (length H, fp32)
- * offsets and sorted_pair are moe_permute's outputs. */
+ * offsets and sorted_pair are moe_permute's outputs. On return the workspace
+ * begins with h in sorted row order ([T*k, I], bf16, or fp32 for fp32
+ * weights), valid until the workspace is reused; in the fp8-MFMA mode this is
+ * the bf16 h that the E4M3 quantisation of the down GEMM's operand starts from. */
 size_t moe_experts_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                                   const moe_expert_weights* w);
 moe_status moe_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I, int32_t E,

@@ -179,6 +179,21 @@ def expert_rows_f8(x, experts: dict, I: int, tokens, expert_ids, want_h: bool = 
     return (y, h, hq) if want_h else y
 
 
+def down_rows_f8(h, experts: dict, expert_ids, H: int):
+    """F8 down stage on given h rows (bf16 values [n, I]): y [n, H]."""
+    h = np.ascontiguousarray(h, dtype=np.float64)
+    n, I = h.shape
+    dt, (gu, dn, gus, dns, gug, dng) = _wargs(experts)
+    E = gu.shape[0]
+    ex = np.ascontiguousarray(expert_ids, dtype=np.int32).ravel()
+    y = np.empty((n, H), np.float64)
+    f = lib().oracle_down_rows_f8
+    f.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_int] + [ctypes.c_void_p] * 7 + [ctypes.c_int64] + [ctypes.c_void_p] * 2
+    _check(f(H, I, E, dt, _p(gu), _p(dn), _p(gus), _p(dns), _p(gug), _p(dng), _p(ex), n, _p(h), _p(y)),
+           "down_rows_f8")
+    return y
+
+
 def quantize_x(x):
     """F8-mode activation quantisation: (E4M3 values [T, H], fp32 scales [T])."""
     x = np.ascontiguousarray(x, dtype=np.uint16)

@@ -450,6 +450,25 @@ static float quantize_x_row(const uint16_t* xr, int64_t H, double* xq) {
   return s;
 }
 
+/* The down stage of F8 mode for one row: h (bf16 values, length I) quantised
+   per 128-column block (hq = q * 2^e, length I), then y = hq W_d[e] times the
+   column scales. */
+static void down_f8(const weights* W, int e, const double* h, double* hq, double* y) {
+  int64_t H = W->H, I = W->I;
+  for (int64_t b0 = 0; b0 < I; b0 += 128) {
+    int64_t b1 = b0 + 128 < I ? b0 + 128 : I;
+    double amax = 0.0;
+    for (int64_t i = b0; i < b1; ++i) amax = fabs(h[i]) > amax ? fabs(h[i]) : amax;
+    int eb = block_exp(amax);
+    for (int64_t i = b0; i < b1; ++i) hq[i] = ldexp(q_e4m3(ldexp(h[i], -eb)), eb);
+  }
+  for (int64_t n = 0; n < H; ++n) {
+    double acc = 0.0;
+    for (int64_t i = 0; i < I; ++i) acc += hq[i] * w8_value(W->dt, W->down, W->down_scale, H, I, e, n, i);
+    y[n] = acc * w8_scale(W->dt, W->down_scale, W->down_gscale, H, e, n);
+  }
+}
+
 /* One expert on one token in F8 mode; h_out (bf16-rounded h) and hq_out (the
    dequantised codes q * 2^e) are optional. */
 static void expert_ffn_f8(const void* x, int64_t t, const weights* W, int e, double* a,
@@ -465,22 +484,9 @@ static void expert_ffn_f8(const void* x, int64_t t, const weights* W, int e, dou
   for (int64_t i = 0; i < I; ++i) a[i] = round_bf16(silu(a[i]) * a[I + i]);
   if (h_out)
     for (int64_t i = 0; i < I; ++i) h_out[i] = a[i];
-  /* h quantisation per 128-column block (a[0..I) -> a[I..2I) as q * 2^e) */
-  for (int64_t b0 = 0; b0 < I; b0 += 128) {
-    int64_t b1 = b0 + 128 < I ? b0 + 128 : I;
-    double amax = 0.0;
-    for (int64_t i = b0; i < b1; ++i) amax = fabs(a[i]) > amax ? fabs(a[i]) : amax;
-    int eb = block_exp(amax);
-    for (int64_t i = b0; i < b1; ++i) a[I + i] = ldexp(q_e4m3(ldexp(a[i], -eb)), eb);
-  }
+  down_f8(W, e, a, a + I, y);
   if (hq_out)
     for (int64_t i = 0; i < I; ++i) hq_out[i] = a[I + i];
-  for (int64_t n = 0; n < H; ++n) {
-    double acc = 0.0;
-    for (int64_t i = 0; i < I; ++i)
-      acc += a[I + i] * w8_value(W->dt, W->down, W->down_scale, H, I, e, n, i);
-    y[n] = acc * w8_scale(W->dt, W->down_scale, W->down_gscale, H, e, n);
-  }
 }
 
 /* y[r] for n (token, expert) rows as oracle_expert_rows, in F8 mode (bf16 x,
@@ -514,6 +520,37 @@ int oracle_expert_rows_f8(const void* x, int64_t T, int32_t H, int32_t I, int32_
     }
     free(a);
     free(xq);
+  }
+  return err;
+}
+
+/* The F8 down stage alone on given h rows (bf16 values [n, I]) of the given
+   experts: y [n, H]; lets a caller take the h quantisation decisions on its
+   own h. */
+int oracle_down_rows_f8(int32_t H, int32_t I, int32_t E, int w_dt, const void* gate_up,
+                        const void* down, const void* gate_up_scale, const void* down_scale,
+                        const float* gate_up_gscale, const float* down_gscale,
+                        const int32_t* experts, int64_t n, const double* h, double* y) {
+  weights W;
+  if (w_dt != ODT_FP8 && w_dt != ODT_FP4) return ORACLE_EINVAL;
+  int rc = make_weights(&W, w_dt, H, I, gate_up, down, gate_up_scale, down_scale,
+                        gate_up_gscale, down_gscale);
+  if (rc) return rc;
+  if (!experts || !h || !y) return ORACLE_EINVAL;
+  for (int64_t r = 0; r < n; ++r)
+    if (experts[r] < 0 || experts[r] >= E) return ORACLE_EINVAL;
+  int err = ORACLE_OK;
+#pragma omp parallel
+  {
+    double* hq = (double*)malloc(sizeof(double) * (size_t)I);
+    if (!hq) {
+#pragma omp atomic write
+      err = ORACLE_ENOMEM;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t r = 0; r < n; ++r) down_f8(&W, experts[r], h + r * I, hq, y + r * H);
+    }
+    free(hq);
   }
   return err;
 }

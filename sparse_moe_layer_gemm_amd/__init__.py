@@ -19,6 +19,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_FP4_E2M1 = 0, 1, 2, 3
+MOE_QMODE_W, MOE_QMODE_F8 = 0, 1
 DTYPE_NAMES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "fp4": MOE_FP4_E2M1}
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_LAUNCH"}
@@ -36,7 +37,7 @@ class MoEError(RuntimeError):
 
 class CExpertWeights(ctypes.Structure):
     """struct moe_expert_weights"""
-    _fields_ = [("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    _fields_ = [("dtype", ctypes.c_int32), ("qmode", ctypes.c_int32),
                 ("gate_up", ctypes.c_void_p), ("down", ctypes.c_void_p),
                 ("gate_up_scale", ctypes.c_void_p), ("down_scale", ctypes.c_void_p),
                 ("gate_up_gscale", ctypes.c_void_p), ("down_gscale", ctypes.c_void_p)]
@@ -118,9 +119,10 @@ class ExpertWeights:
     down_scale: Optional[torch.Tensor] = None
     gate_up_gscale: Optional[torch.Tensor] = None
     down_gscale: Optional[torch.Tensor] = None
+    qmode: int = MOE_QMODE_W
 
     def c_struct(self) -> CExpertWeights:
-        return CExpertWeights(self.dtype, 0, _ptr(self.gate_up), _ptr(self.down),
+        return CExpertWeights(self.dtype, self.qmode, _ptr(self.gate_up), _ptr(self.down),
                               _ptr(self.gate_up_scale), _ptr(self.down_scale),
                               _ptr(self.gate_up_gscale), _ptr(self.down_gscale))
 
@@ -207,7 +209,7 @@ def to_device_bf16(bits, device="cuda") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
 
 
-def experts_to_device(host: dict, device="cuda") -> ExpertWeights:
+def experts_to_device(host: dict, device="cuda", qmode: int = MOE_QMODE_W) -> ExpertWeights:
     """Expert weights as stored on the host (numpy) -> ExpertWeights on the device."""
     import numpy as np
     dt = DTYPE_NAMES[host["dtype"]]
@@ -221,4 +223,4 @@ def experts_to_device(host: dict, device="cuda") -> ExpertWeights:
         return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
     return ExpertWeights(dt, dev("gate_up"), dev("down"), dev("gate_up_scale"), dev("down_scale"),
-                         dev("gate_up_gscale"), dev("down_gscale"))
+                         dev("gate_up_gscale"), dev("down_gscale"), qmode)

@@ -76,6 +76,11 @@ size_t route_ws_bytes(int64_t T, int32_t H, int32_t E) {
 
 moe_status check_weights(const moe_expert_weights* w, int32_t x_dtype, int32_t H, int32_t I) {
   if (!w) return MOE_ERR_INVALID_ARGUMENT;
+  if (w->qmode != MOE_QMODE_W && w->qmode != MOE_QMODE_F8) return MOE_ERR_INVALID_ARGUMENT;
+  if (w->qmode == MOE_QMODE_F8) {
+    if (w->dtype != MOE_FP8_E4M3 && w->dtype != MOE_FP4_E2M1) return MOE_ERR_UNSUPPORTED;
+    if (I > 4096) return MOE_ERR_UNSUPPORTED;
+  }
   if (!w->gate_up || !w->down) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(w->gate_up) || !aligned16(w->down)) return MOE_ERR_INVALID_ARGUMENT;
   if (I <= 0) return MOE_ERR_INVALID_ARGUMENT;
@@ -105,10 +110,21 @@ moe_status check_weights(const moe_expert_weights* w, int32_t x_dtype, int32_t H
   }
 }
 
-size_t experts_ws_bytes(int64_t T, int32_t I, int32_t E, int32_t k, int32_t w_dtype) {
+bool f8_mode(const moe_expert_weights* w) { return w->qmode == MOE_QMODE_F8; }
+// E8M0 block scales per row of h: one per 128 columns, rows padded to 4 bytes
+int h_bstride(int32_t I) { return ((I + 127) / 128 + 3) / 4 * 4; }
+
+// h (bf16, or fp32 for the all-fp32 layer) + tile tables (+ fp8-MFMA mode:
+// E4M3 x, per-token scales, E4M3 h, block scales)
+size_t experts_ws_bytes(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                        const moe_expert_weights* w) {
   const size_t P = (size_t)T * k;
-  const size_t h_elem = w_dtype == MOE_F32 ? sizeof(float) : sizeof(uint16_t);
-  return align_up(P * I * h_elem) + align_up(moe::expert_tile_ws_bytes((int)P, E));
+  const size_t h_elem = w->dtype == MOE_F32 ? sizeof(float) : sizeof(uint16_t);
+  size_t b = align_up(P * I * h_elem) + align_up(moe::expert_tile_ws_bytes((int)P, E));
+  if (f8_mode(w))
+    b += align_up((size_t)T * H) + align_up((size_t)T * sizeof(float)) + align_up(P * I) +
+         align_up(P * (size_t)h_bstride(I));
+  return b;
 }
 
 // The tiled grouped GEMMs pay off once experts average enough rows to fill
@@ -192,6 +208,20 @@ moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H,
   d.w_gscale = w->down_gscale;
   d.h_out = nullptr;
   d.y_out = y_sorted;
+  if (f8_mode(w)) {
+    // the fp8-MFMA mode always runs the tiled kernels
+    char* f8ws = static_cast<char*>(tile_ws) + align_up(moe::expert_tile_ws_bytes(P, E));
+    moe::F8Buffers b{};
+    b.xq = reinterpret_cast<uint8_t*>(f8ws);
+    f8ws += align_up((size_t)T * H);
+    b.xs = reinterpret_cast<float*>(f8ws);
+    f8ws += align_up((size_t)T * sizeof(float));
+    b.hq = reinterpret_cast<uint8_t*>(f8ws);
+    f8ws += align_up((size_t)P * I);
+    b.hs = reinterpret_cast<uint8_t*>(f8ws);
+    b.hs_stride = h_bstride(I);
+    return launch_status(moe::launch_expert_f8(wf, a, d, (int)T, P, b, tile_ws, st));
+  }
   if (use_tile_kernel(w->dtype, P, E))
     return launch_status(moe::launch_expert_tile(wf, a, d, P, tile_ws, st));
   hipError_t e = moe::launch_expert_stream(wf, true, a, st);
@@ -269,7 +299,7 @@ moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
 size_t moe_experts_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                                   const moe_expert_weights* w) {
   if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || !w) return 0;
-  return experts_ws_bytes(T, I, E, k, w->dtype);
+  return experts_ws_bytes(T, H, I, E, k, w);
 }
 
 moe_status moe_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I, int32_t E,
@@ -286,7 +316,7 @@ moe_status moe_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
   if (!aligned16(x) || !aligned16(offsets) || !aligned16(sorted_pair) || !aligned16(y_sorted) ||
       !aligned16(workspace))
     return MOE_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < experts_ws_bytes(T, I, E, k, w->dtype)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace_bytes < experts_ws_bytes(T, H, I, E, k, w)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   return enqueue_experts(x, x_dtype, T, H, I, E, k, offsets, sorted_pair, w, y_sorted, workspace,
                          static_cast<hipStream_t>(stream));
 }
@@ -317,7 +347,7 @@ size_t moe_forward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, in
   return route_ws_bytes(T, H, E) + align_up((size_t)T * E * sizeof(float)) +
          2 * align_up(P * sizeof(int32_t)) /* ids, w */ + align_up(E * sizeof(int32_t)) +
          align_up((E + 1) * sizeof(int32_t)) + 2 * align_up(P * sizeof(int32_t)) +
-         align_up(P * H * sizeof(float)) + experts_ws_bytes(T, I, E, k, w->dtype);
+         align_up(P * H * sizeof(float)) + experts_ws_bytes(T, H, I, E, k, w);
 }
 
 moe_status moe_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I, int32_t E,
@@ -354,7 +384,7 @@ moe_status moe_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
   int32_t* sorted_pair = static_cast<int32_t*>(c.take(P * sizeof(int32_t)));
   int32_t* pair_pos = static_cast<int32_t*>(c.take(P * sizeof(int32_t)));
   float* y_sorted = static_cast<float*>(c.take(P * H * sizeof(float)));
-  void* exp_ws = c.take(experts_ws_bytes(T, I, E, k, w->dtype));
+  void* exp_ws = c.take(experts_ws_bytes(T, H, I, E, k, w));
   if (topk_ids) ids = topk_ids;
   if (topk_w) tw = topk_w;
   if (!logits) logits = lbuf;

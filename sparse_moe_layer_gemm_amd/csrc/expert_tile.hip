@@ -429,6 +429,11 @@ __device__ __forceinline__ u32x2 lds_b64(uint32_t addr) {
 // raw codes of one column per lane per K step: 8 B (E2M1) or 16 B (E4M3)
 template <int WF> struct QRaw { typedef u32x4 type; };
 template <> struct QRaw<W_FP4> { typedef u32x2 type; };
+__device__ __forceinline__ uint32_t lds_b32(uint32_t addr) {
+  uint32_t r;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
 __device__ __forceinline__ uint32_t lds_byte(uint32_t addr) {
   uint32_t r;
   asm volatile("ds_read_u8 %0, %1" : "=v"(r) : "v"(addr));
@@ -754,6 +759,493 @@ __global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
   }
 }
 
+// ------------------------------------------------------------------ fp8-MFMA mode
+// Both expert GEMMs on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, fp32
+// accumulate, 64 K per instruction at twice the bf16 rate). Operands:
+//  - gate/up A: x as E4M3 codes with one fp32 scale per token (applied with
+//    the weight scales in the epilogue, before SwiGLU);
+//  - down A: h as E4M3 codes with one power-of-two (E8M0) scale per row and
+//    128-column block, handed to the MFMA, which applies it exactly;
+//  - B: FP8 weights as stored, or NVFP4 weights re-encoded per value as
+//    RNE_e4m3(e2m1 * s_blk / 8) in registers (the converter gives e2m1 times
+//    the scale's power of two, an fp32 multiply its mantissa factor / 8, and
+//    the hardware f32 -> E4M3 conversion rounds to nearest even).
+// Lane half g takes K 32g .. 32g+31 of each 64-deep step for both operands;
+// the scale of a down-GEMM row is the same over the whole step, so the K
+// order inside the step is free.
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+template <int WF, int WM>
+struct F8Shape {
+  using T = TileShape<WM>;
+  static constexpr int BM = T::BM, BN = T::BN, WN = T::WN;
+  static constexpr int A_STAGE = BM * 64;                            // 64 codes per row
+  static constexpr int B_STAGE = BN * (WF == W_FP8 ? 64 : 32);
+  static constexpr int S_STAGE = WF == W_FP4 ? BN * 4 : 0;
+  static constexpr int STAGE = A_STAGE + B_STAGE + S_STAGE;
+  static constexpr int ROWB = 32;                                    // bytes of row data per row
+  static constexpr int ROWDATA = BM * ROWB;
+  static constexpr int NST = (4 * STAGE + ROWDATA <= 163840) ? 4 : 3;
+  static constexpr int PIPE = NST * STAGE > 65536 ? NST * STAGE : 65536;
+  static constexpr int LDS = PIPE + ROWDATA;
+  static constexpr int QA = BM / 64;                                 // 1 KB A loads per wavefront
+  static constexpr int QB = WF == W_FP8 ? BN / 64 : BN / 128;        // 1 KB code loads per wavefront
+  static constexpr int QS = WF == W_FP4 ? BN / 256 : 0;              // 256 B scale loads per wavefront
+  static constexpr int PER_STEP = QA + QB + QS;
+};
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N <= 40, "vmcnt range");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 7) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+  else if constexpr (N == 14) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if constexpr (N == 20) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+  else if constexpr (N == 21) asm volatile("s_waitcnt vmcnt(21)" ::: "memory");
+  else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  else if constexpr (N == 30) asm volatile("s_waitcnt vmcnt(30)" ::: "memory");
+  else static_assert(N < 0, "add this vmcnt value");
+}
+
+// 8 E2M1 codes (one dword) x block scale (p2 * fm) / 8 -> 8 E4M3 codes (two dwords)
+__device__ __forceinline__ void fp4_to_fp8(uint32_t d, float p2, float fm8, int32_t& o0,
+                                           int32_t& o1) {
+  const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 0);
+  const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 1);
+  const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 2);
+  const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 3);
+  int32_t r = __builtin_amdgcn_cvt_pk_fp8_f32(v0.x * fm8, v0.y * fm8, 0, false);
+  o0 = __builtin_amdgcn_cvt_pk_fp8_f32(v1.x * fm8, v1.y * fm8, r, true);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(v2.x * fm8, v2.y * fm8, 0, false);
+  o1 = __builtin_amdgcn_cvt_pk_fp8_f32(v3.x * fm8, v3.y * fm8, r, true);
+}
+
+template <int WF> struct F8Raw { typedef i32x8 type; };      // E4M3: 32 codes
+template <> struct F8Raw<W_FP4> { typedef u32x4 type; };     // E2M1: 32 codes
+
+template <int WF, bool GATE_UP, int WM>
+__global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmArgs a,
+                                                         const int32_t* __restrict__ tile_e,
+                                                         const int32_t* __restrict__ tile_m0,
+                                                         const int32_t* __restrict__ n_tiles_p,
+                                                         int NT) {
+  using S = F8Shape<WF, WM>;
+  __shared__ __align__(1024) uint8_t smem[S::LDS];
+  uint8_t* rowdata = smem + S::PIPE;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave / S::WN, wn = wave % S::WN;
+
+  const int total = *n_tiles_p * NT;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int per = (total + 7) >> 3;
+  if (slot >= per) return;
+  const int w = xcd * per + slot;
+  if (w >= total) return;
+  const int mt = w / NT, nt = w - mt * NT;
+  const int e = tile_e[mt];
+  const int m0 = tile_m0[mt];
+  const int r0 = a.offsets[e];
+  const int cnt = a.offsets[e + 1] - r0;
+  const int K = a.K, N = a.N;
+  const int nb = (K + 127) / 128;  // 128-column blocks of a down-GEMM row
+
+  // per-row data: gate/up the token's fp32 activation scale; down the row's
+  // E8M0 block scales, stored [block][slot] with slot = 4 * (32 wm + l32) + i
+  // for tile row 128 wm + 32 i + l32, so a lane reads its four rows' scales of
+  // a block as one dword (rows past the expert's end get neutral values)
+  for (int r = tid; r < S::BM; r += 256) {
+    const bool ok = m0 + r < cnt;
+    if (GATE_UP) {
+      const float sc = ok ? f8.x_scale[a.sorted_pair[r0 + m0 + r] / a.k] : 0.f;
+      *reinterpret_cast<float*>(rowdata + r * S::ROWB) = sc;
+    } else {
+      const int slot = 4 * (32 * (r >> 7) + (r & 31)) + ((r >> 5) & 3);
+      const uint8_t* src = f8.h_bscale + (size_t)(ok ? r0 + m0 + r : 0) * f8.h_bstride;
+      for (int b = 0; b < nb; ++b) rowdata[b * S::BM + slot] = ok ? src[b] : (uint8_t)127;
+    }
+  }
+  __syncthreads();
+
+  // A: gathered code rows (64 B per row per step, as the bf16 A tile)
+  const uint8_t* asrc[S::QA];
+#pragma unroll
+  for (int q = 0; q < S::QA; ++q) {
+    const int row = (S::BM / 4) * wave + 16 * q + (lane >> 2);
+    const int lg = (lane & 3) ^ ((row >> 2) & 3);
+    size_t grow = 0;
+    if (m0 + row < cnt)
+      grow = GATE_UP ? (size_t)(a.sorted_pair[r0 + m0 + row] / a.k) : (size_t)(r0 + m0 + row);
+    asrc[q] = f8.a8 + grow * K + 16 * lg;
+  }
+  auto mcol = [&](int c) -> int {
+    if (GATE_UP) {
+      const int gc = nt * (S::BN / 2) + (c < S::BN / 2 ? c : c - S::BN / 2);
+      if (gc >= a.I) return 0;
+      return c < S::BN / 2 ? gc : a.I + gc;
+    }
+    const int col = nt * S::BN + c;
+    return col < N ? col : 0;
+  };
+  const uint8_t* wq = static_cast<const uint8_t*>(a.w);
+  // B: E4M3 codes like A (16 columns x 64 B per load, swizzled granules);
+  // E2M1 codes 32 B per column (two lanes per column), scale dwords one per column
+  const uint8_t* bsrc[S::QB];
+#pragma unroll
+  for (int q = 0; q < S::QB; ++q) {
+    if (WF == W_FP8) {
+      const int col = (S::BN / 4) * wave + 16 * q + (lane >> 2);
+      const int lg = (lane & 3) ^ ((col >> 2) & 3);
+      bsrc[q] = wq + ((size_t)e * N + mcol(col)) * K + 16 * lg;
+    } else {
+      const int qi = wave * S::QB + q;
+      bsrc[q] = wq + ((size_t)e * N + mcol(32 * qi + (lane >> 1))) * (size_t)(K / 2) + 16 * (lane & 1);
+    }
+  }
+  const uint8_t* ssrc[S::QS > 0 ? S::QS : 1];
+#pragma unroll
+  for (int q = 0; q < S::QS; ++q) {
+    const int qi = wave * S::QS + q;
+    ssrc[q] = static_cast<const uint8_t*>(a.w_scale) + ((size_t)e * N + mcol(64 * qi + lane)) * (size_t)(K / 16);
+  }
+  auto issue = [&](int kt, int st) {
+    uint8_t* As = smem + st * S::STAGE;
+    uint8_t* Bs = As + S::A_STAGE;
+    uint8_t* Ss = Bs + S::B_STAGE;
+#pragma unroll
+    for (int q = 0; q < S::QA; ++q) dma16(asrc[q] + 64 * kt, As + ((S::BM / 4) * wave + 16 * q) * 64);
+#pragma unroll
+    for (int q = 0; q < S::QB; ++q) {
+      if (WF == W_FP8)
+        dma16(bsrc[q] + 64 * kt, Bs + ((S::BN / 4) * wave + 16 * q) * 64);
+      else
+        dma16(bsrc[q] + 32 * kt, Bs + (wave * S::QB + q) * 1024);
+    }
+#pragma unroll
+    for (int q = 0; q < S::QS; ++q) dma4(ssrc[q] + 4 * kt, Ss + (wave * S::QS + q) * 256);
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  auto bcol = [&](int j) -> int {
+    if (GATE_UP) return (j < 2) ? 64 * wn + 32 * j : S::BN / 2 + 64 * wn + 32 * (j - 2);
+    return 128 * wn + 32 * j;
+  };
+  const int l32 = lane & 31, kh = lane >> 5;
+  const uint32_t lds0 = (uint32_t)(size_t)(lds_u8*)smem;
+  const uint32_t rowb = (uint32_t)(size_t)(lds_u8*)rowdata;
+  uint32_t aoff[4][2], boff[4][2], soff[4];
+  const uint32_t roff = rowb + 4 * (32 * wm + l32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 128 * wm + 32 * i + l32;
+    aoff[i][0] = a_off(row, 2 * kh);
+    aoff[i][1] = a_off(row, 2 * kh + 1);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = bcol(j) + l32;
+    if (WF == W_FP8) {
+      boff[j][0] = S::A_STAGE + a_off(c, 2 * kh);
+      boff[j][1] = S::A_STAGE + a_off(c, 2 * kh + 1);
+    } else {
+      boff[j][0] = S::A_STAGE + c * 32 + 16 * kh;
+      boff[j][1] = 0;
+    }
+    soff[j] = S::A_STAGE + S::B_STAGE + c * 4;
+  }
+  // One half of a K step: all four A fragments, the B codes of two column
+  // tiles (j = 2h, 2h+1) and, for the down GEMM, the four rows' block scales
+  // (one dword, byte i for row tile i). Raw read results stay separate
+  // registers until their wait (they are the operands of the wait, so nothing
+  // copies them while the reads are in flight).
+  struct Half {
+    u32x4 a[4][2];
+    u32x4 b[2][WF == W_FP8 ? 2 : 1];  // E4M3: two 16 B runs per column tile; E2M1: one
+    uint32_t sc[2];                   // E2M1 block-scale dwords
+    uint32_t as;                      // down: E8M0 scales of the four rows
+  };
+  auto read_half = [&](Half& f, int st, int h, int kt) {
+    const uint32_t base = lds0 + st * S::STAGE;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = 2 * h + jj;
+      f.b[jj][0] = lds_b128(base + boff[j][0]);
+      if constexpr (WF == W_FP8)
+        f.b[jj][1] = lds_b128(base + boff[j][1]);
+      else
+        f.sc[jj] = lds_b32(base + soff[j]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f.a[i][0] = lds_b128(base + aoff[i][0]);
+      f.a[i][1] = lds_b128(base + aoff[i][1]);
+    }
+    if (!GATE_UP) f.as = lds_b32(roff + (kt >> 1) * S::BM);
+  };
+#define MOE_F8_WAIT_A(f, pending, ...)                                                        \
+  asm volatile("s_waitcnt lgkmcnt(" #pending ")"                                              \
+               : "+v"(f.a[0][0]), "+v"(f.a[0][1]), "+v"(f.a[1][0]), "+v"(f.a[1][1]),           \
+                 "+v"(f.a[2][0]), "+v"(f.a[2][1]), "+v"(f.a[3][0]), "+v"(f.a[3][1]),           \
+                 "+v"(f.as), __VA_ARGS__                                                       \
+               :                                                                               \
+               : "memory")
+#define MOE_F8_WAIT_FP8(f, pending) \
+  MOE_F8_WAIT_A(f, pending, "+v"(f.b[0][0]), "+v"(f.b[1][0]), "+v"(f.b[0][1]), "+v"(f.b[1][1]))
+#define MOE_F8_WAIT_FP4(f, pending) \
+  MOE_F8_WAIT_A(f, pending, "+v"(f.b[0][0]), "+v"(f.b[1][0]), "+v"(f.sc[0]), "+v"(f.sc[1]))
+  // reads per half: 12 (gate/up) or 13 (down, with the row scales)
+  auto wait_half = [&](Half& f) {
+    if constexpr (WF == W_FP8) {
+      if constexpr (GATE_UP)
+        MOE_F8_WAIT_FP8(f, 12);
+      else
+        MOE_F8_WAIT_FP8(f, 13);
+    } else {
+      if constexpr (GATE_UP)
+        MOE_F8_WAIT_FP4(f, 12);
+      else
+        MOE_F8_WAIT_FP4(f, 13);
+    }
+  };
+  auto mfma_half = [&](const Half& f, int h) {
+    i32x8 af[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      af[i] = i32x8{(int)f.a[i][0][0], (int)f.a[i][0][1], (int)f.a[i][0][2], (int)f.a[i][0][3],
+                    (int)f.a[i][1][0], (int)f.a[i][1][1], (int)f.a[i][1][2], (int)f.a[i][1][3]};
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      i32x8 bf;
+      if constexpr (WF == W_FP8) {
+        bf = i32x8{(int)f.b[jj][0][0], (int)f.b[jj][0][1], (int)f.b[jj][0][2], (int)f.b[jj][0][3],
+                   (int)f.b[jj][1][0], (int)f.b[jj][1][1], (int)f.b[jj][1][2], (int)f.b[jj][1][3]};
+      } else {
+        // dwords 0-1: block 2g of the step, dwords 2-3: block 2g+1
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          float p2, fm;
+          e4m3_split((f.sc[jj] >> (8 * (2 * kh + blk))) & 0xFFu, p2, fm);
+          const float fm8 = fm * 0.125f;
+          int32_t o0, o1, o2, o3;
+          fp4_to_fp8(f.b[jj][0][2 * blk], p2, fm8, o0, o1);
+          fp4_to_fp8(f.b[jj][0][2 * blk + 1], p2, fm8, o2, o3);
+          bf[4 * blk] = o0;
+          bf[4 * blk + 1] = o1;
+          bf[4 * blk + 2] = o2;
+          bf[4 * blk + 3] = o3;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int sa = GATE_UP ? 127 : (int)((f.as >> (8 * i)) & 0xFFu);
+        acc[i][2 * h + jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            af[i], bf, acc[i][2 * h + jj], 0, 0, 0, sa, 0, 127);
+      }
+    }
+  };
+
+  // Pipeline as in the bf16 kernel, with NST stages and NST - 1 steps in flight.
+  constexpr int AHEAD = S::NST - 1;
+  const int nk = K / 64;
+  issue(0, 0);
+  issue(nk > 1 ? 1 : nk - 1, 1);
+  if constexpr (AHEAD == 3) issue(nk > 2 ? 2 : nk - 1, 2);
+  vm_wait<(AHEAD - 1) * S::PER_STEP>();
+  __builtin_amdgcn_s_barrier();
+  Half f0, f1;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) f0.sc[x] = f1.sc[x] = 0u;
+  f0.as = f1.as = 0x7F7F7F7Fu;
+  read_half(f0, 0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt % S::NST;
+    read_half(f1, st, 1, kt);
+    wait_half(f0);
+    mfma_half(f0, 0);
+    vm_wait<(AHEAD - 2) * S::PER_STEP>();
+    __builtin_amdgcn_s_barrier();
+    issue(kt + AHEAD < nk ? kt + AHEAD : nk - 1, (kt + AHEAD) % S::NST);
+    read_half(f0, (kt + 1) % S::NST, 0, kt + 1);
+    wait_half(f1);
+    mfma_half(f1, 1);
+  }
+  if constexpr (WF == W_FP8)
+    MOE_F8_WAIT_FP8(f0, 0);
+  else
+    MOE_F8_WAIT_FP4(f0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#undef MOE_F8_WAIT_A
+#undef MOE_F8_WAIT_FP8
+#undef MOE_F8_WAIT_FP4
+  __builtin_amdgcn_s_barrier();
+
+  // ---- epilogue (strips reuse the pipeline's LDS; row data lies past it)
+  const float gsc = WF == W_FP4 ? 8.f * a.w_gscale[e] : 1.f;
+  const float* chs = WF == W_FP8 ? static_cast<const float*>(a.w_scale) + (size_t)e * N : nullptr;
+  auto tile_row = [&](int r) { return 8 * (r >> 2) + 4 * kh + (r & 3); };
+  if (GATE_UP) {
+    float sg[2], su[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      sg[j] = WF == W_FP8 ? chs[mcol(bcol(j) + l32)] : gsc;
+      su[j] = WF == W_FP8 ? chs[mcol(bcol(j + 2) + l32)] : gsc;
+    }
+    const float* xs = reinterpret_cast<const float*>(rowdata);
+    uint16_t* strip = reinterpret_cast<uint16_t*>(smem + wave * 4096);  // 32 x 64 bf16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float rs = xs[(128 * wm + 32 * i + tile_row(r)) * (S::ROWB / 4)];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          strip[tile_row(r) * 64 + 32 * j + l32] = (uint16_t)f32_to_bf16_bits(
+              silu(acc[i][j][r] * (rs * sg[j])) * (acc[i][j + 2][r] * (rs * su[j])));
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int c = lane + 64 * t, rr = c >> 3, ch = c & 7;
+        const int m = m0 + 128 * wm + 32 * i + rr;
+        const int col = nt * (S::BN / 2) + 64 * wn + 8 * ch;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(strip + rr * 64 + 8 * ch);
+        if (m < cnt && col < a.I)
+          *reinterpret_cast<u32x4*>(a.h_out + (size_t)(r0 + m) * a.I + col) = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  } else {
+    float sd[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sd[j] = WF == W_FP8 ? chs[mcol(bcol(j) + l32)] : gsc;
+    float* strip = reinterpret_cast<float*>(smem + wave * 16384);  // 32 x 128 fp32
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) strip[tile_row(r) * 128 + 32 * j + l32] = acc[i][j][r] * sd[j];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int c = lane + 64 * t, rr = c >> 5, ch = c & 31;
+        const int m = m0 + 128 * wm + 32 * i + rr;
+        const int col = nt * S::BN + 128 * wn + 4 * ch;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(strip + rr * 128 + 4 * ch);
+        if (m < cnt && col < N) *reinterpret_cast<f32x4*>(a.y_out + (size_t)(r0 + m) * N + col) = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+}
+
+// Activations -> E4M3 codes with one fp32 scale per token (amax / 448, 1 for a
+// zero row); one workgroup per token, 8 values per lane per pass.
+__global__ __launch_bounds__(256) void quant_x_kernel(const uint16_t* __restrict__ x, int H,
+                                                      uint8_t* __restrict__ xq,
+                                                      float* __restrict__ xs) {
+  __shared__ float red[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const uint16_t* xr = x + (size_t)t * H;
+  float m = 0.f;
+  for (int c = 8 * tid; c < H; c += 2048) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(xr + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m = fmaxf(m, fabsf(__uint_as_float(q[i] << 16)));
+      m = fmaxf(m, fabsf(__uint_as_float(q[i] & 0xFFFF0000u)));
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+  if (tid == 0) xs[t] = s;
+  for (int c = 8 * tid; c < H; c += 2048) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(xr + c);
+    uint32_t o[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float v0 = __uint_as_float(q[2 * h] << 16) / s;
+      const float v1 = __uint_as_float(q[2 * h] & 0xFFFF0000u) / s;
+      const float v2 = __uint_as_float(q[2 * h + 1] << 16) / s;
+      const float v3 = __uint_as_float(q[2 * h + 1] & 0xFFFF0000u) / s;
+      const int32_t r = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+      o[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, r, true);
+    }
+    *reinterpret_cast<uint2*>(xq + (size_t)t * H + c) = make_uint2(o[0], o[1]);
+  }
+}
+
+// h (bf16) -> E4M3 codes with one E8M0 scale per row and 128-column block: the
+// smallest 2^e with 448 * 2^e >= the block's amax (clamped to [-127, 127]; 0
+// for a zero block). One wavefront per row; 16 lanes x 8 values per block.
+__global__ __launch_bounds__(256) void quant_h_kernel(const uint16_t* __restrict__ h, int P, int I,
+                                                      uint8_t* __restrict__ hq,
+                                                      uint8_t* __restrict__ hs, int hs_stride) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= P) return;
+  const uint16_t* hr = h + (size_t)row * I;
+  for (int c0 = 0; c0 < I; c0 += 512) {
+    const int c = c0 + 8 * lane;
+    const bool ok = c < I;
+    u32x4 q = u32x4{0u, 0u, 0u, 0u};
+    if (ok) q = *reinterpret_cast<const u32x4*>(hr + c);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(q[i] << 16);
+      v[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));  // within 16 lanes
+    const uint32_t mb = __float_as_uint(m);
+    const int ex = (int)(mb >> 23), man = (int)(mb & 0x7FFFFF);
+    int eb;
+    if (mb == 0u)
+      eb = 0;
+    else if (ex == 0)
+      eb = -127;  // subnormal amax: far below the clamp
+    else
+      eb = (man <= 0x600000) ? ex - 127 - 8 : ex - 127 - 7;
+    eb = eb < -127 ? -127 : (eb > 127 ? 127 : eb);
+    // 2^-eb as fp32 (a normal number: eb <= 120 for any bf16 amax, and
+    // eb = -127 gives 2^127); the scaled values are exact
+    const float inv = __uint_as_float((uint32_t)(127 - eb) << 23);
+    uint32_t o[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int32_t r = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * hh] * inv, v[4 * hh + 1] * inv, 0, false);
+      o[hh] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v[4 * hh + 2] * inv, v[4 * hh + 3] * inv, r, true);
+    }
+    if (ok) {
+      *reinterpret_cast<uint2*>(hq + (size_t)row * I + c) = make_uint2(o[0], o[1]);
+      if ((lane & 15) == 0) hs[(size_t)row * hs_stride + c / 128] = (uint8_t)(eb + 127);
+    }
+  }
+}
+
 // fp32 router weights [H, E] -> three bf16 planes [3][H][256] (columns >= E zero):
 // hi = RNE(w), mid = RNE(w - hi), lo = RNE(w - hi - mid); both differences are
 // exact in fp32. Also writes the one-expert offsets {0, T} the tiled kernel uses.
@@ -876,6 +1368,60 @@ static hipError_t launch_all(const StreamGemmArgs& gu, const StreamGemmArgs& dn,
     if (err == hipSuccess) err = launch_q<WF, false, 1>(dn, half_e, half_m0, counts + 1, E, st);
   }
   return err;
+}
+
+template <int WF, bool GATE_UP, int WM>
+static hipError_t launch_f8(const F8Args& f8, const StreamGemmArgs& g, const int32_t* te,
+                            const int32_t* tm, const int32_t* nt_p, int max_tiles, hipStream_t st) {
+  using S = F8Shape<WF, WM>;
+  const int NT = GATE_UP ? (g.I + S::BN / 2 - 1) / (S::BN / 2) : (g.N + S::BN - 1) / S::BN;
+  const long long items = (long long)max_tiles * NT;
+  const unsigned grid = (unsigned)(((items + 7) / 8) * 8);
+  if (grid == 0) return hipSuccess;
+  tile_f8_kernel<WF, GATE_UP, WM><<<grid, 256, 0, st>>>(f8, g, te, tm, nt_p, NT);
+  return hipGetLastError();
+}
+
+template <int WF>
+static hipError_t launch_f8_all(const StreamGemmArgs& gu, const StreamGemmArgs& dn, int T, int P,
+                                const F8Buffers& b, const int32_t* tile_e, const int32_t* tile_m0,
+                                const int32_t* half_e, const int32_t* half_m0,
+                                const int32_t* counts, int max_tiles, hipStream_t st) {
+  const int E = gu.E;
+  quant_x_kernel<<<T, 256, 0, st>>>(gu.a, gu.K, b.xq, b.xs);
+  hipError_t err = hipGetLastError();
+  F8Args fg{b.xq, b.xs, nullptr, 0};
+  if (err == hipSuccess) err = launch_f8<WF, true, 2>(fg, gu, tile_e, tile_m0, counts, max_tiles, st);
+  if (err == hipSuccess) err = launch_f8<WF, true, 1>(fg, gu, half_e, half_m0, counts + 1, E, st);
+  if (err != hipSuccess) return err;
+  quant_h_kernel<<<(P + 3) / 4, 256, 0, st>>>(gu.h_out, P, gu.I, b.hq, b.hs, b.hs_stride);
+  err = hipGetLastError();
+  F8Args fd{b.hq, nullptr, b.hs, b.hs_stride};
+  if (err == hipSuccess) err = launch_f8<WF, false, 2>(fd, dn, tile_e, tile_m0, counts, max_tiles, st);
+  if (err == hipSuccess) err = launch_f8<WF, false, 1>(fd, dn, half_e, half_m0, counts + 1, E, st);
+  return err;
+}
+
+hipError_t launch_expert_f8(int wfmt, const StreamGemmArgs& gu, const StreamGemmArgs& dn, int T,
+                            int P, const F8Buffers& bufs, void* ws, hipStream_t st) {
+  const int E = gu.E;
+  const int max_tiles = (P + TBM - 1) / TBM + E;
+  int32_t* tile_e = static_cast<int32_t*>(ws);
+  int32_t* tile_m0 = tile_e + max_tiles;
+  int32_t* half_e = tile_m0 + max_tiles;
+  int32_t* half_m0 = half_e + E;
+  int32_t* counts = half_m0 + E;
+  tile_table_kernel<<<1, 256, 0, st>>>(gu.offsets, E, TBM, 1, tile_e, tile_m0, counts, half_e,
+                                       half_m0, counts + 1);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (wfmt == W_FP8)
+    return launch_f8_all<W_FP8>(gu, dn, T, P, bufs, tile_e, tile_m0, half_e, half_m0, counts,
+                                max_tiles, st);
+  if (wfmt == W_FP4)
+    return launch_f8_all<W_FP4>(gu, dn, T, P, bufs, tile_e, tile_m0, half_e, half_m0, counts,
+                                max_tiles, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_expert_tile(int wfmt, const StreamGemmArgs& gu, const StreamGemmArgs& dn, int P,

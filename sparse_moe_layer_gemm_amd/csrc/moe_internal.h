@@ -63,6 +63,22 @@ struct StreamGemmArgs {
   int nsplit = 1, nk_split = 1;
   long long w_plane_stride = 0, y_split_stride = 0;
 };
+// fp8-MFMA mode operands: E4M3 codes of x (gate/up) with one fp32 scale per
+// token, or of h (down) with one E8M0 scale per row and 128-column block.
+struct F8Args {
+  const uint8_t* a8;       // [T, H] (gate/up, gathered by token) or [P, I] (down)
+  const float* x_scale;    // gate/up: [T]
+  const uint8_t* h_bscale; // down: [P, h_bstride] E8M0 codes
+  int h_bstride;
+};
+struct F8Buffers {         // device scratch of the fp8-MFMA mode
+  uint8_t* xq;             // [T, H]
+  float* xs;               // [T]
+  uint8_t* hq;             // [P, I]
+  uint8_t* hs;             // [P, hs_stride]
+  int hs_stride;           // >= ceil(I / 128), a multiple of 4
+};
+
 // Grouped expert GEMM for small row counts per expert: each wavefront owns a
 // 128-column slice of one expert's matrix and streams it once per 32 rows.
 hipError_t launch_expert_stream(int wfmt, bool gate_up, const StreamGemmArgs& a, hipStream_t st);
@@ -71,6 +87,10 @@ hipError_t launch_expert_stream(int wfmt, bool gate_up, const StreamGemmArgs& a,
 // double-buffered LDS (bf16 weights). Runs gate/up then down; ws holds the
 // M-tile table (expert_tile_ws_bytes).
 size_t expert_tile_ws_bytes(int P, int E);
+// fp8-MFMA mode of the quantised experts (x and h quantised in-kernel; the
+// gate/up output h in gate_up.h_out is bf16 scratch of the same size as usual).
+hipError_t launch_expert_f8(int wfmt, const StreamGemmArgs& gate_up, const StreamGemmArgs& down,
+                            int T, int P, const F8Buffers& bufs, void* tile_ws, hipStream_t st);
 hipError_t launch_expert_tile(int wfmt, const StreamGemmArgs& gate_up, const StreamGemmArgs& down,
                               int P, void* ws, hipStream_t st);
 // Router logits as three bf16 GEMMs on the tiled kernel: the fp32 router

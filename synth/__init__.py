@@ -48,6 +48,7 @@ class MoEConfig:
     router_only: bool = False
     zipf_s: float | None = None  # per-expert router bias shaping the load
     weight_seed: int | None = None  # expert weights drawn from this seed instead
+    qmode: str = "w"  # quantised weights: "w" (exact dequant, bf16 MFMA) | "f8" (fp8 MFMA)
 
     @property
     def pairs(self) -> int:

@@ -42,8 +42,8 @@ def test_status_strings():
     assert lib.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
 
 
-def _w(dtype=1, gu=A, dn=B, gus=None, dns=None, gug=None, dng=None):
-    return moe.CExpertWeights(dtype, 0, gu, dn, gus, dns, gug, dng)
+def _w(dtype=1, gu=A, dn=B, gus=None, dns=None, gug=None, dng=None, qmode=0):
+    return moe.CExpertWeights(dtype, qmode, gu, dn, gus, dns, gug, dng)
 
 
 def route(**kw):
@@ -115,6 +115,20 @@ def test_experts_validation():
     assert experts(w=_w(gu=MIS)) == INVAL
     assert experts(ws_bytes=1) == WS_SMALL
     assert moe.load_library().moe_experts(A, 1, 8, 64, 64, 8, 2, B, C, None, D, F, 1 << 30, None) == INVAL
+
+
+def test_experts_qmode_validation():
+    fp4 = dict(dtype=3, gus=G, dns=Hh, gug=A, dng=B)
+    assert experts(w=_w(qmode=7)) == INVAL
+    assert experts(w=_w(dtype=1, qmode=1)) == UNSUP  # fp8-MFMA mode is for quantised weights
+    assert experts(w=_w(**fp4, qmode=1), I=4160) == UNSUP  # h block scales: I <= 4096
+    assert experts(w=_w(**fp4, qmode=1), T=0, x=None, offsets=None, sp=None, y=None, ws=None) == OK
+    lib = moe.load_library()
+    ww, w8 = _w(**fp4), _w(**fp4, qmode=1)
+    sw = lib.moe_experts_workspace_size(4096, 5120, 1536, 256, 8, ctypes.byref(ww))
+    s8 = lib.moe_experts_workspace_size(4096, 5120, 1536, 256, 8, ctypes.byref(w8))
+    # the fp8 mode adds E4M3 x [T, H], per-token scales, E4M3 h [T*k, I] and block scales
+    assert s8 >= sw + 4096 * 5120 + 4096 * 4 + 4096 * 8 * 1536 + 4096 * 8 * 12
 
 
 def test_experts_workspace_size():

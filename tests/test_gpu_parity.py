@@ -40,6 +40,13 @@ SMALL = [
     MC("fp8_tile", 114, T=200, H=256, E=8, k=4, I=192, w_dtype="fp8"),
     MC("fp4_tile_ragged", 115, T=150, H=192, E=4, k=2, I=192, w_dtype="fp4"),
     MC("fp4_tile_zipf", 116, T=512, H=256, E=16, k=4, I=128, zipf_s=1.1, w_dtype="fp4"),
+    # fp8-MFMA mode (against the oracle's F8 encodings): few and many rows per
+    # expert, partial N tiles and a partial 128-column h block (I = 192),
+    # Zipf load for both tile shapes
+    MC("f8_fp8_tile", 117, T=200, H=256, E=8, k=4, I=192, w_dtype="fp8", qmode="f8"),
+    MC("f8_fp4_ragged", 118, T=150, H=192, E=4, k=2, I=192, w_dtype="fp4", qmode="f8"),
+    MC("f8_fp4_zipf", 119, T=512, H=256, E=16, k=4, I=128, zipf_s=1.1, w_dtype="fp4", qmode="f8"),
+    MC("f8_fp8_few_rows", 120, T=20, H=128, E=8, k=2, I=64, w_dtype="fp8", qmode="f8"),
 ]
 
 
@@ -183,9 +190,11 @@ def test_prefill_zipf_sampled():
         f"logits {rt['logit_rel_err']:.2e}; y {ey:.2e} over {len(rows)} rows; out {lay['out_rel_err']:.2e}")
 
 
-@pytest.mark.parametrize("wdt,T", [("fp4", 4096), ("fp8", 1024)])
-def test_quantised_beam_sampled(wdt, T):
-    cfg = synth.CONFIGS["nvfp4_t4096"].with_(name=f"{wdt}_t{T}", w_dtype=wdt, T=T)
+@pytest.mark.parametrize("wdt,T,qmode", [("fp4", 4096, "w"), ("fp8", 1024, "w"),
+                                         ("fp4", 4096, "f8"), ("fp8", 1024, "f8")])
+def test_quantised_beam_sampled(wdt, T, qmode):
+    cfg = synth.CONFIGS["nvfp4_t4096"].with_(name=f"{wdt}_t{T}_{qmode}", w_dtype=wdt, T=T,
+                                             qmode=qmode)
     log(f"[parity] {cfg.name}: generating inputs")
     L = Layer(cfg)
     r = L.stages()

@@ -150,6 +150,8 @@ def test_f8_rows_match_numpy_on_quantised_operands(fmt):
             want = oracle.format_op("round_e4m3", blk * 2.0 ** -eb) * 2.0 ** eb
             assert np.array_equal(hq[r, b0:b0 + 128], want)
         np.testing.assert_allclose(y[r], (hq[r] @ dn[e].T) * sdn[e], rtol=1e-11, atol=1e-13)
+    # the down stage alone, fed the same h, reproduces the rows
+    assert np.array_equal(oracle.down_rows_f8(h, q, eid, H), y)
 
 
 def test_f8_error_against_exact_path_is_small():
