@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s (H5120,E256,k8) + % peak HBM BW decode / % MFMA prefill"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 
 
 def parse():
@@ -301,6 +302,30 @@ def main():
                                "unit": "GB/s" if hbm_frac >= mfma_frac else "TFLOP/s",
                                "frac": max(hbm_frac, mfma_frac), "traffic": None,
                                "weight_GBps": round(tb, 1), "TFLOPs": round(tf, 1)}}
+        # the same layer in the fp8-MFMA mode (activations quantised in-kernel)
+        progress("timing NVFP4, fp8-MFMA mode")
+        import dataclasses
+        qw.w = dataclasses.replace(qw.w, qmode=moe.MOE_QMODE_F8)
+        qw.ws = moe.workspace(moe.moe_forward_workspace_size(q_cfg.T, q_cfg.H, q_cfg.I, q_cfg.E,
+                                                             q_cfg.k, qw.w))
+        qw.ews = moe.workspace(moe.moe_experts_workspace_size(q_cfg.T, q_cfg.H, q_cfg.I, q_cfg.E,
+                                                              q_cfg.k, qw.w))
+        f_ms = qw.time_forward(qsteps, max(1, a.warmup // 2))
+        f_stage = qw.time_stages(qsteps)
+        tb8 = wbytes / (f_stage["experts"] / 1e3) / 1e9
+        tf8 = flops / (f_stage["experts"] / 1e3) / 1e12
+        h8, m8 = tb8 / HBM_PEAK_GBS, tf8 / FP8_PEAK_TFLOPS
+        q_line["fp8_mfma_mode"] = {
+            "value": round(q_cfg.T / (f_ms / 1e3), 1), "unit": "tokens/s",
+            "ms_per_step": round(f_ms, 4),
+            "stages_ms": {k: round(v, 4) for k, v in f_stage.items()},
+            "roofline": {"bound": "hbm" if h8 >= m8 else "mfma",
+                         "kernel": "moe_experts (NVFP4 weights, fp8 MFMA)",
+                         "achieved": tb8 if h8 >= m8 else tf8,
+                         "peak": HBM_PEAK_GBS if h8 >= m8 else FP8_PEAK_TFLOPS,
+                         "unit": "GB/s" if h8 >= m8 else "TFLOP/s",
+                         "frac": max(h8, m8), "traffic": None,
+                         "weight_GBps": round(tb8, 1), "TFLOPs": round(tf8, 1)}}
         del qw
 
     head, head_cfg = (dec_line, dec_cfg) if a.workload == "decode" else (pre_line, pre_cfg)
