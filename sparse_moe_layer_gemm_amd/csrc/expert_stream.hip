@@ -42,6 +42,12 @@ __device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, const
 __device__ __forceinline__ u32x4 load_u32x4(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
+// Weight loads: every weight byte is read once per pass, so they bypass the
+// caches' retention (nontemporal); measured on gfx950 this lifts a plain
+// streaming read from ~6.3 to ~7.0 TB/s.
+__device__ __forceinline__ u32x4 load_w(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 // Rows of the A operand for one 32-row pass: pointer per fragment + validity.
 struct ARows {
@@ -99,7 +105,7 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
     const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int r = 0; r < 8; ++r)
-      braw[r] = col_ok ? load_u32x4(wb + (size_t)(8 * g + r) * N) : zero;
+      braw[r] = col_ok ? load_w(wb + (size_t)(8 * g + r) * N) : zero;
 
     for (int ks = 0; ks < nk; ++ks) {
       u32x4 af[2];
@@ -111,7 +117,7 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
       u32x4 bnext[8];
 #pragma unroll
       for (int r = 0; r < 8; ++r)
-        bnext[r] = col_ok ? load_u32x4(wb + (size_t)(kn * 32 + 8 * g + r) * N) : zero;
+        bnext[r] = col_ok ? load_w(wb + (size_t)(kn * 32 + 8 * g + r) * N) : zero;
 
       // 8x8 transpose: fragment for column 2q / 2q+1 from dword q of rows 2p, 2p+1
 #pragma unroll
@@ -271,7 +277,7 @@ __global__ __launch_bounds__(256) void stream_kmajor_kernel(StreamGemmArgs a) {
       for (int cg = 0; cg < 8; ++cg) {
         const bool ok = k_ok && cok[cg];
         const size_t rowoff = ((size_t)e * N + (cok[cg] ? colv[cg] : 0)) * row_bytes;
-        braw[cg] = ok ? load_u32x4(wq + rowoff + ((WF == W_FP8) ? kl : kl / 2)) : zero;
+        braw[cg] = ok ? load_w(wq + rowoff + ((WF == W_FP8) ? kl : kl / 2)) : zero;
         if (WF == W_FP4) {
           const uint8_t* sp = static_cast<const uint8_t*>(a.w_scale) +
                               ((size_t)e * N + (cok[cg] ? colv[cg] : 0)) * (K / 16) + kl / 16;
