@@ -126,7 +126,9 @@ moe_status moe_route(const void* x, int32_t x_dtype, int64_t T, int32_t H, const
  * T*k); sorted_pair[r] = the r-th pair in (expert, p) order; pair_pos is its
  * inverse (pair_pos[sorted_pair[r]] = r). Results are deterministic.
  * Ids outside [0, E) are not counted and not written (the outputs are then
- * incomplete; the router never produces them). */
+ * incomplete; the router never produces them). Up to 16384 pairs no
+ * workspace is needed (NULL allowed); above, moe_permute_workspace_size()
+ * bytes of scratch hold per-segment histograms. */
 size_t moe_permute_workspace_size(int64_t T, int32_t k, int32_t E);
 moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t* counts,
                        int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, void* workspace,

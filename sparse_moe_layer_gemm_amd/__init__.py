@@ -149,6 +149,9 @@ def moe_permute_workspace_size(T: int, k: int, E: int) -> int:
 def moe_permute(topk_ids, E: int, counts, offsets, sorted_pair, pair_pos, workspace=None,
                 stream=None):
     T, k = topk_ids.shape
+    if workspace is None:
+        need = moe_permute_workspace_size(T, k, E)
+        workspace = globals()["workspace"](need, topk_ids.device) if need else None
     _check("moe_permute", _lib.moe_permute(
         _ptr(topk_ids), T, k, E, _ptr(counts), _ptr(offsets), _ptr(sorted_pair), _ptr(pair_pos),
         _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),

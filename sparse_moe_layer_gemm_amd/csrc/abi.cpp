@@ -272,17 +272,13 @@ moe_status moe_route(const void* x, int32_t x_dtype, int64_t T, int32_t H, const
 
 // ---------------------------------------------------------------- permute
 size_t moe_permute_workspace_size(int64_t T, int32_t k, int32_t E) {
-  (void)T;
-  (void)k;
-  (void)E;
-  return 0;
+  if (T <= 0 || k <= 0 || E <= 0 || E > 256) return 0;
+  return moe::permute_ws_bytes(T * k, E);
 }
 
 moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t* counts,
                        int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, void* workspace,
                        size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (T < 0 || E <= 0 || k <= 0 || k > E) return MOE_ERR_INVALID_ARGUMENT;
   if (k > 8 || E > 256) return MOE_ERR_UNSUPPORTED;
   if (T * k > kMaxPairs || T >= kMaxTokens) return MOE_ERR_UNSUPPORTED;
@@ -291,8 +287,13 @@ moe_status moe_permute(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
   if (!aligned16(topk_ids) || !aligned16(counts) || !aligned16(offsets) ||
       !aligned16(sorted_pair) || !aligned16(pair_pos))
     return MOE_ERR_INVALID_ARGUMENT;
+  const size_t need = moe::permute_ws_bytes(T * k, E);
+  if (need > 0) {
+    if (!workspace || !aligned16(workspace)) return MOE_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  }
   return launch_status(moe::launch_permute(topk_ids, (int)(T * k), E, counts, offsets, sorted_pair,
-                                           pair_pos, static_cast<hipStream_t>(stream)));
+                                           pair_pos, workspace, static_cast<hipStream_t>(stream)));
 }
 
 // ---------------------------------------------------------------- experts
@@ -347,7 +348,8 @@ size_t moe_forward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, in
   return route_ws_bytes(T, H, E) + align_up((size_t)T * E * sizeof(float)) +
          2 * align_up(P * sizeof(int32_t)) /* ids, w */ + align_up(E * sizeof(int32_t)) +
          align_up((E + 1) * sizeof(int32_t)) + 2 * align_up(P * sizeof(int32_t)) +
-         align_up(P * H * sizeof(float)) + experts_ws_bytes(T, H, I, E, k, w);
+         align_up(P * H * sizeof(float)) + experts_ws_bytes(T, H, I, E, k, w) +
+         align_up(moe::permute_ws_bytes((long long)P, E));
 }
 
 moe_status moe_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I, int32_t E,
@@ -385,6 +387,7 @@ moe_status moe_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
   int32_t* pair_pos = static_cast<int32_t*>(c.take(P * sizeof(int32_t)));
   float* y_sorted = static_cast<float*>(c.take(P * H * sizeof(float)));
   void* exp_ws = c.take(experts_ws_bytes(T, H, I, E, k, w));
+  void* perm_ws = c.take(moe::permute_ws_bytes((long long)P, E));
   if (topk_ids) ids = topk_ids;
   if (topk_w) tw = topk_w;
   if (!logits) logits = lbuf;
@@ -392,7 +395,8 @@ moe_status moe_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
   s = enqueue_route(x, x_dtype, T, H, w_router, bias, E, k, logits_dtype, logits, nullptr, ids, tw,
                     route_ws, st);
   if (s != MOE_OK) return s;
-  s = launch_status(moe::launch_permute(ids, (int)P, E, counts, offsets, sorted_pair, pair_pos, st));
+  s = launch_status(
+      moe::launch_permute(ids, (int)P, E, counts, offsets, sorted_pair, pair_pos, perm_ws, st));
   if (s != MOE_OK) return s;
   s = enqueue_experts(x, x_dtype, T, H, I, E, k, offsets, sorted_pair, w, y_sorted, exp_ws, st);
   if (s != MOE_OK) return s;

@@ -39,9 +39,12 @@ hipError_t launch_router_gemm(const void* x, bool x_bf16, int T, int H, const fl
 hipError_t launch_router_select(const float* part, int n_split, int ldp, int T, int E, int k,
                                 const float* bias, bool logits_bf16, void* logits,
                                 float* logits_f32, int32_t* ids, float* w, hipStream_t st);
-// Stable counting sort of pairs by expert.
+// Stable counting sort of pairs by expert (one workgroup up to
+// kPermuteOneBlockMax pairs, else three kernels with permute_ws_bytes of scratch).
+constexpr long long kPermuteOneBlockMax = 16384;
+size_t permute_ws_bytes(long long P, int E);
 hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
-                          int32_t* sorted_pair, int32_t* pair_pos, hipStream_t st);
+                          int32_t* sorted_pair, int32_t* pair_pos, void* ws, hipStream_t st);
 
 enum WFormat { W_BF16 = 1, W_FP8 = 2, W_FP4 = 3 };
 

@@ -4,11 +4,13 @@
 // every pair again (vLLM PR #61978: "MoE finalize" is the weighted
 // un-permute of these rows, Status table row #62366).
 //
-// One workgroup of 16 wavefronts. Each wavefront owns a contiguous segment of
-// pairs and keeps its own 256-bin histogram in LDS, so no atomics are needed
-// and the result is deterministic: ranks within a 64-pair chunk come from a
-// ballot-based match of equal expert ids, chunks are walked in order, and
-// segments are ordered by wavefront index.
+// Each wavefront owns a contiguous segment of pairs and keeps its own 256-bin
+// histogram in LDS, so no atomics are needed and the result is deterministic:
+// ranks within a 64-pair chunk come from a ballot-based match of equal expert
+// ids, chunks are walked in order, and segments are ordered by index. Up to
+// 16384 pairs one workgroup of 16 wavefronts does it all; above, segments of
+// >= 512 pairs spread over many workgroups with a scan kernel between the
+// histogram and scatter passes.
 #include "moe_internal.h"
 
 namespace moe {
@@ -110,11 +112,155 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
   }
 }
 
+// ---- many pairs: the same per-wavefront algorithm over NV segments spread
+// across workgroups. Segment v (wavefront v % 16 of workgroup v / 16) holds
+// pairs [v * seg, (v + 1) * seg); its histogram goes to hist_g[e * NV + v]
+// (expert-major), one workgroup turns those into scatter starts, and the
+// scatter pass replays the same stable ranks.
+__global__ __launch_bounds__(1024) void permute_hist_kernel(const int32_t* __restrict__ ids, int P,
+                                                            int E, int seg, int NV,
+                                                            int32_t* __restrict__ hist_g) {
+  __shared__ int hist[PW][256];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < PW * 256; i += 1024) (&hist[0][0])[i] = 0;
+  __syncthreads();
+  const int v = blockIdx.x * PW + wave;
+  const long long s0l = (long long)v * seg;
+  const int s0 = (int)(s0l < P ? s0l : P), s1 = (int)(s0l + seg < P ? s0l + seg : P);
+  for (int c = s0; c < s1; c += 64) {
+    const int p = c + lane;
+    int id = (p < s1) ? ids[p] : -1;
+    const bool valid = id >= 0 && id < E;
+    if (!valid) id = 0;
+    const uint64_t peers = match_peers(id, valid);
+    if (valid && lane == 63 - __builtin_clzll(peers)) hist[wave][id] += __popcll(peers);
+  }
+  __syncthreads();
+  if (v < NV)
+    for (int e = lane; e < E; e += 64) hist_g[(size_t)e * NV + v] = hist[wave][e];
+}
+
+// One workgroup: for every expert, exclusive prefix of its segment counts in
+// segment order (4 threads per expert, each over a quarter of the segments),
+// then the scan over experts; hist_g becomes each segment's first position.
+__global__ __launch_bounds__(1024) void permute_scan_kernel(int E, int NV, int32_t* __restrict__ hist_g,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets) {
+  __shared__ int part[256][4];
+  __shared__ int base[256];
+  __shared__ int total;
+  const int tid = threadIdx.x, e = tid >> 2, q = tid & 3;
+  const int per = (NV + 3) / 4;
+  const int v0 = min(NV, q * per), v1 = min(NV, v0 + per);
+  int sum = 0;
+  if (e < E)
+    for (int v = v0; v < v1; ++v) sum += hist_g[(size_t)e * NV + v];
+  part[e][q] = sum;
+  __syncthreads();
+  if (tid < 256) {
+    const int c = tid < E ? part[tid][0] + part[tid][1] + part[tid][2] + part[tid][3] : 0;
+    base[tid] = c;
+    if (tid < E) counts[tid] = c;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int lane = tid;
+    const int w0 = base[4 * lane], w1 = base[4 * lane + 1], w2 = base[4 * lane + 2],
+              w3 = base[4 * lane + 3];
+    const int s = w0 + w1 + w2 + w3;
+    int incl = s;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    const int ex = incl - s;
+    if (lane == 63) total = incl;
+    base[4 * lane] = ex;
+    base[4 * lane + 1] = ex + w0;
+    base[4 * lane + 2] = ex + w0 + w1;
+    base[4 * lane + 3] = ex + w0 + w1 + w2;
+  }
+  __syncthreads();
+  if (e < E) {
+    int run = base[e];
+    for (int qq = 0; qq < q; ++qq) run += part[e][qq];
+    for (int v = v0; v < v1; ++v) {
+      const int c = hist_g[(size_t)e * NV + v];
+      hist_g[(size_t)e * NV + v] = run;
+      run += c;
+    }
+  }
+  if (tid < E) offsets[tid] = base[tid];
+  if (tid == 0) offsets[E] = total;
+}
+
+__global__ __launch_bounds__(1024) void permute_scatter_kernel(const int32_t* __restrict__ ids,
+                                                               int P, int E, int seg, int NV,
+                                                               const int32_t* __restrict__ hist_g,
+                                                               int32_t* __restrict__ sorted_pair,
+                                                               int32_t* __restrict__ pair_pos) {
+  __shared__ int hist[PW][256];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int v = blockIdx.x * PW + wave;
+  if (v < NV)
+    for (int e = lane; e < E; e += 64) hist[wave][e] = hist_g[(size_t)e * NV + v];
+  __syncthreads();
+  const long long s0l = (long long)v * seg;
+  const int s0 = (int)(s0l < P ? s0l : P), s1 = (int)(s0l + seg < P ? s0l + seg : P);
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int c = s0; c < s1; c += 64) {
+    const int p = c + lane;
+    int id = (p < s1) ? ids[p] : -1;
+    const bool valid = id >= 0 && id < E;
+    if (!valid) id = 0;
+    const uint64_t peers = match_peers(id, valid);
+    if (valid) {
+      const int pos = hist[wave][id] + __popcll(peers & below);
+      sorted_pair[pos] = p;
+      pair_pos[p] = pos;
+    }
+    if (valid && lane == 63 - __builtin_clzll(peers)) hist[wave][id] += __popcll(peers);
+  }
+}
+
 }  // namespace
 
+void permute_plan(long long P, int* seg, int* nv) {
+  // segments of at least 512 pairs (8 chunks per wavefront), at most 32768 of them
+  long long n = (P + 511) / 512;
+  if (n > 32768) n = 32768;
+  if (n < 1) n = 1;
+  long long s = (P + n - 1) / n;
+  s = (s + 63) / 64 * 64;
+  *seg = (int)s;
+  *nv = (int)((P + s - 1) / s);
+}
+
+size_t permute_ws_bytes(long long P, int E) {
+  if (P <= kPermuteOneBlockMax) return 0;
+  int seg, nv;
+  permute_plan(P, &seg, &nv);
+  return (size_t)E * nv * sizeof(int32_t);
+}
+
 hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
-                          int32_t* sorted_pair, int32_t* pair_pos, hipStream_t st) {
-  permute_kernel<<<1, 1024, 0, st>>>(ids, P, E, counts, offsets, sorted_pair, pair_pos);
+                          int32_t* sorted_pair, int32_t* pair_pos, void* ws, hipStream_t st) {
+  if (P <= kPermuteOneBlockMax) {
+    permute_kernel<<<1, 1024, 0, st>>>(ids, P, E, counts, offsets, sorted_pair, pair_pos);
+    return hipGetLastError();
+  }
+  int seg, nv;
+  permute_plan(P, &seg, &nv);
+  int32_t* hist_g = static_cast<int32_t*>(ws);
+  const unsigned blocks = (unsigned)((nv + PW - 1) / PW);
+  permute_hist_kernel<<<blocks, 1024, 0, st>>>(ids, P, E, seg, nv, hist_g);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  permute_scan_kernel<<<1, 1024, 0, st>>>(E, nv, hist_g, counts, offsets);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  permute_scatter_kernel<<<blocks, 1024, 0, st>>>(ids, P, E, seg, nv, hist_g, sorted_pair, pair_pos);
   return hipGetLastError();
 }
 

@@ -117,6 +117,15 @@ def test_experts_validation():
     assert moe.load_library().moe_experts(A, 1, 8, 64, 64, 8, 2, B, C, None, D, F, 1 << 30, None) == INVAL
 
 
+def test_permute_workspace():
+    lib = moe.load_library()
+    assert lib.moe_permute_workspace_size(2048, 8, 256) == 0  # one workgroup up to 16384 pairs
+    big = lib.moe_permute_workspace_size(16384, 8, 256)
+    assert big >= 256 * (131072 // 4096) * 4  # per-segment histograms
+    assert permute(T=16384, k=8, E=256, ws=None, ws_bytes=0) == INVAL
+    assert permute(T=16384, k=8, E=256, ws=G, ws_bytes=big - 1) == WS_SMALL
+
+
 def test_experts_qmode_validation():
     fp4 = dict(dtype=3, gus=G, dns=Hh, gug=A, dng=B)
     assert experts(w=_w(qmode=7)) == INVAL

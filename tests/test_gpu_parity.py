@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import sparse_moe_layer_gemm_amd as moe
 import synth
 from tests.gpu_harness import (Layer, bits, check_experts, check_finalize, check_layer,
                                check_permute, check_router, log)
@@ -103,6 +104,31 @@ def test_router_split_bf16_full(T, H, E, k):
     torch.cuda.synchronize()
     rt = check_router(L, r)
     log(f"  logits rel err {rt['logit_rel_err']:.2e}, ambiguous tokens {rt['ambiguous']}/{rt['tokens']}")
+
+
+# Above 16384 pairs the permute runs as histogram / scan / scatter kernels over
+# many workgroups; ids with heavy ties, ragged segment ends, few and many experts.
+@pytest.mark.parametrize("P,E", [(40000, 256), (16448, 7), (131072, 256)])
+def test_permute_many_pairs_bit_exact(P, E):
+    import oracle
+    rng = np.random.default_rng(P + E)
+    k = 8 if E >= 8 else 4
+    T = P // k
+    p = rng.zipf(1.3, size=(T, k)) % E  # skewed, so long runs of equal ids
+    ids = p.astype(np.int32)
+    d = torch.from_numpy(ids).cuda()
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    pp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    log(f"[parity] permute P={T * k} E={E}")
+    moe.moe_permute(d, E, counts, offsets, sp, pp)
+    torch.cuda.synchronize()
+    c, o, s, q = oracle.permute(ids, E)
+    assert np.array_equal(counts.cpu().numpy(), c)
+    assert np.array_equal(offsets.cpu().numpy(), o)
+    assert np.array_equal(sp.cpu().numpy(), s)
+    assert np.array_equal(pp.cpu().numpy(), q)
 
 
 @pytest.fixture(scope="module")
