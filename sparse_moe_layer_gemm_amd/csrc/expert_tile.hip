@@ -15,7 +15,9 @@
 //    128 x 512 tile (1 x 4 wavefronts, same 128 x 128 per wavefront) in a
 //    second launch: with skewed routing most experts hold a few hundred
 //    rows, and padding their tails to 256 rows wasted about a quarter of
-//    the MFMA work. The wider tile keeps the weight bytes per MAC unchanged;
+//    the MFMA work. The wider tile keeps the weight bytes per MAC unchanged.
+//    Quantised weights use the 128 x 512 tile throughout (their in-register
+//    conversion, not the MFMA, is the bound, and it is done once per column);
 //  - K advances 32 per step through four LDS stages filled by direct
 //    global->LDS loads (16 B per lane; no registers stage the tiles), issued
 //    three steps ahead of the MFMAs: with one wavefront per SIMD nothing else
@@ -1276,7 +1278,9 @@ constexpr int ROUTER_NKS = 2;  // K slices per plane (3 * 2 splits in all)
 }  // namespace
 
 size_t expert_tile_ws_bytes(int P, int E) {
-  const int max_tiles = (P + TBM - 1) / TBM + E;
+  // covers both tables: 128-row tiles (quantised) and 256-row tiles plus one
+  // partial tile per expert (bf16)
+  const int max_tiles = (P + 127) / 128 + E;
   return (size_t)(2 * max_tiles + 2 * E + 64) * sizeof(int32_t);
 }
 
@@ -1349,24 +1353,28 @@ static hipError_t launch_q(const StreamGemmArgs& g, const int32_t* te, const int
   return hipGetLastError();
 }
 
-template <int WF>
-static hipError_t launch_all(const StreamGemmArgs& gu, const StreamGemmArgs& dn,
-                             const int32_t* tile_e, const int32_t* tile_m0, const int32_t* half_e,
-                             const int32_t* half_m0, const int32_t* counts, int max_tiles,
-                             hipStream_t st) {
+static hipError_t launch_bf16_all(const StreamGemmArgs& gu, const StreamGemmArgs& dn,
+                                  const int32_t* tile_e, const int32_t* tile_m0,
+                                  const int32_t* half_e, const int32_t* half_m0,
+                                  const int32_t* counts, int max_tiles, hipStream_t st) {
   const int E = gu.E;
-  hipError_t err;
-  if constexpr (WF == W_BF16) {
-    err = launch_tiles<true, 2>(gu, tile_e, tile_m0, counts, max_tiles, st);
-    if (err == hipSuccess) err = launch_tiles<true, 1>(gu, half_e, half_m0, counts + 1, E, st);
-    if (err == hipSuccess) err = launch_tiles<false, 2>(dn, tile_e, tile_m0, counts, max_tiles, st);
-    if (err == hipSuccess) err = launch_tiles<false, 1>(dn, half_e, half_m0, counts + 1, E, st);
-  } else {
-    err = launch_q<WF, true, 2>(gu, tile_e, tile_m0, counts, max_tiles, st);
-    if (err == hipSuccess) err = launch_q<WF, true, 1>(gu, half_e, half_m0, counts + 1, E, st);
-    if (err == hipSuccess) err = launch_q<WF, false, 2>(dn, tile_e, tile_m0, counts, max_tiles, st);
-    if (err == hipSuccess) err = launch_q<WF, false, 1>(dn, half_e, half_m0, counts + 1, E, st);
-  }
+  hipError_t err = launch_tiles<true, 2>(gu, tile_e, tile_m0, counts, max_tiles, st);
+  if (err == hipSuccess) err = launch_tiles<true, 1>(gu, half_e, half_m0, counts + 1, E, st);
+  if (err == hipSuccess) err = launch_tiles<false, 2>(dn, tile_e, tile_m0, counts, max_tiles, st);
+  if (err == hipSuccess) err = launch_tiles<false, 1>(dn, half_e, half_m0, counts + 1, E, st);
+  return err;
+}
+
+// Quantised weights run on 128 x 512 tiles only. Their wavefronts sit side by
+// side along N, so each B column is converted by one wavefront (in the 2 x 2
+// layout of the 256 x 256 tile two wavefronts convert every column, and the
+// conversion is what bounds these kernels).
+template <int WF>
+static hipError_t launch_q_all(const StreamGemmArgs& gu, const StreamGemmArgs& dn,
+                               const int32_t* tile_e, const int32_t* tile_m0, const int32_t* counts,
+                               int max_tiles, hipStream_t st) {
+  hipError_t err = launch_q<WF, true, 1>(gu, tile_e, tile_m0, counts, max_tiles, st);
+  if (err == hipSuccess) err = launch_q<WF, false, 1>(dn, tile_e, tile_m0, counts, max_tiles, st);
   return err;
 }
 
@@ -1385,50 +1393,56 @@ static hipError_t launch_f8(const F8Args& f8, const StreamGemmArgs& g, const int
 template <int WF>
 static hipError_t launch_f8_all(const StreamGemmArgs& gu, const StreamGemmArgs& dn, int T, int P,
                                 const F8Buffers& b, const int32_t* tile_e, const int32_t* tile_m0,
-                                const int32_t* half_e, const int32_t* half_m0,
                                 const int32_t* counts, int max_tiles, hipStream_t st) {
-  const int E = gu.E;
   quant_x_kernel<<<T, 256, 0, st>>>(gu.a, gu.K, b.xq, b.xs);
   hipError_t err = hipGetLastError();
   F8Args fg{b.xq, b.xs, nullptr, 0};
-  if (err == hipSuccess) err = launch_f8<WF, true, 2>(fg, gu, tile_e, tile_m0, counts, max_tiles, st);
-  if (err == hipSuccess) err = launch_f8<WF, true, 1>(fg, gu, half_e, half_m0, counts + 1, E, st);
+  if (err == hipSuccess) err = launch_f8<WF, true, 1>(fg, gu, tile_e, tile_m0, counts, max_tiles, st);
   if (err != hipSuccess) return err;
   quant_h_kernel<<<(P + 3) / 4, 256, 0, st>>>(gu.h_out, P, gu.I, b.hq, b.hs, b.hs_stride);
   err = hipGetLastError();
   F8Args fd{b.hq, nullptr, b.hs, b.hs_stride};
-  if (err == hipSuccess) err = launch_f8<WF, false, 2>(fd, dn, tile_e, tile_m0, counts, max_tiles, st);
-  if (err == hipSuccess) err = launch_f8<WF, false, 1>(fd, dn, half_e, half_m0, counts + 1, E, st);
+  if (err == hipSuccess) err = launch_f8<WF, false, 1>(fd, dn, tile_e, tile_m0, counts, max_tiles, st);
   return err;
 }
 
 hipError_t launch_expert_f8(int wfmt, const StreamGemmArgs& gu, const StreamGemmArgs& dn, int T,
                             int P, const F8Buffers& bufs, void* ws, hipStream_t st) {
   const int E = gu.E;
-  const int max_tiles = (P + TBM - 1) / TBM + E;
+  if (wfmt != W_FP8 && wfmt != W_FP4) return hipErrorInvalidValue;
+  // one table of 128-row tiles (128 x 512 tiles, as for the exact dequantisation)
+  const int max_tiles = (P + 127) / 128 + E;
   int32_t* tile_e = static_cast<int32_t*>(ws);
   int32_t* tile_m0 = tile_e + max_tiles;
-  int32_t* half_e = tile_m0 + max_tiles;
-  int32_t* half_m0 = half_e + E;
-  int32_t* counts = half_m0 + E;
-  tile_table_kernel<<<1, 256, 0, st>>>(gu.offsets, E, TBM, 1, tile_e, tile_m0, counts, half_e,
-                                       half_m0, counts + 1);
+  int32_t* counts = tile_m0 + max_tiles;
+  tile_table_kernel<<<1, 256, 0, st>>>(gu.offsets, E, 128, 0, tile_e, tile_m0, counts, nullptr,
+                                       nullptr, nullptr);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (wfmt == W_FP8)
-    return launch_f8_all<W_FP8>(gu, dn, T, P, bufs, tile_e, tile_m0, half_e, half_m0, counts,
-                                max_tiles, st);
-  if (wfmt == W_FP4)
-    return launch_f8_all<W_FP4>(gu, dn, T, P, bufs, tile_e, tile_m0, half_e, half_m0, counts,
-                                max_tiles, st);
-  return hipErrorInvalidValue;
+    return launch_f8_all<W_FP8>(gu, dn, T, P, bufs, tile_e, tile_m0, counts, max_tiles, st);
+  return launch_f8_all<W_FP4>(gu, dn, T, P, bufs, tile_e, tile_m0, counts, max_tiles, st);
 }
 
 hipError_t launch_expert_tile(int wfmt, const StreamGemmArgs& gu, const StreamGemmArgs& dn, int P,
                               void* ws, hipStream_t st) {
   const int E = gu.E;
-  const int max_tiles = (P + TBM - 1) / TBM + E;
   int32_t* tile_e = static_cast<int32_t*>(ws);
+  if (wfmt == W_FP8 || wfmt == W_FP4) {
+    // one table of 128-row tiles: at most P/128 + E of them
+    const int max_tiles = (P + 127) / 128 + E;
+    int32_t* tile_m0 = tile_e + max_tiles;
+    int32_t* counts = tile_m0 + max_tiles;
+    tile_table_kernel<<<1, 256, 0, st>>>(gu.offsets, E, 128, 0, tile_e, tile_m0, counts, nullptr,
+                                         nullptr, nullptr);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (wfmt == W_FP8) return launch_q_all<W_FP8>(gu, dn, tile_e, tile_m0, counts, max_tiles, st);
+    return launch_q_all<W_FP4>(gu, dn, tile_e, tile_m0, counts, max_tiles, st);
+  }
+  if (wfmt != W_BF16) return hipErrorInvalidValue;
+  // full 256-row tiles plus each expert's last partial tile of <= 128 rows
+  const int max_tiles = (P + TBM - 1) / TBM + E;
   int32_t* tile_m0 = tile_e + max_tiles;
   int32_t* half_e = tile_m0 + max_tiles;
   int32_t* half_m0 = half_e + E;
@@ -1437,16 +1451,7 @@ hipError_t launch_expert_tile(int wfmt, const StreamGemmArgs& gu, const StreamGe
                                        half_m0, counts + 1);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  switch (wfmt) {
-    case W_BF16:
-      return launch_all<W_BF16>(gu, dn, tile_e, tile_m0, half_e, half_m0, counts, max_tiles, st);
-    case W_FP8:
-      return launch_all<W_FP8>(gu, dn, tile_e, tile_m0, half_e, half_m0, counts, max_tiles, st);
-    case W_FP4:
-      return launch_all<W_FP4>(gu, dn, tile_e, tile_m0, half_e, half_m0, counts, max_tiles, st);
-    default:
-      return hipErrorInvalidValue;
-  }
+  return launch_bf16_all(gu, dn, tile_e, tile_m0, half_e, half_m0, counts, max_tiles, st);
 }
 
 }  // namespace moe
