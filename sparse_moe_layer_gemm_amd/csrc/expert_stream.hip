@@ -101,44 +101,52 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[f][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 braw[8];
-    const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+    // Every load is unconditional, from an address clamped into the matrix
+    // (column 0 past N, row 0 past the expert's rows): an output element
+    // depends only on its own A row and B column, and those of clamped rows
+    // and columns are never stored. The A and B operands of a K step are
+    // loaded together, one step ahead, into one of two register sets, so the
+    // MFMAs of a step wait only for that step's loads (loads under divergent
+    // branches, or a copy from one set to the other, make the compiler wait
+    // for every load in flight, the next step's included).
+    struct Ops {
+      u32x4 a[2], b[8];
+    };
+    auto load = [&](int ks, Ops& o) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-      braw[r] = col_ok ? load_w(wb + (size_t)(8 * g + r) * N) : zero;
-
-    for (int ks = 0; ks < nk; ++ks) {
-      u32x4 af[2];
+      for (int f = 0; f < 2; ++f) o.a[f] = load_u32x4(ar.row[f] + ks * 32 + 8 * g);
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
-        af[f] = (f < nf && ar.valid[f]) ? load_u32x4(ar.row[f] + ks * 32 + 8 * g) : zero;
-      // next K step's weights, issued before this step's MFMAs
-      const int kn = (ks + 1 < nk) ? ks + 1 : ks;
-      u32x4 bnext[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        bnext[r] = col_ok ? load_w(wb + (size_t)(kn * 32 + 8 * g + r) * N) : zero;
-
+      for (int r = 0; r < 8; ++r) o.b[r] = load_w(wb + (size_t)(ks * 32 + 8 * g + r) * N);
+    };
+    auto step = [&](const Ops& o) {
       // 8x8 transpose: fragment for column 2q / 2q+1 from dword q of rows 2p, 2p+1
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         u32x4 lo, hi;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const uint32_t x0 = braw[2 * p][q], x1 = braw[2 * p + 1][q];
+          const uint32_t x0 = o.b[2 * p][q], x1 = o.b[2 * p + 1][q];
           lo[p] = (x0 & 0xFFFFu) | (x1 << 16);
           hi[p] = (x0 >> 16) | (x1 & 0xFFFF0000u);
         }
 #pragma unroll
         for (int f = 0; f < 2; ++f)
           if (f < nf) {
-            acc[f][2 * q] = mfma_bf16(af[f], lo, acc[f][2 * q]);
-            acc[f][2 * q + 1] = mfma_bf16(af[f], hi, acc[f][2 * q + 1]);
+            acc[f][2 * q] = mfma_bf16(o.a[f], lo, acc[f][2 * q]);
+            acc[f][2 * q + 1] = mfma_bf16(o.a[f], hi, acc[f][2 * q + 1]);
           }
       }
-#pragma unroll
-      for (int r = 0; r < 8; ++r) braw[r] = bnext[r];
+    };
+    Ops o0, o1;
+    load(0, o0);
+    int ks = 0;
+    for (; ks + 1 < nk; ks += 2) {
+      load(ks + 1, o1);
+      step(o0);
+      load(ks + 2 < nk ? ks + 2 : nk - 1, o0);  // the last pair reloads step nk - 1
+      step(o1);
     }
+    if (ks < nk) step(o0);  // odd nk: o0 holds step nk - 1
 
     // epilogue: lane (g, j) holds rows 16f + 4g + r of columns col + i (MFMA i)
 #pragma unroll
@@ -164,10 +172,8 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
           }
         } else if (m < cnt && col_ok) {
           float* o = a.y_out + (size_t)(r0 + m) * N + col;
-          *reinterpret_cast<float4*>(o) =
-              make_float4(acc[f][0][r], acc[f][1][r], acc[f][2][r], acc[f][3][r]);
-          *reinterpret_cast<float4*>(o + 4) =
-              make_float4(acc[f][4][r], acc[f][5][r], acc[f][6][r], acc[f][7][r]);
+          store_rows(o, f32x4{acc[f][0][r], acc[f][1][r], acc[f][2][r], acc[f][3][r]});
+          store_rows(o + 4, f32x4{acc[f][4][r], acc[f][5][r], acc[f][6][r], acc[f][7][r]});
         }
       }
     }
@@ -337,7 +343,7 @@ __global__ __launch_bounds__(256) void stream_kmajor_kernel(StreamGemmArgs a) {
           for (int cg = 0; cg < 8; ++cg)
             if (cok[cg]) {
               const float sc = (WF == W_FP8) ? chs[colv[cg]] : gsc;
-              a.y_out[(size_t)(r0 + m) * N + colv[cg]] = acc[f][cg][r] * sc;
+              store_rows(a.y_out + (size_t)(r0 + m) * N + colv[cg], acc[f][cg][r] * sc);
             }
         }
       }

@@ -379,7 +379,13 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
         const int m = m0 + 128 * wm + 32 * i + rr;
         const int col = nt * S::BN + 128 * wn + 4 * ch;
         const f32x4 v = *reinterpret_cast<const f32x4*>(strip + rr * 128 + 4 * ch);
-        if (m < cnt && col < N) *reinterpret_cast<f32x4*>(Yout + (size_t)(r0 + m) * N + col) = v;
+        if (m < cnt && col < N) {
+          // expert rows stream out; split-K partials of the router are read back at once
+          if (a.nsplit == 1)
+            store_rows(Yout + (size_t)(r0 + m) * N + col, v);
+          else
+            *reinterpret_cast<f32x4*>(Yout + (size_t)(r0 + m) * N + col) = v;
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -752,7 +758,7 @@ __global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
         const int m = m0 + 128 * wm + 32 * i + rr;
         const int col = nt * S::BN + 128 * wn + 4 * ch;
         const f32x4 v = *reinterpret_cast<const f32x4*>(strip + rr * 128 + 4 * ch);
-        if (m < cnt && col < N) *reinterpret_cast<f32x4*>(a.y_out + (size_t)(r0 + m) * N + col) = v;
+        if (m < cnt && col < N) store_rows(a.y_out + (size_t)(r0 + m) * N + col, v);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -1148,7 +1154,7 @@ __global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmAr
         const int m = m0 + 128 * wm + 32 * i + rr;
         const int col = nt * S::BN + 128 * wn + 4 * ch;
         const f32x4 v = *reinterpret_cast<const f32x4*>(strip + rr * 128 + 4 * ch);
-        if (m < cnt && col < N) *reinterpret_cast<f32x4*>(a.y_out + (size_t)(r0 + m) * N + col) = v;
+        if (m < cnt && col < N) store_rows(a.y_out + (size_t)(r0 + m) * N + col, v);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();

@@ -33,10 +33,10 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
       wt[j] = (j < k) ? w[t * k + j] : 0.f;
     }
     if (c >= H) continue;
-    float4 v[8];
+    f32x4 v[8];  // each expert row is read once: nontemporal
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      v[j] = *reinterpret_cast<const float4*>(y + (size_t)pos[j] * H + c);
+      v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + (size_t)pos[j] * H + c));
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
