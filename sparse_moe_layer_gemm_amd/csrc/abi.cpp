@@ -115,7 +115,8 @@ bool f8_mode(const moe_expert_weights* w) { return w->qmode == MOE_QMODE_F8; }
 int h_bstride(int32_t I) { return ((I + 127) / 128 + 3) / 4 * 4; }
 
 // h (bf16, or fp32 for the all-fp32 layer) + tile tables (+ fp8-MFMA mode:
-// E4M3 x, per-token scales, E4M3 h, block scales)
+// E4M3 x, per-token scales, E4M3 h, block scales; + bf16 weights: split-K
+// partial sums of the streaming kernels)
 size_t experts_ws_bytes(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                         const moe_expert_weights* w) {
   const size_t P = (size_t)T * k;
@@ -124,6 +125,8 @@ size_t experts_ws_bytes(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
   if (f8_mode(w))
     b += align_up((size_t)T * H) + align_up((size_t)T * sizeof(float)) + align_up(P * I) +
          align_up(P * (size_t)h_bstride(I));
+  else if (w->dtype == MOE_BF16)
+    b += align_up(moe::stream_ws_bytes((long long)P, E, H, I));  // split-K partial sums
   return b;
 }
 
@@ -224,6 +227,21 @@ moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H,
   }
   if (use_tile_kernel(w->dtype, P, E))
     return launch_status(moe::launch_expert_tile(wf, a, d, P, tile_ws, st));
+  if (wf == moe::W_BF16) {
+    // few touched experts: split K so that enough wavefronts stream weights
+    float* part = reinterpret_cast<float*>(static_cast<char*>(tile_ws) +
+                                           align_up(moe::expert_tile_ws_bytes(P, E)));
+    const moe::StreamSplit sg = moe::stream_split_plan(P, E, H, 2 * I, true);
+    const moe::StreamSplit sd = moe::stream_split_plan(P, E, I, H, false);
+    a.ksplit = sg.ksplit;
+    a.ksteps = sg.ksteps;
+    a.part = part;
+    a.part_stride = (long long)P * 2 * I;
+    d.ksplit = sd.ksplit;
+    d.ksteps = sd.ksteps;
+    d.part = part;
+    d.part_stride = (long long)P * H;
+  }
   hipError_t e = moe::launch_expert_stream(wf, true, a, st);
   if (e != hipSuccess) return MOE_ERR_LAUNCH;
   return launch_status(moe::launch_expert_stream(wf, false, d, st));

@@ -27,6 +27,8 @@
 // MFMA v_mfma_f32_16x16x32_bf16: lane l supplies A row l%16 / B column l%16,
 // K block l/16 (8 values); the result lane l holds rows 4*(l/16)+r of column
 // l%16.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -91,6 +93,11 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
   const bool col_ok = col < N;
   const uint16_t* wb = static_cast<const uint16_t*>(a.w) + (size_t)e * K * N + (col_ok ? col : 0);
   const int nk = K / 32;
+  // this wavefront's K steps (all of them unless K is split)
+  const int split = blockIdx.z;
+  const int ks0 = a.ksplit > 1 ? split * a.ksteps : 0;
+  const int ks1 = a.ksplit > 1 ? min(nk, ks0 + a.ksteps) : nk;
+  if (ks0 >= ks1) return;
 
   for (int mc = 0; mc < cnt; mc += MROWS) {
     const int nf = (cnt - mc) > 16 ? 2 : 1;
@@ -138,15 +145,36 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
       }
     };
     Ops o0, o1;
-    load(0, o0);
-    int ks = 0;
-    for (; ks + 1 < nk; ks += 2) {
+    load(ks0, o0);
+    int ks = ks0;
+    for (; ks + 1 < ks1; ks += 2) {
       load(ks + 1, o1);
       step(o0);
-      load(ks + 2 < nk ? ks + 2 : nk - 1, o0);  // the last pair reloads step nk - 1
+      load(ks + 2 < ks1 ? ks + 2 : ks1 - 1, o0);  // the last pair reloads step ks1 - 1
       step(o1);
     }
-    if (ks < nk) step(o0);  // odd nk: o0 holds step nk - 1
+    if (ks < ks1) step(o0);  // odd count: o0 holds step ks1 - 1
+
+    if (a.ksplit > 1) {
+      // fp32 partial sums of this split; lane (g, j) holds rows 16f + 4g + r
+      // of columns col .. col + 7
+      float* pbase = a.part + (size_t)split * a.part_stride;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        if (f >= nf) break;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = mc + 16 * f + 4 * g + r;
+          if (m < cnt && col_ok) {
+            float* o = pbase + (size_t)(r0 + m) * N + col;
+            *reinterpret_cast<f32x4*>(o) = f32x4{acc[f][0][r], acc[f][1][r], acc[f][2][r], acc[f][3][r]};
+            *reinterpret_cast<f32x4*>(o + 4) =
+                f32x4{acc[f][4][r], acc[f][5][r], acc[f][6][r], acc[f][7][r]};
+          }
+        }
+      }
+      continue;
+    }
 
     // epilogue: lane (g, j) holds rows 16f + 4g + r of columns col + i (MFMA i)
 #pragma unroll
@@ -177,6 +205,62 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
         }
       }
     }
+  }
+}
+
+// ------------------------------------------------------------------ split-K reductions
+// Sums the partial products of the splits in split order (deterministic).
+// gate/up: h = bf16(silu(gate) * up) from the partial sums of both halves.
+__global__ __launch_bounds__(256) void stream_reduce_gu_kernel(const float* __restrict__ part,
+                                                               int S, long long sstride, int P,
+                                                               int I, uint16_t* __restrict__ h) {
+  const int q = I / 4;
+  const long long n = (long long)P * q;
+  for (long long it = (long long)blockIdx.x * 256 + threadIdx.x; it < n;
+       it += (long long)gridDim.x * 256) {
+    const long long r = it / q;
+    const int c = (int)(it - r * q) * 4;
+    const float* pg = part + r * 2 * I + c;
+    f32x4 gv[kMaxStreamSplit], uv[kMaxStreamSplit];  // all loads in flight at once
+#pragma unroll
+    for (int sp = 0; sp < kMaxStreamSplit; ++sp)
+      if (sp < S) {
+        gv[sp] = *reinterpret_cast<const f32x4*>(pg + sp * sstride);
+        uv[sp] = *reinterpret_cast<const f32x4*>(pg + sp * sstride + I);
+      }
+    f32x4 gs = gv[0], us = uv[0];
+#pragma unroll
+    for (int sp = 1; sp < kMaxStreamSplit; ++sp)
+      if (sp < S) {
+        gs += gv[sp];
+        us += uv[sp];
+      }
+    uint2 pk;
+    pk.x = f32_to_bf16_bits(silu(gs[0]) * us[0]) | (f32_to_bf16_bits(silu(gs[1]) * us[1]) << 16);
+    pk.y = f32_to_bf16_bits(silu(gs[2]) * us[2]) | (f32_to_bf16_bits(silu(gs[3]) * us[3]) << 16);
+    *reinterpret_cast<uint2*>(h + r * I + c) = pk;
+  }
+}
+// down: y = sum of the partial rows.
+__global__ __launch_bounds__(256) void stream_reduce_dn_kernel(const float* __restrict__ part,
+                                                               int S, long long sstride, int P,
+                                                               int N, float* __restrict__ y) {
+  const int q = N / 4;
+  const long long n = (long long)P * q;
+  for (long long it = (long long)blockIdx.x * 256 + threadIdx.x; it < n;
+       it += (long long)gridDim.x * 256) {
+    const long long r = it / q;
+    const int c = (int)(it - r * q) * 4;
+    const float* pp = part + r * N + c;
+    f32x4 pv[kMaxStreamSplit];
+#pragma unroll
+    for (int sp = 0; sp < kMaxStreamSplit; ++sp)
+      if (sp < S) pv[sp] = *reinterpret_cast<const f32x4*>(pp + sp * sstride);
+    f32x4 v = pv[0];
+#pragma unroll
+    for (int sp = 1; sp < kMaxStreamSplit; ++sp)
+      if (sp < S) v += pv[sp];
+    store_rows(y + r * N + c, v);
   }
 }
 
@@ -355,6 +439,20 @@ template <bool GU>
 hipError_t launch_one(int wfmt, const StreamGemmArgs& a, hipStream_t st) {
   const int n_tiles = GU ? a.I / 64 : (a.N + 127) / 128;
   dim3 grid((n_tiles + 3) / 4, a.E);
+  if (wfmt == W_BF16 && a.ksplit > 1) {
+    grid.z = a.ksplit;
+    stream_bf16_kernel<GU><<<grid, 256, 0, st>>>(a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int P = (int)(a.part_stride / a.N);
+    const long long items = (long long)P * (GU ? a.I : a.N) / 4;
+    const unsigned blocks = (unsigned)std::min<long long>((items + 255) / 256, 4096);
+    if (GU)
+      stream_reduce_gu_kernel<<<blocks, 256, 0, st>>>(a.part, a.ksplit, a.part_stride, P, a.I, a.h_out);
+    else
+      stream_reduce_dn_kernel<<<blocks, 256, 0, st>>>(a.part, a.ksplit, a.part_stride, P, a.N, a.y_out);
+    return hipGetLastError();
+  }
   switch (wfmt) {
     case W_BF16: stream_bf16_kernel<GU><<<grid, 256, 0, st>>>(a); break;
     case W_FP8: stream_kmajor_kernel<W_FP8, GU><<<grid, 256, 0, st>>>(a); break;
@@ -365,6 +463,32 @@ hipError_t launch_one(int wfmt, const StreamGemmArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+// Wavefronts of one split: touched experts (at most min(E, P)) x column
+// slices. Splits are added until about 4096 wavefronts stream (two rounds at
+// two per SIMD; measured at T = 1 ... 8 this beats one exact round), keeping
+// at least 8 K steps (256 of K) per split.
+StreamSplit stream_split_plan(long long P, int E, int K, int N, bool gate_up) {
+  const long long touched = std::min<long long>(E, P);
+  const long long slices = gate_up ? N / 128 : (N + 127) / 128;
+  const int nk = K / 32;
+  const long long waves = std::max<long long>(1, touched * slices);
+  long long s = (4096 + waves - 1) / waves;
+  s = std::min<long long>(s, std::max(1, nk / 8));
+  s = std::min<long long>(s, kMaxStreamSplit);
+  if (s <= 1) return StreamSplit{1, nk};
+  const int ksteps = (int)((nk + s - 1) / s);
+  return StreamSplit{(nk + ksteps - 1) / ksteps, ksteps};
+}
+
+size_t stream_ws_bytes(long long P, int E, int H, int I) {
+  const StreamSplit gu = stream_split_plan(P, E, H, 2 * I, true);
+  const StreamSplit dn = stream_split_plan(P, E, I, H, false);
+  size_t b = 0;
+  if (gu.ksplit > 1) b = std::max(b, (size_t)gu.ksplit * (size_t)P * 2 * I * sizeof(float));
+  if (dn.ksplit > 1) b = std::max(b, (size_t)dn.ksplit * (size_t)P * H * sizeof(float));
+  return b;
+}
 
 hipError_t launch_expert_stream(int wfmt, bool gate_up, const StreamGemmArgs& a, hipStream_t st) {
   return gate_up ? launch_one<true>(wfmt, a, st) : launch_one<false>(wfmt, a, st);

@@ -73,6 +73,13 @@ struct StreamGemmArgs {
   int lda = 0;             // 0: lda = K
   int nsplit = 1, nk_split = 1;
   long long w_plane_stride = 0, y_split_stride = 0;
+  // Split-K of the streaming kernels (blockIdx.z): split s covers the K steps
+  // [s * ksteps, (s + 1) * ksteps) and writes fp32 partial sums of all N
+  // columns to part + s * part_stride ([P, N] row-major); a reduction kernel
+  // then forms h (SwiGLU) or y from them in split order.
+  int ksplit = 1, ksteps = 0;
+  float* part = nullptr;
+  long long part_stride = 0;
 };
 // fp8-MFMA mode operands: E4M3 codes of x (gate/up) with one fp32 scale per
 // token, or of h (down) with one E8M0 scale per row and 128-column block.
@@ -93,6 +100,16 @@ struct F8Buffers {         // device scratch of the fp8-MFMA mode
 // Grouped expert GEMM for small row counts per expert: each wavefront owns a
 // 128-column slice of one expert's matrix and streams it once per 32 rows.
 hipError_t launch_expert_stream(int wfmt, bool gate_up, const StreamGemmArgs& a, hipStream_t st);
+// Split-K of the streaming kernels for few touched experts: number of splits
+// of a K-deep product with N output columns over P rows (at most min(E, P)
+// touched experts), the K steps (of 32) per split, and the fp32 scratch the
+// partial sums need (the larger of the two products of an expert FFN).
+struct StreamSplit {
+  int ksplit, ksteps;
+};
+constexpr int kMaxStreamSplit = 16;
+StreamSplit stream_split_plan(long long P, int E, int K, int N, bool gate_up);
+size_t stream_ws_bytes(long long P, int E, int H, int I);
 
 // Grouped expert GEMMs for many rows per expert: 128 x 256 MFMA tiles through
 // double-buffered LDS (bf16 weights). Runs gate/up then down; ws holds the

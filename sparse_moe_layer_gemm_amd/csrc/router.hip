@@ -147,7 +147,7 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
 }
 
 // One workgroup per token; wavefront w owns experts 64w .. 64w+63, one per
-// lane, and adds that expert's split partials (all loads in flight at once),
+// lane, and adds that expert's split partials (loaded 32 at a time),
 // the bias, and rounds to the logits dtype. The selection key packs
 // (order-preserving logit, 0xFFFF - id), so a maximum picks the largest logit
 // and, on equal logits, the lowest id. Each wavefront finds its own 8 largest
@@ -165,16 +165,18 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   if (e < E) {
     const float* p = part + (size_t)t * ldp + e;
     const size_t sstride = (size_t)T * ldp;
+    // up to 32 partials are loaded in one batch (one memory latency), then
+    // added in split order
     float v = 0.f;
-    int sp = 0;
-    for (; sp + 8 <= n_split; sp += 8) {
-      float u[8];
+    for (int sp0 = 0; sp0 < n_split; sp0 += 32) {
+      float u[32];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) u[j] = p[(size_t)(sp + j) * sstride];
+      for (int j = 0; j < 32; ++j)
+        if (sp0 + j < n_split) u[j] = p[(size_t)(sp0 + j) * sstride];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v += u[j];
+      for (int j = 0; j < 32; ++j)
+        if (sp0 + j < n_split) v += u[j];
     }
-    for (; sp < n_split; ++sp) v += p[(size_t)sp * sstride];
     if (bias) v += bias[e];
     if (logits_f32) logits_f32[(size_t)t * E + e] = v;
     float sv = v;

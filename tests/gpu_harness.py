@@ -48,10 +48,35 @@ def host_experts(cfg: synth.MoEConfig) -> dict:
     return hostw, dw
 
 
+def touched_bf16_experts(cfg: synth.MoEConfig, touched) -> tuple:
+    """bf16 expert weights of which only the `touched` experts are generated.
+
+    Host: full [E, ...] arrays (untouched slices are never written, so they
+    stay unbacked zero pages); device: full [E, ...] tensors whose untouched
+    slices are left uninitialised. Only routed experts are ever read, by the
+    kernels and by the oracle, so this stands in for the whole layer at a
+    fraction of the generation cost.
+    """
+    assert cfg.w_dtype == "bf16"
+    touched = np.asarray(sorted(set(int(e) for e in touched)))
+    sub = synth.gen_experts(cfg, experts=touched)
+    E, H, I = cfg.E, cfg.H, cfg.I
+    hw = {"dtype": "bf16", "gate_up": np.empty((E, H, 2 * I), np.uint16),
+          "down": np.empty((E, I, H), np.uint16)}
+    hw["gate_up"][touched] = sub["gate_up"]
+    hw["down"][touched] = sub["down"]
+    gu = torch.empty((E, H, 2 * I), dtype=torch.bfloat16, device=DEV)
+    dn = torch.empty((E, I, H), dtype=torch.bfloat16, device=DEV)
+    idx = torch.from_numpy(touched).to(DEV)
+    gu[idx] = torch.from_numpy(sub["gate_up"].view(np.int16)).to(DEV).view(torch.bfloat16)
+    dn[idx] = torch.from_numpy(sub["down"].view(np.int16)).to(DEV).view(torch.bfloat16)
+    return hw, moe.ExpertWeights(moe.MOE_BF16, gu, dn)
+
+
 class Layer:
     """Seeded inputs of one configuration, on the host and on the device."""
 
-    def __init__(self, cfg: synth.MoEConfig, x: np.ndarray | None = None):
+    def __init__(self, cfg: synth.MoEConfig, x: np.ndarray | None = None, weights=None):
         self.cfg = cfg
         self.x = synth.gen_x(cfg) if x is None else x
         self.wr, self.bias = synth.gen_router(cfg)
@@ -61,7 +86,9 @@ class Layer:
             self.dx = moe.to_device_bf16(self.x, DEV)
         self.dwr = torch.from_numpy(self.wr).to(DEV)
         self.dbias = None if self.bias is None else torch.from_numpy(self.bias).to(DEV)
-        if not cfg.router_only:
+        if weights is not None:
+            self.hw, self.dw = weights
+        elif not cfg.router_only:
             self.hw, self.dw = host_experts(cfg)
 
     @property

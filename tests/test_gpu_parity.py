@@ -15,7 +15,7 @@ import torch
 import sparse_moe_layer_gemm_amd as moe
 import synth
 from tests.gpu_harness import (Layer, bits, check_experts, check_finalize, check_layer,
-                               check_permute, check_router, log)
+                               check_permute, check_router, log, touched_bf16_experts)
 
 pytestmark = pytest.mark.gpu
 
@@ -167,6 +167,45 @@ def test_decode_single_token(decode_layer):
     check_finalize(L, r)
     lay = check_layer(L, r, [0])
     log(f"  T=1 out {lay['out_rel_err']:.2e}")
+
+
+@pytest.mark.parametrize("T", [2, 8])
+def test_decode_small_batches(decode_layer, T):
+    """Few touched experts: the streaming kernels split K (several splits at
+    T = 2, two for gate/up at T = 8) and a reduction forms h and y."""
+    cfg = decode_layer.cfg.with_(name=f"decode_t{T}", T=T)
+    L = Layer(cfg, x=decode_layer.x[:T].copy())
+    r = L.stages()
+    check_router(L, r)
+    check_permute(L, r)
+    ey = check_experts(L, r, np.arange(T * cfg.k))
+    check_finalize(L, r)
+    lay = check_layer(L, r, np.arange(T))
+    f = L.forward()
+    assert _same_bits(f["out"], r["out"])
+    log(f"  T={T} y {ey:.2e} out {lay['out_rel_err']:.2e}")
+
+
+@pytest.mark.parametrize("T", [1, 4, 32])
+def test_decode_wide_experts(T):
+    """Expert width I = 2560 (the width the published checkpoint sizes imply),
+    at batch sizes that take the split-K path (T = 1, 4) and the plain one."""
+    cfg = MC(f"decode_i2560_t{T}", 130 + T, T=T, H=5120, E=256, k=8, I=2560, router_only=True)
+    R = Layer(cfg)
+    touched = np.unique(R.route()["ids"].cpu().numpy())
+    cfg = cfg.with_(router_only=False)
+    L = Layer(cfg, x=R.x, weights=touched_bf16_experts(cfg, touched))
+    r = L.stages()
+    check_router(L, r)
+    check_permute(L, r)
+    # every row at T <= 4; at T = 32 a seeded sample of rows and tokens
+    rng = np.random.default_rng(T)
+    rows = np.arange(T * cfg.k) if T <= 4 else np.sort(rng.choice(T * cfg.k, 48, replace=False))
+    tokens = np.arange(T) if T <= 4 else np.sort(rng.choice(T, 6, replace=False))
+    ey = check_experts(L, r, rows)
+    check_finalize(L, r)
+    lay = check_layer(L, r, tokens)
+    log(f"  I=2560 T={T} touched {touched.size}: y {ey:.2e} out {lay['out_rel_err']:.2e}")
 
 
 def test_decode_token_permutation(decode_layer):
