@@ -111,6 +111,9 @@ moe_status check_weights(const moe_expert_weights* w, int32_t x_dtype, int32_t H
 }
 
 bool f8_mode(const moe_expert_weights* w) { return w->qmode == MOE_QMODE_F8; }
+int wfmt_of(int32_t dtype) {
+  return dtype == MOE_BF16 ? moe::W_BF16 : dtype == MOE_FP8_E4M3 ? moe::W_FP8 : moe::W_FP4;
+}
 // E8M0 block scales per row of h: one per 128 columns, rows padded to 4 bytes
 int h_bstride(int32_t I) { return ((I + 127) / 128 + 3) / 4 * 4; }
 
@@ -125,8 +128,8 @@ size_t experts_ws_bytes(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
   if (f8_mode(w))
     b += align_up((size_t)T * H) + align_up((size_t)T * sizeof(float)) + align_up(P * I) +
          align_up(P * (size_t)h_bstride(I));
-  else if (w->dtype == MOE_BF16)
-    b += align_up(moe::stream_ws_bytes((long long)P, E, H, I));  // split-K partial sums
+  else if (w->dtype != MOE_F32)
+    b += align_up(moe::stream_ws_bytes((long long)P, E, H, I, wfmt_of(w->dtype)));  // split-K partials
   return b;
 }
 
@@ -183,7 +186,7 @@ moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H,
         static_cast<float*>(ws), y_sorted, st));
   }
   (void)x_dtype;
-  const int wf = w->dtype == MOE_BF16 ? moe::W_BF16 : w->dtype == MOE_FP8_E4M3 ? moe::W_FP8 : moe::W_FP4;
+  const int wf = wfmt_of(w->dtype);
   uint16_t* h = static_cast<uint16_t*>(ws);
   void* tile_ws = static_cast<char*>(ws) + align_up((size_t)P * I * sizeof(uint16_t));
   moe::StreamGemmArgs a{};
@@ -227,12 +230,13 @@ moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H,
   }
   if (use_tile_kernel(w->dtype, P, E))
     return launch_status(moe::launch_expert_tile(wf, a, d, P, tile_ws, st));
-  if (wf == moe::W_BF16) {
+  {
     // few touched experts: split K so that enough wavefronts stream weights
     float* part = reinterpret_cast<float*>(static_cast<char*>(tile_ws) +
                                            align_up(moe::expert_tile_ws_bytes(P, E)));
-    const moe::StreamSplit sg = moe::stream_split_plan(P, E, H, 2 * I, true);
-    const moe::StreamSplit sd = moe::stream_split_plan(P, E, I, H, false);
+    const int kstep = moe::stream_k_step(wf);
+    const moe::StreamSplit sg = moe::stream_split_plan(P, E, H, 2 * I, true, kstep);
+    const moe::StreamSplit sd = moe::stream_split_plan(P, E, I, H, false, kstep);
     a.ksplit = sg.ksplit;
     a.ksteps = sg.ksteps;
     a.part = part;

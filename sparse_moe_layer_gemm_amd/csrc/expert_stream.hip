@@ -265,64 +265,28 @@ __global__ __launch_bounds__(256) void stream_reduce_dn_kernel(const float* __re
 }
 
 // ------------------------------------------------------------------ FP8 / NVFP4 weights
-// E4M3 code -> bf16 bits (exact; the NaN code is never produced by an encoder).
-__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) {
-  const uint32_t mag = c & 0x7Fu;
-  uint32_t r;
-  if (mag >= 8u) {
-    r = (mag << 4) + (120u << 7);  // exponent bias 7 -> 127, 3 mantissa bits on top
-  } else {
-    // subnormal: m * 2^-9, normalised into bf16
-    r = mag == 0u ? 0u
-        : mag == 1u ? (118u << 7)
-        : mag <= 3u ? ((119u << 7) | ((mag & 1u) << 6))
-                    : ((120u << 7) | ((mag & 3u) << 5));
-  }
-  return r | ((c & 0x80u) << 8);
-}
-
-// E2M1 code (4 bits) -> bf16 bits.
-__device__ __forceinline__ uint32_t e2m1_to_bf16(uint32_t n) {
-  const uint32_t mag = n & 7u;
-  const uint32_t r = mag >= 2u ? ((((mag >> 1) + 126u) << 7) | ((mag & 1u) << 6))
-                               : (mag ? 0x3F00u : 0u);
-  return r | ((n & 8u) << 12);
-}
-
-// 8 consecutive E4M3 codes (two dwords) -> B fragment (4 dwords of bf16 pairs).
-__device__ __forceinline__ u32x4 fp8x8_to_frag(uint32_t d0, uint32_t d1) {
-  u32x4 f;
-  f[0] = e4m3_to_bf16(d0 & 0xFFu) | (e4m3_to_bf16((d0 >> 8) & 0xFFu) << 16);
-  f[1] = e4m3_to_bf16((d0 >> 16) & 0xFFu) | (e4m3_to_bf16(d0 >> 24) << 16);
-  f[2] = e4m3_to_bf16(d1 & 0xFFu) | (e4m3_to_bf16((d1 >> 8) & 0xFFu) << 16);
-  f[3] = e4m3_to_bf16((d1 >> 16) & 0xFFu) | (e4m3_to_bf16(d1 >> 24) << 16);
-  return f;
-}
-
-// 8 E2M1 codes (one dword, element 2i in the low nibble of byte i) scaled by an
-// E4M3 block scale -> B fragment. The product has at most 6 significant bits,
-// so it is exact in fp32 and its upper half is the exact bf16 value.
-__device__ __forceinline__ u32x4 fp4x8_to_frag(uint32_t d, float scale) {
-  u32x4 f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t byte = (d >> (8 * i)) & 0xFFu;
-    const float v0 = bf16_bits_to_f32(e2m1_to_bf16(byte & 0xFu)) * scale;
-    const float v1 = bf16_bits_to_f32(e2m1_to_bf16(byte >> 4)) * scale;
-    f[i] = (__float_as_uint(v0) >> 16) | (__float_as_uint(v1) & 0xFFFF0000u);
-  }
-  return f;
-}
-
-// K-contiguous quantised weights. Per "super step" a lane reads 16 B of each of
-// its 8 columns: FP8 -> 16 K values (2 MFMA K steps), FP4 -> 32 K values (4).
-// In MFMA s of a super step the lane's K block is kb + G*g + 8s (G = 16 or 32);
-// the A fragments use the same K assignment.
+// K-contiguous quantised weights ([E, N, K] E4M3 codes, or [E, N, K/2] E2M1
+// codes with one E4M3 scale per 16 K values). Per "super step" a lane reads
+// 16 B of each of its 8 columns (FP8: 16 K values, 2 MFMA K steps; FP4: 32 K
+// values, 4) with the matching A fragments; like the bf16 kernel, a super
+// step's loads are issued one step ahead into one of two register sets,
+// unconditionally from clamped addresses. A load instruction covers 64 B of
+// each of 16 weight rows, half a cache line: the next super step reads the
+// other half, so these loads keep cache retention (nontemporal loads measured
+// 25-30% slower here). Codes become bf16 with the hardware
+// converters (E4M3 exactly; E2M1 with the power of two of its block scale,
+// then an fp32 multiply by the scale's mantissa factor, exact as well).
+// Per-channel (E4M3) and per-expert (E2M1) fp32 scales multiply the
+// accumulators. In MFMA s of a super step lane group g covers K
+// ss*SPAN + G*g + 8s .. +8, for A and B alike.
 template <int WF, bool GATE_UP>
-__global__ __launch_bounds__(256) void stream_kmajor_kernel(StreamGemmArgs a) {
+__global__ __launch_bounds__(256, 2) void stream_kmajor_kernel(StreamGemmArgs a) {
   constexpr int G = (WF == W_FP8) ? 16 : 32;  // K values per lane per super step
   constexpr int NS = G / 8;                   // MFMA K steps per super step
   constexpr int SPAN = 4 * G;                 // K per super step
+  // row fragments per pass: one for E2M1 (its 4 A fragments per fragment row
+  // and super step would otherwise cost a wave per SIMD of occupancy)
+  constexpr int NF = (WF == W_FP4) ? 1 : 2;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, j = lane & 15;
   const int e = blockIdx.y;
@@ -333,9 +297,21 @@ __global__ __launch_bounds__(256) void stream_kmajor_kernel(StreamGemmArgs a) {
   const int cnt = a.offsets[e + 1] - r0;
   if (cnt <= 0) return;
   const int K = a.K, N = a.N;
+  const int nss = (K + SPAN - 1) / SPAN;
+  const int split = blockIdx.z;
+  const int ss0 = a.ksplit > 1 ? split * a.ksteps : 0;
+  const int ss1 = a.ksplit > 1 ? min(nss, ss0 + a.ksteps) : nss;
+  if (ss0 >= ss1) return;
 
+  // this lane's 8 columns (gate/up: 4 gate, then the 4 matching up columns);
+  // columns past N read column 0 and are never stored
+  const int row_bytes = (WF == W_FP8) ? K : K / 2;
+  const uint8_t* wexp = static_cast<const uint8_t*>(a.w) + (size_t)e * N * row_bytes;
+  const uint8_t* sexp =
+      (WF == W_FP4) ? static_cast<const uint8_t*>(a.w_scale) + (size_t)e * N * (K / 16) : nullptr;
   int colv[8];
   bool cok[8];
+  uint32_t coff[8];
 #pragma unroll
   for (int cg = 0; cg < 8; ++cg) {
     if (GATE_UP)
@@ -343,92 +319,102 @@ __global__ __launch_bounds__(256) void stream_kmajor_kernel(StreamGemmArgs a) {
     else
       colv[cg] = tile * 128 + 16 * cg + j;
     cok[cg] = colv[cg] < N;
+    coff[cg] = (uint32_t)(cok[cg] ? colv[cg] : 0);
   }
-  const uint8_t* wq = static_cast<const uint8_t*>(a.w);
-  const size_t row_bytes = (WF == W_FP8) ? (size_t)K : (size_t)K / 2;
   const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
-  const int nss = (K + SPAN - 1) / SPAN;
 
-  for (int mc = 0; mc < cnt; mc += MROWS) {
-    const int nf = (cnt - mc) > 16 ? 2 : 1;
+  for (int mc = 0; mc < cnt; mc += 16 * NF) {
+    const int nf = (NF == 2 && (cnt - mc) > 16) ? 2 : 1;
     const ARows ar = a_rows(a, GATE_UP, r0, cnt, mc, j);
-    f32x4 acc[2][8];
+    f32x4 acc[NF][8];
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < NF; ++f)
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[f][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int ss = 0; ss < nss; ++ss) {
-      const int kl = ss * SPAN + G * g;  // this lane's first K index
-      const bool k_ok = kl < K;
-      u32x4 braw[8];
-      uint32_t sraw[8];
+    struct Ops {
+      u32x4 a[NF][NS], b[8];
+      uint32_t sc[8];
+      bool kok;  // this lane's K range lies inside K (false only in a K tail)
+    };
+    auto load = [&](int ss, Ops& o) {
+      const int kl = ss * SPAN + G * g;
+      o.kok = kl < K;
+      const int kc = o.kok ? kl : 0;
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int q = 0; q < NS; ++q) o.a[f][q] = load_u32x4(ar.row[f] + kc + 8 * q);
+#pragma unroll
+      for (int cg = 0; cg < 8; ++cg)
+        o.b[cg] = load_u32x4(wexp + (size_t)coff[cg] * row_bytes + (WF == W_FP8 ? kc : kc / 2));
+      if constexpr (WF == W_FP4) {
+#pragma unroll
+        for (int cg = 0; cg < 8; ++cg)  // the two block scales of this lane's 32 K values
+          o.sc[cg] = *reinterpret_cast<const uint16_t*>(sexp + (size_t)coff[cg] * (K / 16) + kc / 16);
+      }
+    };
+    auto step = [&](const Ops& o) {
 #pragma unroll
       for (int cg = 0; cg < 8; ++cg) {
-        const bool ok = k_ok && cok[cg];
-        const size_t rowoff = ((size_t)e * N + (cok[cg] ? colv[cg] : 0)) * row_bytes;
-        braw[cg] = ok ? load_w(wq + rowoff + ((WF == W_FP8) ? kl : kl / 2)) : zero;
-        if (WF == W_FP4) {
-          const uint8_t* sp = static_cast<const uint8_t*>(a.w_scale) +
-                              ((size_t)e * N + (cok[cg] ? colv[cg] : 0)) * (K / 16) + kl / 16;
-          sraw[cg] = ok ? (uint32_t) * reinterpret_cast<const uint16_t*>(sp) : 0u;
+        float p2[2], fm[2];
+        if constexpr (WF == W_FP4) {
+          e4m3_split(o.sc[cg] & 0xFFu, p2[0], fm[0]);
+          e4m3_split((o.sc[cg] >> 8) & 0xFFu, p2[1], fm[1]);
+        }
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+          const u32x4 bf = (WF == W_FP8) ? fp8_frag(o.b[cg][2 * q], o.b[cg][2 * q + 1])
+                                         : fp4_frag(o.b[cg][q], p2[q >> 1], fm[q >> 1]);
+#pragma unroll
+          for (int f = 0; f < NF; ++f)
+            if (f < nf) acc[f][cg] = mfma_bf16(o.kok ? o.a[f][q] : zero, bf, acc[f][cg]);
         }
       }
-      u32x4 af[2][NS];
-#pragma unroll
-      for (int f = 0; f < 2; ++f)
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-          af[f][s] = (f < nf && ar.valid[f] && k_ok) ? load_u32x4(ar.row[f] + kl + 8 * s) : zero;
-
-#pragma unroll
-      for (int cg = 0; cg < 8; ++cg) {
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          u32x4 bf;
-          if (WF == W_FP8) {
-            bf = fp8x8_to_frag(braw[cg][2 * (s & 1)], braw[cg][2 * (s & 1) + 1]);
-          } else {
-            const uint32_t sc = (s < 2) ? (sraw[cg] & 0xFFu) : (sraw[cg] >> 8);
-            bf = fp4x8_to_frag(braw[cg][s], bf16_bits_to_f32(e4m3_to_bf16(sc)));
-          }
-#pragma unroll
-          for (int f = 0; f < 2; ++f)
-            if (f < nf) acc[f][cg] = mfma_bf16(af[f][s], bf, acc[f][cg]);
-        }
-      }
+    };
+    // (the scheduling barriers keep each step's loads ahead of the previous
+    // step's conversions, which register pressure would otherwise sink them past)
+    Ops o0, o1;
+    load(ss0, o0);
+    int ss = ss0;
+    for (; ss + 1 < ss1; ss += 2) {
+      load(ss + 1, o1);
+      __builtin_amdgcn_sched_barrier(0);
+      step(o0);
+      load(ss + 2 < ss1 ? ss + 2 : ss1 - 1, o0);  // the last pair reloads step ss1 - 1
+      __builtin_amdgcn_sched_barrier(0);
+      step(o1);
     }
+    if (ss < ss1) step(o0);
 
     // epilogue: lane (g, j) holds rows 16f + 4g + r of column colv[cg]
     const float gsc = (WF == W_FP4) ? a.w_gscale[e] : 1.f;
     const float* chs = (WF == W_FP8) ? static_cast<const float*>(a.w_scale) + (size_t)e * N : nullptr;
+    float csc[8];
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
+    for (int cg = 0; cg < 8; ++cg) csc[cg] = (WF == W_FP8) ? chs[coff[cg]] : gsc;
+    float* pbase = a.ksplit > 1 ? a.part + (size_t)split * a.part_stride : nullptr;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
       if (f >= nf) break;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = mc + 16 * f + 4 * g + r;
         if (m >= cnt) continue;
-        if (GATE_UP) {
+        if (pbase) {  // split K: scaled fp32 partial sums
+#pragma unroll
+          for (int cg = 0; cg < 8; ++cg)
+            if (cok[cg]) pbase[(size_t)(r0 + m) * N + colv[cg]] = acc[f][cg][r] * csc[cg];
+        } else if (GATE_UP) {
 #pragma unroll
           for (int cg = 0; cg < 4; ++cg) {
-            float gv = acc[f][cg][r], uv = acc[f][cg + 4][r];
-            if (WF == W_FP8) {
-              gv *= chs[colv[cg]];
-              uv *= chs[colv[cg + 4]];
-            } else {
-              gv *= gsc;
-              uv *= gsc;
-            }
+            const float gv = acc[f][cg][r] * csc[cg], uv = acc[f][cg + 4][r] * csc[cg + 4];
             a.h_out[(size_t)(r0 + m) * a.I + colv[cg]] = (uint16_t)f32_to_bf16_bits(silu(gv) * uv);
           }
         } else {
 #pragma unroll
           for (int cg = 0; cg < 8; ++cg)
-            if (cok[cg]) {
-              const float sc = (WF == W_FP8) ? chs[colv[cg]] : gsc;
-              store_rows(a.y_out + (size_t)(r0 + m) * N + colv[cg], acc[f][cg][r] * sc);
-            }
+            if (cok[cg]) store_rows(a.y_out + (size_t)(r0 + m) * N + colv[cg], acc[f][cg][r] * csc[cg]);
         }
       }
     }
@@ -439,9 +425,14 @@ template <bool GU>
 hipError_t launch_one(int wfmt, const StreamGemmArgs& a, hipStream_t st) {
   const int n_tiles = GU ? a.I / 64 : (a.N + 127) / 128;
   dim3 grid((n_tiles + 3) / 4, a.E);
-  if (wfmt == W_BF16 && a.ksplit > 1) {
+  if (a.ksplit > 1) {
     grid.z = a.ksplit;
-    stream_bf16_kernel<GU><<<grid, 256, 0, st>>>(a);
+    switch (wfmt) {
+      case W_BF16: stream_bf16_kernel<GU><<<grid, 256, 0, st>>>(a); break;
+      case W_FP8: stream_kmajor_kernel<W_FP8, GU><<<grid, 256, 0, st>>>(a); break;
+      case W_FP4: stream_kmajor_kernel<W_FP4, GU><<<grid, 256, 0, st>>>(a); break;
+      default: return hipErrorInvalidValue;
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int P = (int)(a.part_stride / a.N);
@@ -467,11 +458,12 @@ hipError_t launch_one(int wfmt, const StreamGemmArgs& a, hipStream_t st) {
 // Wavefronts of one split: touched experts (at most min(E, P)) x column
 // slices. Splits are added until about 4096 wavefronts stream (two rounds at
 // two per SIMD; measured at T = 1 ... 8 this beats one exact round), keeping
-// at least 8 K steps (256 of K) per split.
-StreamSplit stream_split_plan(long long P, int E, int K, int N, bool gate_up) {
+// at least 8 K steps per split. A K step is 32 K values for bf16 weights and
+// one super step (64 or 128 K values) for FP8 / NVFP4 weights.
+StreamSplit stream_split_plan(long long P, int E, int K, int N, bool gate_up, int step) {
   const long long touched = std::min<long long>(E, P);
   const long long slices = gate_up ? N / 128 : (N + 127) / 128;
-  const int nk = K / 32;
+  const int nk = (K + step - 1) / step;
   const long long waves = std::max<long long>(1, touched * slices);
   long long s = (4096 + waves - 1) / waves;
   s = std::min<long long>(s, std::max(1, nk / 8));
@@ -481,9 +473,12 @@ StreamSplit stream_split_plan(long long P, int E, int K, int N, bool gate_up) {
   return StreamSplit{(nk + ksteps - 1) / ksteps, ksteps};
 }
 
-size_t stream_ws_bytes(long long P, int E, int H, int I) {
-  const StreamSplit gu = stream_split_plan(P, E, H, 2 * I, true);
-  const StreamSplit dn = stream_split_plan(P, E, I, H, false);
+int stream_k_step(int wfmt) { return wfmt == W_FP4 ? 128 : wfmt == W_FP8 ? 64 : 32; }
+
+size_t stream_ws_bytes(long long P, int E, int H, int I, int wfmt) {
+  const int step = stream_k_step(wfmt);
+  const StreamSplit gu = stream_split_plan(P, E, H, 2 * I, true, step);
+  const StreamSplit dn = stream_split_plan(P, E, I, H, false, step);
   size_t b = 0;
   if (gu.ksplit > 1) b = std::max(b, (size_t)gu.ksplit * (size_t)P * 2 * I * sizeof(float));
   if (dn.ksplit > 1) b = std::max(b, (size_t)dn.ksplit * (size_t)P * H * sizeof(float));

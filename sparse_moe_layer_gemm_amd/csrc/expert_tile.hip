@@ -452,40 +452,6 @@ __device__ __forceinline__ void dma4(const void* g, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
 }
 
-// E4M3 block scale -> (power of two, mantissa factor) as fp32; subnormal
-// scales m * 2^-9 become (2^-9, m), zero becomes a zero factor.
-__device__ __forceinline__ void e4m3_split(uint32_t c, float& p2, float& fm) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const bool normal = e != 0u;
-  p2 = __uint_as_float(normal ? (e + 120u) << 23 : 118u << 23);
-  const float f = normal ? __uint_as_float(0x3F800000u | (m << 20)) : (float)m;
-  fm = (c & 0x80u) ? -f : f;
-}
-
-// 8 E2M1 codes (one dword, even K in the low nibble) x block scale -> bf16 fragment
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-// two scaled codes -> packed bf16 (upper halves of the exact fp32 products)
-__device__ __forceinline__ uint32_t fp4_pair(f32x2 v, float fm) {
-  return __builtin_amdgcn_perm(__float_as_uint(v.y * fm), __float_as_uint(v.x * fm), 0x07060302u);
-}
-__device__ __forceinline__ u32x4 fp4_frag(uint32_t d, float p2, float fm) {
-  u32x4 r;
-  r[0] = fp4_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 0), fm);
-  r[1] = fp4_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 1), fm);
-  r[2] = fp4_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 2), fm);
-  r[3] = fp4_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 3), fm);
-  return r;
-}
-// 8 E4M3 codes (two dwords) -> bf16 fragment (exact)
-__device__ __forceinline__ u32x4 fp8_frag(uint32_t d0, uint32_t d1) {
-  u32x4 r;
-  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false));
-  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true));
-  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false));
-  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true));
-  return r;
-}
-
 template <int WF, bool GATE_UP, int WM>
 __global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
                                                         const int32_t* __restrict__ tile_e,

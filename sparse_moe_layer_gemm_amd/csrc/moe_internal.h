@@ -39,6 +39,44 @@ __device__ __forceinline__ void store_rows(float* p, f32x4 v) {
 }
 __device__ __forceinline__ void store_rows(float* p, float v) { __builtin_nontemporal_store(v, p); }
 
+// ---- weight-code converters (gfx950 hardware conversions)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// E4M3 block scale -> (power of two, mantissa factor) as fp32, branch-free:
+// normal codes give (2^(e-7), 1 + m/8), subnormal ones m * 2^-9 give
+// (2^-6, m/8), zero gives a zero factor; the sign goes on the factor.
+__device__ __forceinline__ void e4m3_split(uint32_t c, float& p2, float& fm) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const uint32_t normal = e != 0u ? 1u : 0u;
+  p2 = __uint_as_float(((normal ? e : 1u) + 120u) << 23);
+  const float f = (float)((normal << 3) | m) * 0.125f;  // exact
+  fm = __uint_as_float(__float_as_uint(f) | ((c & 0x80u) << 24));
+}
+// Two E2M1 codes scaled by 2^e (converter) and the mantissa factor (fp32
+// multiply) -> packed bf16: the products have at most 6 significant bits, so
+// they and their bf16 upper halves are exact.
+__device__ __forceinline__ uint32_t fp4_pair(f32x2 v, float fm) {
+  return __builtin_amdgcn_perm(__float_as_uint(v.y * fm), __float_as_uint(v.x * fm), 0x07060302u);
+}
+// 8 E2M1 codes (one dword, even K in the low nibble) x block scale -> 8 bf16
+__device__ __forceinline__ u32x4 fp4_frag(uint32_t d, float p2, float fm) {
+  u32x4 r;
+  r[0] = fp4_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 0), fm);
+  r[1] = fp4_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 1), fm);
+  r[2] = fp4_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 2), fm);
+  r[3] = fp4_pair(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 3), fm);
+  return r;
+}
+// 8 E4M3 codes (two dwords) -> 8 bf16 (exact)
+__device__ __forceinline__ u32x4 fp8_frag(uint32_t d0, uint32_t d1) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true));
+  return r;
+}
+
+
 // ---------------------------------------------------------------- launchers
 // Router GEMM partial sums: part[s][t][e] = sum over K-slice s of x[t,h] w[h,e].
 hipError_t launch_router_gemm(const void* x, bool x_bf16, int T, int H, const float* w_router,
@@ -102,14 +140,16 @@ struct F8Buffers {         // device scratch of the fp8-MFMA mode
 hipError_t launch_expert_stream(int wfmt, bool gate_up, const StreamGemmArgs& a, hipStream_t st);
 // Split-K of the streaming kernels for few touched experts: number of splits
 // of a K-deep product with N output columns over P rows (at most min(E, P)
-// touched experts), the K steps (of 32) per split, and the fp32 scratch the
-// partial sums need (the larger of the two products of an expert FFN).
+// touched experts), the K steps (of `step` K values) per split, and the fp32
+// scratch the partial sums need (the larger of the two products of an expert
+// FFN).
 struct StreamSplit {
   int ksplit, ksteps;
 };
 constexpr int kMaxStreamSplit = 16;
-StreamSplit stream_split_plan(long long P, int E, int K, int N, bool gate_up);
-size_t stream_ws_bytes(long long P, int E, int H, int I);
+StreamSplit stream_split_plan(long long P, int E, int K, int N, bool gate_up, int step);
+int stream_k_step(int wfmt);  // K values per split unit of the streaming kernels
+size_t stream_ws_bytes(long long P, int E, int H, int I, int wfmt);
 
 // Grouped expert GEMMs for many rows per expert: 128 x 256 MFMA tiles through
 // double-buffered LDS (bf16 weights). Runs gate/up then down; ws holds the
