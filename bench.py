@@ -326,7 +326,22 @@ def main():
                          "unit": "GB/s" if h8 >= m8 else "TFLOP/s",
                          "frac": max(h8, m8), "traffic": None,
                          "weight_GBps": round(tb8, 1), "TFLOPs": round(tf8, 1)}}
-        del qw
+        # NVFP4 decode (T=128, exact dequantisation): the streaming kernels on the same weights
+        progress("timing NVFP4 decode (T=128)")
+        qd_cfg = q_cfg.with_(name="nvfp4_t128", T=128)
+        qd = Workload(qd_cfg, moe, torch, dev_weights=dataclasses.replace(qw.w, qmode=moe.MOE_QMODE_W))
+        d_ms = qd.time_forward(a.steps, a.warmup)
+        d_stage = qd.time_stages(a.steps)
+        d_bytes = int((qd.touched() > 0).sum()) * expert_bytes(qd_cfg)
+        d_gbs = d_bytes / (d_stage["experts"] / 1e3) / 1e9
+        q_line["decode_t128"] = {
+            "value": round(qd_cfg.T / (d_ms / 1e3), 1), "unit": "tokens/s",
+            "ms_per_step": round(d_ms, 4),
+            "stages_ms": {k: round(v, 4) for k, v in d_stage.items()},
+            "roofline": {"bound": "hbm", "kernel": "moe_experts (NVFP4 weights, stream, bf16 MFMA)",
+                         "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": d_gbs / HBM_PEAK_GBS, "traffic": None}}
+        del qw, qd
 
     head, head_cfg = (dec_line, dec_cfg) if a.workload == "decode" else (pre_line, pre_cfg)
     cpu = None
