@@ -112,6 +112,21 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
   }
 }
 
+// Ids of kChunkBatch consecutive 64-pair chunks from c0 on, loaded together
+// (one memory latency per batch); pairs at or past s1 read as -1 (invalid).
+constexpr int kChunkBatch = 8;
+__device__ __forceinline__ void load_ids(const int32_t* __restrict__ ids, int c0, int s1, int lane,
+                                         int (&idb)[kChunkBatch]) {
+  int raw[kChunkBatch];
+#pragma unroll
+  for (int b = 0; b < kChunkBatch; ++b) {
+    const int p = c0 + 64 * b + lane;
+    raw[b] = ids[p < s1 ? p : s1 - 1];  // clamped: every load is in bounds
+  }
+#pragma unroll
+  for (int b = 0; b < kChunkBatch; ++b) idb[b] = (c0 + 64 * b + lane < s1) ? raw[b] : -1;
+}
+
 // ---- many pairs: the same per-wavefront algorithm over NV segments spread
 // across workgroups. Segment v (wavefront v % 16 of workgroup v / 16) holds
 // pairs [v * seg, (v + 1) * seg); its histogram goes to hist_g[e * NV + v]
@@ -127,13 +142,17 @@ __global__ __launch_bounds__(1024) void permute_hist_kernel(const int32_t* __res
   const int v = blockIdx.x * PW + wave;
   const long long s0l = (long long)v * seg;
   const int s0 = (int)(s0l < P ? s0l : P), s1 = (int)(s0l + seg < P ? s0l + seg : P);
-  for (int c = s0; c < s1; c += 64) {
-    const int p = c + lane;
-    int id = (p < s1) ? ids[p] : -1;
-    const bool valid = id >= 0 && id < E;
-    if (!valid) id = 0;
-    const uint64_t peers = match_peers(id, valid);
-    if (valid && lane == 63 - __builtin_clzll(peers)) hist[wave][id] += __popcll(peers);
+  for (int c0 = s0; c0 < s1; c0 += 64 * kChunkBatch) {
+    int idb[kChunkBatch];
+    load_ids(ids, c0, s1, lane, idb);
+#pragma unroll
+    for (int b = 0; b < kChunkBatch; ++b) {
+      int id = idb[b];
+      const bool valid = id >= 0 && id < E;
+      if (!valid) id = 0;
+      const uint64_t peers = match_peers(id, valid);
+      if (valid && lane == 63 - __builtin_clzll(peers)) hist[wave][id] += __popcll(peers);
+    }
   }
   __syncthreads();
   if (v < NV)
@@ -152,9 +171,18 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int E, int NV, int32
   const int tid = threadIdx.x, e = tid >> 2, q = tid & 3;
   const int per = (NV + 3) / 4;
   const int v0 = min(NV, q * per), v1 = min(NV, v0 + per);
+  // segment counts are read 32 at a time (one memory latency per batch)
+  const int32_t* row = hist_g + (size_t)(e < E ? e : 0) * NV;
   int sum = 0;
   if (e < E)
-    for (int v = v0; v < v1; ++v) sum += hist_g[(size_t)e * NV + v];
+    for (int vb = v0; vb < v1; vb += 32) {
+      int c[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) c[i] = row[vb + i < v1 ? vb + i : v1 - 1];
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if (vb + i < v1) sum += c[i];
+    }
   part[e][q] = sum;
   __syncthreads();
   if (tid < 256) {
@@ -185,10 +213,17 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int E, int NV, int32
   if (e < E) {
     int run = base[e];
     for (int qq = 0; qq < q; ++qq) run += part[e][qq];
-    for (int v = v0; v < v1; ++v) {
-      const int c = hist_g[(size_t)e * NV + v];
-      hist_g[(size_t)e * NV + v] = run;
-      run += c;
+    int32_t* wrow = hist_g + (size_t)e * NV;
+    for (int vb = v0; vb < v1; vb += 32) {
+      int c[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) c[i] = wrow[vb + i < v1 ? vb + i : v1 - 1];
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if (vb + i < v1) {
+          wrow[vb + i] = run;
+          run += c[i];
+        }
     }
   }
   if (tid < E) offsets[tid] = base[tid];
@@ -209,18 +244,23 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(const int32_t* __
   const long long s0l = (long long)v * seg;
   const int s0 = (int)(s0l < P ? s0l : P), s1 = (int)(s0l + seg < P ? s0l + seg : P);
   const uint64_t below = (1ull << lane) - 1ull;
-  for (int c = s0; c < s1; c += 64) {
-    const int p = c + lane;
-    int id = (p < s1) ? ids[p] : -1;
-    const bool valid = id >= 0 && id < E;
-    if (!valid) id = 0;
-    const uint64_t peers = match_peers(id, valid);
-    if (valid) {
-      const int pos = hist[wave][id] + __popcll(peers & below);
-      sorted_pair[pos] = p;
-      pair_pos[p] = pos;
+  for (int c0 = s0; c0 < s1; c0 += 64 * kChunkBatch) {
+    int idb[kChunkBatch];
+    load_ids(ids, c0, s1, lane, idb);
+#pragma unroll
+    for (int b = 0; b < kChunkBatch; ++b) {
+      const int p = c0 + 64 * b + lane;
+      int id = idb[b];
+      const bool valid = id >= 0 && id < E;
+      if (!valid) id = 0;
+      const uint64_t peers = match_peers(id, valid);
+      if (valid) {
+        const int pos = hist[wave][id] + __popcll(peers & below);
+        sorted_pair[pos] = p;
+        pair_pos[p] = pos;
+      }
+      if (valid && lane == 63 - __builtin_clzll(peers)) hist[wave][id] += __popcll(peers);
     }
-    if (valid && lane == 63 - __builtin_clzll(peers)) hist[wave][id] += __popcll(peers);
   }
 }
 
