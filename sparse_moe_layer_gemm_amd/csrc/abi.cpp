@@ -195,6 +195,7 @@ moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H,
   a.k = k;
   a.E = E;
   a.I = I;
+  a.rows = P;
   // gate/up: [T, H] x [H, 2I] -> h [P, I]
   a.a = static_cast<const uint16_t*>(x);
   a.K = H;

@@ -71,15 +71,47 @@ __device__ __forceinline__ ARows a_rows(const StreamGemmArgs& a, bool gate_up, i
   return ar;
 }
 
+// The expert of grid row `slot`. With one row per expert (gridDim.y == E) it
+// is the row itself; with fewer rows (min(E, P) < E: few pairs, so most
+// experts are empty) it is the slot-th expert that has rows, found from the
+// offsets by ballots (every lane of the wavefront gets the same answer), or
+// -1 when fewer experts have rows.
+__device__ __forceinline__ int slot_expert(const int32_t* __restrict__ offsets, int E, int slot,
+                                           int lane) {
+  if ((int)gridDim.y == E) return slot;
+  int o0[4], o1[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {  // E <= 256: lane l looks at experts l, l+64, l+128, l+192
+    const int e = 64 * c + lane;
+    o0[c] = offsets[e < E ? e : 0];
+    o1[c] = offsets[e < E ? e + 1 : 0];
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+  int base = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const bool nz = 64 * c + lane < E && o1[c] > o0[c];
+    const uint64_t m = __ballot(nz);
+    const int want = slot - base;
+    if (want < __popcll(m)) {
+      const uint64_t hit = __ballot(nz && __popcll(m & below) == want);
+      return 64 * c + __builtin_ctzll(hit);
+    }
+    base += __popcll(m);
+  }
+  return -1;
+}
+
 // ------------------------------------------------------------------ bf16 weights
 template <bool GATE_UP>
 __global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, j = lane & 15;
-  const int e = blockIdx.y;
   const int tile = blockIdx.x * 4 + wave;
   const int n_tiles = GATE_UP ? a.I / 64 : (a.N + 127) / 128;
   if (tile >= n_tiles) return;
+  const int e = slot_expert(a.offsets, a.E, blockIdx.y, lane);
+  if (e < 0) return;
   const int r0 = a.offsets[e];
   const int cnt = a.offsets[e + 1] - r0;
   if (cnt <= 0) return;
@@ -289,10 +321,11 @@ __global__ __launch_bounds__(256, 2) void stream_kmajor_kernel(StreamGemmArgs a)
   constexpr int NF = (WF == W_FP4) ? 1 : 2;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, j = lane & 15;
-  const int e = blockIdx.y;
   const int tile = blockIdx.x * 4 + wave;
   const int n_tiles = GATE_UP ? a.I / 64 : (a.N + 127) / 128;
   if (tile >= n_tiles) return;
+  const int e = slot_expert(a.offsets, a.E, blockIdx.y, lane);
+  if (e < 0) return;
   const int r0 = a.offsets[e];
   const int cnt = a.offsets[e + 1] - r0;
   if (cnt <= 0) return;
@@ -424,7 +457,8 @@ __global__ __launch_bounds__(256, 2) void stream_kmajor_kernel(StreamGemmArgs a)
 template <bool GU>
 hipError_t launch_one(int wfmt, const StreamGemmArgs& a, hipStream_t st) {
   const int n_tiles = GU ? a.I / 64 : (a.N + 127) / 128;
-  dim3 grid((n_tiles + 3) / 4, a.E);
+  // one grid row per expert that can have rows: at most min(E, P) do
+  dim3 grid((n_tiles + 3) / 4, a.rows > 0 ? std::min(a.E, a.rows) : a.E);
   if (a.ksplit > 1) {
     grid.z = a.ksplit;
     switch (wfmt) {
@@ -435,7 +469,7 @@ hipError_t launch_one(int wfmt, const StreamGemmArgs& a, hipStream_t st) {
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int P = (int)(a.part_stride / a.N);
+    const int P = a.rows;
     const long long items = (long long)P * (GU ? a.I : a.N) / 4;
     const unsigned blocks = (unsigned)std::min<long long>((items + 255) / 256, 4096);
     if (GU)

@@ -100,6 +100,7 @@ struct StreamGemmArgs {
   const int32_t* sorted_pair;
   int k;                   // experts per token (gather divisor)
   int E, K, N, I;          // N = output columns of the matrix (2I or H)
+  int rows = 0;            // P = T*k pairs (rows of h and y); 0: unknown
   const void* w;           // expert weights of this matrix
   const void* w_scale;     // FP8: f32 [E, N]; FP4: e4m3 [E, N, K/16]
   const float* w_gscale;   // FP4: f32 [E]
