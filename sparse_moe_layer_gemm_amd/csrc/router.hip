@@ -140,10 +140,19 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const void* __restrict
   }
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
-  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
-  return ((uint64_t)hi << 32) | lo;
+}  // namespace
+}  // namespace moe
+
+// Wavefront-wide maximum of a 64-bit key (ROCm device library, DPP row
+// operations; the result is the same in every lane).
+extern "C" __device__ __attribute__((const)) unsigned long long __ockl_wfred_max_u64(
+    unsigned long long);
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  return (uint64_t)__ockl_wfred_max_u64((unsigned long long)v);
 }
 
 // One workgroup per token; wavefront w owns experts 64w .. 64w+63, one per
@@ -151,7 +160,8 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
 // the bias, and rounds to the logits dtype. The selection key packs
 // (order-preserving logit, 0xFFFF - id), so a maximum picks the largest logit
 // and, on equal logits, the lowest id. Each wavefront finds its own 8 largest
-// keys; wavefront 0 merges the 32 candidates into the token's top k.
+// keys (eight wavefront-wide maxima); wavefront 0 merges the 32 candidates
+// into the token's top k.
 template <bool BF16_LOGITS>
 __global__ __launch_bounds__(256) void router_select_kernel(
     const float* __restrict__ part, int n_split, int ldp, int T, int E, int k,
@@ -192,12 +202,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   // this wavefront's 8 largest keys, in decreasing order (0 where it has fewer)
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    uint64_t best = key;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const uint64_t o = shfl_xor_u64(best, m);
-      best = o > best ? o : best;
-    }
+    const uint64_t best = wave_max_u64(key);
     if (key == best) key = 0;
     if (lane == 0) cand[wave][j] = best;
   }
@@ -208,12 +213,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   int topi[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    uint64_t best = c;
-#pragma unroll
-    for (int m = 16; m >= 1; m >>= 1) {
-      const uint64_t o = shfl_xor_u64(best, m);
-      best = o > best ? o : best;
-    }
+    const uint64_t best = wave_max_u64(c);
     if (c == best) c = 0;
     topi[j] = 0xFFFF - (int)(best & 0xFFFFu);
     topv[j] = float_from_order_key((uint32_t)(best >> 32));
