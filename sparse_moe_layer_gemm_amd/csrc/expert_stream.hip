@@ -23,7 +23,12 @@
 //  - FP8 and NVFP4 weights are stored [N, K] (K contiguous): a lane loads 16 B
 //    of one column and dequantises it exactly to bf16 in registers (E4M3 and
 //    E2M1 x E4M3 products fit in bf16); per-channel and per-expert fp32
-//    scales are applied to the fp32 accumulators in the epilogue.
+//    scales are applied to the fp32 accumulators in the epilogue;
+//  - with few touched experts (small batches) there are too few slices to
+//    keep HBM busy, so K is split over the grid's z dimension: the splits
+//    write fp32 partial sums and a reduction kernel forms h or y, adding them
+//    in split order; and the grid has one row per expert that can have rows,
+//    each row finding its expert among the non-empty ones.
 // MFMA v_mfma_f32_16x16x32_bf16: lane l supplies A row l%16 / B column l%16,
 // K block l/16 (8 values); the result lane l holds rows 4*(l/16)+r of column
 // l%16.

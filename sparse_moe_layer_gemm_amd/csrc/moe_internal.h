@@ -137,7 +137,10 @@ struct F8Buffers {         // device scratch of the fp8-MFMA mode
 };
 
 // Grouped expert GEMM for small row counts per expert: each wavefront owns a
-// 128-column slice of one expert's matrix and streams it once per 32 rows.
+// 128-column slice of one expert's matrix and streams it once per 32 rows (16
+// for NVFP4); with few touched experts K is split (StreamGemmArgs::ksplit) and
+// a reduction kernel follows. The grid has one row per expert that can have
+// rows (min(E, rows)).
 hipError_t launch_expert_stream(int wfmt, bool gate_up, const StreamGemmArgs& a, hipStream_t st);
 // Split-K of the streaming kernels for few touched experts: number of splits
 // of a K-deep product with N output columns over P rows (at most min(E, P)
@@ -152,9 +155,10 @@ StreamSplit stream_split_plan(long long P, int E, int K, int N, bool gate_up, in
 int stream_k_step(int wfmt);  // K values per split unit of the streaming kernels
 size_t stream_ws_bytes(long long P, int E, int H, int I, int wfmt);
 
-// Grouped expert GEMMs for many rows per expert: 128 x 256 MFMA tiles through
-// double-buffered LDS (bf16 weights). Runs gate/up then down; ws holds the
-// M-tile table (expert_tile_ws_bytes).
+// Grouped expert GEMMs for many rows per expert: bf16 weights on 256 x 256
+// tiles (plus 128 x 512 tiles for each expert's last <= 128 rows), quantised
+// weights on 128 x 512 tiles, MFMAs fed through a four-stage LDS pipeline.
+// Runs gate/up then down; ws holds the M-tile tables (expert_tile_ws_bytes).
 size_t expert_tile_ws_bytes(int P, int E);
 // fp8-MFMA mode of the quantised experts (x and h quantised in-kernel; the
 // gate/up output h in gate_up.h_out is bf16 scratch of the same size as usual).
