@@ -48,6 +48,13 @@ SMALL = [
     MC("f8_fp4_ragged", 118, T=150, H=192, E=4, k=2, I=192, w_dtype="fp4", qmode="f8"),
     MC("f8_fp4_zipf", 119, T=512, H=256, E=16, k=4, I=128, zipf_s=1.1, w_dtype="fp4", qmode="f8"),
     MC("f8_fp8_few_rows", 120, T=20, H=128, E=8, k=2, I=64, w_dtype="fp8", qmode="f8"),
+    # fewer pairs than experts: the streaming grid runs over touched-expert
+    # slots; K split for gate/up (4 splits bf16, 2 splits E2M1 / E4M3), a
+    # K tail on the E2M1 down product (I = 192 is 1.5 super steps), partial
+    # column slices (I = 320, H = 1024 / 2048)
+    MC("few_pairs_split_bf16", 121, T=2, H=1024, E=64, k=3, I=320),
+    MC("few_pairs_split_fp4", 122, T=3, H=2048, E=32, k=2, I=192, w_dtype="fp4"),
+    MC("few_pairs_split_fp8", 123, T=3, H=1024, E=32, k=2, I=320, w_dtype="fp8"),
 ]
 
 
