@@ -17,6 +17,7 @@ namespace moe {
 namespace {
 
 constexpr int PW = 16;  // wavefronts per workgroup
+constexpr int kScanBatch = 16;  // segment counts the scan loads per batch
 
 // Lanes of this wavefront whose id equals mine (8-bit ids, invalid lanes excluded).
 __device__ __forceinline__ uint64_t match_peers(int id, bool valid) {
@@ -129,9 +130,10 @@ __device__ __forceinline__ void load_ids(const int32_t* __restrict__ ids, int c0
 
 // ---- many pairs: the same per-wavefront algorithm over NV segments spread
 // across workgroups. Segment v (wavefront v % 16 of workgroup v / 16) holds
-// pairs [v * seg, (v + 1) * seg); its histogram goes to hist_g[e * NV + v]
-// (expert-major), one workgroup turns those into scatter starts, and the
-// scatter pass replays the same stable ranks.
+// pairs [v * seg, (v + 1) * seg); its histogram goes to hist_g[v * E + e]
+// (segment-major, so every access to hist_g is coalesced across experts), one
+// workgroup turns those into scatter starts, and the scatter pass replays the
+// same stable ranks.
 __global__ __launch_bounds__(1024) void permute_hist_kernel(const int32_t* __restrict__ ids, int P,
                                                             int E, int seg, int NV,
                                                             int32_t* __restrict__ hist_g) {
@@ -156,53 +158,54 @@ __global__ __launch_bounds__(1024) void permute_hist_kernel(const int32_t* __res
   }
   __syncthreads();
   if (v < NV)
-    for (int e = lane; e < E; e += 64) hist_g[(size_t)e * NV + v] = hist[wave][e];
+    for (int e = lane; e < E; e += 64) hist_g[(size_t)v * E + e] = hist[wave][e];
 }
 
 // One workgroup: for every expert, exclusive prefix of its segment counts in
-// segment order (4 threads per expert, each over a quarter of the segments),
-// then the scan over experts; hist_g becomes each segment's first position.
+// segment order, then the scan over experts; hist_g becomes each segment's
+// first position. Thread (q, e) takes expert e over the q-th quarter of the
+// segments, so a wavefront's loads read 64 adjacent experts of one segment;
+// the loads of kScanBatch segments are issued together.
 __global__ __launch_bounds__(1024) void permute_scan_kernel(int E, int NV, int32_t* __restrict__ hist_g,
                                                             int32_t* __restrict__ counts,
                                                             int32_t* __restrict__ offsets) {
-  __shared__ int part[256][4];
+  __shared__ int part[4][256];
   __shared__ int base[256];
   __shared__ int total;
-  const int tid = threadIdx.x, e = tid >> 2, q = tid & 3;
+  const int tid = threadIdx.x, q = tid >> 8, e = tid & 255, lane = tid & 63;
   const int per = (NV + 3) / 4;
   const int v0 = min(NV, q * per), v1 = min(NV, v0 + per);
-  // segment counts are read 32 at a time (one memory latency per batch)
-  const int32_t* row = hist_g + (size_t)(e < E ? e : 0) * NV;
+  const bool live = e < E;
+  const int ec = live ? e : 0;  // clamped column: every load is in bounds
   int sum = 0;
-  if (e < E)
-    for (int vb = v0; vb < v1; vb += 32) {
-      int c[32];
+  for (int vb = v0; vb < v1; vb += kScanBatch) {
+    int c[kScanBatch];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) c[i] = row[vb + i < v1 ? vb + i : v1 - 1];
+    for (int i = 0; i < kScanBatch; ++i) c[i] = hist_g[(size_t)(vb + i < v1 ? vb + i : v1 - 1) * E + ec];
 #pragma unroll
-      for (int i = 0; i < 32; ++i)
-        if (vb + i < v1) sum += c[i];
-    }
-  part[e][q] = sum;
+    for (int i = 0; i < kScanBatch; ++i)
+      if (vb + i < v1) sum += c[i];
+  }
+  part[q][e] = live ? sum : 0;
   __syncthreads();
   if (tid < 256) {
-    const int c = tid < E ? part[tid][0] + part[tid][1] + part[tid][2] + part[tid][3] : 0;
-    base[tid] = c;
-    if (tid < E) counts[tid] = c;
+    const int t = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
+    base[tid] = t;
+    if (tid < E) counts[tid] = t;
   }
   __syncthreads();
   if (tid < 64) {
-    const int lane = tid;
+    // exclusive scan of base[0..256): lane owns 4 consecutive experts
     const int w0 = base[4 * lane], w1 = base[4 * lane + 1], w2 = base[4 * lane + 2],
               w3 = base[4 * lane + 3];
-    const int s = w0 + w1 + w2 + w3;
-    int incl = s;
+    const int s4 = w0 + w1 + w2 + w3;
+    int incl = s4;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const int o = __shfl_up(incl, d, 64);
       if (lane >= d) incl += o;
     }
-    const int ex = incl - s;
+    const int ex = incl - s4;
     if (lane == 63) total = incl;
     base[4 * lane] = ex;
     base[4 * lane + 1] = ex + w0;
@@ -210,24 +213,22 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int E, int NV, int32
     base[4 * lane + 3] = ex + w0 + w1 + w2;
   }
   __syncthreads();
-  if (e < E) {
-    int run = base[e];
-    for (int qq = 0; qq < q; ++qq) run += part[e][qq];
-    int32_t* wrow = hist_g + (size_t)e * NV;
-    for (int vb = v0; vb < v1; vb += 32) {
-      int c[32];
-#pragma unroll
-      for (int i = 0; i < 32; ++i) c[i] = wrow[vb + i < v1 ? vb + i : v1 - 1];
-#pragma unroll
-      for (int i = 0; i < 32; ++i)
-        if (vb + i < v1) {
-          wrow[vb + i] = run;
-          run += c[i];
-        }
-    }
-  }
   if (tid < E) offsets[tid] = base[tid];
   if (tid == 0) offsets[E] = total;
+  if (!live) return;
+  int run = base[e];
+  for (int qq = 0; qq < q; ++qq) run += part[qq][e];
+  for (int vb = v0; vb < v1; vb += kScanBatch) {
+    int c[kScanBatch];
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i) c[i] = hist_g[(size_t)(vb + i < v1 ? vb + i : v1 - 1) * E + e];
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i)
+      if (vb + i < v1) {
+        hist_g[(size_t)(vb + i) * E + e] = run;
+        run += c[i];
+      }
+  }
 }
 
 __global__ __launch_bounds__(1024) void permute_scatter_kernel(const int32_t* __restrict__ ids,
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(const int32_t* __
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int v = blockIdx.x * PW + wave;
   if (v < NV)
-    for (int e = lane; e < E; e += 64) hist[wave][e] = hist_g[(size_t)e * NV + v];
+    for (int e = lane; e < E; e += 64) hist[wave][e] = hist_g[(size_t)v * E + e];
   __syncthreads();
   const long long s0l = (long long)v * seg;
   const int s0 = (int)(s0l < P ? s0l : P), s1 = (int)(s0l + seg < P ? s0l + seg : P);
