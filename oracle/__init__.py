@@ -223,6 +223,41 @@ def finalize(y_sorted, pair_pos, w, k: int, rows=None) -> np.ndarray:
     return out
 
 
+def rms_norm(v, gamma, eps: float) -> np.ndarray:
+    """RMSNorm of each row in float64: v / sqrt(mean(v^2) + eps) * gamma."""
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(gamma, dtype=np.float64)
+    return v / np.sqrt(np.mean(v * v, axis=1, keepdims=True) + eps) * g
+
+
+def finalize_norm(y_sorted, pair_pos, w, k: int, residual_bits, gamma_post_bits,
+                  gamma_next_bits, eps: float, rows=None) -> dict:
+    """MoE finalize fused with the sandwich post-norm, the residual add and the
+    next sublayer's pre-norm (vLLM PR #61978, Status table row #62366: the
+    fused all-reduce "with Beam's sandwich norms and MoE finalize"; the pages
+    do not define the norm, so these are conventions: RMSNorm with weight
+    gamma and epsilon eps, bf16 residual stream and bf16 norm weights):
+
+        m      = finalize(y_sorted, pair_pos, w)          (slot-ordered sum)
+        post   = m / sqrt(mean(m^2) + eps) * gamma_post
+        r      = RNE_bf16(residual + post)                (the new residual)
+        normed = RNE_bf16(r / sqrt(mean(r^2) + eps) * gamma_next)
+
+    Everything in float64 on the bf16 / fp32 inputs; the next norm reads the
+    rounded residual, as the next sublayer would. Returns m, post, r and
+    normed (float64 values; r and normed are bf16-representable)."""
+    m = finalize(y_sorted, pair_pos, w, k, rows=rows)
+    res = format_op("bf16", np.asarray(residual_bits))
+    if rows is not None:
+        res = res[np.asarray(rows)]
+    gp = format_op("bf16", np.asarray(gamma_post_bits))
+    gn = format_op("bf16", np.asarray(gamma_next_bits))
+    post = rms_norm(m, gp, eps)
+    r = format_op("round_bf16", res + post)
+    normed = format_op("round_bf16", rms_norm(r, gn, eps))
+    return {"m": m, "post": post, "r": r, "normed": normed}
+
+
 def layer(x, w_router, bias, experts: dict, I: int, k: int, sel_dtype: str = "bf16", rows=None,
           qmode: str = "w"):
     """Whole layer for the given tokens: dict(out [n,H], ids [n,k], w [n,k], logits [n,E]).
