@@ -124,7 +124,7 @@ size_t experts_ws_bytes(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                         const moe_expert_weights* w) {
   const size_t P = (size_t)T * k;
   const size_t h_elem = w->dtype == MOE_F32 ? sizeof(float) : sizeof(uint16_t);
-  size_t b = align_up(P * I * h_elem) + align_up(moe::expert_tile_ws_bytes((int)P, E));
+  size_t b = align_up(P * I * h_elem) + align_up(moe::expert_tile_ws_bytes((int)P, E, H, I));
   if (f8_mode(w))
     b += align_up((size_t)T * H) + align_up((size_t)T * sizeof(float)) + align_up(P * I) +
          align_up(P * (size_t)h_bstride(I));
@@ -217,7 +217,7 @@ moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H,
   d.y_out = y_sorted;
   if (f8_mode(w)) {
     // the fp8-MFMA mode always runs the tiled kernels
-    char* f8ws = static_cast<char*>(tile_ws) + align_up(moe::expert_tile_ws_bytes(P, E));
+    char* f8ws = static_cast<char*>(tile_ws) + align_up(moe::expert_tile_ws_bytes(P, E, H, I));
     moe::F8Buffers b{};
     b.xq = reinterpret_cast<uint8_t*>(f8ws);
     f8ws += align_up((size_t)T * H);
@@ -234,7 +234,7 @@ moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H,
   {
     // few touched experts: split K so that enough wavefronts stream weights
     float* part = reinterpret_cast<float*>(static_cast<char*>(tile_ws) +
-                                           align_up(moe::expert_tile_ws_bytes(P, E)));
+                                           align_up(moe::expert_tile_ws_bytes(P, E, H, I)));
     const int kstep = moe::stream_k_step(wf);
     const moe::StreamSplit sg = moe::stream_split_plan(P, E, H, 2 * I, true, kstep);
     const moe::StreamSplit sd = moe::stream_split_plan(P, E, I, H, false, kstep);

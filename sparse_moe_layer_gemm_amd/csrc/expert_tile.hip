@@ -12,10 +12,13 @@
 //    halves LDS reads per MFMA against a 64 x 128 wave tile. The 32x32x16
 //    bf16 MFMA issues at twice the rate of the 16x16x32 one on gfx950;
 //  - an expert's last partial tile of at most 128 rows runs instead as a
-//    128 x 512 tile (1 x 4 wavefronts, same 128 x 128 per wavefront) in a
-//    second launch: with skewed routing most experts hold a few hundred
-//    rows, and padding their tails to 256 rows wasted about a quarter of
-//    the MFMA work. The wider tile keeps the weight bytes per MAC unchanged.
+//    128 x 512 tile (1 x 4 wavefronts, same 128 x 128 per wavefront): with
+//    skewed routing most experts hold a few hundred rows, and padding their
+//    tails to 256 rows wasted about a quarter of the MFMA work. The wider
+//    tile keeps the weight bytes per MAC unchanged. Both shapes run in one
+//    launch from a work list in expert order, so the weight-bound tiles of
+//    experts with few rows overlap the MFMA-bound tiles of the others, and
+//    an expert's tail tile finds its weights still cached;
 //    Quantised weights use the 128 x 512 tile throughout (their in-register
 //    conversion, not the MFMA, is the bound, and it is done once per column);
 //  - K advances 32 per step through four LDS stages filled by direct
@@ -144,27 +147,14 @@ __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restri
   }
 }
 
+// One BM x BN output tile (rows m0.. of expert e, N tile nt) of the bf16
+// grouped GEMM; smem holds TileShape<WM>::LDS bytes of LDS.
 template <bool GATE_UP, int WM>
-__global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
-                                                           const int32_t* __restrict__ tile_e,
-                                                           const int32_t* __restrict__ tile_m0,
-                                                           const int32_t* __restrict__ n_tiles_p,
-                                                           int NT) {
+__device__ __forceinline__ void tile_bf16_body(const StreamGemmArgs& a, uint8_t* smem, int e,
+                                               int m0, int nt) {
   using S = TileShape<WM>;
-  __shared__ __align__(1024) uint8_t smem[S::LDS];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave / S::WN, wn = wave % S::WN;
-
-  // ---- work item: consecutive items (same M tile, neighbouring N tiles) on one XCD
-  const int total = *n_tiles_p * NT;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int per = (total + 7) >> 3;
-  if (slot >= per) return;
-  const int w = xcd * per + slot;
-  if (w >= total) return;
-  const int mt = w / NT, nt = w - mt * NT;
-  const int e = tile_e[mt];
-  const int m0 = tile_m0[mt];
   const int r0 = a.offsets[e];
   const int cnt = a.offsets[e + 1] - r0;
   const int K = a.K, N = a.N;
@@ -394,6 +384,109 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
   }
 }
 
+
+// Work item -> workgroup: consecutive items (same M tile, neighbouring N
+// tiles) run on one XCD, whose L2 they share. Workgroups are dealt to the
+// eight XCDs round robin, so XCD x takes items [x * per, (x + 1) * per).
+__device__ __forceinline__ int xcd_item(int total) {
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int per = (total + 7) >> 3;
+  if (slot >= per) return -1;
+  const int w = xcd * per + slot;
+  return w < total ? w : -1;
+}
+
+// One tile shape: M-tile table x NT N tiles.
+template <bool GATE_UP, int WM>
+__global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
+                                                           const int32_t* __restrict__ tile_e,
+                                                           const int32_t* __restrict__ tile_m0,
+                                                           const int32_t* __restrict__ n_tiles_p,
+                                                           int NT) {
+  __shared__ __align__(1024) uint8_t smem[TileShape<WM>::LDS];
+  const int w = xcd_item(*n_tiles_p * NT);
+  if (w < 0) return;
+  const int mt = w / NT, nt = w - mt * NT;
+  tile_bf16_body<GATE_UP, WM>(a, smem, tile_e[mt], tile_m0[mt], nt);
+}
+
+// Both tile shapes in one launch, from a work list in expert order (each
+// expert's 256-row tiles, then its last <= 128 rows as a 128 x 512 tile):
+// an expert's tiles run close together, while its weights are still cached,
+// and the HBM-bound tiles of experts with few rows overlap the MFMA-bound
+// tiles of the others instead of running after them. Item: x = e | kind << 8
+// | nt << 9 (kind 1: 128 x 512 tile), y = first row.
+template <bool GATE_UP>
+__global__ __launch_bounds__(256, 1) void tile_bf16_mixed_kernel(StreamGemmArgs a,
+                                                                 const int2* __restrict__ items,
+                                                                 const int32_t* __restrict__ n_items_p) {
+  static_assert(TileShape<1>::LDS >= TileShape<2>::LDS, "LDS sized for the larger tile");
+  __shared__ __align__(1024) uint8_t smem[TileShape<1>::LDS];
+  const int w = xcd_item(*n_items_p);
+  if (w < 0) return;
+  const int2 it = items[w];
+  const int e = it.x & 0xff, nt = it.x >> 9;
+  if (it.x & 0x100)
+    tile_bf16_body<GATE_UP, 1>(a, smem, e, it.y, nt);
+  else
+    tile_bf16_body<GATE_UP, 2>(a, smem, e, it.y, nt);
+}
+
+// Work lists of the mixed launch, one per blockIdx.y (gate/up, down). Expert e
+// with c rows has c / 256 full tiles, plus one more if c % 256 > 128, else one
+// 128-row tile if c % 256 > 0; a full tile spans ntf N tiles, a 128-row tile
+// nth. Every workgroup rebuilds the per-expert scan and writes the items
+// blockIdx.x * 256 .. +255 of the list.
+__global__ __launch_bounds__(256) void tile_items_kernel(const int32_t* __restrict__ offsets, int E,
+                                                         int ntf0, int nth0, int2* __restrict__ items0,
+                                                         int32_t* __restrict__ n0, int ntf1, int nth1,
+                                                         int2* __restrict__ items1,
+                                                         int32_t* __restrict__ n1) {
+  __shared__ int incl[256], nfull[256];
+  const int g = blockIdx.y;
+  const int ntf = g ? ntf1 : ntf0, nth = g ? nth1 : nth0;
+  int2* items = g ? items1 : items0;
+  const int e = threadIdx.x;
+  const int rows = (e < E) ? offsets[e + 1] - offsets[e] : 0;
+  const int rem = rows & 255;
+  const int half = (rem > 0 && rem <= 128) ? 1 : 0;
+  const int full = (rows >> 8) + (rem > 128 ? 1 : 0);
+  const int mine = full * ntf + half * nth;
+  incl[e] = mine;
+  nfull[e] = full;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {  // inclusive scan
+    const int v = (e >= d) ? incl[e - d] : 0;
+    __syncthreads();
+    incl[e] += v;
+    __syncthreads();
+  }
+  const int total = incl[255];
+  if (blockIdx.x == 0 && e == 0) *(g ? n1 : n0) = total;
+  const int w = blockIdx.x * 256 + e;
+  if (w >= total) return;
+  int lo = 0, hi = 255;  // the expert: smallest x with incl[x] > w
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (incl[mid] > w)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  const int x = lo;
+  const int local = w - (x ? incl[x - 1] : 0);
+  const int fcount = nfull[x] * ntf;
+  int2 it;
+  if (local < fcount) {
+    const int mt = local / ntf;
+    it.x = x | ((local - mt * ntf) << 9);
+    it.y = mt * 256;
+  } else {
+    it.x = x | 0x100 | ((local - fcount) << 9);
+    it.y = nfull[x] * 256;
+  }
+  items[w] = it;
+}
 
 // ------------------------------------------------------------------ FP8 / NVFP4 weights
 // Same tiling for K-contiguous quantised weights ([E, N, K] E4M3 codes, or
@@ -1247,13 +1340,29 @@ __global__ __launch_bounds__(256) void router_pack_kernel(const float* __restric
 
 constexpr int ROUTER_NKS = 2;  // K slices per plane (3 * 2 splits in all)
 
+// Tile counts of the mixed launch: N tiles of a full (256 x 256) tile and of a
+// 128-row (128 x 512) tile, and the largest work list.
+struct MixedPlan {
+  int ntf, nth, max_items;
+};
+MixedPlan mixed_plan(bool gate_up, int P, int E, int N, int I) {
+  MixedPlan m;
+  m.ntf = gate_up ? (I + 127) / 128 : (N + 255) / 256;
+  m.nth = gate_up ? (I + 255) / 256 : (N + 511) / 512;
+  m.max_items = ((P + TBM - 1) / TBM + E) * m.ntf + E * m.nth;
+  return m;
+}
+
 }  // namespace
 
-size_t expert_tile_ws_bytes(int P, int E) {
-  // covers both tables: 128-row tiles (quantised) and 256-row tiles plus one
-  // partial tile per expert (bf16)
+size_t expert_tile_ws_bytes(int P, int E, int H, int I) {
+  // the larger of: the table of 128-row tiles (quantised weights), and the
+  // counters plus the two work lists of the mixed bf16 launches
   const int max_tiles = (P + 127) / 128 + E;
-  return (size_t)(2 * max_tiles + 2 * E + 64) * sizeof(int32_t);
+  const size_t q = (size_t)(2 * max_tiles + 64) * sizeof(int32_t);
+  const size_t b = 256 + ((size_t)mixed_plan(true, P, E, 2 * I, I).max_items +
+                          mixed_plan(false, P, E, H, I).max_items) * sizeof(int2);
+  return q > b ? q : b;
 }
 
 int router_bf16x3_splits() { return 3 * ROUTER_NKS; }
@@ -1325,16 +1434,22 @@ static hipError_t launch_q(const StreamGemmArgs& g, const int32_t* te, const int
   return hipGetLastError();
 }
 
-static hipError_t launch_bf16_all(const StreamGemmArgs& gu, const StreamGemmArgs& dn,
-                                  const int32_t* tile_e, const int32_t* tile_m0,
-                                  const int32_t* half_e, const int32_t* half_m0,
-                                  const int32_t* counts, int max_tiles, hipStream_t st) {
-  const int E = gu.E;
-  hipError_t err = launch_tiles<true, 2>(gu, tile_e, tile_m0, counts, max_tiles, st);
-  if (err == hipSuccess) err = launch_tiles<true, 1>(gu, half_e, half_m0, counts + 1, E, st);
-  if (err == hipSuccess) err = launch_tiles<false, 2>(dn, tile_e, tile_m0, counts, max_tiles, st);
-  if (err == hipSuccess) err = launch_tiles<false, 1>(dn, half_e, half_m0, counts + 1, E, st);
-  return err;
+static hipError_t launch_bf16_all(const StreamGemmArgs& gu, const StreamGemmArgs& dn, int P,
+                                  int2* items_g, int2* items_d, int32_t* counts, hipStream_t st) {
+  const MixedPlan pg = mixed_plan(true, P, gu.E, gu.N, gu.I);
+  const MixedPlan pd = mixed_plan(false, P, dn.E, dn.N, dn.I);
+  const int most = pg.max_items > pd.max_items ? pg.max_items : pd.max_items;
+  tile_items_kernel<<<dim3((unsigned)((most + 255) / 256), 2), 256, 0, st>>>(
+      gu.offsets, gu.E, pg.ntf, pg.nth, items_g, counts, pd.ntf, pd.nth, items_d, counts + 1);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  tile_bf16_mixed_kernel<true><<<(unsigned)((pg.max_items + 7) / 8 * 8), 256, 0, st>>>(gu, items_g,
+                                                                                      counts);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  tile_bf16_mixed_kernel<false><<<(unsigned)((pd.max_items + 7) / 8 * 8), 256, 0, st>>>(
+      dn, items_d, counts + 1);
+  return hipGetLastError();
 }
 
 // Quantised weights run on 128 x 512 tiles only. Their wavefronts sit side by
@@ -1413,17 +1528,12 @@ hipError_t launch_expert_tile(int wfmt, const StreamGemmArgs& gu, const StreamGe
     return launch_q_all<W_FP4>(gu, dn, tile_e, tile_m0, counts, max_tiles, st);
   }
   if (wfmt != W_BF16) return hipErrorInvalidValue;
-  // full 256-row tiles plus each expert's last partial tile of <= 128 rows
-  const int max_tiles = (P + TBM - 1) / TBM + E;
-  int32_t* tile_m0 = tile_e + max_tiles;
-  int32_t* half_e = tile_m0 + max_tiles;
-  int32_t* half_m0 = half_e + E;
-  int32_t* counts = half_m0 + E;  // [0]: full tiles, [1]: half tiles
-  tile_table_kernel<<<1, 256, 0, st>>>(gu.offsets, E, TBM, 1, tile_e, tile_m0, counts, half_e,
-                                       half_m0, counts + 1);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  return launch_bf16_all(gu, dn, tile_e, tile_m0, half_e, half_m0, counts, max_tiles, st);
+  // work lists of the mixed 256 x 256 / 128 x 512 launches
+  const MixedPlan pg = mixed_plan(true, P, E, gu.N, gu.I);
+  int32_t* counts = tile_e;  // [0]: gate/up items, [1]: down items
+  int2* items_g = reinterpret_cast<int2*>(static_cast<char*>(ws) + 256);
+  int2* items_d = items_g + pg.max_items;
+  return launch_bf16_all(gu, dn, P, items_g, items_d, counts, st);
 }
 
 }  // namespace moe
