@@ -81,6 +81,12 @@ class Workload:
         self.pp = torch.empty(P, dtype=torch.int32, device="cuda")
         self.y = torch.empty((P, H), dtype=torch.float32, device="cuda")
         self.ews = moe.workspace(moe.moe_experts_workspace_size(T, H, I, E, k, self.w))
+        # finalize fused with the sandwich norms (timed beside the plain finalize)
+        self.res = torch.randn((T, H), generator=torch.Generator("cuda").manual_seed(cfg.seed),
+                               device="cuda").to(dt)
+        self.gamma = torch.ones(H, dtype=dt, device="cuda")
+        self.res_out = torch.empty_like(self.res)
+        self.normed = torch.empty_like(self.res)
 
     def forward(self):
         c = self.cfg
@@ -97,6 +103,10 @@ class Workload:
             ("experts", lambda: m.moe_experts(self.x, c.I, c.E, c.k, self.offsets, self.sp, self.w,
                                               self.y, self.ews)),
             ("finalize", lambda: m.moe_finalize(self.y, self.pp, self.tw, self.out)),
+            # not part of the step: the fused finalize + norms on the same rows
+            ("finalize_norm", lambda: m.moe_finalize_norm(self.y, self.pp, self.tw, self.res,
+                                                          self.gamma, self.gamma, 1e-6,
+                                                          self.res_out, self.normed)),
         ]
 
     def time_forward(self, steps, warmup):

@@ -160,6 +160,27 @@ moe_status moe_finalize(const float* y_sorted, const int32_t* pair_pos, const fl
                         int64_t T, int32_t k, int32_t H, int32_t out_dtype, void* out,
                         float* out_f32, void* stream);
 
+/* ------------------------------------------------------------ finalize + sandwich norms
+ * MoE finalize fused with the norms around the routed MoE block (vLLM PR
+ * #61978, Status table row #62366 fuses Beam's sandwich norms with MoE
+ * finalize and the tensor-parallel all-reduce; one GPU has no all-reduce).
+ * The pages define neither the norm nor its epsilon: RMSNorm with a bf16
+ * weight vector on a bf16 residual stream is this library's convention. Per
+ * token t, with m = the fp32 sum moe_finalize forms (slot order):
+ *   post            = m * (1 / sqrt(mean_h(m^2) + eps)) * gamma_post
+ *   residual_out[t] = RNE_bf16(residual[t] + post)
+ *   normed[t]       = RNE_bf16(residual_out[t] * (1 / sqrt(mean_h(residual_out[t]^2) + eps))
+ *                              * gamma_next)
+ * all in fp32 (row sums in a fixed order: deterministic). residual,
+ * residual_out, normed: [T, H] bf16; gamma_post, gamma_next: [H] bf16;
+ * eps >= 0 and finite. residual_out may equal residual (in-place update);
+ * normed must not overlap either. H a multiple of 64 and at most 16384,
+ * else MOE_ERR_UNSUPPORTED; errors as for moe_finalize. */
+moe_status moe_finalize_norm(const float* y_sorted, const int32_t* pair_pos, const float* topk_w,
+                             int64_t T, int32_t k, int32_t H, const void* residual,
+                             const void* gamma_post, const void* gamma_next, float eps,
+                             void* residual_out, void* normed, void* stream);
+
 /* ------------------------------------------------------------ whole layer
  * The five steps in order on one stream: route, permute, experts, finalize.
  * out [T, H] out_dtype; out_f32, logits, topk_ids, topk_w are optional

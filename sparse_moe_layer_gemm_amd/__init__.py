@@ -26,7 +26,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
 
 ENTRY_POINTS = ("moe_status_string", "moe_route_workspace_size", "moe_route",
                 "moe_permute_workspace_size", "moe_permute", "moe_experts_workspace_size",
-                "moe_experts", "moe_finalize", "moe_forward_workspace_size", "moe_forward")
+                "moe_experts", "moe_finalize", "moe_finalize_norm", "moe_forward_workspace_size",
+                "moe_forward")
 
 
 class MoEError(RuntimeError):
@@ -66,6 +67,8 @@ def load_library(path: str = LIB_PATH):
         "moe_experts": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp,
                                ctypes.POINTER(CExpertWeights), _vp, _vp, _sz, _vp]),
         "moe_finalize": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
+        "moe_finalize_norm": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, ctypes.c_float,
+                                     _vp, _vp, _vp]),
         "moe_forward_workspace_size": (_sz, [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(CExpertWeights)]),
         "moe_forward": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp,
                                ctypes.POINTER(CExpertWeights), _i32, _vp, _vp, _i32, _vp, _vp, _vp,
@@ -179,6 +182,20 @@ def moe_finalize(y_sorted, pair_pos, topk_w, out, out_f32=None, stream=None):
     _check("moe_finalize", _lib.moe_finalize(
         _ptr(y_sorted), _ptr(pair_pos), _ptr(topk_w), T, k, H, _dt(out), _ptr(out), _ptr(out_f32),
         _stream(stream)))
+
+
+def moe_finalize_norm(y_sorted, pair_pos, topk_w, residual, gamma_post, gamma_next, eps: float,
+                      residual_out, normed, stream=None):
+    """residual, residual_out, normed: [T, H] bf16 (residual_out may be residual);
+    gamma_post, gamma_next: [H] bf16."""
+    T, k = topk_w.shape
+    H = y_sorted.shape[1]
+    for t in (residual, gamma_post, gamma_next, residual_out, normed):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("moe_finalize_norm takes bf16 residual, norm weights and outputs")
+    _check("moe_finalize_norm", _lib.moe_finalize_norm(
+        _ptr(y_sorted), _ptr(pair_pos), _ptr(topk_w), T, k, H, _ptr(residual), _ptr(gamma_post),
+        _ptr(gamma_next), float(eps), _ptr(residual_out), _ptr(normed), _stream(stream)))
 
 
 def moe_forward_workspace_size(T: int, H: int, I: int, E: int, k: int, w: ExpertWeights) -> int:

@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["abi.cpp", "router.hip", "permute.hip", "expert_stream.hip", "expert_tile.hip", "expert_f32.hip",
-           "finalize.hip"]
+           "finalize.hip",
+           "finalize_norm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -14,6 +14,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int64_t kMaxPairs = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxTokens = int64_t(1) << 24;  // one select workgroup per token
+constexpr int32_t kMaxNormH = 16384;               // fused finalize + norms: row in registers
 
 size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -361,6 +362,30 @@ moe_status moe_finalize(const float* y_sorted, const int32_t* pair_pos, const fl
   return launch_status(moe::launch_finalize(y_sorted, pair_pos, topk_w, (int)T, k, H,
                                             out_dtype == MOE_BF16, out, out_f32,
                                             static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_finalize_norm(const float* y_sorted, const int32_t* pair_pos, const float* topk_w,
+                             int64_t T, int32_t k, int32_t H, const void* residual,
+                             const void* gamma_post, const void* gamma_next, float eps,
+                             void* residual_out, void* normed, void* stream) {
+  if (T < 0 || k <= 0 || H <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (!(eps >= 0.f) || eps > 3.4e38f) return MOE_ERR_INVALID_ARGUMENT;  // NaN or inf
+  if (k > 8 || H % 64 != 0 || H > kMaxNormH) return MOE_ERR_UNSUPPORTED;
+  if (T * k > kMaxPairs || T >= kMaxTokens) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!y_sorted || !pair_pos || !topk_w || !residual || !gamma_post || !gamma_next ||
+      !residual_out || !normed)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(y_sorted) || !aligned16(pair_pos) || !aligned16(topk_w) || !aligned16(residual) ||
+      !aligned16(gamma_post) || !aligned16(gamma_next) || !aligned16(residual_out) ||
+      !aligned16(normed))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (normed == residual_out || normed == residual) return MOE_ERR_INVALID_ARGUMENT;
+  return launch_status(moe::launch_finalize_norm(
+      y_sorted, pair_pos, topk_w, (int)T, k, H, static_cast<const uint16_t*>(residual),
+      static_cast<const uint16_t*>(gamma_post), static_cast<const uint16_t*>(gamma_next), eps,
+      static_cast<uint16_t*>(residual_out), static_cast<uint16_t*>(normed),
+      static_cast<hipStream_t>(stream)));
 }
 
 // ---------------------------------------------------------------- forward

@@ -1,0 +1,145 @@
+// MoE finalize fused with the sandwich norms around Beam's routed MoE block
+// (vLLM PR #61978, Status table row #62366 fuses the all-reduce with Beam's
+// sandwich norms and MoE finalize; on one GPU there is no all-reduce). The
+// pages do not define the norm: RMSNorm with a bf16 weight vector, a bf16
+// residual stream and a caller-given epsilon are this library's conventions.
+// Per token row t:
+//   m      = sum_j w[t, j] * y_sorted[pair_pos[t*k + j]]    fp32, slot order
+//   post   = m * (1 / sqrt(mean(m^2) + eps)) * gamma_post
+//   r      = RNE_bf16(residual + post)                       the new residual
+//   normed = RNE_bf16(r * (1 / sqrt(mean(r^2) + eps)) * gamma_next)
+//
+// Bound by HBM like the plain finalize (each fp32 expert row is read once).
+// Both mean squares need the whole row, so one workgroup owns a token: lane
+// l keeps float4 column chunks l, l + 256, ... of m (and then of r) in
+// registers, the row sums go through a fixed butterfly in each wavefront and
+// a fixed-order add of the four wavefront sums, so results are deterministic.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+// sum over the workgroup (256 lanes), identical in every lane
+__device__ __forceinline__ float row_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);  // a + b == b + a: lanes agree
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  const float s = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();  // red is reused by the next sum
+  return s;
+}
+
+__device__ __forceinline__ float4 bf16x4_to_f32(uint2 b) {
+  return make_float4(bf16_bits_to_f32(b.x & 0xffffu), bf16_bits_to_f32(b.x >> 16),
+                     bf16_bits_to_f32(b.y & 0xffffu), bf16_bits_to_f32(b.y >> 16));
+}
+__device__ __forceinline__ uint2 f32x4_to_bf16(float a, float b, float c, float d) {
+  uint2 r;
+  r.x = f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+  r.y = f32_to_bf16_bits(c) | (f32_to_bf16_bits(d) << 16);
+  return r;
+}
+
+// CH float4 chunks per lane: H <= 1024 * CH. residual and residual_out may alias
+// (a lane reads each of its residual chunks before writing the same chunk).
+template <int CH>
+__global__ __launch_bounds__(256) void finalize_norm_kernel(
+    const float* __restrict__ y, const int32_t* __restrict__ pair_pos, const float* __restrict__ w,
+    int k, int H, const uint16_t* residual, const uint16_t* __restrict__ gamma_post,
+    const uint16_t* __restrict__ gamma_next, float eps, uint16_t* residual_out,
+    uint16_t* __restrict__ normed) {
+  __shared__ float red[4];
+  const long long t = blockIdx.x;
+  int pos[8];
+  float wt[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {  // wave-uniform: rows past k repeat the first and are not added
+    pos[j] = pair_pos[t * k + (j < k ? j : 0)];
+    wt[j] = (j < k) ? w[t * k + j] : 0.f;
+  }
+  const int n4 = H >> 2;
+  float4 m[CH];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int q = threadIdx.x + 256 * c;
+    m[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (q < n4) {
+      f32x4 v[8];  // each expert row is read once: nontemporal
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + (size_t)pos[j] * H) + q);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < k) {
+          m[c].x = fmaf(wt[j], v[j].x, m[c].x);
+          m[c].y = fmaf(wt[j], v[j].y, m[c].y);
+          m[c].z = fmaf(wt[j], v[j].z, m[c].z);
+          m[c].w = fmaf(wt[j], v[j].w, m[c].w);
+        }
+      }
+      ss += (m[c].x * m[c].x + m[c].y * m[c].y) + (m[c].z * m[c].z + m[c].w * m[c].w);
+    }
+  }
+  const float inv_m = 1.0f / sqrtf(row_sum(ss, red) / (float)H + eps);
+  float ss2 = 0.f;
+  const size_t row = (size_t)t * H;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int q = threadIdx.x + 256 * c;
+    if (q < n4) {
+      const float4 res = bf16x4_to_f32(reinterpret_cast<const uint2*>(residual + row)[q]);
+      const float4 gp = bf16x4_to_f32(reinterpret_cast<const uint2*>(gamma_post)[q]);
+      const uint2 rb = f32x4_to_bf16(res.x + m[c].x * inv_m * gp.x, res.y + m[c].y * inv_m * gp.y,
+                                     res.z + m[c].z * inv_m * gp.z, res.w + m[c].w * inv_m * gp.w);
+      reinterpret_cast<uint2*>(residual_out + row)[q] = rb;
+      m[c] = bf16x4_to_f32(rb);  // from here on m holds r
+      ss2 += (m[c].x * m[c].x + m[c].y * m[c].y) + (m[c].z * m[c].z + m[c].w * m[c].w);
+    }
+  }
+  const float inv_r = 1.0f / sqrtf(row_sum(ss2, red) / (float)H + eps);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int q = threadIdx.x + 256 * c;
+    if (q < n4) {
+      const float4 gn = bf16x4_to_f32(reinterpret_cast<const uint2*>(gamma_next)[q]);
+      reinterpret_cast<uint2*>(normed + row)[q] =
+          f32x4_to_bf16(m[c].x * inv_r * gn.x, m[c].y * inv_r * gn.y, m[c].z * inv_r * gn.z,
+                        m[c].w * inv_r * gn.w);
+    }
+  }
+}
+
+template <int CH>
+hipError_t launch_ch(const float* y, const int32_t* pp, const float* w, int T, int k, int H,
+                     const uint16_t* res, const uint16_t* gp, const uint16_t* gn, float eps,
+                     uint16_t* res_out, uint16_t* normed, hipStream_t st) {
+  finalize_norm_kernel<CH><<<(unsigned)T, 256, 0, st>>>(y, pp, w, k, H, res, gp, gn, eps, res_out,
+                                                        normed);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_finalize_norm(const float* y_sorted, const int32_t* pair_pos, const float* w,
+                                int T, int k, int H, const uint16_t* residual,
+                                const uint16_t* gamma_post, const uint16_t* gamma_next, float eps,
+                                uint16_t* residual_out, uint16_t* normed, hipStream_t st) {
+  const int ch = (H + 1023) / 1024;
+#define MOE_FN_CASE(n) \
+  case n:              \
+    return launch_ch<n>(y_sorted, pair_pos, w, T, k, H, residual, gamma_post, gamma_next, eps, residual_out, normed, st)
+  switch (ch) {
+    MOE_FN_CASE(1); MOE_FN_CASE(2); MOE_FN_CASE(3); MOE_FN_CASE(4);
+    MOE_FN_CASE(5); MOE_FN_CASE(6); MOE_FN_CASE(7); MOE_FN_CASE(8);
+    MOE_FN_CASE(9); MOE_FN_CASE(10); MOE_FN_CASE(11); MOE_FN_CASE(12);
+    MOE_FN_CASE(13); MOE_FN_CASE(14); MOE_FN_CASE(15); MOE_FN_CASE(16);
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef MOE_FN_CASE
+}
+
+}  // namespace moe

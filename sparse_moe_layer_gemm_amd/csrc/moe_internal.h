@@ -187,5 +187,11 @@ hipError_t launch_expert_f32(const float* x, int T, int H, int I, int E, int k, 
 hipError_t launch_finalize(const float* y_sorted, const int32_t* pair_pos, const float* w, int T,
                            int k, int H, bool out_bf16, void* out, float* out_f32,
                            hipStream_t st);
+// Weighted un-permute + RMS post-norm + residual add + next RMS pre-norm
+// (bf16 residual and norm weights); H <= 16384.
+hipError_t launch_finalize_norm(const float* y_sorted, const int32_t* pair_pos, const float* w,
+                                int T, int k, int H, const uint16_t* residual,
+                                const uint16_t* gamma_post, const uint16_t* gamma_next, float eps,
+                                uint16_t* residual_out, uint16_t* normed, hipStream_t st);
 
 }  // namespace moe

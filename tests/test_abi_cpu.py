@@ -163,6 +163,28 @@ def test_finalize_validation():
     assert finalize(out_f32=MIS) == INVAL
 
 
+def finalize_norm(**kw):
+    a = dict(y=A, pp=B, w=C, T=128, k=8, H=5120, res=D, gp=F, gn=G, eps=1e-6, res_out=D,
+             normed=Hh, stream=None)
+    a.update(kw)
+    return moe.load_library().moe_finalize_norm(*a.values())
+
+
+def test_finalize_norm_validation():
+    assert finalize_norm(T=0, y=None, pp=None, w=None, res=None, gp=None, gn=None, res_out=None,
+                         normed=None) == OK
+    assert finalize_norm(k=9) == UNSUP
+    assert finalize_norm(H=100) == UNSUP
+    assert finalize_norm(H=16384 + 64) == UNSUP
+    assert finalize_norm(eps=-1.0) == INVAL
+    assert finalize_norm(eps=float("nan")) == INVAL
+    assert finalize_norm(eps=float("inf")) == INVAL
+    assert finalize_norm(gn=None) == INVAL
+    assert finalize_norm(res=MIS) == INVAL
+    assert finalize_norm(normed=D) == INVAL  # normed may not alias the residual
+    assert finalize_norm(k=0) == INVAL
+
+
 def forward(w=None, **kw):
     w = w if w is not None else _w()
     a = dict(x=A, x_dt=1, T=128, H=5120, I=1536, E=256, k=8, wr=B, bias=None, w=ctypes.byref(w),
