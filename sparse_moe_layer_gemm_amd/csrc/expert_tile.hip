@@ -48,19 +48,25 @@ constexpr int TBK = 32, NSTAGE = 4;
 constexpr int TBM = 256;  // rows of the large tile (tile table sizing, router)
 
 // Workgroup tile shapes. WM wavefronts along M: WM = 2 gives 256 x 256 tiles,
-// WM = 1 gives 128 x 512 tiles (for experts, or expert tails, of <= 128 rows);
-// every wavefront computes 128 x 128 either way.
-template <int WM>
+// WM = 1 gives 128 x 512 tiles (for experts, or expert tails, of <= 128 rows).
+// NW wavefronts per workgroup: with 4, each computes 128 x 128 (one per
+// SIMD); with 8, each computes 128 x 64 and two share a SIMD, so that one can
+// issue MFMAs while the other waits on its loads or the barrier.
+template <int WM, int NW = 4>
 struct TileShape {
   static constexpr int BM = 128 * WM, BN = 512 / WM;
-  static constexpr int WN = 4 / WM;             // wavefronts along N
+  static constexpr int WN = NW / WM;            // wavefronts along N
+  static constexpr int WCOLS = BN / WN;         // columns per wavefront (128 or 64)
+  static constexpr int JT = WCOLS / 32;         // 32-column MFMA tiles per wavefront
   static constexpr int A_STAGE = BM * TBK * 2;  // BM rows x 64 B
   static constexpr int B_STAGE = TBK * BN * 2;  // 32 rows x 2*BN B
   static constexpr int STAGE = A_STAGE + B_STAGE;
   static constexpr int LDS = NSTAGE * STAGE;    // 128 KB / 160 KB (also the epilogue staging)
-  static constexpr int QA = BM / 64;            // 1 KB A loads per wavefront per K step
-  static constexpr int QB = BN / 64;            // 1 KB B loads per wavefront per K step
+  static constexpr int QA = BM / 16 / NW;       // 1 KB (16-row) A loads per wavefront per K step
+  static constexpr int QB = BN / 16 / NW;       // 1 KB B loads per wavefront per K step
   static constexpr int RPI = 512 / BN;          // B rows per load
+  static constexpr int ARW = BM / NW;           // A rows each wavefront loads
+  static constexpr int BRW = TBK / NW;          // B rows each wavefront loads
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -149,10 +155,11 @@ __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restri
 
 // One BM x BN output tile (rows m0.. of expert e, N tile nt) of the bf16
 // grouped GEMM; smem holds TileShape<WM>::LDS bytes of LDS.
-template <bool GATE_UP, int WM>
+template <bool GATE_UP, int WM, int NW = 4>
 __device__ __forceinline__ void tile_bf16_body(const StreamGemmArgs& a, uint8_t* smem, int e,
                                                int m0, int nt) {
-  using S = TileShape<WM>;
+  using S = TileShape<WM, NW>;
+  constexpr int JT = S::JT;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave / S::WN, wn = wave % S::WN;
   const int r0 = a.offsets[e];
@@ -169,25 +176,25 @@ __device__ __forceinline__ void tile_bf16_body(const StreamGemmArgs& a, uint8_t*
 
   // ---- global -> register loads. Rows past the expert's end and columns past
   // N read a clamped valid address: they only feed accumulators never stored.
-  // A: instruction q of this wave fills rows 64*wave + 16q .. +16 (1 KB); lane p
-  // holds physical granule p%4 of row 64*wave + 16q + p/4.
+  // A: instruction q of this wave fills rows ARW*wave + 16q .. +16 (1 KB); lane
+  // p holds physical granule p%4 of row ARW*wave + 16q + p/4.
   const uint16_t* asrc[S::QA];
 #pragma unroll
   for (int q = 0; q < S::QA; ++q) {
-    const int row = (S::BM / 4) * wave + 16 * q + (lane >> 2);
+    const int row = S::ARW * wave + 16 * q + (lane >> 2);
     const int lg = (lane & 3) ^ ((row >> 2) & 3);
     size_t grow = 0;
     if (m0 + row < cnt)
       grow = GATE_UP ? (size_t)(a.sorted_pair[r0 + m0 + row] / a.k) : (size_t)(r0 + m0 + row);
     asrc[q] = A + grow * lda + 8 * lg;
   }
-  // B: instruction q fills K rows 8*wave + 2q .. +2 (1 KB); lane p holds
-  // physical granule p%32 of row 8*wave + 2q + p/32.
+  // B: instruction q fills K rows BRW*wave + RPI*q .. +RPI (1 KB); lane p holds
+  // physical granule p%(64/RPI) of row BRW*wave + RPI*q + p/(64/RPI).
   const uint16_t* bsrc[S::QB];
   const uint16_t* wbase = W + (size_t)e * K * N;
 #pragma unroll
   for (int q = 0; q < S::QB; ++q) {
-    const int row = 8 * wave + S::RPI * q + lane / (64 / S::RPI);
+    const int row = S::BRW * wave + S::RPI * q + lane / (64 / S::RPI);
     const int lg = (lane % (64 / S::RPI)) ^ b_swz(row);
     int col;
     bool ok;
@@ -207,31 +214,32 @@ __device__ __forceinline__ void tile_bf16_body(const StreamGemmArgs& a, uint8_t*
     uint8_t* Bs = As + S::A_STAGE;
     const int k0 = kt * TBK;
 #pragma unroll
-    for (int q = 0; q < S::QA; ++q) dma16(asrc[q] + k0, As + ((S::BM / 4) * wave + 16 * q) * 64);
+    for (int q = 0; q < S::QA; ++q) dma16(asrc[q] + k0, As + (S::ARW * wave + 16 * q) * 64);
 #pragma unroll
     for (int q = 0; q < S::QB; ++q)
-      dma16(bsrc[q] + (size_t)k0 * N, Bs + (8 * wave + S::RPI * q) * (2 * S::BN));
+      dma16(bsrc[q] + (size_t)k0 * N, Bs + (S::BRW * wave + S::RPI * q) * (2 * S::BN));
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][JT];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JT; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // LDS column of this wave's 32-column tile j (gate/up: 2 gate tiles, then the
-  // 2 matching up tiles)
+  // LDS column of this wave's 32-column tile j (gate/up: JT/2 gate tiles, then
+  // the JT/2 matching up tiles)
   auto bcol = [&](int j) -> int {
-    if (GATE_UP) return (j < 2) ? 64 * wn + 32 * j : S::BN / 2 + 64 * wn + 32 * (j - 2);
-    return 128 * wn + 32 * j;
+    constexpr int HW = S::WCOLS / 2, HJ = JT / 2;
+    if (GATE_UP) return (j < HJ) ? HW * wn + 32 * j : S::BN / 2 + HW * wn + 32 * (j - HJ);
+    return S::WCOLS * wn + 32 * j;
   };
   const int l32 = lane & 31, kh = lane >> 5;  // MFMA row/column and K block
   const int tj = lane & 15, tg = lane >> 4;   // transpose-read lane and group
   const uint32_t lds0 = (uint32_t)(size_t)(lds_u8*)smem;
   // per-lane LDS byte offsets within a stage, for the two 16-deep K halves
-  uint32_t aoff[2][4], boff[2][4][2];
+  uint32_t aoff[2][4], boff[2][JT][2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
 #pragma unroll
@@ -240,7 +248,7 @@ __device__ __forceinline__ void tile_bf16_body(const StreamGemmArgs& a, uint8_t*
     // bcol + 16*(tg&1) + 4*(tj%4); the lane receives its column's 8 K values
     const int krow = 16 * s + 8 * (tg >> 1) + (tj >> 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < JT; ++j) {
       const int c = bcol(j) + 16 * (tg & 1) + 4 * (tj & 3);
       boff[s][j][0] = S::A_STAGE + krow * (2 * S::BN) + (((c >> 3) ^ b_swz(krow)) << 4) +
                       ((c & 7) << 1);
@@ -248,16 +256,17 @@ __device__ __forceinline__ void tile_bf16_body(const StreamGemmArgs& a, uint8_t*
                       (((c >> 3) ^ b_swz(krow + 4)) << 4) + ((c & 7) << 1);
     }
   }
-  // Fragments of one 16-deep K half: 4 A tiles and 4 B tiles (two transpose
-  // reads each). Reads are issued asynchronously; lgk_wait() publishes them.
+  // Fragments of one 16-deep K half: 4 A tiles and JT B tiles (two transpose
+  // reads each), 4 + 2 JT reads. Reads are issued asynchronously; the wait
+  // macros publish them.
   struct Frag {
     u32x4 a[4];
-    u32x2 lo[4], hi[4];
+    u32x2 lo[JT], hi[JT];
   };
   auto read_frag = [&](Frag& f, int st, int s) {
     const uint32_t base = lds0 + st * S::STAGE;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < JT; ++j) {
       f.lo[j] = lds_tr16(base + boff[s][j][0]);
       f.hi[j] = lds_tr16(base + boff[s][j][1]);
     }
@@ -266,16 +275,33 @@ __device__ __forceinline__ void tile_bf16_body(const StreamGemmArgs& a, uint8_t*
   };
   // Wait until at most `pending` LDS reads (those issued after f's) are
   // outstanding; f's registers are operands so nothing consumes them earlier.
-#define MOE_LGK_WAIT(f, pending)                                                              \
+#define MOE_LGK_WAIT4(f, pending)                                                             \
   asm volatile("s_waitcnt lgkmcnt(" #pending ")"                                              \
                : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.lo[0]),        \
                  "+v"(f.lo[1]), "+v"(f.lo[2]), "+v"(f.lo[3]), "+v"(f.hi[0]), "+v"(f.hi[1]),   \
                  "+v"(f.hi[2]), "+v"(f.hi[3])                                                  \
                :                                                                               \
                : "memory")
+#define MOE_LGK_WAIT2(f, pending)                                                             \
+  asm volatile("s_waitcnt lgkmcnt(" #pending ")"                                              \
+               : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.lo[0]),        \
+                 "+v"(f.lo[1]), "+v"(f.hi[0]), "+v"(f.hi[1])                                   \
+               :                                                                               \
+               : "memory")
+  // wait for f's reads while the next fragment's (4 + 2 JT reads) stay in flight
+#define MOE_LGK_WAIT_NEXT(f)   \
+  if constexpr (JT == 4)       \
+    MOE_LGK_WAIT4(f, 12);      \
+  else                         \
+    MOE_LGK_WAIT2(f, 8)
+#define MOE_LGK_WAIT_ALL(f)    \
+  if constexpr (JT == 4)       \
+    MOE_LGK_WAIT4(f, 0);       \
+  else                         \
+    MOE_LGK_WAIT2(f, 0)
   auto mfma_frag = [&](const Frag& f) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < JT; ++j) {
       const u32x4 b = u32x4{f.lo[j][0], f.lo[j][1], f.hi[j][0], f.hi[j][1]};
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i][j] = mfma32(f.a[i], b, acc[i][j]);
@@ -285,7 +311,7 @@ __device__ __forceinline__ void tile_bf16_body(const StreamGemmArgs& a, uint8_t*
   // never meet a control-flow merge, where copies could read them early):
   // every step issues one K step of loads (clamped to the last step near the
   // end, into the buffer of step kt-1, which is free), so "step kt+1 landed"
-  // is always vmcnt(8); the next half's fragments are always read, the extra
+  // is always vmcnt(QA + QB); the next half's fragments are always read, the extra
   // read after the last step is discarded. Within a step the second K half's
   // fragments are read while the first half's MFMAs run, and the next step's
   // first half is read (after the barrier that publishes that step's data and
@@ -295,30 +321,43 @@ __device__ __forceinline__ void tile_bf16_body(const StreamGemmArgs& a, uint8_t*
   issue(nk > 1 ? 1 : nk - 1, 1);
   issue(nk > 2 ? 2 : nk - 1, 2);
   // "step kt+1 landed" = at most two later steps (2 * (QA + QB) loads) in flight
-  if constexpr (WM == 2)
+  static_assert(S::QA + S::QB == 8 || S::QA + S::QB == 10 || S::QA + S::QB == 4 ||
+                    S::QA + S::QB == 5, "vmcnt literals below");
+  if constexpr (S::QA + S::QB == 8)
     asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else
+  else if constexpr (S::QA + S::QB == 10)
     asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+  else if constexpr (S::QA + S::QB == 4)
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   Frag f0, f1;
   read_frag(f0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     read_frag(f1, kt % NSTAGE, 1);
-    MOE_LGK_WAIT(f0, 12);
+    MOE_LGK_WAIT_NEXT(f0);
     mfma_frag(f0);
-    if constexpr (WM == 2)
+    if constexpr (S::QA + S::QB == 8)
       asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else
+    else if constexpr (S::QA + S::QB == 10)
       asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    else if constexpr (S::QA + S::QB == 4)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     issue(kt + 3 < nk ? kt + 3 : nk - 1, (kt + 3) % NSTAGE);
     read_frag(f0, (kt + 1) % NSTAGE, 0);
-    MOE_LGK_WAIT(f1, 12);
+    MOE_LGK_WAIT_NEXT(f1);
     mfma_frag(f1);
   }
-  MOE_LGK_WAIT(f0, 0);
+  MOE_LGK_WAIT_ALL(f0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#undef MOE_LGK_WAIT
+#undef MOE_LGK_WAIT4
+#undef MOE_LGK_WAIT2
+#undef MOE_LGK_WAIT_NEXT
+#undef MOE_LGK_WAIT_ALL
   __builtin_amdgcn_s_barrier();
 
   // ---- epilogue through LDS (the K loop ended with a barrier, so LDS is free):
@@ -327,24 +366,26 @@ __device__ __forceinline__ void tile_bf16_body(const StreamGemmArgs& a, uint8_t*
   // column l%32 of each 32x32 tile at rows 8*(r/4) + 4*(l/32) + r%4.
   auto tile_row = [&](int r) { return 8 * (r >> 2) + 4 * kh + (r & 3); };
   if (GATE_UP) {
-    uint16_t* strip = reinterpret_cast<uint16_t*>(smem + wave * 4096);  // 32 x 64 bf16
+    // SW h columns per wavefront (64 or 32), CPR 16-byte chunks per strip row
+    constexpr int SW = S::WCOLS / 2, HJ = JT / 2, CPR = SW / 8;
+    uint16_t* strip = reinterpret_cast<uint16_t*>(smem + wave * 4096);  // 32 x SW bf16
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < HJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          strip[tile_row(r) * 64 + 32 * j + l32] =
-              (uint16_t)f32_to_bf16_bits(silu(acc[i][j][r]) * acc[i][j + 2][r]);
+          strip[tile_row(r) * SW + 32 * j + l32] =
+              (uint16_t)f32_to_bf16_bits(silu(acc[i][j][r]) * acc[i][j + HJ][r]);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {  // 32 rows x 8 chunks of 16 B
-        const int c = lane + 64 * t, rr = c >> 3, ch = c & 7;
+      for (int t = 0; t < SW / 16; ++t) {  // 32 rows x CPR chunks of 16 B
+        const int c = lane + 64 * t, rr = c / CPR, ch = c % CPR;
         const int m = m0 + 128 * wm + 32 * i + rr;
-        const int col = nt * (S::BN / 2) + 64 * wn + 8 * ch;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(strip + rr * 64 + 8 * ch);
+        const int col = nt * (S::BN / 2) + SW * wn + 8 * ch;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(strip + rr * SW + 8 * ch);
         if (m < cnt && col < a.I)
           *reinterpret_cast<u32x4*>(a.h_out + (size_t)(r0 + m) * a.I + col) = v;
       }
@@ -353,22 +394,23 @@ __device__ __forceinline__ void tile_bf16_body(const StreamGemmArgs& a, uint8_t*
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   } else {
-    float* strip = reinterpret_cast<float*>(smem + wave * 16384);  // 32 x 128 fp32
+    constexpr int SW = S::WCOLS, CPR = SW / 4;  // fp32 columns, 16-byte chunks per row
+    float* strip = reinterpret_cast<float*>(smem + wave * (32 * SW * 4));  // 32 x SW fp32
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < JT; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) strip[tile_row(r) * 128 + 32 * j + l32] = acc[i][j][r];
+        for (int r = 0; r < 16; ++r) strip[tile_row(r) * SW + 32 * j + l32] = acc[i][j][r];
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {  // 32 rows x 32 chunks of 16 B
-        const int c = lane + 64 * t, rr = c >> 5, ch = c & 31;
+      for (int t = 0; t < SW / 8; ++t) {  // 32 rows x CPR chunks of 16 B
+        const int c = lane + 64 * t, rr = c / CPR, ch = c % CPR;
         const int m = m0 + 128 * wm + 32 * i + rr;
-        const int col = nt * S::BN + 128 * wn + 4 * ch;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(strip + rr * 128 + 4 * ch);
+        const int col = nt * S::BN + SW * wn + 4 * ch;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(strip + rr * SW + 4 * ch);
         if (m < cnt && col < N) {
           // expert rows stream out; split-K partials of the router are read back at once
           if (a.nsplit == 1)
@@ -416,10 +458,10 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_kernel(StreamGemmArgs a,
 // and the HBM-bound tiles of experts with few rows overlap the MFMA-bound
 // tiles of the others instead of running after them. Item: x = e | kind << 8
 // | nt << 9 (kind 1: 128 x 512 tile), y = first row.
-template <bool GATE_UP>
-__global__ __launch_bounds__(256, 1) void tile_bf16_mixed_kernel(StreamGemmArgs a,
-                                                                 const int2* __restrict__ items,
-                                                                 const int32_t* __restrict__ n_items_p) {
+template <bool GATE_UP, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void tile_bf16_mixed_kernel(StreamGemmArgs a,
+                                                                     const int2* __restrict__ items,
+                                                                     const int32_t* __restrict__ n_items_p) {
   static_assert(TileShape<1>::LDS >= TileShape<2>::LDS, "LDS sized for the larger tile");
   __shared__ __align__(1024) uint8_t smem[TileShape<1>::LDS];
   const int w = xcd_item(*n_items_p);
@@ -427,11 +469,14 @@ __global__ __launch_bounds__(256, 1) void tile_bf16_mixed_kernel(StreamGemmArgs 
   const int2 it = items[w];
   const int e = it.x & 0xff, nt = it.x >> 9;
   if (it.x & 0x100)
-    tile_bf16_body<GATE_UP, 1>(a, smem, e, it.y, nt);
+    tile_bf16_body<GATE_UP, 1, NW>(a, smem, e, it.y, nt);
   else
-    tile_bf16_body<GATE_UP, 2>(a, smem, e, it.y, nt);
+    tile_bf16_body<GATE_UP, 2, NW>(a, smem, e, it.y, nt);
 }
 
+#ifndef MOE_TILE_GM
+#define MOE_TILE_GM 4
+#endif
 // Work lists of the mixed launch, one per blockIdx.y (gate/up, down). Expert e
 // with c rows has c / 256 full tiles, plus one more if c % 256 > 128, else one
 // 128-row tile if c % 256 > 0; a full tile spans ntf N tiles, a 128-row tile
@@ -478,8 +523,13 @@ __global__ __launch_bounds__(256) void tile_items_kernel(const int32_t* __restri
   const int fcount = nfull[x] * ntf;
   int2 it;
   if (local < fcount) {
-    const int mt = local / ntf;
-    it.x = x | ((local - mt * ntf) << 9);
+    // groups of GM full M tiles; inside a group N tile major, so the items
+    // one XCD runs at a time span GM M tiles and a few N tiles
+    const int grp = local / (MOE_TILE_GM * ntf), in = local - grp * (MOE_TILE_GM * ntf);
+    const int rest = nfull[x] - grp * MOE_TILE_GM;
+    const int gm = rest < MOE_TILE_GM ? rest : MOE_TILE_GM;
+    const int ntile = in / gm, mt = grp * MOE_TILE_GM + (in - ntile * gm);
+    it.x = x | (ntile << 9);
     it.y = mt * 256;
   } else {
     it.x = x | 0x100 | ((local - fcount) << 9);
@@ -1340,6 +1390,13 @@ __global__ __launch_bounds__(256) void router_pack_kernel(const float* __restric
 
 constexpr int ROUTER_NKS = 2;  // K slices per plane (3 * 2 splits in all)
 
+// Wavefronts per workgroup of the mixed launch (4: 128 x 128 per wavefront,
+// 8: 128 x 64, two per SIMD).
+#ifndef MOE_MIXED_WAVES
+#define MOE_MIXED_WAVES 8
+#endif
+constexpr int kMixedWaves = MOE_MIXED_WAVES;
+
 // Tile counts of the mixed launch: N tiles of a full (256 x 256) tile and of a
 // 128-row (128 x 512) tile, and the largest work list.
 struct MixedPlan {
@@ -1443,12 +1500,12 @@ static hipError_t launch_bf16_all(const StreamGemmArgs& gu, const StreamGemmArgs
       gu.offsets, gu.E, pg.ntf, pg.nth, items_g, counts, pd.ntf, pd.nth, items_d, counts + 1);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  tile_bf16_mixed_kernel<true><<<(unsigned)((pg.max_items + 7) / 8 * 8), 256, 0, st>>>(gu, items_g,
-                                                                                      counts);
+  tile_bf16_mixed_kernel<true, kMixedWaves><<<(unsigned)((pg.max_items + 7) / 8 * 8),
+                                               64 * kMixedWaves, 0, st>>>(gu, items_g, counts);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  tile_bf16_mixed_kernel<false><<<(unsigned)((pd.max_items + 7) / 8 * 8), 256, 0, st>>>(
-      dn, items_d, counts + 1);
+  tile_bf16_mixed_kernel<false, kMixedWaves><<<(unsigned)((pd.max_items + 7) / 8 * 8),
+                                                64 * kMixedWaves, 0, st>>>(dn, items_d, counts + 1);
   return hipGetLastError();
 }
 
