@@ -155,7 +155,8 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return (uint64_t)__ockl_wfred_max_u64((unsigned long long)v);
 }
 
-// One workgroup per token; wavefront w owns experts 64w .. 64w+63, one per
+// Small batches (T < 1024, where the router GEMM splits K up to 32 ways):
+// one workgroup per token; wavefront w owns experts 64w .. 64w+63, one per
 // lane, and adds that expert's split partials (loaded 32 at a time),
 // the bias, and rounds to the logits dtype. The selection key packs
 // (order-preserving logit, 0xFFFF - id), so a maximum picks the largest logit
@@ -163,7 +164,7 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 // keys (eight wavefront-wide maxima); wavefront 0 merges the 32 candidates
 // into the token's top k.
 template <bool BF16_LOGITS>
-__global__ __launch_bounds__(256) void router_select_kernel(
+__global__ __launch_bounds__(256) void router_select_wg_kernel(
     const float* __restrict__ part, int n_split, int ldp, int T, int E, int k,
     const float* __restrict__ bias, void* __restrict__ logits, float* __restrict__ logits_f32,
     int32_t* __restrict__ ids, float* __restrict__ w) {
@@ -235,6 +236,93 @@ __global__ __launch_bounds__(256) void router_select_kernel(
   }
 }
 
+// Large batches: one wavefront per token, four tokens per workgroup. Lane l owns experts
+// l, l + 64, l + 128 and l + 192 (coalesced rows), adds each one's split
+// partials in split order (loaded SB splits at a time, one memory latency per
+// batch; SB covers the split count up to 32), the bias, and rounds to the
+// logits dtype. The selection key packs
+// (order-preserving logit, 0xFFFF - id), so a maximum picks the largest logit
+// and, on equal logits, the lowest id; keys are distinct. Each of the k
+// rounds takes every lane's largest remaining key, their wavefront maximum
+// (DPP), and clears it in the lane that holds it: no LDS, no barrier.
+template <bool BF16_LOGITS, int SB>
+__global__ __launch_bounds__(256) void router_select_kernel(
+    const float* __restrict__ part, int n_split, int ldp, int T, int E, int k,
+    const float* __restrict__ bias, void* __restrict__ logits, float* __restrict__ logits_f32,
+    int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // wave-uniform
+  const float* p = part + (size_t)t * ldp;
+  const size_t sstride = (size_t)T * ldp;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int sp0 = 0; sp0 < n_split; sp0 += SB) {
+    float u[4][SB];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+        if (lane + 64 * q < E && sp0 + j < n_split) u[q][j] = p[(size_t)(sp0 + j) * sstride + lane + 64 * q];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < SB; ++j)
+        if (lane + 64 * q < E && sp0 + j < n_split) v[q] += u[q][j];
+  }
+  uint64_t key[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane + 64 * q;
+    key[q] = 0;
+    if (e < E) {
+      float x = v[q];
+      if (bias) x += bias[e];
+      if (logits_f32) logits_f32[(size_t)t * E + e] = x;
+      float sv = x;
+      if constexpr (BF16_LOGITS) {
+        const uint32_t b = f32_to_bf16_bits(x);
+        static_cast<uint16_t*>(logits)[(size_t)t * E + e] = (uint16_t)b;
+        sv = bf16_bits_to_f32(b);
+      } else {
+        static_cast<float*>(logits)[(size_t)t * E + e] = x;
+      }
+      key[q] = ((uint64_t)float_order_key(sv) << 32) | (uint32_t)(0xFFFF - e);
+    }
+  }
+  float topv[8];
+  int topi[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    topv[j] = 0.f;
+    topi[j] = 0;
+    if (j < k) {
+      const uint64_t m01 = key[0] > key[1] ? key[0] : key[1];
+      const uint64_t m23 = key[2] > key[3] ? key[2] : key[3];
+      const uint64_t best = wave_max_u64(m01 > m23 ? m01 : m23);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (key[q] == best) key[q] = 0;
+      topi[j] = 0xFFFF - (int)(best & 0xFFFFu);
+      topv[j] = float_from_order_key((uint32_t)(best >> 32));
+    }
+  }
+  if (lane == 0) {
+    // softmax over all E, restricted to the chosen set: the normaliser cancels
+    float pr[8], z = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pr[j] = (j < k) ? expf(topv[j] - topv[0]) : 0.f;
+      z += pr[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < k) {
+        ids[(size_t)t * k + j] = topi[j];
+        w[(size_t)t * k + j] = pr[j] / z;
+      }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_router_gemm(const void* x, bool x_bf16, int T, int H, const float* w_router,
@@ -250,12 +338,30 @@ hipError_t launch_router_gemm(const void* x, bool x_bf16, int T, int H, const fl
 hipError_t launch_router_select(const float* part, int n_split, int ldp, int T, int E, int k,
                                 const float* bias, bool logits_bf16, void* logits,
                                 float* logits_f32, int32_t* ids, float* w, hipStream_t st) {
-  if (logits_bf16)
-    router_select_kernel<true><<<T, 256, 0, st>>>(part, n_split, ldp, T, E, k, bias, logits,
-                                                  logits_f32, ids, w);
+  if (T < 1024) {  // one workgroup per token: 4x the load parallelism per token
+    if (logits_bf16)
+      router_select_wg_kernel<true><<<T, 256, 0, st>>>(part, n_split, ldp, T, E, k, bias, logits,
+                                                       logits_f32, ids, w);
+    else
+      router_select_wg_kernel<false><<<T, 256, 0, st>>>(part, n_split, ldp, T, E, k, bias, logits,
+                                                        logits_f32, ids, w);
+    return hipGetLastError();
+  }
+  const unsigned grid = (unsigned)((T + 3) / 4);  // one wavefront per token
+#define MOE_SELECT(SB)                                                                         \
+  (logits_bf16 ? (router_select_kernel<true, SB><<<grid, 256, 0, st>>>(                         \
+                      part, n_split, ldp, T, E, k, bias, logits, logits_f32, ids, w),          \
+                  0)                                                                           \
+               : (router_select_kernel<false, SB><<<grid, 256, 0, st>>>(                        \
+                      part, n_split, ldp, T, E, k, bias, logits, logits_f32, ids, w),          \
+                  0))
+  if (n_split <= 8)
+    MOE_SELECT(8);
+  else if (n_split <= 16)
+    MOE_SELECT(16);
   else
-    router_select_kernel<false><<<T, 256, 0, st>>>(part, n_split, ldp, T, E, k, bias, logits,
-                                                   logits_f32, ids, w);
+    MOE_SELECT(32);
+#undef MOE_SELECT
   return hipGetLastError();
 }
 
