@@ -6,25 +6,29 @@
 // Beam serving...", section "Agents worked on the serving path"), scheduled
 // for the dense-contraction regime, where the budget that matters is LDS
 // bandwidth per MFMA:
-//  - one workgroup (4 wavefronts, 2 x 2) computes a 256 x 256 output tile of
-//    one expert; each wavefront owns 128 x 128 (4 x 4 MFMA 32x32x16 tiles,
-//    256 fp32 accumulators), the largest tile whose accumulators fit, which
-//    halves LDS reads per MFMA against a 64 x 128 wave tile. The 32x32x16
-//    bf16 MFMA issues at twice the rate of the 16x16x32 one on gfx950;
+//  - one workgroup computes a 256 x 256 output tile of one expert on MFMA
+//    32x32x16 (twice the issue rate of 16x16x32 on gfx950). The expert
+//    launch runs 8 wavefronts (2 x 4), each owning 128 x 64 (4 x 2 MFMA
+//    tiles, 128 fp32 accumulators), two per SIMD; the router's split-bf16
+//    GEMM runs 4 wavefronts (2 x 2) of 128 x 128 (256 accumulators, one per
+//    SIMD), which halves LDS reads per MFMA. Both measured the same: under
+//    sustained MFMA load the chip runs at ~1.55 GHz, and the down GEMM also
+//    pays for its fp32 output rows;
 //  - an expert's last partial tile of at most 128 rows runs instead as a
-//    128 x 512 tile (1 x 4 wavefronts, same 128 x 128 per wavefront): with
-//    skewed routing most experts hold a few hundred rows, and padding their
-//    tails to 256 rows wasted about a quarter of the MFMA work. The wider
-//    tile keeps the weight bytes per MAC unchanged. Both shapes run in one
-//    launch from a work list in expert order, so the weight-bound tiles of
-//    experts with few rows overlap the MFMA-bound tiles of the others, and
-//    an expert's tail tile finds its weights still cached;
+//    128 x 512 tile (1 x 8 wavefronts, same per-wavefront tile):
+//    with skewed routing most experts hold a few hundred rows, and padding
+//    their tails to 256 rows wasted about a quarter of the MFMA work. The
+//    wider tile keeps the weight bytes per MAC unchanged. Both shapes run in
+//    one launch from a work list in expert order (groups of 4 M tiles, N tile
+//    major inside a group, for L2 reuse), so the weight-bound tiles of
+//    experts with few rows overlap the MFMA-bound tiles of the others, and an
+//    expert's tail tile finds its weights still cached.
 //    Quantised weights use the 128 x 512 tile throughout (their in-register
 //    conversion, not the MFMA, is the bound, and it is done once per column);
 //  - K advances 32 per step through four LDS stages filled by direct
 //    global->LDS loads (16 B per lane; no registers stage the tiles), issued
-//    three steps ahead of the MFMAs: with one wavefront per SIMD nothing else
-//    hides a load that misses L2, so the pipeline depth has to;
+//    three steps ahead of the MFMAs, so that a load that misses L2 is hidden
+//    by the pipeline depth;
 //  - the fragment reads are issued as inline ds_read instructions with
 //    explicit waits: the compiler would otherwise wait for every
 //    outstanding global->LDS load before any LDS read it can see;
@@ -37,8 +41,8 @@
 //  - for gate/up the tile holds BN/2 gate and the matching BN/2 up columns,
 //    so each lane forms silu(gate) * up from two of its own accumulators;
 //  - the epilogue goes through LDS so output rows leave in 16-byte stores;
-//  - workgroups map onto (M tile, N tile) so that consecutive work items,
-//    which share A rows and B panels, run on the same XCD (and its L2).
+//  - workgroups map onto work items so that consecutive items, which share
+//    A rows and B panels, run on the same XCD (and its L2).
 #include "moe_internal.h"
 
 namespace moe {

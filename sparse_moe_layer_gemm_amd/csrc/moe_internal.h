@@ -158,7 +158,8 @@ size_t stream_ws_bytes(long long P, int E, int H, int I, int wfmt);
 // Grouped expert GEMMs for many rows per expert: bf16 weights on 256 x 256
 // tiles (plus 128 x 512 tiles for each expert's last <= 128 rows), quantised
 // weights on 128 x 512 tiles, MFMAs fed through a four-stage LDS pipeline.
-// Runs gate/up then down; ws holds the M-tile tables (expert_tile_ws_bytes).
+// Runs gate/up then down; ws holds the tile tables and work lists
+// (expert_tile_ws_bytes).
 size_t expert_tile_ws_bytes(int P, int E, int H, int I);
 // fp8-MFMA mode of the quantised experts (x and h quantised in-kernel; the
 // gate/up output h in gate_up.h_out is bf16 scratch of the same size as usual).
