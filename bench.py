@@ -81,6 +81,11 @@ class Workload:
         self.pp = torch.empty(P, dtype=torch.int32, device="cuda")
         self.y = torch.empty((P, H), dtype=torch.float32, device="cuda")
         self.ews = moe.workspace(moe.moe_experts_workspace_size(T, H, I, E, k, self.w))
+        # compact expert rows where the library supports them: moe_forward then
+        # runs those kernels, so the stage timing does too
+        self.y16 = torch.empty((P, H), dtype=torch.int16, device="cuda")
+        self.ysc = torch.empty((P, H // 64), dtype=torch.uint8, device="cuda")
+        self.rows16 = True
         # finalize fused with the sandwich norms (timed beside the plain finalize)
         self.res = torch.randn((T, H), generator=torch.Generator("cuda").manual_seed(cfg.seed),
                                device="cuda").to(dt)
@@ -100,9 +105,13 @@ class Workload:
                                           None, self.ids, self.tw, self.rws)),
             ("permute", lambda: m.moe_permute(self.ids, c.E, self.counts, self.offsets, self.sp,
                                               self.pp)),
-            ("experts", lambda: m.moe_experts(self.x, c.I, c.E, c.k, self.offsets, self.sp, self.w,
-                                              self.y, self.ews)),
-            ("finalize", lambda: m.moe_finalize(self.y, self.pp, self.tw, self.out)),
+            ("experts", lambda: m.moe_experts_rows16(self.x, c.I, c.E, c.k, self.offsets, self.sp,
+                                                     self.w, self.y16, self.ysc, self.ews)
+             if self.rows16 else m.moe_experts(self.x, c.I, c.E, c.k, self.offsets, self.sp,
+                                               self.w, self.y, self.ews)),
+            ("finalize", lambda: m.moe_finalize_rows16(self.y16, self.ysc, self.pp, self.tw,
+                                                       self.out)
+             if self.rows16 else m.moe_finalize(self.y, self.pp, self.tw, self.out)),
             # not part of the step: the fused finalize + norms on the same rows
             ("finalize_norm", lambda: m.moe_finalize_norm(self.y, self.pp, self.tw, self.res,
                                                           self.gamma, self.gamma, 1e-6,
@@ -125,9 +134,20 @@ class Workload:
     def time_stages(self, steps):
         """Per-stage average durations (ms) from events recorded between the stage
         calls on the stream the kernels run on."""
-        torch = self.torch
+        torch, c, m = self.torch, self.cfg, self.moe
         calls = self.stage_calls()
-        for _, f in calls:
+        calls[0][1]()
+        calls[1][1]()
+        try:  # compact rows unless the library does not support them here
+            calls[2][1]()
+        except m.MoEError as err:
+            if err.status != 2:
+                raise
+            self.rows16 = False
+            del self.y16, self.ysc
+        if self.rows16:  # fp32 rows for the fused finalize + norms timing
+            m.moe_experts(self.x, c.I, c.E, c.k, self.offsets, self.sp, self.w, self.y, self.ews)
+        for _, f in calls[2:]:
             f()
         torch.cuda.synchronize()
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
@@ -279,6 +299,7 @@ def main():
             "ms_per_step": pre_ms,
             "stages_ms": pre_stage,
             "expert_load": {"max": int(pc.max()), "median": float(np.median(pc)), "min": int(pc.min())},
+            "expert_rows": "fp16, power-of-two scale per 64 columns" if pre.rows16 else "fp32",
             "layer_mfma_frac": (flops + router_flops) / (pre_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
             "roofline": {"bound": "mfma", "kernel": "moe_experts (gate/up + down grouped GEMMs)",
                          "achieved": flops / (pre_stage["experts"] / 1e3) / 1e12,

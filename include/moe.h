@@ -151,6 +151,33 @@ moe_status moe_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
                        const moe_expert_weights* w, float* y_sorted, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------ compact expert rows
+ * Steps 4 and 5 with the expert rows kept compact: the same y_sorted rows,
+ * stored as fp16 values with one power-of-two scale per row and 64-column
+ * block, y_sorted[r, c] = y16[r, c] * 2^(y16_scale[r, c / 64] - 127). The
+ * scale puts each block's largest magnitude into [2^14, 2^15) before the fp16
+ * rounding (nearest even; it may round up to 2^15), so no finite row overflows;
+ * each value keeps 11 significant bits relative to its block maximum, finer
+ * than the error bf16 h already puts in the rows. This halves the traffic of the largest intermediate at prefill
+ * sizes, where writing fp32 rows bounds the down GEMM; moe_forward uses these
+ * two calls whenever moe_experts_rows16 supports the call.
+ * moe_experts_rows16: as moe_experts, writing y16 [T*k, H] (uint16 fp16 bits)
+ * and y16_scale [T*k, H/64] (uint8) instead of y_sorted; supported for bf16
+ * expert weights (qmode W) when the experts average at least 32 rows
+ * (T*k >= 32*E: the tiled kernels), else MOE_ERR_UNSUPPORTED. Same workspace
+ * as moe_experts.
+ * moe_finalize_rows16: as moe_finalize, reading the compact rows; each value
+ * is decoded exactly to fp32 and summed as moe_finalize sums. */
+moe_status moe_experts_rows16(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I,
+                              int32_t E, int32_t k, const int32_t* offsets,
+                              const int32_t* sorted_pair, const moe_expert_weights* w,
+                              uint16_t* y16, uint8_t* y16_scale, void* workspace,
+                              size_t workspace_bytes, void* stream);
+moe_status moe_finalize_rows16(const uint16_t* y16, const uint8_t* y16_scale,
+                               const int32_t* pair_pos, const float* topk_w, int64_t T, int32_t k,
+                               int32_t H, int32_t out_dtype, void* out, float* out_f32,
+                               void* stream);
+
 /* ------------------------------------------------------------ finalize
  * MoE finalize (step 5), the weighted un-permute:
  *   out[t] = sum_{j=0..k-1} topk_w[t, j] * y_sorted[pair_pos[t*k + j]]
@@ -182,7 +209,8 @@ moe_status moe_finalize_norm(const float* y_sorted, const int32_t* pair_pos, con
                              void* residual_out, void* normed, void* stream);
 
 /* ------------------------------------------------------------ whole layer
- * The five steps in order on one stream: route, permute, experts, finalize.
+ * The five steps in order on one stream: route, permute, experts, finalize
+ * (with compact expert rows where moe_experts_rows16 supports the call).
  * out [T, H] out_dtype; out_f32, logits, topk_ids, topk_w are optional
  * (NULL: kept in the workspace). logits_dtype as for moe_route. */
 size_t moe_forward_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,

@@ -26,8 +26,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
 
 ENTRY_POINTS = ("moe_status_string", "moe_route_workspace_size", "moe_route",
                 "moe_permute_workspace_size", "moe_permute", "moe_experts_workspace_size",
-                "moe_experts", "moe_finalize", "moe_finalize_norm", "moe_forward_workspace_size",
-                "moe_forward")
+                "moe_experts", "moe_experts_rows16", "moe_finalize", "moe_finalize_rows16",
+                "moe_finalize_norm", "moe_forward_workspace_size", "moe_forward")
 
 
 class MoEError(RuntimeError):
@@ -67,6 +67,9 @@ def load_library(path: str = LIB_PATH):
         "moe_experts": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp,
                                ctypes.POINTER(CExpertWeights), _vp, _vp, _sz, _vp]),
         "moe_finalize": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
+        "moe_experts_rows16": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp,
+                                      ctypes.POINTER(CExpertWeights), _vp, _vp, _vp, _sz, _vp]),
+        "moe_finalize_rows16": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
         "moe_finalize_norm": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, ctypes.c_float,
                                      _vp, _vp, _vp]),
         "moe_forward_workspace_size": (_sz, [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(CExpertWeights)]),
@@ -174,6 +177,33 @@ def moe_experts(x, I: int, E: int, k: int, offsets, sorted_pair, w: ExpertWeight
         _ptr(x), _dt(x), T, H, I, E, k, _ptr(offsets), _ptr(sorted_pair), ctypes.byref(s),
         _ptr(y_sorted), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+def moe_experts_rows16(x, I: int, E: int, k: int, offsets, sorted_pair, w: ExpertWeights, y16,
+                       y16_scale, workspace, stream=None):
+    """y16 [T*k, H] int16/uint16 (fp16 bits), y16_scale [T*k, H/64] uint8."""
+    T, H = x.shape
+    s = w.c_struct()
+    _check("moe_experts_rows16", _lib.moe_experts_rows16(
+        _ptr(x), _dt(x), T, H, I, E, k, _ptr(offsets), _ptr(sorted_pair), ctypes.byref(s),
+        _ptr(y16), _ptr(y16_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def moe_finalize_rows16(y16, y16_scale, pair_pos, topk_w, out, out_f32=None, stream=None):
+    T, k = topk_w.shape
+    H = y16.shape[1]
+    _check("moe_finalize_rows16", _lib.moe_finalize_rows16(
+        _ptr(y16), _ptr(y16_scale), _ptr(pair_pos), _ptr(topk_w), T, k, H, _dt(out), _ptr(out),
+        _ptr(out_f32), _stream(stream)))
+
+
+def rows16_decode(y16, y16_scale):
+    """Compact rows -> fp32 rows (torch ops on the tensors given; a test and
+    benchmark helper, not part of the layer's path)."""
+    v = y16.view(torch.float16).float()
+    e = y16_scale.to(torch.int32) - 127
+    return torch.ldexp(v, e.repeat_interleave(64, dim=1).float())
 
 
 def moe_finalize(y_sorted, pair_pos, topk_w, out, out_f32=None, stream=None):

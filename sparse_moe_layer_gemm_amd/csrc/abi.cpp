@@ -140,6 +140,12 @@ bool use_tile_kernel(int32_t w_dtype, int64_t P, int32_t E) {
   return w_dtype != MOE_F32 && P >= (int64_t)moe::kTileMinRowsPerExpert * E;
 }
 
+// Compact expert rows (fp16 + power-of-two scale per 64 columns) are written
+// by the tiled bf16 kernels only.
+bool rows16_supported(const moe_expert_weights* w, int64_t P, int32_t E) {
+  return w->dtype == MOE_BF16 && w->qmode == MOE_QMODE_W && use_tile_kernel(w->dtype, P, E);
+}
+
 // -------------------------------------------------------------- enqueue helpers
 // (arguments already validated, T > 0)
 moe_status enqueue_route(const void* x, int32_t x_dtype, int64_t T, int32_t H, const float* wr,
@@ -178,7 +184,8 @@ moe_status enqueue_route(const void* x, int32_t x_dtype, int64_t T, int32_t H, c
 moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I,
                            int32_t E, int32_t k, const int32_t* offsets,
                            const int32_t* sorted_pair, const moe_expert_weights* w,
-                           float* y_sorted, void* ws, hipStream_t st) {
+                           float* y_sorted, void* ws, hipStream_t st, uint16_t* y16 = nullptr,
+                           uint8_t* y16_scale = nullptr) {
   const int P = (int)(T * k);
   if (w->dtype == MOE_F32) {
     return launch_status(moe::launch_expert_f32(
@@ -216,6 +223,8 @@ moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H,
   d.w_gscale = w->down_gscale;
   d.h_out = nullptr;
   d.y_out = y_sorted;
+  d.y16 = y16;  // compact rows (tiled bf16 path only; the caller checked)
+  d.y16_scale = y16_scale;
   if (f8_mode(w)) {
     // the fp8-MFMA mode always runs the tiled kernels
     char* f8ws = static_cast<char*>(tile_ws) + align_up(moe::expert_tile_ws_bytes(P, E, H, I));
@@ -346,6 +355,46 @@ moe_status moe_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
                          static_cast<hipStream_t>(stream));
 }
 
+moe_status moe_experts_rows16(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I,
+                              int32_t E, int32_t k, const int32_t* offsets,
+                              const int32_t* sorted_pair, const moe_expert_weights* w,
+                              uint16_t* y16, uint8_t* y16_scale, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  moe_status s = check_shape(T, H, E, k);
+  if (s != MOE_OK) return s;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  s = check_weights(w, x_dtype, H, I);
+  if (s != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  if (!rows16_supported(w, T * k, E)) return MOE_ERR_UNSUPPORTED;
+  if (!x || !offsets || !sorted_pair || !y16 || !y16_scale || !workspace)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(offsets) || !aligned16(sorted_pair) || !aligned16(y16) ||
+      !aligned16(y16_scale) || !aligned16(workspace))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < experts_ws_bytes(T, H, I, E, k, w)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return enqueue_experts(x, x_dtype, T, H, I, E, k, offsets, sorted_pair, w, nullptr, workspace,
+                         static_cast<hipStream_t>(stream), y16, y16_scale);
+}
+
+moe_status moe_finalize_rows16(const uint16_t* y16, const uint8_t* y16_scale,
+                               const int32_t* pair_pos, const float* topk_w, int64_t T, int32_t k,
+                               int32_t H, int32_t out_dtype, void* out, float* out_f32,
+                               void* stream) {
+  if (T < 0 || k <= 0 || H <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  if (k > 8 || H % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (T * k > kMaxPairs || T >= kMaxTokens) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!y16 || !y16_scale || !pair_pos || !topk_w || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(y16) || !aligned16(y16_scale) || !aligned16(pair_pos) || !aligned16(topk_w) ||
+      !aligned16(out) || !ok_or_null(out_f32))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return launch_status(moe::launch_finalize_rows16(y16, y16_scale, pair_pos, topk_w, (int)T, k, H,
+                                                   out_dtype == MOE_BF16, out, out_f32,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 // ---------------------------------------------------------------- finalize
 moe_status moe_finalize(const float* y_sorted, const int32_t* pair_pos, const float* topk_w,
                         int64_t T, int32_t k, int32_t H, int32_t out_dtype, void* out,
@@ -446,6 +495,16 @@ moe_status moe_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
   s = launch_status(
       moe::launch_permute(ids, (int)P, E, counts, offsets, sorted_pair, pair_pos, perm_ws, st));
   if (s != MOE_OK) return s;
+  if (rows16_supported(w, (int64_t)P, E)) {
+    // compact rows in the fp32 rows' space: P*H*2 + P*H/64 bytes
+    uint16_t* y16 = reinterpret_cast<uint16_t*>(y_sorted);
+    uint8_t* y16_scale = reinterpret_cast<uint8_t*>(y16 + align_up(P * H * sizeof(uint16_t)) / 2);
+    s = enqueue_experts(x, x_dtype, T, H, I, E, k, offsets, sorted_pair, w, nullptr, exp_ws, st,
+                        y16, y16_scale);
+    if (s != MOE_OK) return s;
+    return launch_status(moe::launch_finalize_rows16(y16, y16_scale, pair_pos, tw, (int)T, k, H,
+                                                     out_dtype == MOE_BF16, out, out_f32, st));
+  }
   s = enqueue_experts(x, x_dtype, T, H, I, E, k, offsets, sorted_pair, w, y_sorted, exp_ws, st);
   if (s != MOE_OK) return s;
   return launch_status(moe::launch_finalize(y_sorted, pair_pos, tw, (int)T, k, H,

@@ -114,6 +114,15 @@ __device__ __forceinline__ int a_off(int row, int g) { return row * 64 + ((g ^ (
 // granule index with 4 * (row % 4) puts those 8 reads in distinct banks.
 __device__ __forceinline__ int b_swz(int row) { return (row & 3) << 2; }
 
+// Maximum over each aligned group of 8 lanes, in every lane of the group
+// (DPP: swap neighbours, swap pairs, then mirror within the half row).
+__device__ __forceinline__ float max8_lanes(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  return v;
+}
+
 // M-tile tables, in expert order: tiles of bm rows per expert; with `split`, an
 // expert's last partial tile of at most bm/2 rows goes to a second table of
 // half-height tiles instead.
@@ -392,6 +401,48 @@ __device__ __forceinline__ void tile_bf16_body(const StreamGemmArgs& a, uint8_t*
         const u32x4 v = *reinterpret_cast<const u32x4*>(strip + rr * SW + 8 * ch);
         if (m < cnt && col < a.I)
           *reinterpret_cast<u32x4*>(a.h_out + (size_t)(r0 + m) * a.I + col) = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  } else if (S::WCOLS == 64 && a.y16 != nullptr) {
+    // compact rows: this wavefront's strip row is exactly one 64-column scale
+    // block. The fp32 results go through LDS as for fp32 rows; then 8 lanes
+    // hold a row's 8 chunks of 8 values, so the block maximum is 3 DPP steps
+    float* strip = reinterpret_cast<float*>(smem + wave * 8192);  // 32 x 64 fp32
+    const int nb = N / 64;
+    const int blk = (nt * S::BN + 64 * wn) / 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < JT; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) strip[tile_row(r) * 64 + 32 * j + l32] = acc[i][j][r];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {  // 32 rows x 8 chunks of 8 values
+        const int c = lane + 64 * t, rr = c >> 3, ch = c & 7;
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(strip + rr * 64 + 8 * ch);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(strip + rr * 64 + 8 * ch + 4);
+        float mx = fmaxf(fmaxf(fmaxf(fabsf(v0[0]), fabsf(v0[1])), fmaxf(fabsf(v0[2]), fabsf(v0[3]))),
+                         fmaxf(fmaxf(fabsf(v1[0]), fabsf(v1[1])), fmaxf(fabsf(v1[2]), fabsf(v1[3]))));
+        mx = max8_lanes(mx);
+        const int sx = rows16_exp(mx);
+        const float inv = __builtin_ldexpf(1.0f, -sx);
+        u32x4 pk;
+        pk[0] = f32_to_f16_bits(v0[0] * inv) | (f32_to_f16_bits(v0[1] * inv) << 16);
+        pk[1] = f32_to_f16_bits(v0[2] * inv) | (f32_to_f16_bits(v0[3] * inv) << 16);
+        pk[2] = f32_to_f16_bits(v1[0] * inv) | (f32_to_f16_bits(v1[1] * inv) << 16);
+        pk[3] = f32_to_f16_bits(v1[2] * inv) | (f32_to_f16_bits(v1[3] * inv) << 16);
+        const int m = m0 + 128 * wm + 32 * i + rr;
+        const int col = nt * S::BN + 64 * wn + 8 * ch;
+        if (m < cnt && col < N) {
+          __builtin_nontemporal_store(pk, reinterpret_cast<u32x4*>(a.y16 + (size_t)(r0 + m) * N + col));
+          if (ch == 0) a.y16_scale[(size_t)(r0 + m) * nb + blk] = (uint8_t)(sx + 127);
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();

@@ -59,7 +59,73 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
   }
 }
 
+// The same over compact rows: fp16 values with one power-of-two scale byte
+// per row and 64-column block; each value is decoded exactly to fp32
+// (fp16 -> fp32, times 2^(b - 127)) and summed as above.
+template <bool BF16_OUT>
+__global__ __launch_bounds__(256) void finalize_rows16_kernel(
+    const uint16_t* __restrict__ y16, const uint8_t* __restrict__ ysc,
+    const int32_t* __restrict__ pair_pos, const float* __restrict__ w, int k, int H, int n_chunks,
+    long long n_items, void* __restrict__ out, float* __restrict__ out_f32) {
+  const int nb = H / 64;
+  for (long long item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const long long t = item / n_chunks;
+    const int c = (int)(item - t * n_chunks) * FCOLS + threadIdx.x * 4;
+    int pos[8];
+    float wt[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pos[j] = pair_pos[t * k + (j < k ? j : 0)];
+      wt[j] = (j < k) ? w[t * k + j] : 0.f;
+    }
+    if (c >= H) continue;
+    typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+    u32x2v v[8];
+    uint32_t sb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x2v*>(y16 + (size_t)pos[j] * H + c));
+      sb[j] = ysc[(size_t)pos[j] * nb + (c >> 6)];
+    }
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < k) {
+        const int e = (int)sb[j] - 127;
+        acc.x = fmaf(wt[j], __builtin_ldexpf(f16_bits_to_f32(v[j].x & 0xffffu), e), acc.x);
+        acc.y = fmaf(wt[j], __builtin_ldexpf(f16_bits_to_f32(v[j].x >> 16), e), acc.y);
+        acc.z = fmaf(wt[j], __builtin_ldexpf(f16_bits_to_f32(v[j].y & 0xffffu), e), acc.z);
+        acc.w = fmaf(wt[j], __builtin_ldexpf(f16_bits_to_f32(v[j].y >> 16), e), acc.w);
+      }
+    }
+    if (out_f32) *reinterpret_cast<float4*>(out_f32 + (size_t)t * H + c) = acc;
+    if constexpr (BF16_OUT) {
+      uint2 pk;
+      pk.x = f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16);
+      pk.y = f32_to_bf16_bits(acc.z) | (f32_to_bf16_bits(acc.w) << 16);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (size_t)t * H + c) = pk;
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)t * H + c) = acc;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_finalize_rows16(const uint16_t* y16, const uint8_t* y16_scale,
+                                  const int32_t* pair_pos, const float* w, int T, int k, int H,
+                                  bool out_bf16, void* out, float* out_f32, hipStream_t st) {
+  const int n_chunks = (H + FCOLS - 1) / FCOLS;
+  const long long items = (long long)T * n_chunks;
+  const unsigned grid = (unsigned)(items < (1 << 20) ? items : (1 << 20));
+  if (out_bf16)
+    finalize_rows16_kernel<true><<<grid, 256, 0, st>>>(y16, y16_scale, pair_pos, w, k, H, n_chunks,
+                                                       items, out, out_f32);
+  else
+    finalize_rows16_kernel<false><<<grid, 256, 0, st>>>(y16, y16_scale, pair_pos, w, k, H,
+                                                        n_chunks, items, out, out_f32);
+  return hipGetLastError();
+}
 
 hipError_t launch_finalize(const float* y_sorted, const int32_t* pair_pos, const float* w, int T,
                            int k, int H, bool out_bf16, void* out, float* out_f32,

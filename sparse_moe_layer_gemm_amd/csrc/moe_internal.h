@@ -30,6 +30,22 @@ __device__ __forceinline__ float float_from_order_key(uint32_t k) {
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Compact expert rows: the power-of-two exponent s that puts a block maximum
+// m > 0 into [2^14, 2^15) after scaling by 2^-s (so fp16 rounding cannot
+// overflow), clamped to the E8M0 byte range; 0 for an all-zero block.
+__device__ __forceinline__ int rows16_exp(float m) {
+  if (!(m > 0.f)) return 0;
+  const int e = __builtin_amdgcn_frexp_expf(m);  // m = f * 2^e, f in [0.5, 1)
+  const int s = e - 1 - 14;
+  return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {  // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
 // Stores of the fp32 expert rows: written once and read once by the finalize
 // step, long after, so they skip cache retention (nontemporal). Measured on
 // gfx950 at decode sizes, this halves what the row stores add to the weight
@@ -106,6 +122,11 @@ struct StreamGemmArgs {
   const float* w_gscale;   // FP4: f32 [E]
   uint16_t* h_out;         // gate/up output [P, I] bf16
   float* y_out;            // down output [P, N] f32
+  // Compact down output instead of y_out (tiled kernel, 8 wavefronts): fp16
+  // rows [P, N] with one power-of-two scale byte (2^(b - 127)) per row and
+  // 64-column block [P, N / 64]; the block maximum is scaled into [2^14, 2^15).
+  uint16_t* y16 = nullptr;
+  uint8_t* y16_scale = nullptr;
   // Split-K over blockIdx.y (tiled kernel, down mode only): split s reads the
   // K slice (s % nk_split) of length K from A (row stride lda) and from weight
   // plane (s / nk_split), and writes partial sums to y_out + s * y_split_stride.
@@ -188,6 +209,11 @@ hipError_t launch_expert_f32(const float* x, int T, int H, int I, int E, int k, 
 hipError_t launch_finalize(const float* y_sorted, const int32_t* pair_pos, const float* w, int T,
                            int k, int H, bool out_bf16, void* out, float* out_f32,
                            hipStream_t st);
+// Weighted un-permute of compact rows (fp16 + per-64-column power-of-two
+// scales), otherwise as launch_finalize.
+hipError_t launch_finalize_rows16(const uint16_t* y16, const uint8_t* y16_scale,
+                                  const int32_t* pair_pos, const float* w, int T, int k, int H,
+                                  bool out_bf16, void* out, float* out_f32, hipStream_t st);
 // Weighted un-permute + RMS post-norm + residual add + next RMS pre-norm
 // (bf16 residual and norm weights); H <= 16384.
 hipError_t launch_finalize_norm(const float* y_sorted, const int32_t* pair_pos, const float* w,

@@ -119,13 +119,27 @@ class Layer:
         r["sorted_pair"] = torch.empty(P, dtype=torch.int32, device=DEV)
         r["pair_pos"] = torch.empty(P, dtype=torch.int32, device=DEV)
         moe.moe_permute(r["ids"], E, r["counts"], r["offsets"], r["sorted_pair"], r["pair_pos"])
-        r["y"] = torch.empty((P, H), dtype=torch.float32, device=DEV)
         ws = moe.workspace(moe.moe_experts_workspace_size(T, H, I, E, k, self.dw))
-        moe.moe_experts(self.dx, I, E, k, r["offsets"], r["sorted_pair"], self.dw, r["y"], ws)
         r["experts_ws"] = ws
         r["out"] = torch.empty((T, H), dtype=self.dx.dtype, device=DEV)
         r["out_f32"] = torch.empty((T, H), dtype=torch.float32, device=DEV)
-        moe.moe_finalize(r["y"], r["pair_pos"], r["w"], r["out"], r["out_f32"])
+        # compact expert rows wherever the library supports them (as moe_forward
+        # does); the checks then see the exactly decoded fp32 rows
+        y16 = torch.empty((P, H), dtype=torch.int16, device=DEV)
+        ysc = torch.empty((P, H // 64), dtype=torch.uint8, device=DEV)
+        try:
+            moe.moe_experts_rows16(self.dx, I, E, k, r["offsets"], r["sorted_pair"], self.dw, y16,
+                                   ysc, ws)
+            r["y16"], r["y16_scale"] = y16, ysc
+            r["y"] = moe.rows16_decode(y16, ysc)
+            moe.moe_finalize_rows16(y16, ysc, r["pair_pos"], r["w"], r["out"], r["out_f32"])
+        except moe.MoEError as err:
+            if err.status != 2:  # MOE_ERR_UNSUPPORTED: the fp32 rows
+                raise
+            del y16, ysc
+            r["y"] = torch.empty((P, H), dtype=torch.float32, device=DEV)
+            moe.moe_experts(self.dx, I, E, k, r["offsets"], r["sorted_pair"], self.dw, r["y"], ws)
+            moe.moe_finalize(r["y"], r["pair_pos"], r["w"], r["out"], r["out_f32"])
         torch.cuda.synchronize()
         return r
 

@@ -24,7 +24,7 @@ MIS = A + 4  # misaligned
 
 def header_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_entry_point():
@@ -161,6 +161,40 @@ def test_finalize_validation():
     assert finalize(out_dt=2) == INVAL
     assert finalize(out=None) == INVAL
     assert finalize(out_f32=MIS) == INVAL
+
+
+def experts_rows16(w=None, **kw):
+    w = w if w is not None else _w()
+    a = dict(x=A, x_dt=1, T=16384, H=5120, I=1536, E=256, k=8, off=B, sp=C, w=ctypes.byref(w),
+             y16=D, ysc=F, ws=G, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return moe.load_library().moe_experts_rows16(*a.values())
+
+
+def test_experts_rows16_validation():
+    assert experts_rows16(T=0, x=None, off=None, sp=None, y16=None, ysc=None, ws=None) == OK
+    assert experts_rows16(T=128) == UNSUP  # 4 rows per expert: the streaming kernels
+    assert experts_rows16(w=_w(dtype=2, gus=G, dns=Hh)) == UNSUP  # FP8 weights
+    assert experts_rows16(ysc=None) == INVAL
+    assert experts_rows16(y16=MIS) == INVAL
+    assert experts_rows16(ws_bytes=1024) == WS_SMALL
+    assert experts_rows16(k=9) == UNSUP
+
+
+def finalize_rows16(**kw):
+    a = dict(y16=A, ysc=B, pp=C, w=D, T=128, k=8, H=5120, out_dt=1, out=F, out_f32=None,
+             stream=None)
+    a.update(kw)
+    return moe.load_library().moe_finalize_rows16(*a.values())
+
+
+def test_finalize_rows16_validation():
+    assert finalize_rows16(T=0, y16=None, ysc=None, pp=None, w=None, out=None) == OK
+    assert finalize_rows16(k=9) == UNSUP
+    assert finalize_rows16(H=100) == UNSUP
+    assert finalize_rows16(out_dt=2) == INVAL
+    assert finalize_rows16(ysc=None) == INVAL
+    assert finalize_rows16(out_f32=MIS) == INVAL
 
 
 def finalize_norm(**kw):
