@@ -123,32 +123,22 @@ __device__ __forceinline__ float max8_lanes(float v) {
   return v;
 }
 
-// M-tile tables, in expert order: tiles of bm rows per expert; with `split`, an
-// expert's last partial tile of at most bm/2 rows goes to a second table of
-// half-height tiles instead.
+// M-tile table, in expert order: ceil(rows / bm) tiles of bm rows per expert.
 __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restrict__ offsets,
-                                                         int E, int bm, int split,
+                                                         int E, int bm,
                                                          int32_t* __restrict__ tile_e,
                                                          int32_t* __restrict__ tile_m0,
-                                                         int32_t* __restrict__ n_tiles,
-                                                         int32_t* __restrict__ half_e,
-                                                         int32_t* __restrict__ half_m0,
-                                                         int32_t* __restrict__ n_half) {
-  __shared__ int cnt[256], hcnt[256];
+                                                         int32_t* __restrict__ n_tiles) {
+  __shared__ int cnt[256];
   const int e = threadIdx.x;
   const int rows = (e < E) ? offsets[e + 1] - offsets[e] : 0;
-  const int rem = rows % bm;
-  const int h = (split && rem > 0 && rem <= bm / 2) ? 1 : 0;
-  const int c = rows / bm + ((rem > 0 && !h) ? 1 : 0);
+  const int c = (rows + bm - 1) / bm;
   cnt[e] = c;
-  hcnt[e] = h;
   __syncthreads();
-  for (int d = 1; d < 256; d <<= 1) {  // inclusive scans
+  for (int d = 1; d < 256; d <<= 1) {  // inclusive scan
     const int v = (e >= d) ? cnt[e - d] : 0;
-    const int vh = (e >= d) ? hcnt[e - d] : 0;
     __syncthreads();
     cnt[e] += v;
-    hcnt[e] += vh;
     __syncthreads();
   }
   const int base = cnt[e] - c;
@@ -156,14 +146,7 @@ __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restri
     tile_e[base + j] = e;
     tile_m0[base + j] = j * bm;
   }
-  if (h) {
-    half_e[hcnt[e] - 1] = e;
-    half_m0[hcnt[e] - 1] = (rows / bm) * bm;
-  }
-  if (e == 255) {
-    *n_tiles = cnt[255];
-    if (split) *n_half = hcnt[255];
-  }
+  if (e == 255) *n_tiles = cnt[255];
 }
 
 // One BM x BN output tile (rows m0.. of expert e, N tile nt) of the bf16
@@ -1497,8 +1480,7 @@ hipError_t launch_router_bf16x3(const uint16_t* x, int T, int H, const float* w_
                                                                               offsets, T);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  tile_table_kernel<<<1, 256, 0, st>>>(offsets, 1, TBM, 0, tile_e, tile_m0, n_tiles, nullptr,
-                                       nullptr, nullptr);
+  tile_table_kernel<<<1, 256, 0, st>>>(offsets, 1, TBM, tile_e, tile_m0, n_tiles);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   StreamGemmArgs a{};
@@ -1519,18 +1501,6 @@ hipError_t launch_router_bf16x3(const uint16_t* x, int T, int H, const float* w_
   a.y_split_stride = (long long)T * 256;
   const unsigned grid = (unsigned)(((max_tiles + 7) / 8) * 8);
   tile_bf16_kernel<false, 2><<<dim3(grid, a.nsplit), 256, 0, st>>>(a, tile_e, tile_m0, n_tiles, 1);
-  return hipGetLastError();
-}
-
-template <bool GATE_UP, int WM>
-static hipError_t launch_tiles(const StreamGemmArgs& g, const int32_t* te, const int32_t* tm,
-                               const int32_t* nt_p, int max_tiles, hipStream_t st) {
-  using S = TileShape<WM>;
-  const int NT = GATE_UP ? (g.I + S::BN / 2 - 1) / (S::BN / 2) : (g.N + S::BN - 1) / S::BN;
-  const long long items = (long long)max_tiles * NT;
-  const unsigned grid = (unsigned)(((items + 7) / 8) * 8);
-  if (grid == 0) return hipSuccess;
-  tile_bf16_kernel<GATE_UP, WM><<<grid, 256, 0, st>>>(g, te, tm, nt_p, NT);
   return hipGetLastError();
 }
 
@@ -1614,8 +1584,7 @@ hipError_t launch_expert_f8(int wfmt, const StreamGemmArgs& gu, const StreamGemm
   int32_t* tile_e = static_cast<int32_t*>(ws);
   int32_t* tile_m0 = tile_e + max_tiles;
   int32_t* counts = tile_m0 + max_tiles;
-  tile_table_kernel<<<1, 256, 0, st>>>(gu.offsets, E, 128, 0, tile_e, tile_m0, counts, nullptr,
-                                       nullptr, nullptr);
+  tile_table_kernel<<<1, 256, 0, st>>>(gu.offsets, E, 128, tile_e, tile_m0, counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (wfmt == W_FP8)
@@ -1632,8 +1601,7 @@ hipError_t launch_expert_tile(int wfmt, const StreamGemmArgs& gu, const StreamGe
     const int max_tiles = (P + 127) / 128 + E;
     int32_t* tile_m0 = tile_e + max_tiles;
     int32_t* counts = tile_m0 + max_tiles;
-    tile_table_kernel<<<1, 256, 0, st>>>(gu.offsets, E, 128, 0, tile_e, tile_m0, counts, nullptr,
-                                         nullptr, nullptr);
+    tile_table_kernel<<<1, 256, 0, st>>>(gu.offsets, E, 128, tile_e, tile_m0, counts);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (wfmt == W_FP8) return launch_q_all<W_FP8>(gu, dn, tile_e, tile_m0, counts, max_tiles, st);
