@@ -198,14 +198,6 @@ def moe_finalize_rows16(y16, y16_scale, pair_pos, topk_w, out, out_f32=None, str
         _ptr(out_f32), _stream(stream)))
 
 
-def rows16_decode(y16, y16_scale):
-    """Compact rows -> fp32 rows (torch ops on the tensors given; a test and
-    benchmark helper, not part of the layer's path)."""
-    v = y16.view(torch.float16).float()
-    e = y16_scale.to(torch.int32) - 127
-    return torch.ldexp(v, e.repeat_interleave(64, dim=1).float())
-
-
 def moe_finalize(y_sorted, pair_pos, topk_w, out, out_f32=None, stream=None):
     T, k = topk_w.shape
     H = y_sorted.shape[1]

@@ -1428,12 +1428,12 @@ __global__ __launch_bounds__(256) void router_pack_kernel(const float* __restric
 
 constexpr int ROUTER_NKS = 2;  // K slices per plane (3 * 2 splits in all)
 
-// Wavefronts per workgroup of the mixed launch (4: 128 x 128 per wavefront,
-// 8: 128 x 64, two per SIMD).
-#ifndef MOE_MIXED_WAVES
-#define MOE_MIXED_WAVES 8
-#endif
-constexpr int kMixedWaves = MOE_MIXED_WAVES;
+// Wavefronts per workgroup of the mixed launch: 8 (128 x 64 each, two per
+// SIMD). The compact-row epilogue needs each wavefront's strip to be one
+// 64-column scale block.
+constexpr int kMixedWaves = 8;
+static_assert(TileShape<2, kMixedWaves>::WCOLS == 64 && TileShape<1, kMixedWaves>::WCOLS == 64,
+              "compact rows take one 64-column block per wavefront strip");
 
 // Tile counts of the mixed launch: N tiles of a full (256 x 256) tile and of a
 // 128-row (128 x 512) tile, and the largest work list.

@@ -131,7 +131,7 @@ class Layer:
             moe.moe_experts_rows16(self.dx, I, E, k, r["offsets"], r["sorted_pair"], self.dw, y16,
                                    ysc, ws)
             r["y16"], r["y16_scale"] = y16, ysc
-            r["y"] = moe.rows16_decode(y16, ysc)
+            r["y"] = rows16_decode(y16, ysc)
             moe.moe_finalize_rows16(y16, ysc, r["pair_pos"], r["w"], r["out"], r["out_f32"])
         except moe.MoEError as err:
             if err.status != 2:  # MOE_ERR_UNSUPPORTED: the fp32 rows
@@ -155,6 +155,14 @@ class Layer:
                         out_f32=f["out_f32"], topk_ids=f["ids"], topk_w=f["w"])
         torch.cuda.synchronize()
         return f
+
+
+def rows16_decode(y16: torch.Tensor, y16_scale: torch.Tensor) -> torch.Tensor:
+    """Compact expert rows -> fp32 rows: fp16 value times 2^(scale byte - 127),
+    one scale per row and 64-column block (exact in fp32)."""
+    v = y16.view(torch.float16).float()
+    e = y16_scale.to(torch.int32) - 127
+    return torch.ldexp(v, e.repeat_interleave(64, dim=1).float())
 
 
 # ------------------------------------------------------------------ comparisons
