@@ -235,12 +235,19 @@ def cpu_baseline(wl, budget_s=10.0):
     dt = time.perf_counter() - t
     n2 = int(min(c.T, max(n, n * budget_s / max(dt, 1e-3))))
     rows = np.linspace(0, c.T - 1, n2).astype(np.int64)
+    # whole passes over the sample until about budget_s of oracle work has run
     t = time.perf_counter()
-    oracle.layer(wl.x_host, wl.wr_host, wl.bias_host, wl.w_host, c.I, c.k, "bf16", rows=rows)
-    dt = time.perf_counter() - t
+    passes = 0
+    while True:
+        oracle.layer(wl.x_host, wl.wr_host, wl.bias_host, wl.w_host, c.I, c.k, "bf16", rows=rows)
+        passes += 1
+        dt = time.perf_counter() - t
+        if dt >= budget_s or passes >= 50:
+            break
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(n2 / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n2} of the {c.T} {c.name} tokens (whole layer per token, fp64), {dt:.1f} s"}
+    return {"value": round(passes * n2 / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{passes} pass(es) over {n2} of the {c.T} {c.name} tokens (whole layer per "
+                      f"token, fp64), {dt:.1f} s"}
 
 
 def main():
