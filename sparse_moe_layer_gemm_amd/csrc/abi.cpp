@@ -140,6 +140,16 @@ bool use_tile_kernel(int32_t w_dtype, int64_t P, int32_t E) {
   return w_dtype != MOE_F32 && P >= (int64_t)moe::kTileMinRowsPerExpert * E;
 }
 
+// Sizes whose tiled work lists would overflow int indexing are unsupported.
+moe_status check_tile_plan(const moe_expert_weights* w, int64_t T, int32_t k, int32_t E, int32_t H,
+                           int32_t I) {
+  const int64_t P = T * k;
+  if ((use_tile_kernel(w->dtype, P, E) || w->qmode == MOE_QMODE_F8) &&
+      !moe::expert_tile_fits(P, E, H, I))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 // Compact expert rows (fp16 + power-of-two scale per 64 columns) are written
 // by the tiled bf16 kernels only.
 bool rows16_supported(const moe_expert_weights* w, int64_t P, int32_t E) {
@@ -345,6 +355,8 @@ moe_status moe_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
   s = check_weights(w, x_dtype, H, I);
   if (s != MOE_OK) return s;
+  s = check_tile_plan(w, T, k, E, H, I);
+  if (s != MOE_OK) return s;
   if (T == 0) return MOE_OK;
   if (!x || !offsets || !sorted_pair || !y_sorted || !workspace) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(x) || !aligned16(offsets) || !aligned16(sorted_pair) || !aligned16(y_sorted) ||
@@ -364,6 +376,8 @@ moe_status moe_experts_rows16(const void* x, int32_t x_dtype, int64_t T, int32_t
   if (s != MOE_OK) return s;
   if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
   s = check_weights(w, x_dtype, H, I);
+  if (s != MOE_OK) return s;
+  s = check_tile_plan(w, T, k, E, H, I);
   if (s != MOE_OK) return s;
   if (T == 0) return MOE_OK;
   if (!rows16_supported(w, T * k, E)) return MOE_ERR_UNSUPPORTED;
@@ -461,6 +475,8 @@ moe_status moe_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
   if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
   if (logits_dtype == MOE_F32 && x_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
   s = check_weights(w, x_dtype, H, I);
+  if (s != MOE_OK) return s;
+  s = check_tile_plan(w, T, k, E, H, I);
   if (s != MOE_OK) return s;
   if (T == 0) return MOE_OK;
   if (!x || !w_router || !out || !workspace) return MOE_ERR_INVALID_ARGUMENT;

@@ -1450,6 +1450,14 @@ MixedPlan mixed_plan(bool gate_up, int P, int E, int N, int I) {
 
 }  // namespace
 
+bool expert_tile_fits(long long P, int E, int H, int I) {
+  // the work lists of the mixed launches are indexed with int
+  const long long full = (P + TBM - 1) / TBM + E;
+  const long long g = full * ((I + 127) / 128) + (long long)E * ((I + 255) / 256);
+  const long long d = full * (((long long)H + 255) / 256) + (long long)E * (((long long)H + 511) / 512);
+  return g < (1LL << 30) && d < (1LL << 30);
+}
+
 size_t expert_tile_ws_bytes(int P, int E, int H, int I) {
   // the larger of: the table of 128-row tiles (quantised weights), and the
   // counters plus the two work lists of the mixed bf16 launches

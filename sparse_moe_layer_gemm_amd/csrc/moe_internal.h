@@ -182,6 +182,8 @@ size_t stream_ws_bytes(long long P, int E, int H, int I, int wfmt);
 // Runs gate/up then down; ws holds the tile tables and work lists
 // (expert_tile_ws_bytes).
 size_t expert_tile_ws_bytes(int P, int E, int H, int I);
+// whether the tiled path's work lists stay within int indexing
+bool expert_tile_fits(long long P, int E, int H, int I);
 // fp8-MFMA mode of the quantised experts (x and h quantised in-kernel; the
 // gate/up output h in gate_up.h_out is bf16 scratch of the same size as usual).
 hipError_t launch_expert_f8(int wfmt, const StreamGemmArgs& gate_up, const StreamGemmArgs& down,

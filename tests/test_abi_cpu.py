@@ -188,6 +188,12 @@ def finalize_rows16(**kw):
     return moe.load_library().moe_finalize_rows16(*a.values())
 
 
+def test_tiled_work_lists_that_overflow_are_unsupported():
+    # H = 2^30: the down GEMM's work list would pass 2^30 items
+    assert experts_rows16(H=1 << 30) == UNSUP
+    assert experts(H=1 << 30, T=16384) == UNSUP
+
+
 def test_finalize_rows16_validation():
     assert finalize_rows16(T=0, y16=None, ysc=None, pp=None, w=None, out=None) == OK
     assert finalize_rows16(k=9) == UNSUP
