@@ -170,6 +170,8 @@ class Workload:
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_t128_moe_experts_hbm_traffic.md")
 STREAM_SRC = os.path.join(ROOT, "sparse_moe_layer_gemm_amd", "csrc", "expert_stream.hip")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_t16384_zipf_moe_experts_hbm_traffic.md")
+TILE_SRC = os.path.join(ROOT, "sparse_moe_layer_gemm_amd", "csrc", "expert_tile.hip")
 
 
 def source_sha256(path):
@@ -178,15 +180,15 @@ def source_sha256(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per moe_experts launch at decode, from the committed rocprofv3 counter
+def measured_traffic(path=TRAFFIC_FILE, src=STREAM_SRC):
+    """HBM bytes per expert stage (moe_experts launch), from a committed rocprofv3 counter
     summary, or None when it is missing or the kernel source changed since."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             for line in f:
                 if line.startswith("TRAFFIC_JSON:"):
                     d = json.loads(line.split(":", 1)[1])
-                    if d.get("source_sha256") == source_sha256(STREAM_SRC):
+                    if d.get("source_sha256") == source_sha256(src):
                         return d["hbm_bytes_per_launch"]
     except (OSError, ValueError, KeyError):
         pass
@@ -310,7 +312,9 @@ def main():
             "layer_mfma_frac": (flops + router_flops) / (pre_ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
             "roofline": {"bound": "mfma", "kernel": "moe_experts (gate/up + down grouped GEMMs)",
                          "achieved": flops / (pre_stage["experts"] / 1e3) / 1e12,
-                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "traffic": None},
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "traffic": measured_traffic(PREFILL_TRAFFIC_FILE, TILE_SRC)
+                         if pre.rows16 else None},
         }
         pre_line["roofline"]["frac"] = pre_line["roofline"]["achieved"] / BF16_PEAK_TFLOPS
 
