@@ -151,9 +151,10 @@ moe_status check_tile_plan(const moe_expert_weights* w, int64_t T, int32_t k, in
 }
 
 // Compact expert rows (fp16 + power-of-two scale per 64 columns) are written
-// by the tiled bf16 kernels only.
+// by the tiled kernels of bf16 weights and of exactly dequantised FP8 / NVFP4
+// weights (not the fp8-MFMA mode).
 bool rows16_supported(const moe_expert_weights* w, int64_t P, int32_t E) {
-  return w->dtype == MOE_BF16 && w->qmode == MOE_QMODE_W && use_tile_kernel(w->dtype, P, E);
+  return w->dtype != MOE_F32 && w->qmode == MOE_QMODE_W && use_tile_kernel(w->dtype, P, E);
 }
 
 // -------------------------------------------------------------- enqueue helpers
@@ -233,7 +234,7 @@ moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H,
   d.w_gscale = w->down_gscale;
   d.h_out = nullptr;
   d.y_out = y_sorted;
-  d.y16 = y16;  // compact rows (tiled bf16 path only; the caller checked)
+  d.y16 = y16;  // compact rows (tiled paths, qmode W; the caller checked)
   d.y16_scale = y16_scale;
   if (f8_mode(w)) {
     // the fp8-MFMA mode always runs the tiled kernels

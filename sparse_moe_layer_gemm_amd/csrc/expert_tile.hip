@@ -890,6 +890,7 @@ __global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
 #pragma unroll
     for (int j = 0; j < 4; ++j) sd[j] = WF == W_FP8 ? chs[mcol(bcol(j) + l32)] : gsc;
     float* strip = reinterpret_cast<float*>(smem + wave * 16384);  // 32 x 128 fp32
+    const bool compact = a.y16 != nullptr;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -899,6 +900,37 @@ __global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (compact) {
+        // compact rows: a strip row holds two 64-column scale blocks; 8
+        // adjacent lanes hold one block's 8 chunks of 8 values
+        const int nb = N / 64;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {  // 32 rows x 16 chunks
+          const int c = lane + 64 * t, rr = c >> 4, ch = c & 15;
+          const f32x4 v0 = *reinterpret_cast<const f32x4*>(strip + rr * 128 + 8 * ch);
+          const f32x4 v1 = *reinterpret_cast<const f32x4*>(strip + rr * 128 + 8 * ch + 4);
+          float mx = fmaxf(fmaxf(fmaxf(fabsf(v0[0]), fabsf(v0[1])), fmaxf(fabsf(v0[2]), fabsf(v0[3]))),
+                           fmaxf(fmaxf(fabsf(v1[0]), fabsf(v1[1])), fmaxf(fabsf(v1[2]), fabsf(v1[3]))));
+          mx = max8_lanes(mx);
+          const int sx = rows16_exp(mx);
+          const float inv = __builtin_ldexpf(1.0f, -sx);
+          u32x4 pk;
+          pk[0] = f32_to_f16_bits(v0[0] * inv) | (f32_to_f16_bits(v0[1] * inv) << 16);
+          pk[1] = f32_to_f16_bits(v0[2] * inv) | (f32_to_f16_bits(v0[3] * inv) << 16);
+          pk[2] = f32_to_f16_bits(v1[0] * inv) | (f32_to_f16_bits(v1[1] * inv) << 16);
+          pk[3] = f32_to_f16_bits(v1[2] * inv) | (f32_to_f16_bits(v1[3] * inv) << 16);
+          const int m = m0 + 128 * wm + 32 * i + rr;
+          const int col = nt * S::BN + 128 * wn + 8 * ch;
+          if (m < cnt && col < N) {
+            __builtin_nontemporal_store(pk, reinterpret_cast<u32x4*>(a.y16 + (size_t)(r0 + m) * N + col));
+            if ((ch & 7) == 0) a.y16_scale[(size_t)(r0 + m) * nb + col / 64] = (uint8_t)(sx + 127);
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        continue;
+      }
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
         const int c = lane + 64 * t, rr = c >> 5, ch = c & 31;

@@ -25,6 +25,8 @@ CASES = [
     MC("r16_ragged", 131, T=150, H=192, E=4, k=2, I=192),       # partial N tiles, 3 blocks per row
     MC("r16_zipf", 132, T=512, H=256, E=16, k=4, I=128, zipf_s=1.1),
     MC("r16_wide", 133, T=700, H=1088, E=8, k=3, I=256),        # a 128 x 512 tail tile per expert
+    MC("r16_fp4", 135, T=300, H=512, E=16, k=4, I=256, w_dtype="fp4"),   # quantised tiles
+    MC("r16_fp8", 136, T=300, H=576, E=16, k=4, I=192, w_dtype="fp8"),   # 9 blocks per row
 ]
 
 
