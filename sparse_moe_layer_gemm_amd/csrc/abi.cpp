@@ -151,10 +151,10 @@ moe_status check_tile_plan(const moe_expert_weights* w, int64_t T, int32_t k, in
 }
 
 // Compact expert rows (fp16 + power-of-two scale per 64 columns) are written
-// by the tiled kernels of bf16 weights and of exactly dequantised FP8 / NVFP4
-// weights (not the fp8-MFMA mode).
+// by the tiled kernels: bf16, FP8 and NVFP4 weights with many rows per expert,
+// and the fp8-MFMA mode (always tiled).
 bool rows16_supported(const moe_expert_weights* w, int64_t P, int32_t E) {
-  return w->dtype != MOE_F32 && w->qmode == MOE_QMODE_W && use_tile_kernel(w->dtype, P, E);
+  return w->dtype != MOE_F32 && (w->qmode == MOE_QMODE_F8 || use_tile_kernel(w->dtype, P, E));
 }
 
 // -------------------------------------------------------------- enqueue helpers
@@ -234,7 +234,7 @@ moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H,
   d.w_gscale = w->down_gscale;
   d.h_out = nullptr;
   d.y_out = y_sorted;
-  d.y16 = y16;  // compact rows (tiled paths, qmode W; the caller checked)
+  d.y16 = y16;  // compact rows (tiled paths; the caller checked)
   d.y16_scale = y16_scale;
   if (f8_mode(w)) {
     // the fp8-MFMA mode always runs the tiled kernels

@@ -123,6 +123,42 @@ __device__ __forceinline__ float max8_lanes(float v) {
   return v;
 }
 
+// Compact rows from a wavefront's LDS strip of 32 rows x SW fp32 columns
+// (SW = 64 or 128: one or two 64-column scale blocks per row), the strip's
+// row rr being output row row0 + rr and its column 0 output column col0. Eight
+// adjacent lanes hold one block's 8 chunks of 8 values, so the block maximum
+// is three DPP steps; each chunk leaves as one 16-byte store of fp16 values,
+// each block's scale as one byte.
+template <int SW>
+__device__ __forceinline__ void store_rows16(const float* strip, int lane, int row0, int cnt,
+                                             int col0, int N, size_t r0, uint16_t* __restrict__ y16,
+                                             uint8_t* __restrict__ y16_scale) {
+  constexpr int CPR = SW / 8;  // 8-value chunks per strip row
+  const int nb = N / 64;
+#pragma unroll
+  for (int t = 0; t < SW / 16; ++t) {  // 32 rows x CPR chunks over 64 lanes
+    const int c = lane + 64 * t, rr = c / CPR, ch = c % CPR;
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(strip + rr * SW + 8 * ch);
+    const f32x4 v1 = *reinterpret_cast<const f32x4*>(strip + rr * SW + 8 * ch + 4);
+    float mx = fmaxf(fmaxf(fmaxf(fabsf(v0[0]), fabsf(v0[1])), fmaxf(fabsf(v0[2]), fabsf(v0[3]))),
+                     fmaxf(fmaxf(fabsf(v1[0]), fabsf(v1[1])), fmaxf(fabsf(v1[2]), fabsf(v1[3]))));
+    mx = max8_lanes(mx);
+    const int sx = rows16_exp(mx);
+    const float inv = __builtin_ldexpf(1.0f, -sx);
+    u32x4 pk;
+    pk[0] = f32_to_f16_bits(v0[0] * inv) | (f32_to_f16_bits(v0[1] * inv) << 16);
+    pk[1] = f32_to_f16_bits(v0[2] * inv) | (f32_to_f16_bits(v0[3] * inv) << 16);
+    pk[2] = f32_to_f16_bits(v1[0] * inv) | (f32_to_f16_bits(v1[1] * inv) << 16);
+    pk[3] = f32_to_f16_bits(v1[2] * inv) | (f32_to_f16_bits(v1[3] * inv) << 16);
+    const int m = row0 + rr;
+    const int col = col0 + 8 * ch;
+    if (m < cnt && col < N) {
+      __builtin_nontemporal_store(pk, reinterpret_cast<u32x4*>(y16 + (r0 + m) * (size_t)N + col));
+      if ((ch & 7) == 0) y16_scale[(r0 + m) * (size_t)nb + col / 64] = (uint8_t)(sx + 127);
+    }
+  }
+}
+
 // M-tile table, in expert order: ceil(rows / bm) tiles of bm rows per expert.
 __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restrict__ offsets,
                                                          int E, int bm,
@@ -391,11 +427,8 @@ __device__ __forceinline__ void tile_bf16_body(const StreamGemmArgs& a, uint8_t*
     }
   } else if (S::WCOLS == 64 && a.y16 != nullptr) {
     // compact rows: this wavefront's strip row is exactly one 64-column scale
-    // block. The fp32 results go through LDS as for fp32 rows; then 8 lanes
-    // hold a row's 8 chunks of 8 values, so the block maximum is 3 DPP steps
+    // block; the fp32 results go through LDS as for fp32 rows
     float* strip = reinterpret_cast<float*>(smem + wave * 8192);  // 32 x 64 fp32
-    const int nb = N / 64;
-    const int blk = (nt * S::BN + 64 * wn) / 64;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -405,28 +438,8 @@ __device__ __forceinline__ void tile_bf16_body(const StreamGemmArgs& a, uint8_t*
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {  // 32 rows x 8 chunks of 8 values
-        const int c = lane + 64 * t, rr = c >> 3, ch = c & 7;
-        const f32x4 v0 = *reinterpret_cast<const f32x4*>(strip + rr * 64 + 8 * ch);
-        const f32x4 v1 = *reinterpret_cast<const f32x4*>(strip + rr * 64 + 8 * ch + 4);
-        float mx = fmaxf(fmaxf(fmaxf(fabsf(v0[0]), fabsf(v0[1])), fmaxf(fabsf(v0[2]), fabsf(v0[3]))),
-                         fmaxf(fmaxf(fabsf(v1[0]), fabsf(v1[1])), fmaxf(fabsf(v1[2]), fabsf(v1[3]))));
-        mx = max8_lanes(mx);
-        const int sx = rows16_exp(mx);
-        const float inv = __builtin_ldexpf(1.0f, -sx);
-        u32x4 pk;
-        pk[0] = f32_to_f16_bits(v0[0] * inv) | (f32_to_f16_bits(v0[1] * inv) << 16);
-        pk[1] = f32_to_f16_bits(v0[2] * inv) | (f32_to_f16_bits(v0[3] * inv) << 16);
-        pk[2] = f32_to_f16_bits(v1[0] * inv) | (f32_to_f16_bits(v1[1] * inv) << 16);
-        pk[3] = f32_to_f16_bits(v1[2] * inv) | (f32_to_f16_bits(v1[3] * inv) << 16);
-        const int m = m0 + 128 * wm + 32 * i + rr;
-        const int col = nt * S::BN + 64 * wn + 8 * ch;
-        if (m < cnt && col < N) {
-          __builtin_nontemporal_store(pk, reinterpret_cast<u32x4*>(a.y16 + (size_t)(r0 + m) * N + col));
-          if (ch == 0) a.y16_scale[(size_t)(r0 + m) * nb + blk] = (uint8_t)(sx + 127);
-        }
-      }
+      store_rows16<64>(strip, lane, m0 + 128 * wm + 32 * i, cnt, nt * S::BN + 64 * wn, N,
+                       (size_t)r0, a.y16, a.y16_scale);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -900,32 +913,9 @@ __global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      if (compact) {
-        // compact rows: a strip row holds two 64-column scale blocks; 8
-        // adjacent lanes hold one block's 8 chunks of 8 values
-        const int nb = N / 64;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {  // 32 rows x 16 chunks
-          const int c = lane + 64 * t, rr = c >> 4, ch = c & 15;
-          const f32x4 v0 = *reinterpret_cast<const f32x4*>(strip + rr * 128 + 8 * ch);
-          const f32x4 v1 = *reinterpret_cast<const f32x4*>(strip + rr * 128 + 8 * ch + 4);
-          float mx = fmaxf(fmaxf(fmaxf(fabsf(v0[0]), fabsf(v0[1])), fmaxf(fabsf(v0[2]), fabsf(v0[3]))),
-                           fmaxf(fmaxf(fabsf(v1[0]), fabsf(v1[1])), fmaxf(fabsf(v1[2]), fabsf(v1[3]))));
-          mx = max8_lanes(mx);
-          const int sx = rows16_exp(mx);
-          const float inv = __builtin_ldexpf(1.0f, -sx);
-          u32x4 pk;
-          pk[0] = f32_to_f16_bits(v0[0] * inv) | (f32_to_f16_bits(v0[1] * inv) << 16);
-          pk[1] = f32_to_f16_bits(v0[2] * inv) | (f32_to_f16_bits(v0[3] * inv) << 16);
-          pk[2] = f32_to_f16_bits(v1[0] * inv) | (f32_to_f16_bits(v1[1] * inv) << 16);
-          pk[3] = f32_to_f16_bits(v1[2] * inv) | (f32_to_f16_bits(v1[3] * inv) << 16);
-          const int m = m0 + 128 * wm + 32 * i + rr;
-          const int col = nt * S::BN + 128 * wn + 8 * ch;
-          if (m < cnt && col < N) {
-            __builtin_nontemporal_store(pk, reinterpret_cast<u32x4*>(a.y16 + (size_t)(r0 + m) * N + col));
-            if ((ch & 7) == 0) a.y16_scale[(size_t)(r0 + m) * nb + col / 64] = (uint8_t)(sx + 127);
-          }
-        }
+      if (compact) {  // compact rows: two 64-column scale blocks per strip row
+        store_rows16<128>(strip, lane, m0 + 128 * wm + 32 * i, cnt, nt * S::BN + 128 * wn, N,
+                          (size_t)r0, a.y16, a.y16_scale);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -1318,6 +1308,7 @@ __global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmAr
 #pragma unroll
     for (int j = 0; j < 4; ++j) sd[j] = WF == W_FP8 ? chs[mcol(bcol(j) + l32)] : gsc;
     float* strip = reinterpret_cast<float*>(smem + wave * 16384);  // 32 x 128 fp32
+    const bool compact = a.y16 != nullptr;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -1327,6 +1318,14 @@ __global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmAr
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (compact) {  // compact rows: two 64-column scale blocks per strip row
+        store_rows16<128>(strip, lane, m0 + 128 * wm + 32 * i, cnt, nt * S::BN + 128 * wn, N,
+                          (size_t)r0, a.y16, a.y16_scale);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        continue;
+      }
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
         const int c = lane + 64 * t, rr = c >> 5, ch = c & 31;

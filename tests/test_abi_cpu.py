@@ -174,7 +174,7 @@ def experts_rows16(w=None, **kw):
 def test_experts_rows16_validation():
     assert experts_rows16(T=0, x=None, off=None, sp=None, y16=None, ysc=None, ws=None) == OK
     assert experts_rows16(T=128) == UNSUP  # 4 rows per expert: the streaming kernels
-    assert experts_rows16(w=_w(dtype=2, gus=G, dns=Hh, qmode=1)) == UNSUP  # fp8-MFMA mode
+    assert experts_rows16(T=128, w=_w(dtype=2, gus=G, dns=Hh)) == UNSUP  # FP8, streaming sizes
     assert experts_rows16(ysc=None) == INVAL
     assert experts_rows16(y16=MIS) == INVAL
     assert experts_rows16(ws_bytes=1024) == WS_SMALL

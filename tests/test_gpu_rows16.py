@@ -27,6 +27,8 @@ CASES = [
     MC("r16_wide", 133, T=700, H=1088, E=8, k=3, I=256),        # a 128 x 512 tail tile per expert
     MC("r16_fp4", 135, T=300, H=512, E=16, k=4, I=256, w_dtype="fp4"),   # quantised tiles
     MC("r16_fp8", 136, T=300, H=576, E=16, k=4, I=192, w_dtype="fp8"),   # 9 blocks per row
+    MC("r16_fp4_f8", 137, T=300, H=512, E=16, k=4, I=256, w_dtype="fp4", qmode="f8"),
+    MC("r16_fp8_f8_small", 138, T=24, H=256, E=16, k=2, I=128, w_dtype="fp8", qmode="f8"),
 ]
 
 
