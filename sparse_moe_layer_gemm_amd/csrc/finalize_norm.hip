@@ -10,25 +10,36 @@
 //   normed = RNE_bf16(r * (1 / sqrt(mean(r^2) + eps)) * gamma_next)
 //
 // Bound by HBM like the plain finalize (each fp32 expert row is read once).
-// Both mean squares need the whole row, so one workgroup owns a token: lane
-// l keeps float4 column chunks l, l + 256, ... of m (and then of r) in
-// registers, the row sums go through a fixed butterfly in each wavefront and
-// a fixed-order add of the four wavefront sums, so results are deterministic.
+// Both mean squares need the whole row, so one workgroup of 1024 lanes owns a
+// token (16 wavefronts: enough loads in flight per token even at decode batch
+// sizes): lane l keeps float4 column chunks l, l + 1024, ... of m (and then
+// of r) in registers, the row sums go through a fixed butterfly in each
+// wavefront and a fixed-order add of the 16 wavefront sums, so results are
+// deterministic.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-// sum over the workgroup (256 lanes), identical in every lane
+constexpr int FN_THREADS = 1024;  // lanes per token
+constexpr int FN_WAVES = FN_THREADS / 64;
+
+// sum over the workgroup, identical in every lane
 __device__ __forceinline__ float row_sum(float v, float* red) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);  // a + b == b + a: lanes agree
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[wave] = v;
   __syncthreads();
-  const float s = (red[0] + red[1]) + (red[2] + red[3]);
+  float s[FN_WAVES];
+#pragma unroll
+  for (int w = 0; w < FN_WAVES; ++w) s[w] = red[w];
+#pragma unroll
+  for (int d = 1; d < FN_WAVES; d <<= 1)  // fixed pairwise order
+#pragma unroll
+    for (int w = 0; w < FN_WAVES; w += 2 * d) s[w] += s[w + d];
   __syncthreads();  // red is reused by the next sum
-  return s;
+  return s[0];
 }
 
 __device__ __forceinline__ float4 bf16x4_to_f32(uint2 b) {
@@ -42,15 +53,15 @@ __device__ __forceinline__ uint2 f32x4_to_bf16(float a, float b, float c, float 
   return r;
 }
 
-// CH float4 chunks per lane: H <= 1024 * CH. residual and residual_out may alias
+// CH float4 chunks per lane: H <= 4096 * CH. residual and residual_out may alias
 // (a lane reads each of its residual chunks before writing the same chunk).
 template <int CH>
-__global__ __launch_bounds__(256) void finalize_norm_kernel(
+__global__ __launch_bounds__(FN_THREADS) void finalize_norm_kernel(
     const float* __restrict__ y, const int32_t* __restrict__ pair_pos, const float* __restrict__ w,
     int k, int H, const uint16_t* residual, const uint16_t* __restrict__ gamma_post,
     const uint16_t* __restrict__ gamma_next, float eps, uint16_t* residual_out,
     uint16_t* __restrict__ normed) {
-  __shared__ float red[4];
+  __shared__ float red[FN_WAVES];
   const long long t = blockIdx.x;
   int pos[8];
   float wt[8];
@@ -64,7 +75,7 @@ __global__ __launch_bounds__(256) void finalize_norm_kernel(
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int q = threadIdx.x + 256 * c;
+    const int q = threadIdx.x + FN_THREADS * c;
     m[c] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (q < n4) {
       f32x4 v[8];  // each expert row is read once: nontemporal
@@ -88,7 +99,7 @@ __global__ __launch_bounds__(256) void finalize_norm_kernel(
   const size_t row = (size_t)t * H;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int q = threadIdx.x + 256 * c;
+    const int q = threadIdx.x + FN_THREADS * c;
     if (q < n4) {
       const float4 res = bf16x4_to_f32(reinterpret_cast<const uint2*>(residual + row)[q]);
       const float4 gp = bf16x4_to_f32(reinterpret_cast<const uint2*>(gamma_post)[q]);
@@ -102,7 +113,7 @@ __global__ __launch_bounds__(256) void finalize_norm_kernel(
   const float inv_r = 1.0f / sqrtf(row_sum(ss2, red) / (float)H + eps);
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int q = threadIdx.x + 256 * c;
+    const int q = threadIdx.x + FN_THREADS * c;
     if (q < n4) {
       const float4 gn = bf16x4_to_f32(reinterpret_cast<const uint2*>(gamma_next)[q]);
       reinterpret_cast<uint2*>(normed + row)[q] =
@@ -116,8 +127,8 @@ template <int CH>
 hipError_t launch_ch(const float* y, const int32_t* pp, const float* w, int T, int k, int H,
                      const uint16_t* res, const uint16_t* gp, const uint16_t* gn, float eps,
                      uint16_t* res_out, uint16_t* normed, hipStream_t st) {
-  finalize_norm_kernel<CH><<<(unsigned)T, 256, 0, st>>>(y, pp, w, k, H, res, gp, gn, eps, res_out,
-                                                        normed);
+  finalize_norm_kernel<CH><<<(unsigned)T, FN_THREADS, 0, st>>>(y, pp, w, k, H, res, gp, gn, eps,
+                                                               res_out, normed);
   return hipGetLastError();
 }
 
@@ -127,15 +138,12 @@ hipError_t launch_finalize_norm(const float* y_sorted, const int32_t* pair_pos, 
                                 int T, int k, int H, const uint16_t* residual,
                                 const uint16_t* gamma_post, const uint16_t* gamma_next, float eps,
                                 uint16_t* residual_out, uint16_t* normed, hipStream_t st) {
-  const int ch = (H + 1023) / 1024;
+  const int ch = (H + 4 * FN_THREADS - 1) / (4 * FN_THREADS);
 #define MOE_FN_CASE(n) \
   case n:              \
     return launch_ch<n>(y_sorted, pair_pos, w, T, k, H, residual, gamma_post, gamma_next, eps, residual_out, normed, st)
   switch (ch) {
     MOE_FN_CASE(1); MOE_FN_CASE(2); MOE_FN_CASE(3); MOE_FN_CASE(4);
-    MOE_FN_CASE(5); MOE_FN_CASE(6); MOE_FN_CASE(7); MOE_FN_CASE(8);
-    MOE_FN_CASE(9); MOE_FN_CASE(10); MOE_FN_CASE(11); MOE_FN_CASE(12);
-    MOE_FN_CASE(13); MOE_FN_CASE(14); MOE_FN_CASE(15); MOE_FN_CASE(16);
     default:
       return hipErrorInvalidValue;
   }

@@ -93,11 +93,11 @@ def check(y, pp, w, res, gp, gn, eps, k):
 
 
 @pytest.mark.parametrize("T,H,k,eps", [
-    (128, 5120, 8, 1e-6),    # Beam decode shape: 5 column chunks per lane
-    (37, 192, 3, 1e-5),      # ragged: one partial chunk
-    (16, 1088, 1, 1e-6),     # second chunk with 16 active lanes; k = 1
-    (5, 16384, 8, 1e-6),     # widest row
-    (1, 64, 2, 0.0),         # smallest row, no epsilon
+    (128, 5120, 8, 1e-6),    # Beam decode shape: 2 column chunks per lane, the second partial
+    (37, 192, 3, 1e-5),      # ragged: 48 of 1024 lanes hold a chunk
+    (16, 1088, 1, 1e-6),     # 272 of 1024 lanes; k = 1
+    (5, 16384, 8, 1e-6),     # widest row: 4 full chunks per lane
+    (1, 64, 2, 0.0),         # smallest row (16 lanes), no epsilon
 ])
 def test_finalize_norm_parity(T, H, k, eps):
     y, pp, w, res, gp, gn = make_inputs(11, T, H, k)
