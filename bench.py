@@ -43,6 +43,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--hbm-probe", action="store_true",
                    help="time a plain 4 GiB device copy (the reference kernel for HBM counters) and exit")
+    p.add_argument("--gemm-probe", action="store_true",
+                   help="time the vendor library's dense bf16 GEMMs (torch.matmul) on shapes with "
+                        "the prefill expert GEMMs' FLOPs, for comparison, and exit")
     return p.parse_args()
 
 
@@ -216,6 +219,44 @@ def hbm_probe(torch):
                       "GB/s (read+write)": 2 * nbytes / (ms / 1e3) / 1e9}), flush=True)
 
 
+def gemm_probe(torch):
+    """torch.matmul / torch.bmm in bf16 (the vendor GEMM library) at the prefill expert shapes.
+
+    Dense: all T*k = 131072 routed rows as one [131072, K] x [K, N] product (gate/up: K = 5120,
+    N = 3072; down: K = 1536, N = 5120), i.e. the grouped GEMMs' FLOPs with no grouping and no
+    gather. Batched: 256 experts x 512 rows each, the same FLOPs at perfectly uniform load.
+    Operands are contiguous; inputs N(0,1) in bf16.
+    """
+    g = torch.Generator(device="cuda").manual_seed(0)
+    P, H, I, E = 131072, 5120, 1536, 256
+    cases = [("dense gate/up", (P, H), (H, 2 * I)), ("dense down", (P, I), (I, H)),
+             ("batched gate/up", (E, P // E, H), (E, H, 2 * I)),
+             ("batched down", (E, P // E, I), (E, I, H))]
+    for name, sa, sb in cases:
+        a = torch.randn(sa, generator=g, device="cuda").to(torch.bfloat16).contiguous()
+        b = torch.randn(sb, generator=g, device="cuda").to(torch.bfloat16).contiguous()
+        f = torch.matmul if a.dim() == 2 else torch.bmm
+        c = f(a, b)
+        for _ in range(3):
+            f(a, b, out=c)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 10
+        e0.record()
+        for _ in range(n):
+            f(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        flops = 2.0 * P * sa[-1] * sb[-1]
+        print(json.dumps({"probe": f"torch bf16 {name}", "a": list(sa), "b": list(sb),
+                          "ms_per_launch": round(ms, 4),
+                          "TFLOP/s": round(flops / (ms / 1e3) / 1e12, 1),
+                          "frac_of_2.5_PFLOPs": round(flops / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 3)}),
+              flush=True)
+        del a, b, c
+
+
 def expert_bytes(cfg):
     """Bytes of one expert's weights: gate/up [H, 2I] + down [I, H] (with scales)."""
     n = cfg.H * 2 * cfg.I + cfg.I * cfg.H
@@ -261,6 +302,9 @@ def main():
     import torch
     if a.hbm_probe:
         hbm_probe(torch)
+        return
+    if a.gemm_probe:
+        gemm_probe(torch)
         return
     import sparse_moe_layer_gemm_amd as moe
     import synth
