@@ -192,11 +192,21 @@ moe_status enqueue_route(const void* x, int32_t x_dtype, int64_t T, int32_t H, c
   return launch_status(e);
 }
 
+// Split partial sums of the down GEMM left for the finalize (S = 0: none).
+struct KeptPartials {
+  const float* part = nullptr;
+  int S = 0;
+  long long stride = 0;
+};
+
+// With `keep` set, a split-K down GEMM of the streaming kernels leaves its
+// partial sums in the workspace (described in *keep) instead of reducing them
+// into y_sorted; the caller then finalizes from them.
 moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I,
                            int32_t E, int32_t k, const int32_t* offsets,
                            const int32_t* sorted_pair, const moe_expert_weights* w,
                            float* y_sorted, void* ws, hipStream_t st, uint16_t* y16 = nullptr,
-                           uint8_t* y16_scale = nullptr) {
+                           uint8_t* y16_scale = nullptr, KeptPartials* keep = nullptr) {
   const int P = (int)(T * k);
   if (w->dtype == MOE_F32) {
     return launch_status(moe::launch_expert_f32(
@@ -267,6 +277,10 @@ moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H,
     d.ksteps = sd.ksteps;
     d.part = part;
     d.part_stride = (long long)P * H;
+    if (keep && d.ksplit > 1) {
+      d.keep_partials = true;
+      *keep = KeptPartials{part, d.ksplit, d.part_stride};
+    }
   }
   hipError_t e = moe::launch_expert_stream(wf, true, a, st);
   if (e != hipSuccess) return MOE_ERR_LAUNCH;
@@ -522,8 +536,14 @@ moe_status moe_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
     return launch_status(moe::launch_finalize_rows16(y16, y16_scale, pair_pos, tw, (int)T, k, H,
                                                      out_dtype == MOE_BF16, out, out_f32, st));
   }
-  s = enqueue_experts(x, x_dtype, T, H, I, E, k, offsets, sorted_pair, w, y_sorted, exp_ws, st);
+  KeptPartials kept;
+  s = enqueue_experts(x, x_dtype, T, H, I, E, k, offsets, sorted_pair, w, y_sorted, exp_ws, st,
+                      nullptr, nullptr, &kept);
   if (s != MOE_OK) return s;
+  if (kept.S > 1)  // small batches: the down GEMM's split reduction folded into the finalize
+    return launch_status(moe::launch_finalize_split(kept.part, kept.S, kept.stride, pair_pos, tw,
+                                                    (int)T, k, H, out_dtype == MOE_BF16, out,
+                                                    out_f32, st));
   return launch_status(moe::launch_finalize(y_sorted, pair_pos, tw, (int)T, k, H,
                                             out_dtype == MOE_BF16, out, out_f32, st));
 }

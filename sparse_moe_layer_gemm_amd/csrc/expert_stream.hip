@@ -473,7 +473,7 @@ hipError_t launch_one(int wfmt, const StreamGemmArgs& a, hipStream_t st) {
       default: return hipErrorInvalidValue;
     }
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    if (err != hipSuccess || (!GU && a.keep_partials)) return err;
     const int P = a.rows;
     const long long items = (long long)P * (GU ? a.I : a.N) / 4;
     const unsigned blocks = (unsigned)std::min<long long>((items + 255) / 256, 4096);

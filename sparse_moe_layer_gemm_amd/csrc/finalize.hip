@@ -110,7 +110,93 @@ __global__ __launch_bounds__(256) void finalize_rows16_kernel(
   }
 }
 
+// The same from the fp32 partial sums of a split-K down GEMM, which the
+// streaming kernels leave at small batches: an expert row is the sum of its S
+// partial rows in split order (exactly as the split reduction forms it), then
+// the k rows are added with their weights in slot order as above. Work item:
+// (token, 256-column chunk); wavefront q forms the rows of slots q and q + 4
+// for the chunk's 64 float4 columns (all 2 S loads issued together) and puts
+// them in LDS, then wavefront 0 adds them. Folding the reduction in here saves
+// a launch and a pass over the rows when the layer is latency-bound.
+template <bool BF16_OUT>
+__global__ __launch_bounds__(256) void finalize_split_kernel(
+    const float* __restrict__ part, int S, long long sstride, const int32_t* __restrict__ pair_pos,
+    const float* __restrict__ w, int k, int H, int n_chunks, long long n_items,
+    void* __restrict__ out, float* __restrict__ out_f32) {
+  __shared__ f32x4 rows[8][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (long long item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const long long t = item / n_chunks;
+    const int c = (int)(item - t * n_chunks) * 256 + lane * 4;
+    const bool col_ok = c < H;
+    bool use[2];
+    const float* src[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // slot wave + 4h; invalid ones read slot 0, column 0
+      const int j = wave + 4 * h;
+      use[h] = j < k && col_ok;
+      src[h] = part + (size_t)pair_pos[t * k + (j < k ? j : 0)] * H + (col_ok ? c : 0);
+    }
+    f32x4 pv[2][kMaxStreamSplit];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int sp = 0; sp < kMaxStreamSplit; ++sp)
+        if (sp < S) pv[h][sp] = __builtin_nontemporal_load(
+                        reinterpret_cast<const f32x4*>(src[h] + sp * sstride));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4 v = pv[h][0];
+#pragma unroll
+      for (int sp = 1; sp < kMaxStreamSplit; ++sp)
+        if (sp < S) v += pv[h][sp];
+      if (use[h]) rows[wave + 4 * h][lane] = v;
+    }
+    __syncthreads();
+    if (wave == 0 && col_ok) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < k) {
+          const float wt = w[t * k + j];
+          const f32x4 v = rows[j][lane];
+          acc.x = fmaf(wt, v.x, acc.x);
+          acc.y = fmaf(wt, v.y, acc.y);
+          acc.z = fmaf(wt, v.z, acc.z);
+          acc.w = fmaf(wt, v.w, acc.w);
+        }
+      }
+      if (out_f32) *reinterpret_cast<float4*>(out_f32 + (size_t)t * H + c) = acc;
+      if constexpr (BF16_OUT) {
+        uint2 pk;
+        pk.x = f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16);
+        pk.y = f32_to_bf16_bits(acc.z) | (f32_to_bf16_bits(acc.w) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (size_t)t * H + c) = pk;
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(out) + (size_t)t * H + c) = acc;
+      }
+    }
+    __syncthreads();  // rows[] is rewritten by the next item
+  }
+}
+
 }  // namespace
+
+hipError_t launch_finalize_split(const float* part, int S, long long sstride,
+                                 const int32_t* pair_pos, const float* w, int T, int k, int H,
+                                 bool out_bf16, void* out, float* out_f32, hipStream_t st) {
+  if (S < 1 || S > kMaxStreamSplit || k < 1 || k > 8) return hipErrorInvalidValue;
+  const int n_chunks = (H + 255) / 256;
+  const long long items = (long long)T * n_chunks;
+  const unsigned grid = (unsigned)(items < (1 << 20) ? items : (1 << 20));
+  if (out_bf16)
+    finalize_split_kernel<true><<<grid, 256, 0, st>>>(part, S, sstride, pair_pos, w, k, H,
+                                                      n_chunks, items, out, out_f32);
+  else
+    finalize_split_kernel<false><<<grid, 256, 0, st>>>(part, S, sstride, pair_pos, w, k, H,
+                                                       n_chunks, items, out, out_f32);
+  return hipGetLastError();
+}
 
 hipError_t launch_finalize_rows16(const uint16_t* y16, const uint8_t* y16_scale,
                                   const int32_t* pair_pos, const float* w, int T, int k, int H,

@@ -140,6 +140,9 @@ struct StreamGemmArgs {
   int ksplit = 1, ksteps = 0;
   float* part = nullptr;
   long long part_stride = 0;
+  // Down GEMM only: leave the split partial sums in `part` for the consumer
+  // (the layer's finalize adds them) instead of launching the reduction.
+  bool keep_partials = false;
 };
 // fp8-MFMA mode operands: E4M3 codes of x (gate/up) with one fp32 scale per
 // token, or of h (down) with one E8M0 scale per row and 128-column block.
@@ -211,6 +214,12 @@ hipError_t launch_expert_f32(const float* x, int T, int H, int I, int E, int k, 
 hipError_t launch_finalize(const float* y_sorted, const int32_t* pair_pos, const float* w, int T,
                            int k, int H, bool out_bf16, void* out, float* out_f32,
                            hipStream_t st);
+// The same from the S fp32 partial sums of a split-K down GEMM
+// (part + s * sstride, [P, H] each): every expert row is their sum in split
+// order, so the result equals reducing first and then finalizing, bit for bit.
+hipError_t launch_finalize_split(const float* part, int S, long long sstride,
+                                 const int32_t* pair_pos, const float* w, int T, int k, int H,
+                                 bool out_bf16, void* out, float* out_f32, hipStream_t st);
 // Weighted un-permute of compact rows (fp16 + per-64-column power-of-two
 // scales), otherwise as launch_finalize.
 hipError_t launch_finalize_rows16(const uint16_t* y16, const uint8_t* y16_scale,

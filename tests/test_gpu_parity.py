@@ -55,6 +55,11 @@ SMALL = [
     MC("few_pairs_split_bf16", 121, T=2, H=1024, E=64, k=3, I=320),
     MC("few_pairs_split_fp4", 122, T=3, H=2048, E=32, k=2, I=192, w_dtype="fp4"),
     MC("few_pairs_split_fp8", 123, T=3, H=1024, E=32, k=2, I=320, w_dtype="fp8"),
+    # K split on the down product too (4 splits bf16, 2 E4M3), whose partial
+    # sums moe_forward adds inside its finalize; H = 320 leaves the second
+    # 256-column chunk of that finalize a quarter full
+    MC("split_down_ragged_h", 124, T=2, H=320, E=16, k=4, I=1024),
+    MC("split_down_fp8", 125, T=3, H=320, E=16, k=3, I=1024, w_dtype="fp8"),
 ]
 
 
@@ -173,13 +178,16 @@ def test_decode_single_token(decode_layer):
     check_experts(L, r, np.arange(cfg.k))
     check_finalize(L, r)
     lay = check_layer(L, r, [0])
+    f = L.forward()  # the down GEMM's split partial sums added inside the finalize
+    assert _same_bits(f["out"], r["out"]) and torch.equal(f["out_f32"], r["out_f32"])
     log(f"  T=1 out {lay['out_rel_err']:.2e}")
 
 
 @pytest.mark.parametrize("T", [2, 8])
 def test_decode_small_batches(decode_layer, T):
     """Few touched experts: the streaming kernels split K (several splits at
-    T = 2, two for gate/up at T = 8) and a reduction forms h and y."""
+    T = 2, two for gate/up at T = 8) and a reduction forms h and y (inside
+    moe_forward, y's is folded into the finalize: bit-identical)."""
     cfg = decode_layer.cfg.with_(name=f"decode_t{T}", T=T)
     L = Layer(cfg, x=decode_layer.x[:T].copy())
     r = L.stages()
@@ -189,7 +197,7 @@ def test_decode_small_batches(decode_layer, T):
     check_finalize(L, r)
     lay = check_layer(L, r, np.arange(T))
     f = L.forward()
-    assert _same_bits(f["out"], r["out"])
+    assert _same_bits(f["out"], r["out"]) and torch.equal(f["out_f32"], r["out_f32"])
     log(f"  T={T} y {ey:.2e} out {lay['out_rel_err']:.2e}")
 
 
