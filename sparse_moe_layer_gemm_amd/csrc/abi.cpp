@@ -162,7 +162,7 @@ bool rows16_supported(const moe_expert_weights* w, int64_t P, int32_t E) {
 moe_status enqueue_route(const void* x, int32_t x_dtype, int64_t T, int32_t H, const float* wr,
                          const float* bias, int32_t E, int32_t k, int32_t logits_dtype,
                          void* logits, float* logits_f32, int32_t* ids, float* w, void* ws,
-                         hipStream_t st) {
+                         hipStream_t st, const moe::PermuteOut* perm = nullptr) {
   int S, L;
   router_plan(T, H, E, &S, &L);
   const bool x3 = router_use_bf16x3(x_dtype, T);
@@ -188,7 +188,7 @@ moe_status enqueue_route(const void* x, int32_t x_dtype, int64_t T, int32_t H, c
   }
   if (e != hipSuccess) return MOE_ERR_LAUNCH;
   e = moe::launch_router_select(part, nsplit, ldp, (int)T, E, k, bias, logits_dtype == MOE_BF16,
-                                logits, logits_f32, ids, w, st);
+                                logits, logits_f32, ids, w, st, perm);
   return launch_status(e);
 }
 
@@ -520,12 +520,16 @@ moe_status moe_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
   if (topk_w) tw = topk_w;
   if (!logits) logits = lbuf;
 
+  // one token: the select kernel also writes the permute (a sort of k distinct ids)
+  const moe::PermuteOut perm{counts, offsets, sorted_pair, pair_pos};
   s = enqueue_route(x, x_dtype, T, H, w_router, bias, E, k, logits_dtype, logits, nullptr, ids, tw,
-                    route_ws, st);
+                    route_ws, st, T == 1 ? &perm : nullptr);
   if (s != MOE_OK) return s;
-  s = launch_status(
-      moe::launch_permute(ids, (int)P, E, counts, offsets, sorted_pair, pair_pos, perm_ws, st));
-  if (s != MOE_OK) return s;
+  if (T != 1) {
+    s = launch_status(
+        moe::launch_permute(ids, (int)P, E, counts, offsets, sorted_pair, pair_pos, perm_ws, st));
+    if (s != MOE_OK) return s;
+  }
   if (rows16_supported(w, (int64_t)P, E)) {
     // compact rows in the fp32 rows' space: P*H*2 + P*H/64 bytes
     uint16_t* y16 = reinterpret_cast<uint16_t*>(y_sorted);

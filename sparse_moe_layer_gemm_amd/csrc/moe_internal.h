@@ -97,10 +97,21 @@ __device__ __forceinline__ u32x4 fp8_frag(uint32_t d0, uint32_t d1) {
 // Router GEMM partial sums: part[s][t][e] = sum over K-slice s of x[t,h] w[h,e].
 hipError_t launch_router_gemm(const void* x, bool x_bf16, int T, int H, const float* w_router,
                               int E, int n_split, int split_len, float* part, hipStream_t st);
+// Outputs of the permute (layouts as launch_permute's).
+struct PermuteOut {
+  int32_t* counts = nullptr;
+  int32_t* offsets = nullptr;
+  int32_t* sorted_pair = nullptr;
+  int32_t* pair_pos = nullptr;
+};
 // Sum of partials + bias -> logits (bf16 or fp32), softmax, top-k, renormalised weights.
+// With `perm` and T == 1 the select also writes the permute of the token's k
+// pairs (its experts are distinct, so that is a sort of k ids); otherwise
+// `perm` must be null.
 hipError_t launch_router_select(const float* part, int n_split, int ldp, int T, int E, int k,
                                 const float* bias, bool logits_bf16, void* logits,
-                                float* logits_f32, int32_t* ids, float* w, hipStream_t st);
+                                float* logits_f32, int32_t* ids, float* w, hipStream_t st,
+                                const PermuteOut* perm = nullptr);
 // Stable counting sort of pairs by expert (one workgroup up to
 // kPermuteOneBlockMax pairs, else three kernels with permute_ws_bytes of scratch).
 constexpr long long kPermuteOneBlockMax = 16384;

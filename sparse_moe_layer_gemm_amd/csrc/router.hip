@@ -167,7 +167,7 @@ template <bool BF16_LOGITS>
 __global__ __launch_bounds__(256) void router_select_wg_kernel(
     const float* __restrict__ part, int n_split, int ldp, int T, int E, int k,
     const float* __restrict__ bias, void* __restrict__ logits, float* __restrict__ logits_f32,
-    int32_t* __restrict__ ids, float* __restrict__ w) {
+    int32_t* __restrict__ ids, float* __restrict__ w, PermuteOut perm) {
   __shared__ uint64_t cand[4][8];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x;
@@ -233,6 +233,39 @@ __global__ __launch_bounds__(256) void router_select_wg_kernel(
         ids[(size_t)t * k + j] = topi[j];
         w[(size_t)t * k + j] = pr[j] / z;
       }
+  }
+  if (perm.counts) {
+    // a single token (launched only for T == 1): its k experts are distinct,
+    // so the stable sort of its pairs by expert is the rank of each id among
+    // the k (topi is the same in every lane of this wavefront)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int ex = 64 * c + lane;
+      if (ex < E) {
+        int below = 0, hit = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j < k) {
+            below += topi[j] < ex;
+            hit |= topi[j] == ex;
+          }
+        perm.counts[ex] = hit;
+        perm.offsets[ex] = below;
+      }
+    }
+    if (lane == 0) perm.offsets[E] = k;
+    int mine = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j == lane) mine = topi[j];
+    if (lane < k) {
+      int pos = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < k) pos += topi[j] < mine;
+      perm.sorted_pair[pos] = lane;
+      perm.pair_pos[lane] = pos;
+    }
   }
 }
 
@@ -337,14 +370,17 @@ hipError_t launch_router_gemm(const void* x, bool x_bf16, int T, int H, const fl
 
 hipError_t launch_router_select(const float* part, int n_split, int ldp, int T, int E, int k,
                                 const float* bias, bool logits_bf16, void* logits,
-                                float* logits_f32, int32_t* ids, float* w, hipStream_t st) {
+                                float* logits_f32, int32_t* ids, float* w, hipStream_t st,
+                                const PermuteOut* perm) {
+  if (perm && T != 1) return hipErrorInvalidValue;
+  const PermuteOut po = perm ? *perm : PermuteOut{};
   if (T < 1024) {  // one workgroup per token: 4x the load parallelism per token
     if (logits_bf16)
       router_select_wg_kernel<true><<<T, 256, 0, st>>>(part, n_split, ldp, T, E, k, bias, logits,
-                                                       logits_f32, ids, w);
+                                                       logits_f32, ids, w, po);
     else
       router_select_wg_kernel<false><<<T, 256, 0, st>>>(part, n_split, ldp, T, E, k, bias, logits,
-                                                        logits_f32, ids, w);
+                                                        logits_f32, ids, w, po);
     return hipGetLastError();
   }
   const unsigned grid = (unsigned)((T + 3) / 4);  // one wavefront per token

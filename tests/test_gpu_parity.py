@@ -60,6 +60,10 @@ SMALL = [
     # 256-column chunk of that finalize a quarter full
     MC("split_down_ragged_h", 124, T=2, H=320, E=16, k=4, I=1024),
     MC("split_down_fp8", 125, T=3, H=320, E=16, k=3, I=1024, w_dtype="fp8"),
+    # one token: moe_forward's select kernel also writes the permute (every
+    # expert chosen; k < E with E not a multiple of 64)
+    MC("one_token_all_experts", 126, T=1, H=256, E=8, k=8, I=128),
+    MC("one_token_k3", 127, T=1, H=192, E=70, k=3, I=64),
 ]
 
 
