@@ -220,7 +220,8 @@ def hbm_probe(torch):
 
 
 def gemm_probe(torch):
-    """torch.matmul / torch.bmm in bf16 (the vendor GEMM library) at the prefill expert shapes.
+    """torch.matmul / torch.bmm in bf16 (the vendor GEMM library) at the prefill expert shapes,
+    then this library's grouped GEMMs on the batched one.
 
     Dense: all T*k = 131072 routed rows as one [131072, K] x [K, N] product (gate/up: K = 5120,
     N = 3072; down: K = 1536, N = 5120), i.e. the grouped GEMMs' FLOPs with no grouping and no
@@ -255,6 +256,44 @@ def gemm_probe(torch):
                           "frac_of_2.5_PFLOPs": round(flops / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 3)}),
               flush=True)
         del a, b, c
+    # this library's grouped GEMMs on the batched shape (moe_experts with compact rows, as
+    # moe_forward runs them at prefill): 256 experts x 512 rows, the rows gathered through a
+    # random permutation of the 131072 (token, slot) pairs; weights N(0, 1/fan_in)
+    import sparse_moe_layer_gemm_amd as moe
+    k = 8
+    T = P // k
+    x = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
+    wgu = torch.empty((E, H, 2 * I), dtype=torch.bfloat16, device="cuda")
+    wdn = torch.empty((E, I, H), dtype=torch.bfloat16, device="cuda")
+    for e in range(E):
+        wgu[e] = torch.randn((H, 2 * I), generator=g, device="cuda") * H ** -0.5
+        wdn[e] = torch.randn((I, H), generator=g, device="cuda") * I ** -0.5
+    w = moe.ExpertWeights(moe.MOE_BF16, wgu, wdn)
+    offsets = (torch.arange(E + 1, device="cuda", dtype=torch.int32) * (P // E)).contiguous()
+    sorted_pair = torch.randperm(P, generator=g, device="cuda").to(torch.int32)
+    y16 = torch.empty((P, H), dtype=torch.int16, device="cuda")
+    ysc = torch.empty((P, H // 64), dtype=torch.uint8, device="cuda")
+    ws = moe.workspace(moe.moe_experts_workspace_size(T, H, I, E, k, w))
+
+    def run():
+        moe.moe_experts_rows16(x, I, E, k, offsets, sorted_pair, w, y16, ysc, ws)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 10
+    e0.record()
+    for _ in range(n):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    flops = 2.0 * P * H * 2 * I + 2.0 * P * I * H
+    print(json.dumps({"probe": "moe_experts_rows16, 256 experts x 512 gathered rows (gate/up + down)",
+                      "ms_per_launch": round(ms, 4),
+                      "TFLOP/s": round(flops / (ms / 1e3) / 1e12, 1),
+                      "frac_of_2.5_PFLOPs": round(flops / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 3)}),
+          flush=True)
 
 
 def expert_bytes(cfg):
