@@ -16,6 +16,7 @@ Prints one JSON line. Options: --gpus N (only 1 is supported), --steps K,
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -133,6 +134,22 @@ class Workload:
         t1.record()
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / steps
+
+    def iter_spread(self, n=50):
+        """Per-call times (ms) of n more forward calls, each bracketed by events
+        with a synchronisation after it: median and the p10 / p90 spread."""
+        torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for _ in range(n):
+            e0.record()
+            self.forward()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        q = np.percentile(ts, [10, 50, 90])
+        return {"n": n, "p10": round(float(q[0]), 4), "median": round(float(q[1]), 4),
+                "p90": round(float(q[2]), 4)}
 
     def time_stages(self, steps):
         """Per-stage average durations (ms) from events recorded between the stage
@@ -296,6 +313,27 @@ def gemm_probe(torch):
           flush=True)
 
 
+def hbm_ceiling(torch, moe, nbytes=4 << 30, reps=10):
+    """The library's own streaming read (moe_hbm_read) over a 4 GiB buffer: the
+    measured HBM read ceiling of this chip."""
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        moe.moe_hbm_read(buf, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        moe.moe_hbm_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del buf
+    return {"kernel": "moe_hbm_read (16-byte nontemporal loads)", "bytes": nbytes,
+            "ms": round(ms, 4), "GB/s": round(nbytes / (ms / 1e3) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def expert_bytes(cfg):
     """Bytes of one expert's weights: gate/up [H, 2I] + down [I, H] (with scales)."""
     n = cfg.H * 2 * cfg.I + cfg.I * cfg.H
@@ -327,9 +365,31 @@ def cpu_baseline(wl, budget_s=10.0):
         if dt >= budget_s or passes >= 50:
             break
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(passes * n2 / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    value = round(passes * n2 / dt, 3)
+    # the same oracle on one thread, over 8 tokens
+    one = None
+    try:
+        gomp = ctypes.CDLL("libgomp.so.1")
+        gomp.omp_set_num_threads(1)
+        rows1 = rows[:8]
+        t = time.perf_counter()
+        oracle.layer(wl.x_host, wl.wr_host, wl.bias_host, wl.w_host, c.I, c.k, "bf16", rows=rows1)
+        one = round(rows1.size / (time.perf_counter() - t), 3)
+        gomp.omp_set_num_threads(cores)
+    except OSError:
+        pass
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{passes} pass(es) over {n2} of the {c.T} {c.name} tokens (whole layer per "
-                      f"token, fp64), {dt:.1f} s"}
+                      f"token, fp64), {dt:.1f} s",
+            "value_1_thread": one,
+            "host": {"cpu_model": model, "os_cpu_count": os.cpu_count(),
+                     "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}}
 
 
 def main():
@@ -372,6 +432,12 @@ def main():
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": measured_traffic()},
         }
         dec_line["roofline"]["frac"] = dec_line["roofline"]["achieved"] / HBM_PEAK_GBS
+        dec_line["iter_ms"] = dec.iter_spread()
+        progress("measuring the HBM read ceiling (4 GiB)")
+        ceil = hbm_ceiling(torch, moe)
+        ceil["decode_experts_frac_of_ceiling"] = round(
+            dec_line["roofline"]["achieved"] / ceil["GB/s"], 4)
+        dec_line["hbm_ceiling"] = ceil
 
     if a.workload == "prefill" or not a.no_prefill:
         progress("generating prefill inputs (T=16384, Zipf load)")
@@ -400,6 +466,7 @@ def main():
                          if pre.rows16 else None},
         }
         pre_line["roofline"]["frac"] = pre_line["roofline"]["achieved"] / BF16_PEAK_TFLOPS
+        pre_line["iter_ms"] = pre.iter_spread(20)
 
     q_cfg = synth.CONFIGS["nvfp4_t4096"]
     q_line = None
@@ -494,16 +561,19 @@ def main():
         "roofline": head["roofline"],
         "cpu_baseline": cpu,
         "stages_ms": {k: round(v, 4) for k, v in head["stages_ms"].items()},
+        "iter_ms": head["iter_ms"],
     }
     if a.workload == "decode":
         line["touched_experts"] = dec_line["touched_experts"]
         line["layer_hbm_frac"] = round(dec_line["layer_hbm_frac"], 4)
+        line["hbm_ceiling"] = dec_line["hbm_ceiling"]
         if pre_line is not None:
             line["prefill"] = {"workload": pre_cfg.name, "value": round(pre_line["value"], 1),
                                "unit": "tokens/s", "ms_per_step": round(pre_line["ms_per_step"], 4),
                                "layer_mfma_frac": round(pre_line["layer_mfma_frac"], 4),
                                "roofline": pre_line["roofline"],
                                "stages_ms": {k: round(v, 4) for k, v in pre_line["stages_ms"].items()},
+                               "iter_ms": pre_line["iter_ms"],
                                "expert_load": pre_line["expert_load"]}
         if q_line is not None:
             line["quantised"] = q_line

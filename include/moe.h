@@ -222,6 +222,18 @@ moe_status moe_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
                        int32_t logits_dtype, void* logits, int32_t* topk_ids, float* topk_w,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------ measurement
+ * Not a step of the layer: the HBM read ceiling its bandwidth-bound kernels
+ * are quoted against. Reads `bytes` (a multiple of 16) of device memory at buf
+ * (16-byte aligned) once, in the decode expert kernels' access pattern
+ * (16-byte nontemporal loads, eight in flight per lane; up to 2048 workgroups
+ * of 256 lanes, each over a contiguous range), and combines them so that the
+ * loads cannot be dropped; sink is
+ * one device word the kernel may write. Caller owns both buffers. Errors:
+ * MOE_ERR_INVALID_ARGUMENT for null or misaligned pointers or a size not a
+ * multiple of 16, MOE_ERR_LAUNCH if the launch fails. */
+moe_status moe_hbm_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
 ENTRY_POINTS = ("moe_status_string", "moe_route_workspace_size", "moe_route",
                 "moe_permute_workspace_size", "moe_permute", "moe_experts_workspace_size",
                 "moe_experts", "moe_experts_rows16", "moe_finalize", "moe_finalize_rows16",
-                "moe_finalize_norm", "moe_forward_workspace_size", "moe_forward")
+                "moe_finalize_norm", "moe_forward_workspace_size", "moe_forward", "moe_hbm_read")
 
 
 class MoEError(RuntimeError):
@@ -76,6 +76,7 @@ def load_library(path: str = LIB_PATH):
         "moe_forward": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp,
                                ctypes.POINTER(CExpertWeights), _i32, _vp, _vp, _i32, _vp, _vp, _vp,
                                _vp, _sz, _vp]),
+        "moe_hbm_read": (_i32, [_vp, _sz, _vp, _vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -240,6 +241,13 @@ def moe_forward(x, w_router, bias, w: ExpertWeights, I: int, k: int, out, worksp
 
 
 # ---------------------------------------------------------------- device plumbing
+def moe_hbm_read(buf, sink, stream=None):
+    """Streaming read of every byte of buf (device, 16-byte aligned, size a
+    multiple of 16); sink: a one-word device tensor the kernel may write."""
+    _check("moe_hbm_read", _lib.moe_hbm_read(_ptr(buf), buf.numel() * buf.element_size(),
+                                             _ptr(sink), _stream(stream)))
+
+
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     """A device byte buffer (256-byte aligned by the caching allocator)."""
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)

@@ -552,4 +552,10 @@ moe_status moe_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
                                             out_dtype == MOE_BF16, out, out_f32, st));
 }
 
+// ---------------------------------------------------------------- measurement
+moe_status moe_hbm_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || !aligned16(buf) || bytes % 16 != 0) return MOE_ERR_INVALID_ARGUMENT;
+  return launch_status(moe::launch_hbm_read(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

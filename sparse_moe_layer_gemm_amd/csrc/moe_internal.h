@@ -97,6 +97,8 @@ __device__ __forceinline__ u32x4 fp8_frag(uint32_t d0, uint32_t d1) {
 // Router GEMM partial sums: part[s][t][e] = sum over K-slice s of x[t,h] w[h,e].
 hipError_t launch_router_gemm(const void* x, bool x_bf16, int T, int H, const float* w_router,
                               int E, int n_split, int split_len, float* part, hipStream_t st);
+// Streaming read of `bytes` (a multiple of 16) from buf; sink: one device word.
+hipError_t launch_hbm_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
 // Outputs of the permute (layouts as launch_permute's).
 struct PermuteOut {
   int32_t* counts = nullptr;

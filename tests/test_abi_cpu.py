@@ -264,3 +264,12 @@ def test_binding_fails_loudly_without_library(tmp_path):
             moe_mod.load_library(str(tmp_path / "missing.so"))
         finally:
             moe_mod._lib = saved
+
+
+def test_hbm_read_validation():
+    f = moe.load_library().moe_hbm_read
+    assert f(A, 0, B, None) == OK  # nothing to read: no launch
+    assert f(None, 16, B, None) == INVAL
+    assert f(A, 16, None, None) == INVAL
+    assert f(MIS, 16, B, None) == INVAL
+    assert f(A, 24, B, None) == INVAL
