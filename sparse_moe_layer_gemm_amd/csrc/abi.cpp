@@ -277,9 +277,20 @@ moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H,
     d.ksteps = sd.ksteps;
     d.part = part;
     d.part_stride = (long long)P * H;
+    int kr;
+    if (moe::stream_fold_h(P, E, H, I, wf, &kr)) {
+      // the down kernel forms h from the gate/up partial sums; its own partial
+      // sums go after them
+      a.keep_partials = true;
+      d.hpart = part;
+      d.hsplit = sg.ksplit;
+      d.hpart_stride = a.part_stride;
+      d.hlds_stride = 2 * kr + 16;
+      d.part = part + moe::stream_gu_part_bytes(P, E, H, I, wf) / sizeof(float);
+    }
     if (keep && d.ksplit > 1) {
       d.keep_partials = true;
-      *keep = KeptPartials{part, d.ksplit, d.part_stride};
+      *keep = KeptPartials{d.part, d.ksplit, d.part_stride};
     }
   }
   hipError_t e = moe::launch_expert_stream(wf, true, a, st);

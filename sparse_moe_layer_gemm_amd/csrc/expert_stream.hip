@@ -108,13 +108,21 @@ __device__ __forceinline__ int slot_expert(const int32_t* __restrict__ offsets, 
 }
 
 // ------------------------------------------------------------------ bf16 weights
-template <bool GATE_UP>
+// FOLD (down only, at most 32 rows per expert): the A operand, h, is formed
+// in LDS by the whole workgroup from the gate/up split partial sums before the
+// K loop (h = bf16(silu(sum of gate) * sum of up), splits added in order, as
+// the reduction kernel does), so the gate/up reduction needs no launch of its
+// own. Until that barrier no wavefront leaves early.
+template <bool GATE_UP, bool FOLD = false>
 __global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
+  static_assert(!(FOLD && GATE_UP), "h is folded into the down GEMM only");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, j = lane & 15;
   const int tile = blockIdx.x * 4 + wave;
   const int n_tiles = GATE_UP ? a.I / 64 : (a.N + 127) / 128;
-  if (tile >= n_tiles) return;
+  if constexpr (!FOLD)
+    if (tile >= n_tiles) return;
+  // the expert, its rows and the K range are the same for the whole workgroup
   const int e = slot_expert(a.offsets, a.E, blockIdx.y, lane);
   if (e < 0) return;
   const int r0 = a.offsets[e];
@@ -135,6 +143,39 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
   const int ks0 = a.ksplit > 1 ? split * a.ksteps : 0;
   const int ks1 = a.ksplit > 1 ? min(nk, ks0 + a.ksteps) : nk;
   if (ks0 >= ks1) return;
+
+  extern __shared__ __align__(16) uint8_t hl[];  // FOLD: 32 rows of h, hlds_stride bytes each
+  if constexpr (FOLD) {
+    const int q = (ks1 - ks0) * 8;  // float4 columns of h this split reads
+    const int hc0 = ks0 * 32;
+    for (int it = threadIdx.x; it < MROWS * q; it += 256) {
+      const int m = it / q;
+      const int c = 4 * (it - m * q);
+      uint2 pk = make_uint2(0u, 0u);  // rows past the expert's end: zeros, never stored
+      if (m < cnt) {
+        const float* pg = a.hpart + (size_t)(r0 + m) * 2 * a.I + hc0 + c;
+        f32x4 gv[kMaxStreamSplit], uv[kMaxStreamSplit];
+#pragma unroll
+        for (int sp = 0; sp < kMaxStreamSplit; ++sp)
+          if (sp < a.hsplit) {
+            gv[sp] = *reinterpret_cast<const f32x4*>(pg + sp * a.hpart_stride);
+            uv[sp] = *reinterpret_cast<const f32x4*>(pg + sp * a.hpart_stride + a.I);
+          }
+        f32x4 gs = gv[0], us = uv[0];
+#pragma unroll
+        for (int sp = 1; sp < kMaxStreamSplit; ++sp)
+          if (sp < a.hsplit) {
+            gs += gv[sp];
+            us += uv[sp];
+          }
+        pk.x = f32_to_bf16_bits(silu(gs[0]) * us[0]) | (f32_to_bf16_bits(silu(gs[1]) * us[1]) << 16);
+        pk.y = f32_to_bf16_bits(silu(gs[2]) * us[2]) | (f32_to_bf16_bits(silu(gs[3]) * us[3]) << 16);
+      }
+      *reinterpret_cast<uint2*>(hl + (size_t)m * a.hlds_stride + 2 * c) = pk;
+    }
+    __syncthreads();
+    if (tile >= n_tiles) return;  // no barrier follows
+  }
 
   for (int mc = 0; mc < cnt; mc += MROWS) {
     const int nf = (cnt - mc) > 16 ? 2 : 1;
@@ -158,7 +199,13 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
     };
     auto load = [&](int ks, Ops& o) {
 #pragma unroll
-      for (int f = 0; f < 2; ++f) o.a[f] = load_u32x4(ar.row[f] + ks * 32 + 8 * g);
+      for (int f = 0; f < 2; ++f) {
+        if constexpr (FOLD)  // row 16f + j of the LDS h rows (mc is 0: cnt <= 32)
+          o.a[f] = *reinterpret_cast<const u32x4*>(hl + (size_t)(16 * f + j) * a.hlds_stride +
+                                                   64 * (ks - ks0) + 16 * g);
+        else
+          o.a[f] = load_u32x4(ar.row[f] + ks * 32 + 8 * g);
+      }
 #pragma unroll
       for (int r = 0; r < 8; ++r) o.b[r] = load_w(wb + (size_t)(ks * 32 + 8 * g + r) * N);
     };
@@ -464,16 +511,25 @@ hipError_t launch_one(int wfmt, const StreamGemmArgs& a, hipStream_t st) {
   const int n_tiles = GU ? a.I / 64 : (a.N + 127) / 128;
   // one grid row per expert that can have rows: at most min(E, P) do
   dim3 grid((n_tiles + 3) / 4, a.rows > 0 ? std::min(a.E, a.rows) : a.E);
+  const bool fold = !GU && a.hpart != nullptr;
+  if (fold && (wfmt != W_BF16 || a.rows > MROWS || a.hsplit < 1 || a.hsplit > kMaxStreamSplit ||
+               MROWS * a.hlds_stride > 65536))
+    return hipErrorInvalidValue;
   if (a.ksplit > 1) {
     grid.z = a.ksplit;
     switch (wfmt) {
-      case W_BF16: stream_bf16_kernel<GU><<<grid, 256, 0, st>>>(a); break;
+      case W_BF16:
+        if (fold)
+          stream_bf16_kernel<false, true><<<grid, 256, MROWS * a.hlds_stride, st>>>(a);
+        else
+          stream_bf16_kernel<GU><<<grid, 256, 0, st>>>(a);
+        break;
       case W_FP8: stream_kmajor_kernel<W_FP8, GU><<<grid, 256, 0, st>>>(a); break;
       case W_FP4: stream_kmajor_kernel<W_FP4, GU><<<grid, 256, 0, st>>>(a); break;
       default: return hipErrorInvalidValue;
     }
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess || (!GU && a.keep_partials)) return err;
+    if (err != hipSuccess || a.keep_partials) return err;
     const int P = a.rows;
     const long long items = (long long)P * (GU ? a.I : a.N) / 4;
     const unsigned blocks = (unsigned)std::min<long long>((items + 255) / 256, 4096);
@@ -484,7 +540,12 @@ hipError_t launch_one(int wfmt, const StreamGemmArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   switch (wfmt) {
-    case W_BF16: stream_bf16_kernel<GU><<<grid, 256, 0, st>>>(a); break;
+    case W_BF16:
+      if (fold)
+        stream_bf16_kernel<false, true><<<grid, 256, MROWS * a.hlds_stride, st>>>(a);
+      else
+        stream_bf16_kernel<GU><<<grid, 256, 0, st>>>(a);
+      break;
     case W_FP8: stream_kmajor_kernel<W_FP8, GU><<<grid, 256, 0, st>>>(a); break;
     case W_FP4: stream_kmajor_kernel<W_FP4, GU><<<grid, 256, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
@@ -514,14 +575,33 @@ StreamSplit stream_split_plan(long long P, int E, int K, int N, bool gate_up, in
 
 int stream_k_step(int wfmt) { return wfmt == W_FP4 ? 128 : wfmt == W_FP8 ? 64 : 32; }
 
+bool stream_fold_h(long long P, int E, int H, int I, int wfmt, int* kr) {
+  if (wfmt != W_BF16 || P > MROWS) return false;
+  const StreamSplit gu = stream_split_plan(P, E, H, 2 * I, true, 32);
+  if (gu.ksplit <= 1) return false;
+  const int k = stream_split_plan(P, E, I, H, false, 32).ksteps * 32;
+  if (MROWS * (2 * k + 16) > 65536) return false;
+  *kr = k;
+  return true;
+}
+
+size_t stream_gu_part_bytes(long long P, int E, int H, int I, int wfmt) {
+  const StreamSplit gu = stream_split_plan(P, E, H, 2 * I, true, stream_k_step(wfmt));
+  const size_t b = gu.ksplit > 1 ? (size_t)gu.ksplit * (size_t)P * 2 * I * sizeof(float) : 0;
+  return (b + 255) / 256 * 256;
+}
+
 size_t stream_ws_bytes(long long P, int E, int H, int I, int wfmt) {
   const int step = stream_k_step(wfmt);
   const StreamSplit gu = stream_split_plan(P, E, H, 2 * I, true, step);
   const StreamSplit dn = stream_split_plan(P, E, I, H, false, step);
   size_t b = 0;
   if (gu.ksplit > 1) b = std::max(b, (size_t)gu.ksplit * (size_t)P * 2 * I * sizeof(float));
-  if (dn.ksplit > 1) b = std::max(b, (size_t)dn.ksplit * (size_t)P * H * sizeof(float));
-  return b;
+  const size_t bd = dn.ksplit > 1 ? (size_t)dn.ksplit * (size_t)P * H * sizeof(float) : 0;
+  int kr;
+  if (stream_fold_h(P, E, H, I, wfmt, &kr))  // gate/up partials live on while down writes its own
+    return stream_gu_part_bytes(P, E, H, I, wfmt) + bd;
+  return std::max(b, bd);
 }
 
 hipError_t launch_expert_stream(int wfmt, bool gate_up, const StreamGemmArgs& a, hipStream_t st) {

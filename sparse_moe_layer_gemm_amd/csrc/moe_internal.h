@@ -153,9 +153,18 @@ struct StreamGemmArgs {
   int ksplit = 1, ksteps = 0;
   float* part = nullptr;
   long long part_stride = 0;
-  // Down GEMM only: leave the split partial sums in `part` for the consumer
-  // (the layer's finalize adds them) instead of launching the reduction.
+  // Leave the split partial sums in `part` for their consumer instead of
+  // launching the reduction: gate/up's for the down kernel (hpart below),
+  // down's for the layer's finalize.
   bool keep_partials = false;
+  // Down GEMM of bf16 weights with at most 32 rows per expert: form the h rows
+  // a workgroup needs in LDS from the gate/up split partial sums
+  // (hpart + s * hpart_stride, [P, 2I], s < hsplit) instead of reading h;
+  // hlds_stride = bytes per LDS row. Bit-identical to the reduction kernel.
+  const float* hpart = nullptr;
+  int hsplit = 0;
+  long long hpart_stride = 0;
+  int hlds_stride = 0;
 };
 // fp8-MFMA mode operands: E4M3 codes of x (gate/up) with one fp32 scale per
 // token, or of h (down) with one E8M0 scale per row and 128-column block.
@@ -190,6 +199,13 @@ struct StreamSplit {
 constexpr int kMaxStreamSplit = 16;
 StreamSplit stream_split_plan(long long P, int E, int K, int N, bool gate_up, int step);
 int stream_k_step(int wfmt);  // K values per split unit of the streaming kernels
+// Whether the down kernel forms h from the gate/up partial sums itself (bf16
+// weights, P <= 32, gate/up split); *kr = the K values of h one down split
+// reads (the LDS rows it needs are 32 x (2 kr + 16) bytes).
+bool stream_fold_h(long long P, int E, int H, int I, int wfmt, int* kr);
+// Bytes of the gate/up split partial sums, rounded up to 256 (where the down
+// GEMM's own partial sums start when h is folded).
+size_t stream_gu_part_bytes(long long P, int E, int H, int I, int wfmt);
 size_t stream_ws_bytes(long long P, int E, int H, int I, int wfmt);
 
 // Grouped expert GEMMs for many rows per expert: bf16 weights on 256 x 256

@@ -64,6 +64,9 @@ SMALL = [
     # expert chosen; k < E with E not a multiple of 64)
     MC("one_token_all_experts", 126, T=1, H=256, E=8, k=8, I=128),
     MC("one_token_k3", 127, T=1, H=192, E=70, k=3, I=64),
+    # at most 32 pairs with gate/up split: the down kernel forms h in LDS from
+    # the gate/up partial sums (here several rows per expert, down split too)
+    MC("fold_h_32_pairs", 128, T=4, H=1024, E=16, k=8, I=1024),
 ]
 
 
@@ -187,11 +190,12 @@ def test_decode_single_token(decode_layer):
     log(f"  T=1 out {lay['out_rel_err']:.2e}")
 
 
-@pytest.mark.parametrize("T", [2, 8])
+@pytest.mark.parametrize("T", [2, 4, 8])
 def test_decode_small_batches(decode_layer, T):
     """Few touched experts: the streaming kernels split K (several splits at
-    T = 2, two for gate/up at T = 8) and a reduction forms h and y (inside
-    moe_forward, y's is folded into the finalize: bit-identical)."""
+    T = 2 and 4, two for gate/up at T = 8) and a reduction forms h and y; up to
+    32 pairs the down kernel forms h itself, and inside moe_forward y's
+    reduction is folded into the finalize (both bit-identical)."""
     cfg = decode_layer.cfg.with_(name=f"decode_t{T}", T=T)
     L = Layer(cfg, x=decode_layer.x[:T].copy())
     r = L.stages()
