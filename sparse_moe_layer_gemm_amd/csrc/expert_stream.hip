@@ -27,8 +27,10 @@
 //  - with few touched experts (small batches) there are too few slices to
 //    keep HBM busy, so K is split over the grid's z dimension: the splits
 //    write fp32 partial sums and a reduction kernel forms h or y, adding them
-//    in split order; and the grid has one row per expert that can have rows,
-//    each row finding its expert among the non-empty ones.
+//    in split order (up to 32 pairs the down kernel forms h itself, and the
+//    layer's finalize may add y's partial sums instead); and the grid has one
+//    row per expert that can have rows, each row finding its expert among the
+//    non-empty ones.
 // MFMA v_mfma_f32_16x16x32_bf16: lane l supplies A row l%16 / B column l%16,
 // K block l/16 (8 values); the result lane l holds rows 4*(l/16)+r of column
 // l%16.
