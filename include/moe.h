@@ -25,7 +25,8 @@
  * Calling conventions (all entry points):
  *  - Array arguments are DEVICE pointers owned by the caller (for example
  *    torch tensors' data_ptr()), row-major and contiguous, 16-byte aligned.
- *    The library allocates no memory and keeps no global state.
+ *    The library allocates no memory and keeps no global state, except the
+ *    device scratch area of moe_forward_noalloc (below).
  *  - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on
  *    it and the call returns without synchronising the host, so a whole
  *    forward pass can be captured into a hipGraph.
@@ -221,6 +222,36 @@ moe_status moe_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
                        const moe_expert_weights* w, int32_t out_dtype, void* out, float* out_f32,
                        int32_t logits_dtype, void* logits, int32_t* topk_ids, float* topk_w,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------ whole layer, no allocation
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * layer as moe_forward (same kernels, bit-identical results), with the
+ * workspace taken from a scratch area the library holds in device memory:
+ * MOE_NOALLOC_SCRATCH_BYTES on every device the library runs on, held until
+ * the process ends. The call allocates nothing (no hipMalloc, no library
+ * routine that allocates) and needs no workspace argument; the device is the
+ * one `stream` belongs to (the current device for the null stream). The
+ * scratch area's address on a device is looked up on the first call on that
+ * device.
+ *  - Limit: calls whose moe_forward_workspace_size exceeds
+ *    MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE_TOO_SMALL and enqueue
+ *    nothing (64 MiB covers the Beam decode layer, H = 5120, E = 256, k = 8,
+ *    up to T = 128 tokens for I <= 2560 in every weight format; use
+ *    moe_forward with a workspace beyond that).
+ *  - Every call on one device shares that device's scratch area, and each
+ *    call overwrites what the last one left there: calls that overlap on one
+ *    device (for example on two streams, or from two host threads without
+ *    ordering) race and give undefined results. Calls ordered on one stream
+ *    are safe.
+ *  - Arguments and errors as moe_forward; MOE_ERR_LAUNCH also when the scratch
+ *    area cannot be located on the device. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_forward_noalloc(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I,
+                               int32_t E, int32_t k, const float* w_router, const float* bias,
+                               const moe_expert_weights* w, int32_t out_dtype, void* out,
+                               float* out_f32, int32_t logits_dtype, void* logits,
+                               int32_t* topk_ids, float* topk_w, void* stream);
 
 /* ------------------------------------------------------------ measurement
  * Not a step of the layer: the HBM read ceiling its bandwidth-bound kernels

@@ -27,7 +27,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
 ENTRY_POINTS = ("moe_status_string", "moe_route_workspace_size", "moe_route",
                 "moe_permute_workspace_size", "moe_permute", "moe_experts_workspace_size",
                 "moe_experts", "moe_experts_rows16", "moe_finalize", "moe_finalize_rows16",
-                "moe_finalize_norm", "moe_forward_workspace_size", "moe_forward", "moe_hbm_read")
+                "moe_finalize_norm", "moe_forward_workspace_size", "moe_forward", "moe_forward_noalloc",
+                "moe_hbm_read")
 
 
 class MoEError(RuntimeError):
@@ -76,6 +77,9 @@ def load_library(path: str = LIB_PATH):
         "moe_forward": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp,
                                ctypes.POINTER(CExpertWeights), _i32, _vp, _vp, _i32, _vp, _vp, _vp,
                                _vp, _sz, _vp]),
+        "moe_forward_noalloc": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp,
+                                       ctypes.POINTER(CExpertWeights), _i32, _vp, _vp, _i32, _vp,
+                                       _vp, _vp, _vp]),
         "moe_hbm_read": (_i32, [_vp, _sz, _vp, _vp]),
     }
     for name, (res, args) in sig.items():
@@ -238,6 +242,24 @@ def moe_forward(x, w_router, bias, w: ExpertWeights, I: int, k: int, out, worksp
         _ptr(x), _dt(x), T, H, I, E, k, _ptr(w_router), _ptr(bias), ctypes.byref(s), _dt(out),
         _ptr(out), _ptr(out_f32), logits_dtype, _ptr(logits), _ptr(topk_ids), _ptr(topk_w),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def moe_forward_noalloc(x, w_router, bias, w: ExpertWeights, I: int, k: int, out, out_f32=None,
+                        logits_dtype: Optional[int] = None, logits=None, topk_ids=None, topk_w=None,
+                        stream=None):
+    """moe_forward on the library's own scratch area (no workspace argument, no allocation)."""
+    T, H = x.shape
+    E = w_router.shape[1]
+    if logits_dtype is None:
+        logits_dtype = _dt(x)
+    s = w.c_struct()
+    _check("moe_forward_noalloc", _lib.moe_forward_noalloc(
+        _ptr(x), _dt(x), T, H, I, E, k, _ptr(w_router), _ptr(bias), ctypes.byref(s), _dt(out),
+        _ptr(out), _ptr(out_f32), logits_dtype, _ptr(logits), _ptr(topk_ids), _ptr(topk_w),
+        _stream(stream)))
 
 
 # ---------------------------------------------------------------- device plumbing

@@ -17,7 +17,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["abi.cpp", "router.hip", "permute.hip", "expert_stream.hip", "expert_tile.hip", "expert_f32.hip",
            "finalize.hip",
-           "finalize_norm.hip", "hbm_read.hip"]
+           "finalize_norm.hip", "hbm_read.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

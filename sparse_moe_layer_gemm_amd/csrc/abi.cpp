@@ -300,6 +300,91 @@ moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H,
 
 }  // namespace
 
+namespace moe {
+
+// Every check moe_forward makes except those on its workspace argument.
+moe_status check_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I,
+                         int32_t E, int32_t k, const float* w_router, const float* bias,
+                         const moe_expert_weights* w, int32_t out_dtype, const void* out,
+                         const float* out_f32, int32_t logits_dtype, const void* logits,
+                         const int32_t* topk_ids, const float* topk_w) {
+  moe_status s = check_shape(T, H, E, k);
+  if (s != MOE_OK) return s;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  if (logits_dtype != MOE_F32 && logits_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  if (logits_dtype == MOE_F32 && x_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  s = check_weights(w, x_dtype, H, I);
+  if (s != MOE_OK) return s;
+  s = check_tile_plan(w, T, k, E, H, I);
+  if (s != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(w_router) || !ok_or_null(bias) || !aligned16(out) ||
+      !ok_or_null(out_f32) || !ok_or_null(logits) || !ok_or_null(topk_ids) || !ok_or_null(topk_w))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return MOE_OK;
+}
+
+// The layer's kernels on one stream (arguments checked by check_forward, T > 0,
+// workspace of at least moe_forward_workspace_size bytes, 16-byte aligned).
+moe_status enqueue_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I,
+                           int32_t E, int32_t k, const float* w_router, const float* bias,
+                           const moe_expert_weights* w, int32_t out_dtype, void* out,
+                           float* out_f32, int32_t logits_dtype, void* logits, int32_t* topk_ids,
+                           float* topk_w, void* workspace, size_t workspace_bytes, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t P = (size_t)T * k;
+  Carver c{static_cast<char*>(workspace), workspace_bytes};
+  void* route_ws = c.take(route_ws_bytes(T, H, E));
+  void* lbuf = c.take((size_t)T * E * sizeof(float));
+  int32_t* ids = static_cast<int32_t*>(c.take(P * sizeof(int32_t)));
+  float* tw = static_cast<float*>(c.take(P * sizeof(float)));
+  int32_t* counts = static_cast<int32_t*>(c.take(E * sizeof(int32_t)));
+  int32_t* offsets = static_cast<int32_t*>(c.take((E + 1) * sizeof(int32_t)));
+  int32_t* sorted_pair = static_cast<int32_t*>(c.take(P * sizeof(int32_t)));
+  int32_t* pair_pos = static_cast<int32_t*>(c.take(P * sizeof(int32_t)));
+  float* y_sorted = static_cast<float*>(c.take(P * H * sizeof(float)));
+  void* exp_ws = c.take(experts_ws_bytes(T, H, I, E, k, w));
+  void* perm_ws = c.take(moe::permute_ws_bytes((long long)P, E));
+  if (topk_ids) ids = topk_ids;
+  if (topk_w) tw = topk_w;
+  if (!logits) logits = lbuf;
+
+  // one token: the select kernel also writes the permute (a sort of k distinct ids)
+  const moe::PermuteOut perm{counts, offsets, sorted_pair, pair_pos};
+  moe_status s = enqueue_route(x, x_dtype, T, H, w_router, bias, E, k, logits_dtype, logits,
+                               nullptr, ids, tw, route_ws, st, T == 1 ? &perm : nullptr);
+  if (s != MOE_OK) return s;
+  if (T != 1) {
+    s = launch_status(
+        moe::launch_permute(ids, (int)P, E, counts, offsets, sorted_pair, pair_pos, perm_ws, st));
+    if (s != MOE_OK) return s;
+  }
+  if (rows16_supported(w, (int64_t)P, E)) {
+    // compact rows in the fp32 rows' space: P*H*2 + P*H/64 bytes
+    uint16_t* y16 = reinterpret_cast<uint16_t*>(y_sorted);
+    uint8_t* y16_scale = reinterpret_cast<uint8_t*>(y16 + align_up(P * H * sizeof(uint16_t)) / 2);
+    s = enqueue_experts(x, x_dtype, T, H, I, E, k, offsets, sorted_pair, w, nullptr, exp_ws, st,
+                        y16, y16_scale);
+    if (s != MOE_OK) return s;
+    return launch_status(moe::launch_finalize_rows16(y16, y16_scale, pair_pos, tw, (int)T, k, H,
+                                                     out_dtype == MOE_BF16, out, out_f32, st));
+  }
+  KeptPartials kept;
+  s = enqueue_experts(x, x_dtype, T, H, I, E, k, offsets, sorted_pair, w, y_sorted, exp_ws, st,
+                      nullptr, nullptr, &kept);
+  if (s != MOE_OK) return s;
+  if (kept.S > 1)  // small batches: the down GEMM's split reduction folded into the finalize
+    return launch_status(moe::launch_finalize_split(kept.part, kept.S, kept.stride, pair_pos, tw,
+                                                    (int)T, k, H, out_dtype == MOE_BF16, out,
+                                                    out_f32, st));
+  return launch_status(moe::launch_finalize(y_sorted, pair_pos, tw, (int)T, k, H,
+                                            out_dtype == MOE_BF16, out, out_f32, st));
+}
+
+}  // namespace moe
+
 extern "C" {
 
 const char* moe_status_string(int32_t s) {
@@ -494,73 +579,15 @@ moe_status moe_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
                        const moe_expert_weights* w, int32_t out_dtype, void* out, float* out_f32,
                        int32_t logits_dtype, void* logits, int32_t* topk_ids, float* topk_w,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  moe_status s = check_shape(T, H, E, k);
-  if (s != MOE_OK) return s;
-  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
-  if (logits_dtype != MOE_F32 && logits_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
-  if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
-  if (logits_dtype == MOE_F32 && x_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
-  s = check_weights(w, x_dtype, H, I);
-  if (s != MOE_OK) return s;
-  s = check_tile_plan(w, T, k, E, H, I);
-  if (s != MOE_OK) return s;
-  if (T == 0) return MOE_OK;
-  if (!x || !w_router || !out || !workspace) return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned16(x) || !aligned16(w_router) || !ok_or_null(bias) || !aligned16(out) ||
-      !ok_or_null(out_f32) || !ok_or_null(logits) || !ok_or_null(topk_ids) ||
-      !ok_or_null(topk_w) || !aligned16(workspace))
-    return MOE_ERR_INVALID_ARGUMENT;
+  moe_status s = moe::check_forward(x, x_dtype, T, H, I, E, k, w_router, bias, w, out_dtype, out,
+                                    out_f32, logits_dtype, logits, topk_ids, topk_w);
+  if (s != MOE_OK || T == 0) return s;
+  if (!workspace || !aligned16(workspace)) return MOE_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < moe_forward_workspace_size(T, H, I, E, k, w))
     return MOE_ERR_WORKSPACE_TOO_SMALL;
-
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const size_t P = (size_t)T * k;
-  Carver c{static_cast<char*>(workspace), workspace_bytes};
-  void* route_ws = c.take(route_ws_bytes(T, H, E));
-  void* lbuf = c.take((size_t)T * E * sizeof(float));
-  int32_t* ids = static_cast<int32_t*>(c.take(P * sizeof(int32_t)));
-  float* tw = static_cast<float*>(c.take(P * sizeof(float)));
-  int32_t* counts = static_cast<int32_t*>(c.take(E * sizeof(int32_t)));
-  int32_t* offsets = static_cast<int32_t*>(c.take((E + 1) * sizeof(int32_t)));
-  int32_t* sorted_pair = static_cast<int32_t*>(c.take(P * sizeof(int32_t)));
-  int32_t* pair_pos = static_cast<int32_t*>(c.take(P * sizeof(int32_t)));
-  float* y_sorted = static_cast<float*>(c.take(P * H * sizeof(float)));
-  void* exp_ws = c.take(experts_ws_bytes(T, H, I, E, k, w));
-  void* perm_ws = c.take(moe::permute_ws_bytes((long long)P, E));
-  if (topk_ids) ids = topk_ids;
-  if (topk_w) tw = topk_w;
-  if (!logits) logits = lbuf;
-
-  // one token: the select kernel also writes the permute (a sort of k distinct ids)
-  const moe::PermuteOut perm{counts, offsets, sorted_pair, pair_pos};
-  s = enqueue_route(x, x_dtype, T, H, w_router, bias, E, k, logits_dtype, logits, nullptr, ids, tw,
-                    route_ws, st, T == 1 ? &perm : nullptr);
-  if (s != MOE_OK) return s;
-  if (T != 1) {
-    s = launch_status(
-        moe::launch_permute(ids, (int)P, E, counts, offsets, sorted_pair, pair_pos, perm_ws, st));
-    if (s != MOE_OK) return s;
-  }
-  if (rows16_supported(w, (int64_t)P, E)) {
-    // compact rows in the fp32 rows' space: P*H*2 + P*H/64 bytes
-    uint16_t* y16 = reinterpret_cast<uint16_t*>(y_sorted);
-    uint8_t* y16_scale = reinterpret_cast<uint8_t*>(y16 + align_up(P * H * sizeof(uint16_t)) / 2);
-    s = enqueue_experts(x, x_dtype, T, H, I, E, k, offsets, sorted_pair, w, nullptr, exp_ws, st,
-                        y16, y16_scale);
-    if (s != MOE_OK) return s;
-    return launch_status(moe::launch_finalize_rows16(y16, y16_scale, pair_pos, tw, (int)T, k, H,
-                                                     out_dtype == MOE_BF16, out, out_f32, st));
-  }
-  KeptPartials kept;
-  s = enqueue_experts(x, x_dtype, T, H, I, E, k, offsets, sorted_pair, w, y_sorted, exp_ws, st,
-                      nullptr, nullptr, &kept);
-  if (s != MOE_OK) return s;
-  if (kept.S > 1)  // small batches: the down GEMM's split reduction folded into the finalize
-    return launch_status(moe::launch_finalize_split(kept.part, kept.S, kept.stride, pair_pos, tw,
-                                                    (int)T, k, H, out_dtype == MOE_BF16, out,
-                                                    out_f32, st));
-  return launch_status(moe::launch_finalize(y_sorted, pair_pos, tw, (int)T, k, H,
-                                            out_dtype == MOE_BF16, out, out_f32, st));
+  return moe::enqueue_forward(x, x_dtype, T, H, I, E, k, w_router, bias, w, out_dtype, out, out_f32,
+                              logits_dtype, logits, topk_ids, topk_w, workspace, workspace_bytes,
+                              stream);
 }
 
 // ---------------------------------------------------------------- measurement

@@ -5,7 +5,24 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "moe.h"
+
 namespace moe {
+
+// ---------------------------------------------------------------- whole layer (abi.cpp)
+// Every check moe_forward makes on its arguments except those on the workspace.
+moe_status check_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I,
+                         int32_t E, int32_t k, const float* w_router, const float* bias,
+                         const moe_expert_weights* w, int32_t out_dtype, const void* out,
+                         const float* out_f32, int32_t logits_dtype, const void* logits,
+                         const int32_t* topk_ids, const float* topk_w);
+// Enqueues the layer (arguments already checked, T > 0, a 16-byte aligned
+// workspace of at least moe_forward_workspace_size bytes).
+moe_status enqueue_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I,
+                           int32_t E, int32_t k, const float* w_router, const float* bias,
+                           const moe_expert_weights* w, int32_t out_dtype, void* out,
+                           float* out_f32, int32_t logits_dtype, void* logits, int32_t* topk_ids,
+                           float* topk_w, void* workspace, size_t workspace_bytes, void* stream);
 
 // ---------------------------------------------------------------- vector types
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -243,8 +243,49 @@ def test_forward_validation():
     assert forward(out=None) == INVAL
     assert forward(ids=MIS) == INVAL
     assert forward(ws_bytes=1024) == WS_SMALL
+    assert forward(ws=None) == INVAL
+    assert forward(ws=MIS) == INVAL
     assert forward(w=_w(dtype=3, gus=G, dns=Hh, gug=J, dng=None)) == INVAL
     assert forward(w=_w(dtype=3, gus=G, dns=Hh, gug=J, dng=J), x_dt=0, l_dt=0) == UNSUP
+
+
+def forward_noalloc(w=None, **kw):
+    w = w if w is not None else _w()
+    a = dict(x=A, x_dt=1, T=128, H=5120, I=1536, E=256, k=8, wr=B, bias=None, w=ctypes.byref(w),
+             out_dt=1, out=C, out_f32=None, l_dt=1, logits=None, ids=None, tw=None, stream=None)
+    a.update(kw)
+    return moe.load_library().moe_forward_noalloc(*a.values())
+
+
+def test_forward_noalloc_validation():
+    """Every rejection happens on the host, before the scratch area is looked up."""
+    assert forward_noalloc(T=0, x=None, wr=None, out=None) == OK
+    assert forward_noalloc(k=9) == UNSUP
+    assert forward_noalloc(E=4, k=8) == INVAL
+    assert forward_noalloc(out=None) == INVAL
+    assert forward_noalloc(x=MIS) == INVAL
+    assert forward_noalloc(ids=MIS) == INVAL
+    assert forward_noalloc(w=_w(dtype=3, gus=G, dns=Hh, gug=J, dng=None)) == INVAL
+    # beyond the scratch area: a prefill-sized call is rejected with a clear status
+    assert forward_noalloc(T=16384) == WS_SMALL
+    assert forward_noalloc(T=512, I=2560) == WS_SMALL
+
+
+def test_forward_noalloc_limit_covers_decode():
+    """64 MiB holds the whole decode layer's workspace up to T = 128 (I <= 2560, every
+    weight format), and the limit is exactly where moe_forward's workspace exceeds it."""
+    lib = moe.load_library()
+    cap = moe.NOALLOC_SCRATCH_BYTES
+    for w in (_w(), _w(dtype=2, gus=G, dns=Hh), _w(dtype=3, gus=G, dns=Hh, gug=J, dng=J),
+              _w(dtype=3, gus=G, dns=Hh, gug=J, dng=J, qmode=1)):
+        for I in (1536, 2560):
+            for T in (1, 2, 8, 32, 128):
+                assert lib.moe_forward_workspace_size(T, 5120, I, 256, 8, ctypes.byref(w)) <= cap
+    w = _w()
+    T = 128
+    while lib.moe_forward_workspace_size(T, 5120, 1536, 256, 8, ctypes.byref(w)) <= cap:
+        T += 1
+    assert forward_noalloc(T=T) == WS_SMALL
 
 
 def test_forward_workspace_covers_stages():
