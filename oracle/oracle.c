@@ -331,14 +331,15 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
 
 /* One routed expert applied to one token, as a SwiGLU FFN:
    a = x_t W_gu[e] (length 2I), h = silu(a[0:I]) * a[I:2I], y = h W_d[e]
-   (length H). Sums run over ascending K; no intermediate rounding. */
-static void expert_ffn(int x_dt, const void* x, int64_t t, const weights* W, int e, double* a,
-                       double* row, double* y, double* h_out) {
-  int64_t H = W->H, I = W->I;
+   (length H). Sums run over ascending K; no intermediate rounding. The
+   expert's weights come decoded (gu [H][2I] and dn [I][H], the values
+   gate_up_row and down_row give). */
+static void expert_ffn(int x_dt, const void* x, int64_t t, int64_t H, int64_t I, const double* gu,
+                       const double* dn, double* a, double* y, double* h_out) {
   for (int64_t n = 0; n < 2 * I; ++n) a[n] = 0.0;
   for (int64_t h = 0; h < H; ++h) {
     double xv = x_value(x_dt, x, t * H + h);
-    gate_up_row(W, e, (int)h, row);
+    const double* row = gu + h * 2 * I;
     for (int64_t n = 0; n < 2 * I; ++n) a[n] += xv * row[n];
   }
   for (int64_t i = 0; i < I; ++i) a[i] = silu(a[i]) * a[I + i];
@@ -346,9 +347,32 @@ static void expert_ffn(int x_dt, const void* x, int64_t t, const weights* W, int
     for (int64_t i = 0; i < I; ++i) h_out[i] = a[i];
   for (int64_t n = 0; n < H; ++n) y[n] = 0.0;
   for (int64_t i = 0; i < I; ++i) {
-    down_row(W, e, (int)i, row);
+    const double* row = dn + i * H;
     for (int64_t n = 0; n < H; ++n) y[n] += a[i] * row[n];
   }
+}
+
+/* Row indices grouped by expert: order[start[e] .. start[e + 1]) are the rows
+   of expert e, ascending. */
+static int group_rows(int64_t n, const int32_t* experts, int32_t E, int64_t** order_out,
+                      int64_t** start_out) {
+  int64_t* start = (int64_t*)calloc((size_t)E + 1, sizeof(int64_t));
+  int64_t* order = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n + 1));
+  int64_t* cur = (int64_t*)malloc(sizeof(int64_t) * (size_t)E);
+  if (!start || !order || !cur) {
+    free(start);
+    free(order);
+    free(cur);
+    return ORACLE_ENOMEM;
+  }
+  for (int64_t r = 0; r < n; ++r) start[experts[r] + 1]++;
+  for (int e = 0; e < E; ++e) start[e + 1] += start[e];
+  for (int e = 0; e < E; ++e) cur[e] = start[e];
+  for (int64_t r = 0; r < n; ++r) order[cur[experts[r]]++] = r;
+  free(cur);
+  *order_out = order;
+  *start_out = start;
+  return ORACLE_OK;
 }
 
 static int make_weights(weights* W, int w_dt, int32_t H, int32_t I, const void* gate_up,
@@ -372,6 +396,10 @@ static int make_weights(weights* W, int w_dt, int32_t H, int32_t I, const void* 
   return ORACLE_OK;
 }
 
+static int expert_rows_grouped(int mode, int x_dt, const void* x, const weights* W, int32_t E,
+                               const int32_t* tokens, const int32_t* experts, const double* h_in,
+                               int64_t n, double* y, double* h_out, double* hq_out);
+
 /* y[r] = FFN_{experts[r]}(x[tokens[r]]) for n (token, expert) rows;
    optionally also the SwiGLU activations h[r] (length I). */
 int oracle_expert_rows(int x_dt, const void* x, int64_t T, int32_t H, int32_t I, int32_t E,
@@ -386,25 +414,7 @@ int oracle_expert_rows(int x_dt, const void* x, int64_t T, int32_t H, int32_t I,
   if (!x || !tokens || !experts || !y) return ORACLE_EINVAL;
   for (int64_t r = 0; r < n; ++r)
     if (tokens[r] < 0 || tokens[r] >= T || experts[r] < 0 || experts[r] >= E) return ORACLE_EINVAL;
-  int err = ORACLE_OK;
-#pragma omp parallel
-  {
-    int64_t wmax = 2 * (int64_t)I > H ? 2 * (int64_t)I : H;
-    double* a = (double*)malloc(sizeof(double) * 2 * (size_t)I);
-    double* row = (double*)malloc(sizeof(double) * (size_t)wmax);
-    if (!a || !row) {
-#pragma omp atomic write
-      err = ORACLE_ENOMEM;
-    } else {
-#pragma omp for schedule(dynamic, 1)
-      for (int64_t r = 0; r < n; ++r)
-        expert_ffn(x_dt, x, tokens[r], &W, experts[r], a, row, y + r * H,
-                   h_out ? h_out + r * I : NULL);
-    }
-    free(a);
-    free(row);
-  }
-  return err;
+  return expert_rows_grouped(0, x_dt, x, &W, E, tokens, experts, NULL, n, y, h_out, NULL);
 }
 
 /* ------------------------------------------------------------------ fp8-MFMA mode */
@@ -452,8 +462,9 @@ static float quantize_x_row(const uint16_t* xr, int64_t H, double* xq) {
 
 /* The down stage of F8 mode for one row: h (bf16 values, length I) quantised
    per 128-column block (hq = q * 2^e, length I), then y = hq W_d[e] times the
-   column scales. */
-static void down_f8(const weights* W, int e, const double* h, double* hq, double* y) {
+   column scales. dn8 [H][I]: expert e's down weights as w8_value gives them. */
+static void down_f8(const weights* W, int e, const double* dn8, const double* h, double* hq,
+                    double* y) {
   int64_t H = W->H, I = W->I;
   for (int64_t b0 = 0; b0 < I; b0 += 128) {
     int64_t b1 = b0 + 128 < I ? b0 + 128 : I;
@@ -463,30 +474,115 @@ static void down_f8(const weights* W, int e, const double* h, double* hq, double
     for (int64_t i = b0; i < b1; ++i) hq[i] = ldexp(q_e4m3(ldexp(h[i], -eb)), eb);
   }
   for (int64_t n = 0; n < H; ++n) {
+    const double* wr = dn8 + n * I;
     double acc = 0.0;
-    for (int64_t i = 0; i < I; ++i) acc += hq[i] * w8_value(W->dt, W->down, W->down_scale, H, I, e, n, i);
+    for (int64_t i = 0; i < I; ++i) acc += hq[i] * wr[i];
     y[n] = acc * w8_scale(W->dt, W->down_scale, W->down_gscale, H, e, n);
   }
 }
 
-/* One expert on one token in F8 mode; h_out (bf16-rounded h) and hq_out (the
-   dequantised codes q * 2^e) are optional. */
-static void expert_ffn_f8(const void* x, int64_t t, const weights* W, int e, double* a,
-                          double* xq, double* y, double* h_out, double* hq_out) {
+/* One expert on one token in F8 mode; gu8 [2I][H]: expert e's gate/up weights
+   as w8_value gives them. h_out (bf16-rounded h) and hq_out (the dequantised
+   codes q * 2^e) are optional. */
+static void expert_ffn_f8(const void* x, int64_t t, const weights* W, int e, const double* gu8,
+                          const double* dn8, double* a, double* xq, double* y, double* h_out,
+                          double* hq_out) {
   int64_t H = W->H, I = W->I, N1 = 2 * I;
   float s_t = quantize_x_row((const uint16_t*)x + t * H, H, xq);
   for (int64_t n = 0; n < N1; ++n) {
+    const double* wr = gu8 + n * H;
     double acc = 0.0;
-    for (int64_t h = 0; h < H; ++h)
-      acc += xq[h] * w8_value(W->dt, W->gate_up, W->gate_up_scale, N1, H, e, n, h);
+    for (int64_t h = 0; h < H; ++h) acc += xq[h] * wr[h];
     a[n] = acc * (double)s_t * w8_scale(W->dt, W->gate_up_scale, W->gate_up_gscale, N1, e, n);
   }
   for (int64_t i = 0; i < I; ++i) a[i] = round_bf16(silu(a[i]) * a[I + i]);
   if (h_out)
     for (int64_t i = 0; i < I; ++i) h_out[i] = a[i];
-  down_f8(W, e, a, a + I, y);
+  down_f8(W, e, dn8, a, a + I, y);
   if (hq_out)
     for (int64_t i = 0; i < I; ++i) hq_out[i] = a[I + i];
+}
+
+/* Expert e's weights decoded into dense doubles, once per expert and call.
+   mode 0 (weights dequantised exactly): gu [H][2I] and dn [I][H], the values
+   gate_up_row and down_row give. Modes 1 and 2 (F8): gu [2I][H] and dn [H][I],
+   the values w8_value gives (mode 2 needs dn only). A work-shared loop of the
+   enclosing parallel region (each ends with a barrier). */
+static void decode_expert(int mode, const weights* W, int e, double* gu, double* dn) {
+  int64_t H = W->H, I = W->I, N1 = 2 * I;
+  if (mode == 0) {
+#pragma omp for schedule(static)
+    for (int64_t h = 0; h < H; ++h) gate_up_row(W, e, (int)h, gu + h * N1);
+#pragma omp for schedule(static)
+    for (int64_t i = 0; i < I; ++i) down_row(W, e, (int)i, dn + i * H);
+    return;
+  }
+  if (mode == 1) {
+#pragma omp for schedule(static)
+    for (int64_t n = 0; n < N1; ++n)
+      for (int64_t h = 0; h < H; ++h)
+        gu[n * H + h] = w8_value(W->dt, W->gate_up, W->gate_up_scale, N1, H, e, n, h);
+  }
+#pragma omp for schedule(static)
+  for (int64_t n = 0; n < H; ++n)
+    for (int64_t i = 0; i < I; ++i) dn[n * I + i] = w8_value(W->dt, W->down, W->down_scale, H, I, e, n, i);
+}
+
+/* The expert rows of one call, grouped by expert so that each expert's
+   weights are decoded once (decode_expert), then its rows computed one by one
+   in parallel. mode 0: FFN with exactly dequantised weights (h_out: h);
+   1: F8-mode FFN (h_out: bf16-rounded h, hq_out: dequantised h codes);
+   2: F8-mode down stage on the given h rows h_in [n, I]. */
+static int expert_rows_grouped(int mode, int x_dt, const void* x, const weights* W, int32_t E,
+                               const int32_t* tokens, const int32_t* experts, const double* h_in,
+                               int64_t n, double* y, double* h_out, double* hq_out) {
+  int64_t H = W->H, I = W->I;
+  int64_t *order = NULL, *start = NULL;
+  int rc = group_rows(n, experts, E, &order, &start);
+  if (rc) return rc;
+  double* gu = mode == 2 ? NULL : (double*)malloc(sizeof(double) * (size_t)(H * 2 * I));
+  double* dn = (double*)malloc(sizeof(double) * (size_t)(H * I));
+  if ((mode != 2 && !gu) || !dn) {
+    free(gu);
+    free(dn);
+    free(order);
+    free(start);
+    return ORACLE_ENOMEM;
+  }
+  int err = ORACLE_OK;
+#pragma omp parallel
+  {
+    double* a = (double*)malloc(sizeof(double) * 2 * (size_t)I);
+    double* xq = (double*)malloc(sizeof(double) * (size_t)H);
+    const int bad = !a || !xq;
+    if (bad) {
+#pragma omp atomic write
+      err = ORACLE_ENOMEM;
+    }
+    for (int e = 0; e < E; ++e) {
+      if (start[e] == start[e + 1]) continue;  /* the same decision in every thread */
+      decode_expert(mode, W, e, gu, dn);
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t q = start[e]; q < start[e + 1]; ++q) {
+        if (bad) continue;
+        int64_t r = order[q];
+        if (mode == 0)
+          expert_ffn(x_dt, x, tokens[r], H, I, gu, dn, a, y + r * H, h_out ? h_out + r * I : NULL);
+        else if (mode == 1)
+          expert_ffn_f8(x, tokens[r], W, e, gu, dn, a, xq, y + r * H,
+                        h_out ? h_out + r * I : NULL, hq_out ? hq_out + r * I : NULL);
+        else
+          down_f8(W, e, dn, h_in + r * I, a, y + r * H);
+      }
+    }
+    free(a);
+    free(xq);
+  }
+  free(gu);
+  free(dn);
+  free(order);
+  free(start);
+  return err;
 }
 
 /* y[r] for n (token, expert) rows as oracle_expert_rows, in F8 mode (bf16 x,
@@ -504,24 +600,7 @@ int oracle_expert_rows_f8(const void* x, int64_t T, int32_t H, int32_t I, int32_
   if (!x || !tokens || !experts || !y) return ORACLE_EINVAL;
   for (int64_t r = 0; r < n; ++r)
     if (tokens[r] < 0 || tokens[r] >= T || experts[r] < 0 || experts[r] >= E) return ORACLE_EINVAL;
-  int err = ORACLE_OK;
-#pragma omp parallel
-  {
-    double* a = (double*)malloc(sizeof(double) * 2 * (size_t)I);
-    double* xq = (double*)malloc(sizeof(double) * (size_t)H);
-    if (!a || !xq) {
-#pragma omp atomic write
-      err = ORACLE_ENOMEM;
-    } else {
-#pragma omp for schedule(dynamic, 1)
-      for (int64_t r = 0; r < n; ++r)
-        expert_ffn_f8(x, tokens[r], &W, experts[r], a, xq, y + r * H, h_out ? h_out + r * I : NULL,
-                      hq_out ? hq_out + r * I : NULL);
-    }
-    free(a);
-    free(xq);
-  }
-  return err;
+  return expert_rows_grouped(1, ODT_BF16, x, &W, E, tokens, experts, NULL, n, y, h_out, hq_out);
 }
 
 /* The F8 down stage alone on given h rows (bf16 values [n, I]) of the given
@@ -539,20 +618,7 @@ int oracle_down_rows_f8(int32_t H, int32_t I, int32_t E, int w_dt, const void* g
   if (!experts || !h || !y) return ORACLE_EINVAL;
   for (int64_t r = 0; r < n; ++r)
     if (experts[r] < 0 || experts[r] >= E) return ORACLE_EINVAL;
-  int err = ORACLE_OK;
-#pragma omp parallel
-  {
-    double* hq = (double*)malloc(sizeof(double) * (size_t)I);
-    if (!hq) {
-#pragma omp atomic write
-      err = ORACLE_ENOMEM;
-    } else {
-#pragma omp for schedule(dynamic, 1)
-      for (int64_t r = 0; r < n; ++r) down_f8(&W, experts[r], h + r * I, hq, y + r * H);
-    }
-    free(hq);
-  }
-  return err;
+  return expert_rows_grouped(2, ODT_BF16, NULL, &W, E, NULL, experts, h, n, y, NULL, NULL);
 }
 
 /* Activation quantisation alone, for the GPU's quantised x: values and scales. */
