@@ -126,8 +126,10 @@ moe_status moe_route(const void* x, int32_t x_dtype, int64_t T, int32_t H, const
  * e; offsets = exclusive prefix sum of counts (E + 1 entries, offsets[E] =
  * T*k); sorted_pair[r] = the r-th pair in (expert, p) order; pair_pos is its
  * inverse (pair_pos[sorted_pair[r]] = r). Results are deterministic.
- * Ids outside [0, E) are not counted and not written (the outputs are then
- * incomplete; the router never produces them). Up to 16384 pairs no
+ * Ids outside [0, E) are not counted (the router never produces them): such
+ * a pair gets pair_pos = -1, offsets[E] is then the number of valid pairs,
+ * and sorted_pair[r] = -1 for r >= offsets[E]; moe_experts computes no row
+ * for it and the finalize calls add nothing for it. Up to 16384 pairs no
  * workspace is needed (NULL allowed); above, moe_permute_workspace_size()
  * bytes of scratch hold per-segment histograms. */
 size_t moe_permute_workspace_size(int64_t T, int32_t k, int32_t E);
@@ -184,7 +186,9 @@ moe_status moe_finalize_rows16(const uint16_t* y16, const uint8_t* y16_scale,
  * MoE finalize (step 5), the weighted un-permute:
  *   out[t] = sum_{j=0..k-1} topk_w[t, j] * y_sorted[pair_pos[t*k + j]]
  * accumulated in fp32 in slot order j = 0..k-1, emitted as out_dtype (bf16:
- * round to nearest even). out_f32 [T, H] (nullable) receives the fp32 sums. */
+ * round to nearest even). out_f32 [T, H] (nullable) receives the fp32 sums.
+ * A slot whose pair_pos is negative (a pair moe_permute left without a row)
+ * adds nothing; every other pair_pos must be a row of y_sorted. */
 moe_status moe_finalize(const float* y_sorted, const int32_t* pair_pos, const float* topk_w,
                         int64_t T, int32_t k, int32_t H, int32_t out_dtype, void* out,
                         float* out_f32, void* stream);
@@ -202,13 +206,21 @@ moe_status moe_finalize(const float* y_sorted, const int32_t* pair_pos, const fl
  *                              * gamma_next)
  * all in fp32 (row sums in a fixed order: deterministic). residual,
  * residual_out, normed: [T, H] bf16; gamma_post, gamma_next: [H] bf16;
- * eps >= 0 and finite. residual_out may equal residual (in-place update);
- * normed must not overlap either. H a multiple of 64 and at most 16384,
- * else MOE_ERR_UNSUPPORTED; errors as for moe_finalize. */
+ * eps >= 0 and finite. residual_out may equal residual (in-place update),
+ * else the two must not overlap; normed must not overlap either (overlapping
+ * [T, H] ranges return MOE_ERR_INVALID_ARGUMENT). H a multiple of 64 and at
+ * most 16384, else MOE_ERR_UNSUPPORTED; errors as for moe_finalize.
+ * moe_finalize_norm_rows16: the same over compact rows (y16, y16_scale as
+ * moe_experts_rows16 writes them; each value decoded exactly). */
 moe_status moe_finalize_norm(const float* y_sorted, const int32_t* pair_pos, const float* topk_w,
                              int64_t T, int32_t k, int32_t H, const void* residual,
                              const void* gamma_post, const void* gamma_next, float eps,
                              void* residual_out, void* normed, void* stream);
+moe_status moe_finalize_norm_rows16(const uint16_t* y16, const uint8_t* y16_scale,
+                                    const int32_t* pair_pos, const float* topk_w, int64_t T,
+                                    int32_t k, int32_t H, const void* residual,
+                                    const void* gamma_post, const void* gamma_next, float eps,
+                                    void* residual_out, void* normed, void* stream);
 
 /* ------------------------------------------------------------ whole layer
  * The five steps in order on one stream: route, permute, experts, finalize
@@ -222,6 +234,26 @@ moe_status moe_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
                        const moe_expert_weights* w, int32_t out_dtype, void* out, float* out_f32,
                        int32_t logits_dtype, void* logits, int32_t* topk_ids, float* topk_w,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------ whole layer + sandwich norms
+ * The layer ending in the fused finalize + norms of moe_finalize_norm (vLLM PR
+ * #61978, Status table row #62366 fuses MoE finalize with Beam's sandwich
+ * norms): route, permute, experts, then, per token, residual_out =
+ * RNE_bf16(residual + RMSNorm(m) * gamma_post) and normed = the next
+ * sublayer's RMSNorm of residual_out, m being the fp32 finalize sum (never
+ * rounded). The expert rows are those moe_forward uses (compact rows on the
+ * tiled kernels), so the fused step reads the rows as the plain finalize
+ * does. x [T, H] bf16 (bf16, FP8 or NVFP4 expert weights); residual,
+ * residual_out, normed [T, H] bf16 and gamma_post, gamma_next [H] bf16 as for
+ * moe_finalize_norm (H <= 16384); logits (bf16), topk_ids, topk_w optional;
+ * workspace of moe_forward_workspace_size() bytes; errors as moe_forward and
+ * moe_finalize_norm. */
+moe_status moe_forward_norm(const void* x, int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                            const float* w_router, const float* bias, const moe_expert_weights* w,
+                            const void* residual, const void* gamma_post, const void* gamma_next,
+                            float eps, void* residual_out, void* normed, void* logits,
+                            int32_t* topk_ids, float* topk_w, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------ whole layer, no allocation
  * For callers that cannot allocate device memory: code under HIP graph

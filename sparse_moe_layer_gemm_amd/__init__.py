@@ -27,7 +27,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
 ENTRY_POINTS = ("moe_status_string", "moe_route_workspace_size", "moe_route",
                 "moe_permute_workspace_size", "moe_permute", "moe_experts_workspace_size",
                 "moe_experts", "moe_experts_rows16", "moe_finalize", "moe_finalize_rows16",
-                "moe_finalize_norm", "moe_forward_workspace_size", "moe_forward", "moe_forward_noalloc",
+                "moe_finalize_norm", "moe_finalize_norm_rows16", "moe_forward_workspace_size",
+                "moe_forward", "moe_forward_norm", "moe_forward_noalloc",
                 "moe_hbm_read")
 
 
@@ -73,6 +74,11 @@ def load_library(path: str = LIB_PATH):
         "moe_finalize_rows16": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
         "moe_finalize_norm": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp, ctypes.c_float,
                                      _vp, _vp, _vp]),
+        "moe_finalize_norm_rows16": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp,
+                                            ctypes.c_float, _vp, _vp, _vp]),
+        "moe_forward_norm": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp,
+                                    ctypes.POINTER(CExpertWeights), _vp, _vp, _vp, ctypes.c_float,
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
         "moe_forward_workspace_size": (_sz, [_i64, _i32, _i32, _i32, _i32, ctypes.POINTER(CExpertWeights)]),
         "moe_forward": (_i32, [_vp, _i32, _i64, _i32, _i32, _i32, _i32, _vp, _vp,
                                ctypes.POINTER(CExpertWeights), _i32, _vp, _vp, _i32, _vp, _vp, _vp,
@@ -225,6 +231,20 @@ def moe_finalize_norm(y_sorted, pair_pos, topk_w, residual, gamma_post, gamma_ne
         _ptr(gamma_next), float(eps), _ptr(residual_out), _ptr(normed), _stream(stream)))
 
 
+def moe_finalize_norm_rows16(y16, y16_scale, pair_pos, topk_w, residual, gamma_post, gamma_next,
+                             eps: float, residual_out, normed, stream=None):
+    """moe_finalize_norm over compact rows (y16 [T*k, H] fp16 bits, y16_scale [T*k, H/64])."""
+    T, k = topk_w.shape
+    H = y16.shape[1]
+    for t in (residual, gamma_post, gamma_next, residual_out, normed):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("moe_finalize_norm_rows16 takes bf16 residual, norm weights and outputs")
+    _check("moe_finalize_norm_rows16", _lib.moe_finalize_norm_rows16(
+        _ptr(y16), _ptr(y16_scale), _ptr(pair_pos), _ptr(topk_w), T, k, H, _ptr(residual),
+        _ptr(gamma_post), _ptr(gamma_next), float(eps), _ptr(residual_out), _ptr(normed),
+        _stream(stream)))
+
+
 def moe_forward_workspace_size(T: int, H: int, I: int, E: int, k: int, w: ExpertWeights) -> int:
     s = w.c_struct()
     return _lib.moe_forward_workspace_size(T, H, I, E, k, ctypes.byref(s))
@@ -242,6 +262,23 @@ def moe_forward(x, w_router, bias, w: ExpertWeights, I: int, k: int, out, worksp
         _ptr(x), _dt(x), T, H, I, E, k, _ptr(w_router), _ptr(bias), ctypes.byref(s), _dt(out),
         _ptr(out), _ptr(out_f32), logits_dtype, _ptr(logits), _ptr(topk_ids), _ptr(topk_w),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_forward_norm(x, w_router, bias, w: ExpertWeights, I: int, k: int, residual, gamma_post,
+                     gamma_next, eps: float, residual_out, normed, workspace, logits=None,
+                     topk_ids=None, topk_w=None, stream=None):
+    """The layer ending in the fused finalize + sandwich norms (bf16 x, residual and outputs)."""
+    T, H = x.shape
+    E = w_router.shape[1]
+    for t in (x, residual, gamma_post, gamma_next, residual_out, normed):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("moe_forward_norm takes bf16 x, residual, norm weights and outputs")
+    s = w.c_struct()
+    _check("moe_forward_norm", _lib.moe_forward_norm(
+        _ptr(x), T, H, I, E, k, _ptr(w_router), _ptr(bias), ctypes.byref(s), _ptr(residual),
+        _ptr(gamma_post), _ptr(gamma_next), float(eps), _ptr(residual_out), _ptr(normed),
+        _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES

@@ -33,6 +33,32 @@ struct Carver {
 
 moe_status launch_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
 
+// Whether the byte ranges [a, a + n) and [b, b + n) intersect.
+bool overlaps(const void* a, const void* b, size_t n) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + n && y < x + n;
+}
+
+// Arguments of the norms fused with finalize (T > 0): bf16 residual, outputs
+// and norm weights, 16-byte aligned; normed must not overlap the residual or
+// residual_out, and residual_out is either residual itself or disjoint from it.
+moe_status check_norm_args(int64_t T, int32_t H, const void* residual, const void* gamma_post,
+                           const void* gamma_next, float eps, const void* residual_out,
+                           const void* normed) {
+  if (!(eps >= 0.f) || eps > 3.4e38f) return MOE_ERR_INVALID_ARGUMENT;  // NaN or inf
+  if (!residual || !gamma_post || !gamma_next || !residual_out || !normed)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(residual) || !aligned16(gamma_post) || !aligned16(gamma_next) ||
+      !aligned16(residual_out) || !aligned16(normed))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const size_t row_bytes = (size_t)T * H * sizeof(uint16_t);
+  if (overlaps(normed, residual, row_bytes) || overlaps(normed, residual_out, row_bytes))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (residual_out != residual && overlaps(residual_out, residual, row_bytes))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return MOE_OK;
+}
+
 // -------------------------------------------------------------- shared checks
 // Sizes common to every call. T == 0 is valid (no-op).
 moe_status check_shape(int64_t T, int32_t H, int32_t E, int32_t k) {
@@ -282,6 +308,7 @@ moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H,
       // the down kernel forms h from the gate/up partial sums; its own partial
       // sums go after them
       a.keep_partials = true;
+      d.h_out = h;  // the down kernel stores the h it forms
       d.hpart = part;
       d.hsplit = sg.ksplit;
       d.hpart_stride = a.part_stride;
@@ -332,7 +359,8 @@ moe_status enqueue_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H,
                            int32_t E, int32_t k, const float* w_router, const float* bias,
                            const moe_expert_weights* w, int32_t out_dtype, void* out,
                            float* out_f32, int32_t logits_dtype, void* logits, int32_t* topk_ids,
-                           float* topk_w, void* workspace, size_t workspace_bytes, void* stream) {
+                           float* topk_w, void* workspace, size_t workspace_bytes, void* stream,
+                           const NormArgs* norm) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const size_t P = (size_t)T * k;
   Carver c{static_cast<char*>(workspace), workspace_bytes};
@@ -368,13 +396,22 @@ moe_status enqueue_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H,
     s = enqueue_experts(x, x_dtype, T, H, I, E, k, offsets, sorted_pair, w, nullptr, exp_ws, st,
                         y16, y16_scale);
     if (s != MOE_OK) return s;
+    if (norm)
+      return launch_status(moe::launch_finalize_norm_rows16(
+          y16, y16_scale, pair_pos, tw, (int)T, k, H, norm->residual, norm->gamma_post,
+          norm->gamma_next, norm->eps, norm->residual_out, norm->normed, st));
     return launch_status(moe::launch_finalize_rows16(y16, y16_scale, pair_pos, tw, (int)T, k, H,
                                                      out_dtype == MOE_BF16, out, out_f32, st));
   }
   KeptPartials kept;
   s = enqueue_experts(x, x_dtype, T, H, I, E, k, offsets, sorted_pair, w, y_sorted, exp_ws, st,
-                      nullptr, nullptr, &kept);
+                      nullptr, nullptr, norm ? nullptr : &kept);
   if (s != MOE_OK) return s;
+  if (norm)  // fp32 rows (a split-K down GEMM reduces them first)
+    return launch_status(moe::launch_finalize_norm(y_sorted, pair_pos, tw, (int)T, k, H,
+                                                   norm->residual, norm->gamma_post,
+                                                   norm->gamma_next, norm->eps,
+                                                   norm->residual_out, norm->normed, st));
   if (kept.S > 1)  // small batches: the down GEMM's split reduction folded into the finalize
     return launch_status(moe::launch_finalize_split(kept.part, kept.S, kept.stride, pair_pos, tw,
                                                     (int)T, k, H, out_dtype == MOE_BF16, out,
@@ -547,16 +584,35 @@ moe_status moe_finalize_norm(const float* y_sorted, const int32_t* pair_pos, con
   if (k > 8 || H % 64 != 0 || H > kMaxNormH) return MOE_ERR_UNSUPPORTED;
   if (T * k > kMaxPairs || T >= kMaxTokens) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
-  if (!y_sorted || !pair_pos || !topk_w || !residual || !gamma_post || !gamma_next ||
-      !residual_out || !normed)
+  if (!y_sorted || !pair_pos || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(y_sorted) || !aligned16(pair_pos) || !aligned16(topk_w))
     return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned16(y_sorted) || !aligned16(pair_pos) || !aligned16(topk_w) || !aligned16(residual) ||
-      !aligned16(gamma_post) || !aligned16(gamma_next) || !aligned16(residual_out) ||
-      !aligned16(normed))
-    return MOE_ERR_INVALID_ARGUMENT;
-  if (normed == residual_out || normed == residual) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status s = check_norm_args(T, H, residual, gamma_post, gamma_next, eps, residual_out, normed);
+  if (s != MOE_OK) return s;
   return launch_status(moe::launch_finalize_norm(
       y_sorted, pair_pos, topk_w, (int)T, k, H, static_cast<const uint16_t*>(residual),
+      static_cast<const uint16_t*>(gamma_post), static_cast<const uint16_t*>(gamma_next), eps,
+      static_cast<uint16_t*>(residual_out), static_cast<uint16_t*>(normed),
+      static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_finalize_norm_rows16(const uint16_t* y16, const uint8_t* y16_scale,
+                                    const int32_t* pair_pos, const float* topk_w, int64_t T,
+                                    int32_t k, int32_t H, const void* residual,
+                                    const void* gamma_post, const void* gamma_next, float eps,
+                                    void* residual_out, void* normed, void* stream) {
+  if (T < 0 || k <= 0 || H <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (!(eps >= 0.f) || eps > 3.4e38f) return MOE_ERR_INVALID_ARGUMENT;  // NaN or inf
+  if (k > 8 || H % 64 != 0 || H > kMaxNormH) return MOE_ERR_UNSUPPORTED;
+  if (T * k > kMaxPairs || T >= kMaxTokens) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!y16 || !y16_scale || !pair_pos || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(y16) || !aligned16(y16_scale) || !aligned16(pair_pos) || !aligned16(topk_w))
+    return MOE_ERR_INVALID_ARGUMENT;
+  moe_status s = check_norm_args(T, H, residual, gamma_post, gamma_next, eps, residual_out, normed);
+  if (s != MOE_OK) return s;
+  return launch_status(moe::launch_finalize_norm_rows16(
+      y16, y16_scale, pair_pos, topk_w, (int)T, k, H, static_cast<const uint16_t*>(residual),
       static_cast<const uint16_t*>(gamma_post), static_cast<const uint16_t*>(gamma_next), eps,
       static_cast<uint16_t*>(residual_out), static_cast<uint16_t*>(normed),
       static_cast<hipStream_t>(stream)));
@@ -588,6 +644,33 @@ moe_status moe_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
   return moe::enqueue_forward(x, x_dtype, T, H, I, E, k, w_router, bias, w, out_dtype, out, out_f32,
                               logits_dtype, logits, topk_ids, topk_w, workspace, workspace_bytes,
                               stream);
+}
+
+moe_status moe_forward_norm(const void* x, int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                            const float* w_router, const float* bias, const moe_expert_weights* w,
+                            const void* residual, const void* gamma_post, const void* gamma_next,
+                            float eps, void* residual_out, void* normed, void* logits,
+                            int32_t* topk_ids, float* topk_w, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  // the layer's output is consumed by the norms: residual_out stands in for
+  // `out` in the common checks (bf16, required)
+  moe_status s = moe::check_forward(x, MOE_BF16, T, H, I, E, k, w_router, bias, w, MOE_BF16,
+                                    residual_out, nullptr, MOE_BF16, logits, topk_ids, topk_w);
+  if (s != MOE_OK) return s;
+  if (H > kMaxNormH) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  s = check_norm_args(T, H, residual, gamma_post, gamma_next, eps, residual_out, normed);
+  if (s != MOE_OK) return s;
+  if (!workspace || !aligned16(workspace)) return MOE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < moe_forward_workspace_size(T, H, I, E, k, w))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const moe::NormArgs norm{static_cast<const uint16_t*>(residual),
+                           static_cast<const uint16_t*>(gamma_post),
+                           static_cast<const uint16_t*>(gamma_next), eps,
+                           static_cast<uint16_t*>(residual_out), static_cast<uint16_t*>(normed)};
+  return moe::enqueue_forward(x, MOE_BF16, T, H, I, E, k, w_router, bias, w, MOE_BF16, nullptr,
+                              nullptr, MOE_BF16, logits, topk_ids, topk_w, workspace,
+                              workspace_bytes, stream, &norm);
 }
 
 // ---------------------------------------------------------------- measurement

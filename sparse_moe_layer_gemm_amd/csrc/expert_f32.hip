@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void f32_gate_up_kernel(const float* __restric
                                                           float* __restrict__ h) {
   const int r = blockIdx.x;
   const int i = blockIdx.y * 256 + threadIdx.x;
-  if (i >= I) return;
+  if (i >= I || r >= offsets[E]) return;  // rows past the last expert's end have no pair
   const int e = expert_of_row(offsets, E, r);
   const float* xr = x + (size_t)(sorted_pair[r] / k) * H;
   const float* wg = w + (size_t)e * H * 2 * I + i;
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void f32_down_kernel(const float* __restrict__
                                                        float* __restrict__ y) {
   const int r = blockIdx.x;
   const int n = blockIdx.y * 256 + threadIdx.x;
-  if (n >= H) return;
+  if (n >= H || r >= offsets[E]) return;
   const int e = expert_of_row(offsets, E, r);
   const float* hr = h + (size_t)r * I;
   const float* wd = w + (size_t)e * I * H + n;

@@ -114,7 +114,8 @@ __device__ __forceinline__ int slot_expert(const int32_t* __restrict__ offsets, 
 // in LDS by the whole workgroup from the gate/up split partial sums before the
 // K loop (h = bf16(silu(sum of gate) * sum of up), splits added in order, as
 // the reduction kernel does), so the gate/up reduction needs no launch of its
-// own. Until that barrier no wavefront leaves early.
+// own; the workgroups of the first column group also write it to h_out. Until
+// that barrier no wavefront leaves early.
 template <bool GATE_UP, bool FOLD = false>
 __global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
   static_assert(!(FOLD && GATE_UP), "h is folded into the down GEMM only");
@@ -172,6 +173,11 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
           }
         pk.x = f32_to_bf16_bits(silu(gs[0]) * us[0]) | (f32_to_bf16_bits(silu(gs[1]) * us[1]) << 16);
         pk.y = f32_to_bf16_bits(silu(gs[2]) * us[2]) | (f32_to_bf16_bits(silu(gs[3]) * us[3]) << 16);
+        // the first column group also stores the h it forms, so that h is in
+        // the workspace as after the reduction kernel (the splits' K ranges
+        // cover every column of h once)
+        if (blockIdx.x == 0 && a.h_out)
+          *reinterpret_cast<uint2*>(a.h_out + (size_t)(r0 + m) * a.I + hc0 + c) = pk;
       }
       *reinterpret_cast<uint2*>(hl + (size_t)m * a.hlds_stride + 2 * c) = pk;
     }

@@ -15,6 +15,21 @@ namespace {
 
 constexpr int FCOLS = 1024;  // columns per workgroup (256 lanes x float4)
 
+// Row positions and weights of token t's k slots (wave-uniform). Slots 8 > j >= k
+// and pairs the permute left without a row (position -1: an expert id outside
+// [0, E)) are not added; their loads read row 0, which always exists.
+__device__ __forceinline__ void slot_rows(const int32_t* __restrict__ pair_pos,
+                                          const float* __restrict__ w, long long t, int k,
+                                          int (&pos)[8], float (&wt)[8], bool (&use)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int p = pair_pos[t * k + (j < k ? j : 0)];
+    use[j] = j < k && p >= 0;
+    pos[j] = use[j] ? p : 0;
+    wt[j] = use[j] ? w[t * k + j] : 0.f;
+  }
+}
+
 template <bool BF16_OUT>
 __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ y,
                                                        const int32_t* __restrict__ pair_pos,
@@ -27,11 +42,8 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
     const int c = (int)(item - t * n_chunks) * FCOLS + threadIdx.x * 4;
     int pos[8];
     float wt[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pos[j] = pair_pos[t * k + (j < k ? j : 0)];
-      wt[j] = (j < k) ? w[t * k + j] : 0.f;
-    }
+    bool use[8];
+    slot_rows(pair_pos, w, t, k, pos, wt, use);
     if (c >= H) continue;
     f32x4 v[8];  // each expert row is read once: nontemporal
 #pragma unroll
@@ -40,7 +52,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (j < k) {
+      if (use[j]) {
         acc.x = fmaf(wt[j], v[j].x, acc.x);
         acc.y = fmaf(wt[j], v[j].y, acc.y);
         acc.z = fmaf(wt[j], v[j].z, acc.z);
@@ -73,11 +85,8 @@ __global__ __launch_bounds__(256) void finalize_rows16_kernel(
     const int c = (int)(item - t * n_chunks) * FCOLS + threadIdx.x * 4;
     int pos[8];
     float wt[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pos[j] = pair_pos[t * k + (j < k ? j : 0)];
-      wt[j] = (j < k) ? w[t * k + j] : 0.f;
-    }
+    bool use[8];
+    slot_rows(pair_pos, w, t, k, pos, wt, use);
     if (c >= H) continue;
     typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
     u32x2v v[8];
@@ -90,7 +99,7 @@ __global__ __launch_bounds__(256) void finalize_rows16_kernel(
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (j < k) {
+      if (use[j]) {
         const int e = (int)sb[j] - 127;
         acc.x = fmaf(wt[j], __builtin_ldexpf(f16_bits_to_f32(v[j].x & 0xffffu), e), acc.x);
         acc.y = fmaf(wt[j], __builtin_ldexpf(f16_bits_to_f32(v[j].x >> 16), e), acc.y);
@@ -132,10 +141,12 @@ __global__ __launch_bounds__(256) void finalize_split_kernel(
     bool use[2];
     const float* src[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {  // slot wave + 4h; invalid ones read slot 0, column 0
+    for (int h = 0; h < 2; ++h) {  // slot wave + 4h; unused ones read row 0, column 0
       const int j = wave + 4 * h;
+      const int p = pair_pos[t * k + (j < k ? j : 0)];
       use[h] = j < k && col_ok;
-      src[h] = part + (size_t)pair_pos[t * k + (j < k ? j : 0)] * H + (col_ok ? c : 0);
+      src[h] = part + (size_t)(p >= 0 ? p : 0) * H + (col_ok ? c : 0);
+      if (p < 0) use[h] = false;  // no row: the slot reads as zeros below
     }
     f32x4 pv[2][kMaxStreamSplit];
 #pragma unroll
@@ -151,6 +162,7 @@ __global__ __launch_bounds__(256) void finalize_split_kernel(
       for (int sp = 1; sp < kMaxStreamSplit; ++sp)
         if (sp < S) v += pv[h][sp];
       if (use[h]) rows[wave + 4 * h][lane] = v;
+      else if (wave + 4 * h < k && col_ok) rows[wave + 4 * h][lane] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     __syncthreads();
     if (wave == 0 && col_ok) {

@@ -9,7 +9,8 @@
 //   r      = RNE_bf16(residual + post)                       the new residual
 //   normed = RNE_bf16(r * (1 / sqrt(mean(r^2) + eps)) * gamma_next)
 //
-// Bound by HBM like the plain finalize (each fp32 expert row is read once).
+// Bound by HBM like the plain finalize (each expert row is read once, as fp32
+// rows or as compact rows: fp16 with a power-of-two scale per 64 columns).
 // Both mean squares need the whole row, so one workgroup of 1024 lanes owns a
 // token (16 wavefronts: enough loads in flight per token even at decode batch
 // sizes): lane l keeps float4 column chunks l, l + 1024, ... of m (and then
@@ -53,11 +54,36 @@ __device__ __forceinline__ uint2 f32x4_to_bf16(float a, float b, float c, float 
   return r;
 }
 
+// Expert rows the kernel reads: fp32 rows, or compact rows (fp16 values with
+// one power-of-two scale byte per row and 64-column block, decoded exactly).
+struct NormRows {
+  const float* y = nullptr;       // [P, H] fp32
+  const uint16_t* y16 = nullptr;  // [P, H] fp16 bits
+  const uint8_t* ysc = nullptr;   // [P, H / 64] scale bytes (2^(b - 127))
+};
+
+// Float4 chunk q (columns 4q .. 4q + 3) of expert row `pos`.
+template <bool R16>
+__device__ __forceinline__ f32x4 load_row4(const NormRows& rows, int pos, int H, int q) {
+  if constexpr (R16) {
+    typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+    const u32x2v v = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x2v*>(rows.y16 + (size_t)pos * H) + q);
+    const int e = (int)rows.ysc[(size_t)pos * (H >> 6) + (q >> 4)] - 127;
+    return f32x4{__builtin_ldexpf(f16_bits_to_f32(v.x & 0xffffu), e),
+                 __builtin_ldexpf(f16_bits_to_f32(v.x >> 16), e),
+                 __builtin_ldexpf(f16_bits_to_f32(v.y & 0xffffu), e),
+                 __builtin_ldexpf(f16_bits_to_f32(v.y >> 16), e)};
+  } else {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(rows.y + (size_t)pos * H) + q);
+  }
+}
+
 // CH float4 chunks per lane: H <= 4096 * CH. residual and residual_out may alias
 // (a lane reads each of its residual chunks before writing the same chunk).
-template <int CH>
+template <int CH, bool R16>
 __global__ __launch_bounds__(FN_THREADS) void finalize_norm_kernel(
-    const float* __restrict__ y, const int32_t* __restrict__ pair_pos, const float* __restrict__ w,
+    NormRows rows, const int32_t* __restrict__ pair_pos, const float* __restrict__ w,
     int k, int H, const uint16_t* residual, const uint16_t* __restrict__ gamma_post,
     const uint16_t* __restrict__ gamma_next, float eps, uint16_t* residual_out,
     uint16_t* __restrict__ normed) {
@@ -65,10 +91,13 @@ __global__ __launch_bounds__(FN_THREADS) void finalize_norm_kernel(
   const long long t = blockIdx.x;
   int pos[8];
   float wt[8];
+  bool use[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {  // wave-uniform: rows past k repeat the first and are not added
-    pos[j] = pair_pos[t * k + (j < k ? j : 0)];
-    wt[j] = (j < k) ? w[t * k + j] : 0.f;
+  for (int j = 0; j < 8; ++j) {  // wave-uniform; slots past k, and pairs without a row
+    const int p = pair_pos[t * k + (j < k ? j : 0)];  // (position -1), read row 0, not added
+    use[j] = j < k && p >= 0;
+    pos[j] = use[j] ? p : 0;
+    wt[j] = use[j] ? w[t * k + j] : 0.f;
   }
   const int n4 = H >> 2;
   float4 m[CH];
@@ -80,11 +109,10 @@ __global__ __launch_bounds__(FN_THREADS) void finalize_norm_kernel(
     if (q < n4) {
       f32x4 v[8];  // each expert row is read once: nontemporal
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + (size_t)pos[j] * H) + q);
+      for (int j = 0; j < 8; ++j) v[j] = load_row4<R16>(rows, pos[j], H, q);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        if (j < k) {
+        if (use[j]) {
           m[c].x = fmaf(wt[j], v[j].x, m[c].x);
           m[c].y = fmaf(wt[j], v[j].y, m[c].y);
           m[c].z = fmaf(wt[j], v[j].z, m[c].z);
@@ -123,13 +151,31 @@ __global__ __launch_bounds__(FN_THREADS) void finalize_norm_kernel(
   }
 }
 
-template <int CH>
-hipError_t launch_ch(const float* y, const int32_t* pp, const float* w, int T, int k, int H,
+template <int CH, bool R16>
+hipError_t launch_ch(const NormRows& rows, const int32_t* pp, const float* w, int T, int k, int H,
                      const uint16_t* res, const uint16_t* gp, const uint16_t* gn, float eps,
                      uint16_t* res_out, uint16_t* normed, hipStream_t st) {
-  finalize_norm_kernel<CH><<<(unsigned)T, FN_THREADS, 0, st>>>(y, pp, w, k, H, res, gp, gn, eps,
-                                                               res_out, normed);
+  finalize_norm_kernel<CH, R16><<<(unsigned)T, FN_THREADS, 0, st>>>(rows, pp, w, k, H, res, gp, gn,
+                                                                    eps, res_out, normed);
   return hipGetLastError();
+}
+
+template <bool R16>
+hipError_t launch_rows(const NormRows& rows, const int32_t* pair_pos, const float* w, int T, int k,
+                       int H, const uint16_t* residual, const uint16_t* gamma_post,
+                       const uint16_t* gamma_next, float eps, uint16_t* residual_out,
+                       uint16_t* normed, hipStream_t st) {
+  const int ch = (H + 4 * FN_THREADS - 1) / (4 * FN_THREADS);
+#define MOE_FN_CASE(n)                                                                          \
+  case n:                                                                                       \
+    return launch_ch<n, R16>(rows, pair_pos, w, T, k, H, residual, gamma_post, gamma_next, eps, \
+                             residual_out, normed, st)
+  switch (ch) {
+    MOE_FN_CASE(1); MOE_FN_CASE(2); MOE_FN_CASE(3); MOE_FN_CASE(4);
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef MOE_FN_CASE
 }
 
 }  // namespace
@@ -138,16 +184,22 @@ hipError_t launch_finalize_norm(const float* y_sorted, const int32_t* pair_pos, 
                                 int T, int k, int H, const uint16_t* residual,
                                 const uint16_t* gamma_post, const uint16_t* gamma_next, float eps,
                                 uint16_t* residual_out, uint16_t* normed, hipStream_t st) {
-  const int ch = (H + 4 * FN_THREADS - 1) / (4 * FN_THREADS);
-#define MOE_FN_CASE(n) \
-  case n:              \
-    return launch_ch<n>(y_sorted, pair_pos, w, T, k, H, residual, gamma_post, gamma_next, eps, residual_out, normed, st)
-  switch (ch) {
-    MOE_FN_CASE(1); MOE_FN_CASE(2); MOE_FN_CASE(3); MOE_FN_CASE(4);
-    default:
-      return hipErrorInvalidValue;
-  }
-#undef MOE_FN_CASE
+  NormRows rows;
+  rows.y = y_sorted;
+  return launch_rows<false>(rows, pair_pos, w, T, k, H, residual, gamma_post, gamma_next, eps,
+                            residual_out, normed, st);
+}
+
+hipError_t launch_finalize_norm_rows16(const uint16_t* y16, const uint8_t* y16_scale,
+                                       const int32_t* pair_pos, const float* w, int T, int k,
+                                       int H, const uint16_t* residual, const uint16_t* gamma_post,
+                                       const uint16_t* gamma_next, float eps,
+                                       uint16_t* residual_out, uint16_t* normed, hipStream_t st) {
+  NormRows rows;
+  rows.y16 = y16;
+  rows.ysc = y16_scale;
+  return launch_rows<true>(rows, pair_pos, w, T, k, H, residual, gamma_post, gamma_next, eps,
+                           residual_out, normed, st);
 }
 
 }  // namespace moe

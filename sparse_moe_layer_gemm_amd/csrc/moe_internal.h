@@ -16,13 +16,26 @@ moe_status check_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, i
                          const moe_expert_weights* w, int32_t out_dtype, const void* out,
                          const float* out_f32, int32_t logits_dtype, const void* logits,
                          const int32_t* topk_ids, const float* topk_w);
+// The layer's last step fused with the sandwich norms (moe_forward_norm):
+// bf16 residual stream, bf16 norm weights, epsilon.
+struct NormArgs {
+  const uint16_t* residual;
+  const uint16_t* gamma_post;
+  const uint16_t* gamma_next;
+  float eps;
+  uint16_t* residual_out;
+  uint16_t* normed;
+};
 // Enqueues the layer (arguments already checked, T > 0, a 16-byte aligned
-// workspace of at least moe_forward_workspace_size bytes).
+// workspace of at least moe_forward_workspace_size bytes). With `norm` the
+// finalize is fused with the norms and writes residual_out and normed instead
+// of out / out_f32.
 moe_status enqueue_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H, int32_t I,
                            int32_t E, int32_t k, const float* w_router, const float* bias,
                            const moe_expert_weights* w, int32_t out_dtype, void* out,
                            float* out_f32, int32_t logits_dtype, void* logits, int32_t* topk_ids,
-                           float* topk_w, void* workspace, size_t workspace_bytes, void* stream);
+                           float* topk_w, void* workspace, size_t workspace_bytes, void* stream,
+                           const NormArgs* norm = nullptr);
 
 // ---------------------------------------------------------------- vector types
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -277,5 +290,11 @@ hipError_t launch_finalize_norm(const float* y_sorted, const int32_t* pair_pos, 
                                 int T, int k, int H, const uint16_t* residual,
                                 const uint16_t* gamma_post, const uint16_t* gamma_next, float eps,
                                 uint16_t* residual_out, uint16_t* normed, hipStream_t st);
+// The same over compact rows (fp16 + per-64-column power-of-two scales).
+hipError_t launch_finalize_norm_rows16(const uint16_t* y16, const uint8_t* y16_scale,
+                                       const int32_t* pair_pos, const float* w, int T, int k,
+                                       int H, const uint16_t* residual, const uint16_t* gamma_post,
+                                       const uint16_t* gamma_next, float eps,
+                                       uint16_t* residual_out, uint16_t* normed, hipStream_t st);
 
 }  // namespace moe

@@ -96,6 +96,9 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
   }
   if (tid == 0) offsets[E] = total;
   __syncthreads();
+  // ids outside [0, E) have no sorted row: the rows past the last expert's
+  // end read -1, and so do those pairs' positions (set in pass 3)
+  for (int r = total + tid; r < P; r += 1024) sorted_pair[r] = -1;
 
   // pass 3: stable scatter
   for (int c = s0; c < s1; c += 64) {
@@ -108,6 +111,8 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
       const int pos = hist[wave][id] + __popcll(peers & below);
       sorted_pair[pos] = p;
       pair_pos[p] = pos;
+    } else if (p < s1) {
+      pair_pos[p] = -1;
     }
     if (valid && lane == 63 - __builtin_clzll(peers)) hist[wave][id] += __popcll(peers);
   }
@@ -234,10 +239,15 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int E, int NV, int32
 __global__ __launch_bounds__(1024) void permute_scatter_kernel(const int32_t* __restrict__ ids,
                                                                int P, int E, int seg, int NV,
                                                                const int32_t* __restrict__ hist_g,
+                                                               const int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ sorted_pair,
                                                                int32_t* __restrict__ pair_pos) {
   __shared__ int hist[PW][256];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // rows past the last expert's end (pairs with ids outside [0, E)) read -1
+  for (long long r = (long long)offsets[E] + (long long)blockIdx.x * 1024 + tid; r < P;
+       r += (long long)gridDim.x * 1024)
+    sorted_pair[r] = -1;
   const int v = blockIdx.x * PW + wave;
   if (v < NV)
     for (int e = lane; e < E; e += 64) hist[wave][e] = hist_g[(size_t)v * E + e];
@@ -259,6 +269,8 @@ __global__ __launch_bounds__(1024) void permute_scatter_kernel(const int32_t* __
         const int pos = hist[wave][id] + __popcll(peers & below);
         sorted_pair[pos] = p;
         pair_pos[p] = pos;
+      } else if (p < s1) {
+        pair_pos[p] = -1;
       }
       if (valid && lane == 63 - __builtin_clzll(peers)) hist[wave][id] += __popcll(peers);
     }
@@ -301,7 +313,8 @@ hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* counts, int
   permute_scan_kernel<<<1, 1024, 0, st>>>(E, nv, hist_g, counts, offsets);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  permute_scatter_kernel<<<blocks, 1024, 0, st>>>(ids, P, E, seg, nv, hist_g, sorted_pair, pair_pos);
+  permute_scatter_kernel<<<blocks, 1024, 0, st>>>(ids, P, E, seg, nv, hist_g, offsets, sorted_pair,
+                                                  pair_pos);
   return hipGetLastError();
 }
 

@@ -225,6 +225,63 @@ def test_finalize_norm_validation():
     assert finalize_norm(k=0) == INVAL
 
 
+# fake addresses far enough apart that [T, H] bf16 rows at them do not overlap
+R1, R2, R3 = 1 << 32, 2 << 32, 3 << 32
+ROWS = 128 * 5120 * 2
+
+
+def test_finalize_norm_rejects_overlapping_outputs():
+    ok = dict(res=R1, res_out=R1, normed=R2)
+    assert finalize_norm(**{**ok, "normed": R1 + ROWS - 16}) == INVAL  # normed inside residual
+    assert finalize_norm(**{**ok, "normed": R1 - ROWS + 16}) == INVAL  # normed ends inside it
+    assert finalize_norm(res=R1, res_out=R2, normed=R2 + 4096) == INVAL  # inside residual_out
+    assert finalize_norm(res=R1, res_out=R1 + 4096, normed=R2) == INVAL  # partial in-place
+
+
+def finalize_norm_rows16(**kw):
+    a = dict(y16=A, ysc=B, pp=C, w=D, T=128, k=8, H=5120, res=R1, gp=F, gn=G, eps=1e-6,
+             res_out=R1, normed=R2, stream=None)
+    a.update(kw)
+    return moe.load_library().moe_finalize_norm_rows16(*a.values())
+
+
+def test_finalize_norm_rows16_validation():
+    assert finalize_norm_rows16(T=0, y16=None, ysc=None, pp=None, w=None, res=None, gp=None,
+                                gn=None, res_out=None, normed=None) == OK
+    assert finalize_norm_rows16(k=9) == UNSUP
+    assert finalize_norm_rows16(H=100) == UNSUP
+    assert finalize_norm_rows16(H=16384 + 64) == UNSUP
+    assert finalize_norm_rows16(eps=float("nan")) == INVAL
+    assert finalize_norm_rows16(y16=None) == INVAL
+    assert finalize_norm_rows16(ysc=MIS) == INVAL
+    assert finalize_norm_rows16(normed=R1 + 64) == INVAL
+    assert finalize_norm_rows16(res_out=R2 + 64) == INVAL
+
+
+def forward_norm(w=None, **kw):
+    w = w if w is not None else _w()
+    a = dict(x=A, T=128, H=5120, I=1536, E=256, k=8, wr=B, bias=None, w=ctypes.byref(w),
+             res=R1, gp=F, gn=G, eps=1e-6, res_out=R1, normed=R2, logits=None, ids=None, tw=None,
+             ws=R3, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return moe.load_library().moe_forward_norm(*a.values())
+
+
+def test_forward_norm_validation():
+    assert forward_norm(T=0, x=None, wr=None, res=None, gp=None, gn=None, res_out=None,
+                        normed=None, ws=None) == OK
+    assert forward_norm(k=9) == UNSUP
+    assert forward_norm(H=16384 + 64) == UNSUP
+    assert forward_norm(w=_w(dtype=0)) == UNSUP  # fp32 experts need fp32 x
+    assert forward_norm(x=None) == INVAL
+    assert forward_norm(res_out=None) == INVAL
+    assert forward_norm(gp=MIS) == INVAL
+    assert forward_norm(eps=-1.0) == INVAL
+    assert forward_norm(normed=R1 + 64) == INVAL
+    assert forward_norm(ws=None) == INVAL
+    assert forward_norm(ws_bytes=1024) == WS_SMALL
+
+
 def forward(w=None, **kw):
     w = w if w is not None else _w()
     a = dict(x=A, x_dt=1, T=128, H=5120, I=1536, E=256, k=8, wr=B, bias=None, w=ctypes.byref(w),
