@@ -15,7 +15,8 @@ import torch
 import sparse_moe_layer_gemm_amd as moe
 import synth
 from tests.gpu_harness import (Layer, bits, check_experts, check_finalize, check_layer,
-                               check_permute, check_router, log, touched_bf16_experts)
+                               check_permute, check_router, forward_norm_vs_stages, log,
+                               touched_bf16_experts)
 
 pytestmark = pytest.mark.gpu
 
@@ -171,6 +172,7 @@ def test_decode_beam_full(decode_layer):
     assert _same_bits(f["out"], r["out"]) and torch.equal(f["out_f32"], r["out_f32"])
     g = L.forward()  # run twice: bit-identical (no atomics, fixed reduction orders)
     assert torch.equal(g["out_f32"], f["out_f32"])
+    forward_norm_vs_stages(L, r)  # the layer ending in the fused finalize + norms
     log(f"  touched experts {int((counts > 0).sum())}, max rows {int(counts.max())}; logits "
         f"{rt['logit_rel_err']:.2e}; ambiguous {rt['ambiguous']}; y {ey:.2e}; out(fp32) "
         f"{lay['out_rel_err']:.2e}; out(bf16) {lay['out_bf16_rel_err']:.2e} (floor {lay['bf16_floor']:.2e})")
@@ -258,28 +260,55 @@ def _sample_rows(counts: np.ndarray, offsets: np.ndarray, n_random: int, seed: i
     return np.array(sorted(rows))
 
 
-def test_prefill_zipf_sampled():
+def _spread_rows(counts: np.ndarray, offsets: np.ndarray, per_expert: int) -> np.ndarray:
+    """Rows of every non-empty expert: up to per_expert evenly spaced ones (its first
+    and last included), plus, for the hottest expert, the rows on each side of every
+    128-row tile boundary and of the 31/32 boundary."""
+    rows = set()
+    for e in np.nonzero(counts)[0]:
+        o0, c = int(offsets[e]), int(counts[e])
+        rows.update((o0 + np.unique(np.linspace(0, c - 1, min(c, per_expert)).astype(np.int64))).tolist())
+    e = int(np.argmax(counts))
+    o0, c = int(offsets[e]), int(counts[e])
+    for b in list(range(128, c, 128)) + [32]:
+        rows.update(o0 + r for r in (b - 1, b) if 0 <= r < c)
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def test_prefill_zipf_wide():
+    """The prefill layer (T = 16384, Zipf load, compact expert rows, the launch the
+    benchmark times): router logits and selection on every token, expert rows of
+    every expert (>= 4096 rows, tile and 31/32 boundaries of the hottest), finalize
+    on every token, 1024 tokens end to end, and the layer ending in the fused
+    finalize + norms on 512 tokens."""
     cfg = synth.CONFIGS["prefill_t16384_zipf"]
     log(f"[parity] {cfg.name}: generating inputs")
     L = Layer(cfg)
     r = L.stages()
-    rng = np.random.default_rng(3)
-    tok = np.sort(rng.choice(cfg.T, 384, replace=False))
-    rt = check_router(L, r, rows=tok)
+    assert "y16" in r  # the prefill layer runs on compact rows, as moe_forward does
+    rt = check_router(L, r)
     counts = check_permute(L, r)
     offsets = r["offsets"].cpu().numpy()
-    rows = _sample_rows(counts, offsets, 160, 4)
+    rows = _spread_rows(counts, offsets, 16)
+    assert len(rows) >= 4096
     ey = check_experts(L, r, rows)
-    check_finalize(L, r, tokens=tok)
-    lay = check_layer(L, r, tok[:40])
+    check_finalize(L, r)
+    rng = np.random.default_rng(3)
+    tok = np.sort(rng.choice(cfg.T, 1024, replace=False))
+    lay = check_layer(L, r, tok)
     f = L.forward()
     assert torch.equal(f["out_f32"], r["out_f32"])
+    forward_norm_vs_stages(L, r, tokens=tok[:512])
     log(f"  load max {int(counts.max())} median {int(np.median(counts))} min {int(counts.min())}; "
-        f"logits {rt['logit_rel_err']:.2e}; y {ey:.2e} over {len(rows)} rows; out {lay['out_rel_err']:.2e}")
+        f"logits {rt['logit_rel_err']:.2e}, ambiguous {rt['ambiguous']} of {rt['tokens']}; "
+        f"y {ey:.2e} over {len(rows)} rows; out over {lay['checked']} tokens: fp32 "
+        f"{lay['out_rel_err']:.3e}, bf16 {lay['out_bf16_rel_err']:.3e} (floor {lay['bf16_floor']:.3e})")
 
 
 # grouped by weight format, so each format's weights are generated once; the
-# decode sizes (T = 1, 2, 128) run the streaming kernels, T = 1 and 2 with K split
+# decode sizes (T = 1, 2, 128) run the streaming kernels, T = 1 and 2 with K
+# split. The NVFP4 layer (T = 4096) is checked end to end on 512 tokens in both
+# modes, the rest on 64.
 @pytest.mark.parametrize("wdt,T,qmode", [("fp4", 4096, "w"), ("fp4", 4096, "f8"), ("fp4", 128, "w"),
                                          ("fp4", 1, "w"), ("fp8", 1024, "w"), ("fp8", 1024, "f8"),
                                          ("fp8", 128, "w"), ("fp8", 2, "w")])
@@ -289,12 +318,65 @@ def test_quantised_beam_sampled(wdt, T, qmode):
     log(f"[parity] {cfg.name}: generating inputs")
     L = Layer(cfg)
     r = L.stages()
+    n_tok = 512 if T == 4096 else min(64, T)
     rng = np.random.default_rng(6)
-    tok = np.sort(rng.choice(cfg.T, min(256, cfg.T), replace=False))
-    check_router(L, r, rows=tok)
+    tok = np.sort(rng.choice(cfg.T, n_tok, replace=False))
+    if T == 4096:
+        check_router(L, r)
+    else:
+        check_router(L, r, rows=tok)
     counts = check_permute(L, r)
-    rows = _sample_rows(counts, r["offsets"].cpu().numpy(), min(64, cfg.T * cfg.k), 7)
+    offsets = r["offsets"].cpu().numpy()
+    rows = (_spread_rows(counts, offsets, 2) if T == 4096
+            else _sample_rows(counts, offsets, min(64, cfg.T * cfg.k), 7))
     ey = check_experts(L, r, rows)
-    check_finalize(L, r, tokens=tok)
-    lay = check_layer(L, r, tok[:16])
-    log(f"  y {ey:.2e} over {len(rows)} rows; out {lay['out_rel_err']:.2e}")
+    check_finalize(L, r, tokens=None if T == 4096 else tok)
+    lay = check_layer(L, r, tok)
+    log(f"  y {ey:.2e} over {len(rows)} rows; out over {lay['checked']} of {lay['tokens']} tokens: "
+        f"fp32 {lay['out_rel_err']:.3e}, bf16 {lay['out_bf16_rel_err']:.3e} "
+        f"(floor {lay['bf16_floor']:.3e}); ambiguous {lay['ambiguous']}"
+        + (f", F8-ambiguous {lay['f8_ambiguous']}" if "f8_ambiguous" in lay else ""))
+
+
+# Ids outside [0, E) (the router never emits them): the permute gives such a pair
+# no row (pair_pos -1, sorted_pair -1 past the last expert's rows) and the
+# finalize adds nothing for it; both permute paths (one workgroup up to 16384
+# pairs, three kernels above).
+@pytest.mark.parametrize("T,k,E", [(100, 4, 16), (5000, 8, 64)])
+def test_permute_and_finalize_skip_invalid_ids(T, k, E):
+    rng = np.random.default_rng(T)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    bad = rng.random((T, k)) < 0.05
+    ids[bad] = np.where(rng.random(int(bad.sum())) < 0.5, -1, E + 3)
+    P = T * k
+    d = torch.from_numpy(ids).cuda()
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    sp = torch.full((P,), 12345, dtype=torch.int32, device="cuda")
+    pp = torch.full((P,), 12345, dtype=torch.int32, device="cuda")
+    log(f"[parity] permute with {int(bad.sum())} invalid ids, P={P}")
+    moe.moe_permute(d, E, counts, offsets, sp, pp)
+    torch.cuda.synchronize()
+    flat = ids.ravel()
+    valid = (flat >= 0) & (flat < E)
+    order = sorted(np.nonzero(valid)[0].tolist(), key=lambda p: (flat[p], p))
+    want_sp = np.full(P, -1, np.int32)
+    want_sp[:len(order)] = order
+    want_pp = np.full(P, -1, np.int32)
+    want_pp[order] = np.arange(len(order))
+    assert np.array_equal(counts.cpu().numpy(), np.bincount(flat[valid], minlength=E))
+    assert int(offsets[-1]) == len(order)
+    assert np.array_equal(sp.cpu().numpy(), want_sp)
+    assert np.array_equal(pp.cpu().numpy(), want_pp)
+    H = 256
+    y = torch.randn((P, H), generator=torch.Generator("cuda").manual_seed(T), device="cuda")
+    w = torch.rand((T, k), generator=torch.Generator("cuda").manual_seed(T + 1), device="cuda")
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    moe.moe_finalize(y, pp, w, out)
+    torch.cuda.synchronize()
+    yh, wh, pph = y.cpu().numpy(), w.cpu().numpy(), pp.cpu().numpy().reshape(T, k)
+    want = np.zeros((T, H), np.float32)
+    for j in range(k):  # slot order, fp32, as the kernel sums
+        use = pph[:, j] >= 0
+        want[use] = np.float32(wh[use, j, None]) * yh[pph[use, j]] + want[use]
+    assert np.allclose(out.cpu().numpy(), want, rtol=1e-6, atol=1e-6)

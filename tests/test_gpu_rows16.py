@@ -76,8 +76,11 @@ def test_rows16_encode_fp32_rows(cfg):
     lay = check_layer(L, r, np.arange(cfg.T))
     f = L.forward()
     assert torch.equal(f["out_f32"], r["out_f32"])
+    out = (f"out {lay['out_rel_err']:.2e}" if "decision_matched_rel_err" not in lay else
+           f"out decision-matched {lay['decision_matched_rel_err']:.2e} over {lay['checked']} tokens, "
+           f"{lay['f8_ambiguous']} F8-ambiguous")
     log(f"[rows16] {cfg.name}: max err/block max {np.max(err / np.maximum(blk_max, 1e-30)):.2e}, "
-        f"finalize {rel:.1e}, out {lay['out_rel_err']:.2e}")
+        f"finalize {rel:.1e}, {out}")
 
 
 def test_rows16_unsupported_for_streaming_sizes():
