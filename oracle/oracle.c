@@ -424,28 +424,35 @@ int oracle_expert_rows(int x_dt, const void* x, int64_t T, int32_t H, int32_t I,
      an all-zero row), computed in fp32 as the kernel does; codes
      RNE_e4m3(x / s_t) with the division in fp32.
    - FP8 weights are used as stored (their per-channel scale multiplies the
-     accumulated sum); NVFP4 weights become E4M3 codes RNE_e4m3(e2m1 * s_blk /
-     8): the exact product scaled by 2^-3, the largest shift any NVFP4 block
-     needs (6 * 448 / 8 = 336 <= 448), so no code saturates; 8 * s_glob
+     accumulated sum). NVFP4 weights become E4M3 codes per 32-deep K block
+     (two 16-value NVFP4 blocks): with sigma the smallest power of two such
+     that 6 * (the larger of the two block scales) <= 448 * 2^sigma (the block
+     exponent below), the codes are RNE_e4m3(e2m1 * s_blk * 2^-sigma), so no
+     code saturates and the products keep E4M3's full precision whatever the
+     scales' range; 2^sigma is the block's scale in the product and s_glob
      multiplies the sum.
    - h = silu(g) * u, rounded to bf16 as in the bf16 path, then per row and
      128-column block a power-of-two scale 2^e (block_exp of the block's amax)
      and codes RNE_e4m3(h * 2^-e).
    - The down GEMM sums each block's code products times its 2^e. */
 
-/* E4M3 value of weight (K index kk, column n) of a quantised matrix, without
-   its per-channel / per-expert scale; q: codes [E, N, K] (fp8) or packed
-   [E, N, K/2] (fp4) with block scales [E, N, K/16]. */
+/* Value of weight (K index kk, column n) of a quantised matrix as the F8 mode
+   uses it, without its per-channel / per-expert scale: the E4M3 code (fp8), or
+   the re-encoded E4M3 code times its 32-block power of two (fp4); q: codes
+   [E, N, K] (fp8) or packed [E, N, K/2] (fp4) with block scales [E, N, K/16]. */
 static double w8_value(int dt, const void* q, const void* sb, int64_t N, int64_t K, int e,
                        int64_t n, int64_t kk) {
   if (dt == ODT_FP8) return e4m3_value(((const uint8_t*)q)[((int64_t)e * N + n) * K + kk]);
   uint8_t byte = ((const uint8_t*)q)[((int64_t)e * N + n) * (K / 2) + kk / 2];
   uint8_t nib = (kk & 1) ? (byte >> 4) : (byte & 15);
-  double s = e4m3_value(((const uint8_t*)sb)[((int64_t)e * N + n) * (K / 16) + kk / 16]);
-  return q_e4m3(e2m1_value(nib) * s / 8.0);
+  const uint8_t* srow = (const uint8_t*)sb + ((int64_t)e * N + n) * (K / 16);
+  double s = e4m3_value(srow[kk / 16]);
+  double s0 = fabs(e4m3_value(srow[(kk / 32) * 2])), s1 = fabs(e4m3_value(srow[(kk / 32) * 2 + 1]));
+  int sigma = block_exp(6.0 * (s0 > s1 ? s0 : s1));
+  return ldexp(q_e4m3(ldexp(e2m1_value(nib) * s, -sigma)), sigma);
 }
 static double w8_scale(int dt, const void* sc, const float* gs, int64_t N, int e, int64_t n) {
-  return dt == ODT_FP8 ? (double)((const float*)sc)[(int64_t)e * N + n] : 8.0 * (double)gs[e];
+  return dt == ODT_FP8 ? (double)((const float*)sc)[(int64_t)e * N + n] : (double)gs[e];
 }
 
 /* Per-token activation quantisation: xq[h] (E4M3 values) and the fp32 scale. */

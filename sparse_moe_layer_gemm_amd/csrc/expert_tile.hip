@@ -943,10 +943,13 @@ __global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
 //    the weight scales in the epilogue, before SwiGLU);
 //  - down A: h as E4M3 codes with one power-of-two (E8M0) scale per row and
 //    128-column block, handed to the MFMA, which applies it exactly;
-//  - B: FP8 weights as stored, or NVFP4 weights re-encoded per value as
-//    RNE_e4m3(e2m1 * s_blk / 8) in registers (the converter gives e2m1 times
-//    the scale's power of two, an fp32 multiply its mantissa factor / 8, and
-//    the hardware f32 -> E4M3 conversion rounds to nearest even).
+//  - B: FP8 weights as stored, or NVFP4 weights re-encoded per 32-deep K
+//    block as RNE_e4m3(e2m1 * s_blk * 2^-s) in registers, s the smallest
+//    integer with 6 * (the larger of the block's two E4M3 scales) <= 448 * 2^s
+//    (the converter gives e2m1 times the scale's power of two, an fp32 multiply
+//    its mantissa factor times 2^-s, and the hardware f32 -> E4M3 conversion
+//    rounds to nearest even); 2^s is the lane's E8M0 B scale in the MFMA, so
+//    the re-encoding is as precise for any range of block scales.
 // Lane half g takes K 32g .. 32g+31 of each 64-deep step for both operands;
 // the scale of a down-GEMM row is the same over the whole step, so the K
 // order inside the step is free.
@@ -987,7 +990,8 @@ __device__ __forceinline__ void vm_wait() {
   else static_assert(N < 0, "add this vmcnt value");
 }
 
-// 8 E2M1 codes (one dword) x block scale (p2 * fm) / 8 -> 8 E4M3 codes (two dwords)
+// 8 E2M1 codes (one dword) x block scale (p2 * fm8: the scale's power of two
+// and its mantissa factor times the block's shift) -> 8 E4M3 codes (two dwords)
 __device__ __forceinline__ void fp4_to_fp8(uint32_t d, float p2, float fm8, int32_t& o0,
                                            int32_t& o1) {
   const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 0);
@@ -1118,23 +1122,28 @@ __global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmAr
   const int l32 = lane & 31, kh = lane >> 5;
   const uint32_t lds0 = (uint32_t)(size_t)(lds_u8*)smem;
   const uint32_t rowb = (uint32_t)(size_t)(lds_u8*)rowdata;
+  // A lane's 32 K values of a 64-deep step: bytes 0-15 of its operand belong
+  // to the MFMA's first 32-value scale block, bytes 16-31 to the second, and
+  // the two lane halves interleave in 16-value runs (measured), so lane half
+  // kh takes K 16 kh .. +16 and 32 + 16 kh .. +16: each scale block is then 32
+  // contiguous K values (two NVFP4 blocks), for A and B alike.
   uint32_t aoff[4][2], boff[4][2], soff[4];
   const uint32_t roff = rowb + 4 * (32 * wm + l32);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 128 * wm + 32 * i + l32;
-    aoff[i][0] = a_off(row, 2 * kh);
-    aoff[i][1] = a_off(row, 2 * kh + 1);
+    aoff[i][0] = a_off(row, kh);
+    aoff[i][1] = a_off(row, kh + 2);
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int c = bcol(j) + l32;
     if (WF == W_FP8) {
-      boff[j][0] = S::A_STAGE + a_off(c, 2 * kh);
-      boff[j][1] = S::A_STAGE + a_off(c, 2 * kh + 1);
-    } else {
-      boff[j][0] = S::A_STAGE + c * 32 + 16 * kh;
-      boff[j][1] = 0;
+      boff[j][0] = S::A_STAGE + a_off(c, kh);
+      boff[j][1] = S::A_STAGE + a_off(c, kh + 2);
+    } else {  // E2M1: 8 B = 16 codes per run
+      boff[j][0] = S::A_STAGE + c * 32 + 8 * kh;
+      boff[j][1] = S::A_STAGE + c * 32 + 16 + 8 * kh;
     }
     soff[j] = S::A_STAGE + S::B_STAGE + c * 4;
   }
@@ -1145,20 +1154,24 @@ __global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmAr
   // copies them while the reads are in flight).
   struct Half {
     u32x4 a[4][2];
-    u32x4 b[2][WF == W_FP8 ? 2 : 1];  // E4M3: two 16 B runs per column tile; E2M1: one
-    uint32_t sc[2];                   // E2M1 block-scale dwords
-    uint32_t as;                      // down: E8M0 scales of the four rows
+    u32x4 b[2][2];     // E4M3: the two 16 B runs per column tile
+    u32x2 q[2][2];     // E2M1: the two 8 B runs per column tile
+    uint32_t sc[2];    // E2M1 block-scale dwords
+    uint32_t as;       // down: E8M0 scales of the four rows
   };
   auto read_half = [&](Half& f, int st, int h, int kt) {
     const uint32_t base = lds0 + st * S::STAGE;
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const int j = 2 * h + jj;
-      f.b[jj][0] = lds_b128(base + boff[j][0]);
-      if constexpr (WF == W_FP8)
+      if constexpr (WF == W_FP8) {
+        f.b[jj][0] = lds_b128(base + boff[j][0]);
         f.b[jj][1] = lds_b128(base + boff[j][1]);
-      else
+      } else {
+        f.q[jj][0] = lds_b64(base + boff[j][0]);
+        f.q[jj][1] = lds_b64(base + boff[j][1]);
         f.sc[jj] = lds_b32(base + soff[j]);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1176,9 +1189,11 @@ __global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmAr
                : "memory")
 #define MOE_F8_WAIT_FP8(f, pending) \
   MOE_F8_WAIT_A(f, pending, "+v"(f.b[0][0]), "+v"(f.b[1][0]), "+v"(f.b[0][1]), "+v"(f.b[1][1]))
-#define MOE_F8_WAIT_FP4(f, pending) \
-  MOE_F8_WAIT_A(f, pending, "+v"(f.b[0][0]), "+v"(f.b[1][0]), "+v"(f.sc[0]), "+v"(f.sc[1]))
-  // reads per half: 12 (gate/up) or 13 (down, with the row scales)
+#define MOE_F8_WAIT_FP4(f, pending)                                                       \
+  MOE_F8_WAIT_A(f, pending, "+v"(f.q[0][0]), "+v"(f.q[0][1]), "+v"(f.q[1][0]), "+v"(f.q[1][1]), \
+                "+v"(f.sc[0]), "+v"(f.sc[1]))
+  // reads per half: E4M3 weights 12 (gate/up) or 13 (down, with the row
+  // scales); E2M1 weights 14 or 15 (at most 15 LDS reads are counted)
   auto wait_half = [&](Half& f) {
     if constexpr (WF == W_FP8) {
       if constexpr (GATE_UP)
@@ -1187,9 +1202,9 @@ __global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmAr
         MOE_F8_WAIT_FP8(f, 13);
     } else {
       if constexpr (GATE_UP)
-        MOE_F8_WAIT_FP4(f, 12);
+        MOE_F8_WAIT_FP4(f, 14);
       else
-        MOE_F8_WAIT_FP4(f, 13);
+        MOE_F8_WAIT_FP4(f, 15);
     }
   };
   auto mfma_half = [&](const Half& f, int h) {
@@ -1201,30 +1216,47 @@ __global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmAr
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       i32x8 bf;
+      int sb = 127;  // E8M0 scale of this lane's 32-deep K block of B
       if constexpr (WF == W_FP8) {
         bf = i32x8{(int)f.b[jj][0][0], (int)f.b[jj][0][1], (int)f.b[jj][0][2], (int)f.b[jj][0][3],
                    (int)f.b[jj][1][0], (int)f.b[jj][1][1], (int)f.b[jj][1][2], (int)f.b[jj][1][3]};
       } else {
-        // dwords 0-1: block 2g of the step, dwords 2-3: block 2g+1
+        // run r (bytes 16 r .. of the operand) holds NVFP4 block kh + 2 r of the
+        // step, in the MFMA's scale block r = K 32 r .. +32 (NVFP4 blocks 2 r,
+        // 2 r + 1). Each scale block gets one shift 2^-s, s the smallest with 6 *
+        // (its larger NVFP4 scale) <= 448 * 2^s, so every product e2m1 * s_blk *
+        // 2^-s lands in E4M3's range with full precision; this lane hands 2^s
+        // of scale block kh to the MFMA (lane l: column l % 32, block l / 32).
+        float p2[4], fm[4];
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          float p2, fm;
-          e4m3_split((f.sc[jj] >> (8 * (2 * kh + blk))) & 0xFFu, p2, fm);
-          const float fm8 = fm * 0.125f;
+        for (int b = 0; b < 4; ++b) e4m3_split((f.sc[jj] >> (8 * b)) & 0xFFu, p2[b], fm[b]);
+        int sig[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const float v = 6.f * fmaxf(p2[2 * r] * fabsf(fm[2 * r]), p2[2 * r + 1] * fabsf(fm[2 * r + 1]));
+          const int ex = __builtin_amdgcn_frexp_expf(v);  // v = m 2^ex, 0.5 <= m < 1
+          sig[r] = v > 0.f ? (2.f * __builtin_amdgcn_frexp_mantf(v) <= 1.75f ? ex - 9 : ex - 8) : 0;
+        }
+        sb = 127 + (kh ? sig[1] : sig[0]);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          // NVFP4 block kh + 2 r (selects, not a lane-dependent register index)
+          const float pb = kh ? p2[2 * r + 1] : p2[2 * r];
+          const float fms = __builtin_ldexpf(kh ? fm[2 * r + 1] : fm[2 * r], -sig[r]);  // exact
           int32_t o0, o1, o2, o3;
-          fp4_to_fp8(f.b[jj][0][2 * blk], p2, fm8, o0, o1);
-          fp4_to_fp8(f.b[jj][0][2 * blk + 1], p2, fm8, o2, o3);
-          bf[4 * blk] = o0;
-          bf[4 * blk + 1] = o1;
-          bf[4 * blk + 2] = o2;
-          bf[4 * blk + 3] = o3;
+          fp4_to_fp8(f.q[jj][r][0], pb, fms, o0, o1);
+          fp4_to_fp8(f.q[jj][r][1], pb, fms, o2, o3);
+          bf[4 * r] = o0;
+          bf[4 * r + 1] = o1;
+          bf[4 * r + 2] = o2;
+          bf[4 * r + 3] = o3;
         }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int sa = GATE_UP ? 127 : (int)((f.as >> (8 * i)) & 0xFFu);
         acc[i][2 * h + jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            af[i], bf, acc[i][2 * h + jj], 0, 0, 0, sa, 0, 127);
+            af[i], bf, acc[i][2 * h + jj], 0, 0, 0, sa, 0, sb);
       }
     }
   };
@@ -1265,7 +1297,7 @@ __global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmAr
   __builtin_amdgcn_s_barrier();
 
   // ---- epilogue (strips reuse the pipeline's LDS; row data lies past it)
-  const float gsc = WF == W_FP4 ? 8.f * a.w_gscale[e] : 1.f;
+  const float gsc = WF == W_FP4 ? a.w_gscale[e] : 1.f;
   const float* chs = WF == W_FP8 ? static_cast<const float*>(a.w_scale) + (size_t)e * N : nullptr;
   auto tile_row = [&](int r) { return 8 * (r >> 2) + 4 * kh + (r & 3); };
   if (GATE_UP) {

@@ -380,3 +380,44 @@ def test_permute_and_finalize_skip_invalid_ids(T, k, E):
         use = pph[:, j] >= 0
         want[use] = np.float32(wh[use, j, None]) * yh[pph[use, j]] + want[use]
     assert np.allclose(out.cpu().numpy(), want, rtol=1e-6, atol=1e-6)
+
+
+def _shift_nvfp4_scales(hw: dict, max_shift: int) -> dict:
+    """The same NVFP4 weights with each matrix's block scales divided by 2^s and its
+    per-expert scales multiplied by 2^s (s the largest shift up to max_shift that
+    keeps every block scale exactly representable): identical dequantised values,
+    block scales far below the 448 the usual recipe gives its largest."""
+    import oracle
+    e4 = oracle.format_op("e4m3", np.arange(256))
+    out = dict(hw)
+    for key, g in (("gate_up_scale", "gate_up_gscale"), ("down_scale", "down_gscale")):
+        for shift in range(max_shift, 0, -1):
+            v = e4[hw[key]] * 2.0 ** -shift
+            codes = synth.encode_e4m3_table(v)
+            if np.array_equal(e4[codes], v):
+                break
+        out[key] = codes
+        out[g] = (hw[g].astype(np.float64) * 2.0 ** shift).astype(np.float32)
+    return out
+
+
+def test_f8_nvfp4_small_block_scales():
+    """NVFP4 weights encoded with small block scales (gate/up <= 2^-3): the
+    fp8-MFMA mode re-encodes each 32-deep K block with its own power of two, so
+    the layer's output is bit-identical to that on the usually scaled encoding
+    of the same weights, and meets the bound against the oracle."""
+    import dataclasses
+    cfg = MC("f8_fp4_small_scales", 141, T=300, H=256, E=8, k=4, I=192, w_dtype="fp4", qmode="f8")
+    hw = synth.gen_experts(cfg)
+    hs = _shift_nvfp4_scales(hw, 12)
+    outs = []
+    for w in (hw, hs):
+        dw = dataclasses.replace(moe.experts_to_device(w), qmode=moe.MOE_QMODE_F8)
+        L = Layer(cfg, weights=(w, dw))
+        outs.append((L, L.stages()))
+    (La, ra), (Lb, rb) = outs
+    assert torch.equal(ra["out_f32"], rb["out_f32"]), "small block scales change the F8 output"
+    check_experts(Lb, rb, np.arange(cfg.T * cfg.k))
+    lay = check_layer(Lb, rb, np.arange(cfg.T))
+    log(f"  small block scales: decision-matched {lay['decision_matched_rel_err']:.3e} over "
+        f"{lay['checked']} tokens")

@@ -107,9 +107,23 @@ def test_f8_gate_up_equals_exact_path_when_lossless(fmt):
     np.testing.assert_allclose(h8, hw_b, rtol=2.0 ** -7, atol=1e-30)
 
 
+def _covering_exponent(m):
+    """Smallest integer e with 448 * 2^e >= m (0 for m = 0), by direct search."""
+    m = np.asarray(m, dtype=np.float64)
+    e = np.where(m > 0, np.floor(np.log2(np.where(m > 0, m, 1.0))) - 9, 0).astype(np.int64)
+    for _ in range(3):  # the estimate is within one or two of the answer
+        e = np.where((m > 0) & (448.0 * np.ldexp(1.0, e) < m), e + 1, e)
+    for _ in range(3):
+        e = np.where((m > 0) & (448.0 * np.ldexp(1.0, e - 1) >= m), e - 1, e)
+    return e
+
+
 def _w8_matrices(q, fmt, E, H, I):
-    """The E4M3 operand values of the F8 mode, built from the format tables:
-    gate/up [E, H, 2I] and down [E, I, H] (K-major rows), and the column scales."""
+    """The operand values of the F8 mode, built from the format tables and the
+    generator's table-driven E4M3 encoder (not the oracle's rounding): gate/up
+    [E, 2I, H] and down [E, H, I] (K-major rows), and the column scales. NVFP4
+    codes are re-encoded per 32-deep K block with the power of two 2^s that
+    covers 6 x the larger of the block's two E4M3 scales."""
     e4 = oracle.format_op("e4m3", np.arange(256))
     e2 = oracle.format_op("e2m1", np.arange(16))
 
@@ -118,9 +132,12 @@ def _w8_matrices(q, fmt, E, H, I):
             return e4[codes.reshape(E, N, K)], scales.astype(np.float64)
         lo, hi = codes & 15, codes >> 4
         nib = np.stack([lo, hi], -1).reshape(E, N, K)
-        blk = np.repeat(e4[scales.reshape(E, N, K // 16)], 16, axis=2)
-        v = oracle.format_op("round_e4m3", e2[nib] * blk / 8.0)
-        return v, 8.0 * np.repeat(gsc.astype(np.float64)[:, None], N, axis=1)
+        sv = e4[scales.reshape(E, N, K // 16)]
+        sig = _covering_exponent(6.0 * np.abs(sv).reshape(E, N, K // 32, 2).max(axis=3))
+        sig = np.repeat(sig, 32, axis=2)
+        prod = e2[nib] * np.repeat(sv, 16, axis=2) * np.ldexp(1.0, -sig)
+        v = e4[synth.encode_e4m3_table(prod)] * np.ldexp(1.0, sig)
+        return v, np.repeat(gsc.astype(np.float64)[:, None], N, axis=1)
 
     gu, sgu = mat(q["gate_up"], q["gate_up_scale"], q.get("gate_up_gscale"), 2 * I, H)
     dn, sdn = mat(q["down"], q["down_scale"], q.get("down_gscale"), H, I)
@@ -165,3 +182,78 @@ def test_f8_error_against_exact_path_is_small():
     yw = oracle.expert_rows(x, q, cfg.I, tok, eid)
     rel = np.abs(y8 - yw).max() / np.sqrt(np.mean(yw ** 2))
     assert 1e-4 < rel < 0.25, rel
+
+
+def test_covering_exponent_matches_block_exp():
+    m = np.concatenate([6.0 * oracle.format_op("e4m3", np.arange(127)), [0.0, 448.0, 449.0, 2688.0]])
+    assert np.array_equal(_covering_exponent(m), oracle.format_op("block_exp", m).astype(np.int64))
+
+
+def _small_scale_copy(q, max_shift):
+    """The same NVFP4 weights with every block scale of a matrix divided by 2^s and
+    its per-expert scales multiplied by 2^s: identical dequantised values (powers
+    of two), block scales far below the 448 the usual recipe gives its largest.
+    s is the largest shift up to max_shift that keeps every scale exactly
+    representable (small scales become E4M3 subnormals)."""
+    e4 = oracle.format_op("e4m3", np.arange(256))
+    out = dict(q)
+    for key, g in (("gate_up_scale", "gate_up_gscale"), ("down_scale", "down_gscale")):
+        for shift in range(max_shift, 0, -1):
+            v = e4[q[key]] * 2.0 ** -shift
+            codes = synth.encode_e4m3_table(v)
+            if np.array_equal(e4[codes], v):
+                break
+        out[key] = codes
+        out[g] = (q[g].astype(np.float64) * 2.0 ** shift).astype(np.float32)
+    return out
+
+
+def test_f8_nvfp4_small_block_scales():
+    """NVFP4 weights whose gate/up block scales are all <= 2^-3 (the usual recipe
+    puts the largest at 448): the exact dequantisation is unchanged, and the F8
+    mode's per-block re-encoding gives the same rows as with the usual scales
+    (the re-encoded products keep full E4M3 precision whatever the scales'
+    range), so its error against the exact path is the same; a fixed shift
+    would not."""
+    cfg = synth.MoEConfig("f8small", 33, T=8, H=256, E=3, k=2, I=256, w_dtype="fp4")
+    q = synth.gen_experts(cfg)
+    qs = _small_scale_copy(q, 12)
+    e4 = oracle.format_op("e4m3", np.arange(256))
+    assert np.abs(e4[qs["gate_up_scale"]]).max() <= 2.0 ** -3
+    x = synth.gen_x(cfg)
+    tok = np.repeat(np.arange(cfg.T), cfg.E)
+    eid = np.tile(np.arange(cfg.E), cfg.T)
+    yw = oracle.expert_rows(x, q, cfg.I, tok, eid)
+    assert np.array_equal(oracle.expert_rows(x, qs, cfg.I, tok, eid), yw)
+    y8 = oracle.expert_rows_f8(x, q, cfg.I, tok, eid)
+    y8s = oracle.expert_rows_f8(x, qs, cfg.I, tok, eid)
+    rms = np.sqrt(np.mean(yw ** 2))
+    eps, eps_s = np.abs(y8 - yw).max() / rms, np.abs(y8s - yw).max() / rms
+    np.testing.assert_allclose(y8s, y8, rtol=0, atol=1e-9 * rms)
+    # a fixed shift of 2^-3 for every block (the largest any NVFP4 block needs)
+    # would push these products into E4M3 subnormals: the gate/up sums on
+    # operands re-encoded that way move far more
+    e4 = oracle.format_op("e4m3", np.arange(256))
+    e2 = oracle.format_op("e2m1", np.arange(16))
+    xq, st = oracle.quantize_x(x)
+
+    def gate_up_sums(qq, fixed):
+        codes = qq["gate_up"]
+        nib = np.stack([codes & 15, codes >> 4], -1).reshape(cfg.E, 2 * cfg.I, cfg.H)
+        sv = np.repeat(e4[qq["gate_up_scale"]], 16, axis=2)
+        if fixed:
+            w8 = e4[synth.encode_e4m3_table(e2[nib] * sv / 8.0)] * 8.0
+        else:
+            w8 = _w8_matrices(qq, "fp4", cfg.E, cfg.H, cfg.I)[0]
+        g = qq["gate_up_gscale"].astype(np.float64)[:, None, None]
+        return np.stack([xq[t] @ (w8[e] * g[e]).T * st[t] for t, e in zip(tok, eid)])
+
+    a_usual = gate_up_sums(q, False)
+    a_small = gate_up_sums(qs, False)
+    a_fixed = gate_up_sums(qs, True)
+    r = np.sqrt(np.mean(a_usual ** 2))
+    d_small = np.abs(a_small - a_usual).max() / r
+    d_fixed = np.abs(a_fixed - a_usual).max() / r
+    print(f"F8 vs exact NVFP4 rows: usual scales {eps:.3e}, scales <= 2^-3 {eps_s:.3e}; gate/up sums "
+          f"moved by the scale change: per-block shift {d_small:.1e}, fixed 2^-3 shift {d_fixed:.1e}")
+    assert d_small < 1e-12 and d_fixed > 1e-2
