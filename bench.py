@@ -9,9 +9,15 @@ routing), bound by streaming the touched experts' weights from HBM; prefill
 against the bf16 MFMA peak, and the NVFP4-weight layer (T=4096) against the
 bound it is closer to (HBM bytes or bf16 MFMA).
 
+Beside the headline line's `roofline` and `cpu_baseline` (the oracle on a
+token sample of the same workload, on the host's cores), the line carries the
+small-batch decode record (T = 1, 8, 32 at I = 1536 and 2560, eager and graph
+replay), the layer ending in the fused finalize + norms (moe_forward_norm), and
+the oracle's rate on prefill and NVFP4 samples.
+
 Prints one JSON line. Options: --gpus N (only 1 is supported), --steps K,
 --warmup W, --workload decode|prefill (headline), --no-prefill, --no-quant,
---no-cpu.
+--no-cpu, --no-small.
 """
 from __future__ import annotations
 
@@ -42,6 +48,8 @@ def parse():
     p.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill line")
     p.add_argument("--no-quant", action="store_true", help="skip the secondary NVFP4 line")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    p.add_argument("--no-small", action="store_true",
+                   help="skip the small-batch decode record (T = 1, 8, 32)")
     p.add_argument("--hbm-probe", action="store_true",
                    help="time a plain 4 GiB device copy (the reference kernel for HBM counters) and exit")
     p.add_argument("--gemm-probe", action="store_true",
@@ -102,6 +110,13 @@ class Workload:
         self.moe.moe_forward(self.x, self.wr, self.bias, self.w, c.I, c.k, self.out, self.ws,
                              logits=self.logits, topk_ids=self.ids, topk_w=self.tw)
 
+    def forward_norm(self):
+        """The layer ending in the fused finalize + sandwich norms (moe_forward_norm)."""
+        c = self.cfg
+        self.moe.moe_forward_norm(self.x, self.wr, self.bias, self.w, c.I, c.k, self.res,
+                                  self.gamma, self.gamma, 1e-6, self.res_out, self.normed,
+                                  self.ws, logits=self.logits, topk_ids=self.ids, topk_w=self.tw)
+
     def stage_calls(self):
         c, m = self.cfg, self.moe
         return [
@@ -116,21 +131,25 @@ class Workload:
             ("finalize", lambda: m.moe_finalize_rows16(self.y16, self.ysc, self.pp, self.tw,
                                                        self.out)
              if self.rows16 else m.moe_finalize(self.y, self.pp, self.tw, self.out)),
-            # not part of the step: the fused finalize + norms on the same rows
-            ("finalize_norm", lambda: m.moe_finalize_norm(self.y, self.pp, self.tw, self.res,
-                                                          self.gamma, self.gamma, 1e-6,
-                                                          self.res_out, self.normed)),
+            # the fused finalize + norms on the same rows (moe_forward_norm's last step)
+            ("finalize_norm", lambda: m.moe_finalize_norm_rows16(
+                self.y16, self.ysc, self.pp, self.tw, self.res, self.gamma, self.gamma, 1e-6,
+                self.res_out, self.normed)
+             if self.rows16 else m.moe_finalize_norm(self.y, self.pp, self.tw, self.res,
+                                                     self.gamma, self.gamma, 1e-6, self.res_out,
+                                                     self.normed)),
         ]
 
-    def time_forward(self, steps, warmup):
+    def time_forward(self, steps, warmup, fn=None):
         torch = self.torch
+        fn = fn or self.forward
         for _ in range(warmup):
-            self.forward()
+            fn()
         torch.cuda.synchronize()
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record()
         for _ in range(steps):
-            self.forward()
+            fn()
         t1.record()
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / steps
@@ -165,8 +184,6 @@ class Workload:
                 raise
             self.rows16 = False
             del self.y16, self.ysc
-        if self.rows16:  # fp32 rows for the fused finalize + norms timing
-            m.moe_experts(self.x, c.I, c.E, c.k, self.offsets, self.sp, self.w, self.y, self.ews)
         for _, f in calls[2:]:
             f()
         torch.cuda.synchronize()
@@ -334,6 +351,85 @@ def hbm_ceiling(torch, moe, nbytes=4 << 30, reps=10):
             "frac_of_peak": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def decode_small(torch, moe, dec, reps=200):
+    """Small-batch decode (H=5120, E=256, k=8): T in {1, 8, 32} at I = 1536 (the decode
+    layer's weights) and I = 2560 (the width the checkpoint sizes imply; only the routed
+    experts' weights are generated, the rest is never read). Per case: moe_forward back to
+    back (events around `reps` calls), and the same call captured once in a HIP graph and
+    replayed back to back; weight GB/s counts the touched experts' bytes."""
+    import synth
+    base = synth.CONFIGS["decode_t128"]
+    E, H, k = base.E, base.H, base.k
+    out = []
+    for I in (base.I, 2560):
+        if I == base.I:
+            dw = dec.w
+        else:
+            x32 = moe.to_device_bf16(dec.x_host[:32])
+            ids = torch.empty((32, k), dtype=torch.int32, device="cuda")
+            tw = torch.empty((32, k), dtype=torch.float32, device="cuda")
+            lg = torch.empty((32, E), dtype=torch.bfloat16, device="cuda")
+            moe.moe_route(x32, dec.wr, None, k, moe.MOE_BF16, lg, None, ids, tw,
+                          moe.workspace(moe.moe_route_workspace_size(32, H, E)))
+            touched = np.unique(ids.cpu().numpy())
+            cfg = base.with_(name="decode_i2560", I=I)
+            sub = synth.gen_experts(cfg, experts=touched)
+            gu = torch.empty((E, H, 2 * I), dtype=torch.bfloat16, device="cuda")
+            dn = torch.empty((E, I, H), dtype=torch.bfloat16, device="cuda")
+            idx = torch.from_numpy(touched).cuda()
+            gu[idx] = moe.to_device_bf16(sub["gate_up"])
+            dn[idx] = moe.to_device_bf16(sub["down"])
+            del sub
+            dw = moe.ExpertWeights(moe.MOE_BF16, gu, dn)
+        for T in (1, 8, 32):
+            cfg = base.with_(name=f"decode_t{T}_i{I}", T=T, I=I)
+            x = moe.to_device_bf16(dec.x_host[:T])
+            o = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+            ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+            ws = moe.workspace(moe.moe_forward_workspace_size(T, H, I, E, k, dw))
+
+            def fwd():
+                moe.moe_forward(x, dec.wr, None, dw, I, k, o, ws, topk_ids=ids)
+            for _ in range(10):
+                fwd()
+            torch.cuda.synchronize()
+            n_touched = int(np.unique(ids.cpu().numpy()).size)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fwd()
+            e1.record()
+            torch.cuda.synchronize()
+            eager_ms = e0.elapsed_time(e1) / reps
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                fwd()
+            torch.cuda.current_stream().wait_stream(side)
+            with torch.cuda.graph(g):
+                fwd()
+            for _ in range(10):
+                g.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            graph_ms = e0.elapsed_time(e1) / reps
+            wbytes = n_touched * expert_bytes(cfg)
+            out.append({"T": T, "I": I, "touched_experts": n_touched,
+                        "ms_per_step": round(eager_ms, 4), "graph_replay_ms": round(graph_ms, 4),
+                        "tokens_per_s": round(T / (graph_ms / 1e3), 1),
+                        "weight_GBps": round(wbytes / (graph_ms / 1e3) / 1e9, 1),
+                        "weight_frac_of_peak_hbm": round(wbytes / (graph_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)})
+            del g
+        if I != base.I:
+            del dw, gu, dn
+    return out
+
+
 def expert_bytes(cfg):
     """Bytes of one expert's weights: gate/up [H, 2I] + down [I, H] (with scales)."""
     n = cfg.H * 2 * cfg.I + cfg.I * cfg.H
@@ -344,14 +440,19 @@ def expert_bytes(cfg):
     return 2 * n
 
 
-def cpu_baseline(wl, budget_s=10.0):
-    """Oracle (fp64, OpenMP) on a bounded sample of the workload's tokens."""
+def cpu_baseline(wl, budget_s=10.0, qmode="w", one_thread=True):
+    """Oracle (fp64, OpenMP) on a bounded sample of the workload's tokens: the whole
+    layer per token (qmode "f8": the oracle's fp8-MFMA-mode layer)."""
     import oracle
     c = wl.cfg
+    sel = c.logits_dtype
+
+    def run(rows):
+        oracle.layer(wl.x_host, wl.wr_host, wl.bias_host, wl.w_host, c.I, c.k, sel, rows=rows,
+                     qmode=qmode)
     n = 8
     t = time.perf_counter()
-    oracle.layer(wl.x_host, wl.wr_host, wl.bias_host, wl.w_host, c.I, c.k, "bf16",
-                 rows=np.arange(n))
+    run(np.arange(n))
     dt = time.perf_counter() - t
     n2 = int(min(c.T, max(n, n * budget_s / max(dt, 1e-3))))
     rows = np.linspace(0, c.T - 1, n2).astype(np.int64)
@@ -359,7 +460,7 @@ def cpu_baseline(wl, budget_s=10.0):
     t = time.perf_counter()
     passes = 0
     while True:
-        oracle.layer(wl.x_host, wl.wr_host, wl.bias_host, wl.w_host, c.I, c.k, "bf16", rows=rows)
+        run(rows)
         passes += 1
         dt = time.perf_counter() - t
         if dt >= budget_s or passes >= 50:
@@ -369,11 +470,13 @@ def cpu_baseline(wl, budget_s=10.0):
     # the same oracle on one thread, over 8 tokens
     one = None
     try:
+        if not one_thread:
+            raise OSError
         gomp = ctypes.CDLL("libgomp.so.1")
         gomp.omp_set_num_threads(1)
         rows1 = rows[:8]
         t = time.perf_counter()
-        oracle.layer(wl.x_host, wl.wr_host, wl.bias_host, wl.w_host, c.I, c.k, "bf16", rows=rows1)
+        run(rows1)
         one = round(rows1.size / (time.perf_counter() - t), 3)
         gomp.omp_set_num_threads(cores)
     except OSError:
@@ -386,7 +489,8 @@ def cpu_baseline(wl, budget_s=10.0):
         pass
     return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{passes} pass(es) over {n2} of the {c.T} {c.name} tokens (whole layer per "
-                      f"token, fp64), {dt:.1f} s",
+                      f"token, fp64{', fp8-MFMA-mode encodings' if qmode == 'f8' else ''}), "
+                      f"{dt:.1f} s",
             "value_1_thread": one,
             "host": {"cpu_model": model, "os_cpu_count": os.cpu_count(),
                      "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}}
@@ -433,6 +537,10 @@ def main():
         }
         dec_line["roofline"]["frac"] = dec_line["roofline"]["achieved"] / HBM_PEAK_GBS
         dec_line["iter_ms"] = dec.iter_spread()
+        dec_line["forward_norm_ms"] = dec.time_forward(a.steps, a.warmup, dec.forward_norm)
+        if not a.no_small:
+            progress("timing small-batch decode (T = 1, 8, 32 at I = 1536 and 2560)")
+            dec_line["decode_small"] = decode_small(torch, moe, dec)
         progress("measuring the HBM read ceiling (4 GiB)")
         ceil = hbm_ceiling(torch, moe)
         ceil["decode_experts_frac_of_ceiling"] = round(
@@ -467,6 +575,10 @@ def main():
         }
         pre_line["roofline"]["frac"] = pre_line["roofline"]["achieved"] / BF16_PEAK_TFLOPS
         pre_line["iter_ms"] = pre.iter_spread(20)
+        pre_line["forward_norm_ms"] = pre.time_forward(psteps, 1, pre.forward_norm)
+        if not a.no_cpu:
+            progress("timing the CPU oracle on a prefill token sample")
+            pre_line["cpu_baseline"] = cpu_baseline(pre, budget_s=8.0, one_thread=False)
 
     q_cfg = synth.CONFIGS["nvfp4_t4096"]
     q_line = None
@@ -494,6 +606,9 @@ def main():
                                "unit": "GB/s" if hbm_frac >= mfma_frac else "TFLOP/s",
                                "frac": max(hbm_frac, mfma_frac), "traffic": None,
                                "weight_GBps": round(tb, 1), "TFLOPs": round(tf, 1)}}
+        if not a.no_cpu:
+            progress("timing the CPU oracle on an NVFP4 token sample")
+            q_line["cpu_baseline"] = cpu_baseline(qw, budget_s=8.0, one_thread=False)
         # the same layer in the fp8-MFMA mode (activations quantised in-kernel)
         progress("timing NVFP4, fp8-MFMA mode")
         import dataclasses
@@ -518,6 +633,10 @@ def main():
                          "unit": "GB/s" if h8 >= m8 else "TFLOP/s",
                          "frac": max(h8, m8), "traffic": None,
                          "weight_GBps": round(tb8, 1), "TFLOPs": round(tf8, 1)}}
+        if not a.no_cpu:
+            progress("timing the CPU oracle (fp8-MFMA mode) on an NVFP4 token sample")
+            q_line["fp8_mfma_mode"]["cpu_baseline"] = cpu_baseline(qw, budget_s=8.0, qmode="f8",
+                                                                   one_thread=False)
         # NVFP4 decode (T=128, exact dequantisation): the streaming kernels on the same weights
         progress("timing NVFP4 decode (T=128)")
         qd_cfg = q_cfg.with_(name="nvfp4_t128", T=128)
@@ -567,6 +686,9 @@ def main():
         line["touched_experts"] = dec_line["touched_experts"]
         line["layer_hbm_frac"] = round(dec_line["layer_hbm_frac"], 4)
         line["hbm_ceiling"] = dec_line["hbm_ceiling"]
+        line["forward_norm_ms"] = round(dec_line["forward_norm_ms"], 4)
+        if "decode_small" in dec_line:
+            line["decode_small"] = dec_line["decode_small"]
         if pre_line is not None:
             line["prefill"] = {"workload": pre_cfg.name, "value": round(pre_line["value"], 1),
                                "unit": "tokens/s", "ms_per_step": round(pre_line["ms_per_step"], 4),
@@ -574,7 +696,9 @@ def main():
                                "roofline": pre_line["roofline"],
                                "stages_ms": {k: round(v, 4) for k, v in pre_line["stages_ms"].items()},
                                "iter_ms": pre_line["iter_ms"],
-                               "expert_load": pre_line["expert_load"]}
+                               "forward_norm_ms": round(pre_line["forward_norm_ms"], 4),
+                               "expert_load": pre_line["expert_load"],
+                               "cpu_baseline": pre_line.get("cpu_baseline")}
         if q_line is not None:
             line["quantised"] = q_line
     else:

@@ -81,10 +81,10 @@ typedef enum moe_dtype {
  *      "reflection/Beam-1.0-501B-A23B", Guide > Variants);
  *  MOE_QMODE_F8 (1): fp8 MFMA: x quantised per token to E4M3 with an fp32
  *      scale (amax / 448), NVFP4 weights re-encoded to E4M3 in registers per
- *      32-deep K block (RNE of e2m1 * s_blk * 2^-s, 2^s the smallest power of
- *      two covering 6 x the larger of the block's two scales / 448, applied as
- *      the MFMA's block scale), h quantised per row and 128-column block to
- *      E4M3 with a power-of-two scale; needs I <= 4096.
+ *      32-deep K block (RNE of e2m1 * s_blk * 2^-s, s = the exponent field of
+ *      the block's larger E4M3 scale - 12, 2^s applied as the MFMA's block
+ *      scale), h quantised per row and 128-column block to E4M3 with a
+ *      power-of-two scale; needs I <= 4096.
  * qmode must be 0 for MOE_F32 / MOE_BF16 weights. */
 typedef enum moe_qmode { MOE_QMODE_W = 0, MOE_QMODE_F8 = 1 } moe_qmode;
 

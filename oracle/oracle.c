@@ -332,23 +332,27 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
 /* One routed expert applied to one token, as a SwiGLU FFN:
    a = x_t W_gu[e] (length 2I), h = silu(a[0:I]) * a[I:2I], y = h W_d[e]
    (length H). Sums run over ascending K; no intermediate rounding. The
-   expert's weights come decoded (gu [H][2I] and dn [I][H], the values
-   gate_up_row and down_row give). */
-static void expert_ffn(int x_dt, const void* x, int64_t t, int64_t H, int64_t I, const double* gu,
-                       const double* dn, double* a, double* y, double* h_out) {
+   expert's weight rows come from gu [H][2I] and dn [I][H] when the caller
+   decoded them, else as stored (gate_up_row / down_row into `row`). */
+static void expert_ffn(int x_dt, const void* x, int64_t t, const weights* W, int e,
+                       const double* gu, const double* dn, double* a, double* row, double* y,
+                       double* h_out) {
+  int64_t H = W->H, I = W->I;
   for (int64_t n = 0; n < 2 * I; ++n) a[n] = 0.0;
   for (int64_t h = 0; h < H; ++h) {
     double xv = x_value(x_dt, x, t * H + h);
-    const double* row = gu + h * 2 * I;
-    for (int64_t n = 0; n < 2 * I; ++n) a[n] += xv * row[n];
+    const double* r = gu ? gu + h * 2 * I : row;
+    if (!gu) gate_up_row(W, e, (int)h, row);
+    for (int64_t n = 0; n < 2 * I; ++n) a[n] += xv * r[n];
   }
   for (int64_t i = 0; i < I; ++i) a[i] = silu(a[i]) * a[I + i];
   if (h_out)
     for (int64_t i = 0; i < I; ++i) h_out[i] = a[i];
   for (int64_t n = 0; n < H; ++n) y[n] = 0.0;
   for (int64_t i = 0; i < I; ++i) {
-    const double* row = dn + i * H;
-    for (int64_t n = 0; n < H; ++n) y[n] += a[i] * row[n];
+    const double* r = dn ? dn + i * H : row;
+    if (!dn) down_row(W, e, (int)i, row);
+    for (int64_t n = 0; n < H; ++n) y[n] += a[i] * r[n];
   }
 }
 
@@ -425,11 +429,13 @@ int oracle_expert_rows(int x_dt, const void* x, int64_t T, int32_t H, int32_t I,
      RNE_e4m3(x / s_t) with the division in fp32.
    - FP8 weights are used as stored (their per-channel scale multiplies the
      accumulated sum). NVFP4 weights become E4M3 codes per 32-deep K block
-     (two 16-value NVFP4 blocks): with sigma the smallest power of two such
-     that 6 * (the larger of the two block scales) <= 448 * 2^sigma (the block
-     exponent below), the codes are RNE_e4m3(e2m1 * s_blk * 2^-sigma), so no
-     code saturates and the products keep E4M3's full precision whatever the
-     scales' range; 2^sigma is the block's scale in the product and s_glob
+     (two 16-value NVFP4 blocks): with e the exponent field (0..15) of the
+     larger of the two E4M3 block scales (0 for a zero or subnormal scale) and
+     sigma = e - 12, the codes are RNE_e4m3(e2m1 * s_blk * 2^-sigma). Every
+     scale of the block is below 2^(e - 6) (2^-6 if subnormal), so the products
+     stay below 6 * 2^6 = 384 <= 448 and never saturate, and the larger scale's
+     nonzero products are at least 16: they keep E4M3's full precision whatever
+     the scales' range. 2^sigma is the block's scale in the product and s_glob
      multiplies the sum.
    - h = silu(g) * u, rounded to bf16 as in the bf16 path, then per row and
      128-column block a power-of-two scale 2^e (block_exp of the block's amax)
@@ -447,8 +453,8 @@ static double w8_value(int dt, const void* q, const void* sb, int64_t N, int64_t
   uint8_t nib = (kk & 1) ? (byte >> 4) : (byte & 15);
   const uint8_t* srow = (const uint8_t*)sb + ((int64_t)e * N + n) * (K / 16);
   double s = e4m3_value(srow[kk / 16]);
-  double s0 = fabs(e4m3_value(srow[(kk / 32) * 2])), s1 = fabs(e4m3_value(srow[(kk / 32) * 2 + 1]));
-  int sigma = block_exp(6.0 * (s0 > s1 ? s0 : s1));
+  int c0 = srow[(kk / 32) * 2] & 0x7F, c1 = srow[(kk / 32) * 2 + 1] & 0x7F;
+  int sigma = ((c0 > c1 ? c0 : c1) >> 3) - 12; /* magnitude codes order like values */
   return ldexp(q_e4m3(ldexp(e2m1_value(nib) * s, -sigma)), sigma);
 }
 static double w8_scale(int dt, const void* sc, const float* gs, int64_t N, int e, int64_t n) {
@@ -511,12 +517,14 @@ static void expert_ffn_f8(const void* x, int64_t t, const weights* W, int e, con
 }
 
 /* Expert e's weights decoded into dense doubles, once per expert and call.
-   mode 0 (weights dequantised exactly): gu [H][2I] and dn [I][H], the values
-   gate_up_row and down_row give. Modes 1 and 2 (F8): gu [2I][H] and dn [H][I],
+   mode 0 (weights dequantised exactly, FP8 / NVFP4 only: bf16 and fp32 rows
+   are read as stored): gu [H][2I] and dn [I][H], the values gate_up_row and
+   down_row give. Modes 1 and 2 (F8): gu [2I][H] and dn [H][I],
    the values w8_value gives (mode 2 needs dn only). A work-shared loop of the
    enclosing parallel region (each ends with a barrier). */
 static void decode_expert(int mode, const weights* W, int e, double* gu, double* dn) {
   int64_t H = W->H, I = W->I, N1 = 2 * I;
+  if (mode == 0 && (W->dt == ODT_F32 || W->dt == ODT_BF16)) return; /* read as stored */
   if (mode == 0) {
 #pragma omp for schedule(static)
     for (int64_t h = 0; h < H; ++h) gate_up_row(W, e, (int)h, gu + h * N1);
@@ -547,9 +555,11 @@ static int expert_rows_grouped(int mode, int x_dt, const void* x, const weights*
   int64_t *order = NULL, *start = NULL;
   int rc = group_rows(n, experts, E, &order, &start);
   if (rc) return rc;
-  double* gu = mode == 2 ? NULL : (double*)malloc(sizeof(double) * (size_t)(H * 2 * I));
-  double* dn = (double*)malloc(sizeof(double) * (size_t)(H * I));
-  if ((mode != 2 && !gu) || !dn) {
+  /* bf16 / fp32 weights are read as stored; quantised ones decoded per expert */
+  const int decode = mode != 0 || (W->dt != ODT_F32 && W->dt != ODT_BF16);
+  double* gu = (mode == 2 || !decode) ? NULL : (double*)malloc(sizeof(double) * (size_t)(H * 2 * I));
+  double* dn = decode ? (double*)malloc(sizeof(double) * (size_t)(H * I)) : NULL;
+  if ((mode != 2 && decode && !gu) || (decode && !dn)) {
     free(gu);
     free(dn);
     free(order);
@@ -560,21 +570,28 @@ static int expert_rows_grouped(int mode, int x_dt, const void* x, const weights*
 #pragma omp parallel
   {
     double* a = (double*)malloc(sizeof(double) * 2 * (size_t)I);
-    double* xq = (double*)malloc(sizeof(double) * (size_t)H);
+    double* xq = (double*)malloc(sizeof(double) * (size_t)(H > 2 * I ? H : 2 * I));
     const int bad = !a || !xq;
     if (bad) {
 #pragma omp atomic write
       err = ORACLE_ENOMEM;
     }
-    for (int e = 0; e < E; ++e) {
+    if (!decode) {  /* weights read as stored: every row in parallel */
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t r = 0; r < n; ++r)
+        if (!bad)
+          expert_ffn(x_dt, x, tokens[r], W, experts[r], NULL, NULL, a, xq, y + r * H,
+                     h_out ? h_out + r * I : NULL);
+    }
+    for (int e = 0; decode && e < E; ++e) {
       if (start[e] == start[e + 1]) continue;  /* the same decision in every thread */
       decode_expert(mode, W, e, gu, dn);
 #pragma omp for schedule(dynamic, 1)
       for (int64_t q = start[e]; q < start[e + 1]; ++q) {
         if (bad) continue;
         int64_t r = order[q];
-        if (mode == 0)
-          expert_ffn(x_dt, x, tokens[r], H, I, gu, dn, a, y + r * H, h_out ? h_out + r * I : NULL);
+        if (mode == 0)  /* xq serves as the row buffer */
+          expert_ffn(x_dt, x, tokens[r], W, e, gu, dn, a, xq, y + r * H, h_out ? h_out + r * I : NULL);
         else if (mode == 1)
           expert_ffn_f8(x, tokens[r], W, e, gu, dn, a, xq, y + r * H,
                         h_out ? h_out + r * I : NULL, hq_out ? hq_out + r * I : NULL);

@@ -944,12 +944,12 @@ __global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
 //  - down A: h as E4M3 codes with one power-of-two (E8M0) scale per row and
 //    128-column block, handed to the MFMA, which applies it exactly;
 //  - B: FP8 weights as stored, or NVFP4 weights re-encoded per 32-deep K
-//    block as RNE_e4m3(e2m1 * s_blk * 2^-s) in registers, s the smallest
-//    integer with 6 * (the larger of the block's two E4M3 scales) <= 448 * 2^s
-//    (the converter gives e2m1 times the scale's power of two, an fp32 multiply
-//    its mantissa factor times 2^-s, and the hardware f32 -> E4M3 conversion
-//    rounds to nearest even); 2^s is the lane's E8M0 B scale in the MFMA, so
-//    the re-encoding is as precise for any range of block scales.
+//    block as RNE_e4m3(e2m1 * s_blk * 2^-s) in registers, s = (the exponent
+//    field of the block's larger E4M3 scale) - 12 (the converter gives e2m1
+//    times the scale's power of two times 2^-s, an fp32 multiply its mantissa
+//    factor, and the hardware f32 -> E4M3 conversion rounds to nearest even);
+//    2^s is the lane's E8M0 B scale in the MFMA, so the re-encoding is as
+//    precise for any range of block scales.
 // Lane half g takes K 32g .. 32g+31 of each 64-deep step for both operands;
 // the scale of a down-GEMM row is the same over the whole step, so the K
 // order inside the step is free.
@@ -990,8 +990,8 @@ __device__ __forceinline__ void vm_wait() {
   else static_assert(N < 0, "add this vmcnt value");
 }
 
-// 8 E2M1 codes (one dword) x block scale (p2 * fm8: the scale's power of two
-// and its mantissa factor times the block's shift) -> 8 E4M3 codes (two dwords)
+// 8 E2M1 codes (one dword) x block scale (p2 * fm8: the scale's power of two,
+// times the block's shift, and its mantissa factor) -> 8 E4M3 codes (two dwords)
 __device__ __forceinline__ void fp4_to_fp8(uint32_t d, float p2, float fm8, int32_t& o0,
                                            int32_t& o1) {
   const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 0);
@@ -1223,29 +1223,29 @@ __global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmAr
       } else {
         // run r (bytes 16 r .. of the operand) holds NVFP4 block kh + 2 r of the
         // step, in the MFMA's scale block r = K 32 r .. +32 (NVFP4 blocks 2 r,
-        // 2 r + 1). Each scale block gets one shift 2^-s, s the smallest with 6 *
-        // (its larger NVFP4 scale) <= 448 * 2^s, so every product e2m1 * s_blk *
-        // 2^-s lands in E4M3's range with full precision; this lane hands 2^s
-        // of scale block kh to the MFMA (lane l: column l % 32, block l / 32).
-        float p2[4], fm[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) e4m3_split((f.sc[jj] >> (8 * b)) & 0xFFu, p2[b], fm[b]);
-        int sig[2];
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const float v = 6.f * fmaxf(p2[2 * r] * fabsf(fm[2 * r]), p2[2 * r + 1] * fabsf(fm[2 * r + 1]));
-          const int ex = __builtin_amdgcn_frexp_expf(v);  // v = m 2^ex, 0.5 <= m < 1
-          sig[r] = v > 0.f ? (2.f * __builtin_amdgcn_frexp_mantf(v) <= 1.75f ? ex - 9 : ex - 8) : 0;
-        }
-        sb = 127 + (kh ? sig[1] : sig[0]);
+        // 2 r + 1). Scale block r is shifted by 2^-s, s = (exponent field of
+        // its larger E4M3 scale) - 12: every product e2m1 * s_blk * 2^-s stays
+        // below 384 (never saturates) and the larger scale's nonzero products
+        // are >= 16, whatever the scales' range. The shift goes into the
+        // converter's power of two; this lane hands 2^s of scale block kh to
+        // the MFMA (lane l: column l % 32, block l / 32).
+        const uint32_t sc = f.sc[jj];
+        const uint32_t s0 = sc & 0x7Fu, s1 = (sc >> 8) & 0x7Fu;  // magnitude codes order
+        const uint32_t s2 = (sc >> 16) & 0x7Fu, s3 = (sc >> 24) & 0x7Fu;  // like values
+        const uint32_t em[2] = {(s0 > s1 ? s0 : s1) >> 3, (s2 > s3 ? s2 : s3) >> 3};
+        sb = (int)(115u + (kh ? em[1] : em[0]));
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-          // NVFP4 block kh + 2 r (selects, not a lane-dependent register index)
-          const float pb = kh ? p2[2 * r + 1] : p2[2 * r];
-          const float fms = __builtin_ldexpf(kh ? fm[2 * r + 1] : fm[2 * r], -sig[r]);  // exact
+          const uint32_t c = (sc >> (8 * (kh + 2 * r))) & 0xFFu;  // NVFP4 block kh + 2 r
+          const uint32_t ce = (c >> 3) & 15u, cm = c & 7u;
+          const uint32_t normal = ce != 0u ? 1u : 0u;
+          // 2^(e - 7) * 2^(12 - em): the block scale's power of two, shifted
+          const float pb = __uint_as_float(((normal ? ce : 1u) + 132u - em[r]) << 23);
+          const float fmr = (float)((normal << 3) | cm) * 0.125f;  // exact
+          const float fm = __uint_as_float(__float_as_uint(fmr) | ((c & 0x80u) << 24));
           int32_t o0, o1, o2, o3;
-          fp4_to_fp8(f.q[jj][r][0], pb, fms, o0, o1);
-          fp4_to_fp8(f.q[jj][r][1], pb, fms, o2, o3);
+          fp4_to_fp8(f.q[jj][r][0], pb, fm, o0, o1);
+          fp4_to_fp8(f.q[jj][r][1], pb, fm, o2, o3);
           bf[4 * r] = o0;
           bf[4 * r + 1] = o1;
           bf[4 * r + 2] = o2;

@@ -385,8 +385,8 @@ def test_permute_and_finalize_skip_invalid_ids(T, k, E):
 def _shift_nvfp4_scales(hw: dict, max_shift: int) -> dict:
     """The same NVFP4 weights with each matrix's block scales divided by 2^s and its
     per-expert scales multiplied by 2^s (s the largest shift up to max_shift that
-    keeps every block scale exactly representable): identical dequantised values,
-    block scales far below the 448 the usual recipe gives its largest."""
+    keeps every nonzero block scale a normal E4M3 value): identical dequantised
+    values, block scales far below the 448 the usual recipe gives its largest."""
     import oracle
     e4 = oracle.format_op("e4m3", np.arange(256))
     out = dict(hw)
@@ -394,7 +394,7 @@ def _shift_nvfp4_scales(hw: dict, max_shift: int) -> dict:
         for shift in range(max_shift, 0, -1):
             v = e4[hw[key]] * 2.0 ** -shift
             codes = synth.encode_e4m3_table(v)
-            if np.array_equal(e4[codes], v):
+            if np.array_equal(e4[codes], v) and np.all((np.abs(v) >= 2.0 ** -6) | (v == 0)):
                 break
         out[key] = codes
         out[g] = (hw[g].astype(np.float64) * 2.0 ** shift).astype(np.float32)

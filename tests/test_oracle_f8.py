@@ -122,8 +122,8 @@ def _w8_matrices(q, fmt, E, H, I):
     """The operand values of the F8 mode, built from the format tables and the
     generator's table-driven E4M3 encoder (not the oracle's rounding): gate/up
     [E, 2I, H] and down [E, H, I] (K-major rows), and the column scales. NVFP4
-    codes are re-encoded per 32-deep K block with the power of two 2^s that
-    covers 6 x the larger of the block's two E4M3 scales."""
+    codes are re-encoded per 32-deep K block with 2^-s, s = (the exponent field
+    of the block's larger E4M3 scale) - 12, and multiplied back by 2^s."""
     e4 = oracle.format_op("e4m3", np.arange(256))
     e2 = oracle.format_op("e2m1", np.arange(16))
 
@@ -133,8 +133,10 @@ def _w8_matrices(q, fmt, E, H, I):
         lo, hi = codes & 15, codes >> 4
         nib = np.stack([lo, hi], -1).reshape(E, N, K)
         sv = e4[scales.reshape(E, N, K // 16)]
-        sig = _covering_exponent(6.0 * np.abs(sv).reshape(E, N, K // 32, 2).max(axis=3))
-        sig = np.repeat(sig, 32, axis=2)
+        mag = (scales.reshape(E, N, K // 32, 2) & 0x7F).astype(np.int64)
+        sig = np.repeat((mag.max(axis=3) >> 3) - 12, 32, axis=2)
+        # the shift keeps every product on the E4M3 grid's normal range unsaturated
+        assert np.all(6.0 * np.abs(np.repeat(sv, 16, axis=2)) * np.ldexp(1.0, -sig) < 448.0)
         prod = e2[nib] * np.repeat(sv, 16, axis=2) * np.ldexp(1.0, -sig)
         v = e4[synth.encode_e4m3_table(prod)] * np.ldexp(1.0, sig)
         return v, np.repeat(gsc.astype(np.float64)[:, None], N, axis=1)
@@ -193,15 +195,15 @@ def _small_scale_copy(q, max_shift):
     """The same NVFP4 weights with every block scale of a matrix divided by 2^s and
     its per-expert scales multiplied by 2^s: identical dequantised values (powers
     of two), block scales far below the 448 the usual recipe gives its largest.
-    s is the largest shift up to max_shift that keeps every scale exactly
-    representable (small scales become E4M3 subnormals)."""
+    s is the largest shift up to max_shift that keeps every nonzero scale a
+    normal E4M3 value (exactly representable, exponent field shifted by s)."""
     e4 = oracle.format_op("e4m3", np.arange(256))
     out = dict(q)
     for key, g in (("gate_up_scale", "gate_up_gscale"), ("down_scale", "down_gscale")):
         for shift in range(max_shift, 0, -1):
             v = e4[q[key]] * 2.0 ** -shift
             codes = synth.encode_e4m3_table(v)
-            if np.array_equal(e4[codes], v):
+            if np.array_equal(e4[codes], v) and np.all((np.abs(v) >= 2.0 ** -6) | (v == 0)):
                 break
         out[key] = codes
         out[g] = (q[g].astype(np.float64) * 2.0 ** shift).astype(np.float32)
