@@ -292,9 +292,8 @@ moe_status enqueue_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H,
     // few touched experts: split K so that enough wavefronts stream weights
     float* part = reinterpret_cast<float*>(static_cast<char*>(tile_ws) +
                                            align_up(moe::expert_tile_ws_bytes(P, E, H, I)));
-    const int kstep = moe::stream_k_step(wf);
-    const moe::StreamSplit sg = moe::stream_split_plan(P, E, H, 2 * I, true, kstep);
-    const moe::StreamSplit sd = moe::stream_split_plan(P, E, I, H, false, kstep);
+    const moe::StreamSplit sg = moe::stream_split_plan(P, E, H, 2 * I, true, wf);
+    const moe::StreamSplit sd = moe::stream_split_plan(P, E, I, H, false, wf);
     a.ksplit = sg.ksplit;
     a.ksteps = sg.ksteps;
     a.part = part;

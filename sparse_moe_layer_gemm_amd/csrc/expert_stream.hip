@@ -358,31 +358,43 @@ __global__ __launch_bounds__(256) void stream_reduce_dn_kernel(const float* __re
 
 // ------------------------------------------------------------------ FP8 / NVFP4 weights
 // K-contiguous quantised weights ([E, N, K] E4M3 codes, or [E, N, K/2] E2M1
-// codes with one E4M3 scale per 16 K values). Per "super step" a lane reads
-// 16 B of each of its 8 columns (FP8: 16 K values, 2 MFMA K steps; FP4: 32 K
-// values, 4) with the matching A fragments; like the bf16 kernel, a super
-// step's loads are issued one step ahead into one of two register sets,
-// unconditionally from clamped addresses. A load instruction covers 64 B of
-// each of 16 weight rows, half a cache line: the next super step reads the
-// other half, so these loads keep cache retention (nontemporal loads measured
-// 25-30% slower here). Codes become bf16 with the hardware
-// converters (E4M3 exactly; E2M1 with the power of two of its block scale,
-// then an fp32 multiply by the scale's mantissa factor, exact as well).
-// Per-channel (E4M3) and per-expert (E2M1) fp32 scales multiply the
-// accumulators. In MFMA s of a super step lane group g covers K
-// ss*SPAN + G*g + 8s .. +8, for A and B alike.
+// codes with one E4M3 scale per 16 K values). Per "super step" the four lane
+// groups of a column each read 32 B of it, together one whole 128 B line
+// (E4M3: 32 K values per lane, E2M1: 64), plus, for E2M1, the dword of this
+// lane's four block scales, with the matching A fragments; like the bf16
+// kernel, a super step's loads are issued one step ahead into one of two
+// register sets, unconditionally from clamped addresses. Each code line is
+// consumed by the load that fetches it, so code loads skip cache retention
+// (nontemporal), leaving L2 to the scale lines, which serve 8 super steps.
+// (Reading half a line per super step measured 2.8x the algorithmic bytes
+// fetched at decode: lines were evicted before their second half was used.)
+// A wavefront owns 64 columns (gate/up: 32 gate + the 32 matching up). Codes
+// become bf16 with the hardware converters (E4M3 exactly; E2M1 with the power
+// of two of its block scale, then an fp32 multiply by the scale's mantissa
+// factor, exact as well). Per-channel (E4M3) and per-expert (E2M1) fp32
+// scales multiply the accumulators. In MFMA s of a super step lane group g
+// covers K ss*SPAN + G*g + 8s .. +8, for A and B alike.
+template <int WF>
+struct KmShape {
+  static constexpr int G = (WF == W_FP8) ? 32 : 64;  // K values per lane per super step
+  static constexpr int NS = G / 8;                   // MFMA K steps per super step
+  static constexpr int SPAN = 4 * G;                 // K per super step
+  static constexpr int NV = 2;                       // 16 B code loads per lane and column
+  static constexpr int CG = 4;                       // 16-column groups per wavefront
+  static constexpr int COLS = 16 * CG;               // columns per wavefront
+  // row fragments per pass: one for E2M1 (its A fragments per fragment row
+  // and super step would otherwise cost a wave per SIMD of occupancy)
+  static constexpr int NF = (WF == W_FP4) ? 1 : 2;
+};
+
 template <int WF, bool GATE_UP>
 __global__ __launch_bounds__(256, 2) void stream_kmajor_kernel(StreamGemmArgs a) {
-  constexpr int G = (WF == W_FP8) ? 16 : 32;  // K values per lane per super step
-  constexpr int NS = G / 8;                   // MFMA K steps per super step
-  constexpr int SPAN = 4 * G;                 // K per super step
-  // row fragments per pass: one for E2M1 (its 4 A fragments per fragment row
-  // and super step would otherwise cost a wave per SIMD of occupancy)
-  constexpr int NF = (WF == W_FP4) ? 1 : 2;
+  using S = KmShape<WF>;
+  constexpr int G = S::G, NS = S::NS, SPAN = S::SPAN, NV = S::NV, CG = S::CG, NF = S::NF;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, j = lane & 15;
   const int tile = blockIdx.x * 4 + wave;
-  const int n_tiles = GATE_UP ? a.I / 64 : (a.N + 127) / 128;
+  const int n_tiles = GATE_UP ? a.I / (S::COLS / 2) : (a.N + S::COLS - 1) / S::COLS;
   if (tile >= n_tiles) return;
   const int e = slot_expert(a.offsets, a.E, blockIdx.y, lane);
   if (e < 0) return;
@@ -396,21 +408,22 @@ __global__ __launch_bounds__(256, 2) void stream_kmajor_kernel(StreamGemmArgs a)
   const int ss1 = a.ksplit > 1 ? min(nss, ss0 + a.ksteps) : nss;
   if (ss0 >= ss1) return;
 
-  // this lane's 8 columns (gate/up: 4 gate, then the 4 matching up columns);
+  // this lane's CG columns (gate/up: CG/2 gate, then the matching up columns);
   // columns past N read column 0 and are never stored
   const int row_bytes = (WF == W_FP8) ? K : K / 2;
   const uint8_t* wexp = static_cast<const uint8_t*>(a.w) + (size_t)e * N * row_bytes;
   const uint8_t* sexp =
       (WF == W_FP4) ? static_cast<const uint8_t*>(a.w_scale) + (size_t)e * N * (K / 16) : nullptr;
-  int colv[8];
-  bool cok[8];
-  uint32_t coff[8];
+  int colv[CG];
+  bool cok[CG];
+  uint32_t coff[CG];
 #pragma unroll
-  for (int cg = 0; cg < 8; ++cg) {
+  for (int cg = 0; cg < CG; ++cg) {
+    constexpr int H2 = CG / 2, HC = S::COLS / 2;
     if (GATE_UP)
-      colv[cg] = cg < 4 ? tile * 64 + 16 * cg + j : a.I + tile * 64 + 16 * (cg - 4) + j;
+      colv[cg] = cg < H2 ? tile * HC + 16 * cg + j : a.I + tile * HC + 16 * (cg - H2) + j;
     else
-      colv[cg] = tile * 128 + 16 * cg + j;
+      colv[cg] = tile * S::COLS + 16 * cg + j;
     cok[cg] = colv[cg] < N;
     coff[cg] = (uint32_t)(cok[cg] ? colv[cg] : 0);
   }
@@ -419,15 +432,15 @@ __global__ __launch_bounds__(256, 2) void stream_kmajor_kernel(StreamGemmArgs a)
   for (int mc = 0; mc < cnt; mc += 16 * NF) {
     const int nf = (NF == 2 && (cnt - mc) > 16) ? 2 : 1;
     const ARows ar = a_rows(a, GATE_UP, r0, cnt, mc, j);
-    f32x4 acc[NF][8];
+    f32x4 acc[NF][CG];
 #pragma unroll
     for (int f = 0; f < NF; ++f)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[f][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < CG; ++i) acc[f][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     struct Ops {
-      u32x4 a[NF][NS], b[8];
-      uint32_t sc[8];
+      u32x4 a[NF][NS], b[CG][NV];
+      uint32_t sc[CG];
       bool kok;  // this lane's K range lies inside K (false only in a K tail)
     };
     auto load = [&](int ss, Ops& o) {
@@ -439,26 +452,31 @@ __global__ __launch_bounds__(256, 2) void stream_kmajor_kernel(StreamGemmArgs a)
 #pragma unroll
         for (int q = 0; q < NS; ++q) o.a[f][q] = load_u32x4(ar.row[f] + kc + 8 * q);
 #pragma unroll
-      for (int cg = 0; cg < 8; ++cg)
-        o.b[cg] = load_u32x4(wexp + (size_t)coff[cg] * row_bytes + (WF == W_FP8 ? kc : kc / 2));
+      for (int cg = 0; cg < CG; ++cg)
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+          o.b[cg][v] = load_w(wexp + (size_t)coff[cg] * row_bytes + (WF == W_FP8 ? kc : kc / 2) + 16 * v);
       if constexpr (WF == W_FP4) {
 #pragma unroll
-        for (int cg = 0; cg < 8; ++cg)  // the two block scales of this lane's 32 K values
-          o.sc[cg] = *reinterpret_cast<const uint16_t*>(sexp + (size_t)coff[cg] * (K / 16) + kc / 16);
+        for (int cg = 0; cg < CG; ++cg)  // the four block scales of this lane's 64 K values
+          o.sc[cg] = *reinterpret_cast<const uint32_t*>(sexp + (size_t)coff[cg] * (K / 16) + kc / 16);
       }
     };
     auto step = [&](const Ops& o) {
 #pragma unroll
-      for (int cg = 0; cg < 8; ++cg) {
-        float p2[2], fm[2];
+      for (int cg = 0; cg < CG; ++cg) {
+        float p2[4], fm[4];
         if constexpr (WF == W_FP4) {
-          e4m3_split(o.sc[cg] & 0xFFu, p2[0], fm[0]);
-          e4m3_split((o.sc[cg] >> 8) & 0xFFu, p2[1], fm[1]);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) e4m3_split((o.sc[cg] >> (8 * b)) & 0xFFu, p2[b], fm[b]);
         }
 #pragma unroll
         for (int q = 0; q < NS; ++q) {
-          const u32x4 bf = (WF == W_FP8) ? fp8_frag(o.b[cg][2 * q], o.b[cg][2 * q + 1])
-                                         : fp4_frag(o.b[cg][q], p2[q >> 1], fm[q >> 1]);
+          u32x4 bf;
+          if constexpr (WF == W_FP8)
+            bf = fp8_frag(o.b[cg][q >> 1][2 * (q & 1)], o.b[cg][q >> 1][2 * (q & 1) + 1]);
+          else
+            bf = fp4_frag(o.b[cg][q >> 2][q & 3], p2[q >> 1], fm[q >> 1]);
 #pragma unroll
           for (int f = 0; f < NF; ++f)
             if (f < nf) acc[f][cg] = mfma_bf16(o.kok ? o.a[f][q] : zero, bf, acc[f][cg]);
@@ -483,9 +501,9 @@ __global__ __launch_bounds__(256, 2) void stream_kmajor_kernel(StreamGemmArgs a)
     // epilogue: lane (g, j) holds rows 16f + 4g + r of column colv[cg]
     const float gsc = (WF == W_FP4) ? a.w_gscale[e] : 1.f;
     const float* chs = (WF == W_FP8) ? static_cast<const float*>(a.w_scale) + (size_t)e * N : nullptr;
-    float csc[8];
+    float csc[CG];
 #pragma unroll
-    for (int cg = 0; cg < 8; ++cg) csc[cg] = (WF == W_FP8) ? chs[coff[cg]] : gsc;
+    for (int cg = 0; cg < CG; ++cg) csc[cg] = (WF == W_FP8) ? chs[coff[cg]] : gsc;
     float* pbase = a.ksplit > 1 ? a.part + (size_t)split * a.part_stride : nullptr;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
@@ -496,17 +514,17 @@ __global__ __launch_bounds__(256, 2) void stream_kmajor_kernel(StreamGemmArgs a)
         if (m >= cnt) continue;
         if (pbase) {  // split K: scaled fp32 partial sums
 #pragma unroll
-          for (int cg = 0; cg < 8; ++cg)
+          for (int cg = 0; cg < CG; ++cg)
             if (cok[cg]) pbase[(size_t)(r0 + m) * N + colv[cg]] = acc[f][cg][r] * csc[cg];
         } else if (GATE_UP) {
 #pragma unroll
-          for (int cg = 0; cg < 4; ++cg) {
-            const float gv = acc[f][cg][r] * csc[cg], uv = acc[f][cg + 4][r] * csc[cg + 4];
+          for (int cg = 0; cg < CG / 2; ++cg) {
+            const float gv = acc[f][cg][r] * csc[cg], uv = acc[f][cg + CG / 2][r] * csc[cg + CG / 2];
             a.h_out[(size_t)(r0 + m) * a.I + colv[cg]] = (uint16_t)f32_to_bf16_bits(silu(gv) * uv);
           }
         } else {
 #pragma unroll
-          for (int cg = 0; cg < 8; ++cg)
+          for (int cg = 0; cg < CG; ++cg)
             if (cok[cg]) store_rows(a.y_out + (size_t)(r0 + m) * N + colv[cg], acc[f][cg][r] * csc[cg]);
         }
       }
@@ -514,9 +532,13 @@ __global__ __launch_bounds__(256, 2) void stream_kmajor_kernel(StreamGemmArgs a)
   }
 }
 
+// Columns per wavefront of the streaming kernels.
+int stream_cols(int wfmt) { return wfmt == W_BF16 ? 128 : KmShape<W_FP8>::COLS; }
+
 template <bool GU>
 hipError_t launch_one(int wfmt, const StreamGemmArgs& a, hipStream_t st) {
-  const int n_tiles = GU ? a.I / 64 : (a.N + 127) / 128;
+  const int cols = stream_cols(wfmt);
+  const int n_tiles = GU ? a.I / (cols / 2) : (a.N + cols - 1) / cols;
   // one grid row per expert that can have rows: at most min(E, P) do
   dim3 grid((n_tiles + 3) / 4, a.rows > 0 ? std::min(a.E, a.rows) : a.E);
   const bool fold = !GU && a.hpart != nullptr;
@@ -567,10 +589,11 @@ hipError_t launch_one(int wfmt, const StreamGemmArgs& a, hipStream_t st) {
 // slices. Splits are added until about 4096 wavefronts stream (two rounds at
 // two per SIMD; measured at T = 1 ... 8 this beats one exact round), keeping
 // at least 8 K steps per split. A K step is 32 K values for bf16 weights and
-// one super step (64 or 128 K values) for FP8 / NVFP4 weights.
-StreamSplit stream_split_plan(long long P, int E, int K, int N, bool gate_up, int step) {
+// one super step (128 or 256 K values) for FP8 / NVFP4 weights.
+StreamSplit stream_split_plan(long long P, int E, int K, int N, bool gate_up, int wfmt) {
+  const int step = stream_k_step(wfmt), cols = stream_cols(wfmt);
   const long long touched = std::min<long long>(E, P);
-  const long long slices = gate_up ? N / 128 : (N + 127) / 128;
+  const long long slices = gate_up ? N / cols : (N + cols - 1) / cols;
   const int nk = (K + step - 1) / step;
   const long long waves = std::max<long long>(1, touched * slices);
   long long s = (4096 + waves - 1) / waves;
@@ -581,28 +604,29 @@ StreamSplit stream_split_plan(long long P, int E, int K, int N, bool gate_up, in
   return StreamSplit{(nk + ksteps - 1) / ksteps, ksteps};
 }
 
-int stream_k_step(int wfmt) { return wfmt == W_FP4 ? 128 : wfmt == W_FP8 ? 64 : 32; }
+int stream_k_step(int wfmt) {
+  return wfmt == W_FP4 ? KmShape<W_FP4>::SPAN : wfmt == W_FP8 ? KmShape<W_FP8>::SPAN : 32;
+}
 
 bool stream_fold_h(long long P, int E, int H, int I, int wfmt, int* kr) {
   if (wfmt != W_BF16 || P > MROWS) return false;
-  const StreamSplit gu = stream_split_plan(P, E, H, 2 * I, true, 32);
+  const StreamSplit gu = stream_split_plan(P, E, H, 2 * I, true, W_BF16);
   if (gu.ksplit <= 1) return false;
-  const int k = stream_split_plan(P, E, I, H, false, 32).ksteps * 32;
+  const int k = stream_split_plan(P, E, I, H, false, W_BF16).ksteps * 32;
   if (MROWS * (2 * k + 16) > 65536) return false;
   *kr = k;
   return true;
 }
 
 size_t stream_gu_part_bytes(long long P, int E, int H, int I, int wfmt) {
-  const StreamSplit gu = stream_split_plan(P, E, H, 2 * I, true, stream_k_step(wfmt));
+  const StreamSplit gu = stream_split_plan(P, E, H, 2 * I, true, wfmt);
   const size_t b = gu.ksplit > 1 ? (size_t)gu.ksplit * (size_t)P * 2 * I * sizeof(float) : 0;
   return (b + 255) / 256 * 256;
 }
 
 size_t stream_ws_bytes(long long P, int E, int H, int I, int wfmt) {
-  const int step = stream_k_step(wfmt);
-  const StreamSplit gu = stream_split_plan(P, E, H, 2 * I, true, step);
-  const StreamSplit dn = stream_split_plan(P, E, I, H, false, step);
+  const StreamSplit gu = stream_split_plan(P, E, H, 2 * I, true, wfmt);
+  const StreamSplit dn = stream_split_plan(P, E, I, H, false, wfmt);
   size_t b = 0;
   if (gu.ksplit > 1) b = std::max(b, (size_t)gu.ksplit * (size_t)P * 2 * I * sizeof(float));
   const size_t bd = dn.ksplit > 1 ? (size_t)dn.ksplit * (size_t)P * H * sizeof(float) : 0;

@@ -603,10 +603,15 @@ __global__ __launch_bounds__(256) void tile_items_kernel(const int32_t* __restri
 // epilogue. Within a K step, lane half kh takes K 16*kh .. 16*kh+15 (MFMA s
 // the 8 from 16*kh + 8*s), so a lane's codes are contiguous and, for E2M1,
 // each lane needs a single block scale per step.
-template <int WF, int WM>
+// The 128 x 512 tile runs 8 wavefronts side by side along N, each 128 rows x
+// 64 columns (128 accumulators), two per SIMD: every weight column is
+// converted by exactly one wavefront, and while one wavefront of a SIMD
+// converts its codes (VALU) the other can issue its MFMAs.
+template <int WF>
 struct QShape {
-  using T = TileShape<WM>;
-  static constexpr int BM = T::BM, BN = T::BN, WN = T::WN;
+  using T = TileShape<1, 8>;
+  static constexpr int NW = 8;
+  static constexpr int BM = T::BM, BN = T::BN, WN = T::WN, JT = T::JT;
   static constexpr int COL = WF == W_FP4 ? 16 : 32;   // code bytes per column per K step
   static constexpr int SCL = WF == W_FP4 ? 4 : 0;     // scale bytes per column per K step
   static constexpr int A_STAGE = T::A_STAGE;
@@ -614,13 +619,13 @@ struct QShape {
   static constexpr int S_STAGE = BN * SCL;
   static constexpr int STAGE = A_STAGE + B_STAGE + S_STAGE;
   static constexpr int PIPE = NSTAGE * STAGE;
-  static constexpr int EPI = 65536;                   // epilogue strips (4 x 16 KB)
+  static constexpr int EPI = NW * 8192;               // epilogue strips (32 x 64 fp32 each)
   static constexpr int LDS = PIPE > EPI ? PIPE : EPI;
-  static constexpr int QA = T::QA;
-  static constexpr int QB = B_STAGE / 4096;           // 1 KB code loads per wavefront
-  static constexpr int QS = S_STAGE / 1024;           // 256 B scale loads per wavefront
+  static constexpr int QA = A_STAGE / 1024 / NW;      // 1 KB A loads per wavefront
+  static constexpr int QB = B_STAGE / 1024 / NW;      // 1 KB code loads per wavefront
+  static constexpr int QS = S_STAGE / 256 / NW;       // 256 B scale loads per wavefront
   static constexpr int PER_STEP = QA + QB + QS;       // loads per wavefront per K step
-  static_assert(PER_STEP == 6, "the waits below assume 6 loads per K step");
+  static_assert(QA == 1 && PER_STEP == 3, "the waits below assume 3 loads per K step");
 };
 
 __device__ __forceinline__ u32x2 lds_b64(uint32_t addr) {
@@ -646,16 +651,17 @@ __device__ __forceinline__ void dma4(const void* g, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
 }
 
-template <int WF, bool GATE_UP, int WM>
-__global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
+template <int WF, bool GATE_UP>
+__global__ __launch_bounds__(512, 1) void tile_q_kernel(StreamGemmArgs a,
                                                         const int32_t* __restrict__ tile_e,
                                                         const int32_t* __restrict__ tile_m0,
                                                         const int32_t* __restrict__ n_tiles_p,
                                                         int NT) {
-  using S = QShape<WF, WM>;
+  using S = QShape<WF>;
+  constexpr int JT = S::JT;
   __shared__ __align__(1024) uint8_t smem[S::LDS];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave / S::WN, wn = wave % S::WN;
+  const int wn = wave;
 
   const int total = *n_tiles_p * NT;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -670,16 +676,16 @@ __global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
   const int cnt = a.offsets[e + 1] - r0;
   const int K = a.K, N = a.N;
 
-  // A: as in the bf16 kernel (gathered rows, 16 rows per 1 KB load)
-  const uint16_t* asrc[S::QA];
-#pragma unroll
-  for (int q = 0; q < S::QA; ++q) {
-    const int row = (S::BM / 4) * wave + 16 * q + (lane >> 2);
+  // A: as in the bf16 kernel (gathered rows, 16 rows per 1 KB load; wavefront
+  // w loads rows 16 w .. 16 w + 15)
+  const uint16_t* asrc;
+  {
+    const int row = 16 * wave + (lane >> 2);
     const int lg = (lane & 3) ^ ((row >> 2) & 3);
     size_t grow = 0;
     if (m0 + row < cnt)
       grow = GATE_UP ? (size_t)(a.sorted_pair[r0 + m0 + row] / a.k) : (size_t)(r0 + m0 + row);
-    asrc[q] = a.a + grow * K + 8 * lg;
+    asrc = a.a + grow * K + 8 * lg;
   }
   // matrix column of LDS column c (gate/up: BN/2 gate, then the matching up)
   auto mcol = [&](int c) -> int {
@@ -693,32 +699,25 @@ __global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
   };
   const uint8_t* wq = static_cast<const uint8_t*>(a.w);
   const size_t row_bytes = WF == W_FP4 ? (size_t)K / 2 : (size_t)K;
-  // codes: fp4 load q covers LDS columns 64*qi .. +63 (16 B each); fp8 load q
-  // covers 32 columns (two 16 B halves each)
+  // codes: the fp4 load of wavefront w covers LDS columns 64 w .. +63 (16 B
+  // each); fp8 load q covers 32 columns (two 16 B halves each)
   const uint8_t* bsrc[S::QB];
 #pragma unroll
   for (int q = 0; q < S::QB; ++q) {
     const int qi = wave * S::QB + q;
-    if (WF == W_FP4) {
+    if (WF == W_FP4)
       bsrc[q] = wq + ((size_t)e * N + mcol(64 * qi + lane)) * row_bytes;
-    } else {
+    else
       bsrc[q] = wq + ((size_t)e * N + mcol(32 * qi + (lane >> 1))) * row_bytes + 16 * (lane & 1);
-    }
   }
-  const uint8_t* ssrc[S::QS > 0 ? S::QS : 1];
-#pragma unroll
-  for (int q = 0; q < S::QS; ++q) {
-    const int qi = wave * S::QS + q;
-    ssrc[q] = static_cast<const uint8_t*>(a.w_scale) +
-              ((size_t)e * N + mcol(64 * qi + lane)) * (size_t)(K / 16);
-  }
+  const uint8_t* ssrc = WF == W_FP4 ? static_cast<const uint8_t*>(a.w_scale) +
+                                          ((size_t)e * N + mcol(64 * wave + lane)) * (size_t)(K / 16)
+                                    : nullptr;
   auto issue = [&](int kt, int st) {
     uint8_t* As = smem + st * S::STAGE;
     uint8_t* Bs = As + S::A_STAGE;
     uint8_t* Ss = Bs + S::B_STAGE;
-    const int k0 = kt * TBK;
-#pragma unroll
-    for (int q = 0; q < S::QA; ++q) dma16(asrc[q] + k0, As + ((S::BM / 4) * wave + 16 * q) * 64);
+    dma16(asrc + kt * TBK, As + 16 * wave * 64);
 #pragma unroll
     for (int q = 0; q < S::QB; ++q) {
       const int qi = wave * S::QB + q;
@@ -727,34 +726,32 @@ __global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
       else
         dma16(bsrc[q] + 32 * kt, Bs + 32 * qi * 32);
     }
-#pragma unroll
-    for (int q = 0; q < S::QS; ++q) {
-      const int qi = wave * S::QS + q;
-      dma4(ssrc[q] + ((2 * kt) & ~3), Ss + 64 * qi * 4);
-    }
+    if (WF == W_FP4) dma4(ssrc + ((2 * kt) & ~3), Ss + 64 * wave * 4);
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][JT];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JT; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // LDS column of this wave's 32-column tile j (gate/up: its gate tile, then
+  // the matching up tile)
   auto bcol = [&](int j) -> int {
-    if (GATE_UP) return (j < 2) ? 64 * wn + 32 * j : S::BN / 2 + 64 * wn + 32 * (j - 2);
-    return 128 * wn + 32 * j;
+    if (GATE_UP) return j == 0 ? 32 * wn : S::BN / 2 + 32 * wn;
+    return 64 * wn + 32 * j;
   };
   const int l32 = lane & 31, kh = lane >> 5;
   const uint32_t lds0 = (uint32_t)(size_t)(lds_u8*)smem;
-  uint32_t aoff[2][4], boff[4], soff[4];
+  uint32_t aoff[2][4], boff[JT], soff[JT];
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) aoff[s][i] = a_off(128 * wm + 32 * i + l32, 2 * kh + s);
+    for (int i = 0; i < 4; ++i) aoff[s2][i] = a_off(32 * i + l32, 2 * kh + s2);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < JT; ++j) {
     const int c = bcol(j) + l32;
     boff[j] = S::A_STAGE + c * S::COL + (S::COL / 2) * kh;
     soff[j] = S::A_STAGE + S::B_STAGE + c * 4 + kh;
@@ -763,8 +760,8 @@ __global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
   // second half: A (K half 1)
   struct FragQ0 {
     u32x4 a[4];
-    typename QRaw<WF>::type b[4];
-    uint32_t sc[4];
+    typename QRaw<WF>::type b[JT];
+    uint32_t sc[JT];
   };
   struct FragQ1 {
     u32x4 a[4];
@@ -772,7 +769,7 @@ __global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
   auto read0 = [&](FragQ0& f, int st, int kt) {
     const uint32_t base = lds0 + st * S::STAGE;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < JT; ++j) {
       if constexpr (WF == W_FP4)
         f.b[j] = lds_b64(base + boff[j]);
       else
@@ -781,7 +778,7 @@ __global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
     if (WF == W_FP4) {
       const uint32_t sh = 2 * (kt & 1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) f.sc[j] = lds_byte(base + soff[j] + sh);
+      for (int j = 0; j < JT; ++j) f.sc[j] = lds_byte(base + soff[j] + sh);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) f.a[i] = lds_b128(base + aoff[0][i]);
@@ -794,8 +791,7 @@ __global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
 #define MOE_LGK_WAIT0(f, pending)                                                              \
   asm volatile("s_waitcnt lgkmcnt(" #pending ")"                                              \
                : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0]),         \
-                 "+v"(f.b[1]), "+v"(f.b[2]), "+v"(f.b[3]), "+v"(f.sc[0]), "+v"(f.sc[1]),       \
-                 "+v"(f.sc[2]), "+v"(f.sc[3])                                                  \
+                 "+v"(f.b[1]), "+v"(f.sc[0]), "+v"(f.sc[1])                                    \
                :                                                                               \
                : "memory")
 #define MOE_LGK_WAIT1(f, pending)                                                              \
@@ -804,10 +800,10 @@ __global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
                :                                                                               \
                : "memory")
   // codes of both K halves -> bf16 fragments
-  u32x4 bq[2][4];
+  u32x4 bq[2][JT];
   auto dequant = [&](const FragQ0& f) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < JT; ++j) {
       if constexpr (WF == W_FP4) {
         float p2, fm;
         e4m3_split(f.sc[j], p2, fm);
@@ -819,37 +815,39 @@ __global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
       }
     }
   };
-  auto mfma_half = [&](const u32x4 (&af)[4], int s) {
+  auto mfma_half = [&](const u32x4 (&af)[4], int s2) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JT; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i][j] = mfma32(af[i], bq[s][j], acc[i][j]);
+      for (int i = 0; i < 4; ++i) acc[i][j] = mfma32(af[i], bq[s2][j], acc[i][j]);
   };
-  // Pipeline as in the bf16 kernel: "step kt+1 landed" is vmcnt(6) once three
+  // Pipeline as in the bf16 kernel: "step kt+1 landed" is vmcnt(3) once three
   // steps are in flight; f1 (4 reads) is read while f0's MFMAs run, f0 of the
-  // next step (8 or 12 reads) while f1's run.
+  // next step (6 or 8 reads) while f1's run.
   const int nk = K / TBK;
   issue(0, 0);
   issue(nk > 1 ? 1 : nk - 1, 1);
   issue(nk > 2 ? 2 : nk - 1, 2);
-  asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   FragQ0 f0;
   FragQ1 f1;
+#pragma unroll
+  for (int j = 0; j < JT; ++j) f0.sc[j] = 0u;
   read0(f0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     read1(f1, kt % NSTAGE);
     MOE_LGK_WAIT0(f0, 4);
     dequant(f0);
     mfma_half(f0.a, 0);
-    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     issue(kt + 3 < nk ? kt + 3 : nk - 1, (kt + 3) % NSTAGE);
     read0(f0, (kt + 1) % NSTAGE, kt + 1);
     if (WF == W_FP4)
-      MOE_LGK_WAIT1(f1, 12);
-    else
       MOE_LGK_WAIT1(f1, 8);
+    else
+      MOE_LGK_WAIT1(f1, 6);
     mfma_half(f1.a, 1);
   }
   MOE_LGK_WAIT0(f0, 0);
@@ -858,39 +856,29 @@ __global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
 #undef MOE_LGK_WAIT1
   __builtin_amdgcn_s_barrier();
 
-  // ---- epilogue through LDS, scales applied first
+  // ---- epilogue through LDS (each wavefront its own strip), scales applied first
   const float gsc = WF == W_FP4 ? a.w_gscale[e] : 1.f;
   const float* chs = WF == W_FP8 ? static_cast<const float*>(a.w_scale) + (size_t)e * N : nullptr;
   auto tile_row = [&](int r) { return 8 * (r >> 2) + 4 * kh + (r & 3); };
   if (GATE_UP) {
-    float sg[2], su[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (WF == W_FP8) {
-        sg[j] = chs[mcol(bcol(j) + l32)];
-        su[j] = chs[mcol(bcol(j + 2) + l32)];
-      } else {
-        sg[j] = su[j] = gsc;
-      }
-    }
-    uint16_t* strip = reinterpret_cast<uint16_t*>(smem + wave * 4096);  // 32 x 64 bf16
+    const float sg = WF == W_FP8 ? chs[mcol(bcol(0) + l32)] : gsc;
+    const float su = WF == W_FP8 ? chs[mcol(bcol(1) + l32)] : gsc;
+    uint16_t* strip = reinterpret_cast<uint16_t*>(smem + wave * 4096);  // 32 x 32 bf16
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          strip[tile_row(r) * 64 + 32 * j + l32] = (uint16_t)f32_to_bf16_bits(
-              silu(acc[i][j][r] * sg[j]) * (acc[i][j + 2][r] * su[j]));
+      for (int r = 0; r < 16; ++r)
+        strip[tile_row(r) * 32 + l32] =
+            (uint16_t)f32_to_bf16_bits(silu(acc[i][0][r] * sg) * (acc[i][1][r] * su));
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int c = lane + 64 * t, rr = c >> 3, ch = c & 7;
-        const int m = m0 + 128 * wm + 32 * i + rr;
-        const int col = nt * (S::BN / 2) + 64 * wn + 8 * ch;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(strip + rr * 64 + 8 * ch);
+      for (int t = 0; t < 2; ++t) {  // 32 rows x 4 chunks of 16 B
+        const int c = lane + 64 * t, rr = c >> 2, ch = c & 3;
+        const int m = m0 + 32 * i + rr;
+        const int col = nt * (S::BN / 2) + 32 * wn + 8 * ch;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(strip + rr * 32 + 8 * ch);
         if (m < cnt && col < a.I)
           *reinterpret_cast<u32x4*>(a.h_out + (size_t)(r0 + m) * a.I + col) = v;
       }
@@ -899,35 +887,32 @@ __global__ __launch_bounds__(256, 1) void tile_q_kernel(StreamGemmArgs a,
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   } else {
-    float sd[4];
+    float sd[JT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sd[j] = WF == W_FP8 ? chs[mcol(bcol(j) + l32)] : gsc;
-    float* strip = reinterpret_cast<float*>(smem + wave * 16384);  // 32 x 128 fp32
+    for (int j = 0; j < JT; ++j) sd[j] = WF == W_FP8 ? chs[mcol(bcol(j) + l32)] : gsc;
+    float* strip = reinterpret_cast<float*>(smem + wave * 8192);  // 32 x 64 fp32
     const bool compact = a.y16 != nullptr;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < JT; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) strip[tile_row(r) * 128 + 32 * j + l32] = acc[i][j][r] * sd[j];
+        for (int r = 0; r < 16; ++r) strip[tile_row(r) * 64 + 32 * j + l32] = acc[i][j][r] * sd[j];
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      if (compact) {  // compact rows: two 64-column scale blocks per strip row
-        store_rows16<128>(strip, lane, m0 + 128 * wm + 32 * i, cnt, nt * S::BN + 128 * wn, N,
-                          (size_t)r0, a.y16, a.y16_scale);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        continue;
-      }
+      if (compact) {  // compact rows: one 64-column scale block per strip row
+        store_rows16<64>(strip, lane, m0 + 32 * i, cnt, nt * S::BN + 64 * wn, N, (size_t)r0,
+                         a.y16, a.y16_scale);
+      } else {
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int c = lane + 64 * t, rr = c >> 5, ch = c & 31;
-        const int m = m0 + 128 * wm + 32 * i + rr;
-        const int col = nt * S::BN + 128 * wn + 4 * ch;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(strip + rr * 128 + 4 * ch);
-        if (m < cnt && col < N) store_rows(a.y_out + (size_t)(r0 + m) * N + col, v);
+        for (int t = 0; t < 8; ++t) {  // 32 rows x 16 chunks of 16 B
+          const int c = lane + 64 * t, rr = c >> 4, ch = c & 15;
+          const int m = m0 + 32 * i + rr;
+          const int col = nt * S::BN + 64 * wn + 4 * ch;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(strip + rr * 64 + 4 * ch);
+          if (m < cnt && col < N) store_rows(a.y_out + (size_t)(r0 + m) * N + col, v);
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -1575,15 +1560,15 @@ hipError_t launch_router_bf16x3(const uint16_t* x, int T, int H, const float* w_
   return hipGetLastError();
 }
 
-template <int WF, bool GATE_UP, int WM>
+template <int WF, bool GATE_UP>
 static hipError_t launch_q(const StreamGemmArgs& g, const int32_t* te, const int32_t* tm,
                            const int32_t* nt_p, int max_tiles, hipStream_t st) {
-  using S = QShape<WF, WM>;
+  using S = QShape<WF>;
   const int NT = GATE_UP ? (g.I + S::BN / 2 - 1) / (S::BN / 2) : (g.N + S::BN - 1) / S::BN;
   const long long items = (long long)max_tiles * NT;
   const unsigned grid = (unsigned)(((items + 7) / 8) * 8);
   if (grid == 0) return hipSuccess;
-  tile_q_kernel<WF, GATE_UP, WM><<<grid, 256, 0, st>>>(g, te, tm, nt_p, NT);
+  tile_q_kernel<WF, GATE_UP><<<grid, 64 * S::NW, 0, st>>>(g, te, tm, nt_p, NT);
   return hipGetLastError();
 }
 
@@ -1613,8 +1598,8 @@ template <int WF>
 static hipError_t launch_q_all(const StreamGemmArgs& gu, const StreamGemmArgs& dn,
                                const int32_t* tile_e, const int32_t* tile_m0, const int32_t* counts,
                                int max_tiles, hipStream_t st) {
-  hipError_t err = launch_q<WF, true, 1>(gu, tile_e, tile_m0, counts, max_tiles, st);
-  if (err == hipSuccess) err = launch_q<WF, false, 1>(dn, tile_e, tile_m0, counts, max_tiles, st);
+  hipError_t err = launch_q<WF, true>(gu, tile_e, tile_m0, counts, max_tiles, st);
+  if (err == hipSuccess) err = launch_q<WF, false>(dn, tile_e, tile_m0, counts, max_tiles, st);
   return err;
 }
 

@@ -11,34 +11,36 @@
 //
 // Bound by HBM like the plain finalize (each expert row is read once, as fp32
 // rows or as compact rows: fp16 with a power-of-two scale per 64 columns).
-// Both mean squares need the whole row, so one workgroup of 1024 lanes owns a
-// token (16 wavefronts: enough loads in flight per token even at decode batch
-// sizes): lane l keeps float4 column chunks l, l + 1024, ... of m (and then
-// of r) in registers, the row sums go through a fixed butterfly in each
-// wavefront and a fixed-order add of the 16 wavefront sums, so results are
-// deterministic.
+// Both mean squares need the whole row, so one workgroup owns a token: lane l
+// keeps float4 column chunks l, l + NT, ... of m (and then of r) in
+// registers, the row sums go through a fixed butterfly in each wavefront and a
+// fixed-order add of the wavefront sums, so results are deterministic. Small
+// batches use 1024 lanes per token (16 wavefronts: enough loads in flight per
+// token); from 1024 tokens on, 256 lanes per token, so that a CU holds four
+// times as many tokens and keeps loading while some of them reduce.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int FN_THREADS = 1024;  // lanes per token
-constexpr int FN_WAVES = FN_THREADS / 64;
+constexpr int kLargeBatch = 1024;  // tokens from which 256 lanes serve a token
 
-// sum over the workgroup, identical in every lane
+// sum over the workgroup of NT lanes, identical in every lane
+template <int NT>
 __device__ __forceinline__ float row_sum(float v, float* red) {
+  constexpr int NWV = NT / 64;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);  // a + b == b + a: lanes agree
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[wave] = v;
   __syncthreads();
-  float s[FN_WAVES];
+  float s[NWV];
 #pragma unroll
-  for (int w = 0; w < FN_WAVES; ++w) s[w] = red[w];
+  for (int w = 0; w < NWV; ++w) s[w] = red[w];
 #pragma unroll
-  for (int d = 1; d < FN_WAVES; d <<= 1)  // fixed pairwise order
+  for (int d = 1; d < NWV; d <<= 1)  // fixed pairwise order
 #pragma unroll
-    for (int w = 0; w < FN_WAVES; w += 2 * d) s[w] += s[w + d];
+    for (int w = 0; w < NWV; w += 2 * d) s[w] += s[w + d];
   __syncthreads();  // red is reused by the next sum
   return s[0];
 }
@@ -79,15 +81,16 @@ __device__ __forceinline__ f32x4 load_row4(const NormRows& rows, int pos, int H,
   }
 }
 
-// CH float4 chunks per lane: H <= 4096 * CH. residual and residual_out may alias
-// (a lane reads each of its residual chunks before writing the same chunk).
-template <int CH, bool R16>
-__global__ __launch_bounds__(FN_THREADS) void finalize_norm_kernel(
+// NT lanes per token, CH float4 chunks per lane: H <= 4 * NT * CH. residual and
+// residual_out may alias (a lane reads each of its residual chunks before
+// writing the same chunk).
+template <int NT, int CH, bool R16>
+__global__ __launch_bounds__(NT) void finalize_norm_kernel(
     NormRows rows, const int32_t* __restrict__ pair_pos, const float* __restrict__ w,
     int k, int H, const uint16_t* residual, const uint16_t* __restrict__ gamma_post,
     const uint16_t* __restrict__ gamma_next, float eps, uint16_t* residual_out,
     uint16_t* __restrict__ normed) {
-  __shared__ float red[FN_WAVES];
+  __shared__ float red[NT / 64];
   const long long t = blockIdx.x;
   int pos[8];
   float wt[8];
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(FN_THREADS) void finalize_norm_kernel(
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int q = threadIdx.x + FN_THREADS * c;
+    const int q = threadIdx.x + NT * c;
     m[c] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (q < n4) {
       f32x4 v[8];  // each expert row is read once: nontemporal
@@ -122,12 +125,12 @@ __global__ __launch_bounds__(FN_THREADS) void finalize_norm_kernel(
       ss += (m[c].x * m[c].x + m[c].y * m[c].y) + (m[c].z * m[c].z + m[c].w * m[c].w);
     }
   }
-  const float inv_m = 1.0f / sqrtf(row_sum(ss, red) / (float)H + eps);
+  const float inv_m = 1.0f / sqrtf(row_sum<NT>(ss, red) / (float)H + eps);
   float ss2 = 0.f;
   const size_t row = (size_t)t * H;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int q = threadIdx.x + FN_THREADS * c;
+    const int q = threadIdx.x + NT * c;
     if (q < n4) {
       const float4 res = bf16x4_to_f32(reinterpret_cast<const uint2*>(residual + row)[q]);
       const float4 gp = bf16x4_to_f32(reinterpret_cast<const uint2*>(gamma_post)[q]);
@@ -138,10 +141,10 @@ __global__ __launch_bounds__(FN_THREADS) void finalize_norm_kernel(
       ss2 += (m[c].x * m[c].x + m[c].y * m[c].y) + (m[c].z * m[c].z + m[c].w * m[c].w);
     }
   }
-  const float inv_r = 1.0f / sqrtf(row_sum(ss2, red) / (float)H + eps);
+  const float inv_r = 1.0f / sqrtf(row_sum<NT>(ss2, red) / (float)H + eps);
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const int q = threadIdx.x + FN_THREADS * c;
+    const int q = threadIdx.x + NT * c;
     if (q < n4) {
       const float4 gn = bf16x4_to_f32(reinterpret_cast<const uint2*>(gamma_next)[q]);
       reinterpret_cast<uint2*>(normed + row)[q] =
@@ -151,12 +154,12 @@ __global__ __launch_bounds__(FN_THREADS) void finalize_norm_kernel(
   }
 }
 
-template <int CH, bool R16>
+template <int NT, int CH, bool R16>
 hipError_t launch_ch(const NormRows& rows, const int32_t* pp, const float* w, int T, int k, int H,
                      const uint16_t* res, const uint16_t* gp, const uint16_t* gn, float eps,
                      uint16_t* res_out, uint16_t* normed, hipStream_t st) {
-  finalize_norm_kernel<CH, R16><<<(unsigned)T, FN_THREADS, 0, st>>>(rows, pp, w, k, H, res, gp, gn,
-                                                                    eps, res_out, normed);
+  finalize_norm_kernel<NT, CH, R16><<<(unsigned)T, NT, 0, st>>>(rows, pp, w, k, H, res, gp, gn,
+                                                                eps, res_out, normed);
   return hipGetLastError();
 }
 
@@ -165,13 +168,20 @@ hipError_t launch_rows(const NormRows& rows, const int32_t* pair_pos, const floa
                        int H, const uint16_t* residual, const uint16_t* gamma_post,
                        const uint16_t* gamma_next, float eps, uint16_t* residual_out,
                        uint16_t* normed, hipStream_t st) {
-  const int ch = (H + 4 * FN_THREADS - 1) / (4 * FN_THREADS);
-#define MOE_FN_CASE(n)                                                                          \
-  case n:                                                                                       \
-    return launch_ch<n, R16>(rows, pair_pos, w, T, k, H, residual, gamma_post, gamma_next, eps, \
-                             residual_out, normed, st)
-  switch (ch) {
-    MOE_FN_CASE(1); MOE_FN_CASE(2); MOE_FN_CASE(3); MOE_FN_CASE(4);
+#define MOE_FN_CASE(nt, n)                                                                        \
+  case n:                                                                                        \
+    return launch_ch<nt, n, R16>(rows, pair_pos, w, T, k, H, residual, gamma_post, gamma_next, eps, \
+                                 residual_out, normed, st)
+  if (T >= kLargeBatch && H <= 4 * 256 * 6) {
+    switch ((H + 4 * 256 - 1) / (4 * 256)) {
+      MOE_FN_CASE(256, 1); MOE_FN_CASE(256, 2); MOE_FN_CASE(256, 3); MOE_FN_CASE(256, 4);
+      MOE_FN_CASE(256, 5); MOE_FN_CASE(256, 6);
+      default:
+        return hipErrorInvalidValue;
+    }
+  }
+  switch ((H + 4 * 1024 - 1) / (4 * 1024)) {
+    MOE_FN_CASE(1024, 1); MOE_FN_CASE(1024, 2); MOE_FN_CASE(1024, 3); MOE_FN_CASE(1024, 4);
     default:
       return hipErrorInvalidValue;
   }

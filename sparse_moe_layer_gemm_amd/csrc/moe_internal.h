@@ -227,7 +227,7 @@ struct StreamSplit {
   int ksplit, ksteps;
 };
 constexpr int kMaxStreamSplit = 16;
-StreamSplit stream_split_plan(long long P, int E, int K, int N, bool gate_up, int step);
+StreamSplit stream_split_plan(long long P, int E, int K, int N, bool gate_up, int wfmt);
 int stream_k_step(int wfmt);  // K values per split unit of the streaming kernels
 // Whether the down kernel forms h from the gate/up partial sums itself (bf16
 // weights, P <= 32, gate/up split); *kr = the K values of h one down split

@@ -62,6 +62,11 @@ def check(y, pp, w, res, gp, gn, eps, k):
     (16, 1088, 1, 1e-6),     # 272 of 1024 lanes; k = 1
     (5, 16384, 8, 1e-6),     # widest row: 4 full chunks per lane
     (1, 64, 2, 0.0),         # smallest row (16 lanes), no epsilon
+    # from 1024 tokens on, 256 lanes per token
+    (1100, 5120, 8, 1e-6),   # 5 chunks per lane
+    (1024, 1088, 3, 1e-5),   # 2 chunks, the second on 16 of 256 lanes
+    (1030, 6144, 8, 1e-6),   # 6 chunks per lane, the most the 256-lane form takes
+    (1040, 8192, 4, 1e-6),   # wider rows: back to 1024 lanes per token
 ])
 def test_finalize_norm_parity(T, H, k, eps):
     y, pp, w, res, gp, gn = make_inputs(11, T, H, k)
@@ -74,8 +79,9 @@ def test_finalize_norm_eps_dominated_rows():
     check(y, pp, w, res, gp, gn, 1e-6, 4)
 
 
-def test_finalize_norm_in_place_and_deterministic():
-    y, pp, w, res, gp, gn = make_inputs(13, 300, 5120, 8)
+@pytest.mark.parametrize("T", [300, 1500])
+def test_finalize_norm_in_place_and_deterministic(T):
+    y, pp, w, res, gp, gn = make_inputs(13, T, 5120, 8)
     a = run(y, pp, w, res, gp, gn, 1e-6)
     b = run(y, pp, w, res, gp, gn, 1e-6, in_place=True)
     c = run(y, pp, w, res, gp, gn, 1e-6)
