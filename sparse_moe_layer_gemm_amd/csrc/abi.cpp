@@ -170,9 +170,10 @@ bool use_tile_kernel(int32_t w_dtype, int64_t P, int32_t E) {
 moe_status check_tile_plan(const moe_expert_weights* w, int64_t T, int32_t k, int32_t E, int32_t H,
                            int32_t I) {
   const int64_t P = T * k;
-  if ((use_tile_kernel(w->dtype, P, E) || w->qmode == MOE_QMODE_F8) &&
-      !moe::expert_tile_fits(P, E, H, I))
-    return MOE_ERR_UNSUPPORTED;
+  const bool tiled = use_tile_kernel(w->dtype, P, E) || w->qmode == MOE_QMODE_F8;
+  if (tiled && !moe::expert_tile_fits(P, E, H, I)) return MOE_ERR_UNSUPPORTED;
+  const bool quant = w->dtype == MOE_FP8_E4M3 || w->dtype == MOE_FP4_E2M1;
+  if (!tiled && quant && P > 0 && !moe::stream_buffers_fit(P, H, I)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -217,6 +217,9 @@ struct F8Buffers {         // device scratch of the fp8-MFMA mode
 // for NVFP4); with few touched experts K is split (StreamGemmArgs::ksplit) and
 // a reduction kernel follows. The grid has one row per expert that can have
 // rows (min(E, rows)).
+// Whether the FP8 / NVFP4 streaming kernels can address A (P rows of H or I
+// bf16 values) and one expert's weights with 31-bit byte offsets.
+bool stream_buffers_fit(long long P, int H, int I);
 hipError_t launch_expert_stream(int wfmt, bool gate_up, const StreamGemmArgs& a, hipStream_t st);
 // Split-K of the streaming kernels for few touched experts: number of splits
 // of a K-deep product with N output columns over P rows (at most min(E, P)
