@@ -217,14 +217,19 @@ def source_sha256(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(path=TRAFFIC_FILE, src=STREAM_SRC):
+QUANT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "nvfp4_moe_experts_counters.md")
+
+
+def measured_traffic(path=TRAFFIC_FILE, src=STREAM_SRC, key=None):
     """HBM bytes per expert stage (moe_experts launch), from a committed rocprofv3 counter
-    summary, or None when it is missing or the kernel source changed since."""
+    summary (its "TRAFFIC_JSON:" line, or "TRAFFIC_JSON[key]:" for one of several
+    workloads), or None when it is missing or the kernel source changed since."""
+    tag = "TRAFFIC_JSON:" if key is None else f"TRAFFIC_JSON[{key}]:"
     try:
         with open(path) as f:
             for line in f:
-                if line.startswith("TRAFFIC_JSON:"):
-                    d = json.loads(line.split(":", 1)[1])
+                if line.startswith(tag):
+                    d = json.loads(line[len(tag):])
                     if d.get("source_sha256") == source_sha256(src):
                         return d["hbm_bytes_per_launch"]
     except (OSError, ValueError, KeyError):
@@ -604,7 +609,8 @@ def main():
                                "achieved": tb if hbm_frac >= mfma_frac else tf,
                                "peak": HBM_PEAK_GBS if hbm_frac >= mfma_frac else BF16_PEAK_TFLOPS,
                                "unit": "GB/s" if hbm_frac >= mfma_frac else "TFLOP/s",
-                               "frac": max(hbm_frac, mfma_frac), "traffic": None,
+                               "frac": max(hbm_frac, mfma_frac),
+                               "traffic": measured_traffic(QUANT_TRAFFIC_FILE, TILE_SRC, "nvfp4_t4096_w"),
                                "weight_GBps": round(tb, 1), "TFLOPs": round(tf, 1)}}
         if not a.no_cpu:
             progress("timing the CPU oracle on an NVFP4 token sample")
@@ -631,7 +637,8 @@ def main():
                          "achieved": tb8 if h8 >= m8 else tf8,
                          "peak": HBM_PEAK_GBS if h8 >= m8 else FP8_PEAK_TFLOPS,
                          "unit": "GB/s" if h8 >= m8 else "TFLOP/s",
-                         "frac": max(h8, m8), "traffic": None,
+                         "frac": max(h8, m8),
+                         "traffic": measured_traffic(QUANT_TRAFFIC_FILE, TILE_SRC, "nvfp4_t4096_f8"),
                          "weight_GBps": round(tb8, 1), "TFLOPs": round(tf8, 1)}}
         if not a.no_cpu:
             progress("timing the CPU oracle (fp8-MFMA mode) on an NVFP4 token sample")
@@ -651,7 +658,8 @@ def main():
             "stages_ms": {k: round(v, 4) for k, v in d_stage.items()},
             "roofline": {"bound": "hbm", "kernel": "moe_experts (NVFP4 weights, stream, bf16 MFMA)",
                          "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": d_gbs / HBM_PEAK_GBS, "traffic": None}}
+                         "frac": d_gbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic(QUANT_TRAFFIC_FILE, STREAM_SRC, "nvfp4_t128")}}
         del qw, qd
 
     head, head_cfg = (dec_line, dec_cfg) if a.workload == "decode" else (pre_line, pre_cfg)

@@ -55,8 +55,12 @@ __device__ __forceinline__ u32x4 load_u32x4(const void* p) {
 // Weight loads: every weight byte is read once per pass, so they bypass the
 // caches' retention (nontemporal); measured on gfx950 this lifts a plain
 // streaming read from ~6.3 to ~7.0 TB/s.
+#ifndef MOE_BF16_NT
+#define MOE_BF16_NT 1
+#endif
 __device__ __forceinline__ u32x4 load_w(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  if constexpr (MOE_BF16_NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return *reinterpret_cast<const u32x4*>(p);
 }
 
 // Rows of the A operand for one 32-row pass: pointer per fragment + validity.

@@ -32,6 +32,20 @@ def test_traffic_lookup_follows_the_source_hash(tmp_path):
     assert bench.measured_traffic(str(tmp_path / "missing.md"), str(src)) is None
 
 
+def test_keyed_traffic_lines_pick_their_workload(tmp_path):
+    src = tmp_path / "kernel.hip"
+    src.write_text("// a kernel\n")
+    h = bench.source_sha256(str(src))
+    summary = tmp_path / "summary.md"
+    summary.write_text("".join(
+        f"TRAFFIC_JSON[{k}]: " + json.dumps({"source_sha256": h, "hbm_bytes_per_launch": v}) + "\n"
+        for k, v in (("a", 10), ("b", 20))))
+    assert bench.measured_traffic(str(summary), str(src), "b") == 20
+    assert bench.measured_traffic(str(summary), str(src), "a") == 10
+    assert bench.measured_traffic(str(summary), str(src), "c") is None
+    assert bench.measured_traffic(str(summary), str(src)) is None  # no unkeyed line
+
+
 def test_cpu_baseline_record():
     cfg = synth.CONFIGS["tiny_fp32"]
     wr, bias = synth.gen_router(cfg)
