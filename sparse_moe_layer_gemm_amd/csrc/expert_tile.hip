@@ -613,19 +613,27 @@ struct QShape {
   static constexpr int NW = 8;
   static constexpr int BM = T::BM, BN = T::BN, WN = T::WN, JT = T::JT;
   static constexpr int COL = WF == W_FP4 ? 16 : 32;   // code bytes per column per K step
-  static constexpr int SCL = WF == W_FP4 ? 4 : 0;     // scale bytes per column per K step
   static constexpr int A_STAGE = T::A_STAGE;
-  static constexpr int B_STAGE = BN * COL;
-  static constexpr int S_STAGE = BN * SCL;
-  static constexpr int STAGE = A_STAGE + B_STAGE + S_STAGE;
-  static constexpr int PIPE = NSTAGE * STAGE;
+  // codes arrive as 64 B per column (CSS K steps) in code stages of the whole
+  // tile's columns, three in LDS; a load instruction covers 16 columns x 64 B
+  static constexpr int CSS = 64 / COL;                // K steps per code stage
+  static constexpr int CSLOT = BN * 64;               // bytes of a code stage
+  static constexpr int NCS = 3;
+  // NVFP4 block scales: 16 B per column (8 K steps) per scale stage, three in LDS
+  static constexpr int SSS = 8;                       // K steps per scale stage
+  static constexpr int SSLOT = WF == W_FP4 ? BN * 16 : 0;
+  static constexpr int NSS = 3;
+  static constexpr int C_OFF = NSTAGE * A_STAGE;      // code stages after the A stages
+  static constexpr int S_OFF = C_OFF + NCS * CSLOT;   // then the scale stages
+  static constexpr int PIPE = S_OFF + NSS * SSLOT;
   static constexpr int EPI = NW * 8192;               // epilogue strips (32 x 64 fp32 each)
   static constexpr int LDS = PIPE > EPI ? PIPE : EPI;
   static constexpr int QA = A_STAGE / 1024 / NW;      // 1 KB A loads per wavefront
-  static constexpr int QB = B_STAGE / 1024 / NW;      // 1 KB code loads per wavefront
-  static constexpr int QS = S_STAGE / 256 / NW;       // 256 B scale loads per wavefront
-  static constexpr int PER_STEP = QA + QB + QS;       // loads per wavefront per K step
-  static_assert(QA == 1 && PER_STEP == 3, "the waits below assume 3 loads per K step");
+  static constexpr int QB = CSLOT / CSS / 1024 / NW;  // code loads per wavefront per K step
+  // loads per wavefront per K step, not counting the scale load one K step in 8 adds
+  static constexpr int PER_STEP = QA + QB;
+  static_assert(QA == 1 && NW * QB * CSS * 16 == BN, "every column's code stage loaded once");
+  static_assert(PIPE <= 160 * 1024, "LDS");
 };
 
 __device__ __forceinline__ u32x2 lds_b64(uint32_t addr) {
@@ -698,35 +706,38 @@ __global__ __launch_bounds__(512, 1) void tile_q_kernel(StreamGemmArgs a,
     return col < N ? col : 0;
   };
   const uint8_t* wq = static_cast<const uint8_t*>(a.w);
-  const size_t row_bytes = WF == W_FP4 ? (size_t)K / 2 : (size_t)K;
-  // codes: the fp4 load of wavefront w covers LDS columns 64 w .. +63 (16 B
-  // each); fp8 load q covers 32 columns (two 16 B halves each)
-  const uint8_t* bsrc[S::QB];
+  const int row_bytes = WF == W_FP4 ? K / 2 : K;
+  // code stage cs holds K steps CSS cs .. CSS cs + CSS - 1 of every column:
+  // 16-column block ib at ib * 1024, 16 B chunk q of the stage's 64 B at
+  // + 256 q, column c of the block at + 16 c (a load's lane l is chunk l / 16
+  // of column l % 16). Wavefront w loads blocks 4 w .. 4 w + 3, QB per K step.
+  const uint8_t* csrc[S::CSS * S::QB];
 #pragma unroll
-  for (int q = 0; q < S::QB; ++q) {
-    const int qi = wave * S::QB + q;
-    if (WF == W_FP4)
-      bsrc[q] = wq + ((size_t)e * N + mcol(64 * qi + lane)) * row_bytes;
-    else
-      bsrc[q] = wq + ((size_t)e * N + mcol(32 * qi + (lane >> 1))) * row_bytes + 16 * (lane & 1);
-  }
+  for (int p = 0; p < S::CSS * S::QB; ++p)
+    csrc[p] = wq + ((size_t)e * N + mcol(16 * (4 * wave + p) + (lane & 15))) * row_bytes + 16 * (lane >> 4);
+  // scale stage t holds 16 B per column (K steps 8 t .. 8 t + 7) at 16 column;
+  // wavefront w loads its 64 columns' 16 B, lane l column 64 w + l
   const uint8_t* ssrc = WF == W_FP4 ? static_cast<const uint8_t*>(a.w_scale) +
                                           ((size_t)e * N + mcol(64 * wave + lane)) * (size_t)(K / 16)
                                     : nullptr;
+  // code piece p of stage cs (chunks past the row, in a K tail, read its start)
+  auto load_code = [&](int cs, int p) {
+    const int ko = 64 * cs + 16 * (lane >> 4);
+    dma16(csrc[p] + (ko + 16 <= row_bytes ? 64 * cs : -16 * (lane >> 4)),
+          smem + S::C_OFF + (cs % S::NCS) * S::CSLOT + (4 * wave + p) * 1024);
+  };
+  auto load_scale = [&](int t) {
+    const int ko = 16 * t;
+    dma16(ssrc + (ko + 16 <= K / 16 ? ko : 0), smem + S::S_OFF + (t % S::NSS) * S::SSLOT + 64 * wave * 16);
+  };
+  // the loads issued for K step kt (three steps ahead): one scale stage piece
+  // (NVFP4, wavefront kt % 8, for the next scale stage), the A rows, and
+  // piece kt % CSS of the next code stage
   auto issue = [&](int kt, int st) {
-    uint8_t* As = smem + st * S::STAGE;
-    uint8_t* Bs = As + S::A_STAGE;
-    uint8_t* Ss = Bs + S::B_STAGE;
-    dma16(asrc + kt * TBK, As + 16 * wave * 64);
+    if (WF == W_FP4 && (kt & 7) == wave) load_scale(kt / S::SSS + 1);
+    dma16(asrc + kt * TBK, smem + st * S::A_STAGE + 16 * wave * 64);
 #pragma unroll
-    for (int q = 0; q < S::QB; ++q) {
-      const int qi = wave * S::QB + q;
-      if (WF == W_FP4)
-        dma16(bsrc[q] + 16 * kt, Bs + 64 * qi * 16);
-      else
-        dma16(bsrc[q] + 32 * kt, Bs + 32 * qi * 32);
-    }
-    if (WF == W_FP4) dma4(ssrc + ((2 * kt) & ~3), Ss + 64 * wave * 4);
+    for (int q = 0; q < S::QB; ++q) load_code(kt / S::CSS + 1, (kt % S::CSS) * S::QB + q);
   };
 
   f32x16 acc[4][JT];
@@ -753,8 +764,9 @@ __global__ __launch_bounds__(512, 1) void tile_q_kernel(StreamGemmArgs a,
 #pragma unroll
   for (int j = 0; j < JT; ++j) {
     const int c = bcol(j) + l32;
-    boff[j] = S::A_STAGE + c * S::COL + (S::COL / 2) * kh;
-    soff[j] = S::A_STAGE + S::B_STAGE + c * 4 + kh;
+    // this lane's 8 B (E2M1) or 16 B (E4M3) of column c at K step 0 of a code stage
+    boff[j] = (c >> 4) * 1024 + 16 * (c & 15) + (WF == W_FP4 ? 8 * kh : 256 * kh);
+    soff[j] = c * 16 + kh;
   }
   // first half of a K step: A (K half 0), the codes and the block scales;
   // second half: A (K half 1)
@@ -767,24 +779,26 @@ __global__ __launch_bounds__(512, 1) void tile_q_kernel(StreamGemmArgs a,
     u32x4 a[4];
   };
   auto read0 = [&](FragQ0& f, int st, int kt) {
-    const uint32_t base = lds0 + st * S::STAGE;
+    const uint32_t cbase = lds0 + S::C_OFF + ((kt / S::CSS) % S::NCS) * S::CSLOT + (kt % S::CSS) * (S::COL / 16) * 256;
 #pragma unroll
     for (int j = 0; j < JT; ++j) {
       if constexpr (WF == W_FP4)
-        f.b[j] = lds_b64(base + boff[j]);
+        f.b[j] = lds_b64(cbase + boff[j]);
       else
-        f.b[j] = lds_b128(base + boff[j]);
+        f.b[j] = lds_b128(cbase + boff[j]);
     }
     if (WF == W_FP4) {
-      const uint32_t sh = 2 * (kt & 1);
+      // block 2 kt + kh: byte 2 (kt % 8) + kh of the column's 16 B
+      const uint32_t sbase = lds0 + S::S_OFF + ((kt / S::SSS) % S::NSS) * S::SSLOT + 2 * (kt % S::SSS);
 #pragma unroll
-      for (int j = 0; j < JT; ++j) f.sc[j] = lds_byte(base + soff[j] + sh);
+      for (int j = 0; j < JT; ++j) f.sc[j] = lds_byte(sbase + soff[j]);
     }
+    const uint32_t base = lds0 + st * S::A_STAGE;
 #pragma unroll
     for (int i = 0; i < 4; ++i) f.a[i] = lds_b128(base + aoff[0][i]);
   };
   auto read1 = [&](FragQ1& f, int st) {
-    const uint32_t base = lds0 + st * S::STAGE;
+    const uint32_t base = lds0 + st * S::A_STAGE;
 #pragma unroll
     for (int i = 0; i < 4; ++i) f.a[i] = lds_b128(base + aoff[1][i]);
   };
@@ -821,14 +835,19 @@ __global__ __launch_bounds__(512, 1) void tile_q_kernel(StreamGemmArgs a,
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i][j] = mfma32(af[i], bq[s2][j], acc[i][j]);
   };
-  // Pipeline as in the bf16 kernel: "step kt+1 landed" is vmcnt(3) once three
-  // steps are in flight; f1 (4 reads) is read while f0's MFMAs run, f0 of the
-  // next step (6 or 8 reads) while f1's run.
+  // Pipeline as in the bf16 kernel: "step kt+1 landed" is vmcnt(PER_STEP)
+  // once three steps are in flight (a K step's scale load is issued first, so
+  // counting it out only waits for it early); f1 (4 reads) is read while f0's
+  // MFMAs run, f0 of the next step (6 or 8 reads) while f1's run. The first
+  // code and scale stages are loaded before the first three steps.
   const int nk = K / TBK;
+  if (WF == W_FP4) load_scale(0);
+#pragma unroll
+  for (int p = 0; p < S::CSS * S::QB; ++p) load_code(0, p);
   issue(0, 0);
   issue(nk > 1 ? 1 : nk - 1, 1);
   issue(nk > 2 ? 2 : nk - 1, 2);
-  asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * S::PER_STEP) : "memory");
   __builtin_amdgcn_s_barrier();
   FragQ0 f0;
   FragQ1 f1;
@@ -840,7 +859,7 @@ __global__ __launch_bounds__(512, 1) void tile_q_kernel(StreamGemmArgs a,
     MOE_LGK_WAIT0(f0, 4);
     dequant(f0);
     mfma_half(f0.a, 0);
-    asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(S::PER_STEP) : "memory");
     __builtin_amdgcn_s_barrier();
     issue(kt + 3 < nk ? kt + 3 : nk - 1, (kt + 3) % NSTAGE);
     read0(f0, (kt + 1) % NSTAGE, kt + 1);
@@ -945,34 +964,36 @@ struct F8Shape {
   using T = TileShape<WM>;
   static constexpr int BM = T::BM, BN = T::BN, WN = T::WN;
   static constexpr int A_STAGE = BM * 64;                            // 64 codes per row
-  static constexpr int B_STAGE = BN * (WF == W_FP8 ? 64 : 32);
-  static constexpr int S_STAGE = WF == W_FP4 ? BN * 4 : 0;
-  static constexpr int STAGE = A_STAGE + B_STAGE + S_STAGE;
+  // E4M3 codes: 64 B per column per K step, in the pipeline stages. E2M1
+  // codes: 64 B per column per two K steps (code stages of the whole tile's
+  // columns, three in LDS, a load covering 16 columns), and their block
+  // scales 16 B per column per four K steps (scale stages, three in LDS, a
+  // load covering 64 columns).
+  static constexpr int B_STAGE = WF == W_FP8 ? BN * 64 : 0;
+  static constexpr int STAGE = A_STAGE + B_STAGE;
+  static constexpr int CSLOT = WF == W_FP4 ? BN * 64 : 0;
+  static constexpr int SSLOT = WF == W_FP4 ? BN * 16 : 0;
   static constexpr int ROWB = 32;                                    // bytes of row data per row
   static constexpr int ROWDATA = BM * ROWB;
-  static constexpr int NST = (4 * STAGE + ROWDATA <= 163840) ? 4 : 3;
-  static constexpr int PIPE = NST * STAGE > 65536 ? NST * STAGE : 65536;
+  static constexpr int SIDE = 3 * CSLOT + 3 * SSLOT;                 // E2M1 code and scale stages
+  static constexpr int NST = (4 * STAGE + SIDE + ROWDATA <= 163840) ? 4 : 3;
+  static constexpr int C_OFF = NST * STAGE;
+  static constexpr int S_OFF = C_OFF + 3 * CSLOT;
+  static constexpr int PIPE = NST * STAGE + SIDE > 65536 ? NST * STAGE + SIDE : 65536;
   static constexpr int LDS = PIPE + ROWDATA;
   static constexpr int QA = BM / 64;                                 // 1 KB A loads per wavefront
   static constexpr int QB = WF == W_FP8 ? BN / 64 : BN / 128;        // 1 KB code loads per wavefront
-  static constexpr int QS = WF == W_FP4 ? BN / 256 : 0;              // 256 B scale loads per wavefront
-  static constexpr int PER_STEP = QA + QB + QS;
+  // loads per wavefront per K step (E2M1: not counting the scale load every
+  // other K step, issued first, so that counting it out only waits for it early)
+  static constexpr int PER_STEP = QA + QB;
+  static_assert(WF == W_FP8 || 4 * QB * 2 * 16 == BN, "E2M1: every column's code stage loaded once");
+  static_assert(WF == W_FP8 || BN == 512 || BN == 256, "E2M1: 8 or 4 scale loads per scale stage");
 };
 
 template <int N>
 __device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N <= 40, "vmcnt range");
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if constexpr (N == 7) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-  else if constexpr (N == 14) asm volatile("s_waitcnt vmcnt(14)" ::: "memory");
-  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if constexpr (N == 20) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
-  else if constexpr (N == 21) asm volatile("s_waitcnt vmcnt(21)" ::: "memory");
-  else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-  else if constexpr (N == 30) asm volatile("s_waitcnt vmcnt(30)" ::: "memory");
-  else static_assert(N < 0, "add this vmcnt value");
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // 8 E2M1 codes (one dword) x block scale (p2 * fm8: the scale's power of two,
@@ -1058,39 +1079,64 @@ __global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmAr
   const uint8_t* wq = static_cast<const uint8_t*>(a.w);
   // B: E4M3 codes like A (16 columns x 64 B per load, swizzled granules);
   // E2M1 codes 32 B per column (two lanes per column), scale dwords one per column
-  const uint8_t* bsrc[S::QB];
+  // E2M1: code stage cs holds K steps 2 cs, 2 cs + 1 of every column (64 B):
+  // 16-column block ib at ib * 1024, 16 B chunk q at + 256 q, column c of the
+  // block at + 16 c (a load's lane l is chunk l / 16 of column l % 16);
+  // wavefront w loads blocks 2 QB w .. +2 QB, QB per K step. Scale stage t
+  // holds 16 B per column (K steps 4 t .. 4 t + 3) at 16 column; its loads
+  // cover 64 columns each.
+  const uint8_t* bsrc[WF == W_FP8 ? S::QB : 2 * S::QB];
+  if constexpr (WF == W_FP8) {
 #pragma unroll
-  for (int q = 0; q < S::QB; ++q) {
-    if (WF == W_FP8) {
+    for (int q = 0; q < S::QB; ++q) {
       const int col = (S::BN / 4) * wave + 16 * q + (lane >> 2);
       const int lg = (lane & 3) ^ ((col >> 2) & 3);
       bsrc[q] = wq + ((size_t)e * N + mcol(col)) * K + 16 * lg;
-    } else {
-      const int qi = wave * S::QB + q;
-      bsrc[q] = wq + ((size_t)e * N + mcol(32 * qi + (lane >> 1))) * (size_t)(K / 2) + 16 * (lane & 1);
     }
-  }
-  const uint8_t* ssrc[S::QS > 0 ? S::QS : 1];
+  } else {
 #pragma unroll
-  for (int q = 0; q < S::QS; ++q) {
-    const int qi = wave * S::QS + q;
-    ssrc[q] = static_cast<const uint8_t*>(a.w_scale) + ((size_t)e * N + mcol(64 * qi + lane)) * (size_t)(K / 16);
+    for (int p = 0; p < 2 * S::QB; ++p)
+      bsrc[p] = wq + ((size_t)e * N + mcol(16 * (2 * S::QB * wave + p) + (lane & 15))) * (size_t)(K / 2) +
+                16 * (lane >> 4);
   }
+  constexpr int NSP = WF == W_FP4 ? S::BN / 64 : 1;  // scale loads per scale stage
+  const uint8_t* ssrc = WF == W_FP4 ? static_cast<const uint8_t*>(a.w_scale) + (size_t)e * N * (size_t)(K / 16)
+                                    : nullptr;
+  // E2M1 code piece p (of this wavefront's 2 QB) of code stage cs; chunks past
+  // the row (a K tail) read the row's start
+  auto load_code = [&](int cs, int p) {
+    const int ko = 64 * cs + 16 * (lane >> 4);
+    dma16(bsrc[p] + (ko + 16 <= K / 2 ? 64 * cs : -16 * (lane >> 4)),
+          smem + S::C_OFF + (cs % 3) * S::CSLOT + (2 * S::QB * wave + p) * 1024);
+  };
+  // scale piece sp (64 columns) of scale stage t
+  auto load_scale = [&](int t, int sp) {
+    const int ko = 16 * t;
+    dma16(ssrc + (size_t)mcol(64 * sp + lane) * (size_t)(K / 16) + (ko + 16 <= K / 16 ? ko : 0),
+          smem + S::S_OFF + (t % 3) * S::SSLOT + 64 * sp * 16);
+  };
+  // the loads issued for K step kt (AHEAD steps ahead). E2M1: first, on two
+  // wavefronts (even kt: 0, 1; odd kt: 2, 3), one scale piece of stage
+  // (kt + 3) / 4; then A; then half (kt + 1) % 2 of code stage (kt + 1) / 2.
+  // (Each stage is loaded after the stage three before it, same LDS slot, was
+  // last read; the first pieces repeat stage 0, loaded before the loop.)
   auto issue = [&](int kt, int st) {
     uint8_t* As = smem + st * S::STAGE;
-    uint8_t* Bs = As + S::A_STAGE;
-    uint8_t* Ss = Bs + S::B_STAGE;
+    if constexpr (WF == W_FP4) {
+      if ((kt & 1) == (wave >> 1)) {
+        const int sp = NSP == 8 ? 2 * ((kt + 3) & 3) + (wave & 1) : ((kt + 3) & 3);
+        if (NSP == 8 || (wave & 1) == 0) load_scale((kt + 3) >> 2, sp);
+      }
+    }
 #pragma unroll
     for (int q = 0; q < S::QA; ++q) dma16(asrc[q] + 64 * kt, As + ((S::BM / 4) * wave + 16 * q) * 64);
 #pragma unroll
     for (int q = 0; q < S::QB; ++q) {
       if (WF == W_FP8)
-        dma16(bsrc[q] + 64 * kt, Bs + ((S::BN / 4) * wave + 16 * q) * 64);
+        dma16(bsrc[q] + 64 * kt, As + S::A_STAGE + ((S::BN / 4) * wave + 16 * q) * 64);
       else
-        dma16(bsrc[q] + 32 * kt, Bs + (wave * S::QB + q) * 1024);
+        load_code((kt + 1) >> 1, ((kt + 1) & 1) * S::QB + q);
     }
-#pragma unroll
-    for (int q = 0; q < S::QS; ++q) dma4(ssrc[q] + 4 * kt, Ss + (wave * S::QS + q) * 256);
   };
 
   f32x16 acc[4][4];
@@ -1126,11 +1172,11 @@ __global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmAr
     if (WF == W_FP8) {
       boff[j][0] = S::A_STAGE + a_off(c, kh);
       boff[j][1] = S::A_STAGE + a_off(c, kh + 2);
-    } else {  // E2M1: 8 B = 16 codes per run
-      boff[j][0] = S::A_STAGE + c * 32 + 8 * kh;
-      boff[j][1] = S::A_STAGE + c * 32 + 16 + 8 * kh;
+    } else {  // E2M1: run r (8 B = 16 codes) = 16 B chunk r of the K step
+      boff[j][0] = (c >> 4) * 1024 + 16 * (c & 15) + 8 * kh;
+      boff[j][1] = boff[j][0] + 256;
     }
-    soff[j] = S::A_STAGE + S::B_STAGE + c * 4;
+    soff[j] = c * 16;
   }
   // One half of a K step: all four A fragments, the B codes of two column
   // tiles (j = 2h, 2h+1) and, for the down GEMM, the four rows' block scales
@@ -1146,6 +1192,10 @@ __global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmAr
   };
   auto read_half = [&](Half& f, int st, int h, int kt) {
     const uint32_t base = lds0 + st * S::STAGE;
+    // E2M1: chunks 2 (kt % 2), +1 of code stage kt / 2; scale bytes 4 (kt % 4) .. +3
+    // of scale stage kt / 4
+    const uint32_t cbase = lds0 + S::C_OFF + ((kt >> 1) % 3) * S::CSLOT + (kt & 1) * 512;
+    const uint32_t sbase = lds0 + S::S_OFF + ((kt >> 2) % 3) * S::SSLOT + 4 * (kt & 3);
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const int j = 2 * h + jj;
@@ -1153,9 +1203,9 @@ __global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmAr
         f.b[jj][0] = lds_b128(base + boff[j][0]);
         f.b[jj][1] = lds_b128(base + boff[j][1]);
       } else {
-        f.q[jj][0] = lds_b64(base + boff[j][0]);
-        f.q[jj][1] = lds_b64(base + boff[j][1]);
-        f.sc[jj] = lds_b32(base + soff[j]);
+        f.q[jj][0] = lds_b64(cbase + boff[j][0]);
+        f.q[jj][1] = lds_b64(cbase + boff[j][1]);
+        f.sc[jj] = lds_b32(sbase + soff[j]);
       }
     }
 #pragma unroll
@@ -1249,6 +1299,11 @@ __global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmAr
   // Pipeline as in the bf16 kernel, with NST stages and NST - 1 steps in flight.
   constexpr int AHEAD = S::NST - 1;
   const int nk = K / 64;
+  if constexpr (WF == W_FP4) {  // code stage 0 and scale stage 0
+#pragma unroll
+    for (int p = 0; p < 2 * S::QB; ++p) load_code(0, p);
+    for (int sp = wave; sp < NSP; sp += 4) load_scale(0, sp);
+  }
   issue(0, 0);
   issue(nk > 1 ? 1 : nk - 1, 1);
   if constexpr (AHEAD == 3) issue(nk > 2 ? 2 : nk - 1, 2);
