@@ -160,15 +160,19 @@ __device__ __forceinline__ void store_rows16(const float* strip, int lane, int r
 }
 
 // M-tile table, in expert order: ceil(rows / bm) tiles of bm rows per expert.
+// With merge > 0 an expert's last tile also takes a tail of up to `merge`
+// rows (tiles of bm rows, the last of up to bm + merge).
 __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restrict__ offsets,
-                                                         int E, int bm,
+                                                         int E, int bm, int merge,
                                                          int32_t* __restrict__ tile_e,
                                                          int32_t* __restrict__ tile_m0,
                                                          int32_t* __restrict__ n_tiles) {
   __shared__ int cnt[256];
   const int e = threadIdx.x;
   const int rows = (e < E) ? offsets[e + 1] - offsets[e] : 0;
-  const int c = (rows + bm - 1) / bm;
+  int c = (rows - merge + bm - 1) / bm;
+  if (rows > 0 && c < 1) c = 1;
+  if (rows <= 0) c = 0;
   cnt[e] = c;
   __syncthreads();
   for (int d = 1; d < 256; d <<= 1) {  // inclusive scan
@@ -613,7 +617,7 @@ struct QShape {
   static constexpr int NW = 8;
   static constexpr int BM = T::BM, BN = T::BN, WN = T::WN, JT = T::JT;
   static constexpr int COL = WF == W_FP4 ? 16 : 32;   // code bytes per column per K step
-  static constexpr int A_STAGE = T::A_STAGE;
+  static constexpr int A_STAGE = 160 * TBK * 2;       // up to 160 rows x 64 B (a merged tail)
   // codes arrive as 64 B per column (CSS K steps) in code stages of the whole
   // tile's columns, three in LDS; a load instruction covers 16 columns x 64 B
   static constexpr int CSS = 64 / COL;                // K steps per code stage
@@ -659,41 +663,32 @@ __device__ __forceinline__ void dma4(const void* g, uint8_t* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
 }
 
-template <int WF, bool GATE_UP>
-__global__ __launch_bounds__(512, 1) void tile_q_kernel(StreamGemmArgs a,
-                                                        const int32_t* __restrict__ tile_e,
-                                                        const int32_t* __restrict__ tile_m0,
-                                                        const int32_t* __restrict__ n_tiles_p,
-                                                        int NT) {
+// One 128-row (NF = 4) or up to 160-row (NF = 5: an expert's last tile
+// with its <= 32-row tail merged in) x 512-column tile of a quantised
+// grouped GEMM.
+template <int WF, bool GATE_UP, int NF>
+__device__ __forceinline__ void tile_q_body(const StreamGemmArgs& a, uint8_t* smem, int e, int m0,
+                                            int nt, int r0, int cnt) {
   using S = QShape<WF>;
   constexpr int JT = S::JT;
-  __shared__ __align__(1024) uint8_t smem[S::LDS];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wn = wave;
-
-  const int total = *n_tiles_p * NT;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int per = (total + 7) >> 3;
-  if (slot >= per) return;
-  const int w = xcd * per + slot;
-  if (w >= total) return;
-  const int mt = w / NT, nt = w - mt * NT;
-  const int e = tile_e[mt];
-  const int m0 = tile_m0[mt];
-  const int r0 = a.offsets[e];
-  const int cnt = a.offsets[e + 1] - r0;
+  (void)tid;
   const int K = a.K, N = a.N;
 
   // A: as in the bf16 kernel (gathered rows, 16 rows per 1 KB load; wavefront
-  // w loads rows 16 w .. 16 w + 15)
-  const uint16_t* asrc;
-  {
-    const int row = 16 * wave + (lane >> 2);
+  // w loads rows 16 w .. 16 w + 15, and with a fifth row fragment wavefronts
+  // 0 and 1 also rows 128 + 16 w ..)
+  constexpr int NX = NF > 4 ? 1 : 0;  // extra A loads of wavefronts 0 and 1
+  const uint16_t* asrc[1 + NX];
+#pragma unroll
+  for (int q = 0; q <= NX; ++q) {
+    const int row = 128 * q + 16 * (q ? (wave & 1) : wave) + (lane >> 2);
     const int lg = (lane & 3) ^ ((row >> 2) & 3);
     size_t grow = 0;
     if (m0 + row < cnt)
       grow = GATE_UP ? (size_t)(a.sorted_pair[r0 + m0 + row] / a.k) : (size_t)(r0 + m0 + row);
-    asrc = a.a + grow * K + 8 * lg;
+    asrc[q] = a.a + grow * K + 8 * lg;
   }
   // matrix column of LDS column c (gate/up: BN/2 gate, then the matching up)
   auto mcol = [&](int c) -> int {
@@ -735,14 +730,15 @@ __global__ __launch_bounds__(512, 1) void tile_q_kernel(StreamGemmArgs a,
   // piece kt % CSS of the next code stage
   auto issue = [&](int kt, int st) {
     if (WF == W_FP4 && (kt & 7) == wave) load_scale(kt / S::SSS + 1);
-    dma16(asrc + kt * TBK, smem + st * S::A_STAGE + 16 * wave * 64);
+    if (NX && wave < 2) dma16(asrc[NX] + kt * TBK, smem + st * S::A_STAGE + (128 + 16 * wave) * 64);
+    dma16(asrc[0] + kt * TBK, smem + st * S::A_STAGE + 16 * wave * 64);
 #pragma unroll
     for (int q = 0; q < S::QB; ++q) load_code(kt / S::CSS + 1, (kt % S::CSS) * S::QB + q);
   };
 
-  f32x16 acc[4][JT];
+  f32x16 acc[NF][JT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NF; ++i)
 #pragma unroll
     for (int j = 0; j < JT; ++j)
 #pragma unroll
@@ -756,11 +752,11 @@ __global__ __launch_bounds__(512, 1) void tile_q_kernel(StreamGemmArgs a,
   };
   const int l32 = lane & 31, kh = lane >> 5;
   const uint32_t lds0 = (uint32_t)(size_t)(lds_u8*)smem;
-  uint32_t aoff[2][4], boff[JT], soff[JT];
+  uint32_t aoff[2][NF], boff[JT], soff[JT];
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) aoff[s2][i] = a_off(32 * i + l32, 2 * kh + s2);
+    for (int i = 0; i < NF; ++i) aoff[s2][i] = a_off(32 * i + l32, 2 * kh + s2);
 #pragma unroll
   for (int j = 0; j < JT; ++j) {
     const int c = bcol(j) + l32;
@@ -771,12 +767,12 @@ __global__ __launch_bounds__(512, 1) void tile_q_kernel(StreamGemmArgs a,
   // first half of a K step: A (K half 0), the codes and the block scales;
   // second half: A (K half 1)
   struct FragQ0 {
-    u32x4 a[4];
+    u32x4 a[NF];
     typename QRaw<WF>::type b[JT];
     uint32_t sc[JT];
   };
   struct FragQ1 {
-    u32x4 a[4];
+    u32x4 a[NF];
   };
   auto read0 = [&](FragQ0& f, int st, int kt) {
     const uint32_t cbase = lds0 + S::C_OFF + ((kt / S::CSS) % S::NCS) * S::CSLOT + (kt % S::CSS) * (S::COL / 16) * 256;
@@ -795,24 +791,42 @@ __global__ __launch_bounds__(512, 1) void tile_q_kernel(StreamGemmArgs a,
     }
     const uint32_t base = lds0 + st * S::A_STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[i] = lds_b128(base + aoff[0][i]);
+    for (int i = 0; i < NF; ++i) f.a[i] = lds_b128(base + aoff[0][i]);
   };
   auto read1 = [&](FragQ1& f, int st) {
     const uint32_t base = lds0 + st * S::A_STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[i] = lds_b128(base + aoff[1][i]);
+    for (int i = 0; i < NF; ++i) f.a[i] = lds_b128(base + aoff[1][i]);
   };
+  // (the fifth A fragment, when there is one, as an operand of its own wait)
 #define MOE_LGK_WAIT0(f, pending)                                                              \
-  asm volatile("s_waitcnt lgkmcnt(" #pending ")"                                              \
-               : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0]),         \
-                 "+v"(f.b[1]), "+v"(f.sc[0]), "+v"(f.sc[1])                                    \
-               :                                                                               \
-               : "memory")
+  do {                                                                                         \
+    if constexpr (NF == 5)                                                                     \
+      asm volatile("s_waitcnt lgkmcnt(%9)"                                                    \
+                   : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0]),     \
+                     "+v"(f.b[1]), "+v"(f.sc[0]), "+v"(f.sc[1]), "+v"(f.a[NF - 1])            \
+                   : "n"(pending)                                                              \
+                   : "memory");                                                                \
+    else                                                                                       \
+      asm volatile("s_waitcnt lgkmcnt(%8)"                                                    \
+                   : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.b[0]),     \
+                     "+v"(f.b[1]), "+v"(f.sc[0]), "+v"(f.sc[1])                                \
+                   : "n"(pending)                                                              \
+                   : "memory");                                                                \
+  } while (0)
 #define MOE_LGK_WAIT1(f, pending)                                                              \
-  asm volatile("s_waitcnt lgkmcnt(" #pending ")"                                              \
-               : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3])                        \
-               :                                                                               \
-               : "memory")
+  do {                                                                                         \
+    if constexpr (NF == 5)                                                                     \
+      asm volatile("s_waitcnt lgkmcnt(%5)"                                                    \
+                   : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.a[NF - 1]) \
+                   : "n"(pending)                                                              \
+                   : "memory");                                                                \
+    else                                                                                       \
+      asm volatile("s_waitcnt lgkmcnt(%4)"                                                    \
+                   : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3])                    \
+                   : "n"(pending)                                                              \
+                   : "memory");                                                                \
+  } while (0)
   // codes of both K halves -> bf16 fragments
   u32x4 bq[2][JT];
   auto dequant = [&](const FragQ0& f) {
@@ -829,11 +843,11 @@ __global__ __launch_bounds__(512, 1) void tile_q_kernel(StreamGemmArgs a,
       }
     }
   };
-  auto mfma_half = [&](const u32x4 (&af)[4], int s2) {
+  auto mfma_half = [&](const u32x4 (&af)[NF], int s2) {
 #pragma unroll
     for (int j = 0; j < JT; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i][j] = mfma32(af[i], bq[s2][j], acc[i][j]);
+      for (int i = 0; i < NF; ++i) acc[i][j] = mfma32(af[i], bq[s2][j], acc[i][j]);
   };
   // Pipeline as in the bf16 kernel: "step kt+1 landed" is vmcnt(PER_STEP)
   // once three steps are in flight (a K step's scale load is issued first, so
@@ -856,7 +870,7 @@ __global__ __launch_bounds__(512, 1) void tile_q_kernel(StreamGemmArgs a,
   read0(f0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     read1(f1, kt % NSTAGE);
-    MOE_LGK_WAIT0(f0, 4);
+    MOE_LGK_WAIT0(f0, NF);
     dequant(f0);
     mfma_half(f0.a, 0);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(S::PER_STEP) : "memory");
@@ -864,9 +878,9 @@ __global__ __launch_bounds__(512, 1) void tile_q_kernel(StreamGemmArgs a,
     issue(kt + 3 < nk ? kt + 3 : nk - 1, (kt + 3) % NSTAGE);
     read0(f0, (kt + 1) % NSTAGE, kt + 1);
     if (WF == W_FP4)
-      MOE_LGK_WAIT1(f1, 8);
+      MOE_LGK_WAIT1(f1, 2 * JT + NF);
     else
-      MOE_LGK_WAIT1(f1, 6);
+      MOE_LGK_WAIT1(f1, JT + NF);
     mfma_half(f1.a, 1);
   }
   MOE_LGK_WAIT0(f0, 0);
@@ -884,7 +898,7 @@ __global__ __launch_bounds__(512, 1) void tile_q_kernel(StreamGemmArgs a,
     const float su = WF == W_FP8 ? chs[mcol(bcol(1) + l32)] : gsc;
     uint16_t* strip = reinterpret_cast<uint16_t*>(smem + wave * 4096);  // 32 x 32 bf16
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NF; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         strip[tile_row(r) * 32 + l32] =
@@ -912,7 +926,7 @@ __global__ __launch_bounds__(512, 1) void tile_q_kernel(StreamGemmArgs a,
     float* strip = reinterpret_cast<float*>(smem + wave * 8192);  // 32 x 64 fp32
     const bool compact = a.y16 != nullptr;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NF; ++i) {
 #pragma unroll
       for (int j = 0; j < JT; ++j)
 #pragma unroll
@@ -938,6 +952,34 @@ __global__ __launch_bounds__(512, 1) void tile_q_kernel(StreamGemmArgs a,
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
+}
+
+template <int WF, bool GATE_UP>
+__global__ __launch_bounds__(512, 1) void tile_q_kernel(StreamGemmArgs a,
+                                                        const int32_t* __restrict__ tile_e,
+                                                        const int32_t* __restrict__ tile_m0,
+                                                        const int32_t* __restrict__ n_tiles_p,
+                                                        int NT) {
+  using S = QShape<WF>;
+  __shared__ __align__(1024) uint8_t smem[S::LDS];
+
+  const int total = *n_tiles_p * NT;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int per = (total + 7) >> 3;
+  if (slot >= per) return;
+  const int w = xcd * per + slot;
+  if (w >= total) return;
+  const int mt = w / NT, nt = w - mt * NT;
+  const int e = tile_e[mt];
+  const int m0 = tile_m0[mt];
+  const int r0 = a.offsets[e];
+  const int cnt = a.offsets[e + 1] - r0;
+  // an expert's last tile holds up to 160 rows (tile_table_kernel merges a
+  // tail of <= 32 rows into it)
+  if (cnt - m0 > 128)
+    tile_q_body<WF, GATE_UP, 5>(a, smem, e, m0, nt, r0, cnt);
+  else
+    tile_q_body<WF, GATE_UP, 4>(a, smem, e, m0, nt, r0, cnt);
 }
 
 // ------------------------------------------------------------------ fp8-MFMA mode
@@ -1591,7 +1633,7 @@ hipError_t launch_router_bf16x3(const uint16_t* x, int T, int H, const float* w_
                                                                               offsets, T);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  tile_table_kernel<<<1, 256, 0, st>>>(offsets, 1, TBM, tile_e, tile_m0, n_tiles);
+  tile_table_kernel<<<1, 256, 0, st>>>(offsets, 1, TBM, 0, tile_e, tile_m0, n_tiles);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   StreamGemmArgs a{};
@@ -1695,7 +1737,7 @@ hipError_t launch_expert_f8(int wfmt, const StreamGemmArgs& gu, const StreamGemm
   int32_t* tile_e = static_cast<int32_t*>(ws);
   int32_t* tile_m0 = tile_e + max_tiles;
   int32_t* counts = tile_m0 + max_tiles;
-  tile_table_kernel<<<1, 256, 0, st>>>(gu.offsets, E, 128, tile_e, tile_m0, counts);
+  tile_table_kernel<<<1, 256, 0, st>>>(gu.offsets, E, 128, 0, tile_e, tile_m0, counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (wfmt == W_FP8)
@@ -1708,11 +1750,12 @@ hipError_t launch_expert_tile(int wfmt, const StreamGemmArgs& gu, const StreamGe
   const int E = gu.E;
   int32_t* tile_e = static_cast<int32_t*>(ws);
   if (wfmt == W_FP8 || wfmt == W_FP4) {
-    // one table of 128-row tiles: at most P/128 + E of them
+    // one table of 128-row tiles, an expert's last of up to 160 (its tail of
+    // <= 32 rows merged): at most P/128 + E of them
     const int max_tiles = (P + 127) / 128 + E;
     int32_t* tile_m0 = tile_e + max_tiles;
     int32_t* counts = tile_m0 + max_tiles;
-    tile_table_kernel<<<1, 256, 0, st>>>(gu.offsets, E, 128, tile_e, tile_m0, counts);
+    tile_table_kernel<<<1, 256, 0, st>>>(gu.offsets, E, 128, 32, tile_e, tile_m0, counts);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (wfmt == W_FP8) return launch_q_all<W_FP8>(gu, dn, tile_e, tile_m0, counts, max_tiles, st);

@@ -42,6 +42,10 @@ SMALL = [
     MC("fp8_tile", 114, T=200, H=256, E=8, k=4, I=192, w_dtype="fp8"),
     MC("fp4_tile_ragged", 115, T=150, H=192, E=4, k=2, I=192, w_dtype="fp4"),
     MC("fp4_tile_zipf", 116, T=512, H=256, E=16, k=4, I=128, zipf_s=1.1, w_dtype="fp4"),
+    # ~150 rows per expert: an expert's last tile takes its tail of <= 32 rows
+    # (tiles of 129 .. 160 rows, five row fragments)
+    MC("fp4_merged_tail", 121, T=300, H=256, E=4, k=2, I=192, w_dtype="fp4"),
+    MC("fp8_merged_tail", 122, T=300, H=192, E=4, k=2, I=128, w_dtype="fp8"),
     # fp8-MFMA mode (against the oracle's F8 encodings): few and many rows per
     # expert, partial N tiles and a partial 128-column h block (I = 192),
     # Zipf load for both tile shapes
