@@ -205,16 +205,25 @@ class Workload:
         return self.counts.cpu().numpy()
 
 
+CSRC = os.path.join(ROOT, "sparse_moe_layer_gemm_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_t128_moe_experts_hbm_traffic.md")
-STREAM_SRC = os.path.join(ROOT, "sparse_moe_layer_gemm_amd", "csrc", "expert_stream.hip")
 PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_t16384_zipf_moe_experts_hbm_traffic.md")
-TILE_SRC = os.path.join(ROOT, "sparse_moe_layer_gemm_amd", "csrc", "expert_tile.hip")
+# Each counter record is keyed to the device source of the kernels it measured: the kernel
+# file and the device headers it includes (host-side declarations are not part of it).
+STREAM_SRC = [os.path.join(CSRC, f) for f in ("expert_stream.hip", "stream_common.h", "device_common.h")]
+STREAM_Q_SRC = [os.path.join(CSRC, f) for f in ("expert_stream_q.hip", "stream_common.h", "device_common.h")]
+TILE_SRC = [os.path.join(CSRC, f) for f in ("expert_tile.hip", "tile_common.h", "device_common.h")]
+TILE_Q_SRC = [os.path.join(CSRC, f) for f in ("expert_tile_q.hip", "tile_common.h", "device_common.h")]
 
 
-def source_sha256(path):
+def source_sha256(paths):
+    """sha256 of one file, or of the concatenated bytes of several, in the order given."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in ([paths] if isinstance(paths, str) else paths):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 QUANT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "nvfp4_moe_experts_counters.md")
@@ -610,7 +619,7 @@ def main():
                                "peak": HBM_PEAK_GBS if hbm_frac >= mfma_frac else BF16_PEAK_TFLOPS,
                                "unit": "GB/s" if hbm_frac >= mfma_frac else "TFLOP/s",
                                "frac": max(hbm_frac, mfma_frac),
-                               "traffic": measured_traffic(QUANT_TRAFFIC_FILE, TILE_SRC, "nvfp4_t4096_w"),
+                               "traffic": measured_traffic(QUANT_TRAFFIC_FILE, TILE_Q_SRC, "nvfp4_t4096_w"),
                                "weight_GBps": round(tb, 1), "TFLOPs": round(tf, 1)}}
         if not a.no_cpu:
             progress("timing the CPU oracle on an NVFP4 token sample")
@@ -638,7 +647,7 @@ def main():
                          "peak": HBM_PEAK_GBS if h8 >= m8 else FP8_PEAK_TFLOPS,
                          "unit": "GB/s" if h8 >= m8 else "TFLOP/s",
                          "frac": max(h8, m8),
-                         "traffic": measured_traffic(QUANT_TRAFFIC_FILE, TILE_SRC, "nvfp4_t4096_f8"),
+                         "traffic": measured_traffic(QUANT_TRAFFIC_FILE, TILE_Q_SRC, "nvfp4_t4096_f8"),
                          "weight_GBps": round(tb8, 1), "TFLOPs": round(tf8, 1)}}
         if not a.no_cpu:
             progress("timing the CPU oracle (fp8-MFMA mode) on an NVFP4 token sample")
@@ -659,7 +668,7 @@ def main():
             "roofline": {"bound": "hbm", "kernel": "moe_experts (NVFP4 weights, stream, bf16 MFMA)",
                          "achieved": round(d_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": d_gbs / HBM_PEAK_GBS,
-                         "traffic": measured_traffic(QUANT_TRAFFIC_FILE, STREAM_SRC, "nvfp4_t128")}}
+                         "traffic": measured_traffic(QUANT_TRAFFIC_FILE, STREAM_Q_SRC, "nvfp4_t128")}}
         del qw, qd
 
     head, head_cfg = (dec_line, dec_cfg) if a.workload == "decode" else (pre_line, pre_cfg)

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["abi.cpp", "router.hip", "permute.hip", "expert_stream.hip", "expert_tile.hip", "expert_f32.hip",
+SOURCES = ["abi.cpp", "router.hip", "permute.hip", "expert_stream.hip", "expert_stream_q.hip", "expert_tile.hip", "expert_tile_q.hip", "expert_f32.hip",
            "finalize.hip",
            "finalize_norm.hip", "hbm_read.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -20,10 +20,8 @@
 //    column c's 8 K values become the B fragment of MFMA c, so the 8 MFMAs of
 //    a K step cover 8 columns per lane at a column stride of 1 and no LDS is
 //    used at all;
-//  - FP8 and NVFP4 weights are stored [N, K] (K contiguous): a lane loads 16 B
-//    of one column and dequantises it exactly to bf16 in registers (E4M3 and
-//    E2M1 x E4M3 products fit in bf16); per-channel and per-expert fp32
-//    scales are applied to the fp32 accumulators in the epilogue;
+//  - FP8 and NVFP4 weights are stored [N, K] (K contiguous); their kernels
+//    (expert_stream_q.hip) run on the same grid and split-K partial sums;
 //  - with few touched experts (small batches) there are too few slices to
 //    keep HBM busy, so K is split over the grid's z dimension: the splits
 //    write fp32 partial sums and a reduction kernel forms h or y, adding them
@@ -35,19 +33,13 @@
 // K block l/16 (8 values); the result lane l holds rows 4*(l/16)+r of column
 // l%16.
 #include <algorithm>
-#include <type_traits>
 
-#include "moe_internal.h"
+#include "stream_common.h"
 
 namespace moe {
 namespace {
 
 constexpr int MROWS = 32;  // rows per pass (two 16-row MFMA fragments)
-
-__device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
 
 __device__ __forceinline__ u32x4 load_u32x4(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -81,37 +73,6 @@ __device__ __forceinline__ ARows a_rows(const StreamGemmArgs& a, bool gate_up, i
     ar.row[f] = a.a + row * a.K;
   }
   return ar;
-}
-
-// The expert of grid row `slot`. With one row per expert (gridDim.y == E) it
-// is the row itself; with fewer rows (min(E, P) < E: few pairs, so most
-// experts are empty) it is the slot-th expert that has rows, found from the
-// offsets by ballots (every lane of the wavefront gets the same answer), or
-// -1 when fewer experts have rows.
-__device__ __forceinline__ int slot_expert(const int32_t* __restrict__ offsets, int E, int slot,
-                                           int lane) {
-  if ((int)gridDim.y == E) return slot;
-  int o0[4], o1[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {  // E <= 256: lane l looks at experts l, l+64, l+128, l+192
-    const int e = 64 * c + lane;
-    o0[c] = offsets[e < E ? e : 0];
-    o1[c] = offsets[e < E ? e + 1 : 0];
-  }
-  const uint64_t below = (1ull << lane) - 1ull;
-  int base = 0;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const bool nz = 64 * c + lane < E && o1[c] > o0[c];
-    const uint64_t m = __ballot(nz);
-    const int want = slot - base;
-    if (want < __popcll(m)) {
-      const uint64_t hit = __ballot(nz && __popcll(m & below) == want);
-      return 64 * c + __builtin_ctzll(hit);
-    }
-    base += __popcll(m);
-  }
-  return -1;
 }
 
 // ------------------------------------------------------------------ bf16 weights
@@ -361,666 +322,8 @@ __global__ __launch_bounds__(256) void stream_reduce_dn_kernel(const float* __re
   }
 }
 
-// ------------------------------------------------------------------ FP8 weights
-// K-contiguous E4M3 weights [E, N, K] with one fp32 scale per output channel.
-// Per "super step" the four lane groups of a column each read 32 B of it,
-// together one whole 128 B line (32 K values per lane). (Reading half a line
-// per super step measured 2.8x the algorithmic bytes fetched at decode:
-// lines were evicted before their second half was used; and the default
-// cache policy measured 1.3x faster than nontemporal loads here.)
-// A workgroup's four wavefronts own 64 columns each of the same expert and K
-// range, so the A rows of a super step (x or h, 8 KB) are loaded once into
-// LDS by direct buffer -> LDS loads (each wavefront a quarter) and shared;
-// the weight codes go to registers (buffer loads with the expert's matrix as
-// the buffer), three super steps rotating through three register sets, so
-// two super steps of loads are in flight while one is converted. Every
-// wavefront issues the same loads per super step (idle ones read column tile
-// 0 and store nothing), so "A of step ss landed" is one vmcnt for all. Codes
-// become bf16 exactly with the hardware converter; the per-channel scales
-// multiply the accumulators. In MFMA s of a super step lane group g covers
-// K ss*SPAN + G*g + 8s .. +8, for A and B alike.
-#ifndef MOE_KM_CPOL
-#define MOE_KM_CPOL 0  // cache policy of the code loads (0: default, 2: nontemporal)
-#endif
-template <int WF>
-struct KmShape {
-  static_assert(WF == W_FP8, "E4M3 weights");
-  static constexpr int G = 32;                       // K values per lane per super step
-  static constexpr int NS = G / 8;                   // MFMA K steps per super step
-  static constexpr int SPAN = 4 * G;                 // K per super step
-  static constexpr int NV = 2;                       // 16 B code loads per lane and column
-  static constexpr int CG = 4;                       // 16-column groups per wavefront
-  static constexpr int COLS = 16 * CG;               // columns per wavefront
-  static constexpr int NF = 2;                       // 16-row fragments per pass
-  static constexpr int AROWS = 16 * NF;              // A rows per pass
-  static constexpr int AROWB = SPAN * 2;             // bytes of an A row per super step
-  static constexpr int ACH = AROWB / 16;             // 16 B chunks per A row
-  static constexpr int ASLOT = AROWS * AROWB;        // LDS bytes of A per super step
-  static constexpr int NSLOT = 3;                    // super steps of A in LDS
-  static constexpr int RPI = 1024 / AROWB;           // A rows per 1 KB direct load
-  static constexpr int DPW = ASLOT / 1024 / 4;       // direct loads per wavefront per super step
-  static constexpr int NWL = CG * NV;                // weight loads per super step
-  static_assert(DPW * 4 * 1024 == ASLOT && AROWS % (4 * DPW) == 0, "A tile split");
-};
-
-// Direct buffer -> LDS load: lane l's 16 bytes (at byte offset off of the
-// buffer) land at lds + 16 * l. The buffer form keeps the compiler's own
-// vmcnt waits for the register loads beside it exact (a FLAT-encoded
-// load to LDS counts as possibly pending on both counters, after which the
-// compiler waits for everything).
-__device__ __forceinline__ void dma16s(__amdgpu_buffer_rsrc_t r, uint32_t off, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0,
-                                           0, 0);
-}
-// LDS read the compiler does not see (valid after an explicit lgkmcnt wait
-// that takes it as an operand).
-__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
-  u32x4 r;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
-  return r;
-}
-
-template <int WF, bool GATE_UP>
-__global__ __launch_bounds__(256, 2) void stream_kmajor_kernel(StreamGemmArgs a) {
-  using S = KmShape<WF>;
-  constexpr int G = S::G, NS = S::NS, SPAN = S::SPAN, NV = S::NV, CG = S::CG, NF = S::NF;
-  __shared__ __align__(16) uint8_t als[S::NSLOT * S::ASLOT];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = lane >> 4, j = lane & 15;
-  const int tile = blockIdx.x * 4 + wave;
-  const int n_tiles = GATE_UP ? a.I / (S::COLS / 2) : (a.N + S::COLS - 1) / S::COLS;
-  const bool tile_ok = tile < n_tiles;  // idle wavefronts still load A and meet the barriers
-  // expert, rows and K range: the same for the whole workgroup
-  const int e = slot_expert(a.offsets, a.E, blockIdx.y, lane);
-  if (e < 0) return;
-  const int r0 = a.offsets[e];
-  const int cnt = a.offsets[e + 1] - r0;
-  if (cnt <= 0) return;
-  const int K = a.K, N = a.N;
-  const int nss = (K + SPAN - 1) / SPAN;
-  const int split = blockIdx.z;
-  const int ss0 = a.ksplit > 1 ? split * a.ksteps : 0;
-  const int ss1 = a.ksplit > 1 ? min(nss, ss0 + a.ksteps) : nss;
-  if (ss0 >= ss1) return;
-
-  // this lane's CG columns (gate/up: CG/2 gate, then the matching up columns);
-  // columns past N read column 0 and are never stored
-  const int row_bytes = K;
-  // this expert's codes as a buffer (31-bit size, checked by the host)
-  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(static_cast<const uint8_t*>(a.w) + (size_t)e * N * row_bytes), (short)0, N * row_bytes,
-      0x00020000);
-  const int tc = tile_ok ? tile : 0;
-  int colv[CG];
-  bool cok[CG];
-  uint32_t coff[CG];
-#pragma unroll
-  for (int cg = 0; cg < CG; ++cg) {
-    constexpr int H2 = CG / 2, HC = S::COLS / 2;
-    if (GATE_UP)
-      colv[cg] = cg < H2 ? tc * HC + 16 * cg + j : a.I + tc * HC + 16 * (cg - H2) + j;
-    else
-      colv[cg] = tc * S::COLS + 16 * cg + j;
-    cok[cg] = tile_ok && colv[cg] < N;
-    coff[cg] = (uint32_t)(colv[cg] < N ? colv[cg] : 0);
-  }
-  const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
-  const uint32_t lds_base = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)als;
-  auto clampss = [&](int x) { return x < ss1 ? x : ss1 - 1; };
-  // A as a buffer: x ([rows / k, K]) for gate/up, h ([rows, K]) for down; its
-  // byte size fits 31 bits (checked by the host)
-  const uint32_t a_bytes = (uint32_t)((GATE_UP ? a.rows / a.k : a.rows) * (long long)K * 2);
-  const __amdgpu_buffer_rsrc_t arsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)a.a, (short)0, (int)a_bytes, 0x00020000);
-
-  for (int mc = 0; mc < cnt; mc += S::AROWS) {
-    const int nf = (NF == 2 && (cnt - mc) > 16) ? 2 : 1;
-    // A rows this wavefront loads: direct load d covers rows RPI * (DPW * wave + d) ..
-    // (lane / ACH within), 16 B chunk position lane % ACH holding K chunk
-    // (lane % ACH) ^ (row % ACH) (the XOR keeps the 16 rows a fragment read
-    // touches in distinct banks)
-    uint32_t arow[S::DPW];  // element offsets of the rows in A
-    int achk[S::DPW];
-#pragma unroll
-    for (int d = 0; d < S::DPW; ++d) {
-      const int row = S::RPI * (S::DPW * wave + d) + lane / S::ACH;
-      const int m = mc + row;
-      uint32_t grow = 0;
-      if (m < cnt) grow = GATE_UP ? (uint32_t)(a.sorted_pair[r0 + m] / a.k) : (uint32_t)(r0 + m);
-      arow[d] = grow * (uint32_t)K;
-      achk[d] = 8 * ((lane % S::ACH) ^ (row % S::ACH));
-    }
-    auto issue_a = [&](int ss, int slot) {
-#pragma unroll
-      for (int d = 0; d < S::DPW; ++d) {
-        // chunks past K (a K tail) read the row's first chunk; their products are zeroed
-        const int ko = ss * SPAN + achk[d];
-        dma16s(arsrc, 2u * (arow[d] + (uint32_t)(ko < K ? ko : 0)),
-               als + slot * S::ASLOT + S::RPI * (S::DPW * wave + d) * S::AROWB);
-      }
-    };
-    f32x4 acc[NF][CG];
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-      for (int i = 0; i < CG; ++i) acc[f][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    struct Ops {
-      u32x4 b[CG][NV];
-    };
-    auto load_ops = [&](int ss, Ops& o) {
-      const int kl = ss * SPAN + G * g;
-      const uint32_t kc = kl < K ? (uint32_t)kl : 0u;
-#pragma unroll
-      for (int cg = 0; cg < CG; ++cg)
-#pragma unroll
-        for (int v = 0; v < NV; ++v)
-          o.b[cg][v] =
-              __builtin_amdgcn_raw_buffer_load_b128(wrsrc, coff[cg] * (uint32_t)row_bytes + kc + 16 * v, 0, MOE_KM_CPOL);
-    };
-    // one super step: wait for its loads (only step ss + 1's may still be in
-    // flight, whatever order the loads of a step were issued in; the barrier
-    // publishes the other wavefronts' A and frees the slot of step ss - 1),
-    // issue step ss + 2, read the A fragments, convert and multiply
-    auto step = [&](int ss, Ops& cur, Ops& next2) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(S::NWL + S::DPW) : "memory");
-      __builtin_amdgcn_s_barrier();
-      issue_a(clampss(ss + 2), (ss + 2) % S::NSLOT);
-      load_ops(clampss(ss + 2), next2);
-      __builtin_amdgcn_sched_barrier(0);
-      const uint32_t slot = lds_base + (ss % S::NSLOT) * S::ASLOT;
-      static_assert(NF * NS == 8, "eight A fragments per super step");
-      u32x4 af[8];
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-#pragma unroll
-        for (int q = 0; q < NS; ++q) {
-          const int row = 16 * f + j;
-          const int ch = ((G * g + 8 * q) / 8) ^ (row % S::ACH);
-          af[NS * f + q] = lds_read16(slot + row * S::AROWB + 16 * ch);
-        }
-      asm volatile("s_waitcnt lgkmcnt(0)"
-                   : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]), "+v"(af[4]), "+v"(af[5]),
-                     "+v"(af[6]), "+v"(af[7])
-                   :
-                   : "memory");
-      const bool kok = ss * SPAN + G * g < K;  // false only in a K tail
-#pragma unroll
-      for (int cg = 0; cg < CG; ++cg) {
-#pragma unroll
-        for (int q = 0; q < NS; ++q) {
-          const u32x4 bf = fp8_frag(cur.b[cg][q >> 1][2 * (q & 1)], cur.b[cg][q >> 1][2 * (q & 1) + 1]);
-#pragma unroll
-          for (int f = 0; f < NF; ++f)
-            if (f < nf) acc[f][cg] = mfma_bf16(kok ? af[NS * f + q] : zero, bf, acc[f][cg]);
-        }
-        // one column group at a time: converting ahead would need registers
-        // the third weight set holds
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    // the previous pass's LDS reads and direct loads are done before the
-    // slots are refilled
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    Ops w0, w1, w2;
-    issue_a(ss0, ss0 % S::NSLOT);
-    load_ops(ss0, w0);
-    issue_a(clampss(ss0 + 1), (ss0 + 1) % S::NSLOT);
-    load_ops(clampss(ss0 + 1), w1);
-    int ss = ss0;
-    for (; ss + 2 < ss1; ss += 3) {
-      step(ss, w0, w2);
-      step(ss + 1, w1, w0);
-      step(ss + 2, w2, w1);
-    }
-    if (ss < ss1) step(ss, w0, w2);  // w0 holds step ss, w1 step ss + 1
-    if (ss + 1 < ss1) step(ss + 1, w1, w0);
-
-    // epilogue: lane (g, j) holds rows 16f + 4g + r of column colv[cg]
-    const float* chs = static_cast<const float*>(a.w_scale) + (size_t)e * N;
-    float csc[CG];
-#pragma unroll
-    for (int cg = 0; cg < CG; ++cg) csc[cg] = chs[coff[cg]];
-    float* pbase = a.ksplit > 1 ? a.part + (size_t)split * a.part_stride : nullptr;
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      if (f >= nf) break;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = mc + 16 * f + 4 * g + r;
-        if (m >= cnt || !tile_ok) continue;
-        if (pbase) {  // split K: scaled fp32 partial sums
-#pragma unroll
-          for (int cg = 0; cg < CG; ++cg)
-            if (cok[cg]) pbase[(size_t)(r0 + m) * N + colv[cg]] = acc[f][cg][r] * csc[cg];
-        } else if (GATE_UP) {
-#pragma unroll
-          for (int cg = 0; cg < CG / 2; ++cg) {
-            const float gv = acc[f][cg][r] * csc[cg], uv = acc[f][cg + CG / 2][r] * csc[cg + CG / 2];
-            a.h_out[(size_t)(r0 + m) * a.I + colv[cg]] = (uint16_t)f32_to_bf16_bits(silu(gv) * uv);
-          }
-        } else {
-#pragma unroll
-          for (int cg = 0; cg < CG; ++cg)
-            if (cok[cg]) store_rows(a.y_out + (size_t)(r0 + m) * N + colv[cg], acc[f][cg][r] * csc[cg]);
-        }
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------------ NVFP4 weights
-// E2M1 codes [E, N, K/2] with one E4M3 scale per 16 K values.
-// The block scale is not multiplied into the weights. Since w = e2m1 * s,
-// sum_k x_k w_k = sum over blocks of s * (sum over the block of x_k e2m1_k):
-// the codes become bf16 with the hardware converter at scale 1 (exact), a
-// 4x4x4 MFMA chain forms each 16-value block's partial sums on their own, and
-// one fp32 FMA per output applies the block scale (its exact fp32 value). At
-// up to four rows per MFMA that is a quarter of an FMA per weight value
-// instead of a multiply per value.
-// Memory: a wavefront owns 32 columns (4 groups of 8) of one expert's matrix;
-// per super step (256 K values) each of its load instructions reads whole
-// 128 B lines, 8 lanes x 16 B per column for 8 columns (measured with the
-// same access pattern: 5.9 TB/s, against 4.4 TB/s for 4 lanes x 2 x 16 B per
-// line plus a scale dword per lane and step). The block scales of 8 super
-// steps (128 B per column) reach LDS by direct loads of whole lines, half a
-// wavefront's worth per super step, two blocks of 8 steps ahead; the A rows
-// (x or h) of a super step are loaded once per workgroup into LDS (each
-// wavefront a quarter) and shared; codes go to registers, super steps rotating
-// through NSET register sets. Loads use the default cache policy (measured
-// faster than nontemporal for this pattern).
-// MFMA v_mfma_f32_4x4x4_16b_bf16 (16 independent 4x4 blocks, K = 4): lane l
-// belongs to block l/4, supplies A row l%4 and B column l%4 (4 K values
-// each), and its result holds column l%4 of its block for rows 0..3. Here
-// lane l's block is (K range q = l/8, column half (l/4)%2): the lane works on
-// column 8 cg + l%8 over K range q (32 values of each super step), with rows
-// (tokens) 4 rg + l%4 as A. After the K loop the eight K ranges' partial
-// sums are added across lanes l, l^8, l^16, l^32.
-#ifndef MOE_FP4_NSET
-#define MOE_FP4_NSET 2  // code register sets at up to 8 rows per pass
-#endif
-#ifndef MOE_FP4_CHAINS
-#define MOE_FP4_CHAINS 4  // independent MFMA chains in flight
-#endif
-template <int RG>
-struct Fp4Shape {
-  static constexpr int KQ = 8;                   // K ranges of a super step (lanes / 8)
-  static constexpr int G = 32;                   // K values per lane per super step
-  static constexpr int SPAN = KQ * G;            // K per super step
-  static constexpr int CG = 4;                   // 8-column groups per wavefront
-  static constexpr int COLS = 8 * CG;            // columns per wavefront
-  static constexpr int AROWS = 4 * RG;           // A rows per pass (RG row groups of 4)
-  static constexpr int AROWB = SPAN * 2;         // bytes of an A row per super step
-  static constexpr int ACH = AROWB / 16;         // 16 B chunks per A row
-  static constexpr int ASLOT = AROWS * AROWB;    // LDS bytes of A per super step
-  static constexpr int NSLOT = 4;                // super steps of A in LDS (at least the code sets)
-  static constexpr int RPI = 1024 / AROWB;       // A rows per 1 KB direct load
-  static constexpr int DPW = ASLOT / 1024 / 4;   // direct A loads per wavefront per super step
-  static constexpr int SBLK = 8;                 // super steps per scale block
-  static constexpr int SSLOT = COLS * SBLK * 16;  // scale bytes of a wavefront per block
-  static constexpr int NWL = CG + 1;             // loads per super step: codes + half a scale block piece
-  static_assert(DPW >= 1 && DPW * 4 * 1024 == ASLOT, "A tile split");
-  static_assert(SSLOT == SBLK * 512, "one half-wavefront scale load per super step");
-};
-
-// LDS position of 16 B K chunk c (0..31) of A row t, XOR-swizzled so that the
-// chunks one fragment read touches (4 rows x 8 K ranges) spread over the
-// banks. An involution: it maps positions back to chunks too.
-__device__ __forceinline__ int fp4_apos(int c, int t) { return c ^ (t & 3) ^ (((c >> 4) & 1) << 1); }
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-// 4 E2M1 codes (bytes SEL, SEL + 1 of d) -> 4 bf16 (exact)
-template <int SEL>
-__device__ __forceinline__ u32x2 e2m1_bf16_4(uint32_t d) {
-  return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, SEL)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, SEL + 1))};
-}
-// 4x4x4 MFMA on half AH (regs 2 AH, 2 AH + 1) of A and a 2-register B
-template <int AH>
-__device__ __forceinline__ f32x4 mfma4h(const u32x4& a, const u32x2& b, const f32x4& c) {
-  const u32x2 av = {a[2 * AH], a[2 * AH + 1]};
-  return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4, av), __builtin_bit_cast(s16x4, b),
-                                                c, 0, 0, 0);
-}
-// LDS reads the compiler does not see (valid after an explicit lgkmcnt wait
-// that takes them as operands), at addr + OFF
-template <int OFF>
-__device__ __forceinline__ uint32_t lds_read_u16o(uint32_t addr) {
-  uint32_t r;
-  asm volatile("ds_read_u16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
-  return r;
-}
-template <int OFF>
-__device__ __forceinline__ u32x4 lds_read16o(uint32_t addr) {
-  u32x4 r;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
-  return r;
-}
-
-template <int RG, bool GATE_UP>
-__global__ __launch_bounds__(256, 2) void stream_fp4_kernel(StreamGemmArgs a) {
-  using S = Fp4Shape<RG>;
-  constexpr int SPAN = S::SPAN, CG = S::CG;
-  __shared__ __align__(16) uint8_t als[S::NSLOT * S::ASLOT];
-  __shared__ __align__(16) uint8_t sls[4][3 * S::SSLOT];  // per wavefront: 3 scale blocks
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int q = lane >> 3, c8 = lane & 7;  // K range, column within an 8-column group
-  const int tile = blockIdx.x * 4 + wave;
-  const int n_tiles = GATE_UP ? a.I / (S::COLS / 2) : (a.N + S::COLS - 1) / S::COLS;
-  const bool tile_ok = tile < n_tiles;  // idle wavefronts still load and meet the barriers
-  // expert, rows and K range: the same for the whole workgroup
-  const int e = slot_expert(a.offsets, a.E, blockIdx.y, lane);
-  if (e < 0) return;
-  const int r0 = a.offsets[e];
-  const int cnt = a.offsets[e + 1] - r0;
-  if (cnt <= 0) return;
-  const int K = a.K, N = a.N;
-  const int nss = (K + SPAN - 1) / SPAN;
-  const int split = blockIdx.z;
-  const int ss0 = a.ksplit > 1 ? split * a.ksteps : 0;
-  const int ss1 = a.ksplit > 1 ? min(nss, ss0 + a.ksteps) : nss;
-  if (ss0 >= ss1) return;
-
-  // this expert's codes and block scales as buffers (31-bit sizes, checked by the host)
-  const int row_bytes = K / 2, srow = K / 16;
-  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(static_cast<const uint8_t*>(a.w) + (size_t)e * N * row_bytes), (short)0, N * row_bytes,
-      0x00020000);
-  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(static_cast<const uint8_t*>(a.w_scale) + (size_t)e * N * srow), (short)0, N * srow,
-      0x00020000);
-  // this lane's CG columns (gate/up: CG/2 gate groups, then the matching up
-  // groups); columns past N read column 0 and are never stored
-  const int tc = tile_ok ? tile : 0;
-  auto column = [&](int cg, int c) {
-    constexpr int H2 = CG / 2, HC = S::COLS / 2;
-    if (GATE_UP) return cg < H2 ? tc * HC + 8 * cg + c : a.I + tc * HC + 8 * (cg - H2) + c;
-    return tc * S::COLS + 8 * cg + c;
-  };
-  uint32_t coff[CG];
-#pragma unroll
-  for (int cg = 0; cg < CG; ++cg) {
-    const int col = column(cg, c8);
-    coff[cg] = (uint32_t)(col < N ? col : 0) * (uint32_t)row_bytes;
-  }
-  const uint32_t lds_base = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)als;
-  uint8_t* const swave = sls[wave];
-  const uint32_t sbase = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)swave;
-  auto clampss = [&](int x) { return x < ss1 ? x : ss1 - 1; };
-  // A as a buffer: x ([rows / k, K]) for gate/up, h ([rows, K]) for down
-  const uint32_t a_bytes = (uint32_t)((GATE_UP ? a.rows / a.k : a.rows) * (long long)K * 2);
-  const __amdgpu_buffer_rsrc_t arsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)a.a, (short)0, (int)a_bytes, 0x00020000);
-  // LDS byte offsets (within a slot) of this lane's A chunks: row lane % 4 (+ 4 rg),
-  // K chunk 4 q + h (h: 16 B piece of the lane's 64 B)
-  uint32_t aoff[4];
-#pragma unroll
-  for (int h = 0; h < 4; ++h) aoff[h] = (uint32_t)((lane & 3) * S::AROWB + 16 * fp4_apos(4 * q + h, lane & 3));
-  // block scales in the wavefront's LDS: column cw = 8 cg + c8 at cw * 128, step
-  // st of the block at + 16 st, blocks 2q, 2q + 1 at + 2q
-  const uint32_t scoff = (uint32_t)(c8 * 128 + 2 * q);
-  // half-wavefront scale load st of scale block rb (super steps ss0 + 8 rb ..):
-  // lane l < 32 reads chunk l % 8 (one super step) of column 4 st + l / 8 of
-  // this wavefront's 32
-  auto issue_s = [&](int rb, int st) {
-    const int cw = 4 * st + (lane >> 3) % 4;
-    const int col = column(cw >> 3, cw & 7);
-    const int k16 = (ss0 + S::SBLK * rb) * (SPAN / 16) + 16 * (lane & 7);  // scale byte of this chunk
-    const uint32_t off = (uint32_t)(col < N ? col : 0) * (uint32_t)srow + (uint32_t)(k16 + 16 <= srow ? k16 : 0);
-    if (lane < 32) dma16s(srsrc, off, swave + (rb % 3) * S::SSLOT + st * 512);
-  };
-
-  // One pass over K for rows mc .. mc + 4 NRG - 1 (NRG row groups; padding
-  // rows are computed and not stored). The row-group count is a compile-time
-  // constant: branching on it inside the K loop costs registers.
-  auto pass = [&](int mc, auto nrg_c) {
-    constexpr int NRG = decltype(nrg_c)::value;
-    constexpr int NSET = NRG <= 2 ? MOE_FP4_NSET : 2;
-    static_assert(NSET <= S::NSLOT, "A slots for every step in flight");
-    // column groups whose MFMA chains run side by side
-    constexpr int CI = (MOE_FP4_CHAINS / NRG) < 1 ? 1 : (MOE_FP4_CHAINS / NRG) > CG ? CG : MOE_FP4_CHAINS / NRG;
-    // A rows this wavefront loads: direct load d covers rows RPI * (DPW * wave + d)
-    // (+ lane / ACH), position lane % ACH holding K chunk fp4_apos(lane % ACH, row)
-    uint32_t arow[S::DPW];
-    int achk[S::DPW];
-#pragma unroll
-    for (int d = 0; d < S::DPW; ++d) {
-      const int row = S::RPI * (S::DPW * wave + d) + lane / S::ACH;
-      const int m = mc + row;
-      uint32_t grow = 0;
-      if (m < cnt) grow = GATE_UP ? (uint32_t)(a.sorted_pair[r0 + m] / a.k) : (uint32_t)(r0 + m);
-      arow[d] = grow * (uint32_t)K;
-      achk[d] = 8 * fp4_apos(lane % S::ACH, row);
-    }
-    // all loads of super step ss, issued while step ss - NSET + 1 runs: A
-    // rows, this lane's codes, and (uniformly, one per issue) a half-wavefront
-    // piece of scale block b + 2, b being the running step's block. A block's
-    // pieces are issued in the 8 steps after the block three before it (same
-    // LDS slot) was last read; the issues before the first step repeat pieces
-    // of block 1 (same data, slot not yet read).
-    auto issue = [&](int ss, u32x4* o, int t) {
-      const int slot = (ss - ss0) % S::NSLOT;
-#pragma unroll
-      for (int d = 0; d < S::DPW; ++d) {
-        // chunks past K (a K tail) read the row's first chunk; their scales are zeroed
-        const int ko = ss * SPAN + achk[d];
-        dma16s(arsrc, 2u * (arow[d] + (uint32_t)(ko < K ? ko : 0)),
-               als + slot * S::ASLOT + S::RPI * (S::DPW * wave + d) * S::AROWB);
-      }
-      if (t >= 0)
-        issue_s(t / S::SBLK + 2, t % S::SBLK);
-      else
-        issue_s(1, t + S::SBLK);
-      const int kl = ss * SPAN + S::G * q;
-      const uint32_t kc = kl < K ? (uint32_t)kl / 2 : 0u;
-#pragma unroll
-      for (int cg = 0; cg < CG; ++cg) o[cg] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, coff[cg] + kc, 0, 0);
-    };
-    f32x4 acc[NRG][CG];
-#pragma unroll
-    for (int r = 0; r < NRG; ++r)
-#pragma unroll
-      for (int i = 0; i < CG; ++i) acc[r][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // one super step: wait for its loads (only those of the next NSET - 2
-    // steps may still be in flight; the barrier publishes the other
-    // wavefronts' A and frees the A slot of step ss - 1, which step
-    // ss + NSET - 1 may reuse), issue step ss + NSET - 1, then per 16-value
-    // block: read the A fragments and scales, convert the codes, MFMA chains
-    // and scale FMAs
-    auto step = [&](int ss, const u32x4* cur, u32x4* next) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSET - 2) * (S::NWL + S::DPW)) : "memory");
-      __builtin_amdgcn_s_barrier();
-      issue(clampss(ss + NSET - 1), next, ss - ss0);
-      __builtin_amdgcn_sched_barrier(0);
-      const uint32_t slot = lds_base + ((ss - ss0) % S::NSLOT) * S::ASLOT;
-      const uint32_t sslot = sbase + (((ss - ss0) / S::SBLK) % 3) * S::SSLOT + ((ss - ss0) % S::SBLK) * 16;
-      const bool kin = ss * SPAN + S::G * q < K;  // false only in a K tail
-      // block scales 2q, 2q + 1 of this lane's columns (bytes 0, 1 of a u16)
-      uint32_t scr[CG];
-      {
-        const uint32_t sa = sslot + scoff;
-        scr[0] = lds_read_u16o<0>(sa);
-        scr[1] = lds_read_u16o<1024>(sa);
-        scr[2] = lds_read_u16o<2048>(sa);
-        scr[3] = lds_read_u16o<3072>(sa);
-        static_assert(CG == 4, "four column groups");
-      }
-      float sf[CG][2];
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        u32x4 af[NRG][2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t aa = slot + aoff[2 * sb + h];
-          af[0][h] = lds_read16o<0>(aa);
-          if constexpr (NRG > 1) af[1][h] = lds_read16o<4 * S::AROWB>(aa);
-          if constexpr (NRG > 2) af[2][h] = lds_read16o<8 * S::AROWB>(aa);
-          if constexpr (NRG > 3) af[3][h] = lds_read16o<12 * S::AROWB>(aa);
-        }
-        if constexpr (NRG == 1)
-          asm volatile("s_waitcnt lgkmcnt(0)"
-                       : "+v"(af[0][0]), "+v"(af[0][1]), "+v"(scr[0]), "+v"(scr[1]), "+v"(scr[2]), "+v"(scr[3])
-                       :
-                       : "memory");
-        else if constexpr (NRG == 2)
-          asm volatile("s_waitcnt lgkmcnt(0)"
-                       : "+v"(af[0][0]), "+v"(af[0][1]), "+v"(af[1][0]), "+v"(af[1][1]), "+v"(scr[0]), "+v"(scr[1]),
-                         "+v"(scr[2]), "+v"(scr[3])
-                       :
-                       : "memory");
-        else
-          asm volatile("s_waitcnt lgkmcnt(0)"
-                       : "+v"(af[0][0]), "+v"(af[0][1]), "+v"(af[1][0]), "+v"(af[1][1]), "+v"(af[2][0]),
-                         "+v"(af[2][1]), "+v"(af[3][0]), "+v"(af[3][1]), "+v"(scr[0]), "+v"(scr[1]), "+v"(scr[2]),
-                         "+v"(scr[3])
-                       :
-                       : "memory");
-        if (sb == 0) {  // as fp32 (exact), zero past K
-#pragma unroll
-          for (int cg = 0; cg < CG; ++cg) {
-            const f32x2 sp = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(scr[cg], 1.0f, false);
-            sf[cg][0] = kin ? sp.x : 0.f;
-            sf[cg][1] = kin ? sp.y : 0.f;
-          }
-        }
-        // MFMA chains (4 K values each, 4 per 16-value block) of CI column
-        // groups x NRG row groups side by side: a lone chain waits out the
-        // full MFMA latency at every link
-#pragma unroll
-        for (int cb = 0; cb < CG / CI; ++cb) {
-          f32x4 t[CI][NRG];
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-#pragma unroll
-            for (int ci = 0; ci < CI; ++ci) {
-              const uint32_t d = cur[cb * CI + ci][2 * sb + (m >> 1)];
-              const u32x2 bv = (m & 1) ? e2m1_bf16_4<2>(d) : e2m1_bf16_4<0>(d);
-#pragma unroll
-              for (int r = 0; r < NRG; ++r) {
-                const f32x4 c = m == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : t[ci][r];
-                t[ci][r] = (m & 1) ? mfma4h<1>(af[r][m >> 1], bv, c) : mfma4h<0>(af[r][m >> 1], bv, c);
-              }
-            }
-          }
-#pragma unroll
-          for (int ci = 0; ci < CI; ++ci)
-#pragma unroll
-            for (int r = 0; r < NRG; ++r) acc[r][cb * CI + ci] += sf[cb * CI + ci][sb] * t[ci][r];
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    };
-    // the previous pass's LDS reads and direct loads are done before the
-    // slots are refilled; then the first two scale blocks and NSET - 1 steps
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-#pragma unroll 1
-    for (int st = 0; st < 2 * S::SBLK; ++st) issue_s(st / S::SBLK, st % S::SBLK);
-    int ss = ss0;
-    if constexpr (NSET == 4) {
-      u32x4 w0[CG], w1[CG], w2[CG], w3[CG];
-      issue(ss0, w0, -3);
-      issue(clampss(ss0 + 1), w1, -2);
-      issue(clampss(ss0 + 2), w2, -1);
-      for (; ss + 3 < ss1; ss += 4) {
-        step(ss, w0, w3);
-        step(ss + 1, w1, w0);
-        step(ss + 2, w2, w1);
-        step(ss + 3, w3, w2);
-      }
-      // w0, w1, w2 hold steps ss, ss + 1, ss + 2
-      if (ss < ss1) step(ss, w0, w3);
-      if (ss + 1 < ss1) step(ss + 1, w1, w0);
-      if (ss + 2 < ss1) step(ss + 2, w2, w1);
-    } else if constexpr (NSET == 2) {
-      u32x4 w0[CG], w1[CG];
-      issue(ss0, w0, -1);
-      for (; ss + 1 < ss1; ss += 2) {
-        step(ss, w0, w1);
-        step(ss + 1, w1, w0);
-      }
-      if (ss < ss1) step(ss, w0, w1);  // w0 holds step ss
-    } else {
-      u32x4 w0[CG], w1[CG], w2[CG];
-      issue(ss0, w0, -2);
-      issue(clampss(ss0 + 1), w1, -1);
-      for (; ss + 2 < ss1; ss += 3) {
-        step(ss, w0, w2);
-        step(ss + 1, w1, w0);
-        step(ss + 2, w2, w1);
-      }
-      if (ss < ss1) step(ss, w0, w2);  // w0 holds step ss, w1 step ss + 1
-      if (ss + 1 < ss1) step(ss + 1, w1, w0);
-    }
-
-    // epilogue: add the eight K ranges' partial sums; then lane (q, c8) holds
-    // rows 4 rg + 0..3 of column colv[cg], and lanes q < 4 store row 4 rg + q
-    const float gsc = a.w_gscale[e];
-    float* pbase = a.ksplit > 1 ? a.part + (size_t)split * a.part_stride : nullptr;
-#pragma unroll
-    for (int r = 0; r < NRG; ++r) {
-      float v[CG];
-#pragma unroll
-      for (int cg = 0; cg < CG; ++cg) {
-        f32x4 t = acc[r][cg];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          t[i] += __shfl_xor(t[i], 8);
-          t[i] += __shfl_xor(t[i], 16);
-          t[i] += __shfl_xor(t[i], 32);
-        }
-        v[cg] = ((q & 3) == 0 ? t[0] : (q & 3) == 1 ? t[1] : (q & 3) == 2 ? t[2] : t[3]) * gsc;
-      }
-      const int m = mc + 4 * r + q;
-      if (q >= 4 || m >= cnt || !tile_ok) continue;
-      if (pbase) {  // split K: scaled fp32 partial sums
-#pragma unroll
-        for (int cg = 0; cg < CG; ++cg) {
-          const int col = column(cg, c8);
-          if (col < N) pbase[(size_t)(r0 + m) * N + col] = v[cg];
-        }
-      } else if (GATE_UP) {
-#pragma unroll
-        for (int cg = 0; cg < CG / 2; ++cg)
-          a.h_out[(size_t)(r0 + m) * a.I + column(cg, c8)] =
-              (uint16_t)f32_to_bf16_bits(silu(v[cg]) * v[cg + CG / 2]);
-      } else {
-#pragma unroll
-        for (int cg = 0; cg < CG; ++cg) {
-          const int col = column(cg, c8);
-          if (col < N) store_rows(a.y_out + (size_t)(r0 + m) * N + col, v[cg]);
-        }
-      }
-    }
-  };
-
-  for (int mc = 0; mc < cnt; mc += S::AROWS) {
-    const int nrg = (cnt - mc + 3) / 4;  // row groups holding rows
-    if (nrg <= 1)
-      pass(mc, std::integral_constant<int, 1>{});
-    else if (RG == 2 || nrg == 2)
-      pass(mc, std::integral_constant<int, 2>{});
-    else
-      pass(mc, std::integral_constant<int, RG>{});
-  }
-}
-
 // Columns per wavefront of the streaming kernels.
-int stream_cols(int wfmt) {
-  return wfmt == W_BF16 ? 128 : wfmt == W_FP8 ? KmShape<W_FP8>::COLS : Fp4Shape<2>::COLS;
-}
-
-// NVFP4: 16 rows per pass once experts average more than 8 rows, else 8
-template <bool GU>
-void launch_fp4(dim3 grid, const StreamGemmArgs& a, hipStream_t st) {
-  if ((long long)a.rows > 8LL * a.E)
-    stream_fp4_kernel<4, GU><<<grid, 256, 0, st>>>(a);
-  else
-    stream_fp4_kernel<2, GU><<<grid, 256, 0, st>>>(a);
-}
+int stream_cols(int wfmt) { return wfmt == W_BF16 ? 128 : stream_q_cols(wfmt); }
 
 template <bool GU>
 hipError_t launch_one(int wfmt, const StreamGemmArgs& a, hipStream_t st) {
@@ -1041,9 +344,10 @@ hipError_t launch_one(int wfmt, const StreamGemmArgs& a, hipStream_t st) {
         else
           stream_bf16_kernel<GU><<<grid, 256, 0, st>>>(a);
         break;
-      case W_FP8: stream_kmajor_kernel<W_FP8, GU><<<grid, 256, 0, st>>>(a); break;
-      case W_FP4: launch_fp4<GU>(grid, a, st); break;
-      default: return hipErrorInvalidValue;
+      default: {
+        const hipError_t e = launch_stream_q(wfmt, GU, grid, a, st);
+        if (e != hipSuccess) return e;
+      }
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.keep_partials) return err;
@@ -1063,9 +367,7 @@ hipError_t launch_one(int wfmt, const StreamGemmArgs& a, hipStream_t st) {
       else
         stream_bf16_kernel<GU><<<grid, 256, 0, st>>>(a);
       break;
-    case W_FP8: stream_kmajor_kernel<W_FP8, GU><<<grid, 256, 0, st>>>(a); break;
-    case W_FP4: launch_fp4<GU>(grid, a, st); break;
-    default: return hipErrorInvalidValue;
+    default: return launch_stream_q(wfmt, GU, grid, a, st);
   }
   return hipGetLastError();
 }
@@ -1091,9 +393,7 @@ StreamSplit stream_split_plan(long long P, int E, int K, int N, bool gate_up, in
   return StreamSplit{(nk + ksteps - 1) / ksteps, ksteps};
 }
 
-int stream_k_step(int wfmt) {
-  return wfmt == W_FP4 ? Fp4Shape<2>::SPAN : wfmt == W_FP8 ? KmShape<W_FP8>::SPAN : 32;
-}
+int stream_k_step(int wfmt) { return wfmt == W_BF16 ? 32 : stream_q_k_step(wfmt); }
 
 bool stream_fold_h(long long P, int E, int H, int I, int wfmt, int* kr) {
   if (wfmt != W_BF16 || P > MROWS) return false;

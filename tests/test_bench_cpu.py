@@ -32,6 +32,21 @@ def test_traffic_lookup_follows_the_source_hash(tmp_path):
     assert bench.measured_traffic(str(tmp_path / "missing.md"), str(src)) is None
 
 
+def test_traffic_hash_covers_the_included_headers(tmp_path):
+    src, hdr = tmp_path / "kernel.hip", tmp_path / "common.h"
+    src.write_text("#include \"common.h\"\n")
+    hdr.write_text("// shared device code\n")
+    files = [str(src), str(hdr)]
+    rec = {"source_sha256": bench.source_sha256(files), "hbm_bytes_per_launch": 99}
+    summary = tmp_path / "summary.md"
+    summary.write_text("TRAFFIC_JSON: " + json.dumps(rec) + "\n")
+    assert bench.measured_traffic(str(summary), files) == 99
+    hdr.write_text("// shared device code, changed\n")  # a header edit makes the record stale
+    assert bench.measured_traffic(str(summary), files) is None
+    for lst in (bench.STREAM_SRC, bench.STREAM_Q_SRC, bench.TILE_SRC, bench.TILE_Q_SRC):
+        assert all(os.path.exists(f) for f in lst)
+
+
 def test_keyed_traffic_lines_pick_their_workload(tmp_path):
     src = tmp_path / "kernel.hip"
     src.write_text("// a kernel\n")
