@@ -69,13 +69,15 @@ moe_status check_shape(int64_t T, int32_t H, int32_t E, int32_t k) {
 }
 
 // Router split plan: enough K slices that the fp32 router GEMM spreads over
-// at least 256 workgroups (64 tokens x 64 experts each); slices are multiples
-// of 32 and there are at most 32 of them.
+// at least 256 workgroups (16 or 64 tokens x 64 experts each); slices are
+// multiples of 32 and there are at most 40 of them (at H = 5120: 128-deep
+// slices, one 32-deep step per wavefront).
 void router_plan(int64_t T, int32_t H, int32_t E, int* n_split, int* split_len) {
-  const int64_t blocks = ((T + 63) / 64) * ((E + 63) / 64);
+  const int rows = T < (1 << 30) ? moe::router_gemm_rows((int)T) : 64;
+  const int64_t blocks = ((T + rows - 1) / rows) * ((E + 63) / 64);
   int64_t s = (256 + blocks - 1) / blocks;
   if (s < 1) s = 1;
-  if (s > 32) s = 32;
+  if (s > 40) s = 40;
   const int chunks = H / 32;
   if (s > chunks) s = chunks;
   const int per = (int)((chunks + s - 1) / s);

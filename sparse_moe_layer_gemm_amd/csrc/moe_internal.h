@@ -40,6 +40,8 @@ moe_status enqueue_forward(const void* x, int32_t x_dtype, int64_t T, int32_t H,
 
 // ---------------------------------------------------------------- launchers
 // Router GEMM partial sums: part[s][t][e] = sum over K-slice s of x[t,h] w[h,e].
+// Tokens per router GEMM workgroup at batch T (16 or 64).
+int router_gemm_rows(int T);
 hipError_t launch_router_gemm(const void* x, bool x_bf16, int T, int H, const float* w_router,
                               int E, int n_split, int split_len, float* part, hipStream_t st);
 // Streaming read of `bytes` (a multiple of 16) from buf; sink: one device word.

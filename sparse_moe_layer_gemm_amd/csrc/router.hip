@@ -8,27 +8,27 @@
 namespace moe {
 namespace {
 
-constexpr int RBM = 64;  // tokens per workgroup
 constexpr int RBN = 64;  // experts per workgroup
 constexpr int RBK = 32;  // K per step
 
-// One workgroup computes a 64-token x 64-expert block of partial logits over
-// one K slice; its four wavefronts take the slice's 32-deep steps in turn and
+// One workgroup computes a (16 MI)-token x 64-expert block of partial logits
+// over one K slice (MI = 1 for batches of at most 16 tokens, whose MFMA work
+// would otherwise be padded to 64 rows, else 4); its four wavefronts take the slice's 32-deep steps in turn and
 // their sums are added in LDS in wave order. fp32 MFMA 16x16x4 with both
 // operands loaded straight into registers, one step ahead: in MFMA s of a step,
 // lane group g supplies k = k0 + 8g + s, so a lane's A values for the step are
 // 8 consecutive x elements (one 16-byte load for bf16) and its B values are
 // rows k0 + 8g + s of W_r at 4 consecutive columns (one float4 each); the four
 // columns feed four MFMAs whose output columns are strided by 4.
-template <bool XBF16>
+template <bool XBF16, int MI>
 __global__ __launch_bounds__(256) void router_gemm_kernel(const void* __restrict__ xv, int T,
                                                           int H, const float* __restrict__ wr,
                                                           int E, int split_len,
                                                           float* __restrict__ part) {
-  __shared__ f32x4 red[4][16][64];  // per wave: 16 accumulator tiles x 64 lanes
+  __shared__ f32x4 red[4][4 * MI][64];  // per wave: 4 MI accumulator tiles x 64 lanes
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, jl = lane & 15;
-  const int m0 = blockIdx.x * RBM, n0 = blockIdx.z * RBN;
+  const int m0 = blockIdx.x * 16 * MI, n0 = blockIdx.z * RBN;
   const int s = blockIdx.y;
   const int kbeg = s * split_len;
   const int kend = min(H, kbeg + split_len);
@@ -36,21 +36,22 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const void* __restrict
   const bool col_ok = c0 < E;
   const bool vec_ok = (E % 4) == 0 && c0 + 3 < E;
 
-  f32x4 acc[4][4];
+  f32x4 acc[MI][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < MI; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // A rows of this lane (rows past T read row 0; their results are never stored)
-  const int arow[4] = {m0 + jl < T ? m0 + jl : 0, m0 + 16 + jl < T ? m0 + 16 + jl : 0,
-                       m0 + 32 + jl < T ? m0 + 32 + jl : 0, m0 + 48 + jl < T ? m0 + 48 + jl : 0};
-  float xa[4][8], xn[4][8];
+  int arow[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) arow[i] = m0 + 16 * i + jl < T ? m0 + 16 * i + jl : 0;
+  float xa[MI][8], xn[MI][8];
   float4 wa[8], wn[8];
-  auto load = [&](int k0, float (&xd)[4][8], float4 (&wd)[8]) {
+  auto load = [&](int k0, float (&xd)[MI][8], float4 (&wd)[8]) {
     const int kk = k0 + 8 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MI; ++i) {
       if constexpr (XBF16) {
         const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xv) +
                                                         (size_t)arow[i] * H + kk);
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const void* __restrict
       for (int e = 0; e < 8; ++e) {
         const float b[4] = {wa[e].x, wa[e].y, wa[e].z, wa[e].w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             acc[i][q] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[i][e], b[q], acc[i][q], 0, 0, 0);
@@ -101,21 +102,23 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const void* __restrict
       for (int e = 0; e < 8; ++e) {
         wa[e] = wn[e];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xa[i][e] = xn[i][e];
+        for (int i = 0; i < MI; ++i) xa[i][e] = xn[i][e];
       }
     }
   }
 
   // add the four wavefronts' sums in wave order
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int q = 0; q < 4; ++q) red[wave][4 * i + q][lane] = acc[i][q];
   __syncthreads();
   // thread (wave, lane) finishes tiles 4*wave .. 4*wave+3 of lane `lane`
+  // (row group i = wave; waves past the MI row groups have none)
   // D layout: lane (g, jl) holds rows 4g + r of column jl of each 16x16 tile;
   // tile (i, q)'s column jl is global column c0 + q.
   const int i = wave;
+  if (i >= MI) return;
   f32x4 v[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -155,7 +158,7 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return (uint64_t)__ockl_wfred_max_u64((unsigned long long)v);
 }
 
-// Small batches (T < 1024, where the router GEMM splits K up to 32 ways):
+// Small batches (T < 1024, where the router GEMM splits K up to 40 ways):
 // one workgroup per token; wavefront w owns experts 64w .. 64w+63, one per
 // lane, and adds that expert's split partials (loaded 32 at a time),
 // the bias, and rounds to the logits dtype. The selection key packs
@@ -176,16 +179,16 @@ __global__ __launch_bounds__(256) void router_select_wg_kernel(
   if (e < E) {
     const float* p = part + (size_t)t * ldp + e;
     const size_t sstride = (size_t)T * ldp;
-    // up to 32 partials are loaded in one batch (one memory latency), then
-    // added in split order
+    // up to 40 partials (the most the split plan makes) are loaded in one
+    // batch (one memory latency), then added in split order
     float v = 0.f;
-    for (int sp0 = 0; sp0 < n_split; sp0 += 32) {
-      float u[32];
+    for (int sp0 = 0; sp0 < n_split; sp0 += 40) {
+      float u[40];
 #pragma unroll
-      for (int j = 0; j < 32; ++j)
+      for (int j = 0; j < 40; ++j)
         if (sp0 + j < n_split) u[j] = p[(size_t)(sp0 + j) * sstride];
 #pragma unroll
-      for (int j = 0; j < 32; ++j)
+      for (int j = 0; j < 40; ++j)
         if (sp0 + j < n_split) v += u[j];
     }
     if (bias) v += bias[e];
@@ -358,13 +361,23 @@ __global__ __launch_bounds__(256) void router_select_kernel(
 
 }  // namespace
 
+int router_gemm_rows(int T) { return T <= 16 ? 16 : 64; }
+
 hipError_t launch_router_gemm(const void* x, bool x_bf16, int T, int H, const float* w_router,
                               int E, int n_split, int split_len, float* part, hipStream_t st) {
-  dim3 grid((T + RBM - 1) / RBM, n_split, (E + RBN - 1) / RBN);
-  if (x_bf16)
-    router_gemm_kernel<true><<<grid, 256, 0, st>>>(x, T, H, w_router, E, split_len, part);
-  else
-    router_gemm_kernel<false><<<grid, 256, 0, st>>>(x, T, H, w_router, E, split_len, part);
+  const int rows = router_gemm_rows(T);
+  dim3 grid((T + rows - 1) / rows, n_split, (E + RBN - 1) / RBN);
+  if (rows == 16) {
+    if (x_bf16)
+      router_gemm_kernel<true, 1><<<grid, 256, 0, st>>>(x, T, H, w_router, E, split_len, part);
+    else
+      router_gemm_kernel<false, 1><<<grid, 256, 0, st>>>(x, T, H, w_router, E, split_len, part);
+  } else {
+    if (x_bf16)
+      router_gemm_kernel<true, 4><<<grid, 256, 0, st>>>(x, T, H, w_router, E, split_len, part);
+    else
+      router_gemm_kernel<false, 4><<<grid, 256, 0, st>>>(x, T, H, w_router, E, split_len, part);
+  }
   return hipGetLastError();
 }
 
