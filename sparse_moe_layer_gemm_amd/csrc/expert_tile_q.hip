@@ -67,9 +67,8 @@ __device__ __forceinline__ void tile_q_body(const StreamGemmArgs& a, uint8_t* sm
                                             int nt, int r0, int cnt) {
   using S = QShape<WF>;
   constexpr int JT = S::JT;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int wn = wave;
-  (void)tid;
   const int K = a.K, N = a.N;
 
   // A: as in the bf16 kernel (gathered rows, 16 rows per 1 KB load; wavefront
@@ -210,33 +209,40 @@ __device__ __forceinline__ void tile_q_body(const StreamGemmArgs& a, uint8_t* sm
                    : "n"(pending)                                                              \
                    : "memory");                                                                \
   } while (0)
-#define MOE_LGK_WAIT1(f, pending)                                                              \
+  // the second-half wait also covers the next step's codes and block scales
+  // (issued before its A reads), which the second half converts
+#define MOE_LGK_WAIT1B(f, g, pending)                                                          \
   do {                                                                                         \
     if constexpr (NF == 5)                                                                     \
-      asm volatile("s_waitcnt lgkmcnt(%5)"                                                    \
-                   : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.a[NF - 1]) \
+      asm volatile("s_waitcnt lgkmcnt(%9)"                                                    \
+                   : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(f.a[NF - 1]), \
+                     "+v"(g.b[0]), "+v"(g.b[1]), "+v"(g.sc[0]), "+v"(g.sc[1])                  \
                    : "n"(pending)                                                              \
                    : "memory");                                                                \
     else                                                                                       \
-      asm volatile("s_waitcnt lgkmcnt(%4)"                                                    \
-                   : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3])                    \
+      asm volatile("s_waitcnt lgkmcnt(%8)"                                                    \
+                   : "+v"(f.a[0]), "+v"(f.a[1]), "+v"(f.a[2]), "+v"(f.a[3]), "+v"(g.b[0]),     \
+                     "+v"(g.b[1]), "+v"(g.sc[0]), "+v"(g.sc[1])                                \
                    : "n"(pending)                                                              \
                    : "memory");                                                                \
   } while (0)
-  // codes of both K halves -> bf16 fragments
+  // codes of K half s2 -> bf16 fragments bq[s2]; an NVFP4 lane's block scale
+  // (one per K step) split once per step
   u32x4 bq[2][JT];
-  auto dequant = [&](const FragQ0& f) {
+  float p2[JT], fm[JT];
+  auto split_scales = [&](const FragQ0& f) {
+    if constexpr (WF == W_FP4) {
+#pragma unroll
+      for (int j = 0; j < JT; ++j) e4m3_split(f.sc[j], p2[j], fm[j]);
+    }
+  };
+  auto dequant_half = [&](const FragQ0& f, int s2) {
 #pragma unroll
     for (int j = 0; j < JT; ++j) {
-      if constexpr (WF == W_FP4) {
-        float p2, fm;
-        e4m3_split(f.sc[j], p2, fm);
-        bq[0][j] = fp4_frag(f.b[j][0], p2, fm);
-        bq[1][j] = fp4_frag(f.b[j][1], p2, fm);
-      } else {
-        bq[0][j] = fp8_frag(f.b[j][0], f.b[j][1]);
-        bq[1][j] = fp8_frag(f.b[j][2], f.b[j][3]);
-      }
+      if constexpr (WF == W_FP4)
+        bq[s2][j] = fp4_frag(f.b[j][s2], p2[j], fm[j]);
+      else
+        bq[s2][j] = fp8_frag(f.b[j][2 * s2], f.b[j][2 * s2 + 1]);
     }
   };
   auto mfma_half = [&](const u32x4 (&af)[NF], int s2) {
@@ -245,10 +251,22 @@ __device__ __forceinline__ void tile_q_body(const StreamGemmArgs& a, uint8_t* sm
 #pragma unroll
       for (int i = 0; i < NF; ++i) acc[i][j] = mfma32(af[i], bq[s2][j], acc[i][j]);
   };
+  // one MFMA, then a few conversion instructions, in turn: the conversion of
+  // the other K half runs in the shadow of this half's MFMAs
+  auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < NF * JT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+    }
+  };
   // Pipeline as in the bf16 kernel: "step kt+1 landed" is vmcnt(PER_STEP)
   // once three steps are in flight (a K step's scale load is issued first, so
   // counting it out only waits for it early); f1 (4 reads) is read while f0's
-  // MFMAs run, f0 of the next step (6 or 8 reads) while f1's run. The first
+  // MFMAs run, f0 of the next step (6 or 8 reads) while f1's run. The B
+  // fragments of a K half are converted while the MFMAs of the other half
+  // run: half 1 of step kt during the first half's MFMAs, half 0 of step
+  // kt + 1 (its codes read mid-step) during the second half's. The first
   // code and scale stages are loaded before the first three steps.
   const int nk = K / TBK;
   if (WF == W_FP4) load_scale(0);
@@ -264,25 +282,35 @@ __device__ __forceinline__ void tile_q_body(const StreamGemmArgs& a, uint8_t* sm
 #pragma unroll
   for (int j = 0; j < JT; ++j) f0.sc[j] = 0u;
   read0(f0, 0, 0);
+  MOE_LGK_WAIT0(f0, NF);  // codes and scales of step 0 (its A may still be in flight)
+  split_scales(f0);
+  dequant_half(f0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     read1(f1, kt % NSTAGE);
     MOE_LGK_WAIT0(f0, NF);
-    dequant(f0);
     mfma_half(f0.a, 0);
+    dequant_half(f0, 1);
+    interleave();
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(S::PER_STEP) : "memory");
     __builtin_amdgcn_s_barrier();
-    issue(kt + 3 < nk ? kt + 3 : nk - 1, (kt + 3) % NSTAGE);
     read0(f0, (kt + 1) % NSTAGE, kt + 1);
-    if (WF == W_FP4)
-      MOE_LGK_WAIT1(f1, 2 * JT + NF);
-    else
-      MOE_LGK_WAIT1(f1, JT + NF);
+    MOE_LGK_WAIT1B(f1, f0, NF);
+    split_scales(f0);
     mfma_half(f1.a, 1);
+    dequant_half(f0, 0);
+    interleave();
+    // (a use here keeps the conversion in this block, beside the MFMAs,
+    // rather than sunk past the branch below to its first real use)
+#pragma unroll
+    for (int j = 0; j < JT; ++j) asm volatile("" ::"v"(bq[0][j]));
+    // the stage of step kt - 1 is free since the barrier; issued last, so
+    // that the scale load's branch ends the loop body
+    issue(kt + 3 < nk ? kt + 3 : nk - 1, (kt + 3) % NSTAGE);
   }
   MOE_LGK_WAIT0(f0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #undef MOE_LGK_WAIT0
-#undef MOE_LGK_WAIT1
+#undef MOE_LGK_WAIT1B
   __builtin_amdgcn_s_barrier();
 
   // ---- epilogue through LDS (each wavefront its own strip), scales applied first
