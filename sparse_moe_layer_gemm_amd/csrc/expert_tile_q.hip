@@ -56,6 +56,41 @@ struct QShape {
   static_assert(PIPE <= 160 * 1024, "LDS");
 };
 
+// Two E4M3 block scales (bytes 0 and 1 of c) -> per scale a power of two and
+// a mantissa factor with p2 * fm = s exactly, taken from s's exact fp32 value
+// (exponent field; sign and mantissa under exponent 0, i.e. in [1, 2)): the
+// scaled converter reads only the exponent of p2, and fm has at most 4
+// significant bits. A zero scale gives a zero factor.
+__device__ __forceinline__ void e4m3_split2(uint32_t c, float (&p2)[2], float (&fm)[2]) {
+  const f32x2 sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, 1.0f, false);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t u = __float_as_uint(sv[i]);
+    p2[i] = __uint_as_float(u & 0x7F800000u);
+    fm[i] = (u & 0x7FFFFFFFu) ? __uint_as_float((u & 0x807FFFFFu) | 0x3F800000u) : 0.f;
+  }
+}
+
+// 16-byte LDS read at addr + OFF (an immediate offset), valid after an
+// explicit lgkmcnt wait that takes the result as an operand
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_b128o(uint32_t addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+// the NF A fragments of one K half: rows 32 i + l32 sit 2 KB apart at the
+// same swizzled chunk (the swizzle depends on row bits 2-3 only)
+template <int NF>
+__device__ __forceinline__ void lds_a_frags(u32x4 (&a)[NF], uint32_t addr) {
+  static_assert(NF == 4 || NF == 5, "four or five row fragments");
+  a[0] = lds_b128o<0>(addr);
+  a[1] = lds_b128o<2048>(addr);
+  a[2] = lds_b128o<4096>(addr);
+  a[3] = lds_b128o<6144>(addr);
+  if constexpr (NF == 5) a[4] = lds_b128o<8192>(addr);
+}
+
 // raw codes of one column per lane per K step: 8 B (E2M1) or 16 B (E4M3)
 template <int WF> struct QRaw { typedef u32x4 type; };
 template <> struct QRaw<W_FP4> { typedef u32x2 type; };
@@ -147,11 +182,9 @@ __device__ __forceinline__ void tile_q_body(const StreamGemmArgs& a, uint8_t* sm
   };
   const int l32 = lane & 31, kh = lane >> 5;
   const uint32_t lds0 = (uint32_t)(size_t)(lds_u8*)smem;
-  uint32_t aoff[2][NF], boff[JT], soff[JT];
+  uint32_t aoff[2], boff[JT], soff[JT];
 #pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-    for (int i = 0; i < NF; ++i) aoff[s2][i] = a_off(32 * i + l32, 2 * kh + s2);
+  for (int s2 = 0; s2 < 2; ++s2) aoff[s2] = a_off(l32, 2 * kh + s2);  // row fragment 0
 #pragma unroll
   for (int j = 0; j < JT; ++j) {
     const int c = bcol(j) + l32;
@@ -184,15 +217,9 @@ __device__ __forceinline__ void tile_q_body(const StreamGemmArgs& a, uint8_t* sm
 #pragma unroll
       for (int j = 0; j < JT; ++j) f.sc[j] = lds_byte(sbase + soff[j]);
     }
-    const uint32_t base = lds0 + st * S::A_STAGE;
-#pragma unroll
-    for (int i = 0; i < NF; ++i) f.a[i] = lds_b128(base + aoff[0][i]);
+    lds_a_frags<NF>(f.a, lds0 + st * S::A_STAGE + aoff[0]);
   };
-  auto read1 = [&](FragQ1& f, int st) {
-    const uint32_t base = lds0 + st * S::A_STAGE;
-#pragma unroll
-    for (int i = 0; i < NF; ++i) f.a[i] = lds_b128(base + aoff[1][i]);
-  };
+  auto read1 = [&](FragQ1& f, int st) { lds_a_frags<NF>(f.a, lds0 + st * S::A_STAGE + aoff[1]); };
   // (the fifth A fragment, when there is one, as an operand of its own wait)
 #define MOE_LGK_WAIT0(f, pending)                                                              \
   do {                                                                                         \
@@ -232,8 +259,8 @@ __device__ __forceinline__ void tile_q_body(const StreamGemmArgs& a, uint8_t* sm
   float p2[JT], fm[JT];
   auto split_scales = [&](const FragQ0& f) {
     if constexpr (WF == W_FP4) {
-#pragma unroll
-      for (int j = 0; j < JT; ++j) e4m3_split(f.sc[j], p2[j], fm[j]);
+      static_assert(JT == 2, "two column tiles: both block scales in one conversion");
+      e4m3_split2(f.sc[0] | (f.sc[1] << 8), p2, fm);
     }
   };
   auto dequant_half = [&](const FragQ0& f, int s2) {
