@@ -146,24 +146,50 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const void* __restrict
 }  // namespace
 }  // namespace moe
 
-// Wavefront-wide maximum of a 64-bit key (ROCm device library, DPP row
+// Wavefront-wide maxima of 64- and 32-bit keys (ROCm device library, DPP row
 // operations; the result is the same in every lane).
 extern "C" __device__ __attribute__((const)) unsigned long long __ockl_wfred_max_u64(
     unsigned long long);
+extern "C" __device__ __attribute__((const)) unsigned int __ockl_wfred_max_u32(unsigned int);
 
 namespace moe {
 namespace {
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+__device__ __forceinline__ uint64_t wave_max(uint64_t v) {
   return (uint64_t)__ockl_wfred_max_u64((unsigned long long)v);
 }
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) { return __ockl_wfred_max_u32(v); }
+
+// Selection keys: (order-preserving logit, 0xFFFF - id), so that a maximum is
+// the largest logit and, on equal logits, the lowest id. A bf16 logit's order
+// key has nothing in its low 16 bits, so with bf16 logits the key is 32 bits
+// (the wavefront maxima then compare one register instead of two).
+template <bool BF16_LOGITS>
+struct SelKey {
+  typedef uint64_t type;
+  static __device__ __forceinline__ type make(float v, int e) {
+    return ((uint64_t)float_order_key(v) << 32) | (uint32_t)(0xFFFF - e);
+  }
+  static __device__ __forceinline__ float value(type k) { return float_from_order_key((uint32_t)(k >> 32)); }
+  static __device__ __forceinline__ int id(type k) { return 0xFFFF - (int)(k & 0xFFFFu); }
+};
+template <>
+struct SelKey<true> {
+  typedef uint32_t type;
+  static __device__ __forceinline__ type make(float v, int e) {  // v: a bf16 value
+    return (float_order_key(v) & 0xFFFF0000u) | (uint32_t)(0xFFFF - e);
+  }
+  static __device__ __forceinline__ float value(type k) {
+    return float_from_order_key((k & 0xFFFF0000u) | ((k & 0x80000000u) ? 0u : 0xFFFFu));
+  }
+  static __device__ __forceinline__ int id(type k) { return 0xFFFF - (int)(k & 0xFFFFu); }
+};
 
 // Small batches (T < 1024, where the router GEMM splits K up to 40 ways):
 // one workgroup per token; wavefront w owns experts 64w .. 64w+63, one per
 // lane, and adds that expert's split partials (loaded 32 at a time),
-// the bias, and rounds to the logits dtype. The selection key packs
-// (order-preserving logit, 0xFFFF - id), so a maximum picks the largest logit
-// and, on equal logits, the lowest id. Each wavefront finds its own 8 largest
+// the bias, and rounds to the logits dtype (keys as above). Each wavefront
+// finds its own 8 largest
 // keys (eight wavefront-wide maxima); wavefront 0 merges the 32 candidates
 // into the token's top k.
 template <bool BF16_LOGITS>
@@ -171,11 +197,13 @@ __global__ __launch_bounds__(256) void router_select_wg_kernel(
     const float* __restrict__ part, int n_split, int ldp, int T, int E, int k,
     const float* __restrict__ bias, void* __restrict__ logits, float* __restrict__ logits_f32,
     int32_t* __restrict__ ids, float* __restrict__ w, PermuteOut perm) {
-  __shared__ uint64_t cand[4][8];
+  using SK = SelKey<BF16_LOGITS>;
+  using Key = typename SK::type;
+  __shared__ Key cand[4][8];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x;
   const int e = 64 * wave + lane;
-  uint64_t key = 0;
+  Key key = 0;
   if (e < E) {
     const float* p = part + (size_t)t * ldp + e;
     const size_t sstride = (size_t)T * ldp;
@@ -201,26 +229,26 @@ __global__ __launch_bounds__(256) void router_select_wg_kernel(
     } else {
       static_cast<float*>(logits)[(size_t)t * E + e] = v;
     }
-    key = ((uint64_t)float_order_key(sv) << 32) | (uint32_t)(0xFFFF - e);
+    key = SK::make(sv, e);
   }
   // this wavefront's 8 largest keys, in decreasing order (0 where it has fewer)
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const uint64_t best = wave_max_u64(key);
+    const Key best = wave_max(key);
     if (key == best) key = 0;
     if (lane == 0) cand[wave][j] = best;
   }
   __syncthreads();
   if (wave != 0) return;
-  uint64_t c = (lane < 32) ? cand[lane >> 3][lane & 7] : 0;
+  Key c = (lane < 32) ? cand[lane >> 3][lane & 7] : (Key)0;
   float topv[8];
   int topi[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const uint64_t best = wave_max_u64(c);
+    const Key best = wave_max(c);
     if (c == best) c = 0;
-    topi[j] = 0xFFFF - (int)(best & 0xFFFFu);
-    topv[j] = float_from_order_key((uint32_t)(best >> 32));
+    topi[j] = SK::id(best);
+    topv[j] = SK::value(best);
   }
   if (lane == 0) {
     // softmax over all E, restricted to the chosen set: the normaliser cancels
@@ -276,9 +304,7 @@ __global__ __launch_bounds__(256) void router_select_wg_kernel(
 // l, l + 64, l + 128 and l + 192 (coalesced rows), adds each one's split
 // partials in split order (loaded SB splits at a time, one memory latency per
 // batch; SB covers the split count up to 32), the bias, and rounds to the
-// logits dtype. The selection key packs
-// (order-preserving logit, 0xFFFF - id), so a maximum picks the largest logit
-// and, on equal logits, the lowest id; keys are distinct. Each of the k
+// logits dtype. Keys (as above) are distinct. Each of the k
 // rounds takes every lane's largest remaining key, their wavefront maximum
 // (DPP), and clears it in the lane that holds it: no LDS, no barrier.
 template <bool BF16_LOGITS, int SB>
@@ -305,7 +331,9 @@ __global__ __launch_bounds__(256) void router_select_kernel(
       for (int j = 0; j < SB; ++j)
         if (lane + 64 * q < E && sp0 + j < n_split) v[q] += u[q][j];
   }
-  uint64_t key[4];
+  using SK = SelKey<BF16_LOGITS>;
+  using Key = typename SK::type;
+  Key key[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = lane + 64 * q;
@@ -322,7 +350,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(
       } else {
         static_cast<float*>(logits)[(size_t)t * E + e] = x;
       }
-      key[q] = ((uint64_t)float_order_key(sv) << 32) | (uint32_t)(0xFFFF - e);
+      key[q] = SK::make(sv, e);
     }
   }
   float topv[8];
@@ -332,14 +360,14 @@ __global__ __launch_bounds__(256) void router_select_kernel(
     topv[j] = 0.f;
     topi[j] = 0;
     if (j < k) {
-      const uint64_t m01 = key[0] > key[1] ? key[0] : key[1];
-      const uint64_t m23 = key[2] > key[3] ? key[2] : key[3];
-      const uint64_t best = wave_max_u64(m01 > m23 ? m01 : m23);
+      const Key m01 = key[0] > key[1] ? key[0] : key[1];
+      const Key m23 = key[2] > key[3] ? key[2] : key[3];
+      const Key best = wave_max(m01 > m23 ? m01 : m23);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if (key[q] == best) key[q] = 0;
-      topi[j] = 0xFFFF - (int)(best & 0xFFFFu);
-      topv[j] = float_from_order_key((uint32_t)(best >> 32));
+      topi[j] = SK::id(best);
+      topv[j] = SK::value(best);
     }
   }
   if (lane == 0) {
