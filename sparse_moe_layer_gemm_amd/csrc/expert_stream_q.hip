@@ -351,7 +351,9 @@ __device__ __forceinline__ u32x4 lds_read16o(uint32_t addr) {
   return r;
 }
 
-template <int RG, bool GATE_UP>
+// KT: K has a tail (K % SPAN != 0), whose chunks are clamped and whose block
+// scales are zeroed; without one those checks compile away.
+template <int RG, bool GATE_UP, bool KT>
 __global__ __launch_bounds__(256, 2) void stream_fp4_kernel(StreamGemmArgs a) {
   using S = Fp4Shape<RG>;
   constexpr int SPAN = S::SPAN, CG = S::CG;
@@ -452,23 +454,35 @@ __global__ __launch_bounds__(256, 2) void stream_fp4_kernel(StreamGemmArgs a) {
     // pieces are issued in the 8 steps after the block three before it (same
     // LDS slot) was last read; the issues before the first step repeat pieces
     // of block 1 (same data, slot not yet read).
+    // (measured: handing the step's K offset to the loads as their scalar
+    // offset, which saves the per-lane adds, made the kernel ~3% slower)
     auto issue = [&](int ss, u32x4* o, int t) {
       const int slot = (ss - ss0) % S::NSLOT;
 #pragma unroll
       for (int d = 0; d < S::DPW; ++d) {
-        // chunks past K (a K tail) read the row's first chunk; their scales are zeroed
-        const int ko = ss * SPAN + achk[d];
-        dma16s(arsrc, 2u * (arow[d] + (uint32_t)(ko < K ? ko : 0)),
-               als + slot * S::ASLOT + S::RPI * (S::DPW * wave + d) * S::AROWB);
+        uint8_t* dst = als + slot * S::ASLOT + S::RPI * (S::DPW * wave + d) * S::AROWB;
+        if constexpr (KT) {
+          // chunks past K (a K tail) read the row's first chunk; their scales are zeroed
+          const int ko = ss * SPAN + achk[d];
+          dma16s(arsrc, 2u * (arow[d] + (uint32_t)(ko < K ? ko : 0)), dst);
+        } else {
+          dma16s(arsrc, 2u * (arow[d] + (uint32_t)(ss * SPAN + achk[d])), dst);
+        }
       }
       if (t >= 0)
         issue_s(t / S::SBLK + 2, t % S::SBLK);
       else
         issue_s(1, t + S::SBLK);
-      const int kl = ss * SPAN + S::G * q;
-      const uint32_t kc = kl < K ? (uint32_t)kl / 2 : 0u;
+      if constexpr (KT) {
+        const int kl = ss * SPAN + S::G * q;
+        const uint32_t kc = kl < K ? (uint32_t)kl / 2 : 0u;
 #pragma unroll
-      for (int cg = 0; cg < CG; ++cg) o[cg] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, coff[cg] + kc, 0, 0);
+        for (int cg = 0; cg < CG; ++cg) o[cg] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, coff[cg] + kc, 0, 0);
+      } else {
+        const uint32_t kc = (uint32_t)(ss * SPAN + S::G * q) / 2;
+#pragma unroll
+        for (int cg = 0; cg < CG; ++cg) o[cg] = __builtin_amdgcn_raw_buffer_load_b128(wrsrc, coff[cg] + kc, 0, 0);
+      }
     };
     f32x4 acc[NRG][CG];
 #pragma unroll
@@ -489,7 +503,7 @@ __global__ __launch_bounds__(256, 2) void stream_fp4_kernel(StreamGemmArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       const uint32_t slot = lds_base + ((ss - ss0) % S::NSLOT) * S::ASLOT;
       const uint32_t sslot = sbase + (((ss - ss0) / S::SBLK) % 3) * S::SSLOT + ((ss - ss0) % S::SBLK) * 16;
-      const bool kin = ss * SPAN + S::G * q < K;  // false only in a K tail
+      const bool kin = !KT || ss * SPAN + S::G * q < K;  // false only in a K tail
       // block scales 2q, 2q + 1 of this lane's columns (bytes 0, 1 of a u16)
       uint32_t scr[CG];
       {
@@ -661,12 +675,19 @@ __global__ __launch_bounds__(256, 2) void stream_fp4_kernel(StreamGemmArgs a) {
 }
 
 // NVFP4: 16 rows per pass once experts average more than 8 rows, else 8
+template <bool GU, bool KT>
+void launch_fp4_k(dim3 grid, const StreamGemmArgs& a, hipStream_t st) {
+  if ((long long)a.rows > 8LL * a.E)
+    stream_fp4_kernel<4, GU, KT><<<grid, 256, 0, st>>>(a);
+  else
+    stream_fp4_kernel<2, GU, KT><<<grid, 256, 0, st>>>(a);
+}
 template <bool GU>
 void launch_fp4(dim3 grid, const StreamGemmArgs& a, hipStream_t st) {
-  if ((long long)a.rows > 8LL * a.E)
-    stream_fp4_kernel<4, GU><<<grid, 256, 0, st>>>(a);
+  if (a.K % Fp4Shape<2>::SPAN != 0)
+    launch_fp4_k<GU, true>(grid, a, st);
   else
-    stream_fp4_kernel<2, GU><<<grid, 256, 0, st>>>(a);
+    launch_fp4_k<GU, false>(grid, a, st);
 }
 
 }  // namespace
