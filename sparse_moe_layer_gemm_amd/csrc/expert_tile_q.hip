@@ -79,6 +79,18 @@ __device__ __forceinline__ u32x4 lds_b128o(uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
   return r;
 }
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_b64o(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ uint32_t lds_b32o(uint32_t addr) {
+  uint32_t r;
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
 // the NF A fragments of one K half: rows 32 i + l32 sit 2 KB apart at the
 // same swizzled chunk (the swizzle depends on row bits 2-3 only)
 template <int NF>
@@ -497,9 +509,13 @@ __device__ __forceinline__ void fp4_to_fp8(uint32_t d, float p2, float fm8, int3
   const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 1);
   const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 2);
   const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, p2, 3);
-  int32_t r = __builtin_amdgcn_cvt_pk_fp8_f32(v0.x * fm8, v0.y * fm8, 0, false);
+  // each first conversion writes the low half of a dword whose high half the
+  // second writes: its "old" operand is one of its own (dead) inputs, whose
+  // register the result can take, rather than a zero that needs a move
+  const float p0 = v0.x * fm8, p1 = v0.y * fm8, p4 = v2.x * fm8, p5 = v2.y * fm8;
+  int32_t r = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(p0), false);
   o0 = __builtin_amdgcn_cvt_pk_fp8_f32(v1.x * fm8, v1.y * fm8, r, true);
-  r = __builtin_amdgcn_cvt_pk_fp8_f32(v2.x * fm8, v2.y * fm8, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(p4, p5, __float_as_int(p4), false);
   o1 = __builtin_amdgcn_cvt_pk_fp8_f32(v3.x * fm8, v3.y * fm8, r, true);
 }
 
@@ -597,9 +613,13 @@ __global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmAr
                                     : nullptr;
   // E2M1 code piece p (of this wavefront's 2 QB) of code stage cs; chunks past
   // the row (a K tail) read the row's start
-  auto load_code = [&](int cs, int p) {
+  // (hf: which half of the pieces, q: the piece within it; selected by value,
+  // not by a runtime index into the pointer array, which costs indexed moves)
+  auto load_code = [&](int cs, int hf, int q) {
+    const int p = hf * S::QB + q;
+    const uint8_t* src = bsrc[q] + (hf ? bsrc[S::QB + q] - bsrc[q] : 0);
     const int ko = 64 * cs + 16 * (lane >> 4);
-    dma16(bsrc[p] + (ko + 16 <= K / 2 ? 64 * cs : -16 * (lane >> 4)),
+    dma16(src + (ko + 16 <= K / 2 ? 64 * cs : -16 * (lane >> 4)),
           smem + S::C_OFF + (cs % 3) * S::CSLOT + (2 * S::QB * wave + p) * 1024);
   };
   // scale piece sp (64 columns) of scale stage t
@@ -628,7 +648,7 @@ __global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmAr
       if (WF == W_FP8)
         dma16(bsrc[q] + 64 * kt, As + S::A_STAGE + ((S::BN / 4) * wave + 16 * q) * 64);
       else
-        load_code((kt + 1) >> 1, ((kt + 1) & 1) * S::QB + q);
+        load_code((kt + 1) >> 1, (kt + 1) & 1, q);
     }
   };
 
@@ -689,23 +709,34 @@ __global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmAr
     // of scale stage kt / 4
     const uint32_t cbase = lds0 + S::C_OFF + ((kt >> 1) % 3) * S::CSLOT + (kt & 1) * 512;
     const uint32_t sbase = lds0 + S::S_OFF + ((kt >> 2) % 3) * S::SSLOT + 4 * (kt & 3);
+    if constexpr (WF == W_FP8) {
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int j = 2 * h + jj;
-      if constexpr (WF == W_FP8) {
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * h + jj;
         f.b[jj][0] = lds_b128(base + boff[j][0]);
         f.b[jj][1] = lds_b128(base + boff[j][1]);
-      } else {
-        f.q[jj][0] = lds_b64(cbase + boff[j][0]);
-        f.q[jj][1] = lds_b64(cbase + boff[j][1]);
-        f.sc[jj] = lds_b32(sbase + soff[j]);
       }
+    } else {
+      // column tiles 2h and 2h + 1 are 32 columns (two 16-column blocks, 2 KB of
+      // codes, 512 B of scales) apart; a column's second 8 B run is 256 B on
+      const uint32_t cb = cbase + boff[2 * h][0], sb = sbase + soff[2 * h];
+      f.q[0][0] = lds_b64o<0>(cb);
+      f.q[0][1] = lds_b64o<256>(cb);
+      f.sc[0] = lds_b32o<0>(sb);
+      f.q[1][0] = lds_b64o<2048>(cb);
+      f.q[1][1] = lds_b64o<2048 + 256>(cb);
+      f.sc[1] = lds_b32o<512>(sb);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f.a[i][0] = lds_b128(base + aoff[i][0]);
-      f.a[i][1] = lds_b128(base + aoff[i][1]);
-    }
+    // rows 32 i + l32 of the A tile sit 2 KB apart at the same swizzled chunks
+    const uint32_t a0 = base + aoff[0][0], a1 = base + aoff[0][1];
+    f.a[0][0] = lds_b128o<0>(a0);
+    f.a[0][1] = lds_b128o<0>(a1);
+    f.a[1][0] = lds_b128o<2048>(a0);
+    f.a[1][1] = lds_b128o<2048>(a1);
+    f.a[2][0] = lds_b128o<4096>(a0);
+    f.a[2][1] = lds_b128o<4096>(a1);
+    f.a[3][0] = lds_b128o<6144>(a0);
+    f.a[3][1] = lds_b128o<6144>(a1);
     if (!GATE_UP) f.as = lds_b32(roff + (kt >> 1) * S::BM);
   };
 #define MOE_F8_WAIT_A(f, pending, ...)                                                        \
@@ -794,7 +825,7 @@ __global__ __launch_bounds__(256, 1) void tile_f8_kernel(F8Args f8, StreamGemmAr
   const int nk = K / 64;
   if constexpr (WF == W_FP4) {  // code stage 0 and scale stage 0
 #pragma unroll
-    for (int p = 0; p < 2 * S::QB; ++p) load_code(0, p);
+    for (int p = 0; p < 2 * S::QB; ++p) load_code(0, p / S::QB, p % S::QB);
     for (int sp = wave; sp < NSP; sp += 4) load_scale(0, sp);
   }
   issue(0, 0);
