@@ -82,8 +82,8 @@ __device__ __forceinline__ ARows a_rows(const StreamGemmArgs& a, bool gate_up, i
 // the reduction kernel does), so the gate/up reduction needs no launch of its
 // own; the workgroups of the first column group also write it to h_out. Until
 // that barrier no wavefront leaves early.
-template <bool GATE_UP, bool FOLD = false>
-__global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
+template <bool GATE_UP, bool FOLD, int NS = kMaxStreamSplit>
+__device__ __forceinline__ void stream_bf16_body(const StreamGemmArgs& a) {
   static_assert(!(FOLD && GATE_UP), "h is folded into the down GEMM only");
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, j = lane & 15;
@@ -113,39 +113,62 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
   const int ks1 = a.ksplit > 1 ? min(nk, ks0 + a.ksteps) : nk;
   if (ks0 >= ks1) return;
 
+  // A and B operands of one K step, in registers
+  struct Ops {
+    u32x4 a[2], b[8];
+  };
+  auto load_b = [&](int ks, Ops& o) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) o.b[r] = load_w(wb + (size_t)(ks * 32 + 8 * g + r) * N);
+  };
+  Ops first;  // FOLD: the first step's weights, loaded while h is formed
   extern __shared__ __align__(16) uint8_t hl[];  // FOLD: 32 rows of h, hlds_stride bytes each
   if constexpr (FOLD) {
-    const int q = (ks1 - ks0) * 8;  // float4 columns of h this split reads
+    // one h column per thread and item; the split sums of an item are loaded
+    // together (unconditionally: an item exists only for rows that hold one)
+    const int q = (ks1 - ks0) * 32;  // columns of h this split reads (>= 256)
     const int hc0 = ks0 * 32;
-    for (int it = threadIdx.x; it < MROWS * q; it += 256) {
+    auto fold = [&](int it, bool with_b) {
       const int m = it / q;
-      const int c = 4 * (it - m * q);
-      uint2 pk = make_uint2(0u, 0u);  // rows past the expert's end: zeros, never stored
-      if (m < cnt) {
-        const float* pg = a.hpart + (size_t)(r0 + m) * 2 * a.I + hc0 + c;
-        f32x4 gv[kMaxStreamSplit], uv[kMaxStreamSplit];
+      const int c = it - m * q;
+      const float* pg = a.hpart + (size_t)(r0 + m) * 2 * a.I + hc0 + c;
+      // all NS split slots are loaded (slots past the split count re-read
+      // split 0) so that no branch separates these loads from the weight
+      // loads below; the unused slots add -0, which changes no sum
+      float gv[NS], uv[NS];
 #pragma unroll
-        for (int sp = 0; sp < kMaxStreamSplit; ++sp)
-          if (sp < a.hsplit) {
-            gv[sp] = *reinterpret_cast<const f32x4*>(pg + sp * a.hpart_stride);
-            uv[sp] = *reinterpret_cast<const f32x4*>(pg + sp * a.hpart_stride + a.I);
-          }
-        f32x4 gs = gv[0], us = uv[0];
-#pragma unroll
-        for (int sp = 1; sp < kMaxStreamSplit; ++sp)
-          if (sp < a.hsplit) {
-            gs += gv[sp];
-            us += uv[sp];
-          }
-        pk.x = f32_to_bf16_bits(silu(gs[0]) * us[0]) | (f32_to_bf16_bits(silu(gs[1]) * us[1]) << 16);
-        pk.y = f32_to_bf16_bits(silu(gs[2]) * us[2]) | (f32_to_bf16_bits(silu(gs[3]) * us[3]) << 16);
-        // the first column group also stores the h it forms, so that h is in
-        // the workspace as after the reduction kernel (the splits' K ranges
-        // cover every column of h once)
-        if (blockIdx.x == 0 && a.h_out)
-          *reinterpret_cast<uint2*>(a.h_out + (size_t)(r0 + m) * a.I + hc0 + c) = pk;
+      for (int sp = 0; sp < NS; ++sp) {
+        const size_t o = (size_t)(sp < a.hsplit ? sp : 0) * a.hpart_stride;
+        gv[sp] = pg[o];
+        uv[sp] = pg[o + a.I];
       }
-      *reinterpret_cast<uint2*>(hl + (size_t)m * a.hlds_stride + 2 * c) = pk;
+      // the first item's loads are followed by the first step's weight
+      // loads, which do not depend on h: the sums below wait only for the
+      // older partial-sum loads, and the weights arrive meanwhile
+      if (with_b) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_b(ks0, first);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      float gs = gv[0], us = uv[0];
+#pragma unroll
+      for (int sp = 1; sp < NS; ++sp) {
+        gs += sp < a.hsplit ? gv[sp] : -0.0f;
+        us += sp < a.hsplit ? uv[sp] : -0.0f;
+      }
+      const uint16_t hv = (uint16_t)f32_to_bf16_bits(silu(gs) * us);
+      // the first column group also stores the h it forms, so that h is in
+      // the workspace as after the reduction kernel (the splits' K ranges
+      // cover every column of h once)
+      if (blockIdx.x == 0 && a.h_out) a.h_out[(size_t)(r0 + m) * a.I + hc0 + c] = hv;
+      *reinterpret_cast<uint16_t*>(hl + (size_t)m * a.hlds_stride + 2 * c) = hv;
+    };
+    fold(threadIdx.x, true);  // row 0: every thread has a column (q >= 256)
+    for (int it = threadIdx.x + 256; it < cnt * q; it += 256) fold(it, false);
+    // rows past the expert's end feed only accumulators that are never stored
+    for (int it = cnt * q + threadIdx.x; it < MROWS * q; it += 256) {
+      const int m = it / q;
+      *reinterpret_cast<uint16_t*>(hl + (size_t)m * a.hlds_stride + 2 * (it - m * q)) = 0;
     }
     __syncthreads();
     if (tile >= n_tiles) return;  // no barrier follows
@@ -168,10 +191,7 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
     // MFMAs of a step wait only for that step's loads (loads under divergent
     // branches, or a copy from one set to the other, make the compiler wait
     // for every load in flight, the next step's included).
-    struct Ops {
-      u32x4 a[2], b[8];
-    };
-    auto load = [&](int ks, Ops& o) {
+    auto load_a = [&](int ks, Ops& o) {
 #pragma unroll
       for (int f = 0; f < 2; ++f) {
         if constexpr (FOLD)  // row 16f + j of the LDS h rows (mc is 0: cnt <= 32)
@@ -180,8 +200,10 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
         else
           o.a[f] = load_u32x4(ar.row[f] + ks * 32 + 8 * g);
       }
-#pragma unroll
-      for (int r = 0; r < 8; ++r) o.b[r] = load_w(wb + (size_t)(ks * 32 + 8 * g + r) * N);
+    };
+    auto load = [&](int ks, Ops& o) {
+      load_a(ks, o);
+      load_b(ks, o);
     };
     auto step = [&](const Ops& o) {
       // 8x8 transpose: fragment for column 2q / 2q+1 from dword q of rows 2p, 2p+1
@@ -203,7 +225,12 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
       }
     };
     Ops o0, o1;
-    load(ks0, o0);
+    if constexpr (FOLD) {  // the first step's weights are already in flight
+      o0 = first;
+      load_a(ks0, o0);
+    } else {
+      load(ks0, o0);
+    }
     int ks = ks0;
     for (; ks + 1 < ks1; ks += 2) {
       load(ks + 1, o1);
@@ -264,6 +291,19 @@ __global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
       }
     }
   }
+}
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(256) void stream_bf16_kernel(StreamGemmArgs a) {
+  stream_bf16_body<GATE_UP, false>(a);
+}
+// down GEMM with h folded in from up to NS gate/up splits: held to two
+// wavefronts per SIMD (256 registers), so that the whole small-batch grid is
+// resident at once
+template <int NS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void stream_bf16_fold_kernel(
+    StreamGemmArgs a) {
+  stream_bf16_body<false, true, NS>(a);
 }
 
 // ------------------------------------------------------------------ split-K reductions
@@ -339,10 +379,12 @@ hipError_t launch_one(int wfmt, const StreamGemmArgs& a, hipStream_t st) {
     grid.z = a.ksplit;
     switch (wfmt) {
       case W_BF16:
-        if (fold)
-          stream_bf16_kernel<false, true><<<grid, 256, MROWS * a.hlds_stride, st>>>(a);
-        else
+        if (!fold)
           stream_bf16_kernel<GU><<<grid, 256, 0, st>>>(a);
+        else if (a.hsplit <= 8)
+          stream_bf16_fold_kernel<8><<<grid, 256, MROWS * a.hlds_stride, st>>>(a);
+        else
+          stream_bf16_fold_kernel<kMaxStreamSplit><<<grid, 256, MROWS * a.hlds_stride, st>>>(a);
         break;
       default: {
         const hipError_t e = launch_stream_q(wfmt, GU, grid, a, st);
@@ -362,10 +404,12 @@ hipError_t launch_one(int wfmt, const StreamGemmArgs& a, hipStream_t st) {
   }
   switch (wfmt) {
     case W_BF16:
-      if (fold)
-        stream_bf16_kernel<false, true><<<grid, 256, MROWS * a.hlds_stride, st>>>(a);
-      else
+      if (!fold)
         stream_bf16_kernel<GU><<<grid, 256, 0, st>>>(a);
+      else if (a.hsplit <= 8)
+        stream_bf16_fold_kernel<8><<<grid, 256, MROWS * a.hlds_stride, st>>>(a);
+      else
+        stream_bf16_fold_kernel<kMaxStreamSplit><<<grid, 256, MROWS * a.hlds_stride, st>>>(a);
       break;
     default: return launch_stream_q(wfmt, GU, grid, a, st);
   }
