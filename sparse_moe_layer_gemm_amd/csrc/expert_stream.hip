@@ -125,13 +125,15 @@ __device__ __forceinline__ void stream_bf16_body(const StreamGemmArgs& a) {
   extern __shared__ __align__(16) uint8_t hl[];  // FOLD: 32 rows of h, hlds_stride bytes each
   if constexpr (FOLD) {
     // one h column per thread and item; the split sums of an item are loaded
-    // together (unconditionally: an item exists only for rows that hold one)
-    const int q = (ks1 - ks0) * 32;  // columns of h this split reads (>= 256)
+    // together, unconditionally (an item past the expert's rows reads its
+    // first row and is stored as zeros)
+    const int q = (ks1 - ks0) * 32;  // columns of h this split reads
     const int hc0 = ks0 * 32;
     auto fold = [&](int it, bool with_b) {
       const int m = it / q;
       const int c = it - m * q;
-      const float* pg = a.hpart + (size_t)(r0 + m) * 2 * a.I + hc0 + c;
+      const bool ok = m < cnt;
+      const float* pg = a.hpart + (size_t)(r0 + (ok ? m : 0)) * 2 * a.I + hc0 + c;
       // all NS split slots are loaded (slots past the split count re-read
       // split 0) so that no branch separates these loads from the weight
       // loads below; the unused slots add -0, which changes no sum
@@ -156,17 +158,19 @@ __device__ __forceinline__ void stream_bf16_body(const StreamGemmArgs& a) {
         gs += sp < a.hsplit ? gv[sp] : -0.0f;
         us += sp < a.hsplit ? uv[sp] : -0.0f;
       }
-      const uint16_t hv = (uint16_t)f32_to_bf16_bits(silu(gs) * us);
+      const uint16_t hv = ok ? (uint16_t)f32_to_bf16_bits(silu(gs) * us) : (uint16_t)0;
       // the first column group also stores the h it forms, so that h is in
       // the workspace as after the reduction kernel (the splits' K ranges
       // cover every column of h once)
-      if (blockIdx.x == 0 && a.h_out) a.h_out[(size_t)(r0 + m) * a.I + hc0 + c] = hv;
+      if (ok && blockIdx.x == 0 && a.h_out) a.h_out[(size_t)(r0 + m) * a.I + hc0 + c] = hv;
       *reinterpret_cast<uint16_t*>(hl + (size_t)m * a.hlds_stride + 2 * c) = hv;
     };
-    fold(threadIdx.x, true);  // row 0: every thread has a column (q >= 256)
+    // every thread has an item below 256 (q >= 32, so they lie in the LDS rows)
+    fold(threadIdx.x, true);
     for (int it = threadIdx.x + 256; it < cnt * q; it += 256) fold(it, false);
     // rows past the expert's end feed only accumulators that are never stored
-    for (int it = cnt * q + threadIdx.x; it < MROWS * q; it += 256) {
+    const int z0 = cnt * q > 256 ? cnt * q : 256;  // items below 256 were written above
+    for (int it = z0 + threadIdx.x; it < MROWS * q; it += 256) {
       const int m = it / q;
       *reinterpret_cast<uint16_t*>(hl + (size_t)m * a.hlds_stride + 2 * (it - m * q)) = 0;
     }

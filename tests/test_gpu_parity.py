@@ -72,6 +72,10 @@ SMALL = [
     # at most 32 pairs with gate/up split: the down kernel forms h in LDS from
     # the gate/up partial sums (here several rows per expert, down split too)
     MC("fold_h_32_pairs", 128, T=4, H=1024, E=16, k=8, I=1024),
+    # h formed in the down kernel where its last K split is short (I = 1600:
+    # 50 K steps in splits of 9, the last of 5), so that split's first items
+    # span more than one row of h
+    MC("fold_short_last_split", 129, T=2, H=2048, E=8, k=2, I=1600),
 ]
 
 
