@@ -33,6 +33,8 @@ SMALL = [
     MC("fp4_small", 108, T=50, H=256, E=8, k=2, I=192, w_dtype="fp4"),
     MC("fp4_many_rows", 109, T=300, H=512, E=16, k=4, I=256, w_dtype="fp4"),
     MC("f32_ragged", 110, T=37, H=64, E=9, k=2, I=64, x_dtype="f32", w_dtype="f32"),
+    # fp32 experts with many 16-row passes per expert
+    MC("f32_many_rows", 130, T=300, H=256, E=4, k=2, I=192, x_dtype="f32", w_dtype="f32"),
     # >= 32 rows per expert: the 128 x 256 tiled kernel, with partial N tiles
     # (I = 192: second gate/up tile half valid; H = 192: down tile 3/4 valid)
     MC("tile_ragged", 112, T=150, H=192, E=4, k=2, I=192),
