@@ -365,12 +365,19 @@ def hbm_ceiling(torch, moe, nbytes=4 << 30, reps=10):
             "frac_of_peak": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+LAYERS_PER_GRAPH = 16  # layer calls per captured graph in the small-batch record
+
+
 def decode_small(torch, moe, dec, reps=200):
     """Small-batch decode (H=5120, E=256, k=8): T in {1, 8, 32} at I = 1536 (the decode
     layer's weights) and I = 2560 (the width the checkpoint sizes imply; only the routed
     experts' weights are generated, the rest is never read). Per case: moe_forward back to
-    back (events around `reps` calls), and the same call captured once in a HIP graph and
-    replayed back to back; weight GB/s counts the touched experts' bytes."""
+    back (events around `reps` calls) on distinct inputs in turn (so consecutive calls read
+    mostly different experts, as consecutive layers do); the same sequence captured as
+    LAYERS_PER_GRAPH calls in one HIP graph and replayed back to back (per-layer time, the
+    way a model's captured decode step runs its layers), and, for reference, one call per
+    graph (which adds a graph launch to every layer); weight GB/s counts the touched
+    experts' bytes (mean over the inputs)."""
     import synth
     base = synth.CONFIGS["decode_t128"]
     E, H, k = base.E, base.H, base.k
@@ -397,48 +404,62 @@ def decode_small(torch, moe, dec, reps=200):
             dw = moe.ExpertWeights(moe.MOE_BF16, gu, dn)
         for T in (1, 8, 32):
             cfg = base.with_(name=f"decode_t{T}_i{I}", T=T, I=I)
-            x = moe.to_device_bf16(dec.x_host[:T])
+            # R distinct inputs (consecutive T-token slices of the first 32 tokens,
+            # whose experts the I = 2560 case generates), used in turn, so that
+            # consecutive calls mostly read different experts, as consecutive
+            # layers do
+            R = max(1, min(LAYERS_PER_GRAPH, 32 // T))
+            xs = [moe.to_device_bf16(dec.x_host[r * T:(r + 1) * T]) for r in range(R)]
+            ids = [torch.empty((T, k), dtype=torch.int32, device="cuda") for _ in range(R)]
             o = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
-            ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
             ws = moe.workspace(moe.moe_forward_workspace_size(T, H, I, E, k, dw))
 
-            def fwd():
-                moe.moe_forward(x, dec.wr, None, dw, I, k, o, ws, topk_ids=ids)
-            for _ in range(10):
-                fwd()
+            def fwd(i):
+                moe.moe_forward(xs[i % R], dec.wr, None, dw, I, k, o, ws, topk_ids=ids[i % R])
+            for i in range(10 * R):
+                fwd(i)
             torch.cuda.synchronize()
-            n_touched = int(np.unique(ids.cpu().numpy()).size)
+            n_touched = float(np.mean([np.unique(t.cpu().numpy()).size for t in ids]))
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            for _ in range(reps):
-                fwd()
+            for i in range(reps):
+                fwd(i)
             e1.record()
             torch.cuda.synchronize()
             eager_ms = e0.elapsed_time(e1) / reps
-            g = torch.cuda.CUDAGraph()
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                fwd()
-            torch.cuda.current_stream().wait_stream(side)
-            with torch.cuda.graph(g):
-                fwd()
-            for _ in range(10):
-                g.replay()
-            torch.cuda.synchronize()
-            e0.record()
-            for _ in range(reps):
-                g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            graph_ms = e0.elapsed_time(e1) / reps
+
+            def graph_ms_per_layer(layers):
+                # `layers` consecutive calls captured in one graph, replayed back to back
+                g = torch.cuda.CUDAGraph()
+                side = torch.cuda.Stream()
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    fwd(0)
+                torch.cuda.current_stream().wait_stream(side)
+                with torch.cuda.graph(g):
+                    for i in range(layers):
+                        fwd(i)
+                for _ in range(3):
+                    g.replay()
+                torch.cuda.synchronize()
+                n = max(1, reps // layers)
+                e0.record()
+                for _ in range(n):
+                    g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / (n * layers)
+                del g
+                return ms
+            graph1_ms = graph_ms_per_layer(1)
+            graph_ms = graph_ms_per_layer(LAYERS_PER_GRAPH)
             wbytes = n_touched * expert_bytes(cfg)
-            out.append({"T": T, "I": I, "touched_experts": n_touched,
+            out.append({"T": T, "I": I, "touched_experts": round(n_touched, 2), "distinct_inputs": R,
                         "ms_per_step": round(eager_ms, 4), "graph_replay_ms": round(graph_ms, 4),
+                        "graph_replay_one_layer_ms": round(graph1_ms, 4),
                         "tokens_per_s": round(T / (graph_ms / 1e3), 1),
                         "weight_GBps": round(wbytes / (graph_ms / 1e3) / 1e9, 1),
                         "weight_frac_of_peak_hbm": round(wbytes / (graph_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)})
-            del g
         if I != base.I:
             del dw, gu, dn
     return out
