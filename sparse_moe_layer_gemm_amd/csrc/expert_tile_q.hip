@@ -56,21 +56,6 @@ struct QShape {
   static_assert(PIPE <= 160 * 1024, "LDS");
 };
 
-// Two E4M3 block scales (bytes 0 and 1 of c) -> per scale a power of two and
-// a mantissa factor with p2 * fm = s exactly, taken from s's exact fp32 value
-// (exponent field; sign and mantissa under exponent 0, i.e. in [1, 2)): the
-// scaled converter reads only the exponent of p2, and fm has at most 4
-// significant bits. A zero scale gives a zero factor.
-__device__ __forceinline__ void e4m3_split2(uint32_t c, float (&p2)[2], float (&fm)[2]) {
-  const f32x2 sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, 1.0f, false);
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t u = __float_as_uint(sv[i]);
-    p2[i] = __uint_as_float(u & 0x7F800000u);
-    fm[i] = (u & 0x7FFFFFFFu) ? __uint_as_float((u & 0x807FFFFFu) | 0x3F800000u) : 0.f;
-  }
-}
-
 // 16-byte LDS read at addr + OFF (an immediate offset), valid after an
 // explicit lgkmcnt wait that takes the result as an operand
 template <int OFF>
@@ -148,20 +133,44 @@ __device__ __forceinline__ void tile_q_body(const StreamGemmArgs& a, uint8_t* sm
   // 16-column block ib at ib * 1024, 16 B chunk q of the stage's 64 B at
   // + 256 q, column c of the block at + 16 c (a load's lane l is chunk l / 16
   // of column l % 16). Wavefront w loads blocks 4 w .. 4 w + 3, QB per K step.
-  const uint8_t* csrc[S::CSS * S::QB];
-#pragma unroll
-  for (int p = 0; p < S::CSS * S::QB; ++p)
-    csrc[p] = wq + ((size_t)e * N + mcol(16 * (4 * wave + p) + (lane & 15))) * row_bytes + 16 * (lane >> 4);
+  // A wavefront's blocks are consecutive matrix columns of one side (gate,
+  // up, or the down GEMM's N): block p's column is col0 + 16 p, columns past
+  // the side's end read its last column (they feed accumulators never
+  // stored), so a block's address is arithmetic in p rather than a runtime
+  // index into per-block pointers.
+  // the expert's codes as a buffer (its byte size fits 31 bits, checked by the host)
+  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(wq + (size_t)e * N * row_bytes), (short)0, N * row_bytes, 0x00020000);
+  int col0, colmax;
+  {
+    const int c = 64 * wave + (lane & 15);  // LDS column of block 0
+    if (GATE_UP) {
+      const bool up = c >= S::BN / 2;
+      col0 = (up ? a.I : 0) + nt * (S::BN / 2) + (up ? c - S::BN / 2 : c);
+      colmax = (up ? 2 * a.I : a.I) - 1;
+    } else {
+      col0 = nt * S::BN + c;
+      colmax = N - 1;
+    }
+  }
+  const uint32_t kq = 16 * (lane >> 4);
+  auto code_off = [&](int p) -> uint32_t {
+    const int col = col0 + 16 * p;
+    return (uint32_t)(col < colmax ? col : colmax) * (uint32_t)row_bytes + kq;
+  };
   // scale stage t holds 16 B per column (K steps 8 t .. 8 t + 7) at 16 column;
   // wavefront w loads its 64 columns' 16 B, lane l column 64 w + l
   const uint8_t* ssrc = WF == W_FP4 ? static_cast<const uint8_t*>(a.w_scale) +
                                           ((size_t)e * N + mcol(64 * wave + lane)) * (size_t)(K / 16)
                                     : nullptr;
   // code piece p of stage cs (chunks past the row, in a K tail, read its start)
+  // (chunks past the row, in a K tail, read the next row's bytes or, past
+  // the buffer, zeros: they belong to K steps that are never computed)
   auto load_code = [&](int cs, int p) {
-    const int ko = 64 * cs + 16 * (lane >> 4);
-    dma16(csrc[p] + (ko + 16 <= row_bytes ? 64 * cs : -16 * (lane >> 4)),
-          smem + S::C_OFF + (cs % S::NCS) * S::CSLOT + (4 * wave + p) * 1024);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc,
+                                             (__attribute__((address_space(3))) void*)(smem + S::C_OFF +
+                                                 (cs % S::NCS) * S::CSLOT + (4 * wave + p) * 1024),
+                                             16, code_off(p), 64 * cs, 0, 0);
   };
   auto load_scale = [&](int t) {
     const int ko = 16 * t;
@@ -265,21 +274,25 @@ __device__ __forceinline__ void tile_q_body(const StreamGemmArgs& a, uint8_t* sm
                    : "n"(pending)                                                              \
                    : "memory");                                                                \
   } while (0)
-  // codes of K half s2 -> bf16 fragments bq[s2]; an NVFP4 lane's block scale
-  // (one per K step) split once per step
+  // codes of K half s2 -> bf16 fragments bq[s2]; an NVFP4 lane's block
+  // scales (one per column tile and K step) as fp32, both in one conversion.
+  // Each code's E2M1 value times its E4M3 scale has at most 6 significant
+  // bits, so the fp32 product, and its bf16 upper half, are exact.
   u32x4 bq[2][JT];
-  float p2[JT], fm[JT];
+  float sfv[JT];
   auto split_scales = [&](const FragQ0& f) {
     if constexpr (WF == W_FP4) {
       static_assert(JT == 2, "two column tiles: both block scales in one conversion");
-      e4m3_split2(f.sc[0] | (f.sc[1] << 8), p2, fm);
+      const f32x2 sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(f.sc[0] | (f.sc[1] << 8), 1.0f, false);
+      sfv[0] = sv.x;
+      sfv[1] = sv.y;
     }
   };
   auto dequant_half = [&](const FragQ0& f, int s2) {
 #pragma unroll
     for (int j = 0; j < JT; ++j) {
       if constexpr (WF == W_FP4)
-        bq[s2][j] = fp4_frag(f.b[j][s2], p2[j], fm[j]);
+        bq[s2][j] = fp4_frag(f.b[j][s2], 1.0f, sfv[j]);
       else
         bq[s2][j] = fp8_frag(f.b[j][2 * s2], f.b[j][2 * s2 + 1]);
     }
@@ -1103,6 +1116,9 @@ hipError_t launch_expert_tile_q(int wfmt, const StreamGemmArgs& gu, const Stream
   // one table of 128-row tiles, an expert's last of up to 160 (its tail of
   // <= 32 rows merged): at most P/128 + E of them
   const int max_tiles = (P + 127) / 128 + E;
+  // the kernels address one expert's codes as a buffer
+  if ((long long)gu.N * gu.K > 0x7FFFFFFFLL || (long long)dn.N * dn.K > 0x7FFFFFFFLL)
+    return hipErrorInvalidValue;
   int32_t* tile_m0 = tile_e + max_tiles;
   int32_t* counts = tile_m0 + max_tiles;
   tile_table_kernel<<<1, 256, 0, st>>>(gu.offsets, E, 128, 32, tile_e, tile_m0, counts);
