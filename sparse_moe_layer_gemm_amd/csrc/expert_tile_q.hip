@@ -15,10 +15,10 @@ namespace {
 // column's codes (16 B for E2M1, 32 B for E4M3) and, for E2M1, the dword of
 // block scales holding this step's two come in by direct loads next to the A
 // tile. B fragments are read as one contiguous run per lane and converted to
-// bf16 in registers: E4M3 -> bf16 is exact in the hardware converter; for
-// E2M1 the converter applies the power of two of the E4M3 block scale and an
-// fp32 multiply the scale's mantissa factor (the product has at most 6
-// significant bits, so it is exact, as is its bf16 upper half). Per-channel
+// bf16 in registers: E4M3 -> bf16 is exact in the hardware converter; E2M1
+// codes become fp32 in the converter and one fp32 multiply applies the E4M3
+// block scale (the product has at most 6 significant bits, so it is exact, as
+// is its bf16 upper half). Per-channel
 // (E4M3) and per-expert (E2M1) fp32 scales multiply the accumulators in the
 // epilogue. Within a K step, lane half kh takes K 16*kh .. 16*kh+15 (MFMA s
 // the 8 from 16*kh + 8*s), so a lane's codes are contiguous and, for E2M1,
@@ -280,7 +280,7 @@ __device__ __forceinline__ void tile_q_body(const StreamGemmArgs& a, uint8_t* sm
   // bits, so the fp32 product, and its bf16 upper half, are exact.
   u32x4 bq[2][JT];
   float sfv[JT];
-  auto split_scales = [&](const FragQ0& f) {
+  auto scales_f32 = [&](const FragQ0& f) {
     if constexpr (WF == W_FP4) {
       static_assert(JT == 2, "two column tiles: both block scales in one conversion");
       const f32x2 sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(f.sc[0] | (f.sc[1] << 8), 1.0f, false);
@@ -335,7 +335,7 @@ __device__ __forceinline__ void tile_q_body(const StreamGemmArgs& a, uint8_t* sm
   for (int j = 0; j < JT; ++j) f0.sc[j] = 0u;
   read0(f0, 0, 0);
   MOE_LGK_WAIT0(f0, NF);  // codes and scales of step 0 (its A may still be in flight)
-  split_scales(f0);
+  scales_f32(f0);
   dequant_half(f0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     read1(f1, kt % NSTAGE);
@@ -347,7 +347,7 @@ __device__ __forceinline__ void tile_q_body(const StreamGemmArgs& a, uint8_t* sm
     __builtin_amdgcn_s_barrier();
     read0(f0, (kt + 1) % NSTAGE, kt + 1);
     MOE_LGK_WAIT1B(f1, f0, NF);
-    split_scales(f0);
+    scales_f32(f0);
     mfma_half(f1.a, 1);
     dequant_half(f0, 0);
     interleave();
