@@ -8,7 +8,8 @@ is overwritten eagerly before each replay, and the input changes once), and
 checks every replay bit for bit against an eager call on the same input.
 The cases cover the three expert paths: streaming with split K (few rows per
 expert), streaming without it, and the tiled kernels (many rows per expert),
-for bf16 and NVFP4 weights.
+for bf16 and NVFP4 weights; a single token (its select kernel also writes the
+permutation); and the fp8-MFMA mode (its quantiser kernels in the graph too).
 """
 import pytest
 import torch
@@ -25,6 +26,9 @@ CASES = [
     MC("graph_stream", 202, T=40, H=256, E=16, k=2, I=128),
     MC("graph_tiled", 203, T=512, H=256, E=16, k=4, I=128, zipf_s=1.1),
     MC("graph_fp4_tiled", 204, T=300, H=512, E=16, k=4, I=256, w_dtype="fp4"),
+    MC("graph_one_token", 205, T=1, H=512, E=32, k=4, I=256),
+    MC("graph_fp4_stream", 206, T=8, H=512, E=16, k=2, I=256, w_dtype="fp4"),
+    MC("graph_f8_tiled", 207, T=300, H=256, E=8, k=4, I=192, w_dtype="fp4", qmode="f8"),
 ]
 
 
