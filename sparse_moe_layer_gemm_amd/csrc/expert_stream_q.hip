@@ -281,7 +281,11 @@ __global__ __launch_bounds__(256, 2) void stream_kmajor_kernel(StreamGemmArgs a)
 // (x or h) of a super step are loaded once per workgroup into LDS (each
 // wavefront a quarter) and shared; codes go to registers, super steps rotating
 // through NSET register sets. Loads use the default cache policy (measured
-// faster than nontemporal for this pattern).
+// faster than nontemporal for this pattern). A workgroup whose K range is at
+// most one scale block (the down GEMM at the decode shape: 6 super steps)
+// instead loads the A rows of all its steps and its scale block once per pass:
+// its K loop then issues only code loads and meets no barrier (measured: the
+// per-step direct loads and barrier cost that kernel 17%).
 // MFMA v_mfma_f32_4x4x4_16b_bf16 (16 independent 4x4 blocks, K = 4): lane l
 // belongs to block l/4, supplies A row l%4 and B column l%4 (4 K values
 // each), and its result holds column l%4 of its block for rows 0..3. Here
@@ -353,12 +357,18 @@ __device__ __forceinline__ u32x4 lds_read16o(uint32_t addr) {
 
 // KT: K has a tail (K % SPAN != 0), whose chunks are clamped and whose block
 // scales are zeroed; without one those checks compile away.
-template <int RG, bool GATE_UP, bool KT>
+template <int RG, bool GATE_UP, bool KT, bool AR>
 __global__ __launch_bounds__(256, 2) void stream_fp4_kernel(StreamGemmArgs a) {
   using S = Fp4Shape<RG>;
   constexpr int SPAN = S::SPAN, CG = S::CG;
-  __shared__ __align__(16) uint8_t als[S::NSLOT * S::ASLOT];
-  __shared__ __align__(16) uint8_t sls[4][3 * S::SSLOT];  // per wavefront: 3 scale blocks
+  // AR (the K range is at most one scale block, SBLK super steps): the A rows
+  // of every step and the wavefront's scale block are loaded once per pass and
+  // stay in LDS, so the K loop issues only its code loads and needs no
+  // barrier. Otherwise A and the scales stream through rings refilled per step.
+  constexpr int ASL = AR ? S::SBLK : S::NSLOT;  // A slots
+  constexpr int NSB = AR ? 1 : 3;               // scale blocks per wavefront
+  __shared__ __align__(16) uint8_t als[ASL * S::ASLOT];
+  __shared__ __align__(16) uint8_t sls[4][NSB * S::SSLOT];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int q = lane >> 3, c8 = lane & 7;  // K range, column within an 8-column group
   const int tile = blockIdx.x * 4 + wave;
@@ -423,7 +433,7 @@ __global__ __launch_bounds__(256, 2) void stream_fp4_kernel(StreamGemmArgs a) {
     const int col = column(cw >> 3, cw & 7);
     const int k16 = (ss0 + S::SBLK * rb) * (SPAN / 16) + 16 * (lane & 7);  // scale byte of this chunk
     const uint32_t off = (uint32_t)(col < N ? col : 0) * (uint32_t)srow + (uint32_t)(k16 + 16 <= srow ? k16 : 0);
-    if (lane < 32) dma16s(srsrc, off, swave + (rb % 3) * S::SSLOT + st * 512);
+    if (lane < 32) dma16s(srsrc, off, swave + (rb % NSB) * S::SSLOT + st * 512);
   };
 
   // One pass over K for rows mc .. mc + 4 NRG - 1 (NRG row groups; padding
@@ -458,8 +468,8 @@ __global__ __launch_bounds__(256, 2) void stream_fp4_kernel(StreamGemmArgs a) {
     // of block 1 (same data, slot not yet read).
     // (measured: handing the step's K offset to the loads as their scalar
     // offset, which saves the per-lane adds, made the kernel ~3% slower)
-    auto issue = [&](int ss, u32x4* o, int t) {
-      const int slot = (ss - ss0) % S::NSLOT;
+    // A rows of super step ss into A slot `slot`
+    auto issue_a = [&](int ss, int slot) {
 #pragma unroll
       for (int d = 0; d < S::DPW; ++d) {
         uint8_t* dst = als + slot * S::ASLOT + S::RPI * (S::DPW * wave + d) * S::AROWB;
@@ -471,10 +481,15 @@ __global__ __launch_bounds__(256, 2) void stream_fp4_kernel(StreamGemmArgs a) {
           dma16s(arsrc, 2u * (arow[d] + (uint32_t)(ss * SPAN + achk[d])), dst);
         }
       }
-      if (t >= 0)
-        issue_s(t / S::SBLK + 2, t % S::SBLK);
-      else
-        issue_s(1, t + S::SBLK);
+    };
+    auto issue = [&](int ss, u32x4* o, int t) {
+      if constexpr (!AR) {
+        issue_a(ss, (ss - ss0) % S::NSLOT);
+        if (t >= 0)
+          issue_s(t / S::SBLK + 2, t % S::SBLK);
+        else
+          issue_s(1, t + S::SBLK);
+      }
       if constexpr (KT) {
         const int kl = ss * SPAN + S::G * q;
         const uint32_t kc = kl < K ? (uint32_t)kl / 2 : 0u;
@@ -499,12 +514,16 @@ __global__ __launch_bounds__(256, 2) void stream_fp4_kernel(StreamGemmArgs a) {
     // block: read the A fragments and scales, convert the codes, MFMA chains
     // and scale FMAs
     auto step = [&](int ss, const u32x4* cur, u32x4* next) {
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSET - 2) * (S::NWL + S::DPW)) : "memory");
-      __builtin_amdgcn_s_barrier();
+      if constexpr (AR) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSET - 2) * CG) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSET - 2) * (S::NWL + S::DPW)) : "memory");
+        __builtin_amdgcn_s_barrier();
+      }
       issue(clampss(ss + NSET - 1), next, ss - ss0);
       __builtin_amdgcn_sched_barrier(0);
-      const uint32_t slot = lds_base + ((ss - ss0) % S::NSLOT) * S::ASLOT;
-      const uint32_t sslot = sbase + (((ss - ss0) / S::SBLK) % 3) * S::SSLOT + ((ss - ss0) % S::SBLK) * 16;
+      const uint32_t slot = lds_base + (AR ? ss - ss0 : (ss - ss0) % S::NSLOT) * S::ASLOT;
+      const uint32_t sslot = sbase + (AR ? 0 : (((ss - ss0) / S::SBLK) % 3) * S::SSLOT) + ((ss - ss0) % S::SBLK) * 16;
       const bool kin = !KT || ss * SPAN + S::G * q < K;  // false only in a K tail
       // block scales 2q, 2q + 1 of this lane's columns (bytes 0, 1 of a u16)
       uint32_t scr[CG];
@@ -585,17 +604,35 @@ __global__ __launch_bounds__(256, 2) void stream_fp4_kernel(StreamGemmArgs a) {
     // slots are refilled; then the first scale blocks and NSET - 1 steps
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    // (only the blocks this K range reads: at most one for 8 super steps)
-    const int nblk = (ss1 - ss0 + S::SBLK - 1) / S::SBLK;
+    if constexpr (AR) {
+      // the scale block and the A rows of every step, before the first codes
 #pragma unroll 1
-    for (int st = 0; st < 2 * S::SBLK; ++st)
-      if (st / S::SBLK < nblk) issue_s(st / S::SBLK, st % S::SBLK);
+      for (int st = 0; st < S::SBLK; ++st) issue_s(0, st);
+#pragma unroll 1
+      for (int s = ss0; s < ss1; ++s) issue_a(s, s - ss0);
+    } else {
+      // (only the blocks this K range reads: at most one for 8 super steps)
+      const int nblk = (ss1 - ss0 + S::SBLK - 1) / S::SBLK;
+#pragma unroll 1
+      for (int st = 0; st < 2 * S::SBLK; ++st)
+        if (st / S::SBLK < nblk) issue_s(st / S::SBLK, st % S::SBLK);
+    }
+    // AR: once the first steps' codes are issued, the direct loads before them
+    // have landed when only those codes are outstanding; the barrier publishes
+    // every wavefront's A rows
+    auto publish = [&]() {
+      if constexpr (AR) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NSET - 1) * CG) : "memory");
+        __syncthreads();
+      }
+    };
     int ss = ss0;
     if constexpr (NSET == 4) {
       u32x4 w0[CG], w1[CG], w2[CG], w3[CG];
       issue(ss0, w0, -3);
       issue(clampss(ss0 + 1), w1, -2);
       issue(clampss(ss0 + 2), w2, -1);
+      publish();
       for (; ss + 3 < ss1; ss += 4) {
         step(ss, w0, w3);
         step(ss + 1, w1, w0);
@@ -609,6 +646,7 @@ __global__ __launch_bounds__(256, 2) void stream_fp4_kernel(StreamGemmArgs a) {
     } else if constexpr (NSET == 2) {
       u32x4 w0[CG], w1[CG];
       issue(ss0, w0, -1);
+      publish();
       for (; ss + 1 < ss1; ss += 2) {
         step(ss, w0, w1);
         step(ss + 1, w1, w0);
@@ -618,6 +656,7 @@ __global__ __launch_bounds__(256, 2) void stream_fp4_kernel(StreamGemmArgs a) {
       u32x4 w0[CG], w1[CG], w2[CG];
       issue(ss0, w0, -2);
       issue(clampss(ss0 + 1), w1, -1);
+      publish();
       for (; ss + 2 < ss1; ss += 3) {
         step(ss, w0, w2);
         step(ss + 1, w1, w0);
@@ -680,19 +719,29 @@ __global__ __launch_bounds__(256, 2) void stream_fp4_kernel(StreamGemmArgs a) {
 }
 
 // NVFP4: 16 rows per pass once experts average more than 8 rows, else 8
-template <bool GU, bool KT>
+template <bool GU, bool KT, bool AR>
 void launch_fp4_k(dim3 grid, const StreamGemmArgs& a, hipStream_t st) {
   if ((long long)a.rows > 8LL * a.E)
-    stream_fp4_kernel<4, GU, KT><<<grid, 256, 0, st>>>(a);
+    stream_fp4_kernel<4, GU, KT, AR><<<grid, 256, 0, st>>>(a);
   else
-    stream_fp4_kernel<2, GU, KT><<<grid, 256, 0, st>>>(a);
+    stream_fp4_kernel<2, GU, KT, AR><<<grid, 256, 0, st>>>(a);
 }
 template <bool GU>
 void launch_fp4(dim3 grid, const StreamGemmArgs& a, hipStream_t st) {
-  if (a.K % Fp4Shape<2>::SPAN != 0)
-    launch_fp4_k<GU, true>(grid, a, st);
-  else
-    launch_fp4_k<GU, false>(grid, a, st);
+  // K range of a workgroup, in super steps
+  const int nss = (a.K + Fp4Shape<2>::SPAN - 1) / Fp4Shape<2>::SPAN;
+  const bool ar = (a.ksplit > 1 ? a.ksteps : nss) <= Fp4Shape<2>::SBLK;
+  if (a.K % Fp4Shape<2>::SPAN != 0) {
+    if (ar)
+      launch_fp4_k<GU, true, true>(grid, a, st);
+    else
+      launch_fp4_k<GU, true, false>(grid, a, st);
+  } else {
+    if (ar)
+      launch_fp4_k<GU, false, true>(grid, a, st);
+    else
+      launch_fp4_k<GU, false, false>(grid, a, st);
+  }
 }
 
 }  // namespace
