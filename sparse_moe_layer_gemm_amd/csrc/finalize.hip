@@ -127,7 +127,11 @@ __global__ __launch_bounds__(256) void finalize_rows16_kernel(
 // for the chunk's 64 float4 columns (all 2 S loads issued together) and puts
 // them in LDS, then wavefront 0 adds them. Folding the reduction in here saves
 // a launch and a pass over the rows when the layer is latency-bound.
-template <bool BF16_OUT>
+// NS (4, 8 or 16) bounds S: the NS loads per slot are unconditional, splits
+// past S re-reading split S - 1 (not added). Loads behind a branch each would
+// leave the count of loads in flight unknown, and the wait for the second
+// slot's row position would then wait for the first slot's rows too.
+template <bool BF16_OUT, int NS>
 __global__ __launch_bounds__(256) void finalize_split_kernel(
     const float* __restrict__ part, int S, long long sstride, const int32_t* __restrict__ pair_pos,
     const float* __restrict__ w, int k, int H, int n_chunks, long long n_items,
@@ -148,18 +152,22 @@ __global__ __launch_bounds__(256) void finalize_split_kernel(
       src[h] = part + (size_t)(p >= 0 ? p : 0) * H + (col_ok ? c : 0);
       if (p < 0) use[h] = false;  // no row: the slot reads as zeros below
     }
-    f32x4 pv[2][kMaxStreamSplit];
+    // the token's weights go out before the partial sums: no load after the barrier
+    float wt[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wt[j] = j < k ? w[t * k + j] : 0.f;
+    f32x4 pv[2][NS];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int sp = 0; sp < kMaxStreamSplit; ++sp)
-        if (sp < S) pv[h][sp] = __builtin_nontemporal_load(
-                        reinterpret_cast<const f32x4*>(src[h] + sp * sstride));
+      for (int sp = 0; sp < NS; ++sp)
+        pv[h][sp] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(src[h] + (sp < S ? sp : S - 1) * sstride));
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       f32x4 v = pv[h][0];
 #pragma unroll
-      for (int sp = 1; sp < kMaxStreamSplit; ++sp)
+      for (int sp = 1; sp < NS; ++sp)
         if (sp < S) v += pv[h][sp];
       if (use[h]) rows[wave + 4 * h][lane] = v;
       else if (wave + 4 * h < k && col_ok) rows[wave + 4 * h][lane] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -170,12 +178,11 @@ __global__ __launch_bounds__(256) void finalize_split_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (j < k) {
-          const float wt = w[t * k + j];
           const f32x4 v = rows[j][lane];
-          acc.x = fmaf(wt, v.x, acc.x);
-          acc.y = fmaf(wt, v.y, acc.y);
-          acc.z = fmaf(wt, v.z, acc.z);
-          acc.w = fmaf(wt, v.w, acc.w);
+          acc.x = fmaf(wt[j], v.x, acc.x);
+          acc.y = fmaf(wt[j], v.y, acc.y);
+          acc.z = fmaf(wt[j], v.z, acc.z);
+          acc.w = fmaf(wt[j], v.w, acc.w);
         }
       }
       if (out_f32) *reinterpret_cast<float4*>(out_f32 + (size_t)t * H + c) = acc;
@@ -201,12 +208,22 @@ hipError_t launch_finalize_split(const float* part, int S, long long sstride,
   const int n_chunks = (H + 255) / 256;
   const long long items = (long long)T * n_chunks;
   const unsigned grid = (unsigned)(items < (1 << 20) ? items : (1 << 20));
-  if (out_bf16)
-    finalize_split_kernel<true><<<grid, 256, 0, st>>>(part, S, sstride, pair_pos, w, k, H,
-                                                      n_chunks, items, out, out_f32);
+  auto go = [&](auto ns) {
+    constexpr int NS = decltype(ns)::value;
+    if (out_bf16)
+      finalize_split_kernel<true, NS><<<grid, 256, 0, st>>>(part, S, sstride, pair_pos, w, k, H,
+                                                            n_chunks, items, out, out_f32);
+    else
+      finalize_split_kernel<false, NS><<<grid, 256, 0, st>>>(part, S, sstride, pair_pos, w, k, H,
+                                                             n_chunks, items, out, out_f32);
+  };
+  static_assert(kMaxStreamSplit == 16, "split bound buckets");
+  if (S <= 4)
+    go(std::integral_constant<int, 4>{});
+  else if (S <= 8)
+    go(std::integral_constant<int, 8>{});
   else
-    finalize_split_kernel<false><<<grid, 256, 0, st>>>(part, S, sstride, pair_pos, w, k, H,
-                                                       n_chunks, items, out, out_f32);
+    go(std::integral_constant<int, 16>{});
   return hipGetLastError();
 }
 

@@ -207,6 +207,8 @@ __global__ __launch_bounds__(256) void router_select_wg_kernel(
   if (e < E) {
     const float* p = part + (size_t)t * ldp + e;
     const size_t sstride = (size_t)T * ldp;
+    // the bias goes out with the partials: the same memory latency
+    const float be = bias ? bias[e] : 0.f;
     // up to 40 partials (the most the split plan makes) are loaded in one
     // batch (one memory latency), then added in split order
     float v = 0.f;
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(256) void router_select_wg_kernel(
       for (int j = 0; j < 40; ++j)
         if (sp0 + j < n_split) v += u[j];
     }
-    if (bias) v += bias[e];
+    if (bias) v += be;
     if (logits_f32) logits_f32[(size_t)t * E + e] = v;
     float sv = v;
     if constexpr (BF16_LOGITS) {
