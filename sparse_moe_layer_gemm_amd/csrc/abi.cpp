@@ -163,9 +163,12 @@ size_t experts_ws_bytes(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
 }
 
 // The tiled grouped GEMMs pay off once experts average enough rows to fill
-// their 128-row tiles; below that, streaming each weight once per 32 rows wins.
+// their 128-row tiles; below that, streaming each weight once per pass of 32
+// rows (bf16, FP8) or 8 rows (NVFP4) wins.
 bool use_tile_kernel(int32_t w_dtype, int64_t P, int32_t E) {
-  return w_dtype != MOE_F32 && P >= (int64_t)moe::kTileMinRowsPerExpert * E;
+  if (w_dtype == MOE_F32) return false;
+  if (w_dtype == MOE_FP4_E2M1) return P > (int64_t)moe::kStreamMaxRowsPerExpertFp4 * E;
+  return P >= (int64_t)moe::kTileMinRowsPerExpert * E;
 }
 
 // Sizes whose tiled work lists would overflow int indexing are unsupported.

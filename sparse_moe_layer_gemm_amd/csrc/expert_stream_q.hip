@@ -718,13 +718,13 @@ __global__ __launch_bounds__(256, 2) void stream_fp4_kernel(StreamGemmArgs a) {
   }
 }
 
-// NVFP4: 16 rows per pass once experts average more than 8 rows, else 8
+// NVFP4: 8 rows per pass at any row count (measured at 12 and 16 rows per
+// expert: two 8-row passes beat one 16-row pass by 20%, whose kernel wants
+// ~400 registers and spills at two workgroups per CU, and by 7% with one
+// workgroup per CU and no spills)
 template <bool GU, bool KT, bool AR>
 void launch_fp4_k(dim3 grid, const StreamGemmArgs& a, hipStream_t st) {
-  if ((long long)a.rows > 8LL * a.E)
-    stream_fp4_kernel<4, GU, KT, AR><<<grid, 256, 0, st>>>(a);
-  else
-    stream_fp4_kernel<2, GU, KT, AR><<<grid, 256, 0, st>>>(a);
+  stream_fp4_kernel<2, GU, KT, AR><<<grid, 256, 0, st>>>(a);
 }
 template <bool GU>
 void launch_fp4(dim3 grid, const StreamGemmArgs& a, hipStream_t st) {

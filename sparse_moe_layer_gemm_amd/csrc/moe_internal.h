@@ -191,6 +191,12 @@ hipError_t launch_router_bf16x3(const uint16_t* x, int T, int H, const float* w_
                                 float* part, void* ws, hipStream_t st);
 // Rows per expert from which the tiled kernel replaces the streaming one.
 constexpr int kTileMinRowsPerExpert = 32;
+// NVFP4 weights: the streaming kernel reads an expert's weights once per 8
+// rows, while the tiled kernel's time hardly depends on the rows (its
+// dequantisation is per weight column). Measured at H = 5120, I = 1536,
+// E = 256, k = 8: streaming 1.03 / 1.36 / 1.69 / 2.23 ms at 8 / 12 / 16 / 24
+// rows per expert, tiled 1.77 ms at each. Tiled above 16 rows per expert.
+constexpr int kStreamMaxRowsPerExpertFp4 = 16;
 
 // fp32 expert path (reference-precision layer; one thread per output element).
 hipError_t launch_expert_f32(const float* x, int T, int H, int I, int E, int k, int P,
