@@ -32,6 +32,11 @@ SMALL = [
     MC("fp8_small", 107, T=50, H=256, E=8, k=2, I=128, w_dtype="fp8"),
     MC("fp4_small", 108, T=50, H=256, E=8, k=2, I=192, w_dtype="fp4"),
     MC("fp4_many_rows", 109, T=300, H=512, E=16, k=4, I=256, w_dtype="fp4"),
+    # either side of the NVFP4 streaming / tiled boundary (more than 16 rows
+    # per expert on average goes tiled): 16 rows per expert stream in 8-row
+    # passes, 18 take the tiled kernels with short experts
+    MC("fp4_stream_16rows", 140, T=64, H=512, E=16, k=4, I=256, w_dtype="fp4"),
+    MC("fp4_tile_18rows", 141, T=72, H=512, E=16, k=4, I=256, w_dtype="fp4"),
     MC("f32_ragged", 110, T=37, H=64, E=9, k=2, I=64, x_dtype="f32", w_dtype="f32"),
     # fp32 experts with many 16-row passes per expert
     MC("f32_many_rows", 130, T=300, H=256, E=4, k=2, I=192, x_dtype="f32", w_dtype="f32"),
