@@ -168,9 +168,10 @@ moe_status moe_experts(const void* x, int32_t x_dtype, int64_t T, int32_t H, int
  * two calls whenever moe_experts_rows16 supports the call.
  * moe_experts_rows16: as moe_experts, writing y16 [T*k, H] (uint16 fp16 bits)
  * and y16_scale [T*k, H/64] (uint8) instead of y_sorted; supported wherever
- * the experts run on the tiled kernels: bf16, FP8 and NVFP4 weights when the
- * experts average at least 32 rows (T*k >= 32*E), and the fp8-MFMA mode
- * (MOE_QMODE_F8) at any size; else MOE_ERR_UNSUPPORTED. Same workspace as
+ * the experts run on the tiled kernels: bf16 and FP8 weights when the experts
+ * average at least 32 rows (T*k >= 32*E), NVFP4 weights when they average
+ * more than 16 (T*k > 16*E), and the fp8-MFMA mode (MOE_QMODE_F8) at any
+ * size; else MOE_ERR_UNSUPPORTED. Same workspace as
  * moe_experts.
  * moe_finalize_rows16: as moe_finalize, reading the compact rows; each value
  * is decoded exactly to fp32 and summed as moe_finalize sums. */

@@ -175,6 +175,10 @@ def test_experts_rows16_validation():
     assert experts_rows16(T=0, x=None, off=None, sp=None, y16=None, ysc=None, ws=None) == OK
     assert experts_rows16(T=128) == UNSUP  # 4 rows per expert: the streaming kernels
     assert experts_rows16(T=128, w=_w(dtype=2, gus=G, dns=Hh)) == UNSUP  # FP8, streaming sizes
+    # NVFP4 streams up to 16 rows per expert (T*k = 16 E here), FP8 up to 31
+    fp4 = _w(dtype=3, gus=G, dns=Hh, gug=J, dng=J)
+    assert experts_rows16(T=512, w=fp4) == UNSUP
+    assert experts_rows16(T=1000, w=_w(dtype=2, gus=G, dns=Hh)) == UNSUP
     assert experts_rows16(ysc=None) == INVAL
     assert experts_rows16(y16=MIS) == INVAL
     assert experts_rows16(ws_bytes=1024) == WS_SMALL
