@@ -37,6 +37,9 @@ SMALL = [
     # passes, 18 take the tiled kernels with short experts
     MC("fp4_stream_16rows", 140, T=64, H=512, E=16, k=4, I=256, w_dtype="fp4"),
     MC("fp4_tile_18rows", 141, T=72, H=512, E=16, k=4, I=256, w_dtype="fp4"),
+    # ~12 rows per expert on wider products (I = 512, H = 1024): one to three
+    # 8-row NVFP4 streaming passes per expert, 32 gate/up and 32 down column tiles
+    MC("fp4_stream_12rows_wide", 142, T=48, H=1024, E=8, k=2, I=512, w_dtype="fp4"),
     MC("f32_ragged", 110, T=37, H=64, E=9, k=2, I=64, x_dtype="f32", w_dtype="f32"),
     # fp32 experts with many 16-row passes per expert
     MC("f32_many_rows", 130, T=300, H=256, E=4, k=2, I=192, x_dtype="f32", w_dtype="f32"),
