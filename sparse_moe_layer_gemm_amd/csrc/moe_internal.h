@@ -198,7 +198,7 @@ constexpr int kTileMinRowsPerExpert = 32;
 // rows per expert, tiled 1.77 ms at each. Tiled above 16 rows per expert.
 constexpr int kStreamMaxRowsPerExpertFp4 = 16;
 
-// fp32 expert path (reference-precision layer; one thread per output element).
+// fp32 expert path (reference-precision layer; fp32 MFMA 16x16x4, fp32 accumulation).
 hipError_t launch_expert_f32(const float* x, int T, int H, int I, int E, int k, int P,
                              const int32_t* offsets, const int32_t* sorted_pair,
                              const float* gate_up, const float* down, float* h, float* y,
