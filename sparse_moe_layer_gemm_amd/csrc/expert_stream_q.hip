@@ -360,6 +360,7 @@ __device__ __forceinline__ u32x4 lds_read16o(uint32_t addr) {
 template <int RG, bool GATE_UP, bool KT, bool AR>
 __global__ __launch_bounds__(256, 2) void stream_fp4_kernel(StreamGemmArgs a) {
   using S = Fp4Shape<RG>;
+  static_assert(RG == 2, "8 rows per pass: 16 need more registers than two workgroups per CU allow");
   constexpr int SPAN = S::SPAN, CG = S::CG;
   // AR (the K range is at most one scale block, SBLK super steps): the A rows
   // of every step and the wavefront's scale block are loaded once per pass and
@@ -441,9 +442,10 @@ __global__ __launch_bounds__(256, 2) void stream_fp4_kernel(StreamGemmArgs a) {
   // constant: branching on it inside the K loop costs registers.
   auto pass = [&](int mc, auto nrg_c) {
     constexpr int NRG = decltype(nrg_c)::value;
+    static_assert(NRG == 1 || NRG == 2, "one or two row groups");
     // (the down GEMM's short K range, 6 super steps at the decode shape,
     // gains from a third code set at up to 4 rows: 4% on that kernel)
-    constexpr int NSET = (!GATE_UP && NRG == 1) ? 3 : NRG <= 2 ? MOE_FP4_NSET : 2;
+    constexpr int NSET = (!GATE_UP && NRG == 1) ? 3 : MOE_FP4_NSET;
     static_assert(NSET <= S::NSLOT, "A slots for every step in flight");
     // column groups whose MFMA chains run side by side
     constexpr int CI = (MOE_FP4_CHAINS / NRG) < 1 ? 1 : (MOE_FP4_CHAINS / NRG) > CG ? CG : MOE_FP4_CHAINS / NRG;
@@ -544,25 +546,16 @@ __global__ __launch_bounds__(256, 2) void stream_fp4_kernel(StreamGemmArgs a) {
           const uint32_t aa = slot + aoff[2 * sb + h];
           af[0][h] = lds_read16o<0>(aa);
           if constexpr (NRG > 1) af[1][h] = lds_read16o<4 * S::AROWB>(aa);
-          if constexpr (NRG > 2) af[2][h] = lds_read16o<8 * S::AROWB>(aa);
-          if constexpr (NRG > 3) af[3][h] = lds_read16o<12 * S::AROWB>(aa);
         }
         if constexpr (NRG == 1)
           asm volatile("s_waitcnt lgkmcnt(0)"
                        : "+v"(af[0][0]), "+v"(af[0][1]), "+v"(scr[0]), "+v"(scr[1]), "+v"(scr[2]), "+v"(scr[3])
                        :
                        : "memory");
-        else if constexpr (NRG == 2)
+        else
           asm volatile("s_waitcnt lgkmcnt(0)"
                        : "+v"(af[0][0]), "+v"(af[0][1]), "+v"(af[1][0]), "+v"(af[1][1]), "+v"(scr[0]), "+v"(scr[1]),
                          "+v"(scr[2]), "+v"(scr[3])
-                       :
-                       : "memory");
-        else
-          asm volatile("s_waitcnt lgkmcnt(0)"
-                       : "+v"(af[0][0]), "+v"(af[0][1]), "+v"(af[1][0]), "+v"(af[1][1]), "+v"(af[2][0]),
-                         "+v"(af[2][1]), "+v"(af[3][0]), "+v"(af[3][1]), "+v"(scr[0]), "+v"(scr[1]), "+v"(scr[2]),
-                         "+v"(scr[3])
                        :
                        : "memory");
         if (sb == 0) {  // as fp32 (exact), zero past K
@@ -711,10 +704,8 @@ __global__ __launch_bounds__(256, 2) void stream_fp4_kernel(StreamGemmArgs a) {
     const int nrg = (cnt - mc + 3) / 4;  // row groups holding rows
     if (nrg <= 1)
       pass(mc, std::integral_constant<int, 1>{});
-    else if (RG == 2 || nrg == 2)
-      pass(mc, std::integral_constant<int, 2>{});
     else
-      pass(mc, std::integral_constant<int, RG>{});
+      pass(mc, std::integral_constant<int, 2>{});
   }
 }
 
