@@ -44,7 +44,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", choices=["decode", "prefill"], default="decode")
+    p.add_argument("--workload", choices=["decode", "prefill", "small"], default="decode",
+                   help="small: only the small-batch decode records (T = 1, 8, 32), one JSON line "
+                        "(for kernel traces of those batches)")
     p.add_argument("--no-prefill", action="store_true", help="skip the secondary prefill line")
     p.add_argument("--no-quant", action="store_true", help="skip the secondary NVFP4 line")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -549,6 +551,11 @@ def main():
 
     dec_cfg = synth.CONFIGS["decode_t128"]
     pre_cfg = synth.CONFIGS["prefill_t16384_zipf"]
+    if a.workload == "small":
+        progress("generating decode inputs (T=128, bf16 experts) for the small batches")
+        dec = Workload(dec_cfg, moe, torch)
+        print(json.dumps({"decode_small": decode_small(torch, moe, dec)}), flush=True)
+        return
     dec_line = pre_line = dec = pre = None
     if a.workload == "decode":
         progress("generating decode inputs (T=128, bf16 experts)")
